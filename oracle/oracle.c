@@ -1,0 +1,317 @@
+/*
+ * oracle.c -- plain, slow CPU oracle of the low-bit quantized MoE expert FFN.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test-suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load or call this library.  It shares no
+ * code, header, table or constant with the HIP library; it computes the plain
+ * definitions the pages give, in double precision, with scalar loops:
+ *
+ *   dequantize   w = s * q            (symmetric INT4 / INT2 and ternary)
+ *                w = s * q + b        (affine; ternary stored as affine has b = -s)
+ *   route        top-k experts per token by logit, weights = softmax over the
+ *                selected logits (sums to one)
+ *   expert FFN   a = W1 x;  h_i = silu(a[2i]) * a[2i+1];  o = W2 h
+ *   combine      y[t] = sum_j w[t][j] * o_(t,j), then one round to nearest
+ *                even into the activation dtype.
+ *
+ * Sources on the pages:
+ *   - onnxruntime pull request 33005, "[CUDA] Enable SM80+ FP16/BF16 mixed
+ *     INT2/INT4 QMoE prefill by default", sections Description and Current
+ *     Scope: symmetric codes without zero points, blocks of 64 along K, gate
+ *     and up rows interleaved for a fused SwiGLU, and the stage order routing,
+ *     rows grouped by expert, FC1, SwiGLU, FC2, top-k weighted finalize.
+ *   - MLX issue 3852, "2-bit quantized_matmul loses its size advantage over
+ *     4-bit at M >= 3", the repro and the closing remarks: affine groups of
+ *     128 with one scale and one bias per group, W stored as [N][K]
+ *     (transpose=True), and ternary checkpoints that are affine with values
+ *     {-s, 0, +s} and bias equal to minus the scale.
+ *   - "The QMoE sub-1-bit expert kernel is a GEMV ..." (inference-research
+ *     gotcha page): an inner loop over the tokens that share an expert
+ *     computes the same products as one GEMV per token.
+ *
+ * Readings where the pages are silent (each is listed in the design notes):
+ *   canonical storage = fields LSB-first along K within each byte; symmetric
+ *   b-bit code q = u - 2^(b-1); ternary q = u - 1 with u = 3 invalid; even
+ *   FC1 row 2i is gate_i and odd row 2i+1 is up_i; SwiGLU is silu(g) * u with
+ *   silu(g) = g / (1 + exp(-g)); top-k ties go to the lower expert index and
+ *   the ids are ordered by descending logit; the routing weights are the
+ *   softmax of the k selected logits; every routed slot is computed.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+enum { ORC_SYM_INT4 = 0, ORC_SYM_INT2 = 1, ORC_TERNARY = 2, ORC_AFFINE_INT2 = 3, ORC_AFFINE_INT4 = 4 };
+enum { ORC_BF16 = 0, ORC_F16 = 1 };
+
+/* ---------- 16-bit floating point, from the IEEE 754 definitions ---------- */
+
+/* bfloat16: 1 sign, 8 exponent (bias 127), 7 fraction bits.
+ * binary16: 1 sign, 5 exponent (bias 15), 10 fraction bits. */
+static void orc_format(int dtype, int *mant, int *ebits, int *bias) {
+  if (dtype == ORC_BF16) { *mant = 7; *ebits = 8; *bias = 127; }
+  else { *mant = 10; *ebits = 5; *bias = 15; }
+}
+
+double orc_half_to_double(uint16_t h, int dtype) {
+  int mant, ebits, bias;
+  orc_format(dtype, &mant, &ebits, &bias);
+  int sign = (h >> 15) & 1;
+  int e = (h >> mant) & ((1 << ebits) - 1);
+  int m = h & ((1 << mant) - 1);
+  double v;
+  if (e == 0) {
+    v = ldexp((double)m, 1 - bias - mant);               /* subnormal or zero */
+  } else if (e == (1 << ebits) - 1) {
+    v = (m == 0) ? INFINITY : NAN;
+  } else {
+    v = ldexp((double)((1 << mant) + m), e - bias - mant); /* (1 + m/2^mant) 2^(e-bias) */
+  }
+  return sign ? -v : v;
+}
+
+/* Round a double to the nearest value of the 16-bit format, ties to even. */
+uint16_t orc_double_to_half(double v, int dtype) {
+  int mant, ebits, bias;
+  orc_format(dtype, &mant, &ebits, &bias);
+  const int emin = 1 - bias, emax = bias;
+  const uint16_t sign = signbit(v) ? (uint16_t)0x8000 : 0;
+  const uint16_t inf_bits = (uint16_t)(((1 << ebits) - 1) << mant);
+  if (isnan(v)) return (uint16_t)(inf_bits | (1 << (mant - 1)));
+  double a = fabs(v);
+  if (isinf(a)) return sign | inf_bits;
+  if (a == 0.0) return sign;
+  int ex;
+  frexp(a, &ex);              /* a = f 2^ex, f in [0.5, 1)  ->  binade exponent ex-1 */
+  int E = ex - 1;
+  if (E < emin) E = emin;     /* subnormal range: fixed spacing */
+  if (E > emax) return sign | inf_bits;
+  double ulp = ldexp(1.0, E - mant);
+  double r = nearbyint(a / ulp); /* default rounding mode: nearest, ties to even */
+  double rv = r * ulp;
+  if (rv == 0.0) return sign;
+  frexp(rv, &ex);
+  int E2 = ex - 1;
+  if (E2 > emax) return sign | inf_bits;
+  if (E2 < emin) { /* subnormal result */
+    uint16_t m = (uint16_t)(rv / ldexp(1.0, emin - mant));
+    return sign | m;
+  }
+  uint16_t ebits_v = (uint16_t)(E2 + bias);
+  uint16_t m = (uint16_t)(rv / ldexp(1.0, E2 - mant) - (double)(1 << mant));
+  return (uint16_t)(sign | (ebits_v << mant) | m);
+}
+
+void orc_halves_to_double(const uint16_t *h, int64_t n, int dtype, double *out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_half_to_double(h[i], dtype);
+}
+
+void orc_doubles_to_half(const double *v, int64_t n, int dtype, uint16_t *out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_double_to_half(v[i], dtype);
+}
+
+/* ---------------------------- codec & dequant ---------------------------- */
+
+int orc_bits(int fmt) {
+  return (fmt == ORC_SYM_INT4 || fmt == ORC_AFFINE_INT4) ? 4 : 2;
+}
+
+/* Stored field u of weight k in a packed row: fields run LSB-first along K. */
+static int orc_field(const uint8_t *row, int bits, int64_t k) {
+  int64_t bit = k * bits;
+  return (row[bit >> 3] >> (bit & 7)) & ((1 << bits) - 1);
+}
+
+/* Field value -> integer code.  *bad is set for the unused ternary value 3. */
+static int orc_code(int fmt, int u, int *bad) {
+  switch (fmt) {
+    case ORC_SYM_INT4: return u - 8;  /* [-8, 7] */
+    case ORC_SYM_INT2: return u - 2;  /* [-2, 1] */
+    case ORC_TERNARY:
+      if (u == 3) { *bad = 1; return 0; }
+      return u - 1;                   /* {-1, 0, 1} */
+    default: return u;                /* affine: unsigned [0, 2^b - 1] */
+  }
+}
+
+static int orc_is_affine(int fmt) { return fmt == ORC_AFFINE_INT2 || fmt == ORC_AFFINE_INT4; }
+
+/* Integer codes of a [rows][K] matrix; returns the number of invalid fields. */
+int64_t orc_unpack_codes(int fmt, const uint8_t *packed, int64_t rows, int64_t K, int8_t *out) {
+  const int bits = orc_bits(fmt);
+  const int64_t row_bytes = K * bits / 8;
+  int64_t nbad = 0;
+  for (int64_t n = 0; n < rows; ++n) {
+    for (int64_t k = 0; k < K; ++k) {
+      int bad = 0;
+      out[n * K + k] = (int8_t)orc_code(fmt, orc_field(packed + n * row_bytes, bits, k), &bad);
+      nbad += bad;
+    }
+  }
+  return nbad;
+}
+
+/* One dequantized row: w[k] = s*q (+ b for affine), s and b of block k/B. */
+static void orc_dequant_row(int fmt, int block, int sdtype, const uint8_t *codes_row,
+                            const uint16_t *scales_row, const uint16_t *biases_row,
+                            int64_t K, double *w, int *bad) {
+  const int bits = orc_bits(fmt);
+  for (int64_t k = 0; k < K; ++k) {
+    int q = orc_code(fmt, orc_field(codes_row, bits, k), bad);
+    double s = orc_half_to_double(scales_row[k / block], sdtype);
+    double v = s * (double)q;
+    if (orc_is_affine(fmt)) v += orc_half_to_double(biases_row[k / block], sdtype);
+    w[k] = v;
+  }
+}
+
+void orc_dequant(int fmt, int block, int sdtype, const uint8_t *codes, const uint16_t *scales,
+                 const uint16_t *biases, int64_t rows, int64_t K, double *W) {
+  const int64_t row_bytes = K * orc_bits(fmt) / 8, nb = K / block;
+  int bad = 0;
+  for (int64_t n = 0; n < rows; ++n)
+    orc_dequant_row(fmt, block, sdtype, codes + n * row_bytes, scales + n * nb,
+                    biases ? biases + n * nb : NULL, K, W + n * K, &bad);
+}
+
+/* -------------------------------- routing -------------------------------- */
+
+/* Per token: the k largest logits (ties to the lower expert index), in
+ * descending order; weights = softmax over the selected logits.  Then the
+ * expert map: counts, exclusive offsets (E+1 entries) and the list of flat
+ * slots r = t*k + j grouped by expert, ascending r within an expert. */
+void orc_route(int T, int E, int k, const float *logits, int32_t *ids, double *w,
+               int32_t *counts, int32_t *offsets, int32_t *row_list) {
+  char *taken = (char *)malloc((size_t)E);
+  for (int t = 0; t < T; ++t) {
+    const float *l = logits + (int64_t)t * E;
+    memset(taken, 0, (size_t)E);
+    for (int j = 0; j < k; ++j) {
+      int best = -1;
+      for (int e = 0; e < E; ++e) {
+        if (taken[e]) continue;
+        if (best < 0 || l[e] > l[best]) best = e;
+      }
+      taken[best] = 1;
+      ids[(int64_t)t * k + j] = best;
+    }
+    double m = (double)l[ids[(int64_t)t * k]];
+    double sum = 0.0;
+    for (int j = 0; j < k; ++j) sum += exp((double)l[ids[(int64_t)t * k + j]] - m);
+    for (int j = 0; j < k; ++j) w[(int64_t)t * k + j] = exp((double)l[ids[(int64_t)t * k + j]] - m) / sum;
+  }
+  free(taken);
+  const int64_t S = (int64_t)T * k;
+  for (int e = 0; e < E; ++e) counts[e] = 0;
+  for (int64_t r = 0; r < S; ++r) counts[ids[r]] += 1;
+  offsets[0] = 0;
+  for (int e = 0; e < E; ++e) offsets[e + 1] = offsets[e] + counts[e];
+  int64_t pos = 0;
+  for (int e = 0; e < E; ++e)
+    for (int64_t r = 0; r < S; ++r)
+      if (ids[r] == e) row_list[pos++] = (int32_t)r;
+}
+
+/* ------------------------------ expert FFN ------------------------------- */
+
+double orc_silu(double g) { return g / (1.0 + exp(-g)); }
+
+typedef struct {
+  int fmt, block, sdtype;
+  const uint8_t *codes;
+  const uint16_t *scales, *biases;
+} orc_mat;
+
+/* out[n] = sum_k W[e][n][k] * v[k] for n in [0, N). */
+static void orc_matvec(const orc_mat *m, int64_t e, int64_t N, int64_t K, const double *v,
+                       double *out, double *wrow, int *bad) {
+  const int64_t row_bytes = K * orc_bits(m->fmt) / 8, nb = K / m->block;
+  for (int64_t n = 0; n < N; ++n) {
+    const int64_t r = e * N + n;
+    orc_dequant_row(m->fmt, m->block, m->sdtype, m->codes + r * row_bytes, m->scales + r * nb,
+                    m->biases ? m->biases + r * nb : NULL, K, wrow, bad);
+    double acc = 0.0;
+    for (int64_t k = 0; k < K; ++k) acc += wrow[k] * v[k];
+    out[n] = acc;
+  }
+}
+
+/*
+ * Full MoE layer for T tokens.  x [T][H] and y16 [T][H] are 16-bit patterns of
+ * act_dtype, logits [T][E] float32, y64 [T][H] the unrounded result.  Optional
+ * per-slot diagnostics in slot order r = t*k + j: a_dbg [T*k][2I] (FC1),
+ * h_dbg [T*k][I] (after SwiGLU), o_dbg [T*k][H] (FC2).  Returns 0, or -1 if a
+ * ternary row it used holds the invalid field value 3 (read as 0).
+ */
+int orc_moe(int E, int H, int I, int k, int act_dtype,
+            int fc1_fmt, int fc1_block, int fc1_sdtype,
+            const uint8_t *fc1_codes, const uint16_t *fc1_scales, const uint16_t *fc1_biases,
+            int fc2_fmt, int fc2_block, int fc2_sdtype,
+            const uint8_t *fc2_codes, const uint16_t *fc2_scales, const uint16_t *fc2_biases,
+            const uint16_t *x, const float *logits, int T,
+            double *y64, uint16_t *y16, double *a_dbg, double *h_dbg, double *o_dbg) {
+  orc_mat w1 = {fc1_fmt, fc1_block, fc1_sdtype, fc1_codes, fc1_scales, fc1_biases};
+  orc_mat w2 = {fc2_fmt, fc2_block, fc2_sdtype, fc2_codes, fc2_scales, fc2_biases};
+  const int64_t S = (int64_t)T * k;
+  int32_t *ids = (int32_t *)malloc(sizeof(int32_t) * (size_t)(S > 0 ? S : 1));
+  double *wts = (double *)malloc(sizeof(double) * (size_t)(S > 0 ? S : 1));
+  int32_t *counts = (int32_t *)malloc(sizeof(int32_t) * (size_t)E);
+  int32_t *offsets = (int32_t *)malloc(sizeof(int32_t) * (size_t)(E + 1));
+  int32_t *rows = (int32_t *)malloc(sizeof(int32_t) * (size_t)(S > 0 ? S : 1));
+  double *xv = (double *)malloc(sizeof(double) * (size_t)H);
+  double *a = (double *)malloc(sizeof(double) * (size_t)(2 * I));
+  double *h = (double *)malloc(sizeof(double) * (size_t)I);
+  double *o = (double *)malloc(sizeof(double) * (size_t)H);
+  double *wrow = (double *)malloc(sizeof(double) * (size_t)(H > I ? H : I));
+  int bad = 0;
+  orc_route(T, E, k, logits, ids, wts, counts, offsets, rows);
+  for (int t = 0; t < T; ++t) {
+    for (int64_t n = 0; n < H; ++n) xv[n] = orc_half_to_double(x[(int64_t)t * H + n], act_dtype);
+    double *yt = y64 + (int64_t)t * H;
+    for (int64_t n = 0; n < H; ++n) yt[n] = 0.0;
+    for (int j = 0; j < k; ++j) {
+      const int64_t r = (int64_t)t * k + j;
+      const int e = ids[r];
+      orc_matvec(&w1, e, 2 * (int64_t)I, H, xv, a, wrow, &bad);
+      for (int64_t i = 0; i < I; ++i) h[i] = orc_silu(a[2 * i]) * a[2 * i + 1];
+      orc_matvec(&w2, e, H, I, h, o, wrow, &bad);
+      for (int64_t n = 0; n < H; ++n) yt[n] += wts[r] * o[n];
+      if (a_dbg) memcpy(a_dbg + r * 2 * I, a, sizeof(double) * (size_t)(2 * I));
+      if (h_dbg) memcpy(h_dbg + r * I, h, sizeof(double) * (size_t)I);
+      if (o_dbg) memcpy(o_dbg + r * H, o, sizeof(double) * (size_t)H);
+    }
+    for (int64_t n = 0; n < H; ++n) y16[(int64_t)t * H + n] = orc_double_to_half(yt[n], act_dtype);
+  }
+  free(ids); free(wts); free(counts); free(offsets); free(rows);
+  free(xv); free(a); free(h); free(o); free(wrow);
+  return bad ? -1 : 0;
+}
+
+/*
+ * Dense quantized matmul y = x W^T for output rows n in [n0, n1):
+ * y64 [M][n1-n0] unrounded, y16 the same rounded to x's dtype.
+ */
+void orc_linear(int fmt, int block, int sdtype, const uint8_t *codes, const uint16_t *scales,
+                const uint16_t *biases, int64_t N, int64_t K, const uint16_t *x, int x_dtype, int M,
+                int64_t n0, int64_t n1, double *y64, uint16_t *y16) {
+  (void)N;
+  const int64_t row_bytes = K * orc_bits(fmt) / 8, nb = K / block, W = n1 - n0;
+  double *wrow = (double *)malloc(sizeof(double) * (size_t)K);
+  double *xv = (double *)malloc(sizeof(double) * (size_t)K * (size_t)(M > 0 ? M : 1));
+  for (int m = 0; m < M; ++m)
+    for (int64_t k = 0; k < K; ++k) xv[(int64_t)m * K + k] = orc_half_to_double(x[(int64_t)m * K + k], x_dtype);
+  int bad = 0;
+  for (int64_t n = n0; n < n1; ++n) {
+    orc_dequant_row(fmt, block, sdtype, codes + n * row_bytes, scales + n * nb,
+                    biases ? biases + n * nb : NULL, K, wrow, &bad);
+    for (int m = 0; m < M; ++m) {
+      double acc = 0.0;
+      for (int64_t k = 0; k < K; ++k) acc += wrow[k] * xv[(int64_t)m * K + k];
+      y64[(int64_t)m * W + (n - n0)] = acc;
+      y16[(int64_t)m * W + (n - n0)] = orc_double_to_half(acc, x_dtype);
+    }
+  }
+  free(wrow);
+  free(xv);
+}

@@ -1,0 +1,22 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+    config.addinivalue_line("markers", "slow: large sizes (full workload shapes)")
+
+
+@pytest.fixture(scope="session")
+def oracle_lib():
+    import oracle
+    from oracle import build as ob
+    ob.build()
+    oracle._lib = None
+    return oracle

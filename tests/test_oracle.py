@@ -1,0 +1,305 @@
+"""Pins of the CPU oracle against facts fixed outside it (no GPU).
+
+Each test ties one part of the oracle to something other than itself: bytes
+hand-packed from the format definitions, library routines (NumPy float16
+casts, lexsort, bincount, stable argsort, softmax), exact integer
+arithmetic, identities between formats that the pages state, and an
+independent dense float64 brute force on tiny shapes.
+"""
+
+import json
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+
+import synth
+from synth.workloads import custom_moe_spec, custom_linear_spec
+from tests import bruteforce as bf
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ------------------------------------------------------------ 16-bit floats
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_half_decode_exhaustive(oracle_lib, dtype):
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    got = oracle_lib.half_to_double(bits, dtype)
+    ref = bf.half_bits_to_f64(bits, dtype)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    # encode(decode(b)) is the identity on every non-NaN pattern
+    back = oracle_lib.double_to_half(got[~nan], dtype)
+    assert np.array_equal(back, bits[~nan])
+
+
+def test_f16_rounding_matches_numpy(oracle_lib):
+    rng = np.random.default_rng(1)
+    v = np.concatenate([
+        rng.standard_normal(20000) * 10.0 ** rng.integers(-9, 6, 20000),
+        (np.arange(-2048, 2048) + 0.5) * 2.0 ** -24,     # subnormal halfway points
+        (np.arange(1024, 2048) + 0.5) * 2.0 ** -10,      # normal halfway points
+        [65504.0, 65519.99, 65520.0, 1e6, -1e-9, 0.0, -0.0],
+    ])
+    got = oracle_lib.double_to_half(v, "f16")
+    ref = v.astype(np.float16).view(np.uint16)
+    assert np.array_equal(got, ref)
+
+
+def test_bf16_rounding_is_nearest_even(oracle_lib):
+    rng = np.random.default_rng(2)
+    v = np.concatenate([
+        rng.standard_normal(20000) * 10.0 ** rng.integers(-38, 30, 20000),
+        (np.arange(128, 256) + 0.5) * 2.0 ** -7,        # ties at exponent 0
+        (np.arange(0, 128) + 0.5) * 2.0 ** -133,        # ties in the subnormal range
+    ])
+    got = oracle_lib.double_to_half(v, "bf16")
+    g = oracle_lib.half_to_double(got, "bf16")
+    # neighbours in bit space of |v|'s encoding
+    mag = got & 0x7FFF
+    lo = oracle_lib.half_to_double((mag - 1).astype(np.uint16), "bf16")
+    hi = oracle_lib.half_to_double((mag + 1).astype(np.uint16), "bf16")
+    a = np.abs(v)
+    d = np.abs(np.abs(g) - a)
+    ok_lo = (mag == 0) | (d <= np.abs(lo - a))
+    ok_hi = d <= np.abs(hi - a)
+    assert np.all(ok_lo & ok_hi)
+    ties = (d == np.abs(lo - a)) | (d == np.abs(hi - a))
+    assert np.all((mag[ties] & 1) == 0)
+    # float32-representable values: bf16 is the RNE of the float32, which torch computes
+    import torch
+    f = rng.standard_normal(5000).astype(np.float32)
+    ref = torch.from_numpy(f).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(oracle_lib.double_to_half(f.astype(np.float64), "bf16"), ref)
+
+
+# ------------------------------------------------------------------- codec
+def test_codec_golden_bytes(oracle_lib):
+    g = json.load(open(os.path.join(GOLD, "codec_bytes.json")))
+    for case in g["cases"]:
+        fmt = case["fmt"]
+        bits = oracle_lib.BITS[fmt]
+        K = 8 // bits
+        codes, nbad = oracle_lib.unpack_codes(fmt, np.array([case["byte"]], np.uint8), 1, K)
+        assert nbad == 0
+        assert codes[0].tolist() == case["codes"], case
+        if "values" in case:
+            sd = "f16"
+            s = oracle_lib.double_to_half(np.array([case["scale"]]), sd)
+            b = oracle_lib.double_to_half(np.array([case["bias"]]), sd)
+            # one block covering the byte (block >= K); pad to a block of 64
+            nfield = 64
+            row = np.full(nfield * bits // 8, case["byte"], dtype=np.uint8)
+            W = oracle_lib.dequant(fmt, 64, sd, row, s, b, 1, nfield)
+            assert W[0, :K].tolist() == case["values"]
+
+
+@pytest.mark.parametrize("fmt", list(synth.FORMATS))
+def test_codec_all_bytes_vs_unpackbits(oracle_lib, fmt):
+    bits = oracle_lib.BITS[fmt]
+    packed = np.arange(256, dtype=np.uint8).reshape(256, 1)
+    K = 8 // bits
+    codes, nbad = oracle_lib.unpack_codes(fmt, packed, 256, K)
+    u = bf.fields(packed, bits, K)
+    if fmt == "ternary":
+        assert nbad == int((u == 3).sum())
+        ok = u != 3
+        assert np.array_equal(codes[ok], (u - 1)[ok])
+    else:
+        assert nbad == 0
+        assert np.array_equal(codes, u - bf.OFFSET[fmt])
+
+
+def _rand_mat(fmt, N, K, block, sdtype, seed):
+    spec = custom_linear_spec(K, fmt=fmt, block=block, scale_dtype=sdtype, act_dtype="bf16",
+                              name=f"pin_{fmt}_{seed}")
+    return synth.linear_inputs(spec, N, 1, seed=seed)
+
+
+@pytest.mark.parametrize("sdtype", ["bf16", "f16"])
+def test_dequant_cross_format_identities(oracle_lib, sdtype):
+    """Symmetric b-bit == affine b-bit with bias -2^(b-1)*s; ternary == affine
+    2-bit with bias -s (MLX issue 3852: ternary stored as affine has
+    bias == -scale)."""
+    N, K, B = 64, 256, 64
+    for sym, aff, off in (("sym_int4", "affine_int4", 8), ("sym_int2", "affine_int2", 2),
+                          ("ternary", "affine_int2", 1)):
+        inp = _rand_mat(sym, N, K, B, sdtype, seed=3)
+        s = oracle_lib.half_to_double(inp["scales"], sdtype)
+        b = oracle_lib.double_to_half(-off * s, sdtype)          # exact: power-of-two multiple
+        assert np.array_equal(oracle_lib.half_to_double(b, sdtype), -off * s)
+        Ws = oracle_lib.dequant(sym, B, sdtype, inp["codes"], inp["scales"], None, N, K)
+        Wa = oracle_lib.dequant(aff, B, sdtype, inp["codes"], inp["scales"], b, N, K)
+        assert np.array_equal(Ws, Wa), sym
+
+
+@pytest.mark.parametrize("fmt", list(synth.FORMATS))
+def test_unit_scale_integer_matmul_is_exact(oracle_lib, fmt):
+    """All-one scales and integer activations reproduce an int64 matmul exactly."""
+    N, K, B, M = 64, 512, 64, 3
+    inp = _rand_mat(fmt, N, K, B, "bf16", seed=5)
+    inp["scales"][:] = 0x3F80                                    # bf16 1.0
+    if inp["biases"] is not None:
+        inp["biases"][:] = 0xC000                                # bf16 -2.0
+    xi = np.random.default_rng(7).integers(-8, 9, size=(M, K))
+    inp["x"] = oracle_lib.double_to_half(xi.astype(np.float64), "bf16").reshape(M, K)
+    inp["M"] = M
+    out = oracle_lib.linear(inp)
+    q = bf.fields(inp["codes"], oracle_lib.BITS[fmt], K) - bf.OFFSET[fmt]
+    if inp["biases"] is not None:
+        q = q - 2
+    ref = xi.astype(np.int64) @ q.T.astype(np.int64)
+    assert np.array_equal(out["y64"], ref.astype(np.float64))
+
+
+def test_moe_fc1_integer_exact(oracle_lib):
+    spec = custom_moe_spec(E=2, H=128, I=64, top_k=1, fc1="sym_int4", name="pin_fc1_int")
+    inp = synth.moe_inputs(spec, T=3, seed=1)
+    inp["fc1_scales"][:] = 0x3F80
+    xi = np.random.default_rng(3).integers(-8, 9, size=(3, 128))
+    inp["x"] = oracle_lib.double_to_half(xi.astype(np.float64), "bf16").reshape(3, 128)
+    out = oracle_lib.moe(inp, debug=True)
+    r = oracle_lib.route(inp["logits"], 1)
+    for t in range(3):
+        e = r["ids"][t, 0]
+        q = bf.fields(inp["fc1_codes"][e], 4, 128) - 8
+        assert np.array_equal(out["a"][t], (q.astype(np.int64) @ xi[t]).astype(np.float64))
+
+
+# ----------------------------------------------------------------- SwiGLU
+def test_silu_pins(oracle_lib):
+    assert oracle_lib.silu(0.0) == 0.0
+    for g in np.linspace(-30, 30, 601):
+        s1, s2 = oracle_lib.silu(g), oracle_lib.silu(-g)
+        assert abs((s1 - s2) - g) <= 4 * np.spacing(max(abs(g), 1e-300)) + 1e-300
+        ref = g * scipy.special.expit(g)
+        assert abs(s1 - ref) <= 4 * np.spacing(abs(ref)) + 1e-300
+
+
+def test_swiglu_zero_up_gives_zero(oracle_lib):
+    spec = custom_moe_spec(E=1, H=64, I=64, top_k=1, name="pin_up0")
+    inp = synth.moe_inputs(spec, T=2, seed=2)
+    c = inp["fc1_codes"].copy()
+    c[:, 1::2, :] = 0x88                                          # int4 code 0 in every up row
+    inp["fc1_codes"] = c
+    out = oracle_lib.moe(inp, debug=True)
+    assert np.all(out["h"] == 0.0) and np.all(out["y64"] == 0.0)
+
+
+# ---------------------------------------------------------------- routing
+def _check_route(oracle_lib, logits, k):
+    r = oracle_lib.route(logits, k)
+    T, E = logits.shape
+    for t in range(T):
+        order = np.lexsort((np.arange(E), -logits[t].astype(np.float64)))
+        assert r["ids"][t].tolist() == order[:k].tolist()
+        sel = logits[t, order[:k]].astype(np.float64)
+        assert np.allclose(r["w"][t], scipy.special.softmax(sel), rtol=1e-13, atol=0)
+        assert abs(r["w"][t].sum() - 1.0) <= k * 2.0 ** -52
+        if k == 1:
+            assert r["w"][t, 0] == 1.0
+    flat = r["ids"].ravel()
+    assert np.array_equal(r["counts"], np.bincount(flat, minlength=E))
+    assert np.array_equal(r["offsets"], np.concatenate([[0], np.cumsum(np.bincount(flat, minlength=E))]))
+    assert np.array_equal(r["row_list"], np.argsort(flat, kind="stable"))
+
+
+@pytest.mark.parametrize("E,k", [(1, 1), (4, 2), (64, 6), (128, 8), (256, 8), (64, 1)])
+def test_route_random(oracle_lib, E, k):
+    lg = np.random.default_rng(E * 10 + k).standard_normal((33, E)).astype(np.float32)
+    _check_route(oracle_lib, lg, k)
+
+
+@pytest.mark.parametrize("E,k", [(8, 4), (64, 6), (256, 8)])
+def test_route_ties(oracle_lib, E, k):
+    rng = np.random.default_rng(11)
+    lg = np.round(rng.standard_normal((40, E)) * 2).astype(np.float32) / 2   # many ties
+    lg[0] = 0.0                                                              # all equal
+    lg[1] = -1.0
+    _check_route(oracle_lib, lg, k)
+    r = oracle_lib.route(lg, k)
+    assert r["ids"][0].tolist() == list(range(k))
+
+
+# --------------------------------------------------- whole layer vs brute force
+TINY = [
+    dict(E=1, H=64, I=64, top_k=1, fc1="sym_int4"),
+    dict(E=4, H=128, I=64, top_k=2, fc1="sym_int4"),
+    dict(E=4, H=64, I=128, top_k=4, fc1="sym_int2", fc2="sym_int4"),
+    dict(E=3, H=128, I=128, top_k=1, fc1="ternary", block1=128, scale_dtype="f16"),
+    dict(E=4, H=128, I=64, top_k=2, fc1="affine_int2", fc2="affine_int4", block1=64, block2=64,
+         scale_dtype="f16", act_dtype="f16"),
+]
+
+
+@pytest.mark.parametrize("cfg", TINY, ids=lambda c: "-".join(str(v) for v in c.values()))
+@pytest.mark.parametrize("T", [1, 2, 5])
+def test_moe_vs_dense_bruteforce(oracle_lib, cfg, T):
+    spec = custom_moe_spec(**cfg)
+    inp = synth.moe_inputs(spec, T=T, seed=T)
+    out = oracle_lib.moe(inp)
+    ref = bf.moe_dense(inp)
+    assert out["status"] == 0
+    assert np.allclose(out["y64"], ref, rtol=1e-10, atol=1e-12 * np.abs(ref).max())
+    if spec.act_dtype == "f16":
+        assert np.array_equal(out["y"], out["y64"].astype(np.float16).view(np.uint16))
+
+
+def test_moe_expert_permutation_invariance(oracle_lib):
+    spec = custom_moe_spec(E=6, H=64, I=64, top_k=3)
+    inp = synth.moe_inputs(spec, T=4, seed=9)
+    base = oracle_lib.moe(inp)["y64"]
+    perm = np.random.default_rng(0).permutation(6)
+    p = dict(inp)
+    for n in ("fc1_codes", "fc1_scales", "fc2_codes", "fc2_scales"):
+        p[n] = inp[n][perm]
+    p["logits"] = np.ascontiguousarray(inp["logits"][:, perm])
+    assert np.array_equal(oracle_lib.moe(p)["y64"], base)
+    tp = np.random.default_rng(1).permutation(4)
+    q = dict(inp)
+    q["x"] = np.ascontiguousarray(inp["x"][tp])
+    q["logits"] = np.ascontiguousarray(inp["logits"][tp])
+    assert np.array_equal(oracle_lib.moe(q)["y64"], base[tp])
+
+
+def test_moe_token_subset_equals_full(oracle_lib):
+    spec = custom_moe_spec(E=4, H=64, I=64, top_k=2)
+    inp = synth.moe_inputs(spec, T=6, seed=4)
+    full = oracle_lib.moe(inp)["y64"]
+    sub = oracle_lib.moe(inp, tokens=[5, 1, 3])["y64"]
+    assert np.array_equal(sub, full[[5, 1, 3]])
+
+
+def test_ternary_invalid_field_reported(oracle_lib):
+    spec = custom_moe_spec(E=1, H=128, I=128, top_k=1, fc1="ternary", block1=128, scale_dtype="f16")
+    inp = synth.moe_inputs(spec, T=1, seed=0)
+    assert oracle_lib.moe(inp)["status"] == 0
+    inp["fc1_codes"] = inp["fc1_codes"].copy()
+    inp["fc1_codes"][0, 5, 3] |= 0xC0
+    assert oracle_lib.moe(inp)["status"] == -1
+
+
+@pytest.mark.parametrize("fmt,block,sd,ad", [("affine_int2", 128, "f16", "f16"), ("sym_int4", 64, "bf16", "bf16"),
+                                             ("ternary", 128, "f16", "bf16")])
+def test_linear_vs_dense_bruteforce(oracle_lib, fmt, block, sd, ad):
+    spec = custom_linear_spec(512, fmt=fmt, block=block, scale_dtype=sd, act_dtype=ad)
+    inp = synth.linear_inputs(spec, 128, 5, seed=1)
+    out = oracle_lib.linear(inp)
+    ref = bf.linear_dense(inp)
+    assert np.allclose(out["y64"], ref, rtol=1e-11, atol=1e-13 * np.abs(ref).max())
+    sub = oracle_lib.linear(inp, 64, 96)
+    assert np.array_equal(sub["y64"], out["y64"][:, 64:96])
+
+
+# --------------------------------------------------------- page arithmetic
+def test_page_byte_and_mac_counts():
+    g = {c["what"]: c for c in json.load(open(os.path.join(GOLD, "page_arithmetic.json")))["cases"]}
+    sp = synth.LINEAR_WORKLOADS["dense_affine2"]
+    for N in sp.Ns:
+        nbytes = synth.canonical_matrix_bytes(sp.fmt, N, sp.K)
+        assert nbytes * 8 / (N * sp.K) == g["effective bits per weight of 2-bit affine, group 128, 16-bit scale and bias"]["value"]
+    assert synth.canonical_matrix_bytes(sp.fmt, 17408, 5120) == 25067520
+    mac = g["FMA per row of the 5120 -> 17408 matmul"]
+    assert 5120 * 17408 == mac["exact"] and abs(mac["exact"] - mac["value_approx"]) / mac["value_approx"] < 0.01
