@@ -1,0 +1,226 @@
+/*
+ * qmoe.h -- C ABI of the MI355X (gfx950) low-bit quantized MoE expert FFN.
+ *
+ * One MoE layer computes, for T tokens x[t] (hidden size H):
+ *
+ *   route    ids[t][0..k-1] = the k experts with the largest router logits
+ *            (ties to the lower expert index, ordered by descending logit);
+ *            w[t][j] = softmax of those k logits, so sum_j w[t][j] = 1.
+ *   expand   tokens grouped by expert: per-expert row counts, exclusive
+ *            offsets and a stable row list of flat slots r = t*k + j.
+ *   FC1      a = W1[e] x[t], W1[e] is [2I][H] with gate/up rows interleaved:
+ *            row 2i is gate_i, row 2i+1 is up_i.
+ *   SwiGLU   h_i = silu(a[2i]) * a[2i+1],  silu(g) = g / (1 + exp(-g)).
+ *   FC2      o = W2[e] h, W2[e] is [H][I].
+ *   combine  y[t] = sum_j w[t][j] * o_(t,j), summed in fp32, rounded once
+ *            (nearest-even) to the activation dtype.
+ *
+ * Weights are block-quantized: every B consecutive weights of a row share a
+ * 16-bit scale s (and, for affine formats, a bias b); w = s*q or w = s*q + b.
+ *
+ * Where each part comes from on the pages:
+ *   - onnxruntime pull request 33005 ("[CUDA] Enable SM80+ FP16/BF16 mixed
+ *     INT2/INT4 QMoE prefill by default"), Description: the stage order
+ *     (routing and expert map, rows expanded by expert, FC1, SwiGLU, FC2,
+ *     top-k weighted finalize), an aligned per-call workspace ordered on the
+ *     stream, prepacked weights with transposed scales; Current Scope:
+ *     FP16/BF16 activations, symmetric codes without zero points, block 64,
+ *     interleaved fused SwiGLU, dimensions divisible by 64, at most 256
+ *     experts, bounded int-sized routed-row counts, and an error instead of
+ *     a larger allocation when scratch does not fit.
+ *   - MLX issue 3852 ("2-bit quantized_matmul loses its size advantage over
+ *     4-bit at M >= 3"), repro and closing remarks: the dense call
+ *     quantized_matmul(x, wq, scales, biases, transpose=True, group_size,
+ *     bits) with W as [N][K], affine groups of 128, ternary as affine.
+ *   - onnx-genai pull request 1167 ("QMoE gate/up SwiGLU expert-GEMV
+ *     occupancy lever"): the fused gate/up SwiGLU expert GEMV and the
+ *     separate down-projection GEMV.
+ *
+ * Canonical input format (what qmoe_prepack / qmoe_linear_prepack read):
+ *   codes   [E][N][K*bits/8] bytes; within a byte, fields run LSB-first along
+ *           K.  Field u maps to the code q by the qtype:
+ *             SYM_INT4     q = u - 8        in [-8, 7]     w = s*q
+ *             SYM_INT2     q = u - 2        in [-2, 1]     w = s*q
+ *             TERNARY      q = u - 1        in {-1, 0, 1}  w = s*q (u = 3 invalid)
+ *             AFFINE_INT2  q = u            in [0, 3]      w = s*q + b
+ *             AFFINE_INT4  q = u            in [0, 15]     w = s*q + b
+ *   scales  [E][N][K/B] 16-bit patterns of scale_dtype; biases likewise
+ *           (affine formats only).
+ *
+ * Conventions:
+ *   - Every pointer argument to a compute call is a DEVICE pointer on the
+ *     current HIP device unless stated otherwise; descriptors and size
+ *     outputs are host pointers.  `stream` is a hipStream_t (NULL = the
+ *     default stream).
+ *   - The caller allocates and owns every buffer.  The library never
+ *     allocates, frees or synchronizes inside qmoe_forward, qmoe_route and
+ *     qmoe_linear; it holds no per-call state between calls.
+ *   - Validation runs before any launch: a non-OK status means nothing was
+ *     enqueued.  Launch failures return QMOE_ERR_DEVICE.  qmoe_last_error()
+ *     gives a thread-local message for the last non-OK status.
+ *   - Alignment: packed buffers and workspaces 256 B; x, y, logits 16 B.
+ */
+#ifndef QMOE_H_
+#define QMOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QMOE_ABI_VERSION 1
+
+typedef enum qmoe_status {
+  QMOE_OK = 0,
+  QMOE_ERR_INVALID_ARGUMENT = 1, /* null/misaligned pointer, inconsistent shape, bad code */
+  QMOE_ERR_UNSUPPORTED = 2,      /* valid request outside what is built (see each call) */
+  QMOE_ERR_WORKSPACE_TOO_SMALL = 3,
+  QMOE_ERR_DEVICE = 4            /* a HIP call or launch failed */
+} qmoe_status;
+
+typedef enum qmoe_dtype {
+  QMOE_DTYPE_BF16 = 0,
+  QMOE_DTYPE_F16 = 1,
+  QMOE_DTYPE_F32 = 2 /* reserved: not accepted as activation or scale dtype */
+} qmoe_dtype;
+
+typedef enum qmoe_qtype {
+  QMOE_QTYPE_SYM_INT4 = 0,
+  QMOE_QTYPE_SYM_INT2 = 1,
+  QMOE_QTYPE_TERNARY = 2,
+  QMOE_QTYPE_AFFINE_INT2 = 3,
+  QMOE_QTYPE_AFFINE_INT4 = 4
+} qmoe_qtype;
+
+typedef enum qmoe_path {
+  QMOE_PATH_AUTO = 0,    /* GEMV kernels when every expert row count can be <= 16, else grouped */
+  QMOE_PATH_GEMV = 1,    /* register-accumulator GEMV kernels (needs T <= 16) */
+  QMOE_PATH_GROUPED = 2  /* grouped MFMA kernels over expert row tiles */
+} qmoe_path;
+
+/* One quantized matrix W [rows][cols] = [N][K]. */
+typedef struct qmoe_qmatrix_desc {
+  int32_t qtype;       /* qmoe_qtype */
+  int32_t block;       /* weights per scale along K: 64 or 128 */
+  int32_t scale_dtype; /* QMOE_DTYPE_BF16 or QMOE_DTYPE_F16 */
+  int32_t reserved;    /* must be 0 */
+  int64_t rows;        /* N, a positive multiple of 64 */
+  int64_t cols;        /* K, a positive multiple of 64 and of block */
+} qmoe_qmatrix_desc;
+
+/* One MoE layer.  fc1 must be [2*inter][hidden], fc2 [hidden][inter]. */
+typedef struct qmoe_layer_desc {
+  int32_t num_experts; /* E in [1, 256] */
+  int32_t hidden;      /* H */
+  int32_t inter;       /* I */
+  int32_t act_dtype;   /* QMOE_DTYPE_BF16 or QMOE_DTYPE_F16: x and y */
+  qmoe_qmatrix_desc fc1;
+  qmoe_qmatrix_desc fc2;
+} qmoe_layer_desc;
+
+/* Optional controls and diagnostics of qmoe_forward_ex.  Zero-initialise. */
+typedef struct qmoe_forward_opts {
+  int32_t path;      /* qmoe_path */
+  int32_t reserved;  /* must be 0 */
+  float *h_out;      /* optional device [T*k][I] fp32: SwiGLU output per slot, slot order t*k+j */
+  int32_t *ids_out;  /* optional device [T][k]: routed expert ids */
+  float *w_out;      /* optional device [T][k]: routing weights */
+  int32_t *counts_out; /* optional device [E]: rows routed to each expert */
+} qmoe_forward_opts;
+
+/* Host-side description of what a forward call would launch (diagnostic). */
+typedef struct qmoe_plan {
+  int32_t path;          /* the path actually taken */
+  int32_t num_launches;  /* kernels enqueued per call */
+  int32_t gemv_mmax;     /* GEMV path: register accumulators per lane (rows per expert) */
+  int32_t gemv_fc1_waves;  /* GEMV path: waves per workgroup (K split) of FC1 */
+  int32_t gemv_fc2_waves;
+  int32_t max_active;    /* upper bound of active experts the grids are sized for */
+  int64_t workspace_bytes;
+  char kernels[256];     /* kernel names in launch order, comma separated */
+} qmoe_plan;
+
+/* ABI version (QMOE_ABI_VERSION) and a thread-local message for the last non-OK status. */
+int32_t qmoe_abi_version(void);
+const char *qmoe_last_error(void);
+
+/* ------------------------------------------------------------------ MoE --- */
+
+/* Bytes of the opaque prepacked buffer for `desc` (host call, no device work).
+ * Errors: INVALID_ARGUMENT (null, inconsistent shapes), UNSUPPORTED (qtype,
+ * block not in {64,128}, E > 256, dims not multiples of 64, f32 dtypes). */
+qmoe_status qmoe_prepacked_size(const qmoe_layer_desc *desc, size_t *bytes);
+
+/* Rearranges canonical codes and scales (device pointers, layout above) into
+ * the prepacked gfx950 layout in `dst` (device, >= qmoe_prepacked_size bytes,
+ * 256-B aligned).  Biases are required for affine formats and must be NULL
+ * otherwise.  Offline call: it synchronizes `stream` to read back a device
+ * error word and returns INVALID_ARGUMENT if a ternary field holds 3.  The
+ * sources may be freed afterwards; `dst` is the only persistent artefact. */
+qmoe_status qmoe_prepack(const qmoe_layer_desc *desc,
+                         const void *fc1_codes, const void *fc1_scales, const void *fc1_biases,
+                         const void *fc2_codes, const void *fc2_scales, const void *fc2_biases,
+                         void *dst, size_t dst_bytes, void *stream);
+
+/* Worst-case workspace bytes of one forward call with T tokens and top_k
+ * (host call).  top_k in [1, min(E, 16)], T >= 0, T*top_k <= INT32_MAX. */
+qmoe_status qmoe_workspace_size(const qmoe_layer_desc *desc, int32_t T, int32_t top_k,
+                                size_t *bytes);
+
+/* One MoE layer.  x [T][H] and y [T][H] row-major in act_dtype; logits
+ * [T][E] fp32 (finite); packed from qmoe_prepack; ws of at least
+ * qmoe_workspace_size bytes.  Asynchronous on `stream`; never allocates,
+ * frees or synchronizes.  T = 0 returns OK without launching. */
+qmoe_status qmoe_forward(const qmoe_layer_desc *desc, const void *packed, const void *x,
+                         const float *logits, int32_t T, int32_t top_k, void *y,
+                         void *ws, size_t ws_bytes, void *stream);
+
+/* qmoe_forward with explicit path choice and optional diagnostic outputs
+ * (opts may be NULL).  UNSUPPORTED if path = GEMV and T > 16. */
+qmoe_status qmoe_forward_ex(const qmoe_layer_desc *desc, const void *packed, const void *x,
+                            const float *logits, int32_t T, int32_t top_k, void *y,
+                            void *ws, size_t ws_bytes, void *stream,
+                            const qmoe_forward_opts *opts);
+
+/* Host-only: the launch plan a qmoe_forward_ex call with these arguments would follow. */
+qmoe_status qmoe_forward_plan(const qmoe_layer_desc *desc, int32_t T, int32_t top_k,
+                              const qmoe_forward_opts *opts, qmoe_plan *plan);
+
+/* Routing alone, with the same kernels as the forward (bit-exact checks).
+ * logits [T][E] fp32 -> ids [T][k] int32, w [T][k] fp32, counts [E],
+ * offsets [E+1] (exclusive scan), row_list [T*k] (slots t*k+j grouped by
+ * expert, ascending within an expert).  ws >= qmoe_route_workspace_size. */
+qmoe_status qmoe_route_workspace_size(int32_t T, int32_t E, int32_t top_k, size_t *bytes);
+qmoe_status qmoe_route(int32_t T, int32_t E, int32_t top_k, const float *logits,
+                       int32_t *ids, float *w, int32_t *counts, int32_t *offsets,
+                       int32_t *row_list, void *ws, size_t ws_bytes, void *stream);
+
+/* Diagnostic: read the prepacked layout back to integer codes.  which = 1
+ * for FC1 ([E][2I][H]), 2 for FC2 ([E][H][I]); codes_out int8, device. */
+qmoe_status qmoe_unpack_codes(const qmoe_layer_desc *desc, const void *packed, int32_t which,
+                              int8_t *codes_out, void *stream);
+
+/* --------------------------------------------------------------- dense --- */
+
+/* Dense skinny-M quantized matmul y = x W^T (MLX issue 3852, repro):
+ * W [N][K] in the canonical format (E = 1), x [M][K] and y [M][N] in
+ * x_dtype.  Same error rules as the MoE calls. */
+qmoe_status qmoe_linear_prepacked_size(const qmoe_qmatrix_desc *desc, size_t *bytes);
+qmoe_status qmoe_linear_prepack(const qmoe_qmatrix_desc *desc, const void *codes,
+                                const void *scales, const void *biases, void *dst,
+                                size_t dst_bytes, void *stream);
+qmoe_status qmoe_linear_workspace_size(const qmoe_qmatrix_desc *desc, int32_t M, size_t *bytes);
+/* path: QMOE_PATH_AUTO, GEMV (M <= 16) or GROUPED (MFMA tiles, any M >= 1). */
+qmoe_status qmoe_linear(const qmoe_qmatrix_desc *desc, const void *packed, const void *x,
+                        int32_t x_dtype, int32_t M, void *y, void *ws, size_t ws_bytes,
+                        int32_t path, void *stream);
+qmoe_status qmoe_linear_unpack_codes(const qmoe_qmatrix_desc *desc, const void *packed,
+                                     int8_t *codes_out, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QMOE_H_ */

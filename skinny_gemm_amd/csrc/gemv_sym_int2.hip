@@ -1,0 +1,11 @@
+// gemv_sym_int2.hip -- GEMV instantiations for the sym_int2 format (see gemv_impl.hpp).
+#include "gemv_impl.hpp"
+
+namespace qmoe {
+
+hipError_t launch_gemv_sym_int2(const GemvArgs &a, int epilogue, int in_f16, int mmax, int waves,
+                          int grid_slots, hipStream_t s) {
+  return launch_gemv_qt<QMOE_QTYPE_SYM_INT2>(a, epilogue, in_f16, mmax, waves, grid_slots, s);
+}
+
+}  // namespace qmoe

@@ -1,0 +1,173 @@
+// qmoe_internal.h -- layout arithmetic and launch argument blocks shared by
+// the host ABI (abi.hip) and the gfx950 kernels.  Host + device.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/qmoe.h"
+
+namespace qmoe {
+
+constexpr int kLanes = 64;            // wavefront width on CDNA4
+constexpr int kRowsPerGroup = 64;     // one output row per lane in the GEMV layout
+constexpr int kChunkBytes = 16;       // one 128-bit load per lane
+constexpr int kMaxExperts = 256;
+constexpr int kMaxTopK = 16;
+constexpr int kGemvMaxRows = 16;      // register accumulators per lane (rows per expert)
+constexpr int64_t kAlign = 256;
+
+__host__ __device__ inline int64_t align_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
+
+__host__ __device__ inline int qtype_bits(int qt) {
+  return (qt == QMOE_QTYPE_SYM_INT4 || qt == QMOE_QTYPE_AFFINE_INT4) ? 4 : 2;
+}
+__host__ __device__ inline bool qtype_affine(int qt) {
+  return qt == QMOE_QTYPE_AFFINE_INT2 || qt == QMOE_QTYPE_AFFINE_INT4;
+}
+// Zero point folded into the symmetric codes: q = u - zp.
+__host__ __device__ inline int qtype_zero_point(int qt) {
+  switch (qt) {
+    case QMOE_QTYPE_SYM_INT4: return 8;
+    case QMOE_QTYPE_SYM_INT2: return 2;
+    case QMOE_QTYPE_TERNARY: return 1;
+    default: return 0;
+  }
+}
+
+// Prepacked layout of one quantized matrix W [N][K] (one expert).
+//
+// codes : [N/64 row groups][K/kc chunks][64 lanes][16 B]; lane l of row
+//         group g holds row 64g + l.  A wave reading chunk c of a row group
+//         issues one 1 KiB contiguous, 16-B-per-lane load.  Inside a lane's
+//         16 B, dword d covers weights [d*wpd, (d+1)*wpd) of the chunk
+//         (wpd = 32/bits) and weight pair j = (2j, 2j+1) of the dword keeps its
+//         even weight in the low half-word and its odd weight in the high
+//         half-word at the same bit offset (4j for 4-bit, 2j for 2-bit), so
+//         one AND-OR places a pair into the mantissas of two 16-bit floats.
+// scales: [N/64][K/B][64 lanes] x (scale) or x (scale, bias) 16-bit values:
+//         the 64 lanes of a wave read one contiguous 128/256 B piece per block.
+struct MatLayout {
+  int qtype, bits, block, sdtype;
+  bool affine;
+  int64_t N, K;
+  int64_t RG;    // row groups
+  int kc;        // weights per lane chunk (16 B)
+  int64_t NC;    // chunks per row
+  int64_t nblk;  // blocks per row
+  int cpb;       // chunks per block
+  int scale_elem;         // bytes per lane per block (2 or 4)
+  int64_t codes_bytes;
+  int64_t scales_off;     // from the start of the expert's matrix
+  int64_t scales_bytes;
+  int64_t stride;         // bytes per expert
+
+  __host__ __device__ static MatLayout make(const qmoe_qmatrix_desc &d) {
+    MatLayout L{};
+    L.qtype = d.qtype;
+    L.bits = qtype_bits(d.qtype);
+    L.block = d.block;
+    L.sdtype = d.scale_dtype;
+    L.affine = qtype_affine(d.qtype);
+    L.N = d.rows;
+    L.K = d.cols;
+    L.RG = d.rows / kRowsPerGroup;
+    L.kc = kChunkBytes * 8 / L.bits;
+    L.NC = d.cols / L.kc;
+    L.nblk = d.cols / d.block;
+    L.cpb = d.block / L.kc;
+    L.scale_elem = L.affine ? 4 : 2;
+    L.codes_bytes = d.rows * d.cols * L.bits / 8;
+    L.scales_off = align_up(L.codes_bytes, kAlign);
+    L.scales_bytes = d.rows * L.nblk * L.scale_elem;
+    L.stride = L.scales_off + align_up(L.scales_bytes, kAlign);
+    return L;
+  }
+};
+
+// Prepacked MoE buffer: [header 256 B][FC1: E x stride1][FC2: E x stride2].
+constexpr int64_t kHeaderBytes = 256;
+constexpr uint64_t kPackMagic = 0x31304b50454f4d51ull;  // "QMOEPK01"
+constexpr int64_t kErrWordOff = 128;                     // u32 invalid-field counter
+
+struct MoeLayout {
+  MatLayout fc1, fc2;
+  int64_t fc1_off, fc2_off, total;
+  static MoeLayout make(const qmoe_layer_desc &d) {
+    MoeLayout L{};
+    L.fc1 = MatLayout::make(d.fc1);
+    L.fc2 = MatLayout::make(d.fc2);
+    L.fc1_off = kHeaderBytes;
+    L.fc2_off = L.fc1_off + (int64_t)d.num_experts * L.fc1.stride;
+    L.total = L.fc2_off + (int64_t)d.num_experts * L.fc2.stride;
+    return L;
+  }
+};
+
+// ------------------------------------------------------------------ routing
+// Device-side routing results, carved from the workspace.
+struct RouteBufs {
+  int32_t *ids;        // [T*k]
+  float *w;            // [T*k]
+  int32_t *counts;     // [E]
+  int32_t *offsets;    // [E+1]
+  int32_t *row_list;   // [T*k]   slot ids grouped by expert
+  int32_t *slot_pos;   // [T*k]   inverse of row_list
+  int32_t *active;     // [E]     experts with count > 0, ascending
+  int32_t *num_active; // [1]
+};
+
+struct RouteArgs {
+  const float *logits;
+  int T, E, k;
+  RouteBufs r;
+  int topk_in_expand;  // 1: the expand kernel also performs top-k (small T)
+};
+
+// -------------------------------------------------------------------- GEMV
+enum GemvEpilogue { kEpiSwiGLU = 0, kEpiStoreF32 = 1, kEpiStoreAct = 2 };
+
+struct GemvArgs {
+  // weights
+  const uint8_t *w;        // matrix section base (expert 0)
+  int64_t expert_stride;
+  int64_t scales_off;
+  int64_t N, K, RG, NC, nblk;
+  int cpb, kc, qtype, sdtype;
+  // rows: either routed (active/counts/offsets/row_list) or dense (M rows)
+  const int32_t *active, *num_active, *counts, *offsets, *row_list;
+  int top_k;
+  int dense_M;             // >0: dense rows 0..M-1, expert 0, no routing
+  // input activations as 16-bit pairs; parts = 1 (x) or 2 (hi, lo)
+  const uint32_t *in;
+  int64_t in_row_pairs;    // row stride in 32-bit pairs
+  int in_parts;            // 2: rows [p] of part 0 at in, of part 1 at in + part_stride
+  int64_t in_part_stride;  // in pairs
+  int in_gather_token;     // 1: input row = row_list[p] / top_k (FC1); 0: input row = p
+  // outputs
+  float *out_f32;          // kEpiStoreF32: [p][N]
+  uint16_t *out_act;       // kEpiStoreAct: [m][N]
+  uint16_t *h_hi, *h_lo;   // kEpiSwiGLU: [p][N/2] bf16 parts of h
+  float *h_dbg;            // kEpiSwiGLU: optional [slot][N/2] fp32
+  int act_dtype;           // kEpiStoreAct
+};
+
+// Dynamic LDS of one GEMV workgroup: per-row block corrections + the
+// cross-wave partial sums.
+inline size_t gemv_lds_bytes(int mmax, int64_t nblk, int waves) {
+  return ((size_t)mmax * (size_t)nblk * 2 + (size_t)waves * (size_t)mmax * kLanes) * sizeof(float);
+}
+
+// Host launchers (defined in the kernel translation units).
+hipError_t launch_prepack_matrix(const MatLayout &L, int E, const uint8_t *codes,
+                                 const uint16_t *scales, const uint16_t *biases, uint8_t *dst,
+                                 uint32_t *err_word, hipStream_t s);
+hipError_t launch_unpack_matrix(const MatLayout &L, int E, const uint8_t *src, int8_t *codes_out,
+                                hipStream_t s);
+hipError_t launch_route(const RouteArgs &a, hipStream_t s);
+hipError_t launch_gemv(const GemvArgs &a, int epilogue, int in_f16, int mmax, int waves,
+                       int grid_slots, hipStream_t s);
+hipError_t launch_combine(const float *o, const int32_t *slot_pos, const float *w, int T, int k,
+                          int H, int act_dtype, uint16_t *y, hipStream_t s);
+
+}  // namespace qmoe

@@ -1,0 +1,204 @@
+// route.hip -- top-k routing and the per-expert row map.
+//
+// The onnxruntime pull request 33005 (Description) reuses routing and
+// expert-map kernels and expands the rows by expert before FC1; its finalize
+// step combines the top-k weighted outputs.  Here:
+//   top-k   one wavefront per token: lanes hold the logits, k rounds of a
+//           wave-wide arg-max (ties to the lower expert index) select the
+//           experts in descending order; weights = softmax of the selected
+//           logits in fp32 (sum 1, exactly 1.0 for k = 1).
+//   expand  one workgroup: LDS histogram -> counts, exclusive scan ->
+//           offsets, list of active experts, then a stable counting sort of
+//           the flat slots r = t*k + j by expert (rank inside a wavefront from
+//           ballots over the expert id bits, ranks across wavefronts from
+//           per-wavefront counts in LDS), giving row_list and its inverse.
+#include <float.h>
+
+#include "qmoe_internal.h"
+
+namespace qmoe {
+
+constexpr int kExpandThreads = 1024;
+constexpr int kExpandWaves = kExpandThreads / kLanes;
+
+// Wave-wide top-k of one token.  Returns ids/weights in lane 0's registers
+// (uniform across the wave after the reductions).
+__device__ inline void wave_topk(const float *__restrict__ l, int E, int k, int32_t *ids_out,
+                                 float *w_out, int32_t *ids_lds) {
+  const int lane = threadIdx.x & (kLanes - 1);
+  float v[kMaxExperts / kLanes];
+  bool taken[kMaxExperts / kLanes];
+#pragma unroll
+  for (int i = 0; i < kMaxExperts / kLanes; ++i) {
+    const int e = lane + kLanes * i;
+    v[i] = (e < E) ? l[e] : -FLT_MAX;
+    taken[i] = (e >= E);
+  }
+  float sel_v[kMaxTopK];
+  int sel_i[kMaxTopK];
+  for (int j = 0; j < k; ++j) {
+    float bv = -FLT_MAX;
+    int bi = 0x7FFFFFFF;
+#pragma unroll
+    for (int i = 0; i < kMaxExperts / kLanes; ++i) {
+      const int e = lane + kLanes * i;
+      if (!taken[i] && (bi == 0x7FFFFFFF || v[i] > bv || (v[i] == bv && e < bi))) {
+        bv = v[i];
+        bi = e;
+      }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float ov = __shfl_xor(bv, off);
+      const int oi = __shfl_xor(bi, off);
+      if (oi != 0x7FFFFFFF && (bi == 0x7FFFFFFF || ov > bv || (ov == bv && oi < bi))) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kMaxExperts / kLanes; ++i)
+      if (lane + kLanes * i == bi) taken[i] = true;
+    sel_v[j] = bv;
+    sel_i[j] = bi;
+  }
+  if (lane == 0) {
+    const float m = sel_v[0];
+    float ex[kMaxTopK];
+    float sum = 0.f;
+    for (int j = 0; j < k; ++j) {
+      ex[j] = expf(sel_v[j] - m);
+      sum += ex[j];
+    }
+    for (int j = 0; j < k; ++j) {
+      ids_out[j] = sel_i[j];
+      w_out[j] = ex[j] / sum;
+      if (ids_lds) ids_lds[j] = sel_i[j];
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void route_topk_kernel(RouteArgs a) {
+  const int t = blockIdx.x * (blockDim.x / kLanes) + (threadIdx.x / kLanes);
+  if (t >= a.T) return;
+  wave_topk(a.logits + (int64_t)t * a.E, a.E, a.k, a.r.ids + (int64_t)t * a.k,
+            a.r.w + (int64_t)t * a.k, nullptr);
+}
+
+// Single workgroup.  With topk_in_expand (T <= kExpandWaves) the workgroup
+// first routes the tokens itself, one wave per token.
+__global__ __launch_bounds__(kExpandThreads) void route_expand_kernel(RouteArgs a) {
+  __shared__ int s_cnt[kMaxExperts];
+  __shared__ int s_off[kMaxExperts + 1];
+  __shared__ int s_base[kMaxExperts];
+  __shared__ int s_wc[kExpandWaves][kMaxExperts];
+  __shared__ int32_t s_ids[kExpandWaves * kMaxTopK];
+  const int tid = threadIdx.x, lane = tid & (kLanes - 1), wave = tid / kLanes;
+  const int E = a.E;
+  const int S = a.T * a.k;
+  const bool fused = a.topk_in_expand != 0;
+
+  if (fused && wave < a.T) {
+    wave_topk(a.logits + (int64_t)wave * E, E, a.k, a.r.ids + (int64_t)wave * a.k,
+              a.r.w + (int64_t)wave * a.k, s_ids + wave * a.k);
+  }
+  for (int e = tid; e < kMaxExperts; e += kExpandThreads) {
+    s_cnt[e] = 0;
+    s_base[e] = 0;
+  }
+  for (int i = tid; i < kExpandWaves * kMaxExperts; i += kExpandThreads) (&s_wc[0][0])[i] = 0;
+  __syncthreads();
+
+  for (int r = tid; r < S; r += kExpandThreads) {
+    const int e = fused ? s_ids[r] : a.r.ids[r];
+    atomicAdd(&s_cnt[e], 1);
+  }
+  __syncthreads();
+
+  // Exclusive scan of counts and compaction of the active experts (wave 0).
+  if (wave == 0) {
+    constexpr int PER = kMaxExperts / kLanes;
+    int c[PER], f[PER];
+    int cs = 0, fs = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int e = lane * PER + i;
+      c[i] = (e < E) ? s_cnt[e] : 0;
+      f[i] = (c[i] > 0) ? 1 : 0;
+      cs += c[i];
+      fs += f[i];
+    }
+    int ci = cs, fi = fs;  // inclusive scans across lanes
+#pragma unroll
+    for (int off = 1; off < kLanes; off <<= 1) {
+      const int oc = __shfl_up(ci, off), of = __shfl_up(fi, off);
+      if (lane >= off) {
+        ci += oc;
+        fi += of;
+      }
+    }
+    int run = ci - cs, frun = fi - fs;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int e = lane * PER + i;
+      if (e < E) {
+        s_off[e] = run;
+        a.r.offsets[e] = run;
+        a.r.counts[e] = c[i];
+        if (f[i]) a.r.active[frun] = e;
+      }
+      run += c[i];
+      frun += f[i];
+    }
+    if (lane == kLanes - 1) {
+      s_off[E] = ci;
+      a.r.offsets[E] = ci;
+      a.r.num_active[0] = fi;
+    }
+  }
+  __syncthreads();
+
+  // Stable scatter, one tile of kExpandThreads slots at a time.
+  for (int t0 = 0; t0 < S; t0 += kExpandThreads) {
+    const int r = t0 + tid;
+    const bool valid = r < S;
+    const int e = valid ? (fused ? s_ids[r] : a.r.ids[r]) : 0;
+    uint64_t same = __ballot(valid);
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      const uint64_t bb = __ballot(valid && ((e >> b) & 1));
+      same &= ((e >> b) & 1) ? bb : ~bb;
+    }
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (kLanes - lane));
+    const int rank = __popcll(same & below);
+    if (valid && rank == 0) s_wc[wave][e] = __popcll(same);
+    __syncthreads();
+    if (valid) {
+      int pos = s_off[e] + s_base[e] + rank;
+      for (int w2 = 0; w2 < wave; ++w2) pos += s_wc[w2][e];
+      a.r.row_list[pos] = r;
+      a.r.slot_pos[r] = pos;
+    }
+    __syncthreads();
+    for (int x = tid; x < E; x += kExpandThreads) {
+      int sum = 0;
+      for (int w2 = 0; w2 < kExpandWaves; ++w2) {
+        sum += s_wc[w2][x];
+        s_wc[w2][x] = 0;
+      }
+      s_base[x] += sum;
+    }
+    __syncthreads();
+  }
+}
+
+hipError_t launch_route(const RouteArgs &a, hipStream_t s) {
+  if (!a.topk_in_expand && a.T > 0) {
+    const int per = 256 / kLanes;
+    hipLaunchKernelGGL(route_topk_kernel, dim3((a.T + per - 1) / per), dim3(256), 0, s, a);
+  }
+  hipLaunchKernelGGL(route_expand_kernel, dim3(1), dim3(kExpandThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace qmoe

@@ -1,0 +1,152 @@
+"""Host-only checks of the C ABI (no GPU): the library loads, exports every
+symbol the header declares, and rejects invalid calls before any launch."""
+
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import skinny_gemm_amd as q
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qmoe.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(q.LIB_PATH), reason="libqmoe.so not built")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qmoe_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    L = q.lib()
+    names = header_functions()
+    assert len(names) >= 15
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(q.exported_symbols())
+
+
+def test_abi_version():
+    assert q.abi_version() == 1
+
+
+def _desc(**kw):
+    d = dict(E=64, H=2048, I=1408, act="bf16", fc1=("sym_int4", 64, "bf16"), fc2=("sym_int4", 64, "bf16"))
+    d.update(kw)
+    return q.layer_desc(d["E"], d["H"], d["I"], d["act"], d["fc1"], d["fc2"])
+
+
+def test_prepacked_size_matches_layout():
+    d = _desc()
+    n = q.prepacked_size(d)
+    # header + per expert: codes + scales, each rounded to 256 bytes
+    fc1 = 2816 * 2048 // 2 + 2816 * 32 * 2
+    fc2 = 2048 * 1408 // 2 + 2048 * 22 * 2
+    r = lambda v: (v + 255) // 256 * 256
+    assert n == 256 + 64 * (r(2816 * 1024) + r(2816 * 32 * 2)) + 64 * (r(2048 * 704) + r(2048 * 22 * 2))
+    assert n >= 64 * (fc1 + fc2)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(E=0), 1), (dict(E=257), 2), (dict(act="f32"), 2),
+    (dict(fc1=("sym_int4", 32, "bf16")), 2), (dict(fc1=("sym_int4", 96, "bf16")), 2),
+    (dict(H=2000), 2), (dict(I=1400), 2),
+    (dict(fc1=("sym_int4", 64, "f32")), 2),
+])
+def test_invalid_layer_rejected(kw, status):
+    d = _desc(**kw)
+    with pytest.raises(q.QmoeError) as ei:
+        q.prepacked_size(d)
+    assert ei.value.status == status, q.last_error()
+
+
+def test_shape_mismatch_rejected():
+    d = _desc()
+    d.fc1.rows = 2048
+    with pytest.raises(q.QmoeError) as ei:
+        q.prepacked_size(d)
+    assert ei.value.status == 1
+    d = _desc()
+    d.fc2.reserved = 1
+    with pytest.raises(q.QmoeError):
+        q.prepacked_size(d)
+
+
+@pytest.mark.parametrize("T,k,status", [(-1, 1, 1), (1, 0, 1), (1, 65, 1), (4, 17, 2)])
+def test_invalid_tokens_rejected(T, k, status):
+    with pytest.raises(q.QmoeError) as ei:
+        q.workspace_size(_desc(), T, k)
+    assert ei.value.status == status
+
+
+def test_forward_validation_before_launch():
+    d = _desc()
+    L = q.lib()
+    fake = C.c_void_p(0x100000)  # never dereferenced: every case fails validation first
+    ws_need = q.workspace_size(d, 4, 6)
+    # null pointers
+    st = L.qmoe_forward(C.byref(d), None, fake, fake, 4, 6, fake, fake, ws_need, None)
+    assert st == 1
+    # misaligned workspace
+    st = L.qmoe_forward(C.byref(d), fake, fake, fake, 4, 6, fake, C.c_void_p(0x100010), ws_need, None)
+    assert st == 1
+    # workspace too small
+    st = L.qmoe_forward(C.byref(d), fake, fake, fake, 4, 6, fake, fake, ws_need - 1, None)
+    assert st == 3
+    # GEMV path forced beyond 16 rows
+    opts = q.ForwardOpts(q.PATH["gemv"], 0, None, None, None, None)
+    st = L.qmoe_forward_ex(C.byref(d), fake, fake, fake, 17, 6, fake, fake, 1 << 40, None, C.byref(opts))
+    assert st == 2
+    # T = 0 is a no-op even with null pointers
+    assert L.qmoe_forward(C.byref(d), None, None, None, 0, 6, None, None, 0, None) == 0
+
+
+def test_prepack_validation():
+    d = _desc(fc1=("affine_int2", 128, "f16"))
+    L = q.lib()
+    fake = C.c_void_p(0x100000)
+    n = q.prepacked_size(d)
+    # affine fc1 without biases
+    assert L.qmoe_prepack(C.byref(d), fake, fake, None, fake, fake, None, fake, n, None) == 1
+    # symmetric fc2 with biases
+    assert L.qmoe_prepack(C.byref(d), fake, fake, fake, fake, fake, fake, fake, n, None) == 1
+    # destination too small
+    assert L.qmoe_prepack(C.byref(d), fake, fake, fake, fake, fake, None, fake, n - 1, None) == 3
+
+
+def test_plan_gemv_decode():
+    p = q.forward_plan(_desc(), 1, 6)
+    assert p["path"] == 1 and p["gemv_mmax"] == 1 and p["max_active"] == 6
+    assert p["kernels"] == ["route_expand", "gemv_fc1_swiglu", "gemv_fc2", "combine"]
+    assert p["num_launches"] == 4
+    p8 = q.forward_plan(_desc(), 8, 6)
+    assert p8["gemv_mmax"] == 8 and p8["max_active"] == 48
+    p3 = q.forward_plan(_desc(), 3, 6)
+    assert p3["gemv_mmax"] == 4
+    p0 = q.forward_plan(_desc(), 0, 6)
+    assert p0["num_launches"] == 0 and p0["kernels"] == []
+
+
+def test_route_validation():
+    L = q.lib()
+    n = C.c_size_t()
+    assert L.qmoe_route_workspace_size(8, 300, 2, C.byref(n)) == 2
+    assert L.qmoe_route_workspace_size(8, 64, 65, C.byref(n)) == 1
+    assert L.qmoe_route_workspace_size(8, 64, 6, C.byref(n)) == 0 and n.value > 0
+
+
+def test_linear_validation():
+    d = q.qmatrix_desc("affine_int2", 128, "f16", 17408, 5120)
+    assert q.linear_prepacked_size(d) > 25067520
+    L = q.lib()
+    fake = C.c_void_p(0x100000)
+    assert L.qmoe_linear(C.byref(d), fake, fake, 2, 4, fake, None, 0, 0, None) == 2   # f32 x
+    assert L.qmoe_linear(C.byref(d), fake, fake, 1, 0, fake, None, 0, 0, None) == 0   # M = 0 no-op
+    assert L.qmoe_linear(C.byref(d), None, fake, 1, 4, fake, None, 0, 0, None) == 1
+    bad = q.qmatrix_desc("affine_int2", 128, "f16", 17400, 5120)
+    with pytest.raises(q.QmoeError):
+        q.linear_prepacked_size(bad)

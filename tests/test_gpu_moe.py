@@ -1,0 +1,220 @@
+"""GPU parity of the MoE path (HIP kernels through the C ABI) against the oracle.
+
+Bit-exact: unpacked codes, routing ids, per-expert counts, offsets, row lists.
+Within the stated tolerance (see tests/metrics.py): the layer output.
+"""
+
+import functools
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from synth.workloads import custom_moe_spec
+from tests.metrics import compare
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def log(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import skinny_gemm_amd as q
+    q.lib()  # raises if the HIP library is missing: no fallback
+    yield
+
+
+@functools.lru_cache(maxsize=2)
+def _weights(name, seed):
+    spec = synth.MOE_WORKLOADS[name]
+    return synth.moe_inputs(spec, 1, seed)
+
+
+def _inputs(spec, T, seed, logits_mode="iid"):
+    if spec.name in synth.MOE_WORKLOADS:
+        w = _weights(spec.name, seed)
+        inp = synth.moe_inputs(spec, T, seed, logits_mode, weights=False)
+        for k in w:
+            if k.startswith("fc"):
+                inp[k] = w[k]
+        return inp
+    return synth.moe_inputs(spec, T, seed, logits_mode)
+
+
+def run_case(spec, T, seed, logits_mode="iid", path="auto", tokens=None):
+    from skinny_gemm_amd.layer import MoeLayer, to_device_bits, bits_of
+    log(f"[moe] {spec.name} T={T} seed={seed} logits={logits_mode} path={path}")
+    inp = _inputs(spec, T, seed, logits_mode)
+    layer = MoeLayer.from_spec(spec, inp)
+    x = to_device_bits(inp["x"], spec.act_dtype)
+    lg = torch.from_numpy(inp["logits"]).cuda()
+    y, dbg = layer.forward(x, lg, spec.top_k, path=path, debug=True)
+    torch.cuda.synchronize()
+    ref = oracle.moe(inp, debug=True, tokens=tokens)
+    r = oracle.route(inp["logits"] if tokens is None else inp["logits"][tokens], spec.top_k)
+    ybits = bits_of(y)
+    if tokens is not None:
+        ybits = ybits[tokens]
+    ids = dbg["ids"].cpu().numpy()
+    w = dbg["w"].cpu().numpy()
+    h = dbg["h"].cpu().numpy()
+    if tokens is not None:
+        ids, w = ids[tokens], w[tokens]
+        h = h.reshape(T, spec.top_k, spec.I)[tokens].reshape(-1, spec.I)
+    assert np.array_equal(ids, r["ids"]), "routing ids differ"
+    if tokens is None:
+        assert np.array_equal(dbg["counts"].cpu().numpy(), r["counts"]), "counts differ"
+    assert np.allclose(w, r["w"], rtol=2e-6, atol=1e-7), "routing weights"
+    hn = np.linalg.norm(h - ref["h"], axis=1) / np.maximum(np.linalg.norm(ref["h"], axis=1), 1e-30)
+    res = compare(ybits, ref["y"], ref["y64"], spec.act_dtype)
+    log(f"       y: max_row_rel={res['max_row_rel']:.3e} identical={res['frac_identical']:.4f} "
+        f"vs_exact={res['max_row_rel_vs_exact']:.3e} h_rel={hn.max():.3e}")
+    assert hn.max() < 1e-3, f"h row error {hn.max()}"
+    assert res["ok"], res
+    return res
+
+
+# ------------------------------------------------------------ full workloads
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_single_expert_int4(seed):
+    run_case(synth.MOE_WORKLOADS["single_expert_int4"], 1, seed)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_switch_base_ternary(seed):
+    run_case(synth.MOE_WORKLOADS["switch_base_ternary"], 1, seed)
+
+
+@pytest.mark.parametrize("T", [1, 2, 4, 8])
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_dsv2lite_int4(T, seed):
+    run_case(synth.MOE_WORKLOADS["dsv2lite_int4"], T, seed)
+
+
+@pytest.mark.parametrize("T", [3, 16])
+def test_dsv2lite_int4_shared_logits(T):
+    """Every selected expert receives all T rows (M_e = T)."""
+    run_case(synth.MOE_WORKLOADS["dsv2lite_int4"], T, 0, logits_mode="shared")
+
+
+# -------------------------------------------------------------- small sweeps
+SWEEP = [
+    dict(E=1, H=64, I=64, top_k=1, fc1="sym_int4"),
+    dict(E=4, H=128, I=128, top_k=2, fc1="sym_int2", fc2="sym_int4"),
+    dict(E=4, H=256, I=128, top_k=4, fc1="ternary", block1=128, scale_dtype="f16"),
+    dict(E=4, H=128, I=192, top_k=2, fc1="affine_int2", fc2="affine_int4", scale_dtype="f16", act_dtype="f16"),
+    dict(E=8, H=512, I=256, top_k=3, fc1="affine_int4", block1=128),
+    dict(E=6, H=192, I=64, top_k=6, fc1="sym_int4", act_dtype="f16"),
+    dict(E=5, H=256, I=256, top_k=2, fc1="sym_int2", block1=128, fc2="ternary", block2=128, scale_dtype="f16"),
+]
+
+
+@pytest.mark.parametrize("cfg", SWEEP, ids=lambda c: "-".join(f"{k}{v}" for k, v in c.items()))
+@pytest.mark.parametrize("T", [1, 2, 3, 5, 16])
+def test_sweep(cfg, T):
+    run_case(custom_moe_spec(**cfg), T, seed=T)
+
+
+def test_zero_tokens_is_noop():
+    from skinny_gemm_amd.layer import MoeLayer
+    spec = custom_moe_spec(E=4, H=64, I=64, top_k=2)
+    inp = synth.moe_inputs(spec, 1, 0)
+    layer = MoeLayer.from_spec(spec, inp)
+    y = torch.full((1, 64), 7.0, dtype=torch.bfloat16, device="cuda")
+    x = torch.zeros((0, 64), dtype=torch.bfloat16, device="cuda")
+    lg = torch.zeros((0, 4), dtype=torch.float32, device="cuda")
+    ws = torch.empty(256, dtype=torch.uint8, device="cuda")
+    import skinny_gemm_amd as q
+    q.forward(layer.desc, layer.packed, x, lg, 0, 2, y, ws)
+    torch.cuda.synchronize()
+    assert torch.all(y == 7.0)
+
+
+def test_ternary_invalid_code_rejected_by_prepack():
+    from skinny_gemm_amd.layer import MoeLayer
+    import skinny_gemm_amd as q
+    spec = custom_moe_spec(E=2, H=128, I=128, top_k=1, fc1="ternary", block1=128, scale_dtype="f16")
+    inp = synth.moe_inputs(spec, 1, 0)
+    MoeLayer.from_spec(spec, inp)  # valid codes pass
+    inp["fc2_codes"] = inp["fc2_codes"].copy()
+    inp["fc2_codes"][1, 3, 7] = 0xFF
+    with pytest.raises(q.QmoeError) as ei:
+        MoeLayer.from_spec(spec, inp)
+    assert ei.value.status == 1
+
+
+# ------------------------------------------------------------------- codecs
+def _check_unpack(spec, seed=0, experts=None):
+    from skinny_gemm_amd.layer import MoeLayer
+    inp = _inputs(spec, 1, seed)
+    layer = MoeLayer.from_spec(spec, inp)
+    for which, name, rows, cols, fmt in ((1, "fc1", 2 * spec.I, spec.H, spec.fc1.fmt),
+                                         (2, "fc2", spec.H, spec.I, spec.fc2.fmt)):
+        got = layer.unpack(which).cpu().numpy()
+        for e in (experts if experts is not None else range(spec.E)):
+            ref, nbad = oracle.unpack_codes(fmt, inp[name + "_codes"][e], rows, cols)
+            assert nbad == 0
+            assert np.array_equal(got[e], ref), f"{spec.name} {name} expert {e}"
+    log(f"[unpack] {spec.name} bit-exact")
+
+
+@pytest.mark.parametrize("name", ["single_expert_int4", "switch_base_ternary", "dsv2lite_int4"])
+def test_unpack_bit_exact_workloads(name):
+    _check_unpack(synth.MOE_WORKLOADS[name])
+
+
+def test_unpack_bit_exact_mixed_prefill_sampled_experts():
+    _check_unpack(synth.MOE_WORKLOADS["mixed_int2_int4_prefill"], experts=[0, 1, 63, 127])
+
+
+@pytest.mark.parametrize("cfg", SWEEP, ids=lambda c: "-".join(f"{k}{v}" for k, v in c.items()))
+def test_unpack_bit_exact_sweep(cfg):
+    _check_unpack(custom_moe_spec(**cfg))
+
+
+# ------------------------------------------------------------------ routing
+def _route(logits, k):
+    import skinny_gemm_amd as q
+    T, E = logits.shape
+    lg = torch.from_numpy(np.ascontiguousarray(logits, dtype=np.float32)).cuda()
+    S = T * k
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    counts = torch.empty(E, dtype=torch.int32, device="cuda")
+    offsets = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    rows = torch.empty(max(S, 1), dtype=torch.int32, device="cuda")
+    ws = torch.empty(q.route_workspace_size(T, E, k), dtype=torch.uint8, device="cuda")
+    q.route(T, E, k, lg, ids, w, counts, offsets, rows, ws)
+    torch.cuda.synchronize()
+    return dict(ids=ids.cpu().numpy(), w=w.cpu().numpy(), counts=counts.cpu().numpy(),
+                offsets=offsets.cpu().numpy(), row_list=rows.cpu().numpy()[:S])
+
+
+@pytest.mark.parametrize("T,E,k", [(1, 1, 1), (1, 64, 1), (1, 64, 6), (8, 64, 6), (16, 256, 8),
+                                   (5, 8, 8), (17, 64, 6), (100, 128, 8), (2048, 128, 8),
+                                   (3000, 256, 16), (33, 7, 3)])
+@pytest.mark.parametrize("ties", [False, True])
+def test_route_bit_exact(T, E, k, ties):
+    rng = np.random.default_rng(T * 1000 + E + k)
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    if ties:
+        lg = (np.round(lg * 2) / 2).astype(np.float32)
+        lg[0] = 0.0
+    got = _route(lg, k)
+    ref = oracle.route(lg, k)
+    for key in ("ids", "counts", "offsets", "row_list"):
+        assert np.array_equal(got[key], ref[key]), key
+    assert np.allclose(got["w"], ref["w"], rtol=2e-6, atol=1e-7)
+    assert np.all(np.abs(got["w"].sum(1) - 1.0) <= k * 2.0 ** -22)
+    if k == 1:
+        assert np.all(got["w"] == 1.0)
+    log(f"[route] T={T} E={E} k={k} ties={ties} bit-exact")
