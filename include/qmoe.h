@@ -58,7 +58,7 @@
  *   - Validation runs before any launch: a non-OK status means nothing was
  *     enqueued.  Launch failures return QMOE_ERR_DEVICE.  qmoe_last_error()
  *     gives a thread-local message for the last non-OK status.
- *   - Alignment: packed buffers and workspaces 256 B; x, y, logits 16 B.
+ *   - Alignment: packed buffers and workspaces 256 B; x and y 16 B; logits 4 B.
  */
 #ifndef QMOE_H_
 #define QMOE_H_
@@ -128,6 +128,10 @@ typedef struct qmoe_forward_opts {
   int32_t *ids_out;  /* optional device [T][k]: routed expert ids */
   float *w_out;      /* optional device [T][k]: routing weights */
   int32_t *counts_out; /* optional device [E]: rows routed to each expert */
+  void **events;     /* optional host array of hipEvent_t: events[2i] / events[2i+1] are
+                        recorded on `stream` before / after stage i of the plan's stage list */
+  int32_t num_events; /* entries in `events` (0 = none) */
+  int32_t reserved2;  /* must be 0 */
 } qmoe_forward_opts;
 
 /* Host-side description of what a forward call would launch (diagnostic). */
@@ -139,7 +143,8 @@ typedef struct qmoe_plan {
   int32_t gemv_fc2_waves;
   int32_t max_active;    /* upper bound of active experts the grids are sized for */
   int64_t workspace_bytes;
-  char kernels[256];     /* kernel names in launch order, comma separated */
+  char kernels[256];     /* stage names in launch order, comma separated; a stage is one
+                            kernel except "route" (one or two kernels) */
 } qmoe_plan;
 
 /* ABI version (QMOE_ABI_VERSION) and a thread-local message for the last non-OK status. */

@@ -94,8 +94,13 @@ struct Carve {
   }
 };
 
+inline int64_t grouped_max_tiles(int64_t S, int E) {
+  const int64_t t = (S + kTileM - 1) / kTileM + std::min<int64_t>(E, S);
+  return (t + 7) / 8 * 8;  // a multiple of 8 lets the kernel spread tiles over the XCDs
+}
+
 struct RouteWs {
-  int64_t ids, w, counts, offsets, row_list, slot_pos, active, num_active, end;
+  int64_t ids, w, counts, offsets, row_list, slot_pos, token_of, active, num_active, slot_info, tile_info, end;
   static RouteWs make(Carve &c, int64_t S, int E) {
     RouteWs r;
     r.ids = c.take(S * 4);
@@ -104,8 +109,11 @@ struct RouteWs {
     r.offsets = c.take(((int64_t)E + 1) * 4);
     r.row_list = c.take(S * 4);
     r.slot_pos = c.take(S * 4);
+    r.token_of = c.take(S * 4);
     r.active = c.take((int64_t)E * 4);
     r.num_active = c.take(4);
+    r.slot_info = c.take((int64_t)E * 16);
+    r.tile_info = c.take(grouped_max_tiles(S, E) * 16);
     r.end = c.off;
     return r;
   }
@@ -117,25 +125,41 @@ struct RouteWs {
     b.offsets = (int32_t *)(ws + offsets);
     b.row_list = (int32_t *)(ws + row_list);
     b.slot_pos = (int32_t *)(ws + slot_pos);
+    b.token_of = (int32_t *)(ws + token_of);
     b.active = (int32_t *)(ws + active);
     b.num_active = (int32_t *)(ws + num_active);
+    b.slot_info = (int4 *)(ws + slot_info);
+    b.tile_info = (int4 *)(ws + tile_info);
     return b;
   }
 };
 
+// GEMV path: h as bf16 hi/lo parts; grouped path: h fp32 + per-row |max|
+// and the per-token activation scales.  Both paths write o [S][H] fp32.
 struct MoeWs {
   RouteWs route;
-  int64_t h_hi, h_lo, o, total;
-  static MoeWs make(const qmoe_layer_desc &d, int32_t T, int32_t k) {
+  int64_t h_hi, h_lo, h32, hmax, xsc, o, total;
+  static MoeWs make(const qmoe_layer_desc &d, int32_t T, int32_t k, bool grouped) {
     MoeWs w;
     Carve c;
     const int64_t S = (int64_t)T * k;
     w.route = RouteWs::make(c, S, d.num_experts);
-    w.h_hi = c.take(S * d.inter * 2);
-    w.h_lo = c.take(S * d.inter * 2);
+    if (grouped) {
+      w.h_hi = w.h_lo = 0;
+      w.h32 = c.take(S * d.inter * 4);
+      w.hmax = c.take(S * 4);
+      w.xsc = c.take((int64_t)T * 4);
+    } else {
+      w.h_hi = c.take(S * d.inter * 2);
+      w.h_lo = c.take(S * d.inter * 2);
+      w.h32 = w.hmax = w.xsc = 0;
+    }
     w.o = c.take(S * d.hidden * 4);
     w.total = c.off;
     return w;
+  }
+  static int64_t worst(const qmoe_layer_desc &d, int32_t T, int32_t k) {
+    return std::max(make(d, T, k, false).total, make(d, T, k, true).total);
   }
 };
 
@@ -149,20 +173,33 @@ int pick_mmax(int64_t rows) {
   return m;
 }
 
-// Waves per workgroup for the split-K GEMV: enough waves in flight to cover
-// HBM latency, no more than the blocks along K, within the LDS budget.
-int pick_waves(int64_t nwg, int64_t nblk, int mmax) {
-  int64_t ks = (kTargetWaves + nwg - 1) / std::max<int64_t>(nwg, 1);
+// Waves per workgroup for the split-K GEMV: enough waves to hold every
+// block of a row group in one load batch, and enough waves on the chip to
+// cover HBM latency; at most 8 waves and one block per wave, within the LDS
+// budget.
+int pick_waves(int64_t nwg, int64_t nblk, int cpb, int mmax, int64_t K, int parts) {
+  const int64_t bpw = gemv_blocks_per_batch(cpb);
+  int64_t ks = std::max<int64_t>((nblk + bpw - 1) / bpw, (kTargetWaves + nwg - 1) / std::max<int64_t>(nwg, 1));
   ks = std::max<int64_t>(1, std::min<int64_t>(ks, 8));
   ks = std::min<int64_t>(ks, nblk);
-  while (ks > 1 && gemv_lds_bytes(mmax, nblk, (int)ks) > kLdsLimit) --ks;
-  if (gemv_lds_bytes(mmax, nblk, (int)ks) > kLdsLimit) return 0;
+  while (ks > 1 && gemv_lds_bytes(mmax, nblk, (int)ks, K, parts) > kLdsLimit) --ks;
+  if (gemv_lds_bytes(mmax, nblk, (int)ks, K, parts) > kLdsLimit) return 0;
   return (int)ks;
+}
+
+// Row-count bound of a GEMV launch and its waves; a bound whose staged
+// activations do not fit in LDS moves to the next (scalar-load) variant.
+bool pick_gemv(int64_t rows, int64_t nwg, const MatLayout &L, int parts, int &mmax, int &ks) {
+  for (mmax = pick_mmax(rows); mmax <= kGemvMaxRows; mmax *= 2) {
+    ks = pick_waves(nwg, L.nblk, L.cpb, mmax, L.K, parts);
+    if (ks > 0) return true;
+  }
+  return false;
 }
 
 struct Plan {
   int path;
-  int mmax, ks1, ks2, max_active;
+  int mmax, mmax1, mmax2, ks1, ks2, max_active, max_tiles;
   int route_fused;
   int launches;
   std::string kernels;
@@ -177,25 +214,63 @@ qmoe_status make_plan(const qmoe_layer_desc &d, int32_t T, int32_t k, int path_r
     return fail(QMOE_ERR_INVALID_ARGUMENT, "unknown path %d", path_req);
   if (path == QMOE_PATH_GEMV && T > kGemvMaxRows)
     return fail(QMOE_ERR_UNSUPPORTED, "GEMV path needs T <= %d (got %d)", kGemvMaxRows, T);
-  if (path == QMOE_PATH_GROUPED)
-    return fail(QMOE_ERR_UNSUPPORTED, "grouped MFMA path not available for T = %d", T);
   p.path = path;
+  p.max_active = (int)std::min<int64_t>(d.num_experts, (int64_t)T * k);
+  if (path == QMOE_PATH_GROUPED) {
+    if ((L.fc1.affine && L.fc1.nblk > kGroupedMaxAffineBlocks) ||
+        (L.fc2.affine && L.fc2.nblk > kGroupedMaxAffineBlocks))
+      return fail(QMOE_ERR_UNSUPPORTED, "affine formats on the grouped path need K/block <= %d",
+                  kGroupedMaxAffineBlocks);
+    p.route_fused = (T <= 16) ? 1 : 0;
+    p.max_tiles = (int)grouped_max_tiles((int64_t)T * k, d.num_experts);
+    p.kernels = "route,rowscale,grouped_fc1_swiglu,grouped_fc2,combine";
+    p.launches = (p.route_fused ? 1 : 2) + 4;
+    return ok();
+  }
   p.route_fused = (T <= 16) ? 1 : 0;
   p.max_active = (int)std::min<int64_t>(d.num_experts, (int64_t)T * k);
-  p.mmax = pick_mmax(T);
-  p.ks1 = pick_waves((int64_t)p.max_active * L.fc1.RG, L.fc1.nblk, p.mmax);
-  p.ks2 = pick_waves((int64_t)p.max_active * L.fc2.RG, L.fc2.nblk, p.mmax);
-  if (p.ks1 == 0 || p.ks2 == 0)
+  if (!pick_gemv(T, (int64_t)p.max_active * L.fc1.RG, L.fc1, 1, p.mmax1, p.ks1) ||
+      !pick_gemv(T, (int64_t)p.max_active * L.fc2.RG, L.fc2, 2, p.mmax2, p.ks2))
     return fail(QMOE_ERR_UNSUPPORTED, "K too large for the GEMV workgroup LDS budget");
-  p.kernels = p.route_fused ? "route_expand" : "route_topk,route_expand";
-  p.kernels += ",gemv_fc1_swiglu,gemv_fc2,combine";
-  p.launches = p.route_fused ? 4 : 5;
+  p.mmax = p.mmax1;
+  // top-1: the down GEMV writes y; otherwise a combine kernel follows
+  p.kernels = k == 1 ? "route,gemv_fc1_swiglu,gemv_fc2" : "route,gemv_fc1_swiglu,gemv_fc2,combine";
+  p.launches = k == 1 ? 3 : 4;
   return ok();
 }
 
 qmoe_status hip_status(hipError_t e, const char *what) {
   if (e != hipSuccess) return fail(QMOE_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
   return ok();
+}
+
+GroupedArgs grouped_base(const MatLayout &L, const uint8_t *w, const float *wsc) {
+  GroupedArgs g;
+  memset(&g, 0, sizeof g);
+  g.w = w;
+  g.expert_stride = L.stride;
+  g.scales_off = L.scales_off;
+  g.N = L.N;
+  g.K = L.K;
+  g.RG = L.RG;
+  g.NC = L.NC;
+  g.nblk = L.nblk;
+  g.qtype = L.qtype;
+  g.sdtype = L.sdtype;
+  g.block = L.block;
+  g.wsc = wsc;
+  return g;
+}
+
+qmoe_status copy_diagnostics(const qmoe_layer_desc *desc, const qmoe_forward_opts *opts, const RouteBufs &r,
+                             int64_t S, hipStream_t s) {
+  hipError_t e = hipSuccess;
+  if (opts && opts->ids_out) e = hipMemcpyAsync(opts->ids_out, r.ids, S * 4, hipMemcpyDeviceToDevice, s);
+  if (e == hipSuccess && opts && opts->w_out)
+    e = hipMemcpyAsync(opts->w_out, r.w, S * 4, hipMemcpyDeviceToDevice, s);
+  if (e == hipSuccess && opts && opts->counts_out)
+    e = hipMemcpyAsync(opts->counts_out, r.counts, (size_t)desc->num_experts * 4, hipMemcpyDeviceToDevice, s);
+  return hip_status(e, "diagnostic copies");
 }
 
 GemvArgs gemv_base(const MatLayout &L, const uint8_t *w) {
@@ -265,6 +340,10 @@ qmoe_status qmoe_prepack(const qmoe_layer_desc *desc, const void *fc1_codes, con
   e = launch_prepack_matrix(L.fc2, desc->num_experts, (const uint8_t *)fc2_codes,
                             (const uint16_t *)fc2_scales, (const uint16_t *)fc2_biases, d + L.fc2_off, err, s);
   if (e != hipSuccess) return hip_status(e, "prepack fc2");
+  e = launch_wscale(L.fc1, desc->num_experts, d + L.fc1_off, (float *)(d + L.wsc_off), s);
+  if (e == hipSuccess)
+    e = launch_wscale(L.fc2, desc->num_experts, d + L.fc2_off, (float *)(d + L.wsc_off) + desc->num_experts, s);
+  if (e != hipSuccess) return hip_status(e, "prepack weight scales");
   uint32_t nbad = 0;
   e = hipMemcpyAsync(&nbad, err, 4, hipMemcpyDeviceToHost, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
@@ -279,7 +358,7 @@ qmoe_status qmoe_workspace_size(const qmoe_layer_desc *desc, int32_t T, int32_t 
   st = check_tokens(desc, T, top_k);
   if (st != QMOE_OK) return st;
   if (!bytes) return fail(QMOE_ERR_INVALID_ARGUMENT, "null size output");
-  *bytes = (size_t)MoeWs::make(*desc, T, top_k).total;
+  *bytes = (size_t)MoeWs::worst(*desc, T, top_k);
   return ok();
 }
 
@@ -300,7 +379,7 @@ qmoe_status qmoe_forward_plan(const qmoe_layer_desc *desc, int32_t T, int32_t to
   plan->gemv_fc1_waves = p.ks1;
   plan->gemv_fc2_waves = p.ks2;
   plan->max_active = p.max_active;
-  plan->workspace_bytes = MoeWs::make(*desc, T, top_k).total;
+  plan->workspace_bytes = MoeWs::make(*desc, T, top_k, p.path == QMOE_PATH_GROUPED).total;
   snprintf(plan->kernels, sizeof plan->kernels, "%s", T == 0 ? "" : p.kernels.c_str());
   return ok();
 }
@@ -312,7 +391,10 @@ qmoe_status qmoe_forward_ex(const qmoe_layer_desc *desc, const void *packed, con
   if (st != QMOE_OK) return st;
   st = check_tokens(desc, T, top_k);
   if (st != QMOE_OK) return st;
-  if (opts && opts->reserved != 0) return fail(QMOE_ERR_INVALID_ARGUMENT, "opts.reserved must be 0");
+  if (opts && (opts->reserved != 0 || opts->reserved2 != 0))
+    return fail(QMOE_ERR_INVALID_ARGUMENT, "opts.reserved fields must be 0");
+  if (opts && opts->num_events > 0 && !opts->events)
+    return fail(QMOE_ERR_INVALID_ARGUMENT, "opts.events is null but num_events > 0");
   if (T == 0) return ok();
   Plan p;
   st = make_plan(*desc, T, top_k, opts ? opts->path : QMOE_PATH_AUTO, p);
@@ -321,9 +403,9 @@ qmoe_status qmoe_forward_ex(const qmoe_layer_desc *desc, const void *packed, con
     return fail(QMOE_ERR_INVALID_ARGUMENT, "null device pointer");
   if (!aligned(packed, kAlign) || !aligned(ws, kAlign))
     return fail(QMOE_ERR_INVALID_ARGUMENT, "packed and ws must be 256-byte aligned");
-  if (!aligned(x, 16) || !aligned(y, 16) || !aligned(logits, 16))
-    return fail(QMOE_ERR_INVALID_ARGUMENT, "x, y and logits must be 16-byte aligned");
-  const MoeWs W = MoeWs::make(*desc, T, top_k);
+  if (!aligned(x, 16) || !aligned(y, 16) || !aligned(logits, 4))
+    return fail(QMOE_ERR_INVALID_ARGUMENT, "x and y must be 16-byte aligned, logits 4-byte aligned");
+  const MoeWs W = MoeWs::make(*desc, T, top_k, p.path == QMOE_PATH_GROUPED);
   if (ws_bytes < (size_t)W.total)
     return fail(QMOE_ERR_WORKSPACE_TOO_SMALL, "workspace holds %zu bytes, %lld needed", ws_bytes,
                 (long long)W.total);
@@ -339,63 +421,109 @@ qmoe_status qmoe_forward_ex(const qmoe_layer_desc *desc, const void *packed, con
   ra.k = top_k;
   ra.r = W.route.bind(wsb);
   ra.topk_in_expand = p.route_fused;
-  hipError_t e = launch_route(ra, s);
+  ra.max_slots = p.max_active;
+  ra.zero_buf = p.path == QMOE_PATH_GROUPED ? (int32_t *)(wsb + W.hmax) : nullptr;
+  ra.zero_len = p.path == QMOE_PATH_GROUPED ? (int)((int64_t)T * top_k) : 0;
+  ra.tile_rows = p.path == QMOE_PATH_GROUPED ? kTileM : 0;
+  ra.max_tiles = p.max_tiles;
+  // optional per-stage events (diagnostic timing)
+  auto rec = [&](int slot) -> hipError_t {
+    if (!opts || !opts->events || slot >= opts->num_events || !opts->events[slot]) return hipSuccess;
+    return hipEventRecord((hipEvent_t)opts->events[slot], s);
+  };
+  hipError_t e = rec(0);
+  if (e == hipSuccess) e = launch_route(ra, s);
+  if (e == hipSuccess) e = rec(1);
   if (e != hipSuccess) return hip_status(e, "route");
 
-  uint16_t *h_hi = (uint16_t *)(wsb + W.h_hi), *h_lo = (uint16_t *)(wsb + W.h_lo);
   float *o = (float *)(wsb + W.o);
+  if (p.path == QMOE_PATH_GROUPED) {
+    float *xsc = (float *)(wsb + W.xsc), *h32 = (float *)(wsb + W.h32);
+    uint32_t *hmax = (uint32_t *)(wsb + W.hmax);
+    const float *wsc = (const float *)(pk + L.wsc_off);
+    e = rec(2);
+    if (e == hipSuccess) e = launch_rowscale(x, T, desc->hidden, desc->act_dtype == QMOE_DTYPE_F16, xsc, s);
+    if (e == hipSuccess) e = rec(3);
+    if (e != hipSuccess) return hip_status(e, "rowscale");
+    GroupedArgs q1 = grouped_base(L.fc1, pk + L.fc1_off, wsc);
+    q1.tile_info = ra.r.tile_info;
+    q1.token_of = ra.r.token_of;
+    q1.in_gather_token = 1;
+    q1.in = x;
+    q1.in_f16 = desc->act_dtype == QMOE_DTYPE_F16;
+    q1.in_row_elems = desc->hidden;
+    q1.in_rowsc = xsc;
+    q1.out_f32 = h32;
+    q1.out_rowmax = hmax;
+    q1.h_dbg = opts ? opts->h_out : nullptr;
+    q1.row_list = ra.r.row_list;
+    e = rec(4);
+    if (e == hipSuccess) e = launch_grouped(q1, kGEpiSwiGLU, p.max_tiles, s);
+    if (e == hipSuccess) e = rec(5);
+    if (e != hipSuccess) return hip_status(e, "grouped fc1");
+    GroupedArgs q2 = grouped_base(L.fc2, pk + L.fc2_off, wsc + desc->num_experts);
+    q2.tile_info = ra.r.tile_info;
+    q2.in = h32;
+    q2.in_f32 = 1;
+    q2.in_row_elems = desc->inter;
+    q2.in_rowmax = hmax;
+    q2.out_f32 = o;
+    e = rec(6);
+    if (e == hipSuccess) e = launch_grouped(q2, kGEpiStoreF32, p.max_tiles, s);
+    if (e == hipSuccess) e = rec(7);
+    if (e != hipSuccess) return hip_status(e, "grouped fc2");
+    e = rec(8);
+    if (e == hipSuccess)
+      e = launch_combine(o, ra.r.slot_pos, ra.r.w, T, top_k, desc->hidden, desc->act_dtype, (uint16_t *)y, s);
+    if (e == hipSuccess) e = rec(9);
+    if (e != hipSuccess) return hip_status(e, "combine");
+    return copy_diagnostics(desc, opts, ra.r, (int64_t)T * top_k, s);
+  }
+  uint16_t *h_hi = (uint16_t *)(wsb + W.h_hi), *h_lo = (uint16_t *)(wsb + W.h_lo);
 
   GemvArgs g1 = gemv_base(L.fc1, pk + L.fc1_off);
-  g1.active = ra.r.active;
-  g1.num_active = ra.r.num_active;
-  g1.counts = ra.r.counts;
-  g1.offsets = ra.r.offsets;
+  g1.slot_info = ra.r.slot_info;
+  g1.token_of = ra.r.token_of;
   g1.row_list = ra.r.row_list;
   g1.top_k = top_k;
   g1.in = (const uint32_t *)x;
   g1.in_row_pairs = desc->hidden / 2;
-  g1.in_parts = 1;
   g1.in_gather_token = 1;
   g1.h_hi = h_hi;
   g1.h_lo = h_lo;
   g1.h_dbg = opts ? opts->h_out : nullptr;
-  e = launch_gemv(g1, kEpiSwiGLU, desc->act_dtype == QMOE_DTYPE_F16, p.mmax, p.ks1, p.max_active, s);
+  e = rec(2);
+  if (e == hipSuccess)
+    e = launch_gemv(g1, kEpiSwiGLU, desc->act_dtype == QMOE_DTYPE_F16, p.mmax1, p.ks1, p.max_active, s);
+  if (e == hipSuccess) e = rec(3);
   if (e != hipSuccess) return hip_status(e, "gemv fc1");
 
   GemvArgs g2 = gemv_base(L.fc2, pk + L.fc2_off);
-  g2.active = ra.r.active;
-  g2.num_active = ra.r.num_active;
-  g2.counts = ra.r.counts;
-  g2.offsets = ra.r.offsets;
+  g2.slot_info = ra.r.slot_info;
+  g2.token_of = ra.r.token_of;
   g2.row_list = ra.r.row_list;
   g2.top_k = top_k;
   g2.in = (const uint32_t *)h_hi;
   g2.in_row_pairs = desc->inter / 2;
-  g2.in_parts = 2;
   g2.in_part_stride = (int64_t)(h_lo - h_hi) / 2;
   g2.in_gather_token = 0;
   g2.out_f32 = o;
-  e = launch_gemv(g2, kEpiStoreF32, 0, p.mmax, p.ks2, p.max_active, s);
+  g2.out_act = (uint16_t *)y;
+  g2.act_dtype = desc->act_dtype;
+  g2.route_w = ra.r.w;
+  e = rec(4);
+  if (e == hipSuccess) e = launch_gemv(g2, kEpiDown, 0, p.mmax2, p.ks2, p.max_active, s);
+  if (e == hipSuccess) e = rec(5);
   if (e != hipSuccess) return hip_status(e, "gemv fc2");
+  if (top_k > 1) {
+    e = rec(6);
+    if (e == hipSuccess)
+      e = launch_combine(o, ra.r.slot_pos, ra.r.w, T, top_k, desc->hidden, desc->act_dtype, (uint16_t *)y, s);
+    if (e == hipSuccess) e = rec(7);
+    if (e != hipSuccess) return hip_status(e, "combine");
+  }
 
-  e = launch_combine(o, ra.r.slot_pos, ra.r.w, T, top_k, desc->hidden, desc->act_dtype, (uint16_t *)y, s);
-  if (e != hipSuccess) return hip_status(e, "combine");
-
-  const int64_t S = (int64_t)T * top_k;
-  if (opts && opts->ids_out) {
-    e = hipMemcpyAsync(opts->ids_out, ra.r.ids, S * 4, hipMemcpyDeviceToDevice, s);
-    if (e != hipSuccess) return hip_status(e, "ids copy");
-  }
-  if (opts && opts->w_out) {
-    e = hipMemcpyAsync(opts->w_out, ra.r.w, S * 4, hipMemcpyDeviceToDevice, s);
-    if (e != hipSuccess) return hip_status(e, "weights copy");
-  }
-  if (opts && opts->counts_out) {
-    e = hipMemcpyAsync(opts->counts_out, ra.r.counts, (size_t)desc->num_experts * 4,
-                       hipMemcpyDeviceToDevice, s);
-    if (e != hipSuccess) return hip_status(e, "counts copy");
-  }
-  return ok();
+  return copy_diagnostics(desc, opts, ra.r, (int64_t)T * top_k, s);
 }
 
 qmoe_status qmoe_forward(const qmoe_layer_desc *desc, const void *packed, const void *x,
@@ -436,6 +564,11 @@ qmoe_status qmoe_route(int32_t T, int32_t E, int32_t top_k, const float *logits,
   ra.k = top_k;
   ra.r = R.bind((uint8_t *)ws);
   ra.topk_in_expand = (T <= 16) ? 1 : 0;
+  ra.max_slots = (int)std::min<int64_t>(E, (int64_t)T * top_k);
+  ra.zero_buf = nullptr;
+  ra.zero_len = 0;
+  ra.tile_rows = 0;
+  ra.max_tiles = 0;
   hipError_t e = launch_route(ra, s);
   if (e != hipSuccess) return hip_status(e, "route");
   const int64_t S = (int64_t)T * top_k;
@@ -469,7 +602,7 @@ qmoe_status qmoe_linear_prepacked_size(const qmoe_qmatrix_desc *desc, size_t *by
   qmoe_status st = check_matrix(*desc, "linear", -1, -1);
   if (st != QMOE_OK) return st;
   if (!bytes) return fail(QMOE_ERR_INVALID_ARGUMENT, "null size output");
-  *bytes = (size_t)(MatLayout::make(*desc).stride + kAlign);  // + a tail for the prepack error word
+  *bytes = (size_t)(MatLayout::make(*desc).stride + kLinearTail);  // + the tail (error word, pre-scale)
   return ok();
 }
 
@@ -493,6 +626,8 @@ qmoe_status qmoe_linear_prepack(const qmoe_qmatrix_desc *desc, const void *codes
   if (e == hipSuccess)
     e = launch_prepack_matrix(L, 1, (const uint8_t *)codes, (const uint16_t *)scales,
                               (const uint16_t *)biases, (uint8_t *)dst, err, s);
+  if (e == hipSuccess)
+    e = launch_wscale(L, 1, (const uint8_t *)dst, (float *)((uint8_t *)dst + L.stride + kLinearWscOff), s);
   uint32_t nbad = 0;
   if (e == hipSuccess) e = hipMemcpyAsync(&nbad, err, 4, hipMemcpyDeviceToHost, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
@@ -506,15 +641,14 @@ qmoe_status qmoe_linear_workspace_size(const qmoe_qmatrix_desc *desc, int32_t M,
   qmoe_status st = qmoe_linear_prepacked_size(desc, &need);
   if (st != QMOE_OK) return st;
   if (M < 0) return fail(QMOE_ERR_INVALID_ARGUMENT, "M must be >= 0");
-  *bytes = 0;  // the GEMV path needs no workspace
+  if (!bytes) return fail(QMOE_ERR_INVALID_ARGUMENT, "null size output");
+  *bytes = (size_t)align_up((int64_t)M * 4, kAlign);  // MFMA path: per-row activation scales
   return ok();
 }
 
 qmoe_status qmoe_linear(const qmoe_qmatrix_desc *desc, const void *packed, const void *x,
                         int32_t x_dtype, int32_t M, void *y, void *ws, size_t ws_bytes, int32_t path,
                         void *stream) {
-  (void)ws;
-  (void)ws_bytes;
   if (!desc) return fail(QMOE_ERR_INVALID_ARGUMENT, "null descriptor");
   qmoe_status st = check_matrix(*desc, "linear", -1, -1);
   if (st != QMOE_OK) return st;
@@ -522,26 +656,49 @@ qmoe_status qmoe_linear(const qmoe_qmatrix_desc *desc, const void *packed, const
     return fail(QMOE_ERR_UNSUPPORTED, "x dtype %d not supported", x_dtype);
   if (M < 0) return fail(QMOE_ERR_INVALID_ARGUMENT, "M must be >= 0");
   if (M == 0) return ok();
-  int pth = path == QMOE_PATH_AUTO ? QMOE_PATH_GEMV : path;
-  if (pth != QMOE_PATH_GEMV) return fail(QMOE_ERR_UNSUPPORTED, "linear path %d not available", path);
-  if (M > kGemvMaxRows) return fail(QMOE_ERR_UNSUPPORTED, "GEMV path needs M <= %d", kGemvMaxRows);
+  if (path != QMOE_PATH_AUTO && path != QMOE_PATH_GEMV && path != QMOE_PATH_GROUPED)
+    return fail(QMOE_ERR_INVALID_ARGUMENT, "unknown path %d", path);
+  const int pth = path == QMOE_PATH_AUTO ? (M <= kGemvMaxRows ? QMOE_PATH_GEMV : QMOE_PATH_GROUPED) : path;
+  if (pth == QMOE_PATH_GEMV && M > kGemvMaxRows)
+    return fail(QMOE_ERR_UNSUPPORTED, "GEMV path needs M <= %d", kGemvMaxRows);
   if (!packed || !x || !y) return fail(QMOE_ERR_INVALID_ARGUMENT, "null device pointer");
   if (!aligned(packed, kAlign) || !aligned(x, 16) || !aligned(y, 16))
     return fail(QMOE_ERR_INVALID_ARGUMENT, "misaligned pointer");
   const MatLayout L = MatLayout::make(*desc);
-  const int mmax = pick_mmax(M);
-  const int ks = pick_waves(L.RG, L.nblk, mmax);
-  if (ks == 0) return fail(QMOE_ERR_UNSUPPORTED, "K too large for the GEMV workgroup LDS budget");
+  hipStream_t s = (hipStream_t)stream;
+  if (pth == QMOE_PATH_GROUPED) {
+    if (L.affine && L.nblk > kGroupedMaxAffineBlocks)
+      return fail(QMOE_ERR_UNSUPPORTED, "affine formats on the MFMA path need K/block <= %d",
+                  kGroupedMaxAffineBlocks);
+    const size_t need = (size_t)align_up((int64_t)M * 4, kAlign);
+    if (!ws) return fail(QMOE_ERR_INVALID_ARGUMENT, "the MFMA path needs a workspace");
+    if (!aligned(ws, kAlign)) return fail(QMOE_ERR_INVALID_ARGUMENT, "ws must be 256-byte aligned");
+    if (ws_bytes < need)
+      return fail(QMOE_ERR_WORKSPACE_TOO_SMALL, "workspace holds %zu bytes, %zu needed", ws_bytes, need);
+    float *xsc = (float *)ws;
+    hipError_t e = launch_rowscale(x, M, L.K, x_dtype == QMOE_DTYPE_F16, xsc, s);
+    if (e != hipSuccess) return hip_status(e, "rowscale");
+    GroupedArgs g = grouped_base(L, (const uint8_t *)packed,
+                                 (const float *)((const uint8_t *)packed + L.stride + kLinearWscOff));
+    g.dense_M = M;
+    g.in = x;
+    g.in_f16 = x_dtype == QMOE_DTYPE_F16;
+    g.in_row_elems = L.K;
+    g.in_rowsc = xsc;
+    g.out_act = (uint16_t *)y;
+    g.act_dtype = x_dtype;
+    return hip_status(launch_grouped(g, kGEpiStoreAct, (M + kTileM - 1) / kTileM, s), "linear mfma");
+  }
+  int mmax = 0, ks = 0;
+  if (!pick_gemv(M, L.RG, L, 1, mmax, ks))
+    return fail(QMOE_ERR_UNSUPPORTED, "K too large for the GEMV workgroup LDS budget");
   GemvArgs g = gemv_base(L, (const uint8_t *)packed);
   g.dense_M = M;
   g.in = (const uint32_t *)x;
   g.in_row_pairs = L.K / 2;
-  g.in_parts = 1;
   g.out_act = (uint16_t *)y;
   g.act_dtype = x_dtype;
-  return hip_status(launch_gemv(g, kEpiStoreAct, x_dtype == QMOE_DTYPE_F16, mmax, ks, 1,
-                                (hipStream_t)stream),
-                    "linear gemv");
+  return hip_status(launch_gemv(g, kEpiStoreAct, x_dtype == QMOE_DTYPE_F16, mmax, ks, 1, s), "linear gemv");
 }
 
 qmoe_status qmoe_linear_unpack_codes(const qmoe_qmatrix_desc *desc, const void *packed,

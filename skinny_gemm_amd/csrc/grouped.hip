@@ -1,0 +1,416 @@
+// grouped.hip -- grouped larger-M path: tiles of 64 routed rows x 128 outputs
+// per workgroup, MFMA (v_mfma_f32_16x16x32_f16) on weights dequantized once
+// per tile in registers.
+//
+// The pages' prefill path runs a grouped GEMM over the rows of each expert
+// that dequantizes each weight tile once instead of materialising dense
+// experts (onnxruntime pull request 33005, Description: no full A16 expert
+// weights; onnx-genai pull request 1167: the grouped M>1 path dequantizes
+// once).  The MLX issue 3852 discussion of a small-M tile (BM = 8/16) for the
+// M in [10, 32] range is the dense counterpart served by the same kernel.
+//
+// gfx950 mapping:
+//   - a weight code q and its block scale s become one exact f16 value
+//     q * s * 2^e: an 8-bit (bf16) significand times a code of at most 3
+//     significant bits fits the 11-bit f16 significand, and the per-expert
+//     power of two 2^e keeps every product a normal f16 (|q s 2^e| < 2^15).
+//     So the fp32 MFMA accumulators run over all of K with no per-block
+//     scale epilogue; 2^-e is removed exactly at the end.  An f16 scale
+//     (11 bits) times a multi-bit code is split into an 8-bit head and its
+//     tail, two exact f16 weights and two MFMAs.  Affine codes are recentred
+//     to q = u - 2^(b-1) (INT2: single-bit values) and the recentred bias
+//     b + 2^(b-1) s meets per-row block sums of x in the epilogue.
+//   - activations are staged in LDS as f16 with a per-row power of two
+//     (x * 2^r < 2^14): exact for bf16/f16 x; the fp32 SwiGLU output h is
+//     split into f16 hi + lo parts (about 22 significant bits) and FC2 runs
+//     one MFMA per part against the same dequantized weights.
+//   - B fragments are read straight from the GEMV prepacked layout: lane l
+//     of a wave reads dword (l / 16) of row (l % 16) of a 16-row slice, one
+//     coalesced 256-B load per slice and chunk; for 2-bit codes a dword holds
+//     16 consecutive k, split over two MFMA k-steps with the A operand
+//     gathered in the same k order.
+//   - workgroup ids are remapped so that the tiles sharing one expert's
+//     weight slice run on the same XCD (its own L2).
+#include <float.h>
+
+#include "codec.hpp"
+#include "gemv_impl.hpp"
+#include "qmoe_internal.h"
+
+namespace qmoe {
+
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float floatx4_t __attribute__((ext_vector_type(4)));
+
+// Power of two p with amax * p < 2^lim (1 for amax = 0 or non-finite).
+__device__ inline float pow2_below(float amax, int lim) {
+  if (!(amax > 0.f) || !(amax <= FLT_MAX)) return 1.f;
+  int e;
+  frexpf(amax, &e);  // amax < 2^e
+  int s = lim - e;
+  s = max(-120, min(120, s));
+  return ldexpf(1.f, s);
+}
+
+// ---------------------------------------------------------------- prep
+// One wave per row: power of two that brings max |x| below 2^14.
+__global__ __launch_bounds__(256) void rowscale_kernel(const uint16_t *__restrict__ x, int rows,
+                                                       int64_t K, int in_f16, float *__restrict__ rowsc) {
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (r >= rows) return;
+  float m = 0.f;
+  const uint16_t *xr = x + (int64_t)r * K;
+  for (int64_t k = lane; k < K; k += 64) m = fmaxf(m, fabsf(half_to_f32_rt(xr[k], in_f16)));
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  if (lane == 0) rowsc[r] = pow2_below(m, 14);
+}
+
+// One workgroup per expert: power of two that keeps max |s| * qmax below 2^15.
+__global__ __launch_bounds__(256) void wscale_kernel(MatLayout L, const uint8_t *__restrict__ mat,
+                                                     float *__restrict__ wsc) {
+  __shared__ float red[4];
+  const int e = blockIdx.x;
+  const uint8_t *sb = mat + (int64_t)e * L.stride + L.scales_off;
+  const int64_t n = L.N * L.nblk;
+  float m = 0.f;
+  const int f16 = L.sdtype == QMOE_DTYPE_F16;
+  const float qmax = (float)qtype_qmax(L.qtype);
+  for (int64_t i = threadIdx.x; i < n; i += blockDim.x) {
+    if (L.affine) {
+      const uint32_t sbb = reinterpret_cast<const uint32_t *>(sb)[i];
+      m = fmaxf(m, fabsf(half_to_f32_rt(sbb & 0xFFFFu, f16)) * qmax);
+    } else {
+      m = fmaxf(m, fabsf(half_to_f32_rt(reinterpret_cast<const uint16_t *>(sb)[i], f16)) * qmax);
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const float mm = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    wsc[e] = pow2_below(mm, 15);
+  }
+}
+
+// ---------------------------------------------------------------- GEMM
+constexpr int kMaxAffineBlocks = kGroupedMaxAffineBlocks;
+
+template <int QT, int EPI, bool IN_F32, bool IN_F16>
+__global__ __launch_bounds__(256) void grouped_kernel(const GroupedArgs a) {
+  using TR = QtTraits<QT>;
+  using CD = Codec<TR::kBits, true>;
+  constexpr int KC = 128 / TR::kBits;  // k per 16-B chunk: 32 (4-bit) or 64 (2-bit)
+  constexpr int KT = 128;              // k per staged tile
+  constexpr int CPT = KT / KC;         // chunks per tile
+  constexpr int KS = KT / 32;          // MFMA k-steps per tile
+  constexpr int APAD = 8;              // row padding of the staged tile (halves)
+  constexpr bool AFF = TR::kAffine;
+  // codes enter the MFMA as q = u - zc: the symmetric codes, and affine codes
+  // recentred to [-2^(b-1), 2^(b-1)-1] (bias b + zc*s added in the epilogue)
+  constexpr int ZC = AFF ? (1 << (TR::kBits - 1)) : TR::kZeroPoint;
+  // codes of more than one significant bit times an 11-bit (f16) scale do not
+  // fit f16: the scale is split into an 8-bit head and its tail (two MFMAs)
+  constexpr bool MULTIBIT = (QT == QMOE_QTYPE_SYM_INT4 || QT == QMOE_QTYPE_AFFINE_INT4);
+
+  constexpr int NPART = IN_F32 ? 2 : 1;  // fp32 input: f16 hi + lo parts (about 22 bits)
+  __shared__ _Float16 sA[NPART][kTileM][KT + APAD];
+  __shared__ int s_row[kTileM];
+  __shared__ float s_rsc[kTileM];
+  __shared__ float s_X[AFF ? kTileM : 1][AFF ? kMaxAffineBlocks : 1];  // per-row block sums of x
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int ntn = (int)((a.N + kTileN - 1) / kTileN);
+
+  // XCD-aware remap: blocks are dealt round-robin to 8 XCDs; give each XCD a
+  // contiguous range of tiles (n-tile major, row tiles of an expert adjacent)
+  const int G = gridDim.x;
+  const int bid = (G % 8 == 0) ? ((int)(blockIdx.x % 8) * (G / 8) + (int)(blockIdx.x / 8)) : (int)blockIdx.x;
+  const int tiles_m = G / ntn;
+  const int nt = bid / tiles_m, tile = bid - nt * tiles_m;
+
+  int e, p0, rows;
+  if (a.dense_M > 0) {
+    e = 0;
+    p0 = tile * kTileM;
+    rows = min(kTileM, a.dense_M - p0);
+  } else {
+    const int4 ti = a.tile_info[tile];
+    e = ti.x;
+    p0 = ti.y;
+    rows = ti.z;
+  }
+  if (rows <= 0) return;
+
+  if (threadIdx.x < kTileM) {
+    const int r = threadIdx.x;
+    int inrow = -1;
+    float sc = 0.f;
+    if (r < rows) {
+      const int p = p0 + r;
+      inrow = (a.dense_M > 0) ? p : (a.in_gather_token ? a.token_of[p] : p);
+      sc = IN_F32 ? pow2_below(__uint_as_float(a.in_rowmax[inrow]), 14) : a.in_rowsc[inrow];
+    }
+    s_row[r] = inrow;
+    s_rsc[r] = sc;
+  }
+  __syncthreads();
+
+  const float wsc = a.wsc[e];
+  const int nw = nt * kTileN + wave * 32;  // first output row of this wave
+  const bool wave_on = nw < a.N;           // N % 128 == 64: the last tile's upper half is idle
+  const int64_t rg = (wave_on ? nw : 0) / kRowsPerGroup;
+  const int nl0 = nw % kRowsPerGroup;
+  const uint8_t *wexp = a.w + (int64_t)e * a.expert_stride;
+  const uint32_t *wbase = reinterpret_cast<const uint32_t *>(wexp) + rg * a.NC * kLanes * 4;
+  const uint8_t *sbase = wexp + a.scales_off;
+  const int g = lane >> 4;
+  int nl[2];
+  nl[0] = nl0 + (lane & 15);
+  nl[1] = nl0 + 16 + (lane & 15);
+  const bool sf16 = a.sdtype == QMOE_DTYPE_F16;
+  const bool split = MULTIBIT && sf16;
+
+  floatx4_t acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+
+  // staging assignment: 4 threads per row, 32 consecutive k each
+  const int st_r = threadIdx.x >> 2, st_k = (threadIdx.x & 3) * 32;
+  const int st_in = s_row[st_r];
+  const float st_sc = s_rsc[st_r];
+
+  for (int64_t kt = 0; kt < a.K; kt += KT) {
+    // weight dwords and scales of this tile (issued before the staging)
+    // (a partial last tile re-reads the last chunk; its A columns are zero)
+    uint32_t bw[CPT][2];
+    uint32_t sv[CPT][2];
+    static_for<CPT>([&](auto cc) {
+      constexpr int c = decltype(cc)::value;
+      const int64_t chunk = min(kt / KC + c, a.NC - 1);
+      const int64_t blk = (chunk * KC) / a.block;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        bw[c][j] = wbase[(chunk * kLanes + nl[j]) * 4 + g];
+        const int64_t si = (rg * a.nblk + blk) * kLanes + nl[j];
+        sv[c][j] = AFF ? reinterpret_cast<const uint32_t *>(sbase)[si]
+                       : reinterpret_cast<const uint16_t *>(sbase)[si];
+      }
+    });
+
+    // stage A: 64 rows x 128 k as scaled f16 (fp32 input: hi and lo parts)
+    {
+      _Float16 *dst = &sA[0][st_r][st_k];
+      float xsum = 0.f;
+      if (st_in >= 0 && kt + st_k < a.K) {
+        if constexpr (IN_F32) {
+          _Float16 *dlo = &sA[NPART - 1][st_r][st_k];
+          const float4 *src = reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(a.in) +
+                                                              (int64_t)st_in * a.in_row_elems + kt + st_k);
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            const float4 v = src[q];
+            const float vv[4] = {v.x * st_sc, v.y * st_sc, v.z * st_sc, v.w * st_sc};
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+              const _Float16 hi = (_Float16)vv[h];
+              dst[4 * q + h] = hi;
+              dlo[4 * q + h] = (_Float16)(vv[h] - (float)hi);
+              xsum += vv[h];
+            }
+          }
+        } else {
+          const uint4 *src = reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(a.in) +
+                                                             (int64_t)st_in * a.in_row_elems + kt + st_k);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const uint4 v = src[q];
+            const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int h = 0; h < 8; ++h) {
+              const uint32_t bits = (wv[h >> 1] >> (16 * (h & 1))) & 0xFFFFu;
+              const float xs = half_to_f32<IN_F16>(bits) * st_sc;
+              dst[8 * q + h] = (_Float16)xs;
+              xsum += xs;
+            }
+          }
+        }
+      } else {
+#pragma unroll
+        for (int pp = 0; pp < NPART; ++pp)
+#pragma unroll
+          for (int q = 0; q < 32; ++q) sA[pp][st_r][st_k + q] = (_Float16)0.f;
+      }
+      if constexpr (AFF) {
+        // block sums of the scaled activations: the 4 threads of a row hold
+        // 4 consecutive 32-k segments; blocks are 64 or 128 k
+        const float p1 = xsum + __shfl_xor(xsum, 1);
+        const float p2 = p1 + __shfl_xor(p1, 2);
+        if (kt + st_k < a.K) {
+          if (a.block == 64 && (threadIdx.x & 1) == 0) s_X[st_r][(kt + st_k) / 64] = p1;
+          if (a.block == 128 && (threadIdx.x & 3) == 0) s_X[st_r][(kt + st_k) / 128] = p2;
+        }
+      }
+    }
+    __syncthreads();
+
+    static_for<KS>([&](auto kc_) {
+      constexpr int ks = decltype(kc_)::value;
+      constexpr int c = ks * 32 / KC;               // chunk of this k-step
+      constexpr int half = (ks * 32 % KC) / 32;     // 2-bit: which 8 of the dword's 16 k
+      half8_t bf[2], bl[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        uint32_t pr[CD::kPairs];
+        CD::extract(bw[c][j], pr);
+        const uint32_t sb = sv[c][j];
+        const float s = sf16 ? f16_to_f32(sb & 0xFFFFu) : bf16_to_f32(sb & 0xFFFFu);
+        // head: s rounded to 8 significant bits; tail: the rest (0 for bf16 scales)
+        const float sh = split ? bf16_to_f32(f32_to_bf16_rne(s)) : s;
+        const _Float16 shs = (_Float16)(sh * wsc), sls = (_Float16)((s - sh) * wsc);
+        const f16x2_t s2 = {shs, shs}, l2 = {sls, sls};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int jj = half * 4 + q;  // pair index within the dword
+          const _Float16 off = (_Float16)(CD::base(jj) + (float)ZC);
+          const f16x2_t off2 = {off, off};
+          const f16x2_t qv = __builtin_bit_cast(f16x2_t, pr[jj]) - off2;  // exact code
+          const f16x2_t wh = qv * s2, wl = qv * l2;                       // exact products
+          bf[j][2 * q] = wh[0];
+          bf[j][2 * q + 1] = wh[1];
+          bl[j][2 * q] = wl[0];
+          bl[j][2 * q + 1] = wl[1];
+        }
+      }
+      // A fragments: row (lane % 16) of each 16-row slice, 8 k in the order of B
+      const int koff = (TR::kBits == 4) ? (ks * 32 + 8 * g) : (c * 64 + 16 * g + 8 * half);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int pp = 0; pp < NPART; ++pp) {
+          const half8_t af = *reinterpret_cast<const half8_t *>(&sA[pp][16 * i + (lane & 15)][koff]);
+          if (wave_on) {
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+              acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf[j], acc[i][j], 0, 0, 0);
+              if (split) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bl[j], acc[i][j], 0, 0, 0);
+            }
+          }
+        }
+      }
+    });
+    __syncthreads();
+  }
+
+  // affine: + sum over blocks of (b + zc*s) * X[row][block], scaled like acc
+  if constexpr (AFF) {
+    if (wave_on) {
+      for (int blk = 0; blk < (int)a.nblk; ++blk) {
+        float bb[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const uint32_t sb = reinterpret_cast<const uint32_t *>(sbase)[(rg * a.nblk + blk) * kLanes + nl[j]];
+          const float s = sf16 ? f16_to_f32(sb & 0xFFFFu) : bf16_to_f32(sb & 0xFFFFu);
+          const float b = sf16 ? f16_to_f32(sb >> 16) : bf16_to_f32(sb >> 16);
+          bb[j] = fmaf((float)ZC, s, b) * wsc;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int el = 0; el < 4; ++el) {
+            const float X = s_X[16 * i + 4 * g + el][blk];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) acc[i][j][el] = fmaf(bb[j], X, acc[i][j][el]);
+          }
+      }
+    }
+  }
+
+  // epilogue: lane holds rows 16i + 4(lane/16) + el, column 16j + lane%16
+  const float winv = 1.f / wsc;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int el = 0; el < 4; ++el) {
+      const int m = 16 * i + 4 * g + el;
+      const bool valid = m < rows && wave_on;
+      const float inv = valid ? winv / s_rsc[m] : 0.f;
+      float hmax = 0.f;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const float v = acc[i][j][el] * inv;
+        const int64_t n = nw + 16 * j + (lane & 15);
+        if constexpr (EPI == kGEpiSwiGLU) {
+          const float up = __shfl_xor(v, 1);
+          if (valid && (lane & 1) == 0) {
+            const float h = v / (1.f + expf(-v)) * up;
+            const int64_t p = p0 + m;
+            a.out_f32[p * (a.N / 2) + n / 2] = h;
+            if (a.h_dbg) a.h_dbg[(int64_t)a.row_list[p] * (a.N / 2) + n / 2] = h;
+            hmax = fmaxf(hmax, fabsf(h));
+          }
+        } else if constexpr (EPI == kGEpiStoreF32) {
+          if (valid) a.out_f32[(int64_t)(p0 + m) * a.N + n] = v;
+        } else {
+          if (valid) a.out_act[(int64_t)(p0 + m) * a.N + n] = f32_to_act(v, a.act_dtype == QMOE_DTYPE_F16);
+        }
+      }
+      if constexpr (EPI == kGEpiSwiGLU) {
+        // max over the 16 lanes that share row m, then one atomic per row
+#pragma unroll
+        for (int off = 8; off >= 1; off >>= 1) hmax = fmaxf(hmax, __shfl_xor(hmax, off));
+        if (valid && (lane & 15) == 0) atomicMax(&a.out_rowmax[p0 + m], __float_as_uint(hmax));
+      }
+    }
+  }
+}
+
+template <int QT, int EPI>
+hipError_t launch_grouped_in(const GroupedArgs &a, int grid, hipStream_t s) {
+  if (a.in_f32)
+    hipLaunchKernelGGL((grouped_kernel<QT, EPI, true, false>), dim3(grid), dim3(256), 0, s, a);
+  else if (a.in_f16)
+    hipLaunchKernelGGL((grouped_kernel<QT, EPI, false, true>), dim3(grid), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((grouped_kernel<QT, EPI, false, false>), dim3(grid), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int QT>
+hipError_t launch_grouped_qt(const GroupedArgs &a, int epi, int grid, hipStream_t s) {
+  if (epi == kGEpiSwiGLU) return launch_grouped_in<QT, kGEpiSwiGLU>(a, grid, s);
+  if (epi == kGEpiStoreF32) return launch_grouped_in<QT, kGEpiStoreF32>(a, grid, s);
+  return launch_grouped_in<QT, kGEpiStoreAct>(a, grid, s);
+}
+
+hipError_t launch_grouped(const GroupedArgs &a, int epilogue, int grid_tiles, hipStream_t s) {
+  const int ntn = (int)((a.N + kTileN - 1) / kTileN);
+  const int grid = grid_tiles * ntn;
+  if (grid == 0) return hipSuccess;
+  switch (a.qtype) {
+    case QMOE_QTYPE_SYM_INT4: return launch_grouped_qt<QMOE_QTYPE_SYM_INT4>(a, epilogue, grid, s);
+    case QMOE_QTYPE_SYM_INT2: return launch_grouped_qt<QMOE_QTYPE_SYM_INT2>(a, epilogue, grid, s);
+    case QMOE_QTYPE_TERNARY: return launch_grouped_qt<QMOE_QTYPE_TERNARY>(a, epilogue, grid, s);
+    case QMOE_QTYPE_AFFINE_INT2: return launch_grouped_qt<QMOE_QTYPE_AFFINE_INT2>(a, epilogue, grid, s);
+    default: return launch_grouped_qt<QMOE_QTYPE_AFFINE_INT4>(a, epilogue, grid, s);
+  }
+}
+
+hipError_t launch_rowscale(const void *x, int rows, int64_t K, int in_f16, float *rowsc, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(rowscale_kernel, dim3((rows + 3) / 4), dim3(256), 0, s, (const uint16_t *)x, rows, K,
+                     in_f16, rowsc);
+  return hipGetLastError();
+}
+
+hipError_t launch_wscale(const MatLayout &L, int E, const uint8_t *mat, float *wsc, hipStream_t s) {
+  hipLaunchKernelGGL(wscale_kernel, dim3(E), dim3(256), 0, s, L, mat, wsc);
+  return hipGetLastError();
+}
+
+}  // namespace qmoe

@@ -90,19 +90,41 @@ constexpr int64_t kHeaderBytes = 256;
 constexpr uint64_t kPackMagic = 0x31304b50454f4d51ull;  // "QMOEPK01"
 constexpr int64_t kErrWordOff = 128;                     // u32 invalid-field counter
 
+// wsc_off: float [2][E] power-of-two pre-scales of the MFMA path (FC1, FC2).
 struct MoeLayout {
   MatLayout fc1, fc2;
-  int64_t fc1_off, fc2_off, total;
+  int64_t fc1_off, fc2_off, wsc_off, total;
   static MoeLayout make(const qmoe_layer_desc &d) {
     MoeLayout L{};
     L.fc1 = MatLayout::make(d.fc1);
     L.fc2 = MatLayout::make(d.fc2);
     L.fc1_off = kHeaderBytes;
     L.fc2_off = L.fc1_off + (int64_t)d.num_experts * L.fc1.stride;
-    L.total = L.fc2_off + (int64_t)d.num_experts * L.fc2.stride;
+    L.wsc_off = L.fc2_off + (int64_t)d.num_experts * L.fc2.stride;
+    L.total = L.wsc_off + align_up(2 * (int64_t)d.num_experts * 4, kAlign);
     return L;
   }
 };
+
+// Dense (linear) prepacked buffer: [matrix][tail 256 B: u32 error word at +0,
+// float power-of-two pre-scale of the MFMA path at +16].
+constexpr int64_t kLinearTail = 256;
+constexpr int64_t kLinearWscOff = 16;
+
+// Largest |q| the MFMA path multiplies a scale by (affine codes recentred to
+// u - 2^(b-1)); its power-of-two pre-scale keeps q*s inside f16 range.
+__host__ __device__ inline int qtype_qmax(int qt) {
+  switch (qt) {
+    case QMOE_QTYPE_SYM_INT4: return 8;
+    case QMOE_QTYPE_SYM_INT2: return 2;
+    case QMOE_QTYPE_TERNARY: return 1;
+    case QMOE_QTYPE_AFFINE_INT2: return 2;
+    default: return 8;
+  }
+}
+
+// Affine formats on the MFMA path keep per-row block sums in LDS.
+constexpr int kGroupedMaxAffineBlocks = 80;
 
 // ------------------------------------------------------------------ routing
 // Device-side routing results, carved from the workspace.
@@ -113,8 +135,11 @@ struct RouteBufs {
   int32_t *offsets;    // [E+1]
   int32_t *row_list;   // [T*k]   slot ids grouped by expert
   int32_t *slot_pos;   // [T*k]   inverse of row_list
+  int32_t *token_of;   // [T*k]   token of the row at each expert-sorted position
   int32_t *active;     // [E]     experts with count > 0, ascending
   int32_t *num_active; // [1]
+  int4 *slot_info;     // [max_slots] {expert, rows, first position, 0}; rows = 0 past num_active
+  int4 *tile_info;     // [max_tiles] {expert, first position, rows (<= tile), 0}; rows = 0 past the end
 };
 
 struct RouteArgs {
@@ -122,10 +147,19 @@ struct RouteArgs {
   int T, E, k;
   RouteBufs r;
   int topk_in_expand;  // 1: the expand kernel also performs top-k (small T)
+  int max_slots;       // entries of slot_info to fill
+  int32_t *zero_buf;   // optional int buffer cleared by the expand kernel
+  int zero_len;
+  int tile_rows;       // rows per grouped-path tile (0: no tile list)
+  int max_tiles;       // entries of tile_info to fill
 };
 
 // -------------------------------------------------------------------- GEMV
-enum GemvEpilogue { kEpiSwiGLU = 0, kEpiStoreF32 = 1, kEpiStoreAct = 2 };
+// kEpiSwiGLU: FC1 -> h (bf16 hi + lo parts, optional fp32 copy);
+// kEpiDown: FC2 -> per-slot fp32 o; with top-1 routing the combine is a
+// single product and y is written directly;
+// kEpiStoreAct: dense rows -> y in the activation dtype.
+enum GemvEpilogue { kEpiSwiGLU = 0, kEpiDown = 1, kEpiStoreAct = 2 };
 
 struct GemvArgs {
   // weights
@@ -134,28 +168,38 @@ struct GemvArgs {
   int64_t scales_off;
   int64_t N, K, RG, NC, nblk;
   int cpb, kc, qtype, sdtype;
-  // rows: either routed (active/counts/offsets/row_list) or dense (M rows)
-  const int32_t *active, *num_active, *counts, *offsets, *row_list;
+  // rows: routed (slot_info / token_of) or dense (M rows)
+  const int4 *slot_info;
+  const int32_t *token_of, *row_list;
   int top_k;
   int dense_M;             // >0: dense rows 0..M-1, expert 0, no routing
   // input activations as 16-bit pairs; parts = 1 (x) or 2 (hi, lo)
   const uint32_t *in;
   int64_t in_row_pairs;    // row stride in 32-bit pairs
-  int in_parts;            // 2: rows [p] of part 0 at in, of part 1 at in + part_stride
-  int64_t in_part_stride;  // in pairs
-  int in_gather_token;     // 1: input row = row_list[p] / top_k (FC1); 0: input row = p
+  int64_t in_part_stride;  // in pairs: part 1 of row p at in + p*in_row_pairs + in_part_stride
+  int in_gather_token;     // 1: input row = token_of[p] (FC1); 0: input row = p
   // outputs
-  float *out_f32;          // kEpiStoreF32: [p][N]
-  uint16_t *out_act;       // kEpiStoreAct: [m][N]
+  float *out_f32;          // kEpiDown: o [p][N]
+  uint16_t *out_act;       // kEpiStoreAct: [m][N]; kEpiDown with top-1: y [t][N]
   uint16_t *h_hi, *h_lo;   // kEpiSwiGLU: [p][N/2] bf16 parts of h
   float *h_dbg;            // kEpiSwiGLU: optional [slot][N/2] fp32
-  int act_dtype;           // kEpiStoreAct
+  int act_dtype;           // kEpiStoreAct, kEpiDown
+  const float *route_w;    // kEpiDown: routing weights [T*k]
 };
 
-// Dynamic LDS of one GEMV workgroup: per-row block corrections + the
-// cross-wave partial sums.
-inline size_t gemv_lds_bytes(int mmax, int64_t nblk, int waves) {
-  return ((size_t)mmax * (size_t)nblk * 2 + (size_t)waves * (size_t)mmax * kLanes) * sizeof(float);
+// Blocks a wave loads in one batch: 8 chunks of 16 B per lane.
+inline int gemv_blocks_per_batch(int cpb) { return cpb >= 8 ? 1 : 8 / cpb; }
+
+// Activations are staged in LDS (broadcast ds_read) for at most this many
+// rows per expert; more rows read them with scalar loads.
+constexpr int kGemvLdsRows = 4;
+
+// Dynamic LDS of one GEMV workgroup: per-row block corrections, staged
+// activations (parts x rows x K 16-bit values, small row counts only) and
+// the cross-wave partial sums.
+inline size_t gemv_lds_bytes(int mmax, int64_t nblk, int waves, int64_t K, int parts) {
+  const size_t x = (mmax <= kGemvLdsRows) ? (size_t)parts * (size_t)mmax * (size_t)K * 2 : 0;
+  return ((size_t)mmax * (size_t)nblk * 2 + (size_t)waves * (size_t)mmax * kLanes) * sizeof(float) + x + 64;
 }
 
 // Host launchers (defined in the kernel translation units).
@@ -169,5 +213,41 @@ hipError_t launch_gemv(const GemvArgs &a, int epilogue, int in_f16, int mmax, in
                        int grid_slots, hipStream_t s);
 hipError_t launch_combine(const float *o, const int32_t *slot_pos, const float *w, int T, int k,
                           int H, int act_dtype, uint16_t *y, hipStream_t s);
+
+// ----------------------------------------------------------- grouped MFMA
+constexpr int kTileM = 64;   // rows (tokens) per grouped tile
+constexpr int kTileN = 128;  // outputs per grouped tile (4 waves x 32)
+
+enum GroupedEpilogue { kGEpiSwiGLU = 0, kGEpiStoreF32 = 1, kGEpiStoreAct = 2 };
+
+struct GroupedArgs {
+  const uint8_t *w;        // matrix section base (expert 0)
+  int64_t expert_stride, scales_off;
+  int64_t N, K, RG, NC, nblk;
+  int qtype, sdtype, block;
+  const float *wsc;        // [E] power-of-two weight pre-scale
+  // rows
+  const int4 *tile_info;   // routed: {expert, first position, rows, 0}
+  int dense_M;             // > 0: dense rows, tiles of kTileM over M
+  const int32_t *token_of; // routed FC1: input row of position p
+  int in_gather_token;
+  // input: 16-bit rows (in_f32 = 0, dtype in_f16) or fp32 rows (in_f32 = 1)
+  const void *in;
+  int in_f32, in_f16;
+  int64_t in_row_elems;
+  const float *in_rowsc;   // 16-bit input: power-of-two scale per input row
+  const uint32_t *in_rowmax; // fp32 input: |max| bits per row (scale derived)
+  // outputs
+  float *out_f32;          // kGEpiSwiGLU: h [p][N/2]; kGEpiStoreF32: o [p][N]
+  uint32_t *out_rowmax;    // kGEpiSwiGLU: |max| bits of h per row (atomicMax), zero on entry
+  uint16_t *out_act;       // kGEpiStoreAct: y [m][N]
+  int act_dtype;
+  float *h_dbg;            // optional fp32 copy of h in slot order
+  const int32_t *row_list;
+};
+
+hipError_t launch_grouped(const GroupedArgs &a, int epilogue, int grid_tiles, hipStream_t s);
+hipError_t launch_rowscale(const void *x, int rows, int64_t K, int in_f16, float *rowsc, hipStream_t s);
+hipError_t launch_wscale(const MatLayout &L, int E, const uint8_t *mat, float *wsc, hipStream_t s);
 
 }  // namespace qmoe

@@ -106,6 +106,7 @@ __global__ __launch_bounds__(kExpandThreads) void route_expand_kernel(RouteArgs 
     s_cnt[e] = 0;
     s_base[e] = 0;
   }
+  for (int i = tid; i < a.zero_len; i += kExpandThreads) a.zero_buf[i] = 0;
   for (int i = tid; i < kExpandWaves * kMaxExperts; i += kExpandThreads) (&s_wc[0][0])[i] = 0;
   __syncthreads();
 
@@ -145,7 +146,10 @@ __global__ __launch_bounds__(kExpandThreads) void route_expand_kernel(RouteArgs 
         s_off[e] = run;
         a.r.offsets[e] = run;
         a.r.counts[e] = c[i];
-        if (f[i]) a.r.active[frun] = e;
+        if (f[i]) {
+          a.r.active[frun] = e;
+          if (frun < a.max_slots) a.r.slot_info[frun] = make_int4(e, c[i], run, 0);
+        }
       }
       run += c[i];
       frun += f[i];
@@ -154,6 +158,39 @@ __global__ __launch_bounds__(kExpandThreads) void route_expand_kernel(RouteArgs 
       s_off[E] = ci;
       a.r.offsets[E] = ci;
       a.r.num_active[0] = fi;
+    }
+    // slots past the active experts do no work
+    const int na = __shfl(fi, kLanes - 1);
+    for (int sl = na + lane; sl < a.max_slots; sl += kLanes) a.r.slot_info[sl] = make_int4(0, 0, 0, 0);
+
+    // grouped path: tiles of tile_rows rows per expert, in expert order
+    if (a.tile_rows > 0) {
+      int nt[PER];
+      int ts = 0;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        nt[i] = (c[i] + a.tile_rows - 1) / a.tile_rows;
+        ts += nt[i];
+      }
+      int ti = ts;
+#pragma unroll
+      for (int off = 1; off < kLanes; off <<= 1) {
+        const int o = __shfl_up(ti, off);
+        if (lane >= off) ti += o;
+      }
+      int tpos = ti - ts;
+      int roff = ci - cs;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        const int e = lane * PER + i;
+        for (int t = 0; t < nt[i]; ++t)
+          if (tpos + t < a.max_tiles)
+            a.r.tile_info[tpos + t] = make_int4(e, roff + t * a.tile_rows, min(a.tile_rows, c[i] - t * a.tile_rows), 0);
+        tpos += nt[i];
+        roff += c[i];
+      }
+      const int ntot = __shfl(ti, kLanes - 1);
+      for (int t = ntot + lane; t < a.max_tiles; t += kLanes) a.r.tile_info[t] = make_int4(0, 0, 0, 0);
     }
   }
   __syncthreads();
@@ -178,6 +215,7 @@ __global__ __launch_bounds__(kExpandThreads) void route_expand_kernel(RouteArgs 
       for (int w2 = 0; w2 < wave; ++w2) pos += s_wc[w2][e];
       a.r.row_list[pos] = r;
       a.r.slot_pos[r] = pos;
+      a.r.token_of[pos] = r / a.k;
     }
     __syncthreads();
     for (int x = tid; x < E; x += kExpandThreads) {

@@ -9,7 +9,8 @@ import numpy as np
 import torch
 
 from . import (layer_desc, qmatrix_desc, prepacked_size, prepack, workspace_size, forward_ex,
-               linear_prepacked_size, linear_prepack, linear, unpack_codes, linear_unpack_codes)
+               linear_prepacked_size, linear_prepack, linear, linear_workspace_size, unpack_codes,
+               linear_unpack_codes)
 
 TORCH_ACT = {"bf16": torch.bfloat16, "f16": torch.float16}
 
@@ -53,7 +54,7 @@ class MoeLayer:
                            device=self.device)
 
     def forward(self, x: torch.Tensor, logits: torch.Tensor, top_k: int, y=None, ws=None,
-                path="auto", debug=False, stream=None):
+                path="auto", debug=False, stream=None, events=None):
         T = x.shape[0]
         if y is None:
             y = torch.empty((T, self.H), dtype=TORCH_ACT[self.act_dtype], device=self.device)
@@ -67,7 +68,7 @@ class MoeLayer:
             dbg["counts"] = torch.full((self.E,), -1, dtype=torch.int32, device=self.device)
         forward_ex(self.desc, self.packed, x, logits, T, top_k, y, ws, stream=stream, path=path,
                    h_out=dbg.get("h"), ids_out=dbg.get("ids"), w_out=dbg.get("w"),
-                   counts_out=dbg.get("counts"))
+                   counts_out=dbg.get("counts"), events=events)
         return (y, dbg) if debug else y
 
     def unpack(self, which: int) -> torch.Tensor:
@@ -91,11 +92,16 @@ class QLinear:
         linear_prepack(self.desc, c, s, b, self.packed)
         del c, s, b
 
-    def __call__(self, x: torch.Tensor, x_dtype: str, y=None, path="auto", stream=None):
+    def workspace(self, M: int) -> torch.Tensor:
+        return torch.empty(max(linear_workspace_size(self.desc, M), 256), dtype=torch.uint8, device=self.device)
+
+    def __call__(self, x: torch.Tensor, x_dtype: str, y=None, ws=None, path="auto", stream=None):
         M = x.shape[0]
         if y is None:
             y = torch.empty((M, self.N), dtype=TORCH_ACT[x_dtype], device=self.device)
-        linear(self.desc, self.packed, x, x_dtype, M, y, None, path=path, stream=stream)
+        if ws is None:
+            ws = self.workspace(M)
+        linear(self.desc, self.packed, x, x_dtype, M, y, ws, path=path, stream=stream)
         return y
 
     def unpack(self) -> torch.Tensor:

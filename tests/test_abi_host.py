@@ -43,11 +43,13 @@ def _desc(**kw):
 def test_prepacked_size_matches_layout():
     d = _desc()
     n = q.prepacked_size(d)
-    # header + per expert: codes + scales, each rounded to 256 bytes
+    # header + per expert: codes + scales, each rounded to 256 bytes, then the
+    # per-expert power-of-two pre-scales of the MFMA path (2 x E floats)
     fc1 = 2816 * 2048 // 2 + 2816 * 32 * 2
     fc2 = 2048 * 1408 // 2 + 2048 * 22 * 2
     r = lambda v: (v + 255) // 256 * 256
-    assert n == 256 + 64 * (r(2816 * 1024) + r(2816 * 32 * 2)) + 64 * (r(2048 * 704) + r(2048 * 22 * 2))
+    assert n == (256 + 64 * (r(2816 * 1024) + r(2816 * 32 * 2)) + 64 * (r(2048 * 704) + r(2048 * 22 * 2))
+                 + r(2 * 64 * 4))
     assert n >= 64 * (fc1 + fc2)
 
 
@@ -87,7 +89,7 @@ def test_forward_validation_before_launch():
     d = _desc()
     L = q.lib()
     fake = C.c_void_p(0x100000)  # never dereferenced: every case fails validation first
-    ws_need = q.workspace_size(d, 4, 6)
+    ws_need = q.forward_plan(d, 4, 6)["workspace_bytes"]  # what this call's path needs
     # null pointers
     st = L.qmoe_forward(C.byref(d), None, fake, fake, 4, 6, fake, fake, ws_need, None)
     assert st == 1
@@ -98,7 +100,7 @@ def test_forward_validation_before_launch():
     st = L.qmoe_forward(C.byref(d), fake, fake, fake, 4, 6, fake, fake, ws_need - 1, None)
     assert st == 3
     # GEMV path forced beyond 16 rows
-    opts = q.ForwardOpts(q.PATH["gemv"], 0, None, None, None, None)
+    opts = q.ForwardOpts(q.PATH["gemv"], 0, None, None, None, None, None, 0, 0)
     st = L.qmoe_forward_ex(C.byref(d), fake, fake, fake, 17, 6, fake, fake, 1 << 40, None, C.byref(opts))
     assert st == 2
     # T = 0 is a no-op even with null pointers
@@ -121,8 +123,10 @@ def test_prepack_validation():
 def test_plan_gemv_decode():
     p = q.forward_plan(_desc(), 1, 6)
     assert p["path"] == 1 and p["gemv_mmax"] == 1 and p["max_active"] == 6
-    assert p["kernels"] == ["route_expand", "gemv_fc1_swiglu", "gemv_fc2", "combine"]
+    assert p["kernels"] == ["route", "gemv_fc1_swiglu", "gemv_fc2", "combine"]
     assert p["num_launches"] == 4
+    p1 = q.forward_plan(_desc(), 1, 1)
+    assert p1["kernels"] == ["route", "gemv_fc1_swiglu", "gemv_fc2"] and p1["num_launches"] == 3
     p8 = q.forward_plan(_desc(), 8, 6)
     assert p8["gemv_mmax"] == 8 and p8["max_active"] == 48
     p3 = q.forward_plan(_desc(), 3, 6)
@@ -150,3 +154,14 @@ def test_linear_validation():
     bad = q.qmatrix_desc("affine_int2", 128, "f16", 17400, 5120)
     with pytest.raises(q.QmoeError):
         q.linear_prepacked_size(bad)
+
+
+def test_plan_grouped_prefill():
+    d = q.layer_desc(128, 4096, 1536, "bf16", ("sym_int2", 64, "bf16"), ("sym_int4", 64, "bf16"))
+    p = q.forward_plan(d, 2048, 8)
+    assert p["path"] == 2
+    assert p["kernels"] == ["route", "rowscale", "grouped_fc1_swiglu", "grouped_fc2", "combine"]
+    assert p["num_launches"] == 6
+    pg = q.forward_plan(_desc(), 4, 6, path="grouped")
+    assert pg["path"] == 2 and pg["num_launches"] == 5
+    assert q.workspace_size(d, 2048, 8) >= p["workspace_bytes"]

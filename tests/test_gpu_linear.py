@@ -117,3 +117,22 @@ def test_dense_unpack_bit_exact(N):
     sl = slice(0, N) if N < 100000 else slice(N - 4096, N)
     ref, nbad = oracle.unpack_codes("affine_int2", w["codes"][sl], got[sl].shape[0], DENSE.K)
     assert nbad == 0 and np.array_equal(got[sl], ref)
+
+
+@pytest.mark.parametrize("M", [17, 32, 64])
+def test_dense_affine2_17408_mfma(M):
+    run_linear(DENSE, 17408, M)
+
+
+def test_dense_affine2_248320_m32_sampled_rows():
+    N = 248320
+    run_linear(DENSE, N, 32, rows=[(0, 512), (123904, 124416), (N - 512, N)])
+
+
+@pytest.mark.parametrize("fmt,block,sd,ad", [
+    ("sym_int4", 64, "bf16", "bf16"), ("sym_int2", 64, "bf16", "f16"), ("ternary", 128, "f16", "bf16"),
+    ("affine_int4", 128, "bf16", "f16"), ("affine_int2", 64, "bf16", "bf16")])
+@pytest.mark.parametrize("M", [1, 7, 40])
+def test_linear_sweep_mfma(fmt, block, sd, ad, M):
+    spec = custom_linear_spec(1024, fmt=fmt, block=block, scale_dtype=sd, act_dtype=ad)
+    run_linear(spec, 320, M, seed=M + 50, path="grouped")

@@ -71,14 +71,18 @@ def run_case(spec, T, seed, logits_mode="iid", path="auto", tokens=None):
         ids, w = ids[tokens], w[tokens]
         h = h.reshape(T, spec.top_k, spec.I)[tokens].reshape(-1, spec.I)
     assert np.array_equal(ids, r["ids"]), "routing ids differ"
-    if tokens is None:
-        assert np.array_equal(dbg["counts"].cpu().numpy(), r["counts"]), "counts differ"
+    full = r if tokens is None else oracle.route(inp["logits"], spec.top_k)
+    assert np.array_equal(dbg["counts"].cpu().numpy(), full["counts"]), "counts differ"
+    if tokens is not None:
+        assert np.array_equal(dbg["ids"].cpu().numpy(), full["ids"]), "routing ids differ"
     assert np.allclose(w, r["w"], rtol=2e-6, atol=1e-7), "routing weights"
     hn = np.linalg.norm(h - ref["h"], axis=1) / np.maximum(np.linalg.norm(ref["h"], axis=1), 1e-30)
     res = compare(ybits, ref["y"], ref["y64"], spec.act_dtype)
     log(f"       y: max_row_rel={res['max_row_rel']:.3e} identical={res['frac_identical']:.4f} "
         f"vs_exact={res['max_row_rel_vs_exact']:.3e} h_rel={hn.max():.3e}")
-    assert hn.max() < 1e-3, f"h row error {hn.max()}"
+    # h is a diagnostic (the gate is y): the MFMA path rounds weights of
+    # 4-bit affine codes or f16 scales once to f16, about 2^-11 relative
+    assert hn.max() < 4e-3, f"h row error {hn.max()}"
     assert res["ok"], res
     return res
 
@@ -218,3 +222,33 @@ def test_route_bit_exact(T, E, k, ties):
     if k == 1:
         assert np.all(got["w"] == 1.0)
     log(f"[route] T={T} E={E} k={k} ties={ties} bit-exact")
+
+
+# ----------------------------------------------------------- grouped MFMA path
+@pytest.mark.parametrize("cfg", SWEEP, ids=lambda c: "-".join(f"{k}{v}" for k, v in c.items()))
+@pytest.mark.parametrize("T", [1, 5, 16, 33])
+def test_sweep_grouped(cfg, T):
+    run_case(custom_moe_spec(**cfg), T, seed=T + 100, path="grouped")
+
+
+@pytest.mark.parametrize("name,T", [("single_expert_int4", 1), ("switch_base_ternary", 1), ("dsv2lite_int4", 8)])
+def test_workloads_grouped_path(name, T):
+    run_case(synth.MOE_WORKLOADS[name], T, 0, path="grouped")
+
+
+def test_dsv2lite_shared_logits_grouped_T32():
+    """32 rows per selected expert through the MFMA tiles."""
+    run_case(synth.MOE_WORKLOADS["dsv2lite_int4"], 32, 0, logits_mode="shared")
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_mixed_int2_int4_prefill(seed):
+    """2048 tokens, 128 experts, top-8, skewed load: routing checked on every
+    token, outputs on a sample of tokens (the oracle computes them one by one)."""
+    spec = synth.MOE_WORKLOADS["mixed_int2_int4_prefill"]
+    rng = np.random.default_rng(seed)
+    sample = np.sort(rng.choice(2048, size=12, replace=False)).tolist()
+    res = run_case(spec, 2048, seed, tokens=sample)
+    inp = _inputs(spec, 2048, seed)
+    r = oracle.route(inp["logits"], spec.top_k)
+    log(f"       expert rows: max {r['counts'].max()} min {r['counts'].min()} (mean {r['counts'].mean():.0f})")
