@@ -57,6 +57,8 @@ def parse():
     ap.add_argument("--no-extras", action="store_true", help="skip the M-sweep / other workloads")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a plain 256 MiB device copy (counter calibration under rocprofv3)")
     return ap.parse_args()
 
 
@@ -200,8 +202,11 @@ class MoeBench:
         torch.cuda.synchronize()
         return (cnt > 0).sum(1).cpu().numpy()
 
-    def stage_times(self):
-        """Average duration (ms) of each plan stage over the K steps, from events."""
+    def stage_times(self, chunk=64):
+        """Average duration (ms) of each plan stage over the K steps, from events
+        recorded on the launch stream around every stage.  Each chunk of steps is
+        queued behind a GPU sleep so the stages run back to back, as in the graph,
+        instead of waiting on the host between launches."""
         import torch
         nst = (4 if self.spec.top_k > 1 else 3) if self.T <= 16 else 5
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * nst)] for _ in range(self.K)]
@@ -209,8 +214,18 @@ class MoeBench:
             for e in row:
                 e.record()
         torch.cuda.synchronize()
-        for i, s in enumerate(range(self.W, self.W + self.K)):
-            self.step(s, events=[e.cuda_event for e in evs[i]])
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        torch.cuda._sleep(1 << 20)
+        b.record()
+        torch.cuda.synchronize()
+        # Enough sleep to cover the host's enqueue of one chunk (~40 us per step).
+        cycles = int((1 << 20) * max(1.0, chunk * 0.04 / max(a.elapsed_time(b), 1e-3)))
+        steps = list(range(self.W, self.W + self.K))
+        for c0 in range(0, self.K, chunk):
+            torch.cuda._sleep(cycles)
+            for i in range(c0, min(self.K, c0 + chunk)):
+                self.step(steps[i], events=[e.cuda_event for e in evs[i]])
         torch.cuda.synchronize()
         out = np.zeros(nst)
         for row in evs:
@@ -345,6 +360,13 @@ def main():
                      "algorithmic_bytes_per_launch": head["fc1_bytes_per_launch"]},
         "stage_us": head["stage_us"],
     }
+    if args.copy_probe:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(b, args.cpu_seconds)
     del b, layers
