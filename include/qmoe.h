@@ -138,7 +138,7 @@ typedef struct qmoe_forward_opts {
 typedef struct qmoe_plan {
   int32_t path;          /* the path actually taken */
   int32_t num_launches;  /* kernels enqueued per call */
-  int32_t gemv_mmax;     /* GEMV path: register accumulators per lane (rows per expert) */
+  int32_t gemv_mmax;     /* GEMV path: bound on the rows of one expert the kernels are built for */
   int32_t gemv_fc1_waves;  /* GEMV path: waves per workgroup (K split) of FC1 */
   int32_t gemv_fc2_waves;
   int32_t max_active;    /* upper bound of active experts the grids are sized for */

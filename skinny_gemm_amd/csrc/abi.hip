@@ -9,6 +9,7 @@
 // error instead of a silent fallback for anything outside that scope.
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <algorithm>
@@ -164,37 +165,60 @@ struct MoeWs {
 };
 
 // ------------------------------------------------------------------ plan
-constexpr size_t kLdsLimit = 64 * 1024;
-constexpr int kTargetWaves = 2048;  // ~8 waves per CU on 256 CUs
+constexpr size_t kLdsLimit = kGemvLdsLimit;
 
-int pick_mmax(int64_t rows) {
-  int m = 1;
-  while (m < rows && m < kGemvMaxRows) m <<= 1;
-  return m;
+// Waves on the chip that a GEMV launch aims for when the kernel's occupancy
+// is unknown; the environment variable QMOE_GEMV_TARGET_WAVES overrides it.
+int64_t gemv_target_waves() {
+  const char *e = getenv("QMOE_GEMV_TARGET_WAVES");
+  const long long x = e ? atoll(e) : 0;
+  return x > 0 ? (int64_t)x : (int64_t)4096;
 }
 
-// Waves per workgroup for the split-K GEMV: enough waves to hold every
-// block of a row group in one load batch, and enough waves on the chip to
-// cover HBM latency; at most 8 waves and one block per wave, within the LDS
-// budget.
-int pick_waves(int64_t nwg, int64_t nblk, int cpb, int mmax, int64_t K, int parts) {
-  const int64_t bpw = gemv_blocks_per_batch(cpb);
-  int64_t ks = std::max<int64_t>((nblk + bpw - 1) / bpw, (kTargetWaves + nwg - 1) / std::max<int64_t>(nwg, 1));
-  ks = std::max<int64_t>(1, std::min<int64_t>(ks, 8));
-  ks = std::min<int64_t>(ks, nblk);
-  while (ks > 1 && gemv_lds_bytes(mmax, nblk, (int)ks, K, parts) > kLdsLimit) --ks;
-  if (gemv_lds_bytes(mmax, nblk, (int)ks, K, parts) > kLdsLimit) return 0;
-  return (int)ks;
-}
-
-// Row-count bound of a GEMV launch and its waves; a bound whose staged
-// activations do not fit in LDS moves to the next (scalar-load) variant.
-bool pick_gemv(int64_t rows, int64_t nwg, const MatLayout &L, int parts, int &mmax, int &ks) {
-  for (mmax = pick_mmax(rows); mmax <= kGemvMaxRows; mmax *= 2) {
-    ks = pick_waves(nwg, L.nblk, L.cpb, mmax, L.K, parts);
-    if (ks > 0) return true;
+// Compute units of the current device (256 on MI355X when there is none).
+int device_cus() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+    (void)hipGetLastError();
+    return 256;
   }
-  return false;
+  return n;
+}
+
+// Waves per workgroup of the split-K GEMV (at most one per k-tile and
+// kGemvMaxWaves).  With the kernel's occupancy known, the choice minimises
+// the critical path: rounds of resident workgroups x k-tiles per wave (ties
+// to fewer waves).  Without it (no device), enough waves on the chip to
+// cover HBM latency.  nwg: workgroups of the launch; rows: its row bound.
+int pick_waves(int64_t nwg, const MatLayout &L, int rows, int epilogue, int in_f16) {
+  const int64_t kmax = std::min<int64_t>(kGemvMaxWaves, L.NKT);
+  if (const char *e = getenv("QMOE_GEMV_WAVES")) {  // tuning override
+    const long long w = atoll(e);
+    if (w > 0) return (int)std::min<int64_t>(w, kmax);
+  }
+  const int64_t cus = device_cus();
+  int best = 0;
+  int64_t best_cost = 0;
+  for (int ks = 1; ks <= kmax; ++ks) {
+    if (gemv_lds_bytes(rows, epilogue, ks) > kLdsLimit) break;
+    const int per_cu = gemv_blocks_per_cu(L.qtype, epilogue, in_f16, rows, ks, L.block);
+    if (per_cu <= 0) {
+      best = 0;
+      break;
+    }
+    const int64_t rounds = (nwg + cus * per_cu - 1) / (cus * per_cu);
+    const int64_t cost = rounds * ((L.NKT + ks - 1) / ks);
+    if (best == 0 || cost < best_cost) {
+      best = ks;
+      best_cost = cost;
+    }
+  }
+  if (best > 0) return best;
+  int64_t ks = (gemv_target_waves() + nwg - 1) / std::max<int64_t>(nwg, 1);
+  ks = std::max<int64_t>(1, std::min<int64_t>(ks, kmax));
+  while (ks > 1 && gemv_lds_bytes(rows, epilogue, (int)ks) > kLdsLimit) --ks;
+  return (int)ks;
 }
 
 struct Plan {
@@ -229,10 +253,9 @@ qmoe_status make_plan(const qmoe_layer_desc &d, int32_t T, int32_t k, int path_r
   }
   p.route_fused = (T <= 16) ? 1 : 0;
   p.max_active = (int)std::min<int64_t>(d.num_experts, (int64_t)T * k);
-  if (!pick_gemv(T, (int64_t)p.max_active * L.fc1.RG, L.fc1, 1, p.mmax1, p.ks1) ||
-      !pick_gemv(T, (int64_t)p.max_active * L.fc2.RG, L.fc2, 2, p.mmax2, p.ks2))
-    return fail(QMOE_ERR_UNSUPPORTED, "K too large for the GEMV workgroup LDS budget");
-  p.mmax = p.mmax1;
+  p.mmax = p.mmax1 = p.mmax2 = T;  // no expert gets more rows than there are tokens
+  p.ks1 = pick_waves((int64_t)p.max_active * L.fc1.RG, L.fc1, T, kEpiSwiGLU, d.act_dtype == QMOE_DTYPE_F16);
+  p.ks2 = pick_waves((int64_t)p.max_active * L.fc2.RG, L.fc2, T, kEpiDown, 0);
   // top-1: the down GEMV writes y; otherwise a combine kernel follows
   p.kernels = k == 1 ? "route,gemv_fc1_swiglu,gemv_fc2" : "route,gemv_fc1_swiglu,gemv_fc2,combine";
   p.launches = k == 1 ? 3 : 4;
@@ -254,10 +277,12 @@ GroupedArgs grouped_base(const MatLayout &L, const uint8_t *w, const float *wsc)
   g.K = L.K;
   g.RG = L.RG;
   g.NC = L.NC;
+  g.NKT = L.NKT;
   g.nblk = L.nblk;
   g.qtype = L.qtype;
   g.sdtype = L.sdtype;
   g.block = L.block;
+  g.bpk = L.bpk;
   g.wsc = wsc;
   return g;
 }
@@ -283,9 +308,8 @@ GemvArgs gemv_base(const MatLayout &L, const uint8_t *w) {
   g.K = L.K;
   g.RG = L.RG;
   g.NC = L.NC;
+  g.NKT = L.NKT;
   g.nblk = L.nblk;
-  g.cpb = L.cpb;
-  g.kc = L.kc;
   g.qtype = L.qtype;
   g.sdtype = L.sdtype;
   return g;
@@ -494,7 +518,8 @@ qmoe_status qmoe_forward_ex(const qmoe_layer_desc *desc, const void *packed, con
   g1.h_dbg = opts ? opts->h_out : nullptr;
   e = rec(2);
   if (e == hipSuccess)
-    e = launch_gemv(g1, kEpiSwiGLU, desc->act_dtype == QMOE_DTYPE_F16, p.mmax1, p.ks1, p.max_active, s);
+    e = launch_gemv(g1, kEpiSwiGLU, desc->act_dtype == QMOE_DTYPE_F16, p.mmax1, p.ks1, L.fc1.block,
+                    p.max_active, s);
   if (e == hipSuccess) e = rec(3);
   if (e != hipSuccess) return hip_status(e, "gemv fc1");
 
@@ -512,7 +537,7 @@ qmoe_status qmoe_forward_ex(const qmoe_layer_desc *desc, const void *packed, con
   g2.act_dtype = desc->act_dtype;
   g2.route_w = ra.r.w;
   e = rec(4);
-  if (e == hipSuccess) e = launch_gemv(g2, kEpiDown, 0, p.mmax2, p.ks2, p.max_active, s);
+  if (e == hipSuccess) e = launch_gemv(g2, kEpiDown, 0, p.mmax2, p.ks2, L.fc2.block, p.max_active, s);
   if (e == hipSuccess) e = rec(5);
   if (e != hipSuccess) return hip_status(e, "gemv fc2");
   if (top_k > 1) {
@@ -658,9 +683,9 @@ qmoe_status qmoe_linear(const qmoe_qmatrix_desc *desc, const void *packed, const
   if (M == 0) return ok();
   if (path != QMOE_PATH_AUTO && path != QMOE_PATH_GEMV && path != QMOE_PATH_GROUPED)
     return fail(QMOE_ERR_INVALID_ARGUMENT, "unknown path %d", path);
-  const int pth = path == QMOE_PATH_AUTO ? (M <= kGemvMaxRows ? QMOE_PATH_GEMV : QMOE_PATH_GROUPED) : path;
-  if (pth == QMOE_PATH_GEMV && M > kGemvMaxRows)
-    return fail(QMOE_ERR_UNSUPPORTED, "GEMV path needs M <= %d", kGemvMaxRows);
+  const int pth = path == QMOE_PATH_AUTO ? (M <= kGemvMaxRowsDense ? QMOE_PATH_GEMV : QMOE_PATH_GROUPED) : path;
+  if (pth == QMOE_PATH_GEMV && M > kGemvMaxRowsDense)
+    return fail(QMOE_ERR_UNSUPPORTED, "GEMV path needs M <= %d", kGemvMaxRowsDense);
   if (!packed || !x || !y) return fail(QMOE_ERR_INVALID_ARGUMENT, "null device pointer");
   if (!aligned(packed, kAlign) || !aligned(x, 16) || !aligned(y, 16))
     return fail(QMOE_ERR_INVALID_ARGUMENT, "misaligned pointer");
@@ -689,16 +714,15 @@ qmoe_status qmoe_linear(const qmoe_qmatrix_desc *desc, const void *packed, const
     g.act_dtype = x_dtype;
     return hip_status(launch_grouped(g, kGEpiStoreAct, (M + kTileM - 1) / kTileM, s), "linear mfma");
   }
-  int mmax = 0, ks = 0;
-  if (!pick_gemv(M, L.RG, L, 1, mmax, ks))
-    return fail(QMOE_ERR_UNSUPPORTED, "K too large for the GEMV workgroup LDS budget");
+  const int ks = pick_waves(L.RG, L, M, kEpiStoreAct, x_dtype == QMOE_DTYPE_F16);
   GemvArgs g = gemv_base(L, (const uint8_t *)packed);
   g.dense_M = M;
   g.in = (const uint32_t *)x;
   g.in_row_pairs = L.K / 2;
   g.out_act = (uint16_t *)y;
   g.act_dtype = x_dtype;
-  return hip_status(launch_gemv(g, kEpiStoreAct, x_dtype == QMOE_DTYPE_F16, mmax, ks, 1, s), "linear gemv");
+  return hip_status(launch_gemv(g, kEpiStoreAct, x_dtype == QMOE_DTYPE_F16, M, ks, L.block, 1, s),
+                    "linear gemv");
 }
 
 qmoe_status qmoe_linear_unpack_codes(const qmoe_qmatrix_desc *desc, const void *packed,

@@ -4,11 +4,11 @@
 // a field u written into mantissa bits [p, p+bits) into the exact value
 // base + u ("magic number" conversion): one AND-OR per two weights, because
 // the prepack puts weight 2j of a dword in the low half-word and weight 2j+1
-// at the same offset of the high half-word.  The resulting pair feeds
-// v_dot2_f32_{bf16,f16} against an activation pair, so a dot product over a
-// block yields sum_k (base_k + u_k) x_k; the block epilogue subtracts
-// sum_k (base_k + zero_point) x_k, which depends on the activations only and
-// is computed once per row and block (see gemv.hip).
+// at the same offset of the high half-word.  The resulting pairs are exact
+// 16-bit float operands of the matrix cores, so a dot product over a block
+// yields sum_k (base_k + u_k) x_k; the block epilogue subtracts
+// sum_k (base_k + zero_point) x_k, which depends on the activations only
+// (gemv_impl.hpp).
 //
 // Field positions and bases (bits of each half-word; p = mantissa bit offset):
 //   4-bit, bf16 pairs: pair j from (w >> 4j), field at bits 0..3, base 128
@@ -40,20 +40,68 @@ __device__ __forceinline__ void static_for(F &&f) {
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 
+// Masks and float constants of a decoder held in registers.  CDNA VOP3
+// encodings take no 32-bit literal, so with literal masks the compiler splits
+// (x & m) | c into v_and_b32 + v_or_b32; once the constants are opaque
+// register values (an empty asm statement that touches only the constant
+// itself) it selects one v_and_or_b32 per weight pair, and its own wait
+// counting stays in charge of every loaded register.
+template <int N>
+struct RegConsts {
+  uint32_t m[N], c[N];
+};
+__device__ inline uint32_t opaque_s(uint32_t v) {
+  asm volatile("" : "+s"(v));
+  return v;
+}
+__device__ inline uint32_t opaque_v(uint32_t v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
 template <int BITS, bool F16>
 struct Codec;
+
+// Every decoder: kNC (mask, constant) pairs; extract(w, p, k) decodes one
+// dword into kPairs 16-bit float pairs with (x & m) | c per pair, from the
+// constants k (literal by default, or opaque registers for the GEMV).
+template <typename CD>
+struct CodecOps {
+  __device__ static inline RegConsts<CD::kNC> literal() {
+    RegConsts<CD::kNC> k;
+#pragma unroll
+    for (int i = 0; i < CD::kNC; ++i) {
+      k.m[i] = CD::kM[i];
+      k.c[i] = CD::kC[i];
+    }
+    return k;
+  }
+  __device__ static inline RegConsts<CD::kNC> in_registers() {
+    RegConsts<CD::kNC> k;
+#pragma unroll
+    for (int i = 0; i < CD::kNC; ++i) {
+      k.m[i] = opaque_s(CD::kM[i]);
+      k.c[i] = opaque_v(CD::kC[i]);
+    }
+    return k;
+  }
+};
 
 template <>
 struct Codec<4, false> {
   static constexpr int kPairs = 4;  // pairs per dword
   static constexpr int kPeriod = 8; // weights per dword
+  static constexpr int kNC = 1;
+  static constexpr uint32_t kM[kNC] = {0x000F000Fu}, kC[kNC] = {0x43004300u};  // bits 0-3 -> 128 + u
   __host__ __device__ static constexpr float base(int) { return 128.f; }
+  __device__ static inline void extract(uint32_t w, uint32_t (&p)[kPairs], const RegConsts<kNC> &k) {
+    p[0] = (w & k.m[0]) | k.c[0];
+    p[1] = ((w >> 4) & k.m[0]) | k.c[0];
+    p[2] = ((w >> 8) & k.m[0]) | k.c[0];
+    p[3] = ((w >> 12) & k.m[0]) | k.c[0];
+  }
   __device__ static inline void extract(uint32_t w, uint32_t (&p)[kPairs]) {
-    constexpr uint32_t M = 0x000F000Fu, C = 0x43004300u;
-    p[0] = (w & M) | C;
-    p[1] = ((w >> 4) & M) | C;
-    p[2] = ((w >> 8) & M) | C;
-    p[3] = ((w >> 12) & M) | C;
+    extract(w, p, CodecOps<Codec>::literal());
   }
 };
 
@@ -61,13 +109,17 @@ template <>
 struct Codec<4, true> {
   static constexpr int kPairs = 4;
   static constexpr int kPeriod = 8;
+  static constexpr int kNC = 1;
+  static constexpr uint32_t kM[kNC] = {0x03C003C0u}, kC[kNC] = {0x4C004C00u};  // bits 6-9 -> 16 + u
   __host__ __device__ static constexpr float base(int) { return 16.f; }
+  __device__ static inline void extract(uint32_t w, uint32_t (&p)[kPairs], const RegConsts<kNC> &k) {
+    p[0] = ((w << 6) & k.m[0]) | k.c[0];
+    p[1] = ((w << 2) & k.m[0]) | k.c[0];
+    p[2] = ((w >> 2) & k.m[0]) | k.c[0];
+    p[3] = ((w >> 6) & k.m[0]) | k.c[0];
+  }
   __device__ static inline void extract(uint32_t w, uint32_t (&p)[kPairs]) {
-    constexpr uint32_t M = 0x03C003C0u, C = 0x4C004C00u;
-    p[0] = ((w << 6) & M) | C;
-    p[1] = ((w << 2) & M) | C;
-    p[2] = ((w >> 2) & M) | C;
-    p[3] = ((w >> 6) & M) | C;
+    extract(w, p, CodecOps<Codec>::literal());
   }
 };
 
@@ -75,22 +127,26 @@ template <>
 struct Codec<2, false> {
   static constexpr int kPairs = 8;
   static constexpr int kPeriod = 16;
+  static constexpr int kNC = 3;
+  // bits 0-1 -> 128 + u, bits 2-3 -> 32 + u, bits 4-5 -> 8 + u
+  static constexpr uint32_t kM[kNC] = {0x00030003u, 0x000C000Cu, 0x00300030u};
+  static constexpr uint32_t kC[kNC] = {0x43004300u, 0x42004200u, 0x41004100u};
   __host__ __device__ static constexpr float base(int j) {
     return (j % 3 == 0) ? 128.f : (j % 3 == 1) ? 32.f : 8.f;
   }
-  __device__ static inline void extract(uint32_t w, uint32_t (&p)[kPairs]) {
-    constexpr uint32_t M0 = 0x00030003u, C0 = 0x43004300u;  // bits 0-1 -> 128 + u
-    constexpr uint32_t M1 = 0x000C000Cu, C1 = 0x42004200u;  // bits 2-3 ->  32 + u
-    constexpr uint32_t M2 = 0x00300030u, C2 = 0x41004100u;  // bits 4-5 ->   8 + u
+  __device__ static inline void extract(uint32_t w, uint32_t (&p)[kPairs], const RegConsts<kNC> &k) {
     const uint32_t w6 = w >> 6, w12 = w >> 12;
-    p[0] = (w & M0) | C0;
-    p[1] = (w & M1) | C1;
-    p[2] = (w & M2) | C2;
-    p[3] = (w6 & M0) | C0;
-    p[4] = (w6 & M1) | C1;
-    p[5] = (w6 & M2) | C2;
-    p[6] = (w12 & M0) | C0;
-    p[7] = (w12 & M1) | C1;
+    p[0] = (w & k.m[0]) | k.c[0];
+    p[1] = (w & k.m[1]) | k.c[1];
+    p[2] = (w & k.m[2]) | k.c[2];
+    p[3] = (w6 & k.m[0]) | k.c[0];
+    p[4] = (w6 & k.m[1]) | k.c[1];
+    p[5] = (w6 & k.m[2]) | k.c[2];
+    p[6] = (w12 & k.m[0]) | k.c[0];
+    p[7] = (w12 & k.m[1]) | k.c[1];
+  }
+  __device__ static inline void extract(uint32_t w, uint32_t (&p)[kPairs]) {
+    extract(w, p, CodecOps<Codec>::literal());
   }
 };
 
@@ -98,23 +154,26 @@ template <>
 struct Codec<2, true> {
   static constexpr int kPairs = 8;
   static constexpr int kPeriod = 16;
+  static constexpr int kNC = 4;
+  // bits 2-3 -> 256 + u, 4-5 -> 64 + u, 6-7 -> 16 + u, 8-9 -> 4 + u
+  static constexpr uint32_t kM[kNC] = {0x000C000Cu, 0x00300030u, 0x00C000C0u, 0x03000300u};
+  static constexpr uint32_t kC[kNC] = {0x5C005C00u, 0x54005400u, 0x4C004C00u, 0x44004400u};
   __host__ __device__ static constexpr float base(int j) {
     return (j % 4 == 0) ? 256.f : (j % 4 == 1) ? 64.f : (j % 4 == 2) ? 16.f : 4.f;
   }
-  __device__ static inline void extract(uint32_t w, uint32_t (&p)[kPairs]) {
-    constexpr uint32_t M0 = 0x000C000Cu, C0 = 0x5C005C00u;  // bits 2-3 -> 256 + u
-    constexpr uint32_t M1 = 0x00300030u, C1 = 0x54005400u;  // bits 4-5 ->  64 + u
-    constexpr uint32_t M2 = 0x00C000C0u, C2 = 0x4C004C00u;  // bits 6-7 ->  16 + u
-    constexpr uint32_t M3 = 0x03000300u, C3 = 0x44004400u;  // bits 8-9 ->   4 + u
+  __device__ static inline void extract(uint32_t w, uint32_t (&p)[kPairs], const RegConsts<kNC> &k) {
     const uint32_t a = w << 2, b = w >> 6;
-    p[0] = (a & M0) | C0;
-    p[1] = (a & M1) | C1;
-    p[2] = (a & M2) | C2;
-    p[3] = (a & M3) | C3;
-    p[4] = (b & M0) | C0;
-    p[5] = (b & M1) | C1;
-    p[6] = (b & M2) | C2;
-    p[7] = (b & M3) | C3;
+    p[0] = (a & k.m[0]) | k.c[0];
+    p[1] = (a & k.m[1]) | k.c[1];
+    p[2] = (a & k.m[2]) | k.c[2];
+    p[3] = (a & k.m[3]) | k.c[3];
+    p[4] = (b & k.m[0]) | k.c[0];
+    p[5] = (b & k.m[1]) | k.c[1];
+    p[6] = (b & k.m[2]) | k.c[2];
+    p[7] = (b & k.m[3]) | k.c[3];
+  }
+  __device__ static inline void extract(uint32_t w, uint32_t (&p)[kPairs]) {
+    extract(w, p, CodecOps<Codec>::literal());
   }
 };
 

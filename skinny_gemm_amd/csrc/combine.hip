@@ -6,6 +6,10 @@
 // ascending j from 0, rounded once to nearest-even in the activation dtype.
 // o holds the per-slot FC2 outputs in expert-sorted order; pos is the
 // inverse of the row list.
+#include <map>
+#include <mutex>
+#include <tuple>
+
 #include "codec.hpp"
 #include "qmoe_internal.h"
 
@@ -44,22 +48,53 @@ hipError_t launch_combine(const float *o, const int32_t *slot_pos, const float *
   return hipGetLastError();
 }
 
-hipError_t launch_gemv_sym_int4(const GemvArgs &, int, int, int, int, int, hipStream_t);
-hipError_t launch_gemv_sym_int2(const GemvArgs &, int, int, int, int, int, hipStream_t);
-hipError_t launch_gemv_ternary(const GemvArgs &, int, int, int, int, int, hipStream_t);
-hipError_t launch_gemv_affine_int2(const GemvArgs &, int, int, int, int, int, hipStream_t);
-hipError_t launch_gemv_affine_int4(const GemvArgs &, int, int, int, int, int, hipStream_t);
+const void *gemv_ptr_sym_int4(int, int, int, int);
+const void *gemv_ptr_sym_int2(int, int, int, int);
+const void *gemv_ptr_ternary(int, int, int, int);
+const void *gemv_ptr_affine_int2(int, int, int, int);
+const void *gemv_ptr_affine_int4(int, int, int, int);
 
-hipError_t launch_gemv(const GemvArgs &a, int epilogue, int in_f16, int mmax, int waves,
-                       int grid_slots, hipStream_t s) {
-  switch (a.qtype) {
-    case QMOE_QTYPE_SYM_INT4: return launch_gemv_sym_int4(a, epilogue, in_f16, mmax, waves, grid_slots, s);
-    case QMOE_QTYPE_SYM_INT2: return launch_gemv_sym_int2(a, epilogue, in_f16, mmax, waves, grid_slots, s);
-    case QMOE_QTYPE_TERNARY: return launch_gemv_ternary(a, epilogue, in_f16, mmax, waves, grid_slots, s);
-    case QMOE_QTYPE_AFFINE_INT2:
-      return launch_gemv_affine_int2(a, epilogue, in_f16, mmax, waves, grid_slots, s);
-    default: return launch_gemv_affine_int4(a, epilogue, in_f16, mmax, waves, grid_slots, s);
+const void *gemv_kernel_ptr(int qtype, int epilogue, int in_f16, int rows, int block) {
+  switch (qtype) {
+    case QMOE_QTYPE_SYM_INT4: return gemv_ptr_sym_int4(epilogue, in_f16, rows, block);
+    case QMOE_QTYPE_SYM_INT2: return gemv_ptr_sym_int2(epilogue, in_f16, rows, block);
+    case QMOE_QTYPE_TERNARY: return gemv_ptr_ternary(epilogue, in_f16, rows, block);
+    case QMOE_QTYPE_AFFINE_INT2: return gemv_ptr_affine_int2(epilogue, in_f16, rows, block);
+    default: return gemv_ptr_affine_int4(epilogue, in_f16, rows, block);
   }
+}
+
+hipError_t launch_gemv(const GemvArgs &a, int epilogue, int in_f16, int rows, int waves, int block,
+                       int grid_slots, hipStream_t s) {
+  const void *fn = gemv_kernel_ptr(a.qtype, epilogue, in_f16, rows, block);
+  GemvArgs args = a;
+  void *kargs[] = {&args};
+  return hipLaunchKernel(fn, dim3((unsigned)(grid_slots * a.RG)), dim3((unsigned)(waves * kLanes)), kargs,
+                         gemv_lds_bytes(rows, epilogue, waves), s);
+}
+
+int gemv_blocks_per_cu(int qtype, int epilogue, int in_f16, int rows, int waves, int block) {
+  const void *fn = gemv_kernel_ptr(qtype, epilogue, in_f16, rows, block);
+  const size_t lds = gemv_lds_bytes(rows, epilogue, waves);
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  // the runtime query is not free: remember it per (device, kernel, waves)
+  static std::mutex mu;
+  static std::map<std::tuple<int, const void *, int, size_t>, int> cache;
+  const auto key = std::make_tuple(dev, fn, waves, lds);
+  {
+    std::lock_guard<std::mutex> g(mu);
+    const auto it = cache.find(key);
+    if (it != cache.end()) return it->second;
+  }
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, waves * kLanes, lds) != hipSuccess) {
+    (void)hipGetLastError();
+    n = 0;
+  }
+  std::lock_guard<std::mutex> g(mu);
+  cache[key] = n;
+  return n;
 }
 
 }  // namespace qmoe

@@ -3,9 +3,8 @@
 
 namespace qmoe {
 
-hipError_t launch_gemv_affine_int4(const GemvArgs &a, int epilogue, int in_f16, int mmax, int waves,
-                          int grid_slots, hipStream_t s) {
-  return launch_gemv_qt<QMOE_QTYPE_AFFINE_INT4>(a, epilogue, in_f16, mmax, waves, grid_slots, s);
+const void *gemv_ptr_affine_int4(int epilogue, int in_f16, int rows, int block) {
+  return gemv_ptr_qt<QMOE_QTYPE_AFFINE_INT4>(epilogue, in_f16, rows, block);
 }
 
 }  // namespace qmoe

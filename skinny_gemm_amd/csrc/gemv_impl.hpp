@@ -1,32 +1,40 @@
-// gemv_impl.hpp -- register-accumulator quantized GEMV for M <= 16 rows.
+// gemv_impl.hpp -- quantized GEMV for up to 16 rows per expert (32 dense rows)
+// on the matrix cores.
 //
 // Computes out[m][n] = sum_k W[n][k] * in[m][k] for the rows m routed to one
 // expert (or M dense rows), dequantizing every weight chunk once in VGPRs and
-// applying it to all M rows held in per-lane accumulators.  This is the
-// register-level answer to the per-token GEMV problem of the inference-research
-// gotcha page on QMoE ("The QMoE sub-1-bit expert kernel is a GEMV ...": loop
+// applying it to all rows at once.  This is the register-level answer to the
+// per-token GEMV problem of the inference-research gotcha page on QMoE (loop
 // over the tokens that share an expert inside the kernel instead of one GEMV
 // per token) and the fused gate/up SwiGLU expert GEMV + down GEMV of
 // onnx-genai pull request 1167.
 //
-// gfx950 mapping (the pages' designs use one warp per row; here):
-//   - one output row per lane, 64 rows per wavefront: every chunk load of the
-//     prepacked layout is a 1 KiB contiguous read of 16 B per lane;
-//   - the activations are the same for all lanes of a wave: for up to 4 rows
-//     the workgroup stages them in LDS while the weight loads are in flight
-//     and every lane reads the same address (broadcast ds_read_b128); for more
-//     rows they are read with scalar loads into SGPRs and used directly as the
-//     second operand of v_dot2_f32_{bf16,f16};
-//   - K is split over the KS wavefronts of a workgroup; each wave issues all
-//     of its weight and scale loads (up to 8 x 16 B per lane) before any
-//     use, and the partial sums meet in LDS, added in a fixed wave order;
-//   - per block: D = sum (base + u) x by dot2, acc += s * (D - C) (+ b X), with
-//     C = sum (base + zero point) x and X = sum x computed once per row and
-//     block by the workgroup while the weight loads are in flight.
+// gfx950 mapping (the pages' designs use one warp or thread group per row):
+//   - a wave owns 64 output rows (4 tiles of 16) and a contiguous run of
+//     k-tiles; per k-tile it issues four 1 KiB contiguous loads (16 B per
+//     lane) of the prepacked layout, whose lane (r, g) = (lane % 16, lane / 16)
+//     holds exactly the v_mfma_f32_16x16x32 B operand of row r for k-group g;
+//   - one AND-OR per weight pair turns the codes into exact 16-bit floats
+//     base + u (magic-number decoding, codec.hpp); the raw codes enter the
+//     MFMA unscaled, so the dequantization costs no multiply;
+//   - the activations of up to 16 rows are the A operand, read straight from
+//     global memory (they are tiny and stay in L2): one tile covers every
+//     row of an expert, so rows 2..16 cost matrix-core cycles only;
+//   - per block, fresh accumulators D = sum (base + u) x; a second MFMA
+//     against a constant B operand gives C = sum (base + zero point) x (and
+//     X = sum x for affine formats) in the same lane layout, and the block
+//     epilogue adds s (D - C) (+ b X) to the fp32 result;
+//   - K is split over the waves of a workgroup; the partial sums meet in LDS
+//     and are added in a fixed wave order.
 #pragma once
 
 #include "codec.hpp"
 #include "qmoe_internal.h"
+
+#ifndef QMOE_GEMV_PREFETCH
+#define QMOE_GEMV_PREFETCH 1
+#endif
+
 
 namespace qmoe {
 
@@ -40,23 +48,72 @@ struct QtTraits {
                                                                   : 0;
 };
 
-template <int QT, bool F16, int EPI, int MMAX, int BLOCK>
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef float floatx4_t __attribute__((ext_vector_type(4)));
+
+// v_mfma_f32_16x16x32_{bf16,f16}: c + A (16 x 32) * B (32 x 16).  Lane l
+// supplies row l % 16 of A and column l % 16 of B for k = 8 (l / 16) .. +7;
+// it receives C rows 4 (l / 16) + i, i = 0..3, of column l % 16.
+template <bool F16>
+__device__ inline floatx4_t mfma16(const uint4 &a, const uint4 &b, const floatx4_t &c) {
+  if constexpr (F16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// 16-bit float bits of a small non-negative integer v < 2048 (exact).
+template <bool F16>
+__host__ __device__ constexpr uint32_t small_int_bits(int v) {
+  if (v == 0) return 0;
+  int e = 0;
+  while ((2 << e) <= v) ++e;  // 2^e <= v < 2^(e+1)
+  if (F16) return (uint32_t)(((15 + e) << 10) | ((v - (1 << e)) << (10 - e)));
+  return (uint32_t)(((127 + e) << 7) | ((v - (1 << e)) << (7 - e)));
+}
+
+// Scales of one row for one k-tile: BYTES = blocks per k-tile x entry size.
+template <int BYTES>
+__device__ inline void load_scales(const uint8_t *p, uint32_t (&sv)[4]) {
+  if constexpr (BYTES == 16) {
+    const uint4 v = *reinterpret_cast<const uint4 *>(p);
+    sv[0] = v.x; sv[1] = v.y; sv[2] = v.z; sv[3] = v.w;
+  } else if constexpr (BYTES == 8) {
+    const uint2 v = *reinterpret_cast<const uint2 *>(p);
+    sv[0] = v.x; sv[1] = v.y; sv[2] = 0; sv[3] = 0;
+  } else if constexpr (BYTES == 4) {
+    sv[0] = *reinterpret_cast<const uint32_t *>(p); sv[1] = sv[2] = sv[3] = 0;
+  } else {
+    sv[0] = *reinterpret_cast<const uint16_t *>(p); sv[1] = sv[2] = sv[3] = 0;
+  }
+}
+
+// QT: code format; XF16: the A operand (and the decoding) is f16, else bf16;
+// PARTS: 2 = the input is an fp32 value split into bf16 hi + lo rows;
+// MR: accumulator rows kept per lane (1: a single row, 4: up to 16 rows per
+// tile); MT: 16-row tiles; BLOCK: scale block along K.
+template <int QT, bool XF16, int PARTS, int EPI, int MR, int MT, int BLOCK>
 __global__ __launch_bounds__(512) void gemv_kernel(const GemvArgs a) {
   using TR = QtTraits<QT>;
-  using CD = Codec<TR::kBits, F16>;
-  constexpr int PPD = CD::kPairs;           // pairs per dword
-  constexpr int PPC = 4 * PPD;              // pairs per 16-B chunk
-  constexpr int KC = 2 * PPC;               // weights per chunk
-  constexpr int CPB = BLOCK / KC;           // chunks per block
-  static_assert(CPB >= 1, "block smaller than a chunk");
-  constexpr int BPW = CPB >= 8 ? 1 : 8 / CPB;          // blocks per load batch (8 chunks)
-  constexpr int PARTS = (EPI == kEpiDown) ? 2 : 1;  // FC2 reads h as bf16 hi + lo
-  constexpr int EPT = BLOCK / 16;           // prologue: elements per thread per block
-  constexpr bool XLDS = MMAX <= kGemvLdsRows;  // activations staged in LDS
+  using CD = Codec<TR::kBits, XF16>;
+  constexpr int BITS = TR::kBits;
+  constexpr int KC = 128 / BITS;             // k per chunk
+  constexpr int KT = 4 * KC;                 // k per k-tile
+  constexpr int HALVES = BITS == 2 ? 2 : 1;  // MFMA k-steps per chunk
+  constexpr int KSTEPS = 4 * HALVES;         // k-steps per k-tile
+  constexpr int CPB = BLOCK / KC;            // chunks per block
+  constexpr int BPK = KT / BLOCK;            // blocks per k-tile
+  constexpr bool AFF = TR::kAffine;
+  constexpr int ESZ = AFF ? 4 : 2;
+  constexpr int ZP = TR::kZeroPoint;
+  static_assert(CPB >= 1 && BPK >= 1, "block must span whole chunks of one k-tile");
+  static_assert(MR == 4 || MT == 1, "several row tiles keep all accumulator rows");
 
-  extern __shared__ float smem[];
+  extern __shared__ float s_red[];  // [waves][4][MT][MR][64]
   const int lane = threadIdx.x & (kLanes - 1);
-  // wave index made provably uniform so activation addresses stay scalar (s_load)
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kLanes);
   const int KS = blockDim.x / kLanes;
   const int RG = (int)a.RG;
@@ -75,195 +132,207 @@ __global__ __launch_bounds__(512) void gemv_kernel(const GemvArgs a) {
     pbase = si.z;
     if (M <= 0) return;
   }
-  if (M > MMAX) M = MMAX;  // the host sizes MMAX >= every row count; the clamp keeps accesses in bounds
-  const int nblk = (int)a.nblk;
-  const int Kp = (int)(a.K / 2);               // pairs per row
-  // LDS: staged activations first (16-B aligned for ds_read_b128), then the
-  // block corrections and the cross-wave partial sums
-  uint32_t *s_x = reinterpret_cast<uint32_t *>(smem);                 // [PARTS][MMAX][Kp]
-  float *s_corr = smem + (XLDS ? PARTS * MMAX * Kp : 0);              // [MMAX][nblk][2]: C, X
-  float *s_red = s_corr + MMAX * nblk * 2;                            // [KS][MMAX][64]
+  if (M > 16 * MT) M = 16 * MT;  // the host sizes MT for every row count; the clamp keeps accesses in bounds
+  const int r = lane & 15, g = lane >> 4;
+  const int NKT = (int)a.NKT, NC = (int)a.NC;
+  const int kt0 = (int)((int64_t)wave * NKT / KS), kt1 = (int)((int64_t)(wave + 1) * NKT / KS);
 
-  // ---- 1. this wave's weight and scale loads, all issued before any use
-  const int b0 = (int)((int64_t)wave * nblk / KS);
-  const int b1 = (int)((int64_t)(wave + 1) * nblk / KS);
+  // A operand rows: lane (r, g) supplies row 16 mt + r
+  const uint32_t *arow[MT];
+  bool aval[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int m = 16 * mt + r;
+    aval[mt] = m < M;
+    int64_t row = 0;
+    if (aval[mt]) {
+      if (a.dense_M > 0) row = m;
+      else row = a.in_gather_token ? (int64_t)a.token_of[pbase + m] : (int64_t)(pbase + m);
+    }
+    arow[mt] = a.in + row * a.in_row_pairs;
+  }
+
   const uint8_t *wexp = a.w + (int64_t)e * a.expert_stride;
-  const uint4 *cptr = reinterpret_cast<const uint4 *>(wexp) + (int64_t)rg * a.NC * kLanes + lane;
-  const uint8_t *sbase = wexp + a.scales_off;
-  const int64_t sidx0 = (int64_t)rg * nblk * kLanes + lane;
-  uint4 cw[BPW * CPB];
-  uint32_t sv[BPW];
-  auto load_batch = [&](int g0) __attribute__((always_inline)) {
-    static_for<BPW>([&](auto ic) {
-      constexpr int i = decltype(ic)::value;
-      const int b = min(g0 + i, b1 - 1);  // past the end: reload the last block (unused)
-      static_for<CPB>([&](auto cc) {
-        constexpr int ci = decltype(cc)::value;
-        cw[i * CPB + ci] = cptr[((int64_t)b * CPB + ci) * kLanes];
-      });
-      if constexpr (TR::kAffine)
-        sv[i] = reinterpret_cast<const uint32_t *>(sbase)[sidx0 + (int64_t)b * kLanes];
-      else
-        sv[i] = reinterpret_cast<const uint16_t *>(sbase)[sidx0 + (int64_t)b * kLanes];
+  const uint4 *wp = reinterpret_cast<const uint4 *>(wexp) + (int64_t)rg * NKT * (4 * kLanes) + lane;
+  const uint8_t *sp = wexp + a.scales_off + ((int64_t)rg * NKT * kLanes + r) * (BPK * ESZ);
+  const bool sf16 = a.sdtype == QMOE_DTYPE_F16;
+
+  // constant B operands: (base + zero point) per k position, and ones
+  uint4 bc[HALVES];
+#pragma unroll
+  for (int h = 0; h < HALVES; ++h) {
+    uint32_t v[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t bits = small_int_bits<XF16>((int)CD::base(4 * h + q) + ZP);
+      v[q] = bits | (bits << 16);
+    }
+    bc[h] = make_uint4(v[0], v[1], v[2], v[3]);
+  }
+  constexpr uint32_t kOne = small_int_bits<XF16>(1) | (small_int_bits<XF16>(1) << 16);
+  const uint4 ones = make_uint4(kOne, kOne, kOne, kOne);
+  const floatx4_t zero = {0.f, 0.f, 0.f, 0.f};
+  const RegConsts<CD::kNC> dk = CodecOps<CD>::in_registers();  // decoder constants in registers
+
+  float out[4][MT][MR];
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int el = 0; el < MR; ++el) out[t][mt][el] = 0.f;
+
+  // One k-tile of operands: weights and scales of the 4 n-tiles, and the
+  // activation fragments of every k-step.
+  struct Tile {
+    uint4 wv[4];
+    uint32_t sv[4][4];
+    uint4 af[KSTEPS][MT][PARTS];
+  };
+  auto load_w = [&](int kt, Tile &T) __attribute__((always_inline)) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      T.wv[t] = wp[((int64_t)kt * 4 + t) * kLanes];
+      load_scales<BPK * ESZ>(sp + ((int64_t)kt * kLanes + 16 * t) * (BPK * ESZ), T.sv[t]);
+    }
+  };
+  auto load_a = [&](int kt, Tile &T) __attribute__((always_inline)) {
+    const int nch = min(4, NC - 4 * kt);
+    static_for<KSTEPS>([&](auto kc_) {
+      constexpr int ks = decltype(kc_)::value;
+      constexpr int j = ks / HALVES, h = ks % HALVES;
+      const int64_t kp = (int64_t)kt * (KT / 2) + (BITS == 2 ? (32 * j + 8 * g + 4 * h) : (16 * j + 4 * g));
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int p = 0; p < PARTS; ++p)
+          T.af[ks][mt][p] = (aval[mt] && j < nch)
+                                ? *reinterpret_cast<const uint4 *>(arow[mt] + p * a.in_part_stride + kp)
+                                : make_uint4(0, 0, 0, 0);
     });
   };
-  load_batch(b0);
-
-  auto in_row = [&](int m) -> int64_t {
-    if (a.dense_M > 0) return m;
-    const int p = pbase + m;
-    return a.in_gather_token ? (int64_t)a.token_of[p] : (int64_t)p;
-  };
-
-  // ---- 2. prologue (overlaps the loads): C and X per row and block, and the
-  //         staged activations.  Row offsets come from scalar loads and every
-  //         thread of the workgroup takes items, several loads in flight each.
-  int64_t rowoff[MMAX];
+  auto compute = [&](int kt, const Tile &T) __attribute__((always_inline)) {
+    const int nch = min(4, NC - 4 * kt);  // chunks present in this k-tile
+    floatx4_t accW[4][MT], accC[MT], accX[MT];
+    static_for<4>([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      if (j < nch) {
+        const uint32_t wd[4][4] = {{T.wv[0].x, T.wv[0].y, T.wv[0].z, T.wv[0].w},
+                                   {T.wv[1].x, T.wv[1].y, T.wv[1].z, T.wv[1].w},
+                                   {T.wv[2].x, T.wv[2].y, T.wv[2].z, T.wv[2].w},
+                                   {T.wv[3].x, T.wv[3].y, T.wv[3].z, T.wv[3].w}};
+        uint32_t pr[4][CD::kPairs];
 #pragma unroll
-  for (int m = 0; m < MMAX; ++m) rowoff[m] = (m < M ? in_row(m) : 0) * a.in_row_pairs;
-  {
-    const int nsum = M * nblk * 16;
-#pragma unroll 4
-    for (int idx = threadIdx.x; idx < nsum; idx += blockDim.x) {
-      const int sub = idx & 15, pm = idx >> 4;
-      const int m = pm / nblk, blk = pm - m * nblk;
-      int64_t roff = rowoff[0];
+        for (int t = 0; t < 4; ++t) CD::extract(wd[t][j], pr[t], dk);
+        static_for<HALVES>([&](auto hc) {
+          constexpr int h = decltype(hc)::value;
+          constexpr int ks = j * HALVES + h;
+          constexpr bool first = (j % CPB == 0) && h == 0;
 #pragma unroll
-      for (int mm = 1; mm < MMAX; ++mm) roff = (m == mm) ? rowoff[mm] : roff;
-      const int k0 = blk * BLOCK + sub * EPT;
-      float cs = 0.f, xs = 0.f;
+          for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
-      for (int part = 0; part < PARTS; ++part) {
-        const uint32_t *xr = a.in + roff + part * a.in_part_stride + k0 / 2;
-        uint32_t xv[EPT / 2];
-        uint32_t *xs_l = s_x + (part * MMAX + m) * Kp + k0 / 2;
-        if constexpr (EPT == 8) {
-          const uint4 v = *reinterpret_cast<const uint4 *>(xr);
-          xv[0] = v.x; xv[1] = v.y; xv[2] = v.z; xv[3] = v.w;
-          if constexpr (XLDS) *reinterpret_cast<uint4 *>(xs_l) = v;
-        } else {
-          const uint2 v = *reinterpret_cast<const uint2 *>(xr);
-          xv[0] = v.x; xv[1] = v.y;
-          if constexpr (XLDS) *reinterpret_cast<uint2 *>(xs_l) = v;
-        }
+            for (int p = 0; p < PARTS; ++p) {
+              const uint4 A = T.af[ks][mt][p];
+              const bool fresh = first && p == 0;
+              accC[mt] = mfma16<XF16>(A, bc[h], fresh ? zero : accC[mt]);
+              if constexpr (AFF) accX[mt] = mfma16<XF16>(A, ones, fresh ? zero : accX[mt]);
 #pragma unroll
-        for (int i = 0; i < EPT; ++i) {
-          const float x = half_to_f32<F16>((xv[i >> 1] >> (16 * (i & 1))) & 0xFFFFu);
-          const int j = ((k0 + i) % CD::kPeriod) >> 1;
-          cs = fmaf(CD::base(j) + (float)TR::kZeroPoint, x, cs);
-          xs += x;
-        }
-      }
-#pragma unroll
-      for (int off = 8; off >= 1; off >>= 1) {
-        cs += __shfl_xor(cs, off);
-        xs += __shfl_xor(xs, off);
-      }
-      if (sub == 0) {
-        s_corr[(m * nblk + blk) * 2 + 0] = cs;
-        s_corr[(m * nblk + blk) * 2 + 1] = xs;
-      }
-    }
-  }
-  const uint32_t *xrow[MMAX];
-#pragma unroll
-  for (int m = 0; m < MMAX; ++m) xrow[m] = a.in + rowoff[m];
-  __syncthreads();
-
-  // ---- 3. consume batches of BPW blocks
-  float acc[MMAX];
-#pragma unroll
-  for (int m = 0; m < MMAX; ++m) acc[m] = 0.f;
-  const bool sf16 = a.sdtype == QMOE_DTYPE_F16;
-  auto consume = [&](int g0) __attribute__((always_inline)) {
-    static_for<BPW>([&](auto ic) {
-      constexpr int i = decltype(ic)::value;
-      const int b = g0 + i;
-      if (b < b1) {
-        float D[MMAX];
-#pragma unroll
-        for (int m = 0; m < MMAX; ++m) D[m] = 0.f;
-        static_for<CPB>([&](auto cc) {
-          constexpr int ci = decltype(cc)::value;
-          const uint4 wv = cw[i * CPB + ci];
-          const uint32_t wd[4] = {wv.x, wv.y, wv.z, wv.w};
-          const int64_t kp0 = ((int64_t)b * CPB + ci) * PPC;
-          static_for<4>([&](auto dc) {
-            constexpr int dd = decltype(dc)::value;
-            uint32_t pr[PPD];
-            CD::extract(wd[dd], pr);
-#pragma unroll
-            for (int m = 0; m < MMAX; ++m) {
-              if (m < M) {
-                float d = D[m];
-#pragma unroll
-                for (int part = 0; part < PARTS; ++part) {
-                  uint32_t xv[PPD];
-                  if constexpr (XLDS) {
-                    // same address in every lane: LDS broadcast
-                    const uint4 *xl =
-                        reinterpret_cast<const uint4 *>(s_x + (part * MMAX + m) * Kp + kp0 + dd * PPD);
-#pragma unroll
-                    for (int q = 0; q < PPD / 4; ++q) {
-                      const uint4 v = xl[q];
-                      xv[4 * q] = v.x; xv[4 * q + 1] = v.y; xv[4 * q + 2] = v.z; xv[4 * q + 3] = v.w;
-                    }
-                  } else {
-                    const uint32_t *xp = xrow[m] + kp0 + dd * PPD + part * a.in_part_stride;
-#pragma unroll
-                    for (int q = 0; q < PPD; ++q) xv[q] = xp[q];
-                  }
-#pragma unroll
-                  for (int j = 0; j < PPD; ++j) d = dot2<F16>(pr[j], xv[j], d);
-                }
-                D[m] = d;
+              for (int t = 0; t < 4; ++t) {
+                const uint4 B = make_uint4(pr[t][4 * h], pr[t][4 * h + 1], pr[t][4 * h + 2], pr[t][4 * h + 3]);
+                accW[t][mt] = mfma16<XF16>(A, B, fresh ? zero : accW[t][mt]);
               }
             }
-          });
+          }
         });
-        const uint32_t sbits = sv[i];
-        const float s = sf16 ? f16_to_f32(sbits & 0xFFFFu) : bf16_to_f32(sbits & 0xFFFFu);
-        float bias = 0.f;
-        if constexpr (TR::kAffine) bias = sf16 ? f16_to_f32(sbits >> 16) : bf16_to_f32(sbits >> 16);
+        if constexpr (j % CPB == CPB - 1) {
+          // block epilogue: out += s (D - C) (+ b X)
+          constexpr int bi = j / CPB;
 #pragma unroll
-        for (int m = 0; m < MMAX; ++m) {
-          if (m < M) {
-            const float2 cx = reinterpret_cast<const float2 *>(s_corr)[m * nblk + b];
-            acc[m] = fmaf(s, D[m] - cx.x, acc[m]);
-            if constexpr (TR::kAffine) acc[m] = fmaf(bias, cx.y, acc[m]);
+          for (int t = 0; t < 4; ++t) {
+            const uint32_t ent = ESZ == 4 ? T.sv[t][bi] : ((T.sv[t][bi / 2] >> (16 * (bi % 2))) & 0xFFFFu);
+            const float s = sf16 ? f16_to_f32(ent & 0xFFFFu) : bf16_to_f32(ent & 0xFFFFu);
+            float b = 0.f;
+            if constexpr (AFF) b = sf16 ? f16_to_f32(ent >> 16) : bf16_to_f32(ent >> 16);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+              for (int el = 0; el < MR; ++el) {
+                float o = fmaf(s, accW[t][mt][el] - accC[mt][el], out[t][mt][el]);
+                if constexpr (AFF) o = fmaf(b, accX[mt][el], o);
+                out[t][mt][el] = o;
+              }
           }
         }
       }
     });
   };
-  for (int g0 = b0;;) {
-    consume(g0);
-    g0 += BPW;
-    if (g0 >= b1) break;
-    load_batch(g0);
+
+  // k-tile loop.  PF 0: load and compute one k-tile at a time; PF 1: the
+  // weights and scales of the next k-tile are in flight during the compute
+  // (the activations, L2 hits, are issued first so that waiting for them
+  // never waits for the prefetch); PF 2: the activations are prefetched too.
+  constexpr int PF = QMOE_GEMV_PREFETCH;
+  Tile TA, TB;
+  if (PF > 0 && kt0 < kt1) {
+    if constexpr (PF == 2) load_a(kt0, TA);
+    load_w(kt0, TA);
+  }
+  if constexpr (PF == 0) {
+    for (int kt = kt0; kt < kt1; ++kt) {
+      load_a(kt, TA);
+      load_w(kt, TA);
+      compute(kt, TA);
+    }
+  } else if (kt0 < kt1) {
+    for (int kt = kt0; kt < kt1; kt += 2) {
+      const bool h1 = kt + 1 < kt1;
+      if constexpr (PF == 1) load_a(kt, TA);
+      if (h1) {
+        if constexpr (PF == 2) load_a(kt + 1, TB);
+        load_w(kt + 1, TB);
+      }
+      compute(kt, TA);
+      if (h1) {
+        const bool h2 = kt + 2 < kt1;
+        if constexpr (PF == 1) load_a(kt + 1, TB);
+        if (h2) {
+          if constexpr (PF == 2) load_a(kt + 2, TA);
+          load_w(kt + 2, TA);
+        }
+        compute(kt + 1, TB);
+      }
+    }
   }
 
-  // ---- 4. cross-wave reduction in a fixed order, then the epilogue
+  // cross-wave reduction in a fixed order, then the epilogue
+  constexpr int NV = 4 * MT * MR;  // values per lane
 #pragma unroll
-  for (int m = 0; m < MMAX; ++m)
-    if (m < M) s_red[(wave * MMAX + m) * kLanes + lane] = acc[m];
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int el = 0; el < MR; ++el)
+        s_red[((wave * 4 + t) * MT + mt) * MR * kLanes + el * kLanes + lane] = out[t][mt][el];
   __syncthreads();
   const int64_t N = a.N;
-  for (int t = threadIdx.x; t < M * kLanes; t += blockDim.x) {
-    const int m = t / kLanes, l = t & (kLanes - 1);
+  for (int idx = threadIdx.x; idx < NV * kLanes; idx += blockDim.x) {
+    const int lo = idx & (kLanes - 1), q = idx / kLanes;
+    const int el = q % MR, mt = (q / MR) % MT, t = q / (MR * MT);
+    const int m = 16 * mt + 4 * (lo >> 4) + el;
+    const bool valid = m < M;
     float v = 0.f;
-    for (int w = 0; w < KS; ++w) v += s_red[(w * MMAX + m) * kLanes + l];
-    const int64_t n = (int64_t)rg * kRowsPerGroup + l;
+    for (int w = 0; w < KS; ++w) v += s_red[w * NV * kLanes + idx];
+    const int64_t n = (int64_t)rg * kRowsPerGroup + 16 * t + (lo & 15);
     if constexpr (EPI == kEpiStoreAct) {
-      a.out_act[(int64_t)m * N + n] = f32_to_act(v, a.act_dtype == QMOE_DTYPE_F16);
+      if (valid) a.out_act[(int64_t)m * N + n] = f32_to_act(v, a.act_dtype == QMOE_DTYPE_F16);
     } else if constexpr (EPI == kEpiSwiGLU) {
       // rows 2i (gate) and 2i+1 (up) sit in neighbouring lanes
       const float up = __shfl_xor(v, 1);
-      if ((l & 1) == 0) {
-        const float g = v;
-        const float h = g / (1.f + expf(-g)) * up;
+      if (valid && (lo & 1) == 0) {
+        const float gt = v;
+        const float h = gt / (1.f + expf(-gt)) * up;
         const int64_t Ih = N / 2;
-        const int64_t i = (int64_t)rg * (kRowsPerGroup / 2) + (l >> 1);
+        const int64_t i = n / 2;
         const int64_t p = pbase + m;
         const uint16_t hi = f32_to_bf16_rne(h);
         a.h_hi[p * Ih + i] = hi;
@@ -271,54 +340,44 @@ __global__ __launch_bounds__(512) void gemv_kernel(const GemvArgs a) {
         if (a.h_dbg) a.h_dbg[(int64_t)a.row_list[p] * Ih + i] = h;
       }
     } else {
-      if (a.top_k == 1) {
-        // one expert per token: y = w * o straight away (w = 1)
-        const int tok = a.token_of[pbase + m];
-        a.out_act[(int64_t)tok * N + n] =
-            f32_to_act(fmaf(a.route_w[tok], v, 0.f), a.act_dtype == QMOE_DTYPE_F16);
-      } else {
-        a.out_f32[(int64_t)(pbase + m) * N + n] = v;
+      if (valid) {
+        if (a.top_k == 1) {
+          // one expert per token: y = w * o straight away (w = 1)
+          const int tok = a.token_of[pbase + m];
+          a.out_act[(int64_t)tok * N + n] =
+              f32_to_act(fmaf(a.route_w[tok], v, 0.f), a.act_dtype == QMOE_DTYPE_F16);
+        } else {
+          a.out_f32[(int64_t)(pbase + m) * N + n] = v;
+        }
       }
     }
   }
 }
 
-template <int QT, bool F16, int EPI, int MMAX>
-hipError_t launch_gemv_block(const GemvArgs &a, int block, int waves, int grid_slots,
-                             hipStream_t s) {
-  const dim3 grid((unsigned)(grid_slots * a.RG));
-  const dim3 thr((unsigned)(waves * kLanes));
-  const size_t lds = gemv_lds_bytes(MMAX, a.nblk, waves, a.K, EPI == kEpiDown ? 2 : 1);
-  if (block == 64)
-    hipLaunchKernelGGL((gemv_kernel<QT, F16, EPI, MMAX, 64>), grid, thr, lds, s, a);
-  else
-    hipLaunchKernelGGL((gemv_kernel<QT, F16, EPI, MMAX, 128>), grid, thr, lds, s, a);
-  return hipGetLastError();
+// Kernel of a configuration: rows = the row bound of the launch.
+template <int QT, bool XF16, int PARTS, int EPI, int MR, int MT>
+const void *gemv_ptr_block(int block) {
+  return block == 64 ? reinterpret_cast<const void *>(&gemv_kernel<QT, XF16, PARTS, EPI, MR, MT, 64>)
+                     : reinterpret_cast<const void *>(&gemv_kernel<QT, XF16, PARTS, EPI, MR, MT, 128>);
 }
 
-template <int QT, bool F16, int EPI>
-hipError_t launch_gemv_m(const GemvArgs &a, int block, int mmax, int waves, int grid_slots,
-                         hipStream_t s) {
-  switch (mmax) {
-    case 1: return launch_gemv_block<QT, F16, EPI, 1>(a, block, waves, grid_slots, s);
-    case 2: return launch_gemv_block<QT, F16, EPI, 2>(a, block, waves, grid_slots, s);
-    case 4: return launch_gemv_block<QT, F16, EPI, 4>(a, block, waves, grid_slots, s);
-    case 8: return launch_gemv_block<QT, F16, EPI, 8>(a, block, waves, grid_slots, s);
-    default: return launch_gemv_block<QT, F16, EPI, 16>(a, block, waves, grid_slots, s);
+template <int QT, bool XF16, int PARTS, int EPI>
+const void *gemv_ptr_rows(int rows, int block) {
+  if (rows <= 1) return gemv_ptr_block<QT, XF16, PARTS, EPI, 1, 1>(block);
+  if constexpr (EPI == kEpiStoreAct) {
+    if (rows > 16) return gemv_ptr_block<QT, XF16, PARTS, EPI, 4, 2>(block);
   }
+  return gemv_ptr_block<QT, XF16, PARTS, EPI, 4, 1>(block);
 }
 
 template <int QT>
-hipError_t launch_gemv_qt(const GemvArgs &a, int epilogue, int in_f16, int mmax, int waves,
-                          int grid_slots, hipStream_t s) {
-  const int block = (int)(a.K / a.nblk);
-  if (epilogue == kEpiDown)
-    return launch_gemv_m<QT, false, kEpiDown>(a, block, mmax, waves, grid_slots, s);
+const void *gemv_ptr_qt(int epilogue, int in_f16, int rows, int block) {
+  if (epilogue == kEpiDown) return gemv_ptr_rows<QT, false, 2, kEpiDown>(rows, block);
   if (epilogue == kEpiSwiGLU)
-    return in_f16 ? launch_gemv_m<QT, true, kEpiSwiGLU>(a, block, mmax, waves, grid_slots, s)
-                  : launch_gemv_m<QT, false, kEpiSwiGLU>(a, block, mmax, waves, grid_slots, s);
-  return in_f16 ? launch_gemv_m<QT, true, kEpiStoreAct>(a, block, mmax, waves, grid_slots, s)
-                : launch_gemv_m<QT, false, kEpiStoreAct>(a, block, mmax, waves, grid_slots, s);
+    return in_f16 ? gemv_ptr_rows<QT, true, 1, kEpiSwiGLU>(rows, block)
+                  : gemv_ptr_rows<QT, false, 1, kEpiSwiGLU>(rows, block);
+  return in_f16 ? gemv_ptr_rows<QT, true, 1, kEpiStoreAct>(rows, block)
+                : gemv_ptr_rows<QT, false, 1, kEpiStoreAct>(rows, block);
 }
 
 }  // namespace qmoe

@@ -24,11 +24,11 @@
 //     (x * 2^r < 2^14): exact for bf16/f16 x; the fp32 SwiGLU output h is
 //     split into f16 hi + lo parts (about 22 significant bits) and FC2 runs
 //     one MFMA per part against the same dequantized weights.
-//   - B fragments are read straight from the GEMV prepacked layout: lane l
-//     of a wave reads dword (l / 16) of row (l % 16) of a 16-row slice, one
-//     coalesced 256-B load per slice and chunk; for 2-bit codes a dword holds
-//     16 consecutive k, split over two MFMA k-steps with the A operand
-//     gathered in the same k order.
+//   - B fragments are read straight from the k-tiled prepacked layout: lane
+//     l of a wave reads dword (l / 16) of row (l % 16) of a 16-row slice,
+//     which that layout stores in the lane's own 16 B; for 2-bit codes a
+//     dword holds 16 consecutive k, split over two MFMA k-steps with the A
+//     operand gathered in the same k order.
 //   - workgroup ids are remapped so that the tiles sharing one expert's
 //     weight slice run on the same XCD (its own L2).
 #include <float.h>
@@ -73,7 +73,7 @@ __global__ __launch_bounds__(256) void wscale_kernel(MatLayout L, const uint8_t 
   __shared__ float red[4];
   const int e = blockIdx.x;
   const uint8_t *sb = mat + (int64_t)e * L.stride + L.scales_off;
-  const int64_t n = L.N * L.nblk;
+  const int64_t n = L.RG * L.NKT * kLanes * L.bpk;  // padded entries are zero
   float m = 0.f;
   const int f16 = L.sdtype == QMOE_DTYPE_F16;
   const float qmax = (float)qtype_qmax(L.qtype);
@@ -165,7 +165,8 @@ __global__ __launch_bounds__(256) void grouped_kernel(const GroupedArgs a) {
   const int64_t rg = (wave_on ? nw : 0) / kRowsPerGroup;
   const int nl0 = nw % kRowsPerGroup;
   const uint8_t *wexp = a.w + (int64_t)e * a.expert_stride;
-  const uint32_t *wbase = reinterpret_cast<const uint32_t *>(wexp) + rg * a.NC * kLanes * 4;
+  // row group base of the k-tiled layout: [NKT][4 n-tiles][64 lanes][4 dwords]
+  const uint32_t *wbase = reinterpret_cast<const uint32_t *>(wexp) + rg * a.NKT * (4 * kLanes * 4);
   const uint8_t *sbase = wexp + a.scales_off;
   const int g = lane >> 4;
   int nl[2];
@@ -196,8 +197,9 @@ __global__ __launch_bounds__(256) void grouped_kernel(const GroupedArgs a) {
       const int64_t blk = (chunk * KC) / a.block;
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        bw[c][j] = wbase[(chunk * kLanes + nl[j]) * 4 + g];
-        const int64_t si = (rg * a.nblk + blk) * kLanes + nl[j];
+        // dword g of the chunk of row nl[j] sits in lane (nl[j] % 16) + 16 g of its n-tile
+        bw[c][j] = wbase[(((chunk / 4) * 4 + (nl[j] >> 4)) * kLanes + lane) * 4 + (chunk % 4)];
+        const int64_t si = ((rg * a.NKT + blk / a.bpk) * kLanes + nl[j]) * a.bpk + blk % a.bpk;
         sv[c][j] = AFF ? reinterpret_cast<const uint32_t *>(sbase)[si]
                        : reinterpret_cast<const uint16_t *>(sbase)[si];
       }
@@ -314,7 +316,8 @@ __global__ __launch_bounds__(256) void grouped_kernel(const GroupedArgs a) {
         float bb[2];
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-          const uint32_t sb = reinterpret_cast<const uint32_t *>(sbase)[(rg * a.nblk + blk) * kLanes + nl[j]];
+          const uint32_t sb = reinterpret_cast<const uint32_t *>(
+              sbase)[((rg * a.NKT + blk / a.bpk) * kLanes + nl[j]) * a.bpk + blk % a.bpk];
           const float s = sf16 ? f16_to_f32(sb & 0xFFFFu) : bf16_to_f32(sb & 0xFFFFu);
           const float b = sf16 ? f16_to_f32(sb >> 16) : bf16_to_f32(sb >> 16);
           bb[j] = fmaf((float)ZC, s, b) * wsc;

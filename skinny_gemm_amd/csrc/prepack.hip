@@ -4,88 +4,92 @@
 // The onnxruntime pull request 33005 (Description) prepacks expert weights
 // once from the initializers and keeps the scales transposed for the
 // kernels; here the prepacked layout is the one described in
-// qmoe_internal.h (MatLayout): one 16-B chunk per lane per row, 64 rows per
-// wave, and per-block scales contiguous across the 64 lanes.
+// qmoe_internal.h (MatLayout): k-tiles of four 16-B chunks per row, laid out
+// so that one 1 KiB wave load is the MFMA B operand of 16 rows, and the
+// scales of a row's k-tile adjacent.
 #include "qmoe_internal.h"
 #include "codec.hpp"
 
 namespace qmoe {
 
-// One thread per (expert, row group, chunk, lane): 16 canonical bytes in,
-// 16 prepacked bytes out.
+// One thread per (expert, row, chunk slot): 16 canonical bytes in, four
+// prepacked dwords out (zeros for the padding chunks of a partial k-tile).
 __global__ __launch_bounds__(256) void prepack_codes_kernel(MatLayout L, int64_t total,
                                                             const uint8_t *__restrict__ src,
                                                             uint8_t *__restrict__ dst,
                                                             uint32_t *__restrict__ err) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= total) return;
-  const int lane = (int)(idx % kLanes);
-  const int64_t c = (idx / kLanes) % L.NC;
-  const int64_t g = (idx / kLanes / L.NC) % L.RG;
-  const int64_t e = idx / kLanes / L.NC / L.RG;
-  const int64_t n = g * kRowsPerGroup + lane;
-  const int64_t row_bytes = L.K * L.bits / 8;
-  const uint8_t *s = src + (e * L.N + n) * row_bytes + c * kChunkBytes;
-  uint8_t in[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) in[i] = s[i];
-  const int fmask = (1 << L.bits) - 1;
+  const int64_t NCP = 4 * L.NKT;  // chunk slots per row
+  const int64_t c = idx % NCP;
+  const int64_t n = (idx / NCP) % L.N;
+  const int64_t e = idx / NCP / L.N;
   uint32_t out[4] = {0, 0, 0, 0};
   int bad = 0;
-  const int wpd = 32 / L.bits;  // weights per dword
-  for (int k = 0; k < L.kc; ++k) {
-    const int bit = k * L.bits;
-    const uint32_t u = (in[bit >> 3] >> (bit & 7)) & fmask;
-    if (L.qtype == QMOE_QTYPE_TERNARY && u == 3) bad = 1;
-    const int d = k / wpd, kk = k % wpd, j = kk >> 1, hi = kk & 1;
-    out[d] |= u << (L.bits * j + 16 * hi);
+  if (c < L.NC) {
+    const int64_t row_bytes = L.K * L.bits / 8;
+    const uint8_t *s = src + (e * L.N + n) * row_bytes + c * kChunkBytes;
+    uint8_t in[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) in[i] = s[i];
+    const int fmask = (1 << L.bits) - 1;
+    const int wpd = 32 / L.bits;  // weights per dword
+    for (int k = 0; k < L.kc; ++k) {
+      const int bit = k * L.bits;
+      const uint32_t u = (in[bit >> 3] >> (bit & 7)) & fmask;
+      if (L.qtype == QMOE_QTYPE_TERNARY && u == 3) bad = 1;
+      const int d = k / wpd, kk = k % wpd, j = kk >> 1, hi = kk & 1;
+      out[d] |= u << (L.bits * j + 16 * hi);
+    }
   }
-  uint4 v;
-  v.x = out[0]; v.y = out[1]; v.z = out[2]; v.w = out[3];
-  uint8_t *o = dst + e * L.stride + ((g * L.NC + c) * kLanes + lane) * kChunkBytes;
-  *reinterpret_cast<uint4 *>(o) = v;
+  uint8_t *o = dst + e * L.stride;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) *reinterpret_cast<uint32_t *>(o + L.code_word_offset(n, c, d)) = out[d];
   if (bad) atomicAdd(err, 1u);
 }
 
-// One thread per (expert, row group, block, lane).
+// One thread per prepacked scale entry (expert, row group, k-tile, row,
+// block of the k-tile); entries past the last block are zero.
 __global__ __launch_bounds__(256) void prepack_scales_kernel(MatLayout L, int64_t total,
                                                              const uint16_t *__restrict__ scales,
                                                              const uint16_t *__restrict__ biases,
                                                              uint8_t *__restrict__ dst) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= total) return;
-  const int lane = (int)(idx % kLanes);
-  const int64_t b = (idx / kLanes) % L.nblk;
-  const int64_t g = (idx / kLanes / L.nblk) % L.RG;
-  const int64_t e = idx / kLanes / L.nblk / L.RG;
-  const int64_t n = g * kRowsPerGroup + lane;
-  const int64_t src = (e * L.N + n) * L.nblk + b;
+  const int64_t per = L.RG * L.NKT * kLanes * L.bpk;  // entries per expert
+  const int64_t e = idx / per, i = idx % per;
+  const int64_t bi = i % L.bpk;
+  const int64_t row = (i / L.bpk) % kLanes;
+  const int64_t kt = (i / L.bpk / kLanes) % L.NKT;
+  const int64_t rg = i / L.bpk / kLanes / L.NKT;
+  const int64_t n = rg * kRowsPerGroup + row, b = kt * L.bpk + bi;
   uint8_t *base = dst + e * L.stride + L.scales_off;
-  const int64_t pos = (g * L.nblk + b) * kLanes + lane;
+  const bool real = b < L.nblk;
+  const int64_t src = (e * L.N + n) * L.nblk + b;
   if (L.affine) {
-    reinterpret_cast<uint32_t *>(base)[pos] = (uint32_t)scales[src] | ((uint32_t)biases[src] << 16);
+    reinterpret_cast<uint32_t *>(base)[i] =
+        real ? ((uint32_t)scales[src] | ((uint32_t)biases[src] << 16)) : 0u;
   } else {
-    reinterpret_cast<uint16_t *>(base)[pos] = scales[src];
+    reinterpret_cast<uint16_t *>(base)[i] = real ? scales[src] : (uint16_t)0;
   }
 }
 
-// Diagnostic read-back through the same register decoders the GEMV uses.
+// Diagnostic read-back through the same register decoders the kernels use.
 // Both activation flavours (bf16 and f16 magic) must agree; a disagreement
-// writes -128, which no valid code takes.
+// writes -128, which no valid code takes.  One thread per (expert, row, chunk).
 template <int BITS>
 __global__ __launch_bounds__(256) void unpack_codes_kernel(MatLayout L, int64_t total,
                                                            const uint8_t *__restrict__ src,
                                                            int8_t *__restrict__ out) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= total) return;
-  const int lane = (int)(idx % kLanes);
-  const int64_t c = (idx / kLanes) % L.NC;
-  const int64_t g = (idx / kLanes / L.NC) % L.RG;
-  const int64_t e = idx / kLanes / L.NC / L.RG;
-  const int64_t n = g * kRowsPerGroup + lane;
-  const uint4 v = *reinterpret_cast<const uint4 *>(src + e * L.stride +
-                                                   ((g * L.NC + c) * kLanes + lane) * kChunkBytes);
-  const uint32_t dw[4] = {v.x, v.y, v.z, v.w};
+  const int64_t c = idx % L.NC;
+  const int64_t n = (idx / L.NC) % L.N;
+  const int64_t e = idx / L.NC / L.N;
+  const uint8_t *m = src + e * L.stride;
+  uint32_t dw[4];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) dw[d] = *reinterpret_cast<const uint32_t *>(m + L.code_word_offset(n, c, d));
   const int zp = qtype_zero_point(L.qtype);
   using CB = Codec<BITS, false>;
   using CF = Codec<BITS, true>;
@@ -113,10 +117,10 @@ static inline unsigned nblocks(int64_t total, int bs) { return (unsigned)((total
 hipError_t launch_prepack_matrix(const MatLayout &L, int E, const uint8_t *codes,
                                  const uint16_t *scales, const uint16_t *biases, uint8_t *dst,
                                  uint32_t *err_word, hipStream_t s) {
-  const int64_t tc = (int64_t)E * L.RG * L.NC * kLanes;
+  const int64_t tc = (int64_t)E * L.N * 4 * L.NKT;
   hipLaunchKernelGGL(prepack_codes_kernel, dim3(nblocks(tc, 256)), dim3(256), 0, s, L, tc, codes, dst,
                      err_word);
-  const int64_t ts = (int64_t)E * L.RG * L.nblk * kLanes;
+  const int64_t ts = (int64_t)E * L.RG * L.NKT * kLanes * L.bpk;
   hipLaunchKernelGGL(prepack_scales_kernel, dim3(nblocks(ts, 256)), dim3(256), 0, s, L, ts, scales,
                      biases, dst);
   return hipGetLastError();
@@ -124,7 +128,7 @@ hipError_t launch_prepack_matrix(const MatLayout &L, int E, const uint8_t *codes
 
 hipError_t launch_unpack_matrix(const MatLayout &L, int E, const uint8_t *src, int8_t *codes_out,
                                 hipStream_t s) {
-  const int64_t tc = (int64_t)E * L.RG * L.NC * kLanes;
+  const int64_t tc = (int64_t)E * L.N * L.NC;
   if (L.bits == 4)
     hipLaunchKernelGGL(unpack_codes_kernel<4>, dim3(nblocks(tc, 256)), dim3(256), 0, s, L, tc, src,
                        codes_out);

@@ -14,7 +14,7 @@ constexpr int kRowsPerGroup = 64;     // one output row per lane in the GEMV lay
 constexpr int kChunkBytes = 16;       // one 128-bit load per lane
 constexpr int kMaxExperts = 256;
 constexpr int kMaxTopK = 16;
-constexpr int kGemvMaxRows = 16;      // register accumulators per lane (rows per expert)
+constexpr int kGemvMaxRows = 16;      // rows per expert on the GEMV path (one MFMA row tile)
 constexpr int64_t kAlign = 256;
 
 __host__ __device__ inline int64_t align_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
@@ -37,16 +37,23 @@ __host__ __device__ inline int qtype_zero_point(int qt) {
 
 // Prepacked layout of one quantized matrix W [N][K] (one expert).
 //
-// codes : [N/64 row groups][K/kc chunks][64 lanes][16 B]; lane l of row
-//         group g holds row 64g + l.  A wave reading chunk c of a row group
-//         issues one 1 KiB contiguous, 16-B-per-lane load.  Inside a lane's
-//         16 B, dword d covers weights [d*wpd, (d+1)*wpd) of the chunk
-//         (wpd = 32/bits) and weight pair j = (2j, 2j+1) of the dword keeps its
-//         even weight in the low half-word and its odd weight in the high
-//         half-word at the same bit offset (4j for 4-bit, 2j for 2-bit), so
-//         one AND-OR places a pair into the mantissas of two 16-bit floats.
-// scales: [N/64][K/B][64 lanes] x (scale) or x (scale, bias) 16-bit values:
-//         the 64 lanes of a wave read one contiguous 128/256 B piece per block.
+// A chunk is 16 B of one row: kc = 128/bits consecutive weights.  Inside a
+// chunk, dword d covers weights [d*wpd, (d+1)*wpd) (wpd = 32/bits) and weight
+// pair j = (2j, 2j+1) of the dword keeps its even weight in the low half-word
+// and its odd weight in the high half-word at the same bit offset (4j for
+// 4-bit, 2j for 2-bit), so one AND-OR places a pair into the mantissas of two
+// 16-bit floats.
+//
+// codes : [N/64 row groups][NKT k-tiles][4 n-tiles][64 lanes][16 B].  A
+//         k-tile is 4 chunks (kt = 4*kc weights).  Lane r + 16 g of n-tile t
+//         holds, as its dword j, dword g of chunk j of row 64 rg + 16 t + r:
+//         one 1 KiB contiguous wave load gives every lane the MFMA B operand
+//         of row (lane % 16) for k-group (lane / 16) of four chunks, and one
+//         chunk is one block-aligned group of MFMA k-steps.  A partial last
+//         k-tile is padded with zero chunks.
+// scales: [N/64][NKT][64 rows][bpk blocks] x (scale) or (scale | bias << 16),
+//         bpk = kt / block blocks per k-tile (padded entries are zero): the
+//         lanes of row r read all scales of a k-tile with one load.
 struct MatLayout {
   int qtype, bits, block, sdtype;
   bool affine;
@@ -54,9 +61,11 @@ struct MatLayout {
   int64_t RG;    // row groups
   int kc;        // weights per lane chunk (16 B)
   int64_t NC;    // chunks per row
+  int64_t NKT;   // k-tiles per row (4 chunks each)
   int64_t nblk;  // blocks per row
   int cpb;       // chunks per block
-  int scale_elem;         // bytes per lane per block (2 or 4)
+  int bpk;       // blocks per k-tile
+  int scale_elem;         // bytes per block entry (2 or 4)
   int64_t codes_bytes;
   int64_t scales_off;     // from the start of the expert's matrix
   int64_t scales_bytes;
@@ -74,14 +83,28 @@ struct MatLayout {
     L.RG = d.rows / kRowsPerGroup;
     L.kc = kChunkBytes * 8 / L.bits;
     L.NC = d.cols / L.kc;
+    L.NKT = (L.NC + 3) / 4;
     L.nblk = d.cols / d.block;
     L.cpb = d.block / L.kc;
+    L.bpk = 4 * L.kc / d.block;
     L.scale_elem = L.affine ? 4 : 2;
-    L.codes_bytes = d.rows * d.cols * L.bits / 8;
+    L.codes_bytes = L.RG * L.NKT * 4 * kLanes * kChunkBytes;
     L.scales_off = align_up(L.codes_bytes, kAlign);
-    L.scales_bytes = d.rows * L.nblk * L.scale_elem;
+    L.scales_bytes = L.RG * L.NKT * kLanes * L.bpk * L.scale_elem;
     L.stride = L.scales_off + align_up(L.scales_bytes, kAlign);
     return L;
+  }
+  // Byte offset (from the expert's matrix) of the 4-byte word holding
+  // dword `d` of chunk `c` of row `n`.
+  __host__ __device__ int64_t code_word_offset(int64_t n, int64_t c, int d) const {
+    const int64_t rg = n / kRowsPerGroup, t = (n % kRowsPerGroup) / 16, r = n % 16;
+    const int64_t kt = c / 4, j = c % 4;
+    return ((((rg * NKT + kt) * 4 + t) * kLanes + r + 16 * d) * kChunkBytes) + 4 * j;
+  }
+  // Index (in entries of scale_elem bytes) of the scale of row n, block b.
+  __host__ __device__ int64_t scale_index(int64_t n, int64_t b) const {
+    const int64_t rg = n / kRowsPerGroup, rl = n % kRowsPerGroup;
+    return ((rg * NKT + b / bpk) * kLanes + rl) * bpk + b % bpk;
   }
 };
 
@@ -166,8 +189,8 @@ struct GemvArgs {
   const uint8_t *w;        // matrix section base (expert 0)
   int64_t expert_stride;
   int64_t scales_off;
-  int64_t N, K, RG, NC, nblk;
-  int cpb, kc, qtype, sdtype;
+  int64_t N, K, RG, NC, NKT, nblk;
+  int qtype, sdtype;
   // rows: routed (slot_info / token_of) or dense (M rows)
   const int4 *slot_info;
   const int32_t *token_of, *row_list;
@@ -187,20 +210,18 @@ struct GemvArgs {
   const float *route_w;    // kEpiDown: routing weights [T*k]
 };
 
-// Blocks a wave loads in one batch: 8 chunks of 16 B per lane.
-inline int gemv_blocks_per_batch(int cpb) { return cpb >= 8 ? 1 : 8 / cpb; }
+// Rows per GEMV launch: one 16-row MFMA tile for routed experts, two for
+// dense inputs.
+constexpr int kGemvMaxRowsDense = 32;
+constexpr int kGemvMaxWaves = 8;
 
-// Activations are staged in LDS (broadcast ds_read) for at most this many
-// rows per expert; more rows read them with scalar loads.
-constexpr int kGemvLdsRows = 4;
-
-// Dynamic LDS of one GEMV workgroup: per-row block corrections, staged
-// activations (parts x rows x K 16-bit values, small row counts only) and
-// the cross-wave partial sums.
-inline size_t gemv_lds_bytes(int mmax, int64_t nblk, int waves, int64_t K, int parts) {
-  const size_t x = (mmax <= kGemvLdsRows) ? (size_t)parts * (size_t)mmax * (size_t)K * 2 : 0;
-  return ((size_t)mmax * (size_t)nblk * 2 + (size_t)waves * (size_t)mmax * kLanes) * sizeof(float) + x + 64;
+// Dynamic LDS of one GEMV workgroup: the cross-wave partial sums of the
+// 4 n-tiles x row tiles x accumulator elements x 64 lanes.
+inline size_t gemv_lds_bytes(int rows, int epilogue, int waves) {
+  const int mt = (epilogue == kEpiStoreAct && rows > 16) ? 2 : 1, mr = rows > 1 ? 4 : 1;
+  return (size_t)waves * 4 * (size_t)mt * (size_t)mr * kLanes * sizeof(float);
 }
+constexpr size_t kGemvLdsLimit = 64 * 1024;
 
 // Host launchers (defined in the kernel translation units).
 hipError_t launch_prepack_matrix(const MatLayout &L, int E, const uint8_t *codes,
@@ -209,8 +230,12 @@ hipError_t launch_prepack_matrix(const MatLayout &L, int E, const uint8_t *codes
 hipError_t launch_unpack_matrix(const MatLayout &L, int E, const uint8_t *src, int8_t *codes_out,
                                 hipStream_t s);
 hipError_t launch_route(const RouteArgs &a, hipStream_t s);
-hipError_t launch_gemv(const GemvArgs &a, int epilogue, int in_f16, int mmax, int waves,
+// rows: bound on the rows of any expert (or dense M), <= kGemvMaxRowsDense.
+hipError_t launch_gemv(const GemvArgs &a, int epilogue, int in_f16, int rows, int waves, int block,
                        int grid_slots, hipStream_t s);
+// Resident workgroups per compute unit of that GEMV kernel with `waves` waves
+// (0 if the runtime cannot tell).
+int gemv_blocks_per_cu(int qtype, int epilogue, int in_f16, int rows, int waves, int block);
 hipError_t launch_combine(const float *o, const int32_t *slot_pos, const float *w, int T, int k,
                           int H, int act_dtype, uint16_t *y, hipStream_t s);
 
@@ -223,8 +248,8 @@ enum GroupedEpilogue { kGEpiSwiGLU = 0, kGEpiStoreF32 = 1, kGEpiStoreAct = 2 };
 struct GroupedArgs {
   const uint8_t *w;        // matrix section base (expert 0)
   int64_t expert_stride, scales_off;
-  int64_t N, K, RG, NC, nblk;
-  int qtype, sdtype, block;
+  int64_t N, K, RG, NC, NKT, nblk;
+  int qtype, sdtype, block, bpk;
   const float *wsc;        // [E] power-of-two weight pre-scale
   // rows
   const int4 *tile_info;   // routed: {expert, first position, rows, 0}

@@ -130,7 +130,7 @@ def test_plan_gemv_decode():
     p8 = q.forward_plan(_desc(), 8, 6)
     assert p8["gemv_mmax"] == 8 and p8["max_active"] == 48
     p3 = q.forward_plan(_desc(), 3, 6)
-    assert p3["gemv_mmax"] == 4
+    assert p3["gemv_mmax"] == 3
     p0 = q.forward_plan(_desc(), 0, 6)
     assert p0["num_launches"] == 0 and p0["kernels"] == []
 
