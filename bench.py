@@ -202,13 +202,19 @@ class MoeBench:
         torch.cuda.synchronize()
         return (cnt > 0).sum(1).cpu().numpy()
 
+    def stage_names(self):
+        """Stage list of the plan the forward call follows (one kernel each)."""
+        from skinny_gemm_amd import forward_plan
+        lay = self.layers[0]
+        return forward_plan(lay.desc, self.T, self.spec.top_k)["kernels"]
+
     def stage_times(self, chunk=64):
         """Average duration (ms) of each plan stage over the K steps, from events
         recorded on the launch stream around every stage.  Each chunk of steps is
         queued behind a GPU sleep so the stages run back to back, as in the graph,
         instead of waiting on the host between launches."""
         import torch
-        nst = (4 if self.spec.top_k > 1 else 3) if self.T <= 16 else 5
+        nst = len(self.stage_names())
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * nst)] for _ in range(self.K)]
         for row in evs:
             for e in row:
@@ -246,9 +252,7 @@ def bench_moe(spec, T, K, W, trials, layers, inp0, stages=True):
     res["frac_of_hbm_peak"] = res["effective_GBps"] / HBM_PEAK_GBS
     if stages:
         st = b.stage_times()
-        names = (["route", "gemv_fc1_swiglu", "gemv_fc2", "combine"][:len(st)] if len(st) < 5 else
-                 ["route", "rowscale", "grouped_fc1_swiglu", "grouped_fc2", "combine"])
-        res["stage_us"] = dict(zip(names, (st * 1e3).tolist()))
+        res["stage_us"] = dict(zip(b.stage_names(), (st * 1e3).tolist()))
         res["fc1_bytes_per_launch"] = float(touched.mean()) * fc1_bytes(spec)
     return res, b
 
@@ -328,7 +332,8 @@ def main():
     layers, inp0 = make_layers(spec, args.rotate_bytes)
     head, b = bench_moe(spec, T, args.steps, args.warmup, args.trials, layers, inp0)
     log(f"[bench] {json.dumps(head)}")
-    fc1_us = head["stage_us"]["gemv_fc1_swiglu"]
+    fc1_stage = next(n for n in head["stage_us"] if "fc1" in n)
+    fc1_us = head["stage_us"][fc1_stage]
     achieved = head["fc1_bytes_per_launch"] / (fc1_us * 1e-6) / 1e9
     traffic = None
     tpath = os.path.join(ROOT, "profiles", "traffic.json")
@@ -354,7 +359,7 @@ def main():
                    "hidden": spec.H, "intermediate": spec.I, "weights": spec.fc1.fmt,
                    "block": spec.fc1.block, "us_per_layer": round(head["us_per_layer"], 3),
                    "frac_of_hbm_peak": head["frac_of_hbm_peak"], "weight_copies": head["weight_copies"]},
-        "roofline": {"bound": "hbm", "kernel": "gemv_fc1_swiglu", "achieved": achieved,
+        "roofline": {"bound": "hbm", "kernel": fc1_stage, "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic, "avg_launch_us": fc1_us,
                      "algorithmic_bytes_per_launch": head["fc1_bytes_per_launch"]},
@@ -405,6 +410,18 @@ def main():
         dense = synth.LINEAR_WORKLOADS["dense_affine2"]
         extras["dense_affine2"] = [bench_linear(dense, N, [1, 2, 3, 4, 5, 8, 10, 16, 32], 50, 3, args.rotate_bytes)
                                    for N in dense.Ns]
+        # The expert GEMV at M=1 with all 64 DeepSeek-V2-Lite-shaped experts
+        # active (one row each): the gate/up matrices of the 64 experts read
+        # as one [64 * 2816][2048] INT4 matrix by the same MFMA GEMV kernel
+        # family (196 MB of weights per launch).
+        from synth.workloads import custom_linear_spec
+        d3 = synth.MOE_WORKLOADS["dsv2lite_int4"]
+        allx = custom_linear_spec(d3.H, fmt=d3.fc1.fmt, block=d3.fc1.block, scale_dtype=d3.fc1.scale_dtype,
+                                  act_dtype=d3.act_dtype)
+        r = bench_linear(allx, d3.E * 2 * d3.I, [1, 2, 4, 8, 16], 20, 3, args.rotate_bytes)
+        r["workload"] = f"dsv2lite_fc1_all{d3.E}_experts_as_dense[N={d3.E * 2 * d3.I},K={d3.H}]"
+        extras["expert_gemv_all_experts_m1"] = r
+        log(f"[bench] {json.dumps(r)}")
         line["extras"] = extras
     print(json.dumps(line), flush=True)
 

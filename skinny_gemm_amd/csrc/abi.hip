@@ -186,23 +186,40 @@ int device_cus() {
   return n;
 }
 
-// Waves per workgroup of the split-K GEMV (at most one per k-tile and
+// Shape of a GEMV launch.  Waves per workgroup of the split-K GEMV (at most one per k-tile and
 // kGemvMaxWaves).  With the kernel's occupancy known, the choice minimises
 // the critical path: rounds of resident workgroups x k-tiles per wave (ties
-// to fewer waves).  Without it (no device), enough waves on the chip to
-// cover HBM latency.  nwg: workgroups of the launch; rows: its row bound.
-int pick_waves(int64_t nwg, const MatLayout &L, int rows, int epilogue, int in_f16) {
+// to fewer waves).  Wave counts that do not divide evenly over the 4 SIMDs
+// of a compute unit (3, 5, 6, 7) leave one SIMD with more waves of every
+// workgroup; such a count is a candidate only when it gives every wave a
+// single k-tile (the shortest critical path).  Without the occupancy (no device),
+// enough waves on the chip to cover HBM latency.  nwg: workgroups of the
+// launch; rows: its row bound.
+struct GemvShape {
+  int waves, tn;
+};
+
+GemvShape pick_gemv(int64_t nwg, const MatLayout &L, int rows, int epilogue, int in_f16) {
   const int64_t kmax = std::min<int64_t>(kGemvMaxWaves, L.NKT);
+  const int64_t cus = device_cus();
+  // four n-tiles per wave unless that leaves compute units idle
+  int tn = nwg < cus ? 1 : 4;
+  if (const char *e = getenv("QMOE_GEMV_TN")) {  // tuning override
+    const int v = atoi(e);
+    if (v == 1 || v == 4) tn = v;
+  }
+  nwg *= 4 / tn;
   if (const char *e = getenv("QMOE_GEMV_WAVES")) {  // tuning override
     const long long w = atoll(e);
-    if (w > 0) return (int)std::min<int64_t>(w, kmax);
+    if (w > 0) return {(int)std::min<int64_t>(w, kmax), tn};
   }
-  const int64_t cus = device_cus();
   int best = 0;
   int64_t best_cost = 0;
   for (int ks = 1; ks <= kmax; ++ks) {
-    if (gemv_lds_bytes(rows, epilogue, ks) > kLdsLimit) break;
-    const int per_cu = gemv_blocks_per_cu(L.qtype, epilogue, in_f16, rows, ks, L.block);
+    if (gemv_lds_bytes(rows, epilogue, ks, tn) > kLdsLimit) break;
+    const bool balanced = (ks & (ks - 1)) == 0;
+    if (!balanced && ks != L.NKT) continue;
+    const int per_cu = gemv_blocks_per_cu(L.qtype, epilogue, in_f16, rows, ks, tn, L.block);
     if (per_cu <= 0) {
       best = 0;
       break;
@@ -214,17 +231,18 @@ int pick_waves(int64_t nwg, const MatLayout &L, int rows, int epilogue, int in_f
       best_cost = cost;
     }
   }
-  if (best > 0) return best;
+  if (best > 0) return {best, tn};
   int64_t ks = (gemv_target_waves() + nwg - 1) / std::max<int64_t>(nwg, 1);
   ks = std::max<int64_t>(1, std::min<int64_t>(ks, kmax));
-  while (ks > 1 && gemv_lds_bytes(rows, epilogue, (int)ks) > kLdsLimit) --ks;
-  return (int)ks;
+  while (ks > 1 && gemv_lds_bytes(rows, epilogue, (int)ks, tn) > kLdsLimit) --ks;
+  return {(int)ks, tn};
 }
 
 struct Plan {
   int path;
-  int mmax, mmax1, mmax2, ks1, ks2, max_active, max_tiles;
+  int mmax, mmax1, mmax2, ks1, ks2, tn1, tn2, max_active, max_tiles;
   int route_fused;
+  int fc1_routes;  // GEMV path: FC1 routes the tokens itself (no routing kernel)
   int launches;
   std::string kernels;
 };
@@ -252,13 +270,23 @@ qmoe_status make_plan(const qmoe_layer_desc &d, int32_t T, int32_t k, int path_r
     return ok();
   }
   p.route_fused = (T <= 16) ? 1 : 0;
+  // a few routed slots: every FC1 workgroup routes them itself (the routing
+  // is repeated by every workgroup, so only while it is a small fraction of
+  // the work: more slots take the routing kernel)
+  p.fc1_routes = ((int64_t)T * k <= kFc1RouteMaxSlots) ? 1 : 0;
   p.max_active = (int)std::min<int64_t>(d.num_experts, (int64_t)T * k);
   p.mmax = p.mmax1 = p.mmax2 = T;  // no expert gets more rows than there are tokens
-  p.ks1 = pick_waves((int64_t)p.max_active * L.fc1.RG, L.fc1, T, kEpiSwiGLU, d.act_dtype == QMOE_DTYPE_F16);
-  p.ks2 = pick_waves((int64_t)p.max_active * L.fc2.RG, L.fc2, T, kEpiDown, 0);
+  const GemvShape g1 = pick_gemv((int64_t)p.max_active * L.fc1.RG, L.fc1, T,
+                                 p.fc1_routes ? kEpiSwiGLURouted : kEpiSwiGLU, d.act_dtype == QMOE_DTYPE_F16);
+  const GemvShape g2 = pick_gemv((int64_t)p.max_active * L.fc2.RG, L.fc2, T, kEpiDown, 0);
+  p.ks1 = g1.waves;
+  p.tn1 = g1.tn;
+  p.ks2 = g2.waves;
+  p.tn2 = g2.tn;
   // top-1: the down GEMV writes y; otherwise a combine kernel follows
-  p.kernels = k == 1 ? "route,gemv_fc1_swiglu,gemv_fc2" : "route,gemv_fc1_swiglu,gemv_fc2,combine";
-  p.launches = k == 1 ? 3 : 4;
+  p.kernels = std::string(p.fc1_routes ? "route_fc1_swiglu" : "route,gemv_fc1_swiglu") + ",gemv_fc2" +
+              (k == 1 ? "" : ",combine");
+  p.launches = (p.fc1_routes ? 2 : 3) + (k == 1 ? 0 : 1);
   return ok();
 }
 
@@ -455,19 +483,27 @@ qmoe_status qmoe_forward_ex(const qmoe_layer_desc *desc, const void *packed, con
     if (!opts || !opts->events || slot >= opts->num_events || !opts->events[slot]) return hipSuccess;
     return hipEventRecord((hipEvent_t)opts->events[slot], s);
   };
-  hipError_t e = rec(0);
-  if (e == hipSuccess) e = launch_route(ra, s);
-  if (e == hipSuccess) e = rec(1);
-  if (e != hipSuccess) return hip_status(e, "route");
+  // stage i of the plan's stage list records events 2i and 2i+1
+  int stage = 0;
+  auto begin = [&]() -> hipError_t { return rec(2 * stage); };
+  auto end = [&]() -> hipError_t { return rec(2 * stage++ + 1); };
+  hipError_t e = hipSuccess;
+  const bool fc1_routes = p.path == QMOE_PATH_GEMV && p.fc1_routes;
+  if (!fc1_routes) {
+    e = begin();
+    if (e == hipSuccess) e = launch_route(ra, s);
+    if (e == hipSuccess) e = end();
+    if (e != hipSuccess) return hip_status(e, "route");
+  }
 
   float *o = (float *)(wsb + W.o);
   if (p.path == QMOE_PATH_GROUPED) {
     float *xsc = (float *)(wsb + W.xsc), *h32 = (float *)(wsb + W.h32);
     uint32_t *hmax = (uint32_t *)(wsb + W.hmax);
     const float *wsc = (const float *)(pk + L.wsc_off);
-    e = rec(2);
+    e = begin();
     if (e == hipSuccess) e = launch_rowscale(x, T, desc->hidden, desc->act_dtype == QMOE_DTYPE_F16, xsc, s);
-    if (e == hipSuccess) e = rec(3);
+    if (e == hipSuccess) e = end();
     if (e != hipSuccess) return hip_status(e, "rowscale");
     GroupedArgs q1 = grouped_base(L.fc1, pk + L.fc1_off, wsc);
     q1.tile_info = ra.r.tile_info;
@@ -481,9 +517,9 @@ qmoe_status qmoe_forward_ex(const qmoe_layer_desc *desc, const void *packed, con
     q1.out_rowmax = hmax;
     q1.h_dbg = opts ? opts->h_out : nullptr;
     q1.row_list = ra.r.row_list;
-    e = rec(4);
+    e = begin();
     if (e == hipSuccess) e = launch_grouped(q1, kGEpiSwiGLU, p.max_tiles, s);
-    if (e == hipSuccess) e = rec(5);
+    if (e == hipSuccess) e = end();
     if (e != hipSuccess) return hip_status(e, "grouped fc1");
     GroupedArgs q2 = grouped_base(L.fc2, pk + L.fc2_off, wsc + desc->num_experts);
     q2.tile_info = ra.r.tile_info;
@@ -492,20 +528,28 @@ qmoe_status qmoe_forward_ex(const qmoe_layer_desc *desc, const void *packed, con
     q2.in_row_elems = desc->inter;
     q2.in_rowmax = hmax;
     q2.out_f32 = o;
-    e = rec(6);
+    e = begin();
     if (e == hipSuccess) e = launch_grouped(q2, kGEpiStoreF32, p.max_tiles, s);
-    if (e == hipSuccess) e = rec(7);
+    if (e == hipSuccess) e = end();
     if (e != hipSuccess) return hip_status(e, "grouped fc2");
-    e = rec(8);
+    e = begin();
     if (e == hipSuccess)
       e = launch_combine(o, ra.r.slot_pos, ra.r.w, T, top_k, desc->hidden, desc->act_dtype, (uint16_t *)y, s);
-    if (e == hipSuccess) e = rec(9);
+    if (e == hipSuccess) e = end();
     if (e != hipSuccess) return hip_status(e, "combine");
     return copy_diagnostics(desc, opts, ra.r, (int64_t)T * top_k, s);
   }
   uint16_t *h_hi = (uint16_t *)(wsb + W.h_hi), *h_lo = (uint16_t *)(wsb + W.h_lo);
 
   GemvArgs g1 = gemv_base(L.fc1, pk + L.fc1_off);
+  if (fc1_routes) {
+    g1.logits = logits;
+    g1.route_T = T;
+    g1.route_E = desc->num_experts;
+    g1.route_k = top_k;
+    g1.route_max_slots = p.max_active;
+    g1.route = ra.r;
+  }
   g1.slot_info = ra.r.slot_info;
   g1.token_of = ra.r.token_of;
   g1.row_list = ra.r.row_list;
@@ -516,11 +560,11 @@ qmoe_status qmoe_forward_ex(const qmoe_layer_desc *desc, const void *packed, con
   g1.h_hi = h_hi;
   g1.h_lo = h_lo;
   g1.h_dbg = opts ? opts->h_out : nullptr;
-  e = rec(2);
+  e = begin();
   if (e == hipSuccess)
-    e = launch_gemv(g1, kEpiSwiGLU, desc->act_dtype == QMOE_DTYPE_F16, p.mmax1, p.ks1, L.fc1.block,
-                    p.max_active, s);
-  if (e == hipSuccess) e = rec(3);
+    e = launch_gemv(g1, fc1_routes ? kEpiSwiGLURouted : kEpiSwiGLU, desc->act_dtype == QMOE_DTYPE_F16, p.mmax1,
+                    p.ks1, p.tn1, L.fc1.block, p.max_active, s);
+  if (e == hipSuccess) e = end();
   if (e != hipSuccess) return hip_status(e, "gemv fc1");
 
   GemvArgs g2 = gemv_base(L.fc2, pk + L.fc2_off);
@@ -536,15 +580,15 @@ qmoe_status qmoe_forward_ex(const qmoe_layer_desc *desc, const void *packed, con
   g2.out_act = (uint16_t *)y;
   g2.act_dtype = desc->act_dtype;
   g2.route_w = ra.r.w;
-  e = rec(4);
-  if (e == hipSuccess) e = launch_gemv(g2, kEpiDown, 0, p.mmax2, p.ks2, L.fc2.block, p.max_active, s);
-  if (e == hipSuccess) e = rec(5);
+  e = begin();
+  if (e == hipSuccess) e = launch_gemv(g2, kEpiDown, 0, p.mmax2, p.ks2, p.tn2, L.fc2.block, p.max_active, s);
+  if (e == hipSuccess) e = end();
   if (e != hipSuccess) return hip_status(e, "gemv fc2");
   if (top_k > 1) {
-    e = rec(6);
+    e = begin();
     if (e == hipSuccess)
       e = launch_combine(o, ra.r.slot_pos, ra.r.w, T, top_k, desc->hidden, desc->act_dtype, (uint16_t *)y, s);
-    if (e == hipSuccess) e = rec(7);
+    if (e == hipSuccess) e = end();
     if (e != hipSuccess) return hip_status(e, "combine");
   }
 
@@ -714,14 +758,14 @@ qmoe_status qmoe_linear(const qmoe_qmatrix_desc *desc, const void *packed, const
     g.act_dtype = x_dtype;
     return hip_status(launch_grouped(g, kGEpiStoreAct, (M + kTileM - 1) / kTileM, s), "linear mfma");
   }
-  const int ks = pick_waves(L.RG, L, M, kEpiStoreAct, x_dtype == QMOE_DTYPE_F16);
+  const GemvShape gs = pick_gemv(L.RG, L, M, kEpiStoreAct, x_dtype == QMOE_DTYPE_F16);
   GemvArgs g = gemv_base(L, (const uint8_t *)packed);
   g.dense_M = M;
   g.in = (const uint32_t *)x;
   g.in_row_pairs = L.K / 2;
   g.out_act = (uint16_t *)y;
   g.act_dtype = x_dtype;
-  return hip_status(launch_gemv(g, kEpiStoreAct, x_dtype == QMOE_DTYPE_F16, M, ks, L.block, 1, s),
+  return hip_status(launch_gemv(g, kEpiStoreAct, x_dtype == QMOE_DTYPE_F16, M, gs.waves, gs.tn, L.block, 1, s),
                     "linear gemv");
 }
 

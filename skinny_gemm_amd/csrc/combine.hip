@@ -48,34 +48,34 @@ hipError_t launch_combine(const float *o, const int32_t *slot_pos, const float *
   return hipGetLastError();
 }
 
-const void *gemv_ptr_sym_int4(int, int, int, int);
-const void *gemv_ptr_sym_int2(int, int, int, int);
-const void *gemv_ptr_ternary(int, int, int, int);
-const void *gemv_ptr_affine_int2(int, int, int, int);
-const void *gemv_ptr_affine_int4(int, int, int, int);
+const void *gemv_ptr_sym_int4(int, int, int, int, int);
+const void *gemv_ptr_sym_int2(int, int, int, int, int);
+const void *gemv_ptr_ternary(int, int, int, int, int);
+const void *gemv_ptr_affine_int2(int, int, int, int, int);
+const void *gemv_ptr_affine_int4(int, int, int, int, int);
 
-const void *gemv_kernel_ptr(int qtype, int epilogue, int in_f16, int rows, int block) {
+const void *gemv_kernel_ptr(int qtype, int epilogue, int in_f16, int rows, int block, int tn) {
   switch (qtype) {
-    case QMOE_QTYPE_SYM_INT4: return gemv_ptr_sym_int4(epilogue, in_f16, rows, block);
-    case QMOE_QTYPE_SYM_INT2: return gemv_ptr_sym_int2(epilogue, in_f16, rows, block);
-    case QMOE_QTYPE_TERNARY: return gemv_ptr_ternary(epilogue, in_f16, rows, block);
-    case QMOE_QTYPE_AFFINE_INT2: return gemv_ptr_affine_int2(epilogue, in_f16, rows, block);
-    default: return gemv_ptr_affine_int4(epilogue, in_f16, rows, block);
+    case QMOE_QTYPE_SYM_INT4: return gemv_ptr_sym_int4(epilogue, in_f16, rows, block, tn);
+    case QMOE_QTYPE_SYM_INT2: return gemv_ptr_sym_int2(epilogue, in_f16, rows, block, tn);
+    case QMOE_QTYPE_TERNARY: return gemv_ptr_ternary(epilogue, in_f16, rows, block, tn);
+    case QMOE_QTYPE_AFFINE_INT2: return gemv_ptr_affine_int2(epilogue, in_f16, rows, block, tn);
+    default: return gemv_ptr_affine_int4(epilogue, in_f16, rows, block, tn);
   }
 }
 
-hipError_t launch_gemv(const GemvArgs &a, int epilogue, int in_f16, int rows, int waves, int block,
+hipError_t launch_gemv(const GemvArgs &a, int epilogue, int in_f16, int rows, int waves, int tn, int block,
                        int grid_slots, hipStream_t s) {
-  const void *fn = gemv_kernel_ptr(a.qtype, epilogue, in_f16, rows, block);
+  const void *fn = gemv_kernel_ptr(a.qtype, epilogue, in_f16, rows, block, tn);
   GemvArgs args = a;
   void *kargs[] = {&args};
-  return hipLaunchKernel(fn, dim3((unsigned)(grid_slots * a.RG)), dim3((unsigned)(waves * kLanes)), kargs,
-                         gemv_lds_bytes(rows, epilogue, waves), s);
+  return hipLaunchKernel(fn, dim3((unsigned)(grid_slots * a.RG * (4 / tn))), dim3((unsigned)(waves * kLanes)),
+                         kargs, gemv_lds_bytes(rows, epilogue, waves, tn), s);
 }
 
-int gemv_blocks_per_cu(int qtype, int epilogue, int in_f16, int rows, int waves, int block) {
-  const void *fn = gemv_kernel_ptr(qtype, epilogue, in_f16, rows, block);
-  const size_t lds = gemv_lds_bytes(rows, epilogue, waves);
+int gemv_blocks_per_cu(int qtype, int epilogue, int in_f16, int rows, int waves, int tn, int block) {
+  const void *fn = gemv_kernel_ptr(qtype, epilogue, in_f16, rows, block, tn);
+  const size_t lds = gemv_lds_bytes(rows, epilogue, waves, tn);
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
   // the runtime query is not free: remember it per (device, kernel, waves)

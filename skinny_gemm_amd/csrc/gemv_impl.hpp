@@ -30,6 +30,7 @@
 
 #include "codec.hpp"
 #include "qmoe_internal.h"
+#include "route_impl.hpp"
 
 #ifndef QMOE_GEMV_PREFETCH
 #define QMOE_GEMV_PREFETCH 1
@@ -95,7 +96,7 @@ __device__ inline void load_scales(const uint8_t *p, uint32_t (&sv)[4]) {
 // PARTS: 2 = the input is an fp32 value split into bf16 hi + lo rows;
 // MR: accumulator rows kept per lane (1: a single row, 4: up to 16 rows per
 // tile); MT: 16-row tiles; BLOCK: scale block along K.
-template <int QT, bool XF16, int PARTS, int EPI, int MR, int MT, int BLOCK>
+template <int QT, bool XF16, int PARTS, int EPI, int MR, int MT, int BLOCK, int TN>
 __global__ __launch_bounds__(512) void gemv_kernel(const GemvArgs a) {
   using TR = QtTraits<QT>;
   using CD = Codec<TR::kBits, XF16>;
@@ -111,20 +112,49 @@ __global__ __launch_bounds__(512) void gemv_kernel(const GemvArgs a) {
   constexpr int ZP = TR::kZeroPoint;
   static_assert(CPB >= 1 && BPK >= 1, "block must span whole chunks of one k-tile");
   static_assert(MR == 4 || MT == 1, "several row tiles keep all accumulator rows");
+  static_assert(TN == 1 || TN == 2 || TN == 4, "n-tiles per wave");
 
-  extern __shared__ float s_red[];  // [waves][4][MT][MR][64]
+  extern __shared__ float s_red[];  // [waves][TN][MT][MR][64]
   const int lane = threadIdx.x & (kLanes - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kLanes);
   const int KS = blockDim.x / kLanes;
+  // workgroup -> (slot, row group, group of TN n-tiles within the row group)
+  constexpr int TQ = 4 / TN;
   const int RG = (int)a.RG;
-  const int slot = (int)blockIdx.x / RG;
-  const int rg = (int)blockIdx.x - slot * RG;
+  const int slot = (int)blockIdx.x / (RG * TQ);
+  const int rgq = (int)blockIdx.x - slot * (RG * TQ);
+  const int rg = rgq / TQ, t0 = (rgq - rg * TQ) * TN;
 
+  constexpr bool ROUTED = EPI == kEpiSwiGLURouted;
+  constexpr bool SWIGLU = EPI == kEpiSwiGLU || ROUTED;
+  // routed: this workgroup's expert and the flat slots of its rows
+  __shared__ int32_t s_rslot[ROUTED ? kGemvMaxRows : 1];
   int e, M, pbase;
   if (a.dense_M > 0) {
     e = 0;
     M = a.dense_M;
     pbase = 0;
+  } else if constexpr (ROUTED) {
+    // every workgroup routes the (at most 64) slots itself; workgroup 0 also
+    // writes the global lists and the top-k ids and weights
+    __shared__ int32_t s_ids[kLanes];
+    __shared__ int s_cnt[kMaxExperts];
+    __shared__ int4 s_slot;
+    const bool lead = blockIdx.x == 0;
+    for (int t = wave; t < a.route_T; t += KS)
+      wave_topk(a.logits + (int64_t)t * a.route_E, a.route_E, a.route_k,
+                lead ? a.route.ids + (int64_t)t * a.route_k : nullptr,
+                lead ? a.route.w + (int64_t)t * a.route_k : nullptr, s_ids + t * a.route_k);
+    __syncthreads();
+    if (wave == 0)
+      wave_expand_small(s_ids, a.route_T * a.route_k, a.route_k, a.route_E, a.route_max_slots, s_cnt,
+                        lead ? &a.route : nullptr, slot, &s_slot, s_rslot);
+    __syncthreads();
+    const int4 si = s_slot;
+    e = si.x;
+    M = si.y;
+    pbase = si.z;
+    if (M <= 0) return;
   } else {
     const int4 si = a.slot_info[slot];
     e = si.x;
@@ -147,6 +177,7 @@ __global__ __launch_bounds__(512) void gemv_kernel(const GemvArgs a) {
     int64_t row = 0;
     if (aval[mt]) {
       if (a.dense_M > 0) row = m;
+      else if constexpr (ROUTED) row = s_rslot[m] / a.route_k;
       else row = a.in_gather_token ? (int64_t)a.token_of[pbase + m] : (int64_t)(pbase + m);
     }
     arow[mt] = a.in + row * a.in_row_pairs;
@@ -174,9 +205,9 @@ __global__ __launch_bounds__(512) void gemv_kernel(const GemvArgs a) {
   const floatx4_t zero = {0.f, 0.f, 0.f, 0.f};
   const RegConsts<CD::kNC> dk = CodecOps<CD>::in_registers();  // decoder constants in registers
 
-  float out[4][MT][MR];
+  float out[TN][MT][MR];
 #pragma unroll
-  for (int t = 0; t < 4; ++t)
+  for (int t = 0; t < TN; ++t)
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -185,15 +216,15 @@ __global__ __launch_bounds__(512) void gemv_kernel(const GemvArgs a) {
   // One k-tile of operands: weights and scales of the 4 n-tiles, and the
   // activation fragments of every k-step.
   struct Tile {
-    uint4 wv[4];
-    uint32_t sv[4][4];
+    uint4 wv[TN];
+    uint32_t sv[TN][4];
     uint4 af[KSTEPS][MT][PARTS];
   };
   auto load_w = [&](int kt, Tile &T) __attribute__((always_inline)) {
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      T.wv[t] = wp[((int64_t)kt * 4 + t) * kLanes];
-      load_scales<BPK * ESZ>(sp + ((int64_t)kt * kLanes + 16 * t) * (BPK * ESZ), T.sv[t]);
+    for (int t = 0; t < TN; ++t) {
+      T.wv[t] = wp[((int64_t)kt * 4 + t0 + t) * kLanes];
+      load_scales<BPK * ESZ>(sp + ((int64_t)kt * kLanes + 16 * (t0 + t)) * (BPK * ESZ), T.sv[t]);
     }
   };
   auto load_a = [&](int kt, Tile &T) __attribute__((always_inline)) {
@@ -213,17 +244,16 @@ __global__ __launch_bounds__(512) void gemv_kernel(const GemvArgs a) {
   };
   auto compute = [&](int kt, const Tile &T) __attribute__((always_inline)) {
     const int nch = min(4, NC - 4 * kt);  // chunks present in this k-tile
-    floatx4_t accW[4][MT], accC[MT], accX[MT];
+    floatx4_t accW[TN][MT], accC[MT], accX[MT];
     static_for<4>([&](auto jc) {
       constexpr int j = decltype(jc)::value;
       if (j < nch) {
-        const uint32_t wd[4][4] = {{T.wv[0].x, T.wv[0].y, T.wv[0].z, T.wv[0].w},
-                                   {T.wv[1].x, T.wv[1].y, T.wv[1].z, T.wv[1].w},
-                                   {T.wv[2].x, T.wv[2].y, T.wv[2].z, T.wv[2].w},
-                                   {T.wv[3].x, T.wv[3].y, T.wv[3].z, T.wv[3].w}};
-        uint32_t pr[4][CD::kPairs];
+        uint32_t pr[TN][CD::kPairs];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) CD::extract(wd[t][j], pr[t], dk);
+        for (int t = 0; t < TN; ++t) {
+          const uint32_t wd[4] = {T.wv[t].x, T.wv[t].y, T.wv[t].z, T.wv[t].w};
+          CD::extract(wd[j], pr[t], dk);
+        }
         static_for<HALVES>([&](auto hc) {
           constexpr int h = decltype(hc)::value;
           constexpr int ks = j * HALVES + h;
@@ -237,7 +267,7 @@ __global__ __launch_bounds__(512) void gemv_kernel(const GemvArgs a) {
               accC[mt] = mfma16<XF16>(A, bc[h], fresh ? zero : accC[mt]);
               if constexpr (AFF) accX[mt] = mfma16<XF16>(A, ones, fresh ? zero : accX[mt]);
 #pragma unroll
-              for (int t = 0; t < 4; ++t) {
+              for (int t = 0; t < TN; ++t) {
                 const uint4 B = make_uint4(pr[t][4 * h], pr[t][4 * h + 1], pr[t][4 * h + 2], pr[t][4 * h + 3]);
                 accW[t][mt] = mfma16<XF16>(A, B, fresh ? zero : accW[t][mt]);
               }
@@ -248,7 +278,7 @@ __global__ __launch_bounds__(512) void gemv_kernel(const GemvArgs a) {
           // block epilogue: out += s (D - C) (+ b X)
           constexpr int bi = j / CPB;
 #pragma unroll
-          for (int t = 0; t < 4; ++t) {
+          for (int t = 0; t < TN; ++t) {
             const uint32_t ent = ESZ == 4 ? T.sv[t][bi] : ((T.sv[t][bi / 2] >> (16 * (bi % 2))) & 0xFFFFu);
             const float s = sf16 ? f16_to_f32(ent & 0xFFFFu) : bf16_to_f32(ent & 0xFFFFu);
             float b = 0.f;
@@ -305,14 +335,14 @@ __global__ __launch_bounds__(512) void gemv_kernel(const GemvArgs a) {
   }
 
   // cross-wave reduction in a fixed order, then the epilogue
-  constexpr int NV = 4 * MT * MR;  // values per lane
+  constexpr int NV = TN * MT * MR;  // values per lane
 #pragma unroll
-  for (int t = 0; t < 4; ++t)
+  for (int t = 0; t < TN; ++t)
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int el = 0; el < MR; ++el)
-        s_red[((wave * 4 + t) * MT + mt) * MR * kLanes + el * kLanes + lane] = out[t][mt][el];
+        s_red[((wave * TN + t) * MT + mt) * MR * kLanes + el * kLanes + lane] = out[t][mt][el];
   __syncthreads();
   const int64_t N = a.N;
   for (int idx = threadIdx.x; idx < NV * kLanes; idx += blockDim.x) {
@@ -322,10 +352,10 @@ __global__ __launch_bounds__(512) void gemv_kernel(const GemvArgs a) {
     const bool valid = m < M;
     float v = 0.f;
     for (int w = 0; w < KS; ++w) v += s_red[w * NV * kLanes + idx];
-    const int64_t n = (int64_t)rg * kRowsPerGroup + 16 * t + (lo & 15);
+    const int64_t n = (int64_t)rg * kRowsPerGroup + 16 * (t0 + t) + (lo & 15);
     if constexpr (EPI == kEpiStoreAct) {
       if (valid) a.out_act[(int64_t)m * N + n] = f32_to_act(v, a.act_dtype == QMOE_DTYPE_F16);
-    } else if constexpr (EPI == kEpiSwiGLU) {
+    } else if constexpr (SWIGLU) {
       // rows 2i (gate) and 2i+1 (up) sit in neighbouring lanes
       const float up = __shfl_xor(v, 1);
       if (valid && (lo & 1) == 0) {
@@ -337,7 +367,12 @@ __global__ __launch_bounds__(512) void gemv_kernel(const GemvArgs a) {
         const uint16_t hi = f32_to_bf16_rne(h);
         a.h_hi[p * Ih + i] = hi;
         a.h_lo[p * Ih + i] = f32_to_bf16_rne(h - bf16_to_f32(hi));
-        if (a.h_dbg) a.h_dbg[(int64_t)a.row_list[p] * Ih + i] = h;
+        if (a.h_dbg) {
+          int64_t slot_of_row;
+          if constexpr (ROUTED) slot_of_row = s_rslot[m];
+          else slot_of_row = a.row_list[p];
+          a.h_dbg[slot_of_row * Ih + i] = h;
+        }
       }
     } else {
       if (valid) {
@@ -354,30 +389,37 @@ __global__ __launch_bounds__(512) void gemv_kernel(const GemvArgs a) {
   }
 }
 
-// Kernel of a configuration: rows = the row bound of the launch.
+// Kernel of a configuration: rows = the row bound of the launch, tn = 16-row
+// tiles per wave (1: four workgroups share a row group's 64 rows).
 template <int QT, bool XF16, int PARTS, int EPI, int MR, int MT>
-const void *gemv_ptr_block(int block) {
-  return block == 64 ? reinterpret_cast<const void *>(&gemv_kernel<QT, XF16, PARTS, EPI, MR, MT, 64>)
-                     : reinterpret_cast<const void *>(&gemv_kernel<QT, XF16, PARTS, EPI, MR, MT, 128>);
+const void *gemv_ptr_block(int block, int tn) {
+  if (tn == 1)
+    return block == 64 ? reinterpret_cast<const void *>(&gemv_kernel<QT, XF16, PARTS, EPI, MR, MT, 64, 1>)
+                       : reinterpret_cast<const void *>(&gemv_kernel<QT, XF16, PARTS, EPI, MR, MT, 128, 1>);
+  return block == 64 ? reinterpret_cast<const void *>(&gemv_kernel<QT, XF16, PARTS, EPI, MR, MT, 64, 4>)
+                     : reinterpret_cast<const void *>(&gemv_kernel<QT, XF16, PARTS, EPI, MR, MT, 128, 4>);
 }
 
 template <int QT, bool XF16, int PARTS, int EPI>
-const void *gemv_ptr_rows(int rows, int block) {
-  if (rows <= 1) return gemv_ptr_block<QT, XF16, PARTS, EPI, 1, 1>(block);
+const void *gemv_ptr_rows(int rows, int block, int tn) {
+  if (rows <= 1) return gemv_ptr_block<QT, XF16, PARTS, EPI, 1, 1>(block, tn);
   if constexpr (EPI == kEpiStoreAct) {
-    if (rows > 16) return gemv_ptr_block<QT, XF16, PARTS, EPI, 4, 2>(block);
+    if (rows > 16) return gemv_ptr_block<QT, XF16, PARTS, EPI, 4, 2>(block, tn);
   }
-  return gemv_ptr_block<QT, XF16, PARTS, EPI, 4, 1>(block);
+  return gemv_ptr_block<QT, XF16, PARTS, EPI, 4, 1>(block, tn);
 }
 
 template <int QT>
-const void *gemv_ptr_qt(int epilogue, int in_f16, int rows, int block) {
-  if (epilogue == kEpiDown) return gemv_ptr_rows<QT, false, 2, kEpiDown>(rows, block);
+const void *gemv_ptr_qt(int epilogue, int in_f16, int rows, int block, int tn) {
+  if (epilogue == kEpiDown) return gemv_ptr_rows<QT, false, 2, kEpiDown>(rows, block, tn);
   if (epilogue == kEpiSwiGLU)
-    return in_f16 ? gemv_ptr_rows<QT, true, 1, kEpiSwiGLU>(rows, block)
-                  : gemv_ptr_rows<QT, false, 1, kEpiSwiGLU>(rows, block);
-  return in_f16 ? gemv_ptr_rows<QT, true, 1, kEpiStoreAct>(rows, block)
-                : gemv_ptr_rows<QT, false, 1, kEpiStoreAct>(rows, block);
+    return in_f16 ? gemv_ptr_rows<QT, true, 1, kEpiSwiGLU>(rows, block, tn)
+                  : gemv_ptr_rows<QT, false, 1, kEpiSwiGLU>(rows, block, tn);
+  if (epilogue == kEpiSwiGLURouted)
+    return in_f16 ? gemv_ptr_rows<QT, true, 1, kEpiSwiGLURouted>(rows, block, tn)
+                  : gemv_ptr_rows<QT, false, 1, kEpiSwiGLURouted>(rows, block, tn);
+  return in_f16 ? gemv_ptr_rows<QT, true, 1, kEpiStoreAct>(rows, block, tn)
+                : gemv_ptr_rows<QT, false, 1, kEpiStoreAct>(rows, block, tn);
 }
 
 }  // namespace qmoe

@@ -182,7 +182,12 @@ struct RouteArgs {
 // kEpiDown: FC2 -> per-slot fp32 o; with top-1 routing the combine is a
 // single product and y is written directly;
 // kEpiStoreAct: dense rows -> y in the activation dtype.
-enum GemvEpilogue { kEpiSwiGLU = 0, kEpiDown = 1, kEpiStoreAct = 2 };
+// kEpiSwiGLURouted: kEpiSwiGLU for small decode batches (T * k <=
+// kFc1RouteMaxSlots) whose workgroups route the tokens themselves (no
+// routing kernel); workgroup 0 also writes the routing lists for FC2, the
+// combine and the diagnostics.
+enum GemvEpilogue { kEpiSwiGLU = 0, kEpiDown = 1, kEpiStoreAct = 2, kEpiSwiGLURouted = 3 };
+constexpr int kFc1RouteMaxSlots = 16;  // <= 64 (one slot per lane of the expand)
 
 struct GemvArgs {
   // weights
@@ -208,6 +213,10 @@ struct GemvArgs {
   float *h_dbg;            // kEpiSwiGLU: optional [slot][N/2] fp32
   int act_dtype;           // kEpiStoreAct, kEpiDown
   const float *route_w;    // kEpiDown: routing weights [T*k]
+  // kEpiSwiGLURouted: router logits [T][E] and the routing outputs
+  const float *logits;
+  int route_T, route_E, route_k, route_max_slots;
+  RouteBufs route;
 };
 
 // Rows per GEMV launch: one 16-row MFMA tile for routed experts, two for
@@ -216,10 +225,10 @@ constexpr int kGemvMaxRowsDense = 32;
 constexpr int kGemvMaxWaves = 8;
 
 // Dynamic LDS of one GEMV workgroup: the cross-wave partial sums of the
-// 4 n-tiles x row tiles x accumulator elements x 64 lanes.
-inline size_t gemv_lds_bytes(int rows, int epilogue, int waves) {
+// tn n-tiles x row tiles x accumulator elements x 64 lanes.
+inline size_t gemv_lds_bytes(int rows, int epilogue, int waves, int tn) {
   const int mt = (epilogue == kEpiStoreAct && rows > 16) ? 2 : 1, mr = rows > 1 ? 4 : 1;
-  return (size_t)waves * 4 * (size_t)mt * (size_t)mr * kLanes * sizeof(float);
+  return (size_t)waves * tn * (size_t)mt * (size_t)mr * kLanes * sizeof(float);
 }
 constexpr size_t kGemvLdsLimit = 64 * 1024;
 
@@ -230,12 +239,13 @@ hipError_t launch_prepack_matrix(const MatLayout &L, int E, const uint8_t *codes
 hipError_t launch_unpack_matrix(const MatLayout &L, int E, const uint8_t *src, int8_t *codes_out,
                                 hipStream_t s);
 hipError_t launch_route(const RouteArgs &a, hipStream_t s);
-// rows: bound on the rows of any expert (or dense M), <= kGemvMaxRowsDense.
-hipError_t launch_gemv(const GemvArgs &a, int epilogue, int in_f16, int rows, int waves, int block,
+// rows: bound on the rows of any expert (or dense M), <= kGemvMaxRowsDense;
+// waves: waves per workgroup (K split); tn: 16-row n-tiles per wave (1 or 4).
+hipError_t launch_gemv(const GemvArgs &a, int epilogue, int in_f16, int rows, int waves, int tn, int block,
                        int grid_slots, hipStream_t s);
-// Resident workgroups per compute unit of that GEMV kernel with `waves` waves
-// (0 if the runtime cannot tell).
-int gemv_blocks_per_cu(int qtype, int epilogue, int in_f16, int rows, int waves, int block);
+// Resident workgroups per compute unit of that GEMV kernel (0 if the runtime
+// cannot tell).
+int gemv_blocks_per_cu(int qtype, int epilogue, int in_f16, int rows, int waves, int tn, int block);
 hipError_t launch_combine(const float *o, const int32_t *slot_pos, const float *w, int T, int k,
                           int H, int act_dtype, uint16_t *y, hipStream_t s);
 

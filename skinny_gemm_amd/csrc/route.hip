@@ -1,82 +1,18 @@
-// route.hip -- top-k routing and the per-expert row map.
+// route.hip -- top-k routing and the per-expert row map (route_impl.hpp
+// holds the per-wavefront pieces).
 //
-// The onnxruntime pull request 33005 (Description) reuses routing and
-// expert-map kernels and expands the rows by expert before FC1; its finalize
-// step combines the top-k weighted outputs.  Here:
-//   top-k   one wavefront per token: lanes hold the logits, k rounds of a
-//           wave-wide arg-max (ties to the lower expert index) select the
-//           experts in descending order; weights = softmax of the selected
-//           logits in fp32 (sum 1, exactly 1.0 for k = 1).
+//   top-k   one wavefront per token (wave_topk).
 //   expand  one workgroup: LDS histogram -> counts, exclusive scan ->
 //           offsets, list of active experts, then a stable counting sort of
 //           the flat slots r = t*k + j by expert (rank inside a wavefront from
 //           ballots over the expert id bits, ranks across wavefronts from
 //           per-wavefront counts in LDS), giving row_list and its inverse.
-#include <float.h>
-
-#include "qmoe_internal.h"
+#include "route_impl.hpp"
 
 namespace qmoe {
 
 constexpr int kExpandThreads = 1024;
 constexpr int kExpandWaves = kExpandThreads / kLanes;
-
-// Wave-wide top-k of one token.  Returns ids/weights in lane 0's registers
-// (uniform across the wave after the reductions).
-__device__ inline void wave_topk(const float *__restrict__ l, int E, int k, int32_t *ids_out,
-                                 float *w_out, int32_t *ids_lds) {
-  const int lane = threadIdx.x & (kLanes - 1);
-  float v[kMaxExperts / kLanes];
-  bool taken[kMaxExperts / kLanes];
-#pragma unroll
-  for (int i = 0; i < kMaxExperts / kLanes; ++i) {
-    const int e = lane + kLanes * i;
-    v[i] = (e < E) ? l[e] : -FLT_MAX;
-    taken[i] = (e >= E);
-  }
-  float sel_v[kMaxTopK];
-  int sel_i[kMaxTopK];
-  for (int j = 0; j < k; ++j) {
-    float bv = -FLT_MAX;
-    int bi = 0x7FFFFFFF;
-#pragma unroll
-    for (int i = 0; i < kMaxExperts / kLanes; ++i) {
-      const int e = lane + kLanes * i;
-      if (!taken[i] && (bi == 0x7FFFFFFF || v[i] > bv || (v[i] == bv && e < bi))) {
-        bv = v[i];
-        bi = e;
-      }
-    }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ov = __shfl_xor(bv, off);
-      const int oi = __shfl_xor(bi, off);
-      if (oi != 0x7FFFFFFF && (bi == 0x7FFFFFFF || ov > bv || (ov == bv && oi < bi))) {
-        bv = ov;
-        bi = oi;
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < kMaxExperts / kLanes; ++i)
-      if (lane + kLanes * i == bi) taken[i] = true;
-    sel_v[j] = bv;
-    sel_i[j] = bi;
-  }
-  if (lane == 0) {
-    const float m = sel_v[0];
-    float ex[kMaxTopK];
-    float sum = 0.f;
-    for (int j = 0; j < k; ++j) {
-      ex[j] = expf(sel_v[j] - m);
-      sum += ex[j];
-    }
-    for (int j = 0; j < k; ++j) {
-      ids_out[j] = sel_i[j];
-      w_out[j] = ex[j] / sum;
-      if (ids_lds) ids_lds[j] = sel_i[j];
-    }
-  }
-}
 
 __global__ __launch_bounds__(256) void route_topk_kernel(RouteArgs a) {
   const int t = blockIdx.x * (blockDim.x / kLanes) + (threadIdx.x / kLanes);
@@ -230,7 +166,24 @@ __global__ __launch_bounds__(kExpandThreads) void route_expand_kernel(RouteArgs 
   }
 }
 
+// Small decode batches (T * k <= 64 slots, no grouped-path lists): one wave
+// per token routes it, then wave 0 alone builds the expert map.
+__global__ __launch_bounds__(1024) void route_small_kernel(RouteArgs a) {
+  __shared__ int32_t s_ids[kExpandWaves * kMaxTopK];
+  __shared__ int s_cnt[kMaxExperts];
+  const int wave = threadIdx.x / kLanes;
+  if (wave < a.T)
+    wave_topk(a.logits + (int64_t)wave * a.E, a.E, a.k, a.r.ids + (int64_t)wave * a.k,
+              a.r.w + (int64_t)wave * a.k, s_ids + wave * a.k);
+  __syncthreads();
+  if (wave == 0) wave_expand_small(s_ids, a.T * a.k, a.k, a.E, a.max_slots, s_cnt, &a.r, -1, nullptr, nullptr);
+}
+
 hipError_t launch_route(const RouteArgs &a, hipStream_t s) {
+  if (a.topk_in_expand && a.T > 0 && (int64_t)a.T * a.k <= kLanes && a.tile_rows == 0 && a.zero_len == 0) {
+    hipLaunchKernelGGL(route_small_kernel, dim3(1), dim3(a.T * kLanes), 0, s, a);
+    return hipGetLastError();
+  }
   if (!a.topk_in_expand && a.T > 0) {
     const int per = 256 / kLanes;
     hipLaunchKernelGGL(route_topk_kernel, dim3((a.T + per - 1) / per), dim3(256), 0, s, a);

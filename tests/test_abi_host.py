@@ -121,14 +121,21 @@ def test_prepack_validation():
 
 
 def test_plan_gemv_decode():
+    # up to 64 routed slots: FC1 routes the tokens itself
     p = q.forward_plan(_desc(), 1, 6)
     assert p["path"] == 1 and p["gemv_mmax"] == 1 and p["max_active"] == 6
-    assert p["kernels"] == ["route", "gemv_fc1_swiglu", "gemv_fc2", "combine"]
-    assert p["num_launches"] == 4
+    assert p["kernels"] == ["route_fc1_swiglu", "gemv_fc2", "combine"]
+    assert p["num_launches"] == 3
     p1 = q.forward_plan(_desc(), 1, 1)
-    assert p1["kernels"] == ["route", "gemv_fc1_swiglu", "gemv_fc2"] and p1["num_launches"] == 3
+    assert p1["kernels"] == ["route_fc1_swiglu", "gemv_fc2"] and p1["num_launches"] == 2
+    p2 = q.forward_plan(_desc(), 2, 6)
+    assert p2["kernels"] == ["route_fc1_swiglu", "gemv_fc2", "combine"]
+    # more slots: a routing kernel first
     p8 = q.forward_plan(_desc(), 8, 6)
     assert p8["gemv_mmax"] == 8 and p8["max_active"] == 48
+    assert p8["kernels"] == ["route", "gemv_fc1_swiglu", "gemv_fc2", "combine"] and p8["num_launches"] == 4
+    p16 = q.forward_plan(_desc(), 16, 1)
+    assert p16["kernels"] == ["route_fc1_swiglu", "gemv_fc2"]
     p3 = q.forward_plan(_desc(), 3, 6)
     assert p3["gemv_mmax"] == 3
     p0 = q.forward_plan(_desc(), 0, 6)
