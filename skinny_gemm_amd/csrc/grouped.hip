@@ -23,7 +23,11 @@
 //   - activations are staged in LDS as f16 with a per-row power of two
 //     (x * 2^r < 2^14): exact for bf16/f16 x; the fp32 SwiGLU output h is
 //     split into f16 hi + lo parts (about 22 significant bits) and FC2 runs
-//     one MFMA per part against the same dequantized weights.
+//     one MFMA per part against the same dequantized weights (a single f16
+//     h flips too many bf16 output roundings for the tolerance).
+//   - the k-tiles run as a two-stage pipeline: the next tile's weights,
+//     scales and activations are loaded during the current tile's MFMAs,
+//     and the staged activation buffers alternate (one barrier per tile).
 //   - B fragments are read straight from the k-tiled prepacked layout: lane
 //     l of a wave reads dword (l / 16) of row (l % 16) of a 16-row slice,
 //     which that layout stores in the lane's own 16 B; for 2-bit codes a
@@ -103,7 +107,8 @@ __global__ __launch_bounds__(256) void grouped_kernel(const GroupedArgs a) {
   using TR = QtTraits<QT>;
   using CD = Codec<TR::kBits, true>;
   constexpr int KC = 128 / TR::kBits;  // k per 16-B chunk: 32 (4-bit) or 64 (2-bit)
-  constexpr int KT = 128;              // k per staged tile
+  constexpr int NPART = IN_F32 ? 2 : 1;  // fp32 input: f16 hi + lo parts (about 22 bits)
+  constexpr int KT = IN_F32 ? 64 : 128;  // k per staged tile (two buffers of NPART parts fit the LDS)
   constexpr int CPT = KT / KC;         // chunks per tile
   constexpr int KS = KT / 32;          // MFMA k-steps per tile
   constexpr int APAD = 8;              // row padding of the staged tile (halves)
@@ -115,8 +120,7 @@ __global__ __launch_bounds__(256) void grouped_kernel(const GroupedArgs a) {
   // fit f16: the scale is split into an 8-bit head and its tail (two MFMAs)
   constexpr bool MULTIBIT = (QT == QMOE_QTYPE_SYM_INT4 || QT == QMOE_QTYPE_AFFINE_INT4);
 
-  constexpr int NPART = IN_F32 ? 2 : 1;  // fp32 input: f16 hi + lo parts (about 22 bits)
-  __shared__ _Float16 sA[NPART][kTileM][KT + APAD];
+  __shared__ _Float16 sA[2][NPART][kTileM][KT + APAD];
   __shared__ int s_row[kTileM];
   __shared__ float s_rsc[kTileM];
   __shared__ float s_X[AFF ? kTileM : 1][AFF ? kMaxAffineBlocks : 1];  // per-row block sums of x
@@ -181,16 +185,80 @@ __global__ __launch_bounds__(256) void grouped_kernel(const GroupedArgs a) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
-  // staging assignment: 4 threads per row, 32 consecutive k each
-  const int st_r = threadIdx.x >> 2, st_k = (threadIdx.x & 3) * 32;
+  // staging assignment: 4 threads per row, KT/4 consecutive k each
+  constexpr int SEG = KT / 4;
+  const int st_r = threadIdx.x >> 2, st_k = (threadIdx.x & 3) * SEG;
   const int st_in = s_row[st_r];
   const float st_sc = s_rsc[st_r];
 
-  for (int64_t kt = 0; kt < a.K; kt += KT) {
-    // weight dwords and scales of this tile (issued before the staging)
-    // (a partial last tile re-reads the last chunk; its A columns are zero)
-    uint32_t bw[CPT][2];
-    uint32_t sv[CPT][2];
+  // raw activations of one tile for this thread: SEG values in 16-B pieces
+  constexpr int SV = SEG * (IN_F32 ? 4 : 2) / 16;
+  auto stage_load = [&](int64_t kt, uint4 (&S)[SV]) __attribute__((always_inline)) {
+    if (st_in >= 0 && kt + st_k < a.K) {
+      const uint4 *src =
+          IN_F32 ? reinterpret_cast<const uint4 *>(reinterpret_cast<const float *>(a.in) +
+                                                   (int64_t)st_in * a.in_row_elems + kt + st_k)
+                 : reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(a.in) +
+                                                   (int64_t)st_in * a.in_row_elems + kt + st_k);
+#pragma unroll
+      for (int q = 0; q < SV; ++q) S[q] = src[q];
+    }
+  };
+  // scaled f16 into LDS buffer `buf` (zeros past the rows or past K), and
+  // the affine block sums of the scaled values
+  auto stage_store = [&](int64_t kt, const uint4 (&S)[SV], int buf) __attribute__((always_inline)) {
+    _Float16 *dst = &sA[buf][0][st_r][st_k];
+    float xsum = 0.f;
+    if (st_in >= 0 && kt + st_k < a.K) {
+#pragma unroll
+      for (int q = 0; q < SV; ++q) {
+        const uint32_t wv[4] = {S[q].x, S[q].y, S[q].z, S[q].w};
+        if constexpr (IN_F32) {
+          _Float16 *dlo = &sA[buf][NPART - 1][st_r][st_k];
+#pragma unroll
+          for (int h = 0; h < 4; ++h) {
+            const float xs = __uint_as_float(wv[h]) * st_sc;
+            const _Float16 hi = (_Float16)xs;
+            dst[4 * q + h] = hi;
+            dlo[4 * q + h] = (_Float16)(xs - (float)hi);
+            xsum += xs;
+          }
+        } else {
+#pragma unroll
+          for (int h = 0; h < 8; ++h) {
+            const uint32_t bits = (wv[h >> 1] >> (16 * (h & 1))) & 0xFFFFu;
+            const float xs = half_to_f32<IN_F16>(bits) * st_sc;
+            dst[8 * q + h] = (_Float16)xs;
+            xsum += xs;
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int pp = 0; pp < NPART; ++pp)
+#pragma unroll
+        for (int q = 0; q < SEG; ++q) sA[buf][pp][st_r][st_k + q] = (_Float16)0.f;
+    }
+    if constexpr (AFF) {
+      // the 4 threads of a row hold 4 consecutive SEG-k segments; blocks are
+      // 64 or 128 k: a block inside the tile (64 < KT) sums 2 threads, a
+      // block spanning tiles (block >= KT) sums all 4 and is written by its
+      // first tile and added by the next (same thread, in order)
+      const float p1 = xsum + __shfl_xor(xsum, 1);
+      const float p2 = p1 + __shfl_xor(p1, 2);
+      if (kt + st_k < a.K) {
+        if (a.block < KT) {
+          if ((threadIdx.x & 1) == 0) s_X[st_r][(kt + st_k) / a.block] = p1;
+        } else if ((threadIdx.x & 3) == 0) {
+          float &d = s_X[st_r][kt / a.block];
+          d = (kt % a.block == 0) ? p2 : d + p2;
+        }
+      }
+    }
+  };
+  // weight dwords and scales of one tile (a partial last tile re-reads the
+  // last chunk; its A columns are zero)
+  auto load_b = [&](int64_t kt, uint32_t (&bw)[CPT][2], uint32_t (&sv)[CPT][2]) __attribute__((always_inline)) {
     static_for<CPT>([&](auto cc) {
       constexpr int c = decltype(cc)::value;
       const int64_t chunk = min(kt / KC + c, a.NC - 1);
@@ -204,63 +272,25 @@ __global__ __launch_bounds__(256) void grouped_kernel(const GroupedArgs a) {
                        : reinterpret_cast<const uint16_t *>(sbase)[si];
       }
     });
-
-    // stage A: 64 rows x 128 k as scaled f16 (fp32 input: hi and lo parts)
-    {
-      _Float16 *dst = &sA[0][st_r][st_k];
-      float xsum = 0.f;
-      if (st_in >= 0 && kt + st_k < a.K) {
-        if constexpr (IN_F32) {
-          _Float16 *dlo = &sA[NPART - 1][st_r][st_k];
-          const float4 *src = reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(a.in) +
-                                                              (int64_t)st_in * a.in_row_elems + kt + st_k);
+  };
+  const RegConsts<CD::kNC> dk = CodecOps<CD>::in_registers();  // decoder constants in registers
+  auto compute = [&](int buf, const uint32_t (&bw)[CPT][2], const uint32_t (&sv)[CPT][2])
+                     __attribute__((always_inline)) {
+    // per chunk and slice: the pre-scaled f16 scale (head) and its tail,
+    // once per tile
+    f16x2_t s2c[CPT][2], l2c[CPT][2];
 #pragma unroll
-          for (int q = 0; q < 8; ++q) {
-            const float4 v = src[q];
-            const float vv[4] = {v.x * st_sc, v.y * st_sc, v.z * st_sc, v.w * st_sc};
+    for (int c = 0; c < CPT; ++c)
 #pragma unroll
-            for (int h = 0; h < 4; ++h) {
-              const _Float16 hi = (_Float16)vv[h];
-              dst[4 * q + h] = hi;
-              dlo[4 * q + h] = (_Float16)(vv[h] - (float)hi);
-              xsum += vv[h];
-            }
-          }
-        } else {
-          const uint4 *src = reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(a.in) +
-                                                             (int64_t)st_in * a.in_row_elems + kt + st_k);
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const uint4 v = src[q];
-            const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-            for (int h = 0; h < 8; ++h) {
-              const uint32_t bits = (wv[h >> 1] >> (16 * (h & 1))) & 0xFFFFu;
-              const float xs = half_to_f32<IN_F16>(bits) * st_sc;
-              dst[8 * q + h] = (_Float16)xs;
-              xsum += xs;
-            }
-          }
-        }
-      } else {
-#pragma unroll
-        for (int pp = 0; pp < NPART; ++pp)
-#pragma unroll
-          for (int q = 0; q < 32; ++q) sA[pp][st_r][st_k + q] = (_Float16)0.f;
+      for (int j = 0; j < 2; ++j) {
+        const uint32_t sb = sv[c][j];
+        const float s = sf16 ? f16_to_f32(sb & 0xFFFFu) : bf16_to_f32(sb & 0xFFFFu);
+        // head: s rounded to 8 significant bits; tail: the rest (0 for bf16 scales)
+        const float sh = split ? bf16_to_f32(f32_to_bf16_rne(s)) : s;
+        const _Float16 shs = (_Float16)(sh * wsc), sls = (_Float16)((s - sh) * wsc);
+        s2c[c][j] = f16x2_t{shs, shs};
+        l2c[c][j] = f16x2_t{sls, sls};
       }
-      if constexpr (AFF) {
-        // block sums of the scaled activations: the 4 threads of a row hold
-        // 4 consecutive 32-k segments; blocks are 64 or 128 k
-        const float p1 = xsum + __shfl_xor(xsum, 1);
-        const float p2 = p1 + __shfl_xor(p1, 2);
-        if (kt + st_k < a.K) {
-          if (a.block == 64 && (threadIdx.x & 1) == 0) s_X[st_r][(kt + st_k) / 64] = p1;
-          if (a.block == 128 && (threadIdx.x & 3) == 0) s_X[st_r][(kt + st_k) / 128] = p2;
-        }
-      }
-    }
-    __syncthreads();
-
     static_for<KS>([&](auto kc_) {
       constexpr int ks = decltype(kc_)::value;
       constexpr int c = ks * 32 / KC;               // chunk of this k-step
@@ -269,13 +299,8 @@ __global__ __launch_bounds__(256) void grouped_kernel(const GroupedArgs a) {
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         uint32_t pr[CD::kPairs];
-        CD::extract(bw[c][j], pr);
-        const uint32_t sb = sv[c][j];
-        const float s = sf16 ? f16_to_f32(sb & 0xFFFFu) : bf16_to_f32(sb & 0xFFFFu);
-        // head: s rounded to 8 significant bits; tail: the rest (0 for bf16 scales)
-        const float sh = split ? bf16_to_f32(f32_to_bf16_rne(s)) : s;
-        const _Float16 shs = (_Float16)(sh * wsc), sls = (_Float16)((s - sh) * wsc);
-        const f16x2_t s2 = {shs, shs}, l2 = {sls, sls};
+        CD::extract(bw[c][j], pr, dk);
+        const f16x2_t s2 = s2c[c][j], l2 = l2c[c][j];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int jj = half * 4 + q;  // pair index within the dword
@@ -295,7 +320,7 @@ __global__ __launch_bounds__(256) void grouped_kernel(const GroupedArgs a) {
       for (int i = 0; i < 4; ++i) {
 #pragma unroll
         for (int pp = 0; pp < NPART; ++pp) {
-          const half8_t af = *reinterpret_cast<const half8_t *>(&sA[pp][16 * i + (lane & 15)][koff]);
+          const half8_t af = *reinterpret_cast<const half8_t *>(&sA[buf][pp][16 * i + (lane & 15)][koff]);
           if (wave_on) {
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
@@ -306,7 +331,35 @@ __global__ __launch_bounds__(256) void grouped_kernel(const GroupedArgs a) {
         }
       }
     });
+  };
+
+  // Two-stage pipeline over the k-tiles: the next tile's weights, scales and
+  // activations are loaded while the current one is multiplied; one barrier
+  // per tile (the staged buffers alternate).
+  uint32_t bwA[CPT][2], svA[CPT][2], bwB[CPT][2], svB[CPT][2];
+  uint4 S[SV];
+  load_b(0, bwA, svA);
+  stage_load(0, S);
+  stage_store(0, S, 0);
+  __syncthreads();
+  int buf = 0;
+  for (int64_t kt = 0; kt < a.K; kt += KT) {
+    const bool more = kt + KT < a.K;
+    if (more) {
+      load_b(kt + KT, bwB, svB);
+      stage_load(kt + KT, S);
+    }
+    compute(buf, bwA, svA);
+    if (more) stage_store(kt + KT, S, buf ^ 1);
     __syncthreads();
+#pragma unroll
+    for (int c = 0; c < CPT; ++c)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        bwA[c][j] = bwB[c][j];
+        svA[c][j] = svB[c][j];
+      }
+    buf ^= 1;
   }
 
   // affine: + sum over blocks of (b + zc*s) * X[row][block], scaled like acc
