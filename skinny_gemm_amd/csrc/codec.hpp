@@ -201,6 +201,14 @@ __device__ inline float half_to_f32(uint32_t h) {
 __device__ inline float half_to_f32_rt(uint32_t h, int is_f16) {
   return is_f16 ? f16_to_f32(h) : bf16_to_f32(h);
 }
+// Branch-free variant for loops that must not split on the (wave-uniform)
+// scale type: `f16_mask` is all ones for f16, zero for bf16, and should come
+// from opaque_v so the compiler cannot turn the bit select back into a branch.
+__device__ inline float half_to_f32_sel(uint32_t h, uint32_t f16_mask) {
+  const uint32_t f = __float_as_uint(f16_to_f32(h & 0xFFFFu));
+  const uint32_t b = h << 16;
+  return __uint_as_float((f & f16_mask) | (b & ~f16_mask));
+}
 
 // Round to nearest even.  bf16: integer rounding of the float32 pattern.
 __device__ inline uint16_t f32_to_bf16_rne(float v) {

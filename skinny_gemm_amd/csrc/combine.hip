@@ -67,6 +67,7 @@ const void *gemv_kernel_ptr(int qtype, int epilogue, int in_f16, int rows, int b
 hipError_t launch_gemv(const GemvArgs &a, int epilogue, int in_f16, int rows, int waves, int tn, int block,
                        int grid_slots, hipStream_t s) {
   const void *fn = gemv_kernel_ptr(a.qtype, epilogue, in_f16, rows, block, tn);
+  if (fn == nullptr) return hipErrorInvalidConfiguration;  // no kernel for this (rows, tn) pairing
   GemvArgs args = a;
   void *kargs[] = {&args};
   return hipLaunchKernel(fn, dim3((unsigned)(grid_slots * a.RG * (4 / tn))), dim3((unsigned)(waves * kLanes)),
@@ -75,6 +76,7 @@ hipError_t launch_gemv(const GemvArgs &a, int epilogue, int in_f16, int rows, in
 
 int gemv_blocks_per_cu(int qtype, int epilogue, int in_f16, int rows, int waves, int tn, int block) {
   const void *fn = gemv_kernel_ptr(qtype, epilogue, in_f16, rows, block, tn);
+  if (fn == nullptr) return 0;
   const size_t lds = gemv_lds_bytes(rows, epilogue, waves, tn);
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;

@@ -76,19 +76,33 @@ __host__ __device__ constexpr uint32_t small_int_bits(int v) {
   return (uint32_t)(((127 + e) << 7) | ((v - (1 << e)) << (7 - e)));
 }
 
+// Raw buffer loads for the weight stream.  They are intrinsic calls, not IR
+// loads, so the optimiser cannot fold a loop-carried prefetch back into a
+// load at the top of the next iteration (which a phi of two plain loads
+// invites); the wave-uniform base sits in a buffer descriptor in SGPRs and
+// the uniform part of each offset goes in soffset.  Descriptor word 3 is the
+// gfx9-family raw-dword format; num_records bounds the region.
+constexpr int kBufferWord3 = 0x00020000;
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, kBufferWord3);
+}
+__device__ inline uint4 buf_load16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
 // Scales of one row for one k-tile: BYTES = blocks per k-tile x entry size.
 template <int BYTES>
-__device__ inline void load_scales(const uint8_t *p, uint32_t (&sv)[4]) {
+__device__ inline void load_scales(__amdgpu_buffer_rsrc_t r, int voff, int soff, uint32_t (&sv)[4]) {
   if constexpr (BYTES == 16) {
-    const uint4 v = *reinterpret_cast<const uint4 *>(p);
+    const uint4 v = buf_load16(r, voff, soff);
     sv[0] = v.x; sv[1] = v.y; sv[2] = v.z; sv[3] = v.w;
   } else if constexpr (BYTES == 8) {
-    const uint2 v = *reinterpret_cast<const uint2 *>(p);
+    const uint2 v = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
     sv[0] = v.x; sv[1] = v.y; sv[2] = 0; sv[3] = 0;
   } else if constexpr (BYTES == 4) {
-    sv[0] = *reinterpret_cast<const uint32_t *>(p); sv[1] = sv[2] = sv[3] = 0;
+    sv[0] = __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0); sv[1] = sv[2] = sv[3] = 0;
   } else {
-    sv[0] = *reinterpret_cast<const uint16_t *>(p); sv[1] = sv[2] = sv[3] = 0;
+    sv[0] = __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0); sv[1] = sv[2] = sv[3] = 0;
   }
 }
 
@@ -150,10 +164,10 @@ __global__ __launch_bounds__(512) void gemv_kernel(const GemvArgs a) {
       wave_expand_small(s_ids, a.route_T * a.route_k, a.route_k, a.route_E, a.route_max_slots, s_cnt,
                         lead ? &a.route : nullptr, slot, &s_slot, s_rslot);
     __syncthreads();
-    const int4 si = s_slot;
-    e = si.x;
-    M = si.y;
-    pbase = si.z;
+    const int4 si = s_slot;  // the same for every lane: keep it in SGPRs
+    e = __builtin_amdgcn_readfirstlane(si.x);
+    M = __builtin_amdgcn_readfirstlane(si.y);
+    pbase = __builtin_amdgcn_readfirstlane(si.z);
     if (M <= 0) return;
   } else {
     const int4 si = a.slot_info[slot];
@@ -167,15 +181,16 @@ __global__ __launch_bounds__(512) void gemv_kernel(const GemvArgs a) {
   const int NKT = (int)a.NKT, NC = (int)a.NC;
   const int kt0 = (int)((int64_t)wave * NKT / KS), kt1 = (int)((int64_t)(wave + 1) * NKT / KS);
 
-  // A operand rows: lane (r, g) supplies row 16 mt + r
+  // A operand rows: lane (r, g) supplies row 16 mt + r.  Rows past M read
+  // row 0 instead: an A row only feeds the output row of the same index,
+  // which is never stored, so the loads need no per-lane masking.
   const uint32_t *arow[MT];
-  bool aval[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
-    const int m = 16 * mt + r;
-    aval[mt] = m < M;
+    const int m0 = 16 * mt + r;
+    const int m = m0 < M ? m0 : 0;
     int64_t row = 0;
-    if (aval[mt]) {
+    {
       if (a.dense_M > 0) row = m;
       else if constexpr (ROUTED) row = s_rslot[m] / a.route_k;
       else row = a.in_gather_token ? (int64_t)a.token_of[pbase + m] : (int64_t)(pbase + m);
@@ -183,10 +198,13 @@ __global__ __launch_bounds__(512) void gemv_kernel(const GemvArgs a) {
     arow[mt] = a.in + row * a.in_row_pairs;
   }
 
+  // this row group's codes (NKT x 4 KiB) and scales (NKT x 64 rows x BPK entries)
   const uint8_t *wexp = a.w + (int64_t)e * a.expert_stride;
-  const uint4 *wp = reinterpret_cast<const uint4 *>(wexp) + (int64_t)rg * NKT * (4 * kLanes) + lane;
-  const uint8_t *sp = wexp + a.scales_off + ((int64_t)rg * NKT * kLanes + r) * (BPK * ESZ);
-  const bool sf16 = a.sdtype == QMOE_DTYPE_F16;
+  const __amdgpu_buffer_rsrc_t wrs = make_rsrc(wexp + (int64_t)rg * NKT * (4 * kLanes * 16), (uint32_t)NKT * (4 * kLanes * 16));
+  const __amdgpu_buffer_rsrc_t srs = make_rsrc(wexp + a.scales_off + (int64_t)rg * NKT * kLanes * (BPK * ESZ),
+                                               (uint32_t)NKT * kLanes * (BPK * ESZ));
+  const int wvoff = lane * 16, svoff = r * (BPK * ESZ);
+  const uint32_t smask = opaque_v(a.sdtype == QMOE_DTYPE_F16 ? 0xFFFFFFFFu : 0u);
 
   // constant B operands: (base + zero point) per k position, and ones
   uint4 bc[HALVES];
@@ -223,12 +241,17 @@ __global__ __launch_bounds__(512) void gemv_kernel(const GemvArgs a) {
   auto load_w = [&](int kt, Tile &T) __attribute__((always_inline)) {
 #pragma unroll
     for (int t = 0; t < TN; ++t) {
-      T.wv[t] = wp[((int64_t)kt * 4 + t0 + t) * kLanes];
-      load_scales<BPK * ESZ>(sp + ((int64_t)kt * kLanes + 16 * (t0 + t)) * (BPK * ESZ), T.sv[t]);
+      T.wv[t] = buf_load16(wrs, wvoff, (kt * 4 + t0 + t) * (kLanes * 16));
+      load_scales<BPK * ESZ>(srs, svoff, (kt * kLanes + 16 * (t0 + t)) * (BPK * ESZ), T.sv[t]);
     }
   };
+  // Activation fragments of one k-tile.  The main loop covers whole k-tiles
+  // with unconditional loads: any branch around a load makes the compiler's
+  // wait counting fall back to waiting for every load in flight, prefetch
+  // included.  Only the matrix's last k-tile can be partial; it runs after
+  // the loop, its missing chunks with zero activations (their codes are
+  // zero-padded and their scales and biases zero, so they add nothing).
   auto load_a = [&](int kt, Tile &T) __attribute__((always_inline)) {
-    const int nch = min(4, NC - 4 * kt);
     static_for<KSTEPS>([&](auto kc_) {
       constexpr int ks = decltype(kc_)::value;
       constexpr int j = ks / HALVES, h = ks % HALVES;
@@ -237,17 +260,28 @@ __global__ __launch_bounds__(512) void gemv_kernel(const GemvArgs a) {
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int p = 0; p < PARTS; ++p)
-          T.af[ks][mt][p] = (aval[mt] && j < nch)
-                                ? *reinterpret_cast<const uint4 *>(arow[mt] + p * a.in_part_stride + kp)
-                                : make_uint4(0, 0, 0, 0);
+          T.af[ks][mt][p] = *reinterpret_cast<const uint4 *>(arow[mt] + p * a.in_part_stride + kp);
+    });
+  };
+  auto load_a_partial = [&](int kt, Tile &T) __attribute__((always_inline)) {
+    const int nch = NC - 4 * kt;  // chunks present in the partial k-tile (1..3)
+    static_for<KSTEPS>([&](auto kc_) {
+      constexpr int ks = decltype(kc_)::value;
+      constexpr int j = ks / HALVES, h = ks % HALVES;
+      const int64_t kp = (int64_t)kt * (KT / 2) + (BITS == 2 ? (32 * j + 8 * g + 4 * h) : (16 * j + 4 * g));
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int p = 0; p < PARTS; ++p)
+          T.af[ks][mt][p] = (j < nch) ? *reinterpret_cast<const uint4 *>(arow[mt] + p * a.in_part_stride + kp)
+                                      : make_uint4(0, 0, 0, 0);
     });
   };
   auto compute = [&](int kt, const Tile &T) __attribute__((always_inline)) {
-    const int nch = min(4, NC - 4 * kt);  // chunks present in this k-tile
     floatx4_t accW[TN][MT], accC[MT], accX[MT];
     static_for<4>([&](auto jc) {
       constexpr int j = decltype(jc)::value;
-      if (j < nch) {
+      {
         uint32_t pr[TN][CD::kPairs];
 #pragma unroll
         for (int t = 0; t < TN; ++t) {
@@ -280,9 +314,9 @@ __global__ __launch_bounds__(512) void gemv_kernel(const GemvArgs a) {
 #pragma unroll
           for (int t = 0; t < TN; ++t) {
             const uint32_t ent = ESZ == 4 ? T.sv[t][bi] : ((T.sv[t][bi / 2] >> (16 * (bi % 2))) & 0xFFFFu);
-            const float s = sf16 ? f16_to_f32(ent & 0xFFFFu) : bf16_to_f32(ent & 0xFFFFu);
+            const float s = half_to_f32_sel(ent & 0xFFFFu, smask);
             float b = 0.f;
-            if constexpr (AFF) b = sf16 ? f16_to_f32(ent >> 16) : bf16_to_f32(ent >> 16);
+            if constexpr (AFF) b = half_to_f32_sel(ent >> 16, smask);
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -297,41 +331,59 @@ __global__ __launch_bounds__(512) void gemv_kernel(const GemvArgs a) {
     });
   };
 
-  // k-tile loop.  PF 0: load and compute one k-tile at a time; PF 1: the
-  // weights and scales of the next k-tile are in flight during the compute
-  // (the activations, L2 hits, are issued first so that waiting for them
-  // never waits for the prefetch); PF 2: the activations are prefetched too.
-  constexpr int PF = QMOE_GEMV_PREFETCH;
+  // k-tile loop.  PF 0: load and compute one k-tile at a time.  PF 1: the
+  // weights and scales of the next k-tile are in flight during the compute;
+  // the activations (L2 hits) are issued before that prefetch, so waiting for
+  // them never waits for it.  The loop body is straight-line code over two
+  // k-tiles (the two register sets swap roles without moves) and the
+  // prefetch is unconditional -- past the last whole k-tile it re-reads that
+  // tile -- because a load under a branch makes the compiler's wait counting
+  // assume the shorter path and wait for the prefetch too.
+  // Two row tiles hold twice the activations and accumulators; with a
+  // second register set for the prefetch they would spill, so they load
+  // one k-tile at a time.
+  static_assert(QMOE_GEMV_PREFETCH == 0 || QMOE_GEMV_PREFETCH == 1, "QMOE_GEMV_PREFETCH is 0 or 1");
+  constexpr int PF = MT > 1 ? 0 : QMOE_GEMV_PREFETCH;
+  const int ktf = min(kt1, NC / 4);  // end of this wave's whole k-tiles
   Tile TA, TB;
-  if (PF > 0 && kt0 < kt1) {
-    if constexpr (PF == 2) load_a(kt0, TA);
-    load_w(kt0, TA);
-  }
   if constexpr (PF == 0) {
-    for (int kt = kt0; kt < kt1; ++kt) {
+    for (int kt = kt0; kt < ktf; ++kt) {
       load_a(kt, TA);
       load_w(kt, TA);
       compute(kt, TA);
     }
-  } else if (kt0 < kt1) {
-    for (int kt = kt0; kt < kt1; kt += 2) {
-      const bool h1 = kt + 1 < kt1;
-      if constexpr (PF == 1) load_a(kt, TA);
-      if (h1) {
-        if constexpr (PF == 2) load_a(kt + 1, TB);
-        load_w(kt + 1, TB);
-      }
+  } else if (kt0 < ktf) {
+    int kt = kt0;
+    if ((ktf - kt0) & 1) {  // odd count: one k-tile without prefetch first
+      load_a(kt, TA);
+      load_w(kt, TA);
       compute(kt, TA);
-      if (h1) {
-        const bool h2 = kt + 2 < kt1;
-        if constexpr (PF == 1) load_a(kt + 1, TB);
-        if (h2) {
-          if constexpr (PF == 2) load_a(kt + 2, TA);
-          load_w(kt + 2, TA);
-        }
+      ++kt;
+    }
+    if (kt < ktf) {
+      const int last = ktf - 1;
+      load_w(kt, TA);
+      // the fences keep the scheduler from starting a k-tile's decode before
+      // the loads issued ahead of it, which would wait for the prefetch
+      for (; kt < ktf; kt += 2) {
+        load_a(kt, TA);
+        load_w(kt + 1, TB);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(kt, TA);
+        __builtin_amdgcn_sched_barrier(0);
+        load_a(kt + 1, TB);
+        load_w(min(kt + 2, last), TA);
+        __builtin_amdgcn_sched_barrier(0);
         compute(kt + 1, TB);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
+  }
+  // the partial last k-tile of the matrix, when it is this wave's
+  for (int kt = max(kt0, ktf); kt < kt1; ++kt) {
+    load_a_partial(kt, TA);
+    load_w(kt, TA);
+    compute(kt, TA);
   }
 
   // cross-wave reduction in a fixed order, then the epilogue
@@ -396,6 +448,7 @@ const void *gemv_ptr_block(int block, int tn) {
   if (tn == 1)
     return block == 64 ? reinterpret_cast<const void *>(&gemv_kernel<QT, XF16, PARTS, EPI, MR, MT, 64, 1>)
                        : reinterpret_cast<const void *>(&gemv_kernel<QT, XF16, PARTS, EPI, MR, MT, 128, 1>);
+  if (tn != 4) return nullptr;
   return block == 64 ? reinterpret_cast<const void *>(&gemv_kernel<QT, XF16, PARTS, EPI, MR, MT, 64, 4>)
                      : reinterpret_cast<const void *>(&gemv_kernel<QT, XF16, PARTS, EPI, MR, MT, 128, 4>);
 }

@@ -1,4 +1,4 @@
-// grouped.hip -- grouped larger-M path: tiles of 64 routed rows x 128 outputs
+// grouped.hip -- grouped larger-M path: tiles of 64 routed rows x 128 or 256 outputs
 // per workgroup, MFMA (v_mfma_f32_16x16x32_f16) on weights dequantized once
 // per tile in registers.
 //
@@ -127,7 +127,13 @@ __global__ __launch_bounds__(256) void grouped_kernel(const GroupedArgs a) {
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int ntn = (int)((a.N + kTileN - 1) / kTileN);
+  // 16-column slices per wave: 4 (tile of 256 outputs) for the fp32 FC2
+  // input, whose f16 hi + lo parts double the MFMAs per dequantized weight
+  // fragment; 2 (128 outputs) for 16-bit inputs, where the occupancy of the
+  // narrower tile measured faster
+  constexpr int NJ = IN_F32 ? 4 : 2;
+  constexpr int TW = 4 * 16 * NJ;  // outputs per tile
+  const int ntn = (int)((a.N + TW - 1) / TW);
 
   // XCD-aware remap: blocks are dealt round-robin to 8 XCDs; give each XCD a
   // contiguous range of tiles (n-tile major, row tiles of an expert adjacent)
@@ -164,8 +170,8 @@ __global__ __launch_bounds__(256) void grouped_kernel(const GroupedArgs a) {
   __syncthreads();
 
   const float wsc = a.wsc[e];
-  const int nw = nt * kTileN + wave * 32;  // first output row of this wave
-  const bool wave_on = nw < a.N;           // N % 128 == 64: the last tile's upper half is idle
+  const int nw = nt * TW + wave * 16 * NJ;  // first output row of this wave
+  const bool wave_on = nw < a.N;           // N not a multiple of the tile: the last tile's upper waves idle
   const int64_t rg = (wave_on ? nw : 0) / kRowsPerGroup;
   const int nl0 = nw % kRowsPerGroup;
   const uint8_t *wexp = a.w + (int64_t)e * a.expert_stride;
@@ -173,17 +179,17 @@ __global__ __launch_bounds__(256) void grouped_kernel(const GroupedArgs a) {
   const uint32_t *wbase = reinterpret_cast<const uint32_t *>(wexp) + rg * a.NKT * (4 * kLanes * 4);
   const uint8_t *sbase = wexp + a.scales_off;
   const int g = lane >> 4;
-  int nl[2];
-  nl[0] = nl0 + (lane & 15);
-  nl[1] = nl0 + 16 + (lane & 15);
+  int nl[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) nl[j] = nl0 + 16 * j + (lane & 15);
   const bool sf16 = a.sdtype == QMOE_DTYPE_F16;
   const bool split = MULTIBIT && sf16;
 
-  floatx4_t acc[4][2];
+  floatx4_t acc[4][NJ];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < NJ; ++j) acc[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
   // staging assignment: 4 threads per row, KT/4 consecutive k each
   constexpr int SEG = KT / 4;
@@ -207,37 +213,50 @@ __global__ __launch_bounds__(256) void grouped_kernel(const GroupedArgs a) {
   // scaled f16 into LDS buffer `buf` (zeros past the rows or past K), and
   // the affine block sums of the scaled values
   auto stage_store = [&](int64_t kt, const uint4 (&S)[SV], int buf) __attribute__((always_inline)) {
-    _Float16 *dst = &sA[buf][0][st_r][st_k];
+    // 16-B LDS stores of 8 converted values each
+    half8_t *dst = reinterpret_cast<half8_t *>(&sA[buf][0][st_r][st_k]);
+    half8_t *dlo = reinterpret_cast<half8_t *>(&sA[buf][NPART - 1][st_r][st_k]);
     float xsum = 0.f;
     if (st_in >= 0 && kt + st_k < a.K) {
+      if constexpr (IN_F32) {
 #pragma unroll
-      for (int q = 0; q < SV; ++q) {
-        const uint32_t wv[4] = {S[q].x, S[q].y, S[q].z, S[q].w};
-        if constexpr (IN_F32) {
-          _Float16 *dlo = &sA[buf][NPART - 1][st_r][st_k];
+        for (int q = 0; q < SV / 2; ++q) {
+          half8_t hv, lv;
 #pragma unroll
-          for (int h = 0; h < 4; ++h) {
-            const float xs = __uint_as_float(wv[h]) * st_sc;
+          for (int h = 0; h < 8; ++h) {
+            const uint4 &v = S[2 * q + h / 4];
+            const uint32_t w = (h % 4 == 0) ? v.x : (h % 4 == 1) ? v.y : (h % 4 == 2) ? v.z : v.w;
+            const float xs = __uint_as_float(w) * st_sc;
             const _Float16 hi = (_Float16)xs;
-            dst[4 * q + h] = hi;
-            dlo[4 * q + h] = (_Float16)(xs - (float)hi);
+            hv[h] = hi;
+            lv[h] = (_Float16)(xs - (float)hi);
             xsum += xs;
           }
-        } else {
+          dst[q] = hv;
+          dlo[q] = lv;
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < SV; ++q) {
+          const uint32_t wv[4] = {S[q].x, S[q].y, S[q].z, S[q].w};
+          half8_t hv;
 #pragma unroll
           for (int h = 0; h < 8; ++h) {
             const uint32_t bits = (wv[h >> 1] >> (16 * (h & 1))) & 0xFFFFu;
             const float xs = half_to_f32<IN_F16>(bits) * st_sc;
-            dst[8 * q + h] = (_Float16)xs;
+            hv[h] = (_Float16)xs;
             xsum += xs;
           }
+          dst[q] = hv;
         }
       }
     } else {
+      const half8_t z = {};
 #pragma unroll
-      for (int pp = 0; pp < NPART; ++pp)
-#pragma unroll
-        for (int q = 0; q < SEG; ++q) sA[buf][pp][st_r][st_k + q] = (_Float16)0.f;
+      for (int q = 0; q < SEG / 8; ++q) {
+        dst[q] = z;
+        if constexpr (NPART == 2) dlo[q] = z;
+      }
     }
     if constexpr (AFF) {
       // the 4 threads of a row hold 4 consecutive SEG-k segments; blocks are
@@ -258,31 +277,36 @@ __global__ __launch_bounds__(256) void grouped_kernel(const GroupedArgs a) {
   };
   // weight dwords and scales of one tile (a partial last tile re-reads the
   // last chunk; its A columns are zero)
-  auto load_b = [&](int64_t kt, uint32_t (&bw)[CPT][2], uint32_t (&sv)[CPT][2]) __attribute__((always_inline)) {
+  // chunk -> scale entry without divisions: a k-tile holds 4 chunks, and
+  // blocks x chunks-per-block = 4, so the k-tile of chunk c is c >> 2 and
+  // its block within the k-tile is (c >> log2(chunks per block)) & (bpk - 1)
+  const int cpb_log = __builtin_ctz((unsigned)(a.block / KC));
+  const int bpk = a.bpk;
+  auto load_b = [&](int64_t kt, uint32_t (&bw)[CPT][NJ], uint32_t (&sv)[CPT][NJ]) __attribute__((always_inline)) {
     static_for<CPT>([&](auto cc) {
       constexpr int c = decltype(cc)::value;
-      const int64_t chunk = min(kt / KC + c, a.NC - 1);
-      const int64_t blk = (chunk * KC) / a.block;
+      const int chunk = min((int)(kt / KC) + c, (int)a.NC - 1);
+      const int ktile = chunk >> 2, bi = (chunk >> cpb_log) & (bpk - 1);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
+      for (int j = 0; j < NJ; ++j) {
         // dword g of the chunk of row nl[j] sits in lane (nl[j] % 16) + 16 g of its n-tile
-        bw[c][j] = wbase[(((chunk / 4) * 4 + (nl[j] >> 4)) * kLanes + lane) * 4 + (chunk % 4)];
-        const int64_t si = ((rg * a.NKT + blk / a.bpk) * kLanes + nl[j]) * a.bpk + blk % a.bpk;
+        bw[c][j] = wbase[(((int64_t)ktile * 4 + (nl[j] >> 4)) * kLanes + lane) * 4 + (chunk & 3)];
+        const int64_t si = ((rg * a.NKT + ktile) * kLanes + nl[j]) * bpk + bi;
         sv[c][j] = AFF ? reinterpret_cast<const uint32_t *>(sbase)[si]
                        : reinterpret_cast<const uint16_t *>(sbase)[si];
       }
     });
   };
   const RegConsts<CD::kNC> dk = CodecOps<CD>::in_registers();  // decoder constants in registers
-  auto compute = [&](int buf, const uint32_t (&bw)[CPT][2], const uint32_t (&sv)[CPT][2])
+  auto compute = [&](int buf, const uint32_t (&bw)[CPT][NJ], const uint32_t (&sv)[CPT][NJ])
                      __attribute__((always_inline)) {
     // per chunk and slice: the pre-scaled f16 scale (head) and its tail,
     // once per tile
-    f16x2_t s2c[CPT][2], l2c[CPT][2];
+    f16x2_t s2c[CPT][NJ], l2c[CPT][NJ];
 #pragma unroll
     for (int c = 0; c < CPT; ++c)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
+      for (int j = 0; j < NJ; ++j) {
         const uint32_t sb = sv[c][j];
         const float s = sf16 ? f16_to_f32(sb & 0xFFFFu) : bf16_to_f32(sb & 0xFFFFu);
         // head: s rounded to 8 significant bits; tail: the rest (0 for bf16 scales)
@@ -295,9 +319,9 @@ __global__ __launch_bounds__(256) void grouped_kernel(const GroupedArgs a) {
       constexpr int ks = decltype(kc_)::value;
       constexpr int c = ks * 32 / KC;               // chunk of this k-step
       constexpr int half = (ks * 32 % KC) / 32;     // 2-bit: which 8 of the dword's 16 k
-      half8_t bf[2], bl[2];
+      half8_t bf[NJ], bl[NJ];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
+      for (int j = 0; j < NJ; ++j) {
         uint32_t pr[CD::kPairs];
         CD::extract(bw[c][j], pr, dk);
         const f16x2_t s2 = s2c[c][j], l2 = l2c[c][j];
@@ -323,7 +347,7 @@ __global__ __launch_bounds__(256) void grouped_kernel(const GroupedArgs a) {
           const half8_t af = *reinterpret_cast<const half8_t *>(&sA[buf][pp][16 * i + (lane & 15)][koff]);
           if (wave_on) {
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
+            for (int j = 0; j < NJ; ++j) {
               acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf[j], acc[i][j], 0, 0, 0);
               if (split) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bl[j], acc[i][j], 0, 0, 0);
             }
@@ -336,7 +360,7 @@ __global__ __launch_bounds__(256) void grouped_kernel(const GroupedArgs a) {
   // Two-stage pipeline over the k-tiles: the next tile's weights, scales and
   // activations are loaded while the current one is multiplied; one barrier
   // per tile (the staged buffers alternate).
-  uint32_t bwA[CPT][2], svA[CPT][2], bwB[CPT][2], svB[CPT][2];
+  uint32_t bwA[CPT][NJ], svA[CPT][NJ], bwB[CPT][NJ], svB[CPT][NJ];
   uint4 S[SV];
   load_b(0, bwA, svA);
   stage_load(0, S);
@@ -355,7 +379,7 @@ __global__ __launch_bounds__(256) void grouped_kernel(const GroupedArgs a) {
 #pragma unroll
     for (int c = 0; c < CPT; ++c)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
+      for (int j = 0; j < NJ; ++j) {
         bwA[c][j] = bwB[c][j];
         svA[c][j] = svB[c][j];
       }
@@ -366,9 +390,9 @@ __global__ __launch_bounds__(256) void grouped_kernel(const GroupedArgs a) {
   if constexpr (AFF) {
     if (wave_on) {
       for (int blk = 0; blk < (int)a.nblk; ++blk) {
-        float bb[2];
+        float bb[NJ];
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+        for (int j = 0; j < NJ; ++j) {
           const uint32_t sb = reinterpret_cast<const uint32_t *>(
               sbase)[((rg * a.NKT + blk / a.bpk) * kLanes + nl[j]) * a.bpk + blk % a.bpk];
           const float s = sf16 ? f16_to_f32(sb & 0xFFFFu) : bf16_to_f32(sb & 0xFFFFu);
@@ -381,7 +405,7 @@ __global__ __launch_bounds__(256) void grouped_kernel(const GroupedArgs a) {
           for (int el = 0; el < 4; ++el) {
             const float X = s_X[16 * i + 4 * g + el][blk];
 #pragma unroll
-            for (int j = 0; j < 2; ++j) acc[i][j][el] = fmaf(bb[j], X, acc[i][j][el]);
+            for (int j = 0; j < NJ; ++j) acc[i][j][el] = fmaf(bb[j], X, acc[i][j][el]);
           }
       }
     }
@@ -398,7 +422,7 @@ __global__ __launch_bounds__(256) void grouped_kernel(const GroupedArgs a) {
       const float inv = valid ? winv / s_rsc[m] : 0.f;
       float hmax = 0.f;
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
+      for (int j = 0; j < NJ; ++j) {
         const float v = acc[i][j][el] * inv;
         const int64_t n = nw + 16 * j + (lane & 15);
         if constexpr (EPI == kGEpiSwiGLU) {
@@ -445,7 +469,8 @@ hipError_t launch_grouped_qt(const GroupedArgs &a, int epi, int grid, hipStream_
 }
 
 hipError_t launch_grouped(const GroupedArgs &a, int epilogue, int grid_tiles, hipStream_t s) {
-  const int ntn = (int)((a.N + kTileN - 1) / kTileN);
+  const int tw = a.in_f32 ? kTileNWide : kTileN;  // as the kernel's tile width
+  const int ntn = (int)((a.N + tw - 1) / tw);
   const int grid = grid_tiles * ntn;
   if (grid == 0) return hipSuccess;
   switch (a.qtype) {

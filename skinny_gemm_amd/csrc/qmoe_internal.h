@@ -226,10 +226,12 @@ constexpr int kGemvMaxWaves = 8;
 
 // Dynamic LDS of one GEMV workgroup: the cross-wave partial sums of the
 // tn n-tiles x row tiles x accumulator elements x 64 lanes.
+inline int gemv_row_tiles(int rows, int epilogue) { return (epilogue == kEpiStoreAct && rows > 16) ? 2 : 1; }
 inline size_t gemv_lds_bytes(int rows, int epilogue, int waves, int tn) {
-  const int mt = (epilogue == kEpiStoreAct && rows > 16) ? 2 : 1, mr = rows > 1 ? 4 : 1;
+  const int mt = gemv_row_tiles(rows, epilogue), mr = rows > 1 ? 4 : 1;
   return (size_t)waves * tn * (size_t)mt * (size_t)mr * kLanes * sizeof(float);
 }
+
 constexpr size_t kGemvLdsLimit = 64 * 1024;
 
 // Host launchers (defined in the kernel translation units).
@@ -251,7 +253,8 @@ hipError_t launch_combine(const float *o, const int32_t *slot_pos, const float *
 
 // ----------------------------------------------------------- grouped MFMA
 constexpr int kTileM = 64;   // rows (tokens) per grouped tile
-constexpr int kTileN = 128;  // outputs per grouped tile (4 waves x 32)
+constexpr int kTileN = 128;      // outputs per grouped tile, 16-bit input (4 waves x 32)
+constexpr int kTileNWide = 256;  // outputs per grouped tile, fp32 input (4 waves x 64)
 
 enum GroupedEpilogue { kGEpiSwiGLU = 0, kGEpiStoreF32 = 1, kGEpiStoreAct = 2 };
 
