@@ -128,8 +128,11 @@ typedef struct qmoe_forward_opts {
   int32_t *ids_out;  /* optional device [T][k]: routed expert ids */
   float *w_out;      /* optional device [T][k]: routing weights */
   int32_t *counts_out; /* optional device [E]: rows routed to each expert */
-  void **events;     /* optional host array of hipEvent_t: events[2i] / events[2i+1] are
-                        recorded on `stream` before / after stage i of the plan's stage list */
+  void **events;     /* optional host array of hipEvent_t created with timing: events[2i] /
+                        events[2i+1] receive the begin timestamp of the first kernel and the
+                        end timestamp of the last kernel of stage i of the plan's stage list
+                        (the kernels' own dispatch timestamps, as a kernel trace reports them);
+                        a stage whose pair is incomplete is not timed */
   int32_t num_events; /* entries in `events` (0 = none) */
   int32_t reserved2;  /* must be 0 */
 } qmoe_forward_opts;

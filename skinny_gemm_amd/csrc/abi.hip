@@ -19,6 +19,13 @@
 
 using namespace qmoe;
 
+namespace qmoe {
+StageEvents &stage_events() {
+  thread_local StageEvents ev;
+  return ev;
+}
+}  // namespace qmoe
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -478,15 +485,27 @@ qmoe_status qmoe_forward_ex(const qmoe_layer_desc *desc, const void *packed, con
   ra.zero_len = p.path == QMOE_PATH_GROUPED ? (int)((int64_t)T * top_k) : 0;
   ra.tile_rows = p.path == QMOE_PATH_GROUPED ? kTileM : 0;
   ra.max_tiles = p.max_tiles;
-  // optional per-stage events (diagnostic timing)
-  auto rec = [&](int slot) -> hipError_t {
-    if (!opts || !opts->events || slot >= opts->num_events || !opts->events[slot]) return hipSuccess;
-    return hipEventRecord((hipEvent_t)opts->events[slot], s);
+  // optional per-stage events (diagnostic timing): stage i of the plan's
+  // stage list stamps events 2i / 2i+1 with the begin of its first kernel
+  // and the end of its last (see StageEvents)
+  auto ev = [&](int slot) -> hipEvent_t {
+    if (!opts || !opts->events || slot >= opts->num_events) return nullptr;
+    return (hipEvent_t)opts->events[slot];
   };
-  // stage i of the plan's stage list records events 2i and 2i+1
   int stage = 0;
-  auto begin = [&]() -> hipError_t { return rec(2 * stage); };
-  auto end = [&]() -> hipError_t { return rec(2 * stage++ + 1); };
+  struct StageReset {  // no events stay set past this call, error returns included
+    ~StageReset() { stage_events() = StageEvents{}; }
+  } stage_reset;
+  auto begin = [&]() -> hipError_t {
+    hipEvent_t a = ev(2 * stage), b = ev(2 * stage + 1);
+    stage_events() = (a && b) ? StageEvents{a, b, false} : StageEvents{};
+    return hipSuccess;
+  };
+  auto end = [&]() -> hipError_t {
+    stage_events() = StageEvents{};
+    ++stage;
+    return hipSuccess;
+  };
   hipError_t e = hipSuccess;
   const bool fc1_routes = p.path == QMOE_PATH_GEMV && p.fc1_routes;
   if (!fc1_routes) {

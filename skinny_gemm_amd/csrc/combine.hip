@@ -43,9 +43,8 @@ hipError_t launch_combine(const float *o, const int32_t *slot_pos, const float *
                           int H, int act_dtype, uint16_t *y, hipStream_t s) {
   const int64_t total = (int64_t)T * (H / 4);
   if (total == 0) return hipSuccess;
-  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, o,
-                     slot_pos, w, T, k, H, act_dtype == QMOE_DTYPE_F16 ? 1 : 0, y);
-  return hipGetLastError();
+  return qlaunch(combine_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, o, slot_pos, w, T, k, H,
+                 act_dtype == QMOE_DTYPE_F16 ? 1 : 0, y);
 }
 
 const void *gemv_ptr_sym_int4(int, int, int, int, int);
@@ -70,8 +69,8 @@ hipError_t launch_gemv(const GemvArgs &a, int epilogue, int in_f16, int rows, in
   if (fn == nullptr) return hipErrorInvalidConfiguration;  // no kernel for this (rows, tn) pairing
   GemvArgs args = a;
   void *kargs[] = {&args};
-  return hipLaunchKernel(fn, dim3((unsigned)(grid_slots * a.RG * (4 / tn))), dim3((unsigned)(waves * kLanes)),
-                         kargs, gemv_lds_bytes(rows, epilogue, waves, tn), s);
+  return launch_raw(fn, dim3((unsigned)(grid_slots * a.RG * (4 / tn))), dim3((unsigned)(waves * kLanes)), kargs,
+                    gemv_lds_bytes(rows, epilogue, waves, tn), s);
 }
 
 int gemv_blocks_per_cu(int qtype, int epilogue, int in_f16, int rows, int waves, int tn, int block) {

@@ -452,13 +452,9 @@ __global__ __launch_bounds__(256) void grouped_kernel(const GroupedArgs a) {
 
 template <int QT, int EPI>
 hipError_t launch_grouped_in(const GroupedArgs &a, int grid, hipStream_t s) {
-  if (a.in_f32)
-    hipLaunchKernelGGL((grouped_kernel<QT, EPI, true, false>), dim3(grid), dim3(256), 0, s, a);
-  else if (a.in_f16)
-    hipLaunchKernelGGL((grouped_kernel<QT, EPI, false, true>), dim3(grid), dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL((grouped_kernel<QT, EPI, false, false>), dim3(grid), dim3(256), 0, s, a);
-  return hipGetLastError();
+  if (a.in_f32) return qlaunch(grouped_kernel<QT, EPI, true, false>, dim3(grid), dim3(256), 0, s, a);
+  if (a.in_f16) return qlaunch(grouped_kernel<QT, EPI, false, true>, dim3(grid), dim3(256), 0, s, a);
+  return qlaunch(grouped_kernel<QT, EPI, false, false>, dim3(grid), dim3(256), 0, s, a);
 }
 
 template <int QT>
@@ -484,14 +480,12 @@ hipError_t launch_grouped(const GroupedArgs &a, int epilogue, int grid_tiles, hi
 
 hipError_t launch_rowscale(const void *x, int rows, int64_t K, int in_f16, float *rowsc, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
-  hipLaunchKernelGGL(rowscale_kernel, dim3((rows + 3) / 4), dim3(256), 0, s, (const uint16_t *)x, rows, K,
-                     in_f16, rowsc);
-  return hipGetLastError();
+  return qlaunch(rowscale_kernel, dim3((rows + 3) / 4), dim3(256), 0, s, (const uint16_t *)x, rows, K, in_f16,
+                 rowsc);
 }
 
 hipError_t launch_wscale(const MatLayout &L, int E, const uint8_t *mat, float *wsc, hipStream_t s) {
-  hipLaunchKernelGGL(wscale_kernel, dim3(E), dim3(256), 0, s, L, mat, wsc);
-  return hipGetLastError();
+  return qlaunch(wscale_kernel, dim3(E), dim3(256), 0, s, L, mat, wsc);
 }
 
 }  // namespace qmoe

@@ -2,8 +2,12 @@
 // the host ABI (abi.hip) and the gfx950 kernels.  Host + device.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <tuple>
+#include <utility>
 
 #include "../../include/qmoe.h"
 
@@ -287,5 +291,39 @@ struct GroupedArgs {
 hipError_t launch_grouped(const GroupedArgs &a, int epilogue, int grid_tiles, hipStream_t s);
 hipError_t launch_rowscale(const void *x, int rows, int64_t K, int in_f16, float *rowsc, hipStream_t s);
 hipError_t launch_wscale(const MatLayout &L, int E, const uint8_t *mat, float *wsc, hipStream_t s);
+
+// ---------------------------------------------------------------- launches
+// Stage timing: while the calling thread has stage events set, every kernel
+// goes through hipExtLaunchKernel, which stamps `start` with the begin
+// timestamp of the stage's first kernel and `stop` with the end timestamp of
+// each kernel (the last kernel's stays), the dispatch timestamps a kernel
+// trace reads.  Without events the launch is a plain hipLaunchKernel.
+struct StageEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+  bool started = false;
+};
+StageEvents &stage_events();  // per host thread
+
+inline hipError_t launch_raw(const void *fn, dim3 grid, dim3 block, void **argv, size_t lds, hipStream_t s) {
+  StageEvents &ev = stage_events();
+  if (ev.stop == nullptr) return hipLaunchKernel(fn, grid, block, argv, lds, s);
+  hipEvent_t st = ev.started ? nullptr : ev.start;
+  ev.started = true;
+  return hipExtLaunchKernel(fn, grid, block, argv, lds, s, st, ev.stop, 0);
+}
+
+// Typed launch: the arguments are converted to the kernel's parameter types
+// before their addresses are handed to the runtime.
+template <typename... P, typename... A>
+inline hipError_t qlaunch(void (*kernel)(P...), dim3 grid, dim3 block, size_t lds, hipStream_t s, A &&...args) {
+  static_assert(sizeof...(P) == sizeof...(A), "kernel argument count");
+  std::tuple<P...> t(static_cast<P>(std::forward<A>(args))...);
+  void *argv[sizeof...(P) > 0 ? sizeof...(P) : 1];
+  std::apply([&](auto &...x) {
+    int i = 0;
+    ((argv[i++] = static_cast<void *>(&x)), ...);
+  }, t);
+  return launch_raw(reinterpret_cast<const void *>(kernel), grid, block, argv, lds, s);
+}
 
 }  // namespace qmoe

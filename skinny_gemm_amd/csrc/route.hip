@@ -181,15 +181,14 @@ __global__ __launch_bounds__(1024) void route_small_kernel(RouteArgs a) {
 
 hipError_t launch_route(const RouteArgs &a, hipStream_t s) {
   if (a.topk_in_expand && a.T > 0 && (int64_t)a.T * a.k <= kLanes && a.tile_rows == 0 && a.zero_len == 0) {
-    hipLaunchKernelGGL(route_small_kernel, dim3(1), dim3(a.T * kLanes), 0, s, a);
-    return hipGetLastError();
+    return qlaunch(route_small_kernel, dim3(1), dim3(a.T * kLanes), 0, s, a);
   }
   if (!a.topk_in_expand && a.T > 0) {
     const int per = 256 / kLanes;
-    hipLaunchKernelGGL(route_topk_kernel, dim3((a.T + per - 1) / per), dim3(256), 0, s, a);
+    const hipError_t e = qlaunch(route_topk_kernel, dim3((a.T + per - 1) / per), dim3(256), 0, s, a);
+    if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(route_expand_kernel, dim3(1), dim3(kExpandThreads), 0, s, a);
-  return hipGetLastError();
+  return qlaunch(route_expand_kernel, dim3(1), dim3(kExpandThreads), 0, s, a);
 }
 
 }  // namespace qmoe
