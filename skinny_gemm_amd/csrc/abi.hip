@@ -146,7 +146,7 @@ struct RouteWs {
 // and the per-token activation scales.  Both paths write o [S][H] fp32.
 struct MoeWs {
   RouteWs route;
-  int64_t h_hi, h_lo, h32, hmax, xsc, o, total;
+  int64_t h_hi, h_lo, h32, hmax, xsc, xs16, o, total;
   static MoeWs make(const qmoe_layer_desc &d, int32_t T, int32_t k, bool grouped) {
     MoeWs w;
     Carve c;
@@ -157,10 +157,11 @@ struct MoeWs {
       w.h32 = c.take(S * d.inter * 4);
       w.hmax = c.take(S * 4);
       w.xsc = c.take((int64_t)T * 4);
+      w.xs16 = c.take((int64_t)T * d.hidden * 2);
     } else {
       w.h_hi = c.take(S * d.inter * 2);
       w.h_lo = c.take(S * d.inter * 2);
-      w.h32 = w.hmax = w.xsc = 0;
+      w.h32 = w.hmax = w.xsc = w.xs16 = 0;
     }
     w.o = c.take(S * d.hidden * 4);
     w.total = c.off;
@@ -519,17 +520,18 @@ qmoe_status qmoe_forward_ex(const qmoe_layer_desc *desc, const void *packed, con
   if (p.path == QMOE_PATH_GROUPED) {
     float *xsc = (float *)(wsb + W.xsc), *h32 = (float *)(wsb + W.h32);
     uint32_t *hmax = (uint32_t *)(wsb + W.hmax);
+    uint16_t *xs16 = (uint16_t *)(wsb + W.xs16);
     const float *wsc = (const float *)(pk + L.wsc_off);
     e = begin();
-    if (e == hipSuccess) e = launch_rowscale(x, T, desc->hidden, desc->act_dtype == QMOE_DTYPE_F16, xsc, s);
+    if (e == hipSuccess) e = launch_rowscale(x, T, desc->hidden, desc->act_dtype == QMOE_DTYPE_F16, xsc, xs16, s);
     if (e == hipSuccess) e = end();
     if (e != hipSuccess) return hip_status(e, "rowscale");
     GroupedArgs q1 = grouped_base(L.fc1, pk + L.fc1_off, wsc);
     q1.tile_info = ra.r.tile_info;
     q1.token_of = ra.r.token_of;
     q1.in_gather_token = 1;
-    q1.in = x;
-    q1.in_f16 = desc->act_dtype == QMOE_DTYPE_F16;
+    q1.in = xs16;  // the token rows scaled once, staged by copy in every tile
+    q1.in_scaled = 1;
     q1.in_row_elems = desc->hidden;
     q1.in_rowsc = xsc;
     q1.out_f32 = h32;
@@ -764,7 +766,7 @@ qmoe_status qmoe_linear(const qmoe_qmatrix_desc *desc, const void *packed, const
     if (ws_bytes < need)
       return fail(QMOE_ERR_WORKSPACE_TOO_SMALL, "workspace holds %zu bytes, %zu needed", ws_bytes, need);
     float *xsc = (float *)ws;
-    hipError_t e = launch_rowscale(x, M, L.K, x_dtype == QMOE_DTYPE_F16, xsc, s);
+    hipError_t e = launch_rowscale(x, M, L.K, x_dtype == QMOE_DTYPE_F16, xsc, nullptr, s);
     if (e != hipSuccess) return hip_status(e, "rowscale");
     GroupedArgs g = grouped_base(L, (const uint8_t *)packed,
                                  (const float *)((const uint8_t *)packed + L.stride + kLinearWscOff));

@@ -57,18 +57,37 @@ __device__ inline float pow2_below(float amax, int lim) {
 }
 
 // ---------------------------------------------------------------- prep
-// One wave per row: power of two that brings max |x| below 2^14.
-__global__ __launch_bounds__(256) void rowscale_kernel(const uint16_t *__restrict__ x, int rows,
-                                                       int64_t K, int in_f16, float *__restrict__ rowsc) {
+// One wave per row: power of two that brings max |x| below 2^14, and
+// optionally the row times it as f16 (K is a multiple of 64, rows 16-B aligned).
+__global__ __launch_bounds__(256) void rowscale_kernel(const uint16_t *__restrict__ x, int rows, int64_t K,
+                                                       int in_f16, float *__restrict__ rowsc,
+                                                       uint16_t *__restrict__ xs) {
   const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (r >= rows) return;
+  const uint4 *xr = reinterpret_cast<const uint4 *>(x + (int64_t)r * K);
+  const int64_t n8 = K / 8;
   float m = 0.f;
-  const uint16_t *xr = x + (int64_t)r * K;
-  for (int64_t k = lane; k < K; k += 64) m = fmaxf(m, fabsf(half_to_f32_rt(xr[k], in_f16)));
+  for (int64_t i = lane; i < n8; i += 64) {
+    const uint4 v = xr[i];
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int h = 0; h < 8; ++h) m = fmaxf(m, fabsf(half_to_f32_rt((w[h >> 1] >> (16 * (h & 1))) & 0xFFFFu, in_f16)));
+  }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-  if (lane == 0) rowsc[r] = pow2_below(m, 14);
+  const float sc = pow2_below(m, 14);
+  if (lane == 0) rowsc[r] = sc;
+  if (xs == nullptr) return;
+  uint4 *xo = reinterpret_cast<uint4 *>(xs + (int64_t)r * K);
+  for (int64_t i = lane; i < n8; i += 64) {
+    const uint4 v = xr[i];
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    half8_t hv;
+#pragma unroll
+    for (int h = 0; h < 8; ++h) hv[h] = (_Float16)(half_to_f32_rt((w[h >> 1] >> (16 * (h & 1))) & 0xFFFFu, in_f16) * sc);
+    xo[i] = __builtin_bit_cast(uint4, hv);
+  }
 }
 
 // One workgroup per expert: power of two that keeps max |s| * qmax below 2^15.
@@ -102,8 +121,13 @@ __global__ __launch_bounds__(256) void wscale_kernel(MatLayout L, const uint8_t 
 // ---------------------------------------------------------------- GEMM
 constexpr int kMaxAffineBlocks = kGroupedMaxAffineBlocks;
 
-template <int QT, int EPI, bool IN_F32, bool IN_F16>
+// Input modes: 16-bit rows (bf16 or f16) scaled while staged, fp32 rows
+// split into f16 hi + lo while staged, or f16 rows already scaled (copied).
+enum { kInBf16 = 0, kInF16 = 1, kInF32 = 2, kInScaled = 3 };
+
+template <int QT, int EPI, int INM>
 __global__ __launch_bounds__(256) void grouped_kernel(const GroupedArgs a) {
+  constexpr bool IN_F32 = INM == kInF32, IN_F16 = INM == kInF16, PRE = INM == kInScaled;
   using TR = QtTraits<QT>;
   using CD = Codec<TR::kBits, true>;
   constexpr int KC = 128 / TR::kBits;  // k per 16-B chunk: 32 (4-bit) or 64 (2-bit)
@@ -178,10 +202,21 @@ __global__ __launch_bounds__(256) void grouped_kernel(const GroupedArgs a) {
   // row group base of the k-tiled layout: [NKT][4 n-tiles][64 lanes][4 dwords]
   const uint32_t *wbase = reinterpret_cast<const uint32_t *>(wexp) + rg * a.NKT * (4 * kLanes * 4);
   const uint8_t *sbase = wexp + a.scales_off;
+  // buffer descriptors of this row group's codes and scales: the lane part of
+  // each address is fixed per slice, the k-tile part is uniform (soffset)
+  constexpr int SES = AFF ? 4 : 2;  // bytes per scale entry
+  const __amdgpu_buffer_rsrc_t wrs = make_rsrc(wbase, (uint32_t)(a.NKT * (4 * kLanes * 16)));
+  const __amdgpu_buffer_rsrc_t srs =
+      make_rsrc(sbase + rg * a.NKT * kLanes * a.bpk * SES, (uint32_t)(a.NKT * kLanes * a.bpk * SES));
   const int g = lane >> 4;
   int nl[NJ];
 #pragma unroll
   for (int j = 0; j < NJ; ++j) nl[j] = nl0 + 16 * j + (lane & 15);
+  // dword g of the chunk of row nl[j] sits in lane (nl[j] % 16) + 16 g of
+  // n-tile nl[j] / 16; nl0 is a multiple of 16, so slice j adds the uniform
+  // j n-tiles (codes) or 16 j rows (scales) to the first slice's offset
+  const int wvo = ((nl0 >> 4) * kLanes + lane) * 16;
+  const int svo = nl[0] * a.bpk * SES;
   const bool sf16 = a.sdtype == QMOE_DTYPE_F16;
   const bool split = MULTIBIT && sf16;
 
@@ -235,6 +270,16 @@ __global__ __launch_bounds__(256) void grouped_kernel(const GroupedArgs a) {
           dst[q] = hv;
           dlo[q] = lv;
         }
+      } else if constexpr (PRE) {
+#pragma unroll
+        for (int q = 0; q < SV; ++q) {
+          const half8_t hv = __builtin_bit_cast(half8_t, S[q]);
+          dst[q] = hv;
+          if constexpr (AFF) {
+#pragma unroll
+            for (int h = 0; h < 8; ++h) xsum += (float)hv[h];
+          }
+        }
       } else {
 #pragma unroll
         for (int q = 0; q < SV; ++q) {
@@ -287,13 +332,14 @@ __global__ __launch_bounds__(256) void grouped_kernel(const GroupedArgs a) {
       constexpr int c = decltype(cc)::value;
       const int chunk = min((int)(kt / KC) + c, (int)a.NC - 1);
       const int ktile = chunk >> 2, bi = (chunk >> cpb_log) & (bpk - 1);
+      const int wso = ktile * (4 * kLanes * 16) + (chunk & 3) * 4;
+      const int sso = (ktile * kLanes * bpk + bi) * SES;
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
-        // dword g of the chunk of row nl[j] sits in lane (nl[j] % 16) + 16 g of its n-tile
-        bw[c][j] = wbase[(((int64_t)ktile * 4 + (nl[j] >> 4)) * kLanes + lane) * 4 + (chunk & 3)];
-        const int64_t si = ((rg * a.NKT + ktile) * kLanes + nl[j]) * bpk + bi;
-        sv[c][j] = AFF ? reinterpret_cast<const uint32_t *>(sbase)[si]
-                       : reinterpret_cast<const uint16_t *>(sbase)[si];
+        const int wj = wso + j * (kLanes * 16), sj = sso + j * 16 * bpk * SES;
+        bw[c][j] = __builtin_amdgcn_raw_buffer_load_b32(wrs, wvo, wj, 0);
+        sv[c][j] = AFF ? __builtin_amdgcn_raw_buffer_load_b32(srs, svo, sj, 0)
+                       : (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(srs, svo, sj, 0);
       }
     });
   };
@@ -452,9 +498,10 @@ __global__ __launch_bounds__(256) void grouped_kernel(const GroupedArgs a) {
 
 template <int QT, int EPI>
 hipError_t launch_grouped_in(const GroupedArgs &a, int grid, hipStream_t s) {
-  if (a.in_f32) return qlaunch(grouped_kernel<QT, EPI, true, false>, dim3(grid), dim3(256), 0, s, a);
-  if (a.in_f16) return qlaunch(grouped_kernel<QT, EPI, false, true>, dim3(grid), dim3(256), 0, s, a);
-  return qlaunch(grouped_kernel<QT, EPI, false, false>, dim3(grid), dim3(256), 0, s, a);
+  if (a.in_f32) return qlaunch(grouped_kernel<QT, EPI, kInF32>, dim3(grid), dim3(256), 0, s, a);
+  if (a.in_scaled) return qlaunch(grouped_kernel<QT, EPI, kInScaled>, dim3(grid), dim3(256), 0, s, a);
+  if (a.in_f16) return qlaunch(grouped_kernel<QT, EPI, kInF16>, dim3(grid), dim3(256), 0, s, a);
+  return qlaunch(grouped_kernel<QT, EPI, kInBf16>, dim3(grid), dim3(256), 0, s, a);
 }
 
 template <int QT>
@@ -478,10 +525,11 @@ hipError_t launch_grouped(const GroupedArgs &a, int epilogue, int grid_tiles, hi
   }
 }
 
-hipError_t launch_rowscale(const void *x, int rows, int64_t K, int in_f16, float *rowsc, hipStream_t s) {
+hipError_t launch_rowscale(const void *x, int rows, int64_t K, int in_f16, float *rowsc, uint16_t *xs,
+                           hipStream_t s) {
   if (rows <= 0) return hipSuccess;
   return qlaunch(rowscale_kernel, dim3((rows + 3) / 4), dim3(256), 0, s, (const uint16_t *)x, rows, K, in_f16,
-                 rowsc);
+                 rowsc, xs);
 }
 
 hipError_t launch_wscale(const MatLayout &L, int E, const uint8_t *mat, float *wsc, hipStream_t s) {

@@ -273,9 +273,10 @@ struct GroupedArgs {
   int dense_M;             // > 0: dense rows, tiles of kTileM over M
   const int32_t *token_of; // routed FC1: input row of position p
   int in_gather_token;
-  // input: 16-bit rows (in_f32 = 0, dtype in_f16) or fp32 rows (in_f32 = 1)
+  // input: 16-bit rows (in_f32 = 0, dtype in_f16), fp32 rows (in_f32 = 1),
+  // or f16 rows already multiplied by their power-of-two scale (in_scaled = 1)
   const void *in;
-  int in_f32, in_f16;
+  int in_f32, in_f16, in_scaled;
   int64_t in_row_elems;
   const float *in_rowsc;   // 16-bit input: power-of-two scale per input row
   const uint32_t *in_rowmax; // fp32 input: |max| bits per row (scale derived)
@@ -289,7 +290,10 @@ struct GroupedArgs {
 };
 
 hipError_t launch_grouped(const GroupedArgs &a, int epilogue, int grid_tiles, hipStream_t s);
-hipError_t launch_rowscale(const void *x, int rows, int64_t K, int in_f16, float *rowsc, hipStream_t s);
+// Per-row power of two of the f16 A operand; with xs non-null, also the
+// scaled rows as f16 (exact: x * 2^r of a bf16/f16 x below 2^14).
+hipError_t launch_rowscale(const void *x, int rows, int64_t K, int in_f16, float *rowsc, uint16_t *xs,
+                           hipStream_t s);
 hipError_t launch_wscale(const MatLayout &L, int E, const uint8_t *mat, float *wsc, hipStream_t s);
 
 // ---------------------------------------------------------------- launches
