@@ -143,26 +143,29 @@ __global__ __launch_bounds__(512) void gemv_kernel(const GemvArgs a) {
   constexpr bool SWIGLU = EPI == kEpiSwiGLU || ROUTED;
   // routed: this workgroup's expert and the flat slots of its rows
   __shared__ int32_t s_rslot[ROUTED ? kGemvMaxRows : 1];
+  __shared__ int32_t s_ids[ROUTED ? kLanes : 1];  // routed: expert of each flat slot
   int e, M, pbase;
   if (a.dense_M > 0) {
     e = 0;
     M = a.dense_M;
     pbase = 0;
   } else if constexpr (ROUTED) {
-    // every workgroup routes the (at most 64) slots itself; workgroup 0 also
-    // writes the global lists and the top-k ids and weights
-    __shared__ int32_t s_ids[kLanes];
-    __shared__ int s_cnt[kMaxExperts];
+    // every workgroup routes the (at most 64) slots itself and finds its own
+    // expert's entry; workgroup 0 also writes the top-k ids and weights, and
+    // the global lists at the end of the kernel (read by later kernels only)
     __shared__ int4 s_slot;
+    __shared__ TopkScratch s_tk[kGemvMaxWaves];
     const bool lead = blockIdx.x == 0;
     for (int t = wave; t < a.route_T; t += KS)
       wave_topk(a.logits + (int64_t)t * a.route_E, a.route_E, a.route_k,
                 lead ? a.route.ids + (int64_t)t * a.route_k : nullptr,
-                lead ? a.route.w + (int64_t)t * a.route_k : nullptr, s_ids + t * a.route_k);
+                lead ? a.route.w + (int64_t)t * a.route_k : nullptr, s_ids + t * a.route_k, &s_tk[wave]);
     __syncthreads();
-    if (wave == 0)
-      wave_expand_small(s_ids, a.route_T * a.route_k, a.route_k, a.route_E, a.route_max_slots, s_cnt,
-                        lead ? &a.route : nullptr, slot, &s_slot, s_rslot);
+    if (wave == 0) wave_expand_want(s_ids, a.route_T * a.route_k, slot, &s_slot, s_rslot);
+    // workgroup 0: the expert map of all slots for the later kernels (on a
+    // wave that is otherwise waiting here, when there is one)
+    if (lead && wave == (KS > 1 ? 1 : 0))
+      wave_expand_lists(s_ids, a.route_T * a.route_k, a.route_k, a.route_E, a.route_max_slots, a.route);
     __syncthreads();
     const int4 si = s_slot;  // the same for every lane: keep it in SGPRs
     e = __builtin_amdgcn_readfirstlane(si.x);

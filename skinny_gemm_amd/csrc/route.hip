@@ -15,10 +15,11 @@ constexpr int kExpandThreads = 1024;
 constexpr int kExpandWaves = kExpandThreads / kLanes;
 
 __global__ __launch_bounds__(256) void route_topk_kernel(RouteArgs a) {
+  __shared__ TopkScratch s_tk[256 / kLanes];
   const int t = blockIdx.x * (blockDim.x / kLanes) + (threadIdx.x / kLanes);
   if (t >= a.T) return;
   wave_topk(a.logits + (int64_t)t * a.E, a.E, a.k, a.r.ids + (int64_t)t * a.k,
-            a.r.w + (int64_t)t * a.k, nullptr);
+            a.r.w + (int64_t)t * a.k, nullptr, &s_tk[threadIdx.x / kLanes]);
 }
 
 // Single workgroup.  With topk_in_expand (T <= kExpandWaves) the workgroup
@@ -29,6 +30,7 @@ __global__ __launch_bounds__(kExpandThreads) void route_expand_kernel(RouteArgs 
   __shared__ int s_base[kMaxExperts];
   __shared__ int s_wc[kExpandWaves][kMaxExperts];
   __shared__ int32_t s_ids[kExpandWaves * kMaxTopK];
+  __shared__ TopkScratch s_tk[kExpandWaves];
   const int tid = threadIdx.x, lane = tid & (kLanes - 1), wave = tid / kLanes;
   const int E = a.E;
   const int S = a.T * a.k;
@@ -36,7 +38,7 @@ __global__ __launch_bounds__(kExpandThreads) void route_expand_kernel(RouteArgs 
 
   if (fused && wave < a.T) {
     wave_topk(a.logits + (int64_t)wave * E, E, a.k, a.r.ids + (int64_t)wave * a.k,
-              a.r.w + (int64_t)wave * a.k, s_ids + wave * a.k);
+              a.r.w + (int64_t)wave * a.k, s_ids + wave * a.k, &s_tk[wave]);
   }
   for (int e = tid; e < kMaxExperts; e += kExpandThreads) {
     s_cnt[e] = 0;
@@ -170,13 +172,13 @@ __global__ __launch_bounds__(kExpandThreads) void route_expand_kernel(RouteArgs 
 // per token routes it, then wave 0 alone builds the expert map.
 __global__ __launch_bounds__(1024) void route_small_kernel(RouteArgs a) {
   __shared__ int32_t s_ids[kExpandWaves * kMaxTopK];
-  __shared__ int s_cnt[kMaxExperts];
+  __shared__ TopkScratch s_tk[kExpandWaves];
   const int wave = threadIdx.x / kLanes;
   if (wave < a.T)
     wave_topk(a.logits + (int64_t)wave * a.E, a.E, a.k, a.r.ids + (int64_t)wave * a.k,
-              a.r.w + (int64_t)wave * a.k, s_ids + wave * a.k);
+              a.r.w + (int64_t)wave * a.k, s_ids + wave * a.k, &s_tk[wave]);
   __syncthreads();
-  if (wave == 0) wave_expand_small(s_ids, a.T * a.k, a.k, a.E, a.max_slots, s_cnt, &a.r, -1, nullptr, nullptr);
+  if (wave == 0) wave_expand_lists(s_ids, a.T * a.k, a.k, a.E, a.max_slots, a.r);
 }
 
 hipError_t launch_route(const RouteArgs &a, hipStream_t s) {

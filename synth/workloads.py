@@ -156,7 +156,9 @@ def moe_inputs(spec: MoeSpec, T: int, seed: int = 0, logits_mode: str = "iid",
 
     logits_mode: "iid" draws logits[t][e] ~ N(0,1) independently (plus the
     per-expert bias when the workload has one); "shared" draws one row and
-    repeats it for every token, so every selected expert receives all T rows.
+    repeats it for every token, so every selected expert receives all T rows;
+    "ties" rounds the iid draws to multiples of 0.5, so many logits of a row
+    are equal and the selection depends on the tie rule.
     weight_copy selects an independent set of expert weights (distinct copies
     for cache-cold timing); activations and logits do not depend on it.
     """
@@ -174,6 +176,8 @@ def moe_inputs(spec: MoeSpec, T: int, seed: int = 0, logits_mode: str = "iid",
         z = normals(Key(seed, wl, f"logits[T={T}]"), T * spec.E).reshape(T, spec.E)
     elif logits_mode == "shared":
         z = np.broadcast_to(normals(Key(seed, wl, "logits[shared]"), spec.E), (T, spec.E)).copy()
+    elif logits_mode == "ties":
+        z = np.round(2.0 * normals(Key(seed, wl, f"logits[T={T}]"), T * spec.E).reshape(T, spec.E)) / 2.0
     else:
         raise ValueError(logits_mode)
     if spec.logit_bias:

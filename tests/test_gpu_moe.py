@@ -110,6 +110,15 @@ def test_dsv2lite_int4_shared_logits(T):
     run_case(synth.MOE_WORKLOADS["dsv2lite_int4"], T, 0, logits_mode="shared")
 
 
+@pytest.mark.parametrize("name,T", [("dsv2lite_int4", 1), ("dsv2lite_int4", 2), ("dsv2lite_int4", 4),
+                                    ("switch_base_ternary", 1)])
+def test_tied_logits(name, T):
+    """Logits rounded to halves: many equal values per row, so the selected
+    experts and their order follow the tie rule (lower expert index first).
+    T*k <= 16 routes inside FC1; T = 4 takes the small routing kernel."""
+    run_case(synth.MOE_WORKLOADS[name], T, 5, logits_mode="ties")
+
+
 # -------------------------------------------------------------- small sweeps
 SWEEP = [
     dict(E=1, H=64, I=64, top_k=1, fc1="sym_int4"),
