@@ -37,7 +37,6 @@ __device__ __forceinline__ void static_for(F &&f) {
   static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 
 // Masks and float constants of a decoder held in registers.  CDNA VOP3
@@ -176,18 +175,6 @@ struct Codec<2, true> {
     extract(w, p, CodecOps<Codec>::literal());
   }
 };
-
-// v_dot2_f32_{bf16,f16}: acc + lo(a)*lo(b) + hi(a)*hi(b).
-template <bool F16>
-__device__ inline float dot2(uint32_t a, uint32_t b, float acc) {
-  if constexpr (F16) {
-    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a), __builtin_bit_cast(f16x2_t, b), acc,
-                                  false);
-  } else {
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
-                                           __builtin_bit_cast(bf16x2_t, b), acc, false);
-  }
-}
 
 __device__ inline float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
 __device__ inline float f16_to_f32(uint32_t h) {
