@@ -13,6 +13,7 @@ namespace qmoe {
 
 constexpr int kExpandThreads = 1024;
 constexpr int kExpandWaves = kExpandThreads / kLanes;
+constexpr int kCachedTiles = 16;  // slot ids per thread held in registers by the expand kernel
 
 __global__ __launch_bounds__(256) void route_topk_kernel(RouteArgs a) {
   __shared__ TopkScratch s_tk[256 / kLanes];
@@ -28,7 +29,7 @@ __global__ __launch_bounds__(kExpandThreads) void route_expand_kernel(RouteArgs 
   __shared__ int s_cnt[kMaxExperts];
   __shared__ int s_off[kMaxExperts + 1];
   __shared__ int s_base[kMaxExperts];
-  __shared__ int s_wc[kExpandWaves][kMaxExperts];
+  __shared__ int s_wc[2][kExpandWaves][kMaxExperts];  // per tile parity: wave counts, then prefixes
   __shared__ int32_t s_ids[kExpandWaves * kMaxTopK];
   __shared__ TopkScratch s_tk[kExpandWaves];
   const int tid = threadIdx.x, lane = tid & (kLanes - 1), wave = tid / kLanes;
@@ -45,10 +46,21 @@ __global__ __launch_bounds__(kExpandThreads) void route_expand_kernel(RouteArgs 
     s_base[e] = 0;
   }
   for (int i = tid; i < a.zero_len; i += kExpandThreads) a.zero_buf[i] = 0;
-  for (int i = tid; i < kExpandWaves * kMaxExperts; i += kExpandThreads) (&s_wc[0][0])[i] = 0;
+  for (int i = tid; i < 2 * kExpandWaves * kMaxExperts; i += kExpandThreads) (&s_wc[0][0][0])[i] = 0;
   __syncthreads();
 
-  for (int r = tid; r < S; r += kExpandThreads) {
+  // the first kCachedTiles tiles of slot ids, loaded once into registers
+  // (one memory latency for all of them instead of one per tile)
+  int ecache[kCachedTiles];
+#pragma unroll
+  for (int i = 0; i < kCachedTiles; ++i) {
+    const int r = i * kExpandThreads + tid;
+    ecache[i] = (r < S) ? (fused ? s_ids[r] : a.r.ids[r]) : 0;
+  }
+#pragma unroll
+  for (int i = 0; i < kCachedTiles; ++i)
+    if (i * kExpandThreads + tid < S) atomicAdd(&s_cnt[ecache[i]], 1);
+  for (int r = kCachedTiles * kExpandThreads + tid; r < S; r += kExpandThreads) {
     const int e = fused ? s_ids[r] : a.r.ids[r];
     atomicAdd(&s_cnt[e], 1);
   }
@@ -133,11 +145,11 @@ __global__ __launch_bounds__(kExpandThreads) void route_expand_kernel(RouteArgs 
   }
   __syncthreads();
 
-  // Stable scatter, one tile of kExpandThreads slots at a time.
-  for (int t0 = 0; t0 < S; t0 += kExpandThreads) {
+  // Stable scatter, one tile of kExpandThreads slots at a time (ids of the
+  // first tiles from registers, later ones loaded).
+  auto scatter = [&](int t0, int e) __attribute__((always_inline)) {
     const int r = t0 + tid;
     const bool valid = r < S;
-    const int e = valid ? (fused ? s_ids[r] : a.r.ids[r]) : 0;
     uint64_t same = __ballot(valid);
 #pragma unroll
     for (int b = 0; b < 8; ++b) {
@@ -146,25 +158,37 @@ __global__ __launch_bounds__(kExpandThreads) void route_expand_kernel(RouteArgs 
     }
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (kLanes - lane));
     const int rank = __popcll(same & below);
-    if (valid && rank == 0) s_wc[wave][e] = __popcll(same);
+    const int pb = (t0 / kExpandThreads) & 1;  // this tile's buffer (all zero on entry)
+    if (valid && rank == 0) s_wc[pb][wave][e] = __popcll(same);
+    __syncthreads();
+    // per expert: the wave counts become exclusive prefixes over the waves
+    // (plus the rows of earlier tiles), the base moves past this tile, and
+    // the other buffer -- read by the previous tile before the barrier
+    // above -- is cleared for the next tile
+    for (int x = tid; x < E; x += kExpandThreads) {
+      int run = s_base[x];
+      for (int w2 = 0; w2 < kExpandWaves; ++w2) {
+        const int c = s_wc[pb][w2][x];
+        s_wc[pb][w2][x] = run;
+        s_wc[pb ^ 1][w2][x] = 0;
+        run += c;
+      }
+      s_base[x] = run;
+    }
     __syncthreads();
     if (valid) {
-      int pos = s_off[e] + s_base[e] + rank;
-      for (int w2 = 0; w2 < wave; ++w2) pos += s_wc[w2][e];
+      const int pos = s_off[e] + s_wc[pb][wave][e] + rank;
       a.r.row_list[pos] = r;
       a.r.slot_pos[r] = pos;
       a.r.token_of[pos] = r / a.k;
     }
-    __syncthreads();
-    for (int x = tid; x < E; x += kExpandThreads) {
-      int sum = 0;
-      for (int w2 = 0; w2 < kExpandWaves; ++w2) {
-        sum += s_wc[w2][x];
-        s_wc[w2][x] = 0;
-      }
-      s_base[x] += sum;
-    }
-    __syncthreads();
+  };
+#pragma unroll
+  for (int i = 0; i < kCachedTiles; ++i)
+    if (i * kExpandThreads < S) scatter(i * kExpandThreads, ecache[i]);
+  for (int t0 = kCachedTiles * kExpandThreads; t0 < S; t0 += kExpandThreads) {
+    const int r = t0 + tid;
+    scatter(t0, r < S ? (fused ? s_ids[r] : a.r.ids[r]) : 0);
   }
 }
 

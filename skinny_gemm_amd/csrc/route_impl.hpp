@@ -43,8 +43,8 @@ struct TopkScratch {
 __device__ inline void wave_topk(const float *__restrict__ l, int E, int k, int32_t *ids_out, float *w_out,
                                  int32_t *ids_lds, TopkScratch *sc) {
   const int lane = threadIdx.x & (kLanes - 1);
-  float sel_v[kMaxTopK];
-  int sel_i[kMaxTopK];
+  // the selection goes to sc->id / sc->v in selection order (LDS: no
+  // private arrays indexed by the runtime k)
   if (E <= kLanes && k > 1) {
     const bool have = lane < E;
     const float v = have ? l[lane] : 0.f;
@@ -58,23 +58,14 @@ __device__ inline void wave_topk(const float *__restrict__ l, int E, int k, int3
       sc->id[rank] = lane;
       sc->v[rank] = v;
     }
-    // other lanes' LDS writes are read below by lane 0
-    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    if (lane == 0) {
-      for (int j = 0; j < k; ++j) {
-        sel_i[j] = sc->id[j];
-        sel_v[j] = sc->v[j];
-      }
-    }
   } else {
     float v[kMaxExperts / kLanes];
-    bool taken[kMaxExperts / kLanes];
+    unsigned taken = 0;  // bit i: expert lane + 64 i is taken or absent
 #pragma unroll
     for (int i = 0; i < kMaxExperts / kLanes; ++i) {
       const int e = lane + kLanes * i;
       v[i] = (e < E) ? l[e] : -FLT_MAX;
-      taken[i] = (e >= E);
+      taken |= (e >= E) ? (1u << i) : 0u;
     }
     for (int j = 0; j < k; ++j) {
       float bv = -FLT_MAX;
@@ -82,7 +73,7 @@ __device__ inline void wave_topk(const float *__restrict__ l, int E, int k, int3
 #pragma unroll
       for (int i = 0; i < kMaxExperts / kLanes; ++i) {
         const int e = lane + kLanes * i;
-        if (!taken[i] && (bi == 0x7FFFFFFF || v[i] > bv || (v[i] == bv && e < bi))) {
+        if (!((taken >> i) & 1u) && (bi == 0x7FFFFFFF || v[i] > bv || (v[i] == bv && e < bi))) {
           bv = v[i];
           bi = e;
         }
@@ -98,23 +89,25 @@ __device__ inline void wave_topk(const float *__restrict__ l, int E, int k, int3
       }
 #pragma unroll
       for (int i = 0; i < kMaxExperts / kLanes; ++i)
-        if (lane + kLanes * i == bi) taken[i] = true;
-      sel_v[j] = bv;
-      sel_i[j] = bi;
+        if (lane + kLanes * i == bi) taken |= 1u << i;
+      if (lane == 0) {
+        sc->id[j] = bi;
+        sc->v[j] = bv;
+      }
     }
   }
+  // other lanes' LDS writes are read below by lane 0
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  __builtin_amdgcn_wave_barrier();
   if (lane == 0) {
-    const float m = sel_v[0];
-    float ex[kMaxTopK];
+    const float m = sc->v[0];
     float sum = 0.f;
+    for (int j = 0; j < k; ++j) sum += expf(sc->v[j] - m);
     for (int j = 0; j < k; ++j) {
-      ex[j] = expf(sel_v[j] - m);
-      sum += ex[j];
-    }
-    for (int j = 0; j < k; ++j) {
-      if (ids_out) ids_out[j] = sel_i[j];
-      if (w_out) w_out[j] = ex[j] / sum;
-      if (ids_lds) ids_lds[j] = sel_i[j];
+      const int id = sc->id[j];
+      if (ids_out) ids_out[j] = id;
+      if (w_out) w_out[j] = expf(sc->v[j] - m) / sum;
+      if (ids_lds) ids_lds[j] = id;
     }
   }
 }
