@@ -49,11 +49,19 @@ __device__ inline void wave_topk(const float *__restrict__ l, int E, int k, int3
     const bool have = lane < E;
     const float v = have ? l[lane] : 0.f;
     const int vb = __float_as_int(v);
-    int rank = 0;
-    for (int j = 0; j < E; ++j) {
-      const float o = __int_as_float(__builtin_amdgcn_readlane(vb, j));
-      rank += (o > v || (o == v && j < lane)) ? 1 : 0;
+    // four independent chains over the quarters of the lane range, so the
+    // cross-lane reads overlap instead of forming one dependent chain
+    int rc[4] = {0, 0, 0, 0};
+#pragma unroll 4
+    for (int j = 0; j < kLanes / 4; ++j) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int jj = j + q * (kLanes / 4);
+        const float o = __int_as_float(__builtin_amdgcn_readlane(vb, jj));
+        rc[q] += (jj < E && (o > v || (o == v && jj < lane))) ? 1 : 0;
+      }
     }
+    const int rank = rc[0] + rc[1] + rc[2] + rc[3];
     if (have && rank < k) {
       sc->id[rank] = lane;
       sc->v[rank] = v;
