@@ -31,15 +31,17 @@ struct TopkScratch {
 };
 
 // Wave-wide top-k of one token.  Lane 0 writes the ids and weights to
-// ids_out / w_out (when not null) and the ids to ids_lds (when not null).
+// ids_out / w_out (when not null) and the ids to ids_lds (when not null),
+// in selection order.  Requires 1 <= k <= E.
 //
 // Selection order: an expert's position is the number of logits greater
 // than its own plus the number of equal logits of lower index (the k rounds
 // of first-strictly-greater arg-max, ties to the lower index, for finite
 // logits).  For E <= 64 and k > 1 each lane holds one logit and counts the
 // others, read with v_readlane, so all k positions come out of one pass;
-// otherwise k rounds of a wave-wide arg-max run (one round for k = 1).  The weights are the softmax of the
-// selected logits in selection order, computed by lane 0 in fp32.
+// otherwise k rounds of a wave-wide arg-max run (one round for k = 1).
+// Either way the selection is recorded in sc; the weights are the softmax
+// of the selected logits, computed by lane 0 in fp32 in selection order.
 __device__ inline void wave_topk(const float *__restrict__ l, int E, int k, int32_t *ids_out, float *w_out,
                                  int32_t *ids_lds, TopkScratch *sc) {
   const int lane = threadIdx.x & (kLanes - 1);
@@ -47,18 +49,20 @@ __device__ inline void wave_topk(const float *__restrict__ l, int E, int k, int3
   // private arrays indexed by the runtime k)
   if (E <= kLanes && k > 1) {
     const bool have = lane < E;
-    const float v = have ? l[lane] : 0.f;
+    // lanes past E hold NaN: it compares false with everything, so every
+    // lane reads all 64 without a bound check
+    const float v = have ? l[lane] : __builtin_nanf("");
     const int vb = __float_as_int(v);
-    // four independent chains over the quarters of the lane range, so the
-    // cross-lane reads overlap instead of forming one dependent chain
+    // branch-free counts (no short-circuit: bitwise ors of the compares) in
+    // four independent chains over the quarters of the lane range
     int rc[4] = {0, 0, 0, 0};
-#pragma unroll 4
+#pragma unroll 1
     for (int j = 0; j < kLanes / 4; ++j) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int jj = j + q * (kLanes / 4);
         const float o = __int_as_float(__builtin_amdgcn_readlane(vb, jj));
-        rc[q] += (jj < E && (o > v || (o == v && jj < lane))) ? 1 : 0;
+        rc[q] += (int)((o > v) | ((o == v) & (jj < lane)));
       }
     }
     const int rank = rc[0] + rc[1] + rc[2] + rc[3];
