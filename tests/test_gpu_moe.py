@@ -250,6 +250,14 @@ def test_dsv2lite_shared_logits_grouped_T32():
     run_case(synth.MOE_WORKLOADS["dsv2lite_int4"], 32, 0, logits_mode="shared")
 
 
+@pytest.mark.parametrize("T", [1, 2])
+def test_mixed_int2_int4_decode(T):
+    """The 128-expert top-8 layer at decode sizes: 8 or 16 slots routed
+    inside FC1, with E > 64 (the arg-max rounds of the top-k), INT2 FC1 and
+    INT4 FC2 on the GEMV path."""
+    run_case(synth.MOE_WORKLOADS["mixed_int2_int4_prefill"], T, 3)
+
+
 @pytest.mark.parametrize("seed", [0, 1])
 def test_mixed_int2_int4_prefill(seed):
     """2048 tokens, 128 experts, top-8, skewed load: routing checked on every
