@@ -10,10 +10,13 @@
 // onnx-genai pull request 1167.
 //
 // gfx950 mapping (the pages' designs use one warp or thread group per row):
-//   - a wave owns 64 output rows (4 tiles of 16) and a contiguous run of
-//     k-tiles; per k-tile it issues four 1 KiB contiguous loads (16 B per
-//     lane) of the prepacked layout, whose lane (r, g) = (lane % 16, lane / 16)
-//     holds exactly the v_mfma_f32_16x16x32 B operand of row r for k-group g;
+//   - a wave owns TN n-tiles of 16 output rows (TN = 4: a whole 64-row
+//     group; TN = 1 when the grid would otherwise leave compute units idle)
+//     and a contiguous run of k-tiles; per k-tile it issues TN 1 KiB
+//     contiguous loads (16 B per lane) of the prepacked layout, whose lane
+//     (r, g) = (lane % 16, lane / 16) holds exactly the v_mfma_f32_16x16x32 B
+//     operand of row r for k-group g, and the next k-tile's loads are in
+//     flight during the current one's MFMAs (buffer loads, see the k loop);
 //   - one AND-OR per weight pair turns the codes into exact 16-bit floats
 //     base + u (magic-number decoding, codec.hpp); the raw codes enter the
 //     MFMA unscaled, so the dequantization costs no multiply;
@@ -25,13 +28,18 @@
 //     X = sum x for affine formats) in the same lane layout, and the block
 //     epilogue adds s (D - C) (+ b X) to the fp32 result;
 //   - K is split over the waves of a workgroup; the partial sums meet in LDS
-//     and are added in a fixed wave order.
+//     and are added in a fixed wave order;
+//   - for small decode batches the FC1 launch routes the tokens itself
+//     (epilogue kEpiSwiGLURouted): every workgroup runs the top-k and finds
+//     its own expert's rows, so no routing kernel precedes it.
 #pragma once
 
 #include "codec.hpp"
 #include "qmoe_internal.h"
 #include "route_impl.hpp"
 
+// Build option: 1 (default) keeps the next k-tile's weights in flight during
+// the current one's MFMAs; 0 loads and computes one k-tile at a time.
 #ifndef QMOE_GEMV_PREFETCH
 #define QMOE_GEMV_PREFETCH 1
 #endif

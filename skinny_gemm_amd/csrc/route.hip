@@ -6,7 +6,11 @@
 //           offsets, list of active experts, then a stable counting sort of
 //           the flat slots r = t*k + j by expert (rank inside a wavefront from
 //           ballots over the expert id bits, ranks across wavefronts from
-//           per-wavefront counts in LDS), giving row_list and its inverse.
+//           per-wavefront counts in LDS), giving row_list and its inverse;
+//           the slot ids of the first tiles stay in registers.
+//   small   (T*k <= 64 slots, no tile list) one workgroup: one wavefront
+//           per token for the top-k, then one wavefront builds every list
+//           from ballots (wave_expand_lists).
 #include "route_impl.hpp"
 
 namespace qmoe {
