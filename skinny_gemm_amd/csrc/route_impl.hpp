@@ -30,6 +30,22 @@ struct TopkScratch {
   float v[kMaxTopK];
 };
 
+// Maximum of v over the wavefront, in every lane: DPP row shifts reduce
+// each row of 16 lanes, row broadcasts combine the rows (lanes without a
+// source keep -inf), lane 63 ends with the maximum and is read back.
+__device__ inline float wave_max(float v) {
+  constexpr int kRowShr = 0x110, kBcast15 = 0x142, kBcast31 = 0x143;
+  const int ninf = __float_as_int(-__builtin_inff());
+  float m = v;
+  m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(ninf, __float_as_int(m), kRowShr + 1, 0xf, 0xf, false)));
+  m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(ninf, __float_as_int(m), kRowShr + 2, 0xf, 0xf, false)));
+  m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(ninf, __float_as_int(m), kRowShr + 4, 0xf, 0xf, false)));
+  m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(ninf, __float_as_int(m), kRowShr + 8, 0xf, 0xf, false)));
+  m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(ninf, __float_as_int(m), kBcast15, 0xa, 0xf, false)));
+  m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(ninf, __float_as_int(m), kBcast31, 0xc, 0xf, false)));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), kLanes - 1));
+}
+
 // Wave-wide top-k of one token.  Lane 0 writes the ids and weights to
 // ids_out / w_out (when not null) and the ids to ids_lds (when not null),
 // in selection order.  Requires 1 <= k <= E.
@@ -39,7 +55,8 @@ struct TopkScratch {
 // of first-strictly-greater arg-max, ties to the lower index, for finite
 // logits).  For E <= 64 and k > 1 each lane holds one logit and counts the
 // others, read with v_readlane, so all k positions come out of one pass;
-// otherwise k rounds of a wave-wide arg-max run (one round for k = 1).
+// for E <= 64 and k = 1 a DPP maximum and a ballot give the arg-max;
+// otherwise k rounds of a wave-wide arg-max run.
 // Either way the selection is recorded in sc; the weights are the softmax
 // of the selected logits, computed by lane 0 in fp32 in selection order.
 __device__ inline void wave_topk(const float *__restrict__ l, int E, int k, int32_t *ids_out, float *w_out,
@@ -47,7 +64,17 @@ __device__ inline void wave_topk(const float *__restrict__ l, int E, int k, int3
   const int lane = threadIdx.x & (kLanes - 1);
   // the selection goes to sc->id / sc->v in selection order (LDS: no
   // private arrays indexed by the runtime k)
-  if (E <= kLanes && k > 1) {
+  if (E <= kLanes && k == 1) {
+    // arg-max: the wave maximum, then the lowest lane holding it
+    const bool have = lane < E;
+    const float v = have ? l[lane] : -__builtin_inff();
+    const float m = wave_max(v);
+    const uint64_t at = __ballot(have && v == m);
+    if (lane == 0) {
+      sc->id[0] = at ? __builtin_ctzll(at) : 0;
+      sc->v[0] = m;
+    }
+  } else if (E <= kLanes && k > 1) {
     const bool have = lane < E;
     // lanes past E hold NaN: it compares false with everything, so every
     // lane reads all 64 without a bound check
@@ -133,6 +160,13 @@ __device__ inline void wave_topk(const float *__restrict__ l, int E, int k, int3
 // in wave_expand_lists.
 __device__ inline void wave_expand_want(const int32_t *ids, int S, int want, int4 *slot_out, int32_t *slots_out) {
   const int lane = threadIdx.x & (kLanes - 1);
+  if (S == 1) {  // one slot: one active expert with one row
+    if (lane == 0) {
+      *slot_out = want == 0 ? make_int4(ids[0], 1, 0, 0) : make_int4(0, 0, 0, 0);
+      if (want == 0) slots_out[0] = 0;
+    }
+    return;
+  }
   const bool valid = lane < S;
   const int e = valid ? ids[lane] : 0;
   // slots of smaller id (less) and of the same id (eq)
