@@ -53,10 +53,10 @@ __device__ inline float wave_max(float v) {
 // Selection order: an expert's position is the number of logits greater
 // than its own plus the number of equal logits of lower index (the k rounds
 // of first-strictly-greater arg-max, ties to the lower index, for finite
-// logits).  For E <= 64 and k > 1 each lane holds one logit and counts the
-// others, read with v_readlane, so all k positions come out of one pass;
-// for E <= 64 and k = 1 a DPP maximum and a ballot give the arg-max;
-// otherwise k rounds of a wave-wide arg-max run.
+// logits).  For E <= 64 each lane holds one logit and each of the k rounds
+// takes a DPP wave maximum over the experts not yet taken and the lowest
+// lane holding it; larger E runs k rounds of a shuffle-based arg-max over
+// E / 64 logits per lane.
 // Either way the selection is recorded in sc; the weights are the softmax
 // of the selected logits, computed by lane 0 in fp32 in selection order.
 __device__ inline void wave_topk(const float *__restrict__ l, int E, int k, int32_t *ids_out, float *w_out,
@@ -64,38 +64,21 @@ __device__ inline void wave_topk(const float *__restrict__ l, int E, int k, int3
   const int lane = threadIdx.x & (kLanes - 1);
   // the selection goes to sc->id / sc->v in selection order (LDS: no
   // private arrays indexed by the runtime k)
-  if (E <= kLanes && k == 1) {
-    // arg-max: the wave maximum, then the lowest lane holding it
+  if (E <= kLanes) {
+    // k rounds of arg-max: the wave maximum of the experts not yet taken
+    // (DPP), then the lowest lane holding it
     const bool have = lane < E;
     const float v = have ? l[lane] : -__builtin_inff();
-    const float m = wave_max(v);
-    const uint64_t at = __ballot(have && v == m);
-    if (lane == 0) {
-      sc->id[0] = at ? __builtin_ctzll(at) : 0;
-      sc->v[0] = m;
-    }
-  } else if (E <= kLanes && k > 1) {
-    const bool have = lane < E;
-    // lanes past E hold NaN: it compares false with everything, so every
-    // lane reads all 64 without a bound check
-    const float v = have ? l[lane] : __builtin_nanf("");
-    const int vb = __float_as_int(v);
-    // branch-free counts (no short-circuit: bitwise ors of the compares) in
-    // four independent chains over the quarters of the lane range
-    int rc[4] = {0, 0, 0, 0};
-#pragma unroll 1
-    for (int j = 0; j < kLanes / 4; ++j) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int jj = j + q * (kLanes / 4);
-        const float o = __int_as_float(__builtin_amdgcn_readlane(vb, jj));
-        rc[q] += (int)((o > v) | ((o == v) & (jj < lane)));
+    bool avail = have;
+    for (int j = 0; j < k; ++j) {
+      const float m = wave_max(avail ? v : -__builtin_inff());
+      const uint64_t at = __ballot(avail && v == m);
+      const int sel = at ? __builtin_ctzll(at) : 0;
+      if (lane == sel) avail = false;
+      if (lane == 0) {
+        sc->id[j] = sel;
+        sc->v[j] = m;
       }
-    }
-    const int rank = rc[0] + rc[1] + rc[2] + rc[3];
-    if (have && rank < k) {
-      sc->id[rank] = lane;
-      sc->v[rank] = v;
     }
   } else {
     float v[kMaxExperts / kLanes];
