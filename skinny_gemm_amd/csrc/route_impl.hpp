@@ -4,10 +4,10 @@
 // The onnxruntime pull request 33005 (Description) reuses routing and
 // expert-map kernels and expands the rows by expert before FC1.  Here:
 //   top-k   one wavefront per token selects the experts in descending
-//           logit order (ties to the lower expert index): for E <= 64 each
-//           lane ranks its own logit against all others in one pass, for
-//           larger E k rounds of a wave-wide arg-max run; weights = softmax
-//           of the selected logits in fp32 (sum 1, exactly 1.0 for k = 1).
+//           logit order (ties to the lower expert index) in k rounds, each
+//           a DPP wave maximum over the experts not yet taken and the lowest
+//           expert holding it; weights = softmax of the selected logits in
+//           fp32 (sum 1, exactly 1.0 for k = 1).
 //   expand  (at most 64 slots) one wavefront, one slot per lane: a slot's
 //           position in the expert-sorted list is the number of slots with
 //           a smaller expert id plus its rank among the slots of its own
@@ -53,12 +53,11 @@ __device__ inline float wave_max(float v) {
 // Selection order: an expert's position is the number of logits greater
 // than its own plus the number of equal logits of lower index (the k rounds
 // of first-strictly-greater arg-max, ties to the lower index, for finite
-// logits).  For E <= 64 each lane holds one logit and each of the k rounds
-// takes a DPP wave maximum over the experts not yet taken and the lowest
-// lane holding it; larger E runs k rounds of a shuffle-based arg-max over
-// E / 64 logits per lane.
-// Either way the selection is recorded in sc; the weights are the softmax
-// of the selected logits, computed by lane 0 in fp32 in selection order.
+// logits).  Each of the k rounds takes a DPP wave maximum over the experts
+// not yet taken and the lowest expert holding it (one logit per lane for
+// E <= 64, E / 64 per lane beyond).  The selection is recorded in sc; the
+// weights are the softmax of the selected logits, computed by lane 0 in
+// fp32 in selection order.
 __device__ inline void wave_topk(const float *__restrict__ l, int E, int k, int32_t *ids_out, float *w_out,
                                  int32_t *ids_lds, TopkScratch *sc) {
   const int lane = threadIdx.x & (kLanes - 1);
@@ -81,46 +80,37 @@ __device__ inline void wave_topk(const float *__restrict__ l, int E, int k, int3
       }
     }
   } else {
-    float v[kMaxExperts / kLanes];
-    unsigned taken = 0;  // bit i: expert lane + 64 i is taken or absent
+    // the same rounds over E / 64 logits per lane (expert lane + 64 i):
+    // the lane maximum, the wave maximum, then the lowest expert holding it
+    constexpr int PER = kMaxExperts / kLanes;
+    float v[PER];
+    unsigned avail = 0;  // bit i: expert lane + 64 i present and not taken
 #pragma unroll
-    for (int i = 0; i < kMaxExperts / kLanes; ++i) {
+    for (int i = 0; i < PER; ++i) {
       const int e = lane + kLanes * i;
-      v[i] = (e < E) ? l[e] : -FLT_MAX;
-      taken |= (e >= E) ? (1u << i) : 0u;
+      v[i] = (e < E) ? l[e] : -__builtin_inff();
+      avail |= (e < E) ? (1u << i) : 0u;
     }
     for (int j = 0; j < k; ++j) {
-      float bv = -FLT_MAX;
-      int bi = 0x7FFFFFFF;
+      float lm = -__builtin_inff();
 #pragma unroll
-      for (int i = 0; i < kMaxExperts / kLanes; ++i) {
-        const int e = lane + kLanes * i;
-        if (!((taken >> i) & 1u) && (bi == 0x7FFFFFFF || v[i] > bv || (v[i] == bv && e < bi))) {
-          bv = v[i];
-          bi = e;
-        }
+      for (int i = 0; i < PER; ++i) lm = fmaxf(lm, ((avail >> i) & 1u) ? v[i] : -__builtin_inff());
+      const float m = wave_max(lm);
+      int sel = -1;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        const uint64_t at = __ballot(((avail >> i) & 1u) && v[i] == m);
+        if (sel < 0 && at) sel = kLanes * i + __builtin_ctzll(at);
       }
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) {
-        const float ov = __shfl_xor(bv, off);
-        const int oi = __shfl_xor(bi, off);
-        if (oi != 0x7FFFFFFF && (bi == 0x7FFFFFFF || ov > bv || (ov == bv && oi < bi))) {
-          bv = ov;
-          bi = oi;
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < kMaxExperts / kLanes; ++i)
-        if (lane + kLanes * i == bi) taken |= 1u << i;
+      if (sel < 0) sel = 0;
+      if (lane == (sel & (kLanes - 1))) avail &= ~(1u << (sel / kLanes));
       if (lane == 0) {
-        sc->id[j] = bi;
-        sc->v[j] = bv;
+        sc->id[j] = sel;
+        sc->v[j] = m;
       }
     }
   }
-  // other lanes' LDS writes are read below by lane 0
-  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-  __builtin_amdgcn_wave_barrier();
+  // lane 0 recorded the selection above and computes the weights
   if (lane == 0) {
     const float m = sc->v[0];
     float sum = 0.f;
