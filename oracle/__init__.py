@@ -58,7 +58,7 @@ def lib():
         L.orc_silu.argtypes = [C.c_double]
         L.orc_moe.restype = C.c_int
         L.orc_moe.argtypes = ([C.c_int] * 5 + [C.c_int] * 3 + [P] * 3 + [C.c_int] * 3 + [P] * 3
-                              + [P, P, C.c_int] + [P] * 5)
+                              + [P, P] + [P, P, C.c_int] + [P] * 5)
         L.orc_linear.argtypes = [C.c_int, C.c_int, C.c_int, P, P, P, i64, i64, P, C.c_int, C.c_int,
                                  i64, i64, P, P]
         _lib = L
@@ -131,7 +131,9 @@ def moe(inp: dict, debug: bool = False, tokens=None):
     """One MoE layer on the canonical inputs of ``synth.moe_inputs``.
 
     ``tokens`` selects a subset of token rows (each token's output depends
-    only on its own activation and logits).  Returns a dict with ``y64``
+    only on its own activation and logits).  Optional ``fc1_expert_bias``
+    [E][2I] and ``fc2_expert_bias`` [E][H] (16-bit patterns of the activation
+    dtype) are per-expert output biases of FC1 and FC2.  Returns a dict with ``y64``
     (float64, unrounded), ``y`` (16-bit patterns of the activation dtype) and,
     with ``debug``, per-slot ``a``/``h``/``o`` in slot order t*k+j.
     """
@@ -152,12 +154,14 @@ def moe(inp: dict, debug: bool = False, tokens=None):
         o = np.empty((T * k, H), dtype=np.float64)
     arr = {n: _c(inp[n], np.uint8 if n.endswith("codes") else np.uint16)
            for n in ("fc1_codes", "fc1_scales", "fc1_biases", "fc2_codes", "fc2_scales", "fc2_biases")}
+    eb = {n: _c(inp.get(n), np.uint16) for n in ("fc1_expert_bias", "fc2_expert_bias")}
     rc = lib().orc_moe(
         sp.E, H, I, k, DT[sp.act_dtype],
         FMT[sp.fc1.fmt], sp.fc1.block, DT[sp.fc1.scale_dtype],
         _p(arr["fc1_codes"]), _p(arr["fc1_scales"]), _p(arr["fc1_biases"]),
         FMT[sp.fc2.fmt], sp.fc2.block, DT[sp.fc2.scale_dtype],
         _p(arr["fc2_codes"]), _p(arr["fc2_scales"]), _p(arr["fc2_biases"]),
+        _p(eb["fc1_expert_bias"]), _p(eb["fc2_expert_bias"]),
         _p(x), _p(lg), T, _p(y64), _p(y16), _p(a), _p(h), _p(o))
     out = {"y64": y64, "y": y16, "status": rc}
     if debug:

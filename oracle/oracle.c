@@ -241,14 +241,20 @@ static void orc_matvec(const orc_mat *m, int64_t e, int64_t N, int64_t K, const 
  * Full MoE layer for T tokens.  x [T][H] and y16 [T][H] are 16-bit patterns of
  * act_dtype, logits [T][E] float32, y64 [T][H] the unrounded result.  Optional
  * per-slot diagnostics in slot order r = t*k + j: a_dbg [T*k][2I] (FC1),
- * h_dbg [T*k][I] (after SwiGLU), o_dbg [T*k][H] (FC2).  Returns 0, or -1 if a
- * ternary row it used holds the invalid field value 3 (read as 0).
+ * h_dbg [T*k][I] (after SwiGLU), o_dbg [T*k][H] (FC2).  Optional expert
+ * biases in act_dtype: fc1_ebias [E][2I], in FC1's interleaved row order, is
+ * added to FC1's output before the SwiGLU, and fc2_ebias [E][H] to FC2's
+ * output before the top-k weighting (onnxruntime pull request 33005,
+ * Description: expert bias before the SwiGLU, FC2 bias in the finalize).
+ * Returns 0, or -1 if a ternary row it used holds the invalid field value 3
+ * (read as 0).
  */
 int orc_moe(int E, int H, int I, int k, int act_dtype,
             int fc1_fmt, int fc1_block, int fc1_sdtype,
             const uint8_t *fc1_codes, const uint16_t *fc1_scales, const uint16_t *fc1_biases,
             int fc2_fmt, int fc2_block, int fc2_sdtype,
             const uint8_t *fc2_codes, const uint16_t *fc2_scales, const uint16_t *fc2_biases,
+            const uint16_t *fc1_ebias, const uint16_t *fc2_ebias,
             const uint16_t *x, const float *logits, int T,
             double *y64, uint16_t *y16, double *a_dbg, double *h_dbg, double *o_dbg) {
   orc_mat w1 = {fc1_fmt, fc1_block, fc1_sdtype, fc1_codes, fc1_scales, fc1_biases};
@@ -274,8 +280,13 @@ int orc_moe(int E, int H, int I, int k, int act_dtype,
       const int64_t r = (int64_t)t * k + j;
       const int e = ids[r];
       orc_matvec(&w1, e, 2 * (int64_t)I, H, xv, a, wrow, &bad);
+      if (fc1_ebias)
+        for (int64_t n = 0; n < 2 * I; ++n)
+          a[n] += orc_half_to_double(fc1_ebias[(int64_t)e * 2 * I + n], act_dtype);
       for (int64_t i = 0; i < I; ++i) h[i] = orc_silu(a[2 * i]) * a[2 * i + 1];
       orc_matvec(&w2, e, H, I, h, o, wrow, &bad);
+      if (fc2_ebias)
+        for (int64_t n = 0; n < H; ++n) o[n] += orc_half_to_double(fc2_ebias[(int64_t)e * H + n], act_dtype);
       for (int64_t n = 0; n < H; ++n) yt[n] += wts[r] * o[n];
       if (a_dbg) memcpy(a_dbg + r * 2 * I, a, sizeof(double) * (size_t)(2 * I));
       if (h_dbg) memcpy(h_dbg + r * I, h, sizeof(double) * (size_t)I);

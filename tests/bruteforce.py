@@ -69,9 +69,14 @@ def moe_dense(inp: dict) -> np.ndarray:
         W2 = dequant(sp.fc2.fmt, sp.fc2.block, sp.fc2.scale_dtype, inp["fc2_codes"][e],
                      inp["fc2_scales"][e], None if inp["fc2_biases"] is None else inp["fc2_biases"][e], I)
         a = x @ W1.T
+        if inp.get("fc1_expert_bias") is not None:
+            a = a + half_bits_to_f64(inp["fc1_expert_bias"][e], sp.act_dtype)[None, :]
         gate, up = a[:, 0::2], a[:, 1::2]
         h = gate / (1.0 + np.exp(-gate)) * up
-        y += g[:, e:e + 1] * (h @ W2.T)
+        o = h @ W2.T
+        if inp.get("fc2_expert_bias") is not None:
+            o = o + half_bits_to_f64(inp["fc2_expert_bias"][e], sp.act_dtype)[None, :]
+        y += g[:, e:e + 1] * o
     return y
 
 

@@ -247,6 +247,38 @@ def test_moe_vs_dense_bruteforce(oracle_lib, cfg, T):
         assert np.array_equal(out["y"], out["y64"].astype(np.float16).view(np.uint16))
 
 
+@pytest.mark.parametrize("cfg", [TINY[1], TINY[2], TINY[4]], ids=["int4-k2", "int2-int4-k4", "affine-f16"])
+@pytest.mark.parametrize("T", [1, 3])
+def test_moe_expert_bias_vs_dense_bruteforce(oracle_lib, cfg, T):
+    spec = custom_moe_spec(**cfg)
+    inp = synth.moe_inputs(spec, T=T, seed=20 + T, expert_bias=True)
+    out = oracle_lib.moe(inp)
+    ref = bf.moe_dense(inp)
+    assert np.allclose(out["y64"], ref, rtol=1e-10, atol=1e-12 * np.abs(ref).max())
+    plain = oracle_lib.moe(synth.moe_inputs(spec, T=T, seed=20 + T))["y64"]
+    assert not np.allclose(out["y64"], plain)                     # the biases change the result
+
+
+def test_moe_expert_bias_zero_weights_closed_form(oracle_lib):
+    # all codes 0: FC1's output is its bias, so h = silu(b_gate) * b_up with the
+    # gate in even rows, and y = sum_j w_j * b2[e_j]
+    spec = custom_moe_spec(E=5, H=64, I=64, top_k=3)
+    inp = synth.moe_inputs(spec, T=4, seed=3, expert_bias=True)
+    inp["fc1_codes"] = np.full_like(inp["fc1_codes"], 0x88)
+    inp["fc2_codes"] = np.full_like(inp["fc2_codes"], 0x88)
+    out = oracle_lib.moe(inp, debug=True)
+    r = oracle_lib.route(inp["logits"], 3)
+    b1 = bf.half_bits_to_f64(inp["fc1_expert_bias"], "bf16")
+    b2 = bf.half_bits_to_f64(inp["fc2_expert_bias"], "bf16")
+    ids = r["ids"].ravel()
+    assert np.array_equal(out["a"], b1[ids])
+    g, u = b1[ids][:, 0::2], b1[ids][:, 1::2]
+    assert np.allclose(out["h"], g / (1.0 + np.exp(-g)) * u, rtol=1e-14, atol=0)
+    assert np.array_equal(out["o"], b2[ids])
+    y = (r["w"][:, :, None] * b2[r["ids"]]).sum(axis=1)
+    assert np.allclose(out["y64"], y, rtol=1e-14, atol=1e-16)
+
+
 def test_moe_expert_permutation_invariance(oracle_lib):
     spec = custom_moe_spec(E=6, H=64, I=64, top_k=3)
     inp = synth.moe_inputs(spec, T=4, seed=9)
