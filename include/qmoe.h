@@ -70,7 +70,7 @@
 extern "C" {
 #endif
 
-#define QMOE_ABI_VERSION 1
+#define QMOE_ABI_VERSION 2
 
 typedef enum qmoe_status {
   QMOE_OK = 0,
@@ -135,6 +135,15 @@ typedef struct qmoe_forward_opts {
                         a stage whose pair is incomplete is not timed */
   int32_t num_events; /* entries in `events` (0 = none) */
   int32_t reserved2;  /* must be 0 */
+  /* Optional per-expert output biases, device, 16-bit values of the layer's
+     act_dtype (onnxruntime pull request 33005, Description: an expert bias
+     applied after FC1 and before the SwiGLU, and the FC2 bias in the top-k
+     finalize).  fc1_bias [E][2I] is in FC1's interleaved row order (row 2i
+     gate, 2i+1 up) and is added to FC1's output before the SwiGLU; fc2_bias
+     [E][H] is added to each expert's FC2 output before that output is scaled
+     by its routing weight.  Null: no bias. */
+  const void *fc1_bias;
+  const void *fc2_bias;
 } qmoe_forward_opts;
 
 /* Host-side description of what a forward call would launch (diagnostic). */

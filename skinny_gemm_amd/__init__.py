@@ -41,7 +41,8 @@ class LayerDesc(C.Structure):
 class ForwardOpts(C.Structure):
     _fields_ = [("path", C.c_int32), ("reserved", C.c_int32), ("h_out", C.c_void_p),
                 ("ids_out", C.c_void_p), ("w_out", C.c_void_p), ("counts_out", C.c_void_p),
-                ("events", C.POINTER(C.c_void_p)), ("num_events", C.c_int32), ("reserved2", C.c_int32)]
+                ("events", C.POINTER(C.c_void_p)), ("num_events", C.c_int32), ("reserved2", C.c_int32),
+                ("fc1_bias", C.c_void_p), ("fc2_bias", C.c_void_p)]
 
 
 class Plan(C.Structure):
@@ -161,13 +162,15 @@ def forward(desc, packed, x, logits, T, top_k, y, ws, stream=None):
 
 
 def forward_ex(desc, packed, x, logits, T, top_k, y, ws, stream=None, path="auto", h_out=None,
-               ids_out=None, w_out=None, counts_out=None, events=None):
-    """``events``: optional list of raw hipEvent_t handles (ints), two per plan stage."""
+               ids_out=None, w_out=None, counts_out=None, events=None, fc1_bias=None, fc2_bias=None):
+    """``events``: optional list of raw hipEvent_t handles (ints), two per plan stage.
+    ``fc1_bias`` [E][2I] / ``fc2_bias`` [E][H]: optional per-expert output biases
+    in the activation dtype."""
     ev = None
     if events:
         ev = (C.c_void_p * len(events))(*[C.c_void_p(int(e)) for e in events])
     opts = ForwardOpts(PATH[path], 0, _ptr(h_out), _ptr(ids_out), _ptr(w_out), _ptr(counts_out),
-                       ev, len(events) if events else 0, 0)
+                       ev, len(events) if events else 0, 0, _ptr(fc1_bias), _ptr(fc2_bias))
     _check(lib().qmoe_forward_ex(C.byref(desc), _ptr(packed), _ptr(x), _ptr(logits), T, top_k,
                                  _ptr(y), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream),
                                  C.byref(opts)))

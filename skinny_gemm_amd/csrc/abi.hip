@@ -538,6 +538,8 @@ qmoe_status qmoe_forward_ex(const qmoe_layer_desc *desc, const void *packed, con
     q1.out_rowmax = hmax;
     q1.h_dbg = opts ? opts->h_out : nullptr;
     q1.row_list = ra.r.row_list;
+    q1.bias = opts ? (const uint16_t *)opts->fc1_bias : nullptr;
+    q1.act_dtype = desc->act_dtype;
     e = begin();
     if (e == hipSuccess) e = launch_grouped(q1, kGEpiSwiGLU, p.max_tiles, s);
     if (e == hipSuccess) e = end();
@@ -549,6 +551,8 @@ qmoe_status qmoe_forward_ex(const qmoe_layer_desc *desc, const void *packed, con
     q2.in_row_elems = desc->inter;
     q2.in_rowmax = hmax;
     q2.out_f32 = o;
+    q2.bias = opts ? (const uint16_t *)opts->fc2_bias : nullptr;
+    q2.act_dtype = desc->act_dtype;
     e = begin();
     if (e == hipSuccess) e = launch_grouped(q2, kGEpiStoreF32, p.max_tiles, s);
     if (e == hipSuccess) e = end();
@@ -581,6 +585,8 @@ qmoe_status qmoe_forward_ex(const qmoe_layer_desc *desc, const void *packed, con
   g1.h_hi = h_hi;
   g1.h_lo = h_lo;
   g1.h_dbg = opts ? opts->h_out : nullptr;
+  g1.bias = opts ? (const uint16_t *)opts->fc1_bias : nullptr;
+  g1.act_dtype = desc->act_dtype;
   e = begin();
   if (e == hipSuccess)
     e = launch_gemv(g1, fc1_routes ? kEpiSwiGLURouted : kEpiSwiGLU, desc->act_dtype == QMOE_DTYPE_F16, p.mmax1,
@@ -600,6 +606,7 @@ qmoe_status qmoe_forward_ex(const qmoe_layer_desc *desc, const void *packed, con
   g2.out_f32 = o;
   g2.out_act = (uint16_t *)y;
   g2.act_dtype = desc->act_dtype;
+  g2.bias = opts ? (const uint16_t *)opts->fc2_bias : nullptr;
   g2.route_w = ra.r.w;
   e = begin();
   if (e == hipSuccess) e = launch_gemv(g2, kEpiDown, 0, p.mmax2, p.ks2, p.tn2, L.fc2.block, p.max_active, s);

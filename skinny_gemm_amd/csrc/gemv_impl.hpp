@@ -416,6 +416,11 @@ __global__ __launch_bounds__(512) void gemv_kernel(const GemvArgs a) {
     float v = 0.f;
     for (int w = 0; w < KS; ++w) v += s_red[w * NV * kLanes + idx];
     const int64_t n = (int64_t)rg * kRowsPerGroup + 16 * (t0 + t) + (lo & 15);
+    // optional per-expert output bias: FC1 before the SwiGLU, FC2 before the
+    // routing weight
+    if constexpr (EPI != kEpiStoreAct) {
+      if (a.bias) v += half_to_f32_rt(a.bias[(int64_t)e * N + n], a.act_dtype == QMOE_DTYPE_F16);
+    }
     if constexpr (EPI == kEpiStoreAct) {
       if (valid) a.out_act[(int64_t)m * N + n] = f32_to_act(v, a.act_dtype == QMOE_DTYPE_F16);
     } else if constexpr (SWIGLU) {

@@ -457,8 +457,15 @@ __global__ __launch_bounds__(256) void grouped_kernel(const GroupedArgs a) {
     }
   }
 
-  // epilogue: lane holds rows 16i + 4(lane/16) + el, column 16j + lane%16
+  // epilogue: lane holds rows 16i + 4(lane/16) + el, column 16j + lane%16;
+  // the optional per-expert output bias goes in before the SwiGLU or store
   const float winv = 1.f / wsc;
+  float bv[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j)
+    bv[j] = a.bias ? half_to_f32_rt(a.bias[(int64_t)e * a.N + nw + 16 * j + (lane & 15)],
+                                    a.act_dtype == QMOE_DTYPE_F16)
+                   : 0.f;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
 #pragma unroll
@@ -469,7 +476,7 @@ __global__ __launch_bounds__(256) void grouped_kernel(const GroupedArgs a) {
       float hmax = 0.f;
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
-        const float v = acc[i][j][el] * inv;
+        const float v = fmaf(acc[i][j][el], inv, bv[j]);
         const int64_t n = nw + 16 * j + (lane & 15);
         if constexpr (EPI == kGEpiSwiGLU) {
           const float up = __shfl_xor(v, 1);

@@ -215,7 +215,8 @@ struct GemvArgs {
   uint16_t *out_act;       // kEpiStoreAct: [m][N]; kEpiDown with top-1: y [t][N]
   uint16_t *h_hi, *h_lo;   // kEpiSwiGLU: [p][N/2] bf16 parts of h
   float *h_dbg;            // kEpiSwiGLU: optional [slot][N/2] fp32
-  int act_dtype;           // kEpiStoreAct, kEpiDown
+  const uint16_t *bias;    // kEpiSwiGLU, kEpiDown: optional per-expert output bias [E][N] in act_dtype
+  int act_dtype;           // activation dtype of out_act and bias
   const float *route_w;    // kEpiDown: routing weights [T*k]
   // kEpiSwiGLURouted: router logits [T][E] and the routing outputs
   const float *logits;
@@ -284,7 +285,8 @@ struct GroupedArgs {
   float *out_f32;          // kGEpiSwiGLU: h [p][N/2]; kGEpiStoreF32: o [p][N]
   uint32_t *out_rowmax;    // kGEpiSwiGLU: |max| bits of h per row (atomicMax), zero on entry
   uint16_t *out_act;       // kGEpiStoreAct: y [m][N]
-  int act_dtype;
+  const uint16_t *bias;    // routed: optional per-expert output bias [E][N] in act_dtype
+  int act_dtype;           // activation dtype of out_act and bias
   float *h_dbg;            // optional fp32 copy of h in slot order
   const int32_t *row_list;
 };

@@ -42,6 +42,9 @@ class MoeLayer:
         prepack(self.desc, dev["fc1_codes"], dev["fc1_scales"], dev["fc1_biases"], dev["fc2_codes"],
                 dev["fc2_scales"], dev["fc2_biases"], self.packed)
         del dev
+        # optional per-expert output biases of FC1 [E][2I] and FC2 [E][H]
+        self.fc1_bias = to_device_bits(arrays.get("fc1_expert_bias"), None, device)
+        self.fc2_bias = to_device_bits(arrays.get("fc2_expert_bias"), None, device)
 
     @classmethod
     def from_spec(cls, spec, arrays, device="cuda"):
@@ -68,7 +71,8 @@ class MoeLayer:
             dbg["counts"] = torch.full((self.E,), -1, dtype=torch.int32, device=self.device)
         forward_ex(self.desc, self.packed, x, logits, T, top_k, y, ws, stream=stream, path=path,
                    h_out=dbg.get("h"), ids_out=dbg.get("ids"), w_out=dbg.get("w"),
-                   counts_out=dbg.get("counts"), events=events)
+                   counts_out=dbg.get("counts"), events=events, fc1_bias=self.fc1_bias,
+                   fc2_bias=self.fc2_bias)
         return (y, dbg) if debug else y
 
     def unpack(self, which: int) -> torch.Tensor:

@@ -151,7 +151,7 @@ def _matrix(workload: str, tag: str, seed: int, fmt: MatFmt, E: int, N: int, K: 
 
 
 def moe_inputs(spec: MoeSpec, T: int, seed: int = 0, logits_mode: str = "iid",
-               weight_copy: int = 0, weights: bool = True, expert_bias: bool = False) -> dict:
+               weight_copy: int = 0, weights: bool = True, expert_bias: float = 0.0) -> dict:
     """Inputs of one MoE layer call with T tokens.
 
     logits_mode: "iid" draws logits[t][e] ~ N(0,1) independently (plus the
@@ -161,8 +161,9 @@ def moe_inputs(spec: MoeSpec, T: int, seed: int = 0, logits_mode: str = "iid",
     are equal and the selection depends on the tie rule.
     weight_copy selects an independent set of expert weights (distinct copies
     for cache-cold timing); activations and logits do not depend on it.
-    expert_bias adds per-expert output biases of FC1 ([E][2I]) and FC2
-    ([E][H]), N(0, 0.1) in the activation dtype; otherwise both are None.
+    expert_bias > 0 adds per-expert output biases of FC1 ([E][2I]) and FC2
+    ([E][H]), N(0, expert_bias^2) in the activation dtype; otherwise both are
+    None.
     """
     wl = spec.name
     out = {"spec": spec, "T": T, "seed": seed}
@@ -173,10 +174,10 @@ def moe_inputs(spec: MoeSpec, T: int, seed: int = 0, logits_mode: str = "iid",
         out["fc2_codes"], out["fc2_scales"], out["fc2_biases"] = _matrix(
             wl, "fc2" + wtag, seed, spec.fc2, spec.E, spec.H, spec.I, spec.scale_sigma, spec.bias_sigma)
     out["fc1_expert_bias"] = out["fc2_expert_bias"] = None
-    if expert_bias:
+    if expert_bias > 0:
         wtag = "" if weight_copy == 0 else f"@copy{weight_copy}"
-        b1 = 0.1 * normals(Key(seed, wl, "fc1_expert_bias" + wtag), spec.E * 2 * spec.I)
-        b2 = 0.1 * normals(Key(seed, wl, "fc2_expert_bias" + wtag), spec.E * spec.H)
+        b1 = expert_bias * normals(Key(seed, wl, "fc1_expert_bias" + wtag), spec.E * 2 * spec.I)
+        b2 = expert_bias * normals(Key(seed, wl, "fc2_expert_bias" + wtag), spec.E * spec.H)
         out["fc1_expert_bias"] = _to_bits(b1, spec.act_dtype).reshape(spec.E, 2 * spec.I)
         out["fc2_expert_bias"] = _to_bits(b2, spec.act_dtype).reshape(spec.E, spec.H)
     x = normals(Key(seed, wl, f"x[T={T}]"), T * spec.H)

@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_abi_version():
-    assert q.abi_version() == 1
+    assert q.abi_version() == 2
 
 
 def _desc(**kw):

@@ -39,21 +39,21 @@ def _weights(name, seed):
     return synth.moe_inputs(spec, 1, seed)
 
 
-def _inputs(spec, T, seed, logits_mode="iid"):
+def _inputs(spec, T, seed, logits_mode="iid", expert_bias=0.0):
     if spec.name in synth.MOE_WORKLOADS:
         w = _weights(spec.name, seed)
-        inp = synth.moe_inputs(spec, T, seed, logits_mode, weights=False)
+        inp = synth.moe_inputs(spec, T, seed, logits_mode, weights=False, expert_bias=expert_bias)
         for k in w:
-            if k.startswith("fc"):
+            if k.startswith("fc") and not k.endswith("expert_bias"):
                 inp[k] = w[k]
         return inp
-    return synth.moe_inputs(spec, T, seed, logits_mode)
+    return synth.moe_inputs(spec, T, seed, logits_mode, expert_bias=expert_bias)
 
 
-def run_case(spec, T, seed, logits_mode="iid", path="auto", tokens=None):
+def run_case(spec, T, seed, logits_mode="iid", path="auto", tokens=None, expert_bias=0.0):
     from skinny_gemm_amd.layer import MoeLayer, to_device_bits, bits_of
-    log(f"[moe] {spec.name} T={T} seed={seed} logits={logits_mode} path={path}")
-    inp = _inputs(spec, T, seed, logits_mode)
+    log(f"[moe] {spec.name} T={T} seed={seed} logits={logits_mode} path={path} expert_bias={expert_bias}")
+    inp = _inputs(spec, T, seed, logits_mode, expert_bias)
     layer = MoeLayer.from_spec(spec, inp)
     x = to_device_bits(inp["x"], spec.act_dtype)
     lg = torch.from_numpy(inp["logits"]).cuda()
@@ -84,6 +84,7 @@ def run_case(spec, T, seed, logits_mode="iid", path="auto", tokens=None):
     # 4-bit affine codes or f16 scales once to f16, about 2^-11 relative
     assert hn.max() < 4e-3, f"h row error {hn.max()}"
     assert res["ok"], res
+    res["ybits"], res["inp"] = ybits, inp
     return res
 
 
@@ -269,3 +270,48 @@ def test_mixed_int2_int4_prefill(seed):
     inp = _inputs(spec, 2048, seed)
     r = oracle.route(inp["logits"], spec.top_k)
     log(f"       expert rows: max {r['counts'].max()} min {r['counts'].min()} (mean {r['counts'].mean():.0f})")
+
+
+# ------------------------------------------------- per-expert output biases
+def _bias_case(spec, T, seed, sigma, path="auto", tokens=None):
+    """Parity with FC1 and FC2 expert biases; the inputs must be such that
+    leaving out either bias fails the tolerance by a wide margin (checked on
+    the oracle), so the comparison really tests both."""
+    res = run_case(spec, T, seed, path=path, tokens=tokens, expert_bias=sigma)
+    inp = res["inp"]
+    for drop in ("fc1_expert_bias", "fc2_expert_bias"):
+        alt = dict(inp)
+        alt[drop] = None
+        ref = oracle.moe(alt, tokens=tokens)
+        y = ref["y64"]
+        base = oracle.moe(inp, tokens=tokens)["y64"]
+        rel = np.linalg.norm(y - base, axis=1) / np.linalg.norm(base, axis=1)
+        assert rel.min() > 1e-2, f"inputs too weak to test {drop}: {rel.min():.2e}"
+        assert not compare(res["ybits"], ref["y"], ref["y64"], spec.act_dtype)["ok"]
+
+
+@pytest.mark.parametrize("name,T,path,sigma", [
+    ("switch_base_ternary", 1, "auto", 0.1),   # routing inside FC1, y written by FC2 (top-1)
+    ("dsv2lite_int4", 1, "auto", 1.0),         # routing inside FC1, weighted combine
+    ("dsv2lite_int4", 4, "auto", 1.0),         # small routing kernel
+    ("dsv2lite_int4", 8, "auto", 1.0),         # routing kernels
+    ("dsv2lite_int4", 8, "grouped", 1.0),
+    ("single_expert_int4", 1, "grouped", 0.5),
+    ("switch_base_ternary", 1, "grouped", 0.1),
+])
+def test_expert_bias_workloads(name, T, path, sigma):
+    _bias_case(synth.MOE_WORKLOADS[name], T, 7, sigma, path)
+
+
+@pytest.mark.parametrize("cfg", [SWEEP[1], SWEEP[3], SWEEP[6]], ids=["int2-int4", "affine-f16", "int2-ternary"])
+@pytest.mark.parametrize("path", ["auto", "grouped"])
+@pytest.mark.parametrize("T", [3, 33])
+def test_expert_bias_sweep(cfg, path, T):
+    _bias_case(custom_moe_spec(**cfg), T, 40 + T, 0.1, path)
+
+
+def test_expert_bias_mixed_prefill_sampled():
+    """2048 tokens through the grouped path with biases; outputs sampled."""
+    spec = synth.MOE_WORKLOADS["mixed_int2_int4_prefill"]
+    sample = [0, 17, 555, 1024, 2047]
+    _bias_case(spec, 2048, 3, 0.5, tokens=sample)

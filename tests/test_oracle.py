@@ -251,7 +251,7 @@ def test_moe_vs_dense_bruteforce(oracle_lib, cfg, T):
 @pytest.mark.parametrize("T", [1, 3])
 def test_moe_expert_bias_vs_dense_bruteforce(oracle_lib, cfg, T):
     spec = custom_moe_spec(**cfg)
-    inp = synth.moe_inputs(spec, T=T, seed=20 + T, expert_bias=True)
+    inp = synth.moe_inputs(spec, T=T, seed=20 + T, expert_bias=0.1)
     out = oracle_lib.moe(inp)
     ref = bf.moe_dense(inp)
     assert np.allclose(out["y64"], ref, rtol=1e-10, atol=1e-12 * np.abs(ref).max())
@@ -263,7 +263,7 @@ def test_moe_expert_bias_zero_weights_closed_form(oracle_lib):
     # all codes 0: FC1's output is its bias, so h = silu(b_gate) * b_up with the
     # gate in even rows, and y = sum_j w_j * b2[e_j]
     spec = custom_moe_spec(E=5, H=64, I=64, top_k=3)
-    inp = synth.moe_inputs(spec, T=4, seed=3, expert_bias=True)
+    inp = synth.moe_inputs(spec, T=4, seed=3, expert_bias=0.1)
     inp["fc1_codes"] = np.full_like(inp["fc1_codes"], 0x88)
     inp["fc2_codes"] = np.full_like(inp["fc2_codes"], 0x88)
     out = oracle_lib.moe(inp, debug=True)
