@@ -53,12 +53,12 @@ def lib():
         L.orc_unpack_codes.restype = i64
         L.orc_unpack_codes.argtypes = [C.c_int, P, i64, i64, P]
         L.orc_dequant.argtypes = [C.c_int, C.c_int, C.c_int, P, P, P, i64, i64, P]
-        L.orc_route.argtypes = [C.c_int, C.c_int, C.c_int, P, P, P, P, P, P]
+        L.orc_route.argtypes = [C.c_int, C.c_int, C.c_int, C.c_int, P, P, P, P, P, P]
         L.orc_silu.restype = C.c_double
         L.orc_silu.argtypes = [C.c_double]
         L.orc_moe.restype = C.c_int
         L.orc_moe.argtypes = ([C.c_int] * 5 + [C.c_int] * 3 + [P] * 3 + [C.c_int] * 3 + [P] * 3
-                              + [P, P] + [P, P, C.c_int] + [P] * 5)
+                              + [P, P, C.c_int] + [P, P, C.c_int] + [P] * 5)
         L.orc_linear.argtypes = [C.c_int, C.c_int, C.c_int, P, P, P, i64, i64, P, C.c_int, C.c_int,
                                  i64, i64, P, P]
         _lib = L
@@ -113,7 +113,10 @@ def dequant(fmt: str, block: int, scale_dtype: str, codes, scales, biases, rows:
 
 
 # ---------------------------------------------------------------- routing
-def route(logits, top_k: int):
+def route(logits, top_k: int, renorm: bool = True):
+    """Top-k ids, weights and the expert map.  ``renorm``: weights are the
+    softmax over the selected logits; otherwise the softmax over all experts'
+    logits, the selected probabilities kept unnormalised."""
     lg = _c(logits, np.float32)
     T, E = lg.shape
     S = T * top_k
@@ -122,18 +125,19 @@ def route(logits, top_k: int):
     counts = np.empty(E, dtype=np.int32)
     offsets = np.empty(E + 1, dtype=np.int32)
     rows = np.empty(max(S, 1), dtype=np.int32)
-    lib().orc_route(T, E, top_k, _p(lg), _p(ids), _p(w), _p(counts), _p(offsets), _p(rows))
+    lib().orc_route(T, E, top_k, int(bool(renorm)), _p(lg), _p(ids), _p(w), _p(counts), _p(offsets), _p(rows))
     return {"ids": ids, "w": w, "counts": counts, "offsets": offsets, "row_list": rows[:S]}
 
 
 # -------------------------------------------------------------------- MoE
-def moe(inp: dict, debug: bool = False, tokens=None):
+def moe(inp: dict, debug: bool = False, tokens=None, renorm: bool = True):
     """One MoE layer on the canonical inputs of ``synth.moe_inputs``.
 
     ``tokens`` selects a subset of token rows (each token's output depends
     only on its own activation and logits).  Optional ``fc1_expert_bias``
     [E][2I] and ``fc2_expert_bias`` [E][H] (16-bit patterns of the activation
-    dtype) are per-expert output biases of FC1 and FC2.  Returns a dict with ``y64``
+    dtype) are per-expert output biases of FC1 and FC2.  ``renorm`` selects
+    the routing weights as in ``route``.  Returns a dict with ``y64``
     (float64, unrounded), ``y`` (16-bit patterns of the activation dtype) and,
     with ``debug``, per-slot ``a``/``h``/``o`` in slot order t*k+j.
     """
@@ -161,7 +165,7 @@ def moe(inp: dict, debug: bool = False, tokens=None):
         _p(arr["fc1_codes"]), _p(arr["fc1_scales"]), _p(arr["fc1_biases"]),
         FMT[sp.fc2.fmt], sp.fc2.block, DT[sp.fc2.scale_dtype],
         _p(arr["fc2_codes"]), _p(arr["fc2_scales"]), _p(arr["fc2_biases"]),
-        _p(eb["fc1_expert_bias"]), _p(eb["fc2_expert_bias"]),
+        _p(eb["fc1_expert_bias"]), _p(eb["fc2_expert_bias"]), int(bool(renorm)),
         _p(x), _p(lg), T, _p(y64), _p(y16), _p(a), _p(h), _p(o))
     out = {"y64": y64, "y": y16, "status": rc}
     if debug:

@@ -178,10 +178,13 @@ void orc_dequant(int fmt, int block, int sdtype, const uint8_t *codes, const uin
 /* -------------------------------- routing -------------------------------- */
 
 /* Per token: the k largest logits (ties to the lower expert index), in
- * descending order; weights = softmax over the selected logits.  Then the
- * expert map: counts, exclusive offsets (E+1 entries) and the list of flat
- * slots r = t*k + j grouped by expert, ascending r within an expert. */
-void orc_route(int T, int E, int k, const float *logits, int32_t *ids, double *w,
+ * descending order.  Weights: with renorm, the softmax over the k selected
+ * logits (they sum to 1); without, the softmax over all E logits, of which
+ * the k selected probabilities are kept as they are (for k = 1 the Switch
+ * router's top probability).  Then the expert map: counts, exclusive offsets
+ * (E+1 entries) and the list of flat slots r = t*k + j grouped by expert,
+ * ascending r within an expert. */
+void orc_route(int T, int E, int k, int renorm, const float *logits, int32_t *ids, double *w,
                int32_t *counts, int32_t *offsets, int32_t *row_list) {
   char *taken = (char *)malloc((size_t)E);
   for (int t = 0; t < T; ++t) {
@@ -198,7 +201,10 @@ void orc_route(int T, int E, int k, const float *logits, int32_t *ids, double *w
     }
     double m = (double)l[ids[(int64_t)t * k]];
     double sum = 0.0;
-    for (int j = 0; j < k; ++j) sum += exp((double)l[ids[(int64_t)t * k + j]] - m);
+    if (renorm)
+      for (int j = 0; j < k; ++j) sum += exp((double)l[ids[(int64_t)t * k + j]] - m);
+    else
+      for (int e = 0; e < E; ++e) sum += exp((double)l[e] - m);
     for (int j = 0; j < k; ++j) w[(int64_t)t * k + j] = exp((double)l[ids[(int64_t)t * k + j]] - m) / sum;
   }
   free(taken);
@@ -247,14 +253,14 @@ static void orc_matvec(const orc_mat *m, int64_t e, int64_t N, int64_t K, const 
  * output before the top-k weighting (onnxruntime pull request 33005,
  * Description: expert bias before the SwiGLU, FC2 bias in the finalize).
  * Returns 0, or -1 if a ternary row it used holds the invalid field value 3
- * (read as 0).
+ * (read as 0).  renorm selects the routing weights as in orc_route.
  */
 int orc_moe(int E, int H, int I, int k, int act_dtype,
             int fc1_fmt, int fc1_block, int fc1_sdtype,
             const uint8_t *fc1_codes, const uint16_t *fc1_scales, const uint16_t *fc1_biases,
             int fc2_fmt, int fc2_block, int fc2_sdtype,
             const uint8_t *fc2_codes, const uint16_t *fc2_scales, const uint16_t *fc2_biases,
-            const uint16_t *fc1_ebias, const uint16_t *fc2_ebias,
+            const uint16_t *fc1_ebias, const uint16_t *fc2_ebias, int renorm,
             const uint16_t *x, const float *logits, int T,
             double *y64, uint16_t *y16, double *a_dbg, double *h_dbg, double *o_dbg) {
   orc_mat w1 = {fc1_fmt, fc1_block, fc1_sdtype, fc1_codes, fc1_scales, fc1_biases};
@@ -271,7 +277,7 @@ int orc_moe(int E, int H, int I, int k, int act_dtype,
   double *o = (double *)malloc(sizeof(double) * (size_t)H);
   double *wrow = (double *)malloc(sizeof(double) * (size_t)(H > I ? H : I));
   int bad = 0;
-  orc_route(T, E, k, logits, ids, wts, counts, offsets, rows);
+  orc_route(T, E, k, renorm, logits, ids, wts, counts, offsets, rows);
   for (int t = 0; t < T; ++t) {
     for (int64_t n = 0; n < H; ++n) xv[n] = orc_half_to_double(x[(int64_t)t * H + n], act_dtype);
     double *yt = y64 + (int64_t)t * H;

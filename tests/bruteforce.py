@@ -42,24 +42,25 @@ def dequant(fmt: str, block: int, sdtype: str, codes, scales, biases, K: int) ->
     return w
 
 
-def topk_gates(logits: np.ndarray, k: int) -> np.ndarray:
-    """Dense gate matrix g [T][E]."""
+def topk_gates(logits: np.ndarray, k: int, renorm: bool = True) -> np.ndarray:
+    """Dense gate matrix g [T][E]: softmax over the selected logits, or
+    (renorm False) the selected entries of the softmax over all logits."""
     T, E = logits.shape
     g = np.zeros((T, E), dtype=np.float64)
     for t in range(T):
         order = np.lexsort((np.arange(E), -logits[t].astype(np.float64)))
         sel = order[:k]
-        z = logits[t, sel].astype(np.float64)
+        z = logits[t].astype(np.float64)
         p = np.exp(z - z.max())
-        g[t, sel] = p / p.sum()
+        g[t, sel] = p[sel] / (p[sel].sum() if renorm else p.sum())
     return g
 
 
-def moe_dense(inp: dict) -> np.ndarray:
+def moe_dense(inp: dict, renorm: bool = True) -> np.ndarray:
     sp = inp["spec"]
     E, H, I, k = sp.E, sp.H, sp.I, sp.top_k
     x = half_bits_to_f64(inp["x"], sp.act_dtype)
-    g = topk_gates(np.asarray(inp["logits"]), k)
+    g = topk_gates(np.asarray(inp["logits"]), k, renorm)
     y = np.zeros((x.shape[0], H), dtype=np.float64)
     for e in range(E):
         if not np.any(g[:, e]):

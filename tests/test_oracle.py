@@ -223,6 +223,24 @@ def test_route_ties(oracle_lib, E, k):
     assert r["ids"][0].tolist() == list(range(k))
 
 
+@pytest.mark.parametrize("E,k", [(1, 1), (64, 1), (64, 6), (128, 8), (256, 8), (7, 7)])
+def test_route_unnormalised(oracle_lib, E, k):
+    # the selected entries of the softmax over all logits (scipy's), same ids
+    # and expert map as the renormalised routing
+    lg = np.random.default_rng(E + 7 * k).standard_normal((21, E)).astype(np.float32) * 2
+    lg[3] = np.round(lg[3])                                      # ties
+    r = oracle_lib.route(lg, k, renorm=False)
+    n = oracle_lib.route(lg, k)
+    for key in ("ids", "counts", "offsets", "row_list"):
+        assert np.array_equal(r[key], n[key])
+    p = scipy.special.softmax(lg.astype(np.float64), axis=1)
+    assert np.allclose(r["w"], np.take_along_axis(p, r["ids"], axis=1), rtol=1e-13, atol=0)
+    if k == E:                                                   # nothing left out: both agree
+        assert np.allclose(r["w"], n["w"], rtol=1e-14, atol=0)
+    else:
+        assert np.all(r["w"].sum(1) < 1.0)
+
+
 # --------------------------------------------------- whole layer vs brute force
 TINY = [
     dict(E=1, H=64, I=64, top_k=1, fc1="sym_int4"),
@@ -257,6 +275,17 @@ def test_moe_expert_bias_vs_dense_bruteforce(oracle_lib, cfg, T):
     assert np.allclose(out["y64"], ref, rtol=1e-10, atol=1e-12 * np.abs(ref).max())
     plain = oracle_lib.moe(synth.moe_inputs(spec, T=T, seed=20 + T))["y64"]
     assert not np.allclose(out["y64"], plain)                     # the biases change the result
+
+
+@pytest.mark.parametrize("cfg", [TINY[1], dict(E=6, H=64, I=128, top_k=3, fc1="sym_int2", fc2="sym_int4")],
+                         ids=["int4-k2", "int2-int4-k3"])
+def test_moe_unnormalised_weights_vs_dense_bruteforce(oracle_lib, cfg):
+    spec = custom_moe_spec(**cfg)
+    inp = synth.moe_inputs(spec, T=3, seed=31)
+    out = oracle_lib.moe(inp, renorm=False)
+    ref = bf.moe_dense(inp, renorm=False)
+    assert np.allclose(out["y64"], ref, rtol=1e-10, atol=1e-12 * np.abs(ref).max())
+    assert not np.allclose(out["y64"], oracle_lib.moe(inp)["y64"])
 
 
 def test_moe_expert_bias_zero_weights_closed_form(oracle_lib):
