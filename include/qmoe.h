@@ -70,7 +70,7 @@
 extern "C" {
 #endif
 
-#define QMOE_ABI_VERSION 2
+#define QMOE_ABI_VERSION 3
 
 typedef enum qmoe_status {
   QMOE_OK = 0,
@@ -120,6 +120,16 @@ typedef struct qmoe_layer_desc {
   qmoe_qmatrix_desc fc2;
 } qmoe_layer_desc;
 
+/* Routing weights of the k selected experts of a token (top-k by logit, ties
+   to the lower expert index).  RENORMALIZED: the softmax over the k selected
+   logits, so the weights sum to 1.  SOFTMAX_ALL: the softmax over all E
+   logits, of which the k selected probabilities are used as they are (for
+   k = 1, the top probability of a Switch-style router); they sum to at most 1. */
+typedef enum qmoe_topk_weights {
+  QMOE_TOPK_RENORMALIZED = 0,
+  QMOE_TOPK_SOFTMAX_ALL = 1
+} qmoe_topk_weights;
+
 /* Optional controls and diagnostics of qmoe_forward_ex.  Zero-initialise. */
 typedef struct qmoe_forward_opts {
   int32_t path;      /* qmoe_path */
@@ -144,6 +154,8 @@ typedef struct qmoe_forward_opts {
      by its routing weight.  Null: no bias. */
   const void *fc1_bias;
   const void *fc2_bias;
+  int32_t topk_weights; /* qmoe_topk_weights: how the routing weights are formed */
+  int32_t reserved3;    /* must be 0 */
 } qmoe_forward_opts;
 
 /* Host-side description of what a forward call would launch (diagnostic). */

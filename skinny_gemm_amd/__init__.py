@@ -18,6 +18,7 @@ LIB_PATH = os.environ.get("QMOE_LIBRARY") or os.path.join(HERE, "libqmoe.so")
 QTYPE = {"sym_int4": 0, "sym_int2": 1, "ternary": 2, "affine_int2": 3, "affine_int4": 4}
 DTYPE = {"bf16": 0, "f16": 1, "f32": 2}
 PATH = {"auto": 0, "gemv": 1, "grouped": 2}
+TOPK_WEIGHTS = {"renormalized": 0, "softmax_all": 1}
 STATUS = {0: "OK", 1: "ERR_INVALID_ARGUMENT", 2: "ERR_UNSUPPORTED", 3: "ERR_WORKSPACE_TOO_SMALL",
           4: "ERR_DEVICE"}
 
@@ -42,7 +43,8 @@ class ForwardOpts(C.Structure):
     _fields_ = [("path", C.c_int32), ("reserved", C.c_int32), ("h_out", C.c_void_p),
                 ("ids_out", C.c_void_p), ("w_out", C.c_void_p), ("counts_out", C.c_void_p),
                 ("events", C.POINTER(C.c_void_p)), ("num_events", C.c_int32), ("reserved2", C.c_int32),
-                ("fc1_bias", C.c_void_p), ("fc2_bias", C.c_void_p)]
+                ("fc1_bias", C.c_void_p), ("fc2_bias", C.c_void_p), ("topk_weights", C.c_int32),
+                ("reserved3", C.c_int32)]
 
 
 class Plan(C.Structure):
@@ -162,22 +164,26 @@ def forward(desc, packed, x, logits, T, top_k, y, ws, stream=None):
 
 
 def forward_ex(desc, packed, x, logits, T, top_k, y, ws, stream=None, path="auto", h_out=None,
-               ids_out=None, w_out=None, counts_out=None, events=None, fc1_bias=None, fc2_bias=None):
+               ids_out=None, w_out=None, counts_out=None, events=None, fc1_bias=None, fc2_bias=None,
+               topk_weights="renormalized"):
     """``events``: optional list of raw hipEvent_t handles (ints), two per plan stage.
     ``fc1_bias`` [E][2I] / ``fc2_bias`` [E][H]: optional per-expert output biases
-    in the activation dtype."""
+    in the activation dtype.  ``topk_weights``: "renormalized" (softmax over
+    the selected logits) or "softmax_all" (selected entries of the softmax
+    over all experts)."""
     ev = None
     if events:
         ev = (C.c_void_p * len(events))(*[C.c_void_p(int(e)) for e in events])
     opts = ForwardOpts(PATH[path], 0, _ptr(h_out), _ptr(ids_out), _ptr(w_out), _ptr(counts_out),
-                       ev, len(events) if events else 0, 0, _ptr(fc1_bias), _ptr(fc2_bias))
+                       ev, len(events) if events else 0, 0, _ptr(fc1_bias), _ptr(fc2_bias),
+                       TOPK_WEIGHTS[topk_weights], 0)
     _check(lib().qmoe_forward_ex(C.byref(desc), _ptr(packed), _ptr(x), _ptr(logits), T, top_k,
                                  _ptr(y), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream),
                                  C.byref(opts)))
 
 
-def forward_plan(desc, T: int, top_k: int, path: str = "auto") -> dict:
-    opts = ForwardOpts(PATH[path], 0, None, None, None, None, None, 0, 0)
+def forward_plan(desc, T: int, top_k: int, path: str = "auto", topk_weights: str = "renormalized") -> dict:
+    opts = ForwardOpts(PATH[path], 0, None, None, None, None, None, 0, 0, None, None, TOPK_WEIGHTS[topk_weights], 0)
     p = Plan()
     _check(lib().qmoe_forward_plan(C.byref(desc), T, top_k, C.byref(opts), C.byref(p)))
     return {"path": p.path, "num_launches": p.num_launches, "gemv_mmax": p.gemv_mmax,

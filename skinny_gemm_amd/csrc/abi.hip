@@ -251,11 +251,12 @@ struct Plan {
   int mmax, mmax1, mmax2, ks1, ks2, tn1, tn2, max_active, max_tiles;
   int route_fused;
   int fc1_routes;  // GEMV path: FC1 routes the tokens itself (no routing kernel)
+  bool softmax_all;  // a route_weights stage replaces the routing weights
   int launches;
   std::string kernels;
 };
 
-qmoe_status make_plan(const qmoe_layer_desc &d, int32_t T, int32_t k, int path_req, Plan &p) {
+qmoe_status make_plan(const qmoe_layer_desc &d, int32_t T, int32_t k, int path_req, bool softmax_all, Plan &p) {
   const MoeLayout L = MoeLayout::make(d);
   p = Plan{};
   int path = path_req;
@@ -273,8 +274,10 @@ qmoe_status make_plan(const qmoe_layer_desc &d, int32_t T, int32_t k, int path_r
                   kGroupedMaxAffineBlocks);
     p.route_fused = (T <= 16) ? 1 : 0;
     p.max_tiles = (int)grouped_max_tiles((int64_t)T * k, d.num_experts);
-    p.kernels = "route,rowscale,grouped_fc1_swiglu,grouped_fc2,combine";
-    p.launches = (p.route_fused ? 1 : 2) + 4;
+    p.softmax_all = softmax_all;
+    p.kernels = std::string("route,") + (softmax_all ? "route_weights," : "") +
+                "rowscale,grouped_fc1_swiglu,grouped_fc2,combine";
+    p.launches = (p.route_fused ? 1 : 2) + 4 + (softmax_all ? 1 : 0);
     return ok();
   }
   p.route_fused = (T <= 16) ? 1 : 0;
@@ -292,9 +295,12 @@ qmoe_status make_plan(const qmoe_layer_desc &d, int32_t T, int32_t k, int path_r
   p.ks2 = g2.waves;
   p.tn2 = g2.tn;
   // top-1: the down GEMV writes y; otherwise a combine kernel follows
-  p.kernels = std::string(p.fc1_routes ? "route_fc1_swiglu" : "route,gemv_fc1_swiglu") + ",gemv_fc2" +
-              (k == 1 ? "" : ",combine");
-  p.launches = (p.fc1_routes ? 2 : 3) + (k == 1 ? 0 : 1);
+  // the weights of SOFTMAX_ALL replace the routing's weights once the ids
+  // exist, before the first reader of the weights (FC2 or the combine)
+  p.softmax_all = softmax_all;
+  p.kernels = std::string(p.fc1_routes ? "route_fc1_swiglu" : "route,gemv_fc1_swiglu") +
+              (softmax_all ? ",route_weights" : "") + ",gemv_fc2" + (k == 1 ? "" : ",combine");
+  p.launches = (p.fc1_routes ? 2 : 3) + (k == 1 ? 0 : 1) + (softmax_all ? 1 : 0);
   return ok();
 }
 
@@ -430,7 +436,8 @@ qmoe_status qmoe_forward_plan(const qmoe_layer_desc *desc, int32_t T, int32_t to
   if (st != QMOE_OK) return st;
   if (!plan) return fail(QMOE_ERR_INVALID_ARGUMENT, "null plan output");
   Plan p;
-  st = make_plan(*desc, T, top_k, opts ? opts->path : QMOE_PATH_AUTO, p);
+  st = make_plan(*desc, T, top_k, opts ? opts->path : QMOE_PATH_AUTO,
+                 opts && opts->topk_weights == QMOE_TOPK_SOFTMAX_ALL, p);
   if (st != QMOE_OK) return st;
   memset(plan, 0, sizeof *plan);
   plan->path = p.path;
@@ -455,9 +462,14 @@ qmoe_status qmoe_forward_ex(const qmoe_layer_desc *desc, const void *packed, con
     return fail(QMOE_ERR_INVALID_ARGUMENT, "opts.reserved fields must be 0");
   if (opts && opts->num_events > 0 && !opts->events)
     return fail(QMOE_ERR_INVALID_ARGUMENT, "opts.events is null but num_events > 0");
+  if (opts && opts->reserved3 != 0) return fail(QMOE_ERR_INVALID_ARGUMENT, "opts.reserved3 must be 0");
+  if (opts && opts->topk_weights != QMOE_TOPK_RENORMALIZED && opts->topk_weights != QMOE_TOPK_SOFTMAX_ALL)
+    return fail(QMOE_ERR_INVALID_ARGUMENT, "opts.topk_weights %d is not a qmoe_topk_weights value",
+                opts->topk_weights);
   if (T == 0) return ok();
   Plan p;
-  st = make_plan(*desc, T, top_k, opts ? opts->path : QMOE_PATH_AUTO, p);
+  st = make_plan(*desc, T, top_k, opts ? opts->path : QMOE_PATH_AUTO,
+                 opts && opts->topk_weights == QMOE_TOPK_SOFTMAX_ALL, p);
   if (st != QMOE_OK) return st;
   if (!packed || !x || !logits || !y || !ws)
     return fail(QMOE_ERR_INVALID_ARGUMENT, "null device pointer");
@@ -516,8 +528,19 @@ qmoe_status qmoe_forward_ex(const qmoe_layer_desc *desc, const void *packed, con
     if (e != hipSuccess) return hip_status(e, "route");
   }
 
+  // SOFTMAX_ALL weights, once the ids exist and before FC2 or the combine reads them
+  auto route_weights = [&]() -> qmoe_status {
+    if (!p.softmax_all) return QMOE_OK;
+    hipError_t e2 = begin();
+    if (e2 == hipSuccess)
+      e2 = launch_route_weights_all(logits, T, desc->num_experts, top_k, ra.r.ids, ra.r.w, s);
+    if (e2 == hipSuccess) e2 = end();
+    return e2 == hipSuccess ? QMOE_OK : hip_status(e2, "route weights");
+  };
+
   float *o = (float *)(wsb + W.o);
   if (p.path == QMOE_PATH_GROUPED) {
+    if ((st = route_weights()) != QMOE_OK) return st;
     float *xsc = (float *)(wsb + W.xsc), *h32 = (float *)(wsb + W.h32);
     uint32_t *hmax = (uint32_t *)(wsb + W.hmax);
     uint16_t *xs16 = (uint16_t *)(wsb + W.xs16);
@@ -593,6 +616,7 @@ qmoe_status qmoe_forward_ex(const qmoe_layer_desc *desc, const void *packed, con
                     p.ks1, p.tn1, L.fc1.block, p.max_active, s);
   if (e == hipSuccess) e = end();
   if (e != hipSuccess) return hip_status(e, "gemv fc1");
+  if ((st = route_weights()) != QMOE_OK) return st;
 
   GemvArgs g2 = gemv_base(L.fc2, pk + L.fc2_off);
   g2.slot_info = ra.r.slot_info;

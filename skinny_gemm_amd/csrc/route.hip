@@ -209,6 +209,33 @@ __global__ __launch_bounds__(1024) void route_small_kernel(RouteArgs a) {
   if (wave == 0) wave_expand_lists(s_ids, a.T * a.k, a.k, a.E, a.max_slots, a.r);
 }
 
+// One wave per token: m = the token's maximum logit (that of its first
+// selected expert), the wave sum of exp(l - m) over all E logits, then lane j
+// writes exp(l[id_j] - m) / sum for j < k.
+__global__ __launch_bounds__(256) void route_weights_all_kernel(const float *__restrict__ logits, int T, int E,
+                                                                int k, const int32_t *__restrict__ ids,
+                                                                float *__restrict__ w) {
+  const int lane = threadIdx.x & (kLanes - 1);
+  const int t = blockIdx.x * (blockDim.x / kLanes) + (threadIdx.x / kLanes);
+  if (t >= T) return;  // whole waves leave together
+  const float *l = logits + (int64_t)t * E;
+  const float m = l[ids[(int64_t)t * k]];
+  float part = 0.f;
+  for (int e = lane; e < E; e += kLanes) part += expf(l[e] - m);
+#pragma unroll
+  for (int off = 1; off < kLanes; off <<= 1) part += __shfl_xor(part, off);
+  if (lane < k) w[(int64_t)t * k + lane] = expf(l[ids[(int64_t)t * k + lane]] - m) / part;
+}
+
+hipError_t launch_route_weights_all(const float *logits, int T, int E, int k, const int32_t *ids, float *w,
+                                    hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  if (k < 1 || k > kLanes || E < 1) return hipErrorInvalidValue;
+  constexpr int kWaves = 256 / kLanes;
+  const int grid = (T + kWaves - 1) / kWaves;
+  return qlaunch(route_weights_all_kernel, dim3(grid), dim3(256), 0, s, logits, T, E, k, ids, w);
+}
+
 hipError_t launch_route(const RouteArgs &a, hipStream_t s) {
   if (a.topk_in_expand && a.T > 0 && (int64_t)a.T * a.k <= kLanes && a.tile_rows == 0 && a.zero_len == 0) {
     return qlaunch(route_small_kernel, dim3(1), dim3(a.T * kLanes), 0, s, a);

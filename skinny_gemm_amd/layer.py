@@ -57,7 +57,7 @@ class MoeLayer:
                            device=self.device)
 
     def forward(self, x: torch.Tensor, logits: torch.Tensor, top_k: int, y=None, ws=None,
-                path="auto", debug=False, stream=None, events=None):
+                path="auto", debug=False, stream=None, events=None, topk_weights="renormalized"):
         T = x.shape[0]
         if y is None:
             y = torch.empty((T, self.H), dtype=TORCH_ACT[self.act_dtype], device=self.device)
@@ -72,7 +72,7 @@ class MoeLayer:
         forward_ex(self.desc, self.packed, x, logits, T, top_k, y, ws, stream=stream, path=path,
                    h_out=dbg.get("h"), ids_out=dbg.get("ids"), w_out=dbg.get("w"),
                    counts_out=dbg.get("counts"), events=events, fc1_bias=self.fc1_bias,
-                   fc2_bias=self.fc2_bias)
+                   fc2_bias=self.fc2_bias, topk_weights=topk_weights)
         return (y, dbg) if debug else y
 
     def unpack(self, which: int) -> torch.Tensor:

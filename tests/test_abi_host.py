@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_abi_version():
-    assert q.abi_version() == 2
+    assert q.abi_version() == 3
 
 
 def _desc(**kw):
@@ -105,6 +105,13 @@ def test_forward_validation_before_launch():
     assert st == 2
     # T = 0 is a no-op even with null pointers
     assert L.qmoe_forward(C.byref(d), None, None, None, 0, 6, None, None, 0, None) == 0
+    # unknown routing-weight mode, nonzero reserved field
+    for bad in (dict(topk_weights=2), dict(topk_weights=-1), dict(reserved3=1)):
+        opts = q.ForwardOpts(0, 0, None, None, None, None, None, 0, 0, None, None, 0, 0)
+        for k, v in bad.items():
+            setattr(opts, k, v)
+        st = L.qmoe_forward_ex(C.byref(d), fake, fake, fake, 4, 6, fake, fake, ws_need, None, C.byref(opts))
+        assert st == 1, bad
 
 
 def test_prepack_validation():
@@ -172,3 +179,20 @@ def test_plan_grouped_prefill():
     pg = q.forward_plan(_desc(), 4, 6, path="grouped")
     assert pg["path"] == 2 and pg["num_launches"] == 5
     assert q.workspace_size(d, 2048, 8) >= p["workspace_bytes"]
+
+
+def test_plan_softmax_all_weights_stage():
+    """The unnormalised routing weights add one stage right after the ids
+    exist and before FC2 or the combine reads the weights."""
+    d = _desc()
+    for T, k, path, want in [
+        (1, 6, "auto", ["route_fc1_swiglu", "route_weights", "gemv_fc2", "combine"]),
+        (8, 6, "auto", ["route", "gemv_fc1_swiglu", "route_weights", "gemv_fc2", "combine"]),
+        (1, 1, "auto", ["route_fc1_swiglu", "route_weights", "gemv_fc2"]),
+        (64, 6, "auto", ["route", "route_weights", "rowscale", "grouped_fc1_swiglu", "grouped_fc2", "combine"]),
+    ]:
+        base = q.forward_plan(d, T, k, path)
+        p = q.forward_plan(d, T, k, path, topk_weights="softmax_all")
+        assert p["kernels"] == want, (T, k, p["kernels"])
+        assert p["num_launches"] == base["num_launches"] + 1
+        assert [s for s in p["kernels"] if s != "route_weights"] == base["kernels"]

@@ -50,17 +50,20 @@ def _inputs(spec, T, seed, logits_mode="iid", expert_bias=0.0):
     return synth.moe_inputs(spec, T, seed, logits_mode, expert_bias=expert_bias)
 
 
-def run_case(spec, T, seed, logits_mode="iid", path="auto", tokens=None, expert_bias=0.0):
+def run_case(spec, T, seed, logits_mode="iid", path="auto", tokens=None, expert_bias=0.0,
+             topk_weights="renormalized"):
     from skinny_gemm_amd.layer import MoeLayer, to_device_bits, bits_of
-    log(f"[moe] {spec.name} T={T} seed={seed} logits={logits_mode} path={path} expert_bias={expert_bias}")
+    renorm = topk_weights == "renormalized"
+    log(f"[moe] {spec.name} T={T} seed={seed} logits={logits_mode} path={path} expert_bias={expert_bias} "
+        f"topk_weights={topk_weights}")
     inp = _inputs(spec, T, seed, logits_mode, expert_bias)
     layer = MoeLayer.from_spec(spec, inp)
     x = to_device_bits(inp["x"], spec.act_dtype)
     lg = torch.from_numpy(inp["logits"]).cuda()
-    y, dbg = layer.forward(x, lg, spec.top_k, path=path, debug=True)
+    y, dbg = layer.forward(x, lg, spec.top_k, path=path, debug=True, topk_weights=topk_weights)
     torch.cuda.synchronize()
-    ref = oracle.moe(inp, debug=True, tokens=tokens)
-    r = oracle.route(inp["logits"] if tokens is None else inp["logits"][tokens], spec.top_k)
+    ref = oracle.moe(inp, debug=True, tokens=tokens, renorm=renorm)
+    r = oracle.route(inp["logits"] if tokens is None else inp["logits"][tokens], spec.top_k, renorm)
     ybits = bits_of(y)
     if tokens is not None:
         ybits = ybits[tokens]
@@ -315,3 +318,35 @@ def test_expert_bias_mixed_prefill_sampled():
     spec = synth.MOE_WORKLOADS["mixed_int2_int4_prefill"]
     sample = [0, 17, 555, 1024, 2047]
     _bias_case(spec, 2048, 3, 0.5, tokens=sample)
+
+
+# ------------------------------------- unnormalised top-k routing weights
+@pytest.mark.parametrize("name,T,path", [
+    ("switch_base_ternary", 1, "auto"),   # top-1: FC2 writes y = p_max * o
+    ("dsv2lite_int4", 1, "auto"),         # routing inside FC1, combine
+    ("dsv2lite_int4", 8, "auto"),         # routing kernels
+    ("dsv2lite_int4", 8, "grouped"),
+    ("mixed_int2_int4_decode", 2, "auto"),  # E = 128: two logits per lane in the sum
+])
+def test_softmax_all_weights_workloads(name, T, path):
+    spec = synth.MOE_WORKLOADS["mixed_int2_int4_prefill" if name == "mixed_int2_int4_decode" else name]
+    res = run_case(spec, T, 9, path=path, topk_weights="softmax_all")
+    # the weights really differ from the renormalised ones (unless k = E)
+    ref = oracle.moe(res["inp"])
+    assert not compare(res["ybits"], ref["y"], ref["y64"], spec.act_dtype)["ok"]
+
+
+@pytest.mark.parametrize("path", ["auto", "grouped"])
+def test_softmax_all_weights_E256(path):
+    run_case(custom_moe_spec(E=256, H=128, I=64, top_k=8), 5, 12, path=path, topk_weights="softmax_all")
+
+
+def test_softmax_all_weights_k_equals_E():
+    """Nothing left out of the sum: identical to the renormalised weights."""
+    spec = custom_moe_spec(E=4, H=128, I=64, top_k=4)
+    run_case(spec, 3, 13, topk_weights="softmax_all")
+
+
+def test_softmax_all_weights_mixed_prefill_sampled():
+    spec = synth.MOE_WORKLOADS["mixed_int2_int4_prefill"]
+    run_case(spec, 2048, 5, tokens=[3, 900, 2000], topk_weights="softmax_all")
