@@ -70,7 +70,7 @@
 extern "C" {
 #endif
 
-#define QMOE_ABI_VERSION 3
+#define QMOE_ABI_VERSION 4
 
 typedef enum qmoe_status {
   QMOE_OK = 0,
@@ -156,6 +156,19 @@ typedef struct qmoe_forward_opts {
   const void *fc2_bias;
   int32_t topk_weights; /* qmoe_topk_weights: how the routing weights are formed */
   int32_t reserved3;    /* must be 0 */
+  /* Row tiling under a workspace budget (onnxruntime pull request 33005,
+     Current Scope: the prefill is row-tiled to keep its temporary scratch
+     within a budget, the tile size halved until it fits, full and final
+     partial tiles sized explicitly).  0: no limit, all T tokens in one pass.
+     Otherwise the tokens run in consecutive tiles of R rows and a final tile
+     of the rest, R = T halved (rounding up) until the workspace of a full
+     tile and of the final tile each fit in workspace_limit bytes; each tile
+     takes its own path (auto: by its row count).  ws_bytes must hold the
+     tile workspace that qmoe_forward_plan reports.  counts_out and events
+     need a single tile (QMOE_ERR_UNSUPPORTED otherwise); ids_out, w_out and
+     h_out are written as without tiling.  If one row does not fit:
+     QMOE_ERR_WORKSPACE_TOO_SMALL.  Must not be negative. */
+  int64_t workspace_limit;
 } qmoe_forward_opts;
 
 /* Host-side description of what a forward call would launch (diagnostic). */
@@ -168,7 +181,11 @@ typedef struct qmoe_plan {
   int32_t max_active;    /* upper bound of active experts the grids are sized for */
   int64_t workspace_bytes;
   char kernels[256];     /* stage names in launch order, comma separated; a stage is one
-                            kernel except "route" (one or two kernels) */
+                            kernel except "route" (one or two kernels); with row tiling,
+                            those of a full tile */
+  int32_t row_tile;      /* rows of a full tile (T without tiling) */
+  int32_t num_tiles;     /* tiles run one after another (1 without tiling); num_launches and
+                            workspace_bytes cover all of them */
 } qmoe_plan;
 
 /* ABI version (QMOE_ABI_VERSION) and a thread-local message for the last non-OK status. */

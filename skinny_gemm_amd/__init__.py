@@ -44,13 +44,14 @@ class ForwardOpts(C.Structure):
                 ("ids_out", C.c_void_p), ("w_out", C.c_void_p), ("counts_out", C.c_void_p),
                 ("events", C.POINTER(C.c_void_p)), ("num_events", C.c_int32), ("reserved2", C.c_int32),
                 ("fc1_bias", C.c_void_p), ("fc2_bias", C.c_void_p), ("topk_weights", C.c_int32),
-                ("reserved3", C.c_int32)]
+                ("reserved3", C.c_int32), ("workspace_limit", C.c_int64)]
 
 
 class Plan(C.Structure):
     _fields_ = [("path", C.c_int32), ("num_launches", C.c_int32), ("gemv_mmax", C.c_int32),
                 ("gemv_fc1_waves", C.c_int32), ("gemv_fc2_waves", C.c_int32),
-                ("max_active", C.c_int32), ("workspace_bytes", C.c_int64), ("kernels", C.c_char * 256)]
+                ("max_active", C.c_int32), ("workspace_bytes", C.c_int64), ("kernels", C.c_char * 256),
+                ("row_tile", C.c_int32), ("num_tiles", C.c_int32)]
 
 
 _lib = None
@@ -165,31 +166,35 @@ def forward(desc, packed, x, logits, T, top_k, y, ws, stream=None):
 
 def forward_ex(desc, packed, x, logits, T, top_k, y, ws, stream=None, path="auto", h_out=None,
                ids_out=None, w_out=None, counts_out=None, events=None, fc1_bias=None, fc2_bias=None,
-               topk_weights="renormalized"):
+               topk_weights="renormalized", workspace_limit=0):
     """``events``: optional list of raw hipEvent_t handles (ints), two per plan stage.
     ``fc1_bias`` [E][2I] / ``fc2_bias`` [E][H]: optional per-expert output biases
     in the activation dtype.  ``topk_weights``: "renormalized" (softmax over
     the selected logits) or "softmax_all" (selected entries of the softmax
-    over all experts)."""
+    over all experts).  ``workspace_limit`` > 0 runs the tokens in row tiles
+    whose workspace fits the limit (``forward_plan`` gives the tile sizes)."""
     ev = None
     if events:
         ev = (C.c_void_p * len(events))(*[C.c_void_p(int(e)) for e in events])
     opts = ForwardOpts(PATH[path], 0, _ptr(h_out), _ptr(ids_out), _ptr(w_out), _ptr(counts_out),
                        ev, len(events) if events else 0, 0, _ptr(fc1_bias), _ptr(fc2_bias),
-                       TOPK_WEIGHTS[topk_weights], 0)
+                       TOPK_WEIGHTS[topk_weights], 0, int(workspace_limit))
     _check(lib().qmoe_forward_ex(C.byref(desc), _ptr(packed), _ptr(x), _ptr(logits), T, top_k,
                                  _ptr(y), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream),
                                  C.byref(opts)))
 
 
-def forward_plan(desc, T: int, top_k: int, path: str = "auto", topk_weights: str = "renormalized") -> dict:
-    opts = ForwardOpts(PATH[path], 0, None, None, None, None, None, 0, 0, None, None, TOPK_WEIGHTS[topk_weights], 0)
+def forward_plan(desc, T: int, top_k: int, path: str = "auto", topk_weights: str = "renormalized",
+                 workspace_limit: int = 0) -> dict:
+    opts = ForwardOpts(PATH[path], 0, None, None, None, None, None, 0, 0, None, None, TOPK_WEIGHTS[topk_weights], 0,
+                       int(workspace_limit))
     p = Plan()
     _check(lib().qmoe_forward_plan(C.byref(desc), T, top_k, C.byref(opts), C.byref(p)))
     return {"path": p.path, "num_launches": p.num_launches, "gemv_mmax": p.gemv_mmax,
             "gemv_fc1_waves": p.gemv_fc1_waves, "gemv_fc2_waves": p.gemv_fc2_waves,
             "max_active": p.max_active, "workspace_bytes": p.workspace_bytes,
-            "kernels": p.kernels.decode().split(",") if p.kernels else []}
+            "kernels": p.kernels.decode().split(",") if p.kernels else [],
+            "row_tile": p.row_tile, "num_tiles": p.num_tiles}
 
 
 def route_workspace_size(T: int, E: int, top_k: int) -> int:

@@ -428,6 +428,45 @@ qmoe_status qmoe_workspace_size(const qmoe_layer_desc *desc, int32_t T, int32_t 
   return ok();
 }
 
+// Row tiling under a workspace limit: R = T halved (rounding up) until the
+// workspaces of a full tile and of the final partial tile, each on its own
+// path, fit within the limit.
+struct Tiling {
+  int32_t rows = 0, tiles = 0;
+  int64_t ws = 0;       // the largest tile workspace
+  int launches = 0;     // kernels over all tiles
+};
+
+qmoe_status tile_need(const qmoe_layer_desc &d, int32_t T, int32_t k, int path_req, bool softmax_all,
+                      int32_t R, Tiling &t) {
+  t = Tiling{};
+  t.rows = R;
+  t.tiles = (int32_t)(((int64_t)T + R - 1) / R);
+  const int32_t last = T - (t.tiles - 1) * R;  // in [1, R]
+  Plan pf, pl;
+  qmoe_status st = make_plan(d, R, k, path_req, softmax_all, pf);
+  if (st == QMOE_OK) st = make_plan(d, last, k, path_req, softmax_all, pl);
+  if (st != QMOE_OK) return st;
+  t.ws = std::max(MoeWs::make(d, R, k, pf.path == QMOE_PATH_GROUPED).total,
+                  MoeWs::make(d, last, k, pl.path == QMOE_PATH_GROUPED).total);
+  t.launches = (t.tiles - 1) * pf.launches + pl.launches;
+  return QMOE_OK;
+}
+
+qmoe_status pick_tiling(const qmoe_layer_desc &d, int32_t T, int32_t k, int path_req, bool softmax_all,
+                        int64_t limit, Tiling &t) {
+  int32_t R = T;
+  for (;;) {
+    qmoe_status st = tile_need(d, T, k, path_req, softmax_all, R, t);
+    if (st != QMOE_OK) return st;
+    if (limit <= 0 || t.ws <= limit) return QMOE_OK;
+    if (R == 1)
+      return fail(QMOE_ERR_WORKSPACE_TOO_SMALL, "one row needs %lld workspace bytes, the limit is %lld",
+                  (long long)t.ws, (long long)limit);
+    R = (R + 1) / 2;
+  }
+}
+
 qmoe_status qmoe_forward_plan(const qmoe_layer_desc *desc, int32_t T, int32_t top_k,
                               const qmoe_forward_opts *opts, qmoe_plan *plan) {
   qmoe_status st = check_layer(desc);
@@ -435,9 +474,9 @@ qmoe_status qmoe_forward_plan(const qmoe_layer_desc *desc, int32_t T, int32_t to
   st = check_tokens(desc, T, top_k);
   if (st != QMOE_OK) return st;
   if (!plan) return fail(QMOE_ERR_INVALID_ARGUMENT, "null plan output");
+  const bool softmax_all = opts && opts->topk_weights == QMOE_TOPK_SOFTMAX_ALL;
   Plan p;
-  st = make_plan(*desc, T, top_k, opts ? opts->path : QMOE_PATH_AUTO,
-                 opts && opts->topk_weights == QMOE_TOPK_SOFTMAX_ALL, p);
+  st = make_plan(*desc, T, top_k, opts ? opts->path : QMOE_PATH_AUTO, softmax_all, p);
   if (st != QMOE_OK) return st;
   memset(plan, 0, sizeof *plan);
   plan->path = p.path;
@@ -448,6 +487,26 @@ qmoe_status qmoe_forward_plan(const qmoe_layer_desc *desc, int32_t T, int32_t to
   plan->max_active = p.max_active;
   plan->workspace_bytes = MoeWs::make(*desc, T, top_k, p.path == QMOE_PATH_GROUPED).total;
   snprintf(plan->kernels, sizeof plan->kernels, "%s", T == 0 ? "" : p.kernels.c_str());
+  plan->row_tile = T;
+  plan->num_tiles = T == 0 ? 0 : 1;
+  if (T > 0 && opts && opts->workspace_limit != 0) {
+    if (opts->workspace_limit < 0) return fail(QMOE_ERR_INVALID_ARGUMENT, "negative workspace_limit");
+    Tiling tl;
+    st = pick_tiling(*desc, T, top_k, opts->path, softmax_all, opts->workspace_limit, tl);
+    if (st != QMOE_OK) return st;
+    st = make_plan(*desc, tl.rows, top_k, opts->path, softmax_all, p);
+    if (st != QMOE_OK) return st;
+    plan->path = p.path;
+    plan->num_launches = tl.launches;
+    plan->gemv_mmax = p.mmax;
+    plan->gemv_fc1_waves = p.ks1;
+    plan->gemv_fc2_waves = p.ks2;
+    plan->max_active = p.max_active;
+    plan->workspace_bytes = tl.ws;
+    snprintf(plan->kernels, sizeof plan->kernels, "%s", p.kernels.c_str());
+    plan->row_tile = tl.rows;
+    plan->num_tiles = tl.tiles;
+  }
   return ok();
 }
 
@@ -466,10 +525,45 @@ qmoe_status qmoe_forward_ex(const qmoe_layer_desc *desc, const void *packed, con
   if (opts && opts->topk_weights != QMOE_TOPK_RENORMALIZED && opts->topk_weights != QMOE_TOPK_SOFTMAX_ALL)
     return fail(QMOE_ERR_INVALID_ARGUMENT, "opts.topk_weights %d is not a qmoe_topk_weights value",
                 opts->topk_weights);
+  if (opts && opts->workspace_limit < 0) return fail(QMOE_ERR_INVALID_ARGUMENT, "negative workspace_limit");
   if (T == 0) return ok();
+  const bool softmax_all = opts && opts->topk_weights == QMOE_TOPK_SOFTMAX_ALL;
+  if (opts && opts->workspace_limit > 0) {
+    Tiling tl;
+    st = pick_tiling(*desc, T, top_k, opts->path, softmax_all, opts->workspace_limit, tl);
+    if (st != QMOE_OK) return st;
+    if (tl.tiles > 1) {
+      // everything a tile could reject is checked here, before the first launch
+      if (opts->counts_out || opts->num_events > 0)
+        return fail(QMOE_ERR_UNSUPPORTED, "counts_out and events need a single tile (%d tiles)", tl.tiles);
+      if (!packed || !x || !logits || !y || !ws) return fail(QMOE_ERR_INVALID_ARGUMENT, "null device pointer");
+      if (!aligned(packed, kAlign) || !aligned(ws, kAlign))
+        return fail(QMOE_ERR_INVALID_ARGUMENT, "packed and ws must be 256-byte aligned");
+      if (!aligned(x, 16) || !aligned(y, 16) || !aligned(logits, 4))
+        return fail(QMOE_ERR_INVALID_ARGUMENT, "x and y must be 16-byte aligned, logits 4-byte aligned");
+      if (ws_bytes < (size_t)tl.ws)
+        return fail(QMOE_ERR_WORKSPACE_TOO_SMALL, "workspace holds %zu bytes, %lld needed per tile", ws_bytes,
+                    (long long)tl.ws);
+      // tiles in order on the stream, sharing the workspace; a tile's rows
+      // start at row t0 of x, logits, y and the per-slot diagnostics
+      qmoe_forward_opts o = *opts;
+      o.workspace_limit = 0;
+      const int64_t H = desc->hidden, E = desc->num_experts, I = desc->inter;
+      for (int32_t t0 = 0; t0 < T; t0 += tl.rows) {
+        const int32_t n = std::min(tl.rows, T - t0);
+        const int64_t s0 = (int64_t)t0 * top_k;
+        o.h_out = opts->h_out ? opts->h_out + s0 * I : nullptr;
+        o.ids_out = opts->ids_out ? opts->ids_out + s0 : nullptr;
+        o.w_out = opts->w_out ? opts->w_out + s0 : nullptr;
+        st = qmoe_forward_ex(desc, packed, (const uint16_t *)x + (int64_t)t0 * H, logits + (int64_t)t0 * E, n,
+                             top_k, (uint16_t *)y + (int64_t)t0 * H, ws, ws_bytes, stream, &o);
+        if (st != QMOE_OK) return st;
+      }
+      return ok();
+    }
+  }
   Plan p;
-  st = make_plan(*desc, T, top_k, opts ? opts->path : QMOE_PATH_AUTO,
-                 opts && opts->topk_weights == QMOE_TOPK_SOFTMAX_ALL, p);
+  st = make_plan(*desc, T, top_k, opts ? opts->path : QMOE_PATH_AUTO, softmax_all, p);
   if (st != QMOE_OK) return st;
   if (!packed || !x || !logits || !y || !ws)
     return fail(QMOE_ERR_INVALID_ARGUMENT, "null device pointer");

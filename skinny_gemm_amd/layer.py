@@ -8,7 +8,7 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import (layer_desc, qmatrix_desc, prepacked_size, prepack, workspace_size, forward_ex,
+from . import (layer_desc, qmatrix_desc, prepacked_size, prepack, workspace_size, forward_ex, forward_plan,
                linear_prepacked_size, linear_prepack, linear, linear_workspace_size, unpack_codes,
                linear_unpack_codes)
 
@@ -57,22 +57,26 @@ class MoeLayer:
                            device=self.device)
 
     def forward(self, x: torch.Tensor, logits: torch.Tensor, top_k: int, y=None, ws=None,
-                path="auto", debug=False, stream=None, events=None, topk_weights="renormalized"):
+                path="auto", debug=False, stream=None, events=None, topk_weights="renormalized",
+                workspace_limit=0):
         T = x.shape[0]
         if y is None:
             y = torch.empty((T, self.H), dtype=TORCH_ACT[self.act_dtype], device=self.device)
         if ws is None:
-            ws = self.workspace(T, top_k)
+            ws = self.workspace(T, top_k) if not workspace_limit else torch.empty(
+                max(forward_plan(self.desc, T, top_k, path, topk_weights, workspace_limit)["workspace_bytes"], 256),
+                dtype=torch.uint8, device=self.device)
         dbg = {}
         if debug:
             dbg["h"] = torch.full((T * top_k, self.I), float("nan"), dtype=torch.float32, device=self.device)
             dbg["ids"] = torch.full((T, top_k), -1, dtype=torch.int32, device=self.device)
             dbg["w"] = torch.full((T, top_k), float("nan"), dtype=torch.float32, device=self.device)
-            dbg["counts"] = torch.full((self.E,), -1, dtype=torch.int32, device=self.device)
+            if not workspace_limit:  # per-expert counts need a single tile
+                dbg["counts"] = torch.full((self.E,), -1, dtype=torch.int32, device=self.device)
         forward_ex(self.desc, self.packed, x, logits, T, top_k, y, ws, stream=stream, path=path,
                    h_out=dbg.get("h"), ids_out=dbg.get("ids"), w_out=dbg.get("w"),
                    counts_out=dbg.get("counts"), events=events, fc1_bias=self.fc1_bias,
-                   fc2_bias=self.fc2_bias, topk_weights=topk_weights)
+                   fc2_bias=self.fc2_bias, topk_weights=topk_weights, workspace_limit=workspace_limit)
         return (y, dbg) if debug else y
 
     def unpack(self, which: int) -> torch.Tensor:

@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_abi_version():
-    assert q.abi_version() == 3
+    assert q.abi_version() == 4
 
 
 def _desc(**kw):
@@ -196,3 +196,59 @@ def test_plan_softmax_all_weights_stage():
         assert p["kernels"] == want, (T, k, p["kernels"])
         assert p["num_launches"] == base["num_launches"] + 1
         assert [s for s in p["kernels"] if s != "route_weights"] == base["kernels"]
+
+
+def _mixed_desc():
+    return _desc(E=128, H=4096, I=1536, fc1=("sym_int2", 64, "bf16"), fc2=("sym_int4", 64, "bf16"))
+
+
+@pytest.mark.parametrize("T,div", [(8193, 3), (8193, 40), (2048, 5), (37, 2)])
+def test_plan_row_tiling_halves_until_the_tile_fits(T, div):
+    d = _mixed_desc()
+    full = q.forward_plan(d, T, 8)
+    limit = full["workspace_bytes"] // div
+    p = q.forward_plan(d, T, 8, workspace_limit=limit)
+    R = T
+    while True:                                      # the halving sequence, rounding up
+        tiles = -(-T // R)
+        last = T - (tiles - 1) * R
+        need = max(q.forward_plan(d, n, 8)["workspace_bytes"] for n in {R, last})
+        if need <= limit:
+            break
+        R = (R + 1) // 2
+    assert (p["row_tile"], p["num_tiles"], p["workspace_bytes"]) == (R, tiles, need)
+    assert p["workspace_bytes"] <= limit < full["workspace_bytes"]
+    per = {n: q.forward_plan(d, n, 8)["num_launches"] for n in {R, last}}
+    assert p["num_launches"] == (tiles - 1) * per[R] + per[last]
+
+
+def test_plan_row_tiling_edges():
+    d = _mixed_desc()
+    big = q.forward_plan(d, 100, 8)
+    p = q.forward_plan(d, 100, 8, workspace_limit=big["workspace_bytes"])       # fits: one tile
+    assert (p["row_tile"], p["num_tiles"]) == (100, 1) and p["workspace_bytes"] == big["workspace_bytes"]
+    with pytest.raises(q.QmoeError) as ei:                                       # not even one row
+        q.forward_plan(d, 100, 8, workspace_limit=1)
+    assert ei.value.status == 3
+    with pytest.raises(q.QmoeError) as ei:
+        q.forward_plan(d, 100, 8, workspace_limit=-1)
+    assert ei.value.status == 1
+
+
+def test_forward_row_tiling_validation_before_launch():
+    d = _mixed_desc()
+    L = q.lib()
+    fake = C.c_void_p(0x100000)  # never dereferenced: every case fails validation first
+    limit = q.forward_plan(d, 4096, 8)["workspace_bytes"] // 3
+    tile_ws = q.forward_plan(d, 4096, 8, workspace_limit=limit)["workspace_bytes"]
+
+    def call(ws_bytes, **kw):
+        o = q.ForwardOpts(0, 0, None, None, None, None, None, 0, 0, None, None, 0, 0, limit)
+        for k, v in kw.items():
+            setattr(o, k, v)
+        return L.qmoe_forward_ex(C.byref(d), fake, fake, fake, 4096, 8, fake, fake, ws_bytes, None, C.byref(o))
+    assert call(tile_ws, counts_out=0x100000) == 2                               # counts need one tile
+    assert call(tile_ws, num_events=2, events=C.cast(fake, C.POINTER(C.c_void_p))) == 2
+    assert call(tile_ws - 1) == 3                                                # workspace of a tile
+    o = q.ForwardOpts(0, 0, None, None, None, None, None, 0, 0, None, None, 0, 0, limit)
+    assert L.qmoe_forward_ex(C.byref(d), None, fake, fake, 4096, 8, fake, fake, tile_ws, None, C.byref(o)) == 1

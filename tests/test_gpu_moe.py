@@ -350,3 +350,71 @@ def test_softmax_all_weights_k_equals_E():
 def test_softmax_all_weights_mixed_prefill_sampled():
     spec = synth.MOE_WORKLOADS["mixed_int2_int4_prefill"]
     run_case(spec, 2048, 5, tokens=[3, 900, 2000], topk_weights="softmax_all")
+
+
+# ------------------------------------------------ row tiling under a budget
+def _tiled_run(spec, inp, T, limit, path="auto"):
+    from skinny_gemm_amd.layer import MoeLayer, to_device_bits, bits_of
+    layer = MoeLayer.from_spec(spec, inp)
+    x = to_device_bits(inp["x"], spec.act_dtype)
+    lg = torch.from_numpy(inp["logits"]).cuda()
+    y, dbg = layer.forward(x, lg, spec.top_k, path=path, debug=True, workspace_limit=limit)
+    torch.cuda.synchronize()
+    return layer, x, lg, bits_of(y), dbg
+
+
+def test_row_tiling_8193_tokens_bit_identical():
+    """8193 prefill tokens in four tiles (3 x 2049 + 2046 rows) under a third
+    of the untiled workspace: every output bit equals the untiled run (a
+    token's output depends on its own row only), and sampled rows at the
+    tile edges match the oracle."""
+    import skinny_gemm_amd as q
+    from skinny_gemm_amd.layer import bits_of
+    spec = synth.MOE_WORKLOADS["mixed_int2_int4_prefill"]
+    T = 8193
+    inp = _inputs(spec, T, 0)
+    layer, x, lg, ytile, dbg = _tiled_run(spec, inp, T, 0)  # build the layer; untiled first
+    full = q.forward_plan(layer.desc, T, spec.top_k)
+    limit = full["workspace_bytes"] // 3
+    plan = q.forward_plan(layer.desc, T, spec.top_k, workspace_limit=limit)
+    log(f"[tiling] T={T} limit={limit} row_tile={plan['row_tile']} tiles={plan['num_tiles']}")
+    assert plan["num_tiles"] > 1 and plan["workspace_bytes"] <= limit
+    y0 = ytile
+    y1, dbg1 = layer.forward(x, lg, spec.top_k, debug=True, workspace_limit=limit)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits_of(y1), y0), "tiled output differs from the untiled run"
+    r = oracle.route(inp["logits"], spec.top_k)
+    assert np.array_equal(dbg1["ids"].cpu().numpy(), r["ids"])
+    assert np.allclose(dbg1["w"].cpu().numpy(), r["w"], rtol=2e-6, atol=1e-7)
+    R = plan["row_tile"]
+    sample = [0, R - 1, R, 2 * R, T - 1]
+    ref = oracle.moe(inp, tokens=sample)
+    res = compare(y0[sample], ref["y"], ref["y64"], spec.act_dtype)
+    log(f"       sampled rows: max_row_rel={res['max_row_rel']:.3e}")
+    assert res["ok"], res
+
+
+@pytest.mark.parametrize("div", [2, 6])
+def test_row_tiling_small_tiles(div):
+    """37 tokens in tiles of 10 (routing kernels) or 5 (routing inside FC1)
+    rows on the GEMV path, against the oracle on every token."""
+    import skinny_gemm_amd as q
+    spec = custom_moe_spec(E=8, H=256, I=128, top_k=2, fc1="sym_int2", fc2="sym_int4")
+    T = 37
+    inp = synth.moe_inputs(spec, T, 50 + div, expert_bias=0.1)
+    from skinny_gemm_amd.layer import MoeLayer
+    d = MoeLayer.from_spec(spec, inp).desc
+    limit = q.forward_plan(d, T, 2)["workspace_bytes"] // div
+    plan = q.forward_plan(d, T, 2, workspace_limit=limit)
+    log(f"[tiling] T={T} limit={limit} row_tile={plan['row_tile']} tiles={plan['num_tiles']} {plan['kernels']}")
+    assert plan["num_tiles"] > 1 and plan["path"] == 1
+    _, _, _, y, dbg = _tiled_run(spec, inp, T, limit)
+    ref = oracle.moe(inp, debug=True)
+    r = oracle.route(inp["logits"], 2)
+    assert np.array_equal(dbg["ids"].cpu().numpy(), r["ids"])
+    h = dbg["h"].cpu().numpy()
+    hn = np.linalg.norm(h - ref["h"], axis=1) / np.linalg.norm(ref["h"], axis=1)
+    assert hn.max() < 4e-3
+    res = compare(y, ref["y"], ref["y64"], spec.act_dtype)
+    log(f"       y: max_row_rel={res['max_row_rel']:.3e}")
+    assert res["ok"], res
