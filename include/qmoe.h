@@ -70,7 +70,7 @@
 extern "C" {
 #endif
 
-#define QMOE_ABI_VERSION 4
+#define QMOE_ABI_VERSION 5
 
 typedef enum qmoe_status {
   QMOE_OK = 0,
@@ -209,6 +209,19 @@ qmoe_status qmoe_prepack(const qmoe_layer_desc *desc,
                          const void *fc1_codes, const void *fc1_scales, const void *fc1_biases,
                          const void *fc2_codes, const void *fc2_scales, const void *fc2_biases,
                          void *dst, size_t dst_bytes, void *stream);
+
+/* Runtime scales (onnxruntime pull request 33005, Description: the packed
+ * weights and transposed scales are reused, runtime scale inputs included).
+ * Rewrites only the scale (and affine bias) sections of a buffer made by
+ * qmoe_prepack for the same desc, from canonical scales and biases in the
+ * layout above (device pointers; biases required for affine formats and NULL
+ * otherwise); the codes are left as they are.  Stream-ordered, no
+ * synchronisation: forward calls enqueued after it on `stream` use the new
+ * scales, and calls on other streams must be ordered by the caller.  The
+ * sources may be freed once the stream has passed this call. */
+qmoe_status qmoe_prepack_scales(const qmoe_layer_desc *desc, const void *fc1_scales, const void *fc1_biases,
+                                const void *fc2_scales, const void *fc2_biases, void *packed,
+                                size_t packed_bytes, void *stream);
 
 /* Worst-case workspace bytes of one forward call with T tokens and top_k
  * (host call).  top_k in [1, min(E, 16)], T >= 0, T*top_k <= INT32_MAX. */

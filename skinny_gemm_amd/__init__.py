@@ -63,6 +63,7 @@ _SIGS = {
     "qmoe_last_error": (C.c_char_p, []),
     "qmoe_prepacked_size": (C.c_int, [C.POINTER(LayerDesc), C.POINTER(_SZ)]),
     "qmoe_prepack": (C.c_int, [C.POINTER(LayerDesc)] + [_P] * 7 + [_SZ, _P]),
+    "qmoe_prepack_scales": (C.c_int, [C.POINTER(LayerDesc)] + [_P] * 5 + [_SZ, _P]),
     "qmoe_workspace_size": (C.c_int, [C.POINTER(LayerDesc), _I32, _I32, C.POINTER(_SZ)]),
     "qmoe_forward": (C.c_int, [C.POINTER(LayerDesc), _P, _P, _P, _I32, _I32, _P, _P, _SZ, _P]),
     "qmoe_forward_ex": (C.c_int, [C.POINTER(LayerDesc), _P, _P, _P, _I32, _I32, _P, _P, _SZ, _P,
@@ -151,6 +152,13 @@ def prepack(desc, fc1_codes, fc1_scales, fc1_biases, fc2_codes, fc2_scales, fc2_
     _check(lib().qmoe_prepack(C.byref(desc), _ptr(fc1_codes), _ptr(fc1_scales), _ptr(fc1_biases),
                               _ptr(fc2_codes), _ptr(fc2_scales), _ptr(fc2_biases), _ptr(dst),
                               dst.numel() * dst.element_size(), _stream(stream)))
+
+
+def prepack_scales(desc, fc1_scales, fc1_biases, fc2_scales, fc2_biases, packed, stream=None):
+    """New scales (and affine biases) for an existing prepacked buffer; codes unchanged."""
+    _check(lib().qmoe_prepack_scales(C.byref(desc), _ptr(fc1_scales), _ptr(fc1_biases), _ptr(fc2_scales),
+                                     _ptr(fc2_biases), _ptr(packed), packed.numel() * packed.element_size(),
+                                     _stream(stream)))
 
 
 def workspace_size(desc, T: int, top_k: int) -> int:

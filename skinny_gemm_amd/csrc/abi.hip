@@ -418,6 +418,35 @@ qmoe_status qmoe_prepack(const qmoe_layer_desc *desc, const void *fc1_codes, con
   return ok();
 }
 
+qmoe_status qmoe_prepack_scales(const qmoe_layer_desc *desc, const void *fc1_scales, const void *fc1_biases,
+                                const void *fc2_scales, const void *fc2_biases, void *packed, size_t packed_bytes,
+                                void *stream) {
+  qmoe_status st = check_layer(desc);
+  if (st != QMOE_OK) return st;
+  const MoeLayout L = MoeLayout::make(*desc);
+  if (!fc1_scales || !fc2_scales || !packed) return fail(QMOE_ERR_INVALID_ARGUMENT, "null scale or packed pointer");
+  if (L.fc1.affine != (fc1_biases != nullptr) || L.fc2.affine != (fc2_biases != nullptr))
+    return fail(QMOE_ERR_INVALID_ARGUMENT, "biases are required for affine formats and only for them");
+  if (!aligned(packed, kAlign)) return fail(QMOE_ERR_INVALID_ARGUMENT, "packed must be 256-byte aligned");
+  if (!aligned(fc1_scales, 2) || !aligned(fc2_scales, 2) || (fc1_biases && !aligned(fc1_biases, 2)) ||
+      (fc2_biases && !aligned(fc2_biases, 2)))
+    return fail(QMOE_ERR_INVALID_ARGUMENT, "scale/bias arrays must be 2-byte aligned");
+  if (packed_bytes < (size_t)L.total)
+    return fail(QMOE_ERR_WORKSPACE_TOO_SMALL, "packed holds %zu bytes, %lld needed", packed_bytes,
+                (long long)L.total);
+  hipStream_t s = (hipStream_t)stream;
+  uint8_t *d = (uint8_t *)packed;
+  hipError_t e = launch_prepack_scales(L.fc1, desc->num_experts, (const uint16_t *)fc1_scales,
+                                       (const uint16_t *)fc1_biases, d + L.fc1_off, s);
+  if (e == hipSuccess)
+    e = launch_prepack_scales(L.fc2, desc->num_experts, (const uint16_t *)fc2_scales, (const uint16_t *)fc2_biases,
+                              d + L.fc2_off, s);
+  if (e == hipSuccess) e = launch_wscale(L.fc1, desc->num_experts, d + L.fc1_off, (float *)(d + L.wsc_off), s);
+  if (e == hipSuccess)
+    e = launch_wscale(L.fc2, desc->num_experts, d + L.fc2_off, (float *)(d + L.wsc_off) + desc->num_experts, s);
+  return e == hipSuccess ? ok() : hip_status(e, "prepack scales");
+}
+
 qmoe_status qmoe_workspace_size(const qmoe_layer_desc *desc, int32_t T, int32_t top_k, size_t *bytes) {
   qmoe_status st = check_layer(desc);
   if (st != QMOE_OK) return st;

@@ -126,6 +126,14 @@ hipError_t launch_prepack_matrix(const MatLayout &L, int E, const uint8_t *codes
   return hipGetLastError();
 }
 
+hipError_t launch_prepack_scales(const MatLayout &L, int E, const uint16_t *scales, const uint16_t *biases,
+                                 uint8_t *dst, hipStream_t s) {
+  const int64_t ts = (int64_t)E * L.RG * L.NKT * kLanes * L.bpk;
+  hipLaunchKernelGGL(prepack_scales_kernel, dim3(nblocks(ts, 256)), dim3(256), 0, s, L, ts, scales,
+                     biases, dst);
+  return hipGetLastError();
+}
+
 hipError_t launch_unpack_matrix(const MatLayout &L, int E, const uint8_t *src, int8_t *codes_out,
                                 hipStream_t s) {
   const int64_t tc = (int64_t)E * L.N * L.NC;

@@ -243,6 +243,9 @@ constexpr size_t kGemvLdsLimit = 64 * 1024;
 hipError_t launch_prepack_matrix(const MatLayout &L, int E, const uint8_t *codes,
                                  const uint16_t *scales, const uint16_t *biases, uint8_t *dst,
                                  uint32_t *err_word, hipStream_t s);
+// The scale (and bias) section alone, codes untouched.
+hipError_t launch_prepack_scales(const MatLayout &L, int E, const uint16_t *scales, const uint16_t *biases,
+                                 uint8_t *dst, hipStream_t s);
 hipError_t launch_unpack_matrix(const MatLayout &L, int E, const uint8_t *src, int8_t *codes_out,
                                 hipStream_t s);
 hipError_t launch_route(const RouteArgs &a, hipStream_t s);

@@ -8,7 +8,8 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import (layer_desc, qmatrix_desc, prepacked_size, prepack, workspace_size, forward_ex, forward_plan,
+from . import (layer_desc, qmatrix_desc, prepacked_size, prepack, prepack_scales, workspace_size, forward_ex,
+               forward_plan,
                linear_prepacked_size, linear_prepack, linear, linear_workspace_size, unpack_codes,
                linear_unpack_codes)
 
@@ -51,6 +52,15 @@ class MoeLayer:
         return cls(spec.E, spec.H, spec.I, spec.act_dtype,
                    (spec.fc1.fmt, spec.fc1.block, spec.fc1.scale_dtype),
                    (spec.fc2.fmt, spec.fc2.block, spec.fc2.scale_dtype), arrays, device)
+
+    def update_scales(self, arrays: dict, stream=None):
+        """Runtime scales: new fc1/fc2 scales (and affine biases), codes kept."""
+        dev = {k: to_device_bits(arrays[k], None, self.device) for k in
+               ("fc1_scales", "fc1_biases", "fc2_scales", "fc2_biases")}
+        prepack_scales(self.desc, dev["fc1_scales"], dev["fc1_biases"], dev["fc2_scales"], dev["fc2_biases"],
+                       self.packed, stream=stream)
+        torch.cuda.synchronize()  # the device copies of the sources are freed on return
+        del dev
 
     def workspace(self, T: int, top_k: int) -> torch.Tensor:
         return torch.empty(max(workspace_size(self.desc, T, top_k), 256), dtype=torch.uint8,

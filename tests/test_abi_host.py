@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_abi_version():
-    assert q.abi_version() == 4
+    assert q.abi_version() == 5
 
 
 def _desc(**kw):
@@ -252,3 +252,16 @@ def test_forward_row_tiling_validation_before_launch():
     assert call(tile_ws - 1) == 3                                                # workspace of a tile
     o = q.ForwardOpts(0, 0, None, None, None, None, None, 0, 0, None, None, 0, 0, limit)
     assert L.qmoe_forward_ex(C.byref(d), None, fake, fake, 4096, 8, fake, fake, tile_ws, None, C.byref(o)) == 1
+
+
+def test_prepack_scales_validation():
+    L = q.lib()
+    fake = C.c_void_p(0x100000)
+    d = _desc()
+    need = q.prepacked_size(d)
+    assert L.qmoe_prepack_scales(C.byref(d), None, None, fake, None, fake, need, None) == 1       # null scales
+    assert L.qmoe_prepack_scales(C.byref(d), fake, fake, fake, None, fake, need, None) == 1       # bias, symmetric
+    assert L.qmoe_prepack_scales(C.byref(d), fake, None, fake, None, C.c_void_p(0x100010), need, None) == 1
+    assert L.qmoe_prepack_scales(C.byref(d), fake, None, fake, None, fake, need - 1, None) == 3
+    da = _desc(fc1=("affine_int2", 128, "f16"))
+    assert L.qmoe_prepack_scales(C.byref(da), fake, None, fake, None, fake, q.prepacked_size(da), None) == 1
