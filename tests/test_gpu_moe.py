@@ -454,3 +454,45 @@ def test_runtime_scales(spec, T, path):
     res = compare(y_new, ref["y"], ref["y64"], spec.act_dtype)
     log(f"       y: max_row_rel={res['max_row_rel']:.3e}")
     assert res["ok"], res
+
+
+# ------------------------------------------------------- HIP graph replays
+@pytest.mark.parametrize("name,T,path", [
+    ("switch_base_ternary", 1, "auto"),     # routing inside FC1, top-1
+    ("dsv2lite_int4", 8, "auto"),           # routing kernels, combine
+    ("dsv2lite_int4", 64, "grouped"),       # row scale, grouped MFMA tiles
+])
+def test_graph_replays_match_eager(name, T, path):
+    """One forward captured in a HIP graph and replayed three times over new
+    inputs copied into its static buffers, with eager work between the
+    replays: every replay equals an eager call on the same inputs, bit for bit."""
+    from skinny_gemm_amd.layer import MoeLayer, to_device_bits, bits_of
+    spec = synth.MOE_WORKLOADS[name]
+    log(f"[graph] {name} T={T} path={path}")
+    inp = _inputs(spec, T, 0)
+    layer = MoeLayer.from_spec(spec, inp)
+    x = to_device_bits(inp["x"], spec.act_dtype).clone()
+    lg = torch.from_numpy(inp["logits"]).cuda()
+    y = torch.empty((T, spec.H), dtype=x.dtype, device="cuda")
+    ws = layer.workspace(T, spec.top_k)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):                       # warm-up off the capture
+        layer.forward(x, lg, spec.top_k, y=y, ws=ws, path=path)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        layer.forward(x, lg, spec.top_k, y=y, ws=ws, path=path)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        nxt = synth.moe_inputs(spec, T, 100 + rep, weights=False)
+        x.copy_(to_device_bits(nxt["x"], spec.act_dtype))
+        lg.copy_(torch.from_numpy(nxt["logits"]).cuda())
+        g.replay()
+        torch.cuda.synchronize()
+        got = bits_of(y)
+        ref = bits_of(layer.forward(x.clone(), lg.clone(), spec.top_k, path=path))   # eager, own buffers
+        torch.cuda.synchronize()
+        assert np.array_equal(got, ref), f"replay {rep} differs from eager"
+    log("       3 replays equal to eager")
