@@ -171,9 +171,11 @@ class MoeBench:
         self.lg = torch.from_numpy(np.ascontiguousarray(lg)).cuda().view(n, T, spec.E)
         self.y = torch.empty((T, spec.H), dtype=self.x.dtype, device="cuda")
         self.ws = self.layers[0].workspace(T, spec.top_k)
+        self.kw = {}  # forward options of every step (the variants)
 
     def step(self, s, **kw):
-        self.layers[s % self.L].forward(self.x[s], self.lg[s], self.spec.top_k, y=self.y, ws=self.ws, **kw)
+        self.layers[s % self.L].forward(self.x[s], self.lg[s], self.spec.top_k, y=self.y, ws=self.ws,
+                                        **self.kw, **kw)
 
     def run(self):
         for s in range(self.W, self.W + self.K):
@@ -297,6 +299,75 @@ def bench_linear(spec, N, Ms, K_steps, trials, rotate_bytes, seed=0):
 
 
 # ----------------------------------------------------------- CPU baseline
+def variant_times(b: "MoeBench", trials: int, inp_seed: int = 0) -> dict:
+    """The same timed steps with per-expert FC1/FC2 output biases, then with
+    unnormalised top-k weights (us per layer, graph replays)."""
+    import synth
+    from skinny_gemm_amd.layer import to_device_bits
+    out = {}
+    eb = synth.moe_inputs(b.spec, 1, inp_seed, weights=False, expert_bias=0.1)
+    b1, b2 = to_device_bits(eb["fc1_expert_bias"]), to_device_bits(eb["fc2_expert_bias"])
+    for lay in b.layers:
+        lay.fc1_bias, lay.fc2_bias = b1, b2
+    out["expert_bias_us"] = b.time_graph(trials)[0] * 1e3
+    for lay in b.layers:
+        lay.fc1_bias = lay.fc2_bias = None
+    b.kw = {"topk_weights": "softmax_all"}
+    out["softmax_all_weights_us"] = b.time_graph(trials)[0] * 1e3
+    b.kw = {}
+    return out
+
+
+def runtime_scales_time(layer, inp, reps: int = 20) -> dict:
+    """qmoe_prepack_scales on one prepacked layer, canonical scales resident."""
+    import torch
+    from skinny_gemm_amd import prepack_scales
+    from skinny_gemm_amd.layer import to_device_bits
+    dev = {k: to_device_bits(inp[k]) for k in ("fc1_scales", "fc1_biases", "fc2_scales", "fc2_biases")}
+    args = (layer.desc, dev["fc1_scales"], dev["fc1_biases"], dev["fc2_scales"], dev["fc2_biases"], layer.packed)
+    for _ in range(3):
+        prepack_scales(*args)
+    a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        prepack_scales(*args)
+    e.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(e) * 1e3 / reps
+    nbytes = sum(v.numel() * v.element_size() for v in dev.values() if v is not None)
+    return {"us": us, "canonical_scale_bytes": nbytes, "read_GBps": nbytes / (us * 1e-6) / 1e9}
+
+
+def tiled_prefill_time(layer, spec, T: int, div: int, reps: int = 3) -> dict:
+    """One T-token prefill call untiled and row-tiled under 1/div of the
+    untiled workspace (ms per call, event-timed)."""
+    import torch
+    import synth
+    from skinny_gemm_amd import forward_plan
+    from skinny_gemm_amd.layer import to_device_bits
+    inp = synth.moe_inputs(spec, T, 5, weights=False)
+    x = to_device_bits(inp["x"], spec.act_dtype)
+    lg = torch.from_numpy(inp["logits"]).cuda()
+    y = torch.empty((T, spec.H), dtype=x.dtype, device="cuda")
+    full = forward_plan(layer.desc, T, spec.top_k)
+    limit = full["workspace_bytes"] // div
+    tiled = forward_plan(layer.desc, T, spec.top_k, workspace_limit=limit)
+    res = {"T": T, "workspace_untiled": full["workspace_bytes"], "workspace_limit": limit,
+           "workspace_tiled": tiled["workspace_bytes"], "row_tile": tiled["row_tile"], "tiles": tiled["num_tiles"]}
+    for name, lim, nbytes in (("untiled_ms", 0, full["workspace_bytes"]), ("tiled_ms", limit, tiled["workspace_bytes"])):
+        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device="cuda")
+        layer.forward(x, lg, spec.top_k, y=y, ws=ws, workspace_limit=lim)
+        a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            layer.forward(x, lg, spec.top_k, y=y, ws=ws, workspace_limit=lim)
+        e.record()
+        torch.cuda.synchronize()
+        res[name] = a.elapsed_time(e) / reps
+        del ws
+    return res
+
+
 def cpu_baseline(b: "MoeBench", seconds: float):
     import oracle
     spec = b.spec
@@ -381,6 +452,10 @@ def main():
         del src, dst
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(b, args.cpu_seconds)
+    variants = {}
+    if not args.no_extras:
+        variants[f"{spec.name}_T{T}"] = {"base_us": head["us_per_layer"], **variant_times(b, 3)}
+        log(f"[bench] variants {json.dumps(variants)}")
     del b, layers
     torch.cuda.empty_cache()
     if not args.no_extras:
@@ -394,7 +469,12 @@ def main():
                                                               "frac_of_hbm_peak", "experts_touched_per_step",
                                                               "stage_us")})
             log(f"[bench] {json.dumps(extras['dsv2lite_int4'][-1])}")
+            if t == 1:
+                variants[f"{d3.name}_T1"] = {"base_us": r["us_per_layer"], **variant_times(bb, 3)}
+                log(f"[bench] variants {json.dumps(variants)}")
             del bb
+        variants[f"runtime_scales_{d3.name}"] = runtime_scales_time(lay3[0], i3)
+        log(f"[bench] variants {json.dumps(variants)}")
         del lay3
         torch.cuda.empty_cache()
         s1 = synth.MOE_WORKLOADS["single_expert_int4"]
@@ -412,7 +492,11 @@ def main():
         extras["mixed_int2_int4_prefill"] = {k: r[k] for k in ("us_per_layer", "effective_GBps", "tflops",
                                                                "stage_us", "experts_touched_per_step")}
         log(f"[bench] {json.dumps(extras['mixed_int2_int4_prefill'])}")
-        del bb, layp
+        del bb
+        torch.cuda.empty_cache()
+        variants[f"{pf.name}_row_tiling"] = tiled_prefill_time(layp[0], pf, 8193, 3)
+        log(f"[bench] variants {json.dumps(variants)}")
+        del layp
         torch.cuda.empty_cache()
         dense = synth.LINEAR_WORKLOADS["dense_affine2"]
         extras["dense_affine2"] = [bench_linear(dense, N, [1, 2, 3, 4, 5, 8, 10, 16, 32], 50, 3, args.rotate_bytes)
@@ -429,6 +513,7 @@ def main():
         r["workload"] = f"dsv2lite_fc1_all{d3.E}_experts_as_dense[N={d3.E * 2 * d3.I},K={d3.H}]"
         extras["expert_gemv_all_experts_m1"] = r
         log(f"[bench] {json.dumps(r)}")
+        extras["variants"] = variants
         line["extras"] = extras
     print(json.dumps(line), flush=True)
 

@@ -90,22 +90,25 @@ __global__ __launch_bounds__(256) void rowscale_kernel(const uint16_t *__restric
   }
 }
 
-// One workgroup per expert: power of two that keeps max |s| * qmax below 2^15.
-__global__ __launch_bounds__(256) void wscale_kernel(MatLayout L, const uint8_t *__restrict__ mat,
-                                                     float *__restrict__ wsc) {
-  __shared__ float red[4];
+// One 1024-thread workgroup per expert: power of two that keeps
+// max |s| * qmax below 2^15.  The prepacked scale section is read in 16-byte
+// vectors (it is 256-B aligned and a multiple of 128 B long; padding
+// entries are zero); affine entries hold the scale in their low half.
+__global__ __launch_bounds__(1024) void wscale_kernel(MatLayout L, const uint8_t *__restrict__ mat,
+                                                      float *__restrict__ wsc) {
+  __shared__ float red[1024 / 64];
   const int e = blockIdx.x;
-  const uint8_t *sb = mat + (int64_t)e * L.stride + L.scales_off;
-  const int64_t n = L.RG * L.NKT * kLanes * L.bpk;  // padded entries are zero
-  float m = 0.f;
+  const uint4 *sb = reinterpret_cast<const uint4 *>(mat + (int64_t)e * L.stride + L.scales_off);
+  const int64_t nv = L.RG * L.NKT * kLanes * L.bpk * (L.affine ? 4 : 2) / 16;
   const int f16 = L.sdtype == QMOE_DTYPE_F16;
-  const float qmax = (float)qtype_qmax(L.qtype);
-  for (int64_t i = threadIdx.x; i < n; i += blockDim.x) {
-    if (L.affine) {
-      const uint32_t sbb = reinterpret_cast<const uint32_t *>(sb)[i];
-      m = fmaxf(m, fabsf(half_to_f32_rt(sbb & 0xFFFFu, f16)) * qmax);
-    } else {
-      m = fmaxf(m, fabsf(half_to_f32_rt(reinterpret_cast<const uint16_t *>(sb)[i], f16)) * qmax);
+  float m = 0.f;
+  for (int64_t i = threadIdx.x; i < nv; i += blockDim.x) {
+    const uint4 v = sb[i];
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      m = fmaxf(m, fabsf(half_to_f32_rt(w[q] & 0xFFFFu, f16)));
+      if (!L.affine) m = fmaxf(m, fabsf(half_to_f32_rt(w[q] >> 16, f16)));
     }
   }
 #pragma unroll
@@ -113,8 +116,9 @@ __global__ __launch_bounds__(256) void wscale_kernel(MatLayout L, const uint8_t 
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
   __syncthreads();
   if (threadIdx.x == 0) {
-    const float mm = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    wsc[e] = pow2_below(mm, 15);
+    float mm = 0.f;
+    for (int w = 0; w < (int)(blockDim.x >> 6); ++w) mm = fmaxf(mm, red[w]);
+    wsc[e] = pow2_below(mm * (float)qtype_qmax(L.qtype), 15);
   }
 }
 
@@ -540,7 +544,7 @@ hipError_t launch_rowscale(const void *x, int rows, int64_t K, int in_f16, float
 }
 
 hipError_t launch_wscale(const MatLayout &L, int E, const uint8_t *mat, float *wsc, hipStream_t s) {
-  return qlaunch(wscale_kernel, dim3(E), dim3(256), 0, s, L, mat, wsc);
+  return qlaunch(wscale_kernel, dim3(E), dim3(1024), 0, s, L, mat, wsc);
 }
 
 }  // namespace qmoe

@@ -48,29 +48,31 @@ __global__ __launch_bounds__(256) void prepack_codes_kernel(MatLayout L, int64_t
   if (bad) atomicAdd(err, 1u);
 }
 
-// One thread per prepacked scale entry (expert, row group, k-tile, row,
-// block of the k-tile); entries past the last block are zero.
-__global__ __launch_bounds__(256) void prepack_scales_kernel(MatLayout L, int64_t total,
-                                                             const uint16_t *__restrict__ scales,
+// One workgroup per (row group, expert).  The source of a row group is one
+// contiguous [64 rows][nblk] block of the canonical scales; threads walk the
+// destination [k-tile][row][block of the k-tile] in order (coalesced
+// stores), and the reads stay inside that small block (cache-resident).
+// Entries past the last block are zero.
+__global__ __launch_bounds__(256) void prepack_scales_kernel(MatLayout L, const uint16_t *__restrict__ scales,
                                                              const uint16_t *__restrict__ biases,
                                                              uint8_t *__restrict__ dst) {
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= total) return;
-  const int64_t per = L.RG * L.NKT * kLanes * L.bpk;  // entries per expert
-  const int64_t e = idx / per, i = idx % per;
-  const int64_t bi = i % L.bpk;
-  const int64_t row = (i / L.bpk) % kLanes;
-  const int64_t kt = (i / L.bpk / kLanes) % L.NKT;
-  const int64_t rg = i / L.bpk / kLanes / L.NKT;
-  const int64_t n = rg * kRowsPerGroup + row, b = kt * L.bpk + bi;
-  uint8_t *base = dst + e * L.stride + L.scales_off;
-  const bool real = b < L.nblk;
-  const int64_t src = (e * L.N + n) * L.nblk + b;
-  if (L.affine) {
-    reinterpret_cast<uint32_t *>(base)[i] =
-        real ? ((uint32_t)scales[src] | ((uint32_t)biases[src] << 16)) : 0u;
-  } else {
-    reinterpret_cast<uint16_t *>(base)[i] = real ? scales[src] : (uint16_t)0;
+  const int rg = blockIdx.x, e = blockIdx.y;
+  const int nblk = (int)L.nblk, bpk = L.bpk;
+  const int per_rg = (int)L.NKT * kLanes * bpk;  // destination entries of one row group
+  const int64_t src0 = ((int64_t)e * L.N + (int64_t)rg * kRowsPerGroup) * nblk;
+  const int64_t dst0 = (int64_t)rg * per_rg;
+  uint8_t *base = dst + (int64_t)e * L.stride + L.scales_off;
+  for (int i = threadIdx.x; i < per_rg; i += blockDim.x) {
+    const int bi = i % bpk, row = (i / bpk) & (kLanes - 1), kt = i / (bpk * kLanes);
+    const int b = kt * bpk + bi;
+    const bool real = b < nblk;
+    const int64_t src = src0 + (int64_t)row * nblk + b;
+    if (L.affine) {
+      reinterpret_cast<uint32_t *>(base)[dst0 + i] =
+          real ? ((uint32_t)scales[src] | ((uint32_t)biases[src] << 16)) : 0u;
+    } else {
+      reinterpret_cast<uint16_t *>(base)[dst0 + i] = real ? scales[src] : (uint16_t)0;
+    }
   }
 }
 
@@ -120,17 +122,15 @@ hipError_t launch_prepack_matrix(const MatLayout &L, int E, const uint8_t *codes
   const int64_t tc = (int64_t)E * L.N * 4 * L.NKT;
   hipLaunchKernelGGL(prepack_codes_kernel, dim3(nblocks(tc, 256)), dim3(256), 0, s, L, tc, codes, dst,
                      err_word);
-  const int64_t ts = (int64_t)E * L.RG * L.NKT * kLanes * L.bpk;
-  hipLaunchKernelGGL(prepack_scales_kernel, dim3(nblocks(ts, 256)), dim3(256), 0, s, L, ts, scales,
-                     biases, dst);
+  hipLaunchKernelGGL(prepack_scales_kernel, dim3((unsigned)L.RG, (unsigned)E), dim3(256), 0, s, L, scales, biases,
+                     dst);
   return hipGetLastError();
 }
 
 hipError_t launch_prepack_scales(const MatLayout &L, int E, const uint16_t *scales, const uint16_t *biases,
                                  uint8_t *dst, hipStream_t s) {
-  const int64_t ts = (int64_t)E * L.RG * L.NKT * kLanes * L.bpk;
-  hipLaunchKernelGGL(prepack_scales_kernel, dim3(nblocks(ts, 256)), dim3(256), 0, s, L, ts, scales,
-                     biases, dst);
+  hipLaunchKernelGGL(prepack_scales_kernel, dim3((unsigned)L.RG, (unsigned)E), dim3(256), 0, s, L, scales, biases,
+                     dst);
   return hipGetLastError();
 }
 
