@@ -29,7 +29,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "liboracle.so")
 
 FMT = {"sym_int4": 0, "sym_int2": 1, "ternary": 2, "affine_int2": 3, "affine_int4": 4}
-DT = {"bf16": 0, "f16": 1}
+DT = {"bf16": 0, "f16": 1, "f32": 2}
 BITS = {"sym_int4": 4, "sym_int2": 2, "ternary": 2, "affine_int2": 2, "affine_int4": 4}
 
 _lib = None
@@ -138,11 +138,13 @@ def moe(inp: dict, debug: bool = False, tokens=None, renorm: bool = True):
     [E][2I] and ``fc2_expert_bias`` [E][H] (16-bit patterns of the activation
     dtype) are per-expert output biases of FC1 and FC2.  ``renorm`` selects
     the routing weights as in ``route``.  Returns a dict with ``y64``
-    (float64, unrounded), ``y`` (16-bit patterns of the activation dtype) and,
+    (float64, unrounded), ``y`` (16-bit patterns of the activation dtype, or
+    float32 values for f32 activations) and,
     with ``debug``, per-slot ``a``/``h``/``o`` in slot order t*k+j.
     """
     sp = inp["spec"]
-    x = _c(inp["x"], np.uint16)
+    adt = np.float32 if sp.act_dtype == "f32" else np.uint16   # f32 activations as values
+    x = _c(inp["x"], adt)
     lg = _c(inp["logits"], np.float32)
     if tokens is not None:
         x = np.ascontiguousarray(x[tokens])
@@ -150,7 +152,7 @@ def moe(inp: dict, debug: bool = False, tokens=None, renorm: bool = True):
     T = x.shape[0]
     H, I, k = sp.H, sp.I, sp.top_k
     y64 = np.empty((T, H), dtype=np.float64)
-    y16 = np.empty((T, H), dtype=np.uint16)
+    y16 = np.empty((T, H), dtype=adt)
     a = h = o = None
     if debug:
         a = np.empty((T * k, 2 * I), dtype=np.float64)
@@ -158,7 +160,7 @@ def moe(inp: dict, debug: bool = False, tokens=None, renorm: bool = True):
         o = np.empty((T * k, H), dtype=np.float64)
     arr = {n: _c(inp[n], np.uint8 if n.endswith("codes") else np.uint16)
            for n in ("fc1_codes", "fc1_scales", "fc1_biases", "fc2_codes", "fc2_scales", "fc2_biases")}
-    eb = {n: _c(inp.get(n), np.uint16) for n in ("fc1_expert_bias", "fc2_expert_bias")}
+    eb = {n: _c(inp.get(n), adt) for n in ("fc1_expert_bias", "fc2_expert_bias")}
     rc = lib().orc_moe(
         sp.E, H, I, k, DT[sp.act_dtype],
         FMT[sp.fc1.fmt], sp.fc1.block, DT[sp.fc1.scale_dtype],

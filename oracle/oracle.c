@@ -43,7 +43,7 @@
 #include <string.h>
 
 enum { ORC_SYM_INT4 = 0, ORC_SYM_INT2 = 1, ORC_TERNARY = 2, ORC_AFFINE_INT2 = 3, ORC_AFFINE_INT4 = 4 };
-enum { ORC_BF16 = 0, ORC_F16 = 1 };
+enum { ORC_BF16 = 0, ORC_F16 = 1, ORC_F32 = 2 };
 
 /* ---------- 16-bit floating point, from the IEEE 754 definitions ---------- */
 
@@ -223,6 +223,12 @@ void orc_route(int T, int E, int k, int renorm, const float *logits, int32_t *id
 
 double orc_silu(double g) { return g / (1.0 + exp(-g)); }
 
+/* Activation-dtype element i of p: 16-bit patterns of bf16 / f16, or f32. */
+static double orc_act(const void *p, int64_t i, int dtype) {
+  if (dtype == ORC_F32) return (double)((const float *)p)[i];
+  return orc_half_to_double(((const uint16_t *)p)[i], dtype);
+}
+
 typedef struct {
   int fmt, block, sdtype;
   const uint8_t *codes;
@@ -244,11 +250,12 @@ static void orc_matvec(const orc_mat *m, int64_t e, int64_t N, int64_t K, const 
 }
 
 /*
- * Full MoE layer for T tokens.  x [T][H] and y16 [T][H] are 16-bit patterns of
- * act_dtype, logits [T][E] float32, y64 [T][H] the unrounded result.  Optional
+ * Full MoE layer for T tokens.  x [T][H] and y_out [T][H] hold act_dtype
+ * elements (16-bit patterns of bf16 / f16, or f32; y_out is y64 rounded once
+ * to that dtype), logits [T][E] float32, y64 [T][H] the unrounded result.  Optional
  * per-slot diagnostics in slot order r = t*k + j: a_dbg [T*k][2I] (FC1),
  * h_dbg [T*k][I] (after SwiGLU), o_dbg [T*k][H] (FC2).  Optional expert
- * biases in act_dtype: fc1_ebias [E][2I], in FC1's interleaved row order, is
+ * biases, act_dtype elements: fc1_ebias [E][2I], in FC1's interleaved row order, is
  * added to FC1's output before the SwiGLU, and fc2_ebias [E][H] to FC2's
  * output before the top-k weighting (onnxruntime pull request 33005,
  * Description: expert bias before the SwiGLU, FC2 bias in the finalize).
@@ -260,9 +267,9 @@ int orc_moe(int E, int H, int I, int k, int act_dtype,
             const uint8_t *fc1_codes, const uint16_t *fc1_scales, const uint16_t *fc1_biases,
             int fc2_fmt, int fc2_block, int fc2_sdtype,
             const uint8_t *fc2_codes, const uint16_t *fc2_scales, const uint16_t *fc2_biases,
-            const uint16_t *fc1_ebias, const uint16_t *fc2_ebias, int renorm,
-            const uint16_t *x, const float *logits, int T,
-            double *y64, uint16_t *y16, double *a_dbg, double *h_dbg, double *o_dbg) {
+            const void *fc1_ebias, const void *fc2_ebias, int renorm,
+            const void *x, const float *logits, int T,
+            double *y64, void *y_out, double *a_dbg, double *h_dbg, double *o_dbg) {
   orc_mat w1 = {fc1_fmt, fc1_block, fc1_sdtype, fc1_codes, fc1_scales, fc1_biases};
   orc_mat w2 = {fc2_fmt, fc2_block, fc2_sdtype, fc2_codes, fc2_scales, fc2_biases};
   const int64_t S = (int64_t)T * k;
@@ -279,7 +286,7 @@ int orc_moe(int E, int H, int I, int k, int act_dtype,
   int bad = 0;
   orc_route(T, E, k, renorm, logits, ids, wts, counts, offsets, rows);
   for (int t = 0; t < T; ++t) {
-    for (int64_t n = 0; n < H; ++n) xv[n] = orc_half_to_double(x[(int64_t)t * H + n], act_dtype);
+    for (int64_t n = 0; n < H; ++n) xv[n] = orc_act(x, (int64_t)t * H + n, act_dtype);
     double *yt = y64 + (int64_t)t * H;
     for (int64_t n = 0; n < H; ++n) yt[n] = 0.0;
     for (int j = 0; j < k; ++j) {
@@ -288,17 +295,20 @@ int orc_moe(int E, int H, int I, int k, int act_dtype,
       orc_matvec(&w1, e, 2 * (int64_t)I, H, xv, a, wrow, &bad);
       if (fc1_ebias)
         for (int64_t n = 0; n < 2 * I; ++n)
-          a[n] += orc_half_to_double(fc1_ebias[(int64_t)e * 2 * I + n], act_dtype);
+          a[n] += orc_act(fc1_ebias, (int64_t)e * 2 * I + n, act_dtype);
       for (int64_t i = 0; i < I; ++i) h[i] = orc_silu(a[2 * i]) * a[2 * i + 1];
       orc_matvec(&w2, e, H, I, h, o, wrow, &bad);
       if (fc2_ebias)
-        for (int64_t n = 0; n < H; ++n) o[n] += orc_half_to_double(fc2_ebias[(int64_t)e * H + n], act_dtype);
+        for (int64_t n = 0; n < H; ++n) o[n] += orc_act(fc2_ebias, (int64_t)e * H + n, act_dtype);
       for (int64_t n = 0; n < H; ++n) yt[n] += wts[r] * o[n];
       if (a_dbg) memcpy(a_dbg + r * 2 * I, a, sizeof(double) * (size_t)(2 * I));
       if (h_dbg) memcpy(h_dbg + r * I, h, sizeof(double) * (size_t)I);
       if (o_dbg) memcpy(o_dbg + r * H, o, sizeof(double) * (size_t)H);
     }
-    for (int64_t n = 0; n < H; ++n) y16[(int64_t)t * H + n] = orc_double_to_half(yt[n], act_dtype);
+    for (int64_t n = 0; n < H; ++n) {
+      if (act_dtype == ORC_F32) ((float *)y_out)[(int64_t)t * H + n] = (float)yt[n];  /* one RNE */
+      else ((uint16_t *)y_out)[(int64_t)t * H + n] = orc_double_to_half(yt[n], act_dtype);
+    }
   }
   free(ids); free(wts); free(counts); free(offsets); free(rows);
   free(xv); free(a); free(h); free(o); free(wrow);

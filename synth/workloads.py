@@ -120,6 +120,8 @@ def _to_bits(v64: np.ndarray, dtype: str) -> np.ndarray:
         return f32_to_bf16_bits(v32)
     if dtype == "f16":
         return f32_to_f16_bits(v32)
+    if dtype == "f32":  # f32 activations are carried as float32 values
+        return v32
     raise ValueError(dtype)
 
 

@@ -27,6 +27,8 @@ def fields(packed: np.ndarray, bits: int, K: int) -> np.ndarray:
 
 
 def half_bits_to_f64(bits: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == "f32":  # f32 activations are carried as float32 values
+        return np.asarray(bits, dtype=np.float32).astype(np.float64)
     bits = np.asarray(bits, dtype=np.uint16)
     if dtype == "f16":
         return bits.view(np.float16).astype(np.float64)

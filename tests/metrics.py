@@ -1,4 +1,4 @@
-"""Parity metric for 16-bit outputs against the oracle.
+"""Parity metric for 16-bit (and f32) outputs against the oracle.
 
 The workloads state a maximum relative error of 2e-3 with bf16 output and
 fp32 accumulation.  Per element that bound is below one bf16 ulp (2^-8
@@ -21,6 +21,8 @@ TOL = 2e-3
 
 
 def decode(bits: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == "f32":  # f32 outputs are carried as float32 values
+        return np.asarray(bits, dtype=np.float32).astype(np.float64)
     bits = np.asarray(bits, dtype=np.uint16)
     if dtype == "f16":
         return bits.view(np.float16).astype(np.float64)
@@ -28,6 +30,8 @@ def decode(bits: np.ndarray, dtype: str) -> np.ndarray:
 
 
 def ulp(bits: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == "f32":
+        return np.spacing(np.abs(np.asarray(bits, dtype=np.float32))).astype(np.float64)
     mag = np.asarray(bits, dtype=np.uint16) & np.uint16(0x7FFF)
     nxt = (mag.astype(np.uint32) + 1).astype(np.uint16)
     return np.abs(decode(nxt, dtype) - decode(mag, dtype))

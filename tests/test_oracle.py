@@ -249,6 +249,7 @@ TINY = [
     dict(E=3, H=128, I=128, top_k=1, fc1="ternary", block1=128, scale_dtype="f16"),
     dict(E=4, H=128, I=64, top_k=2, fc1="affine_int2", fc2="affine_int4", block1=64, block2=64,
          scale_dtype="f16", act_dtype="f16"),
+    dict(E=4, H=128, I=64, top_k=2, fc1="sym_int4", act_dtype="f32"),
 ]
 
 
@@ -263,9 +264,13 @@ def test_moe_vs_dense_bruteforce(oracle_lib, cfg, T):
     assert np.allclose(out["y64"], ref, rtol=1e-10, atol=1e-12 * np.abs(ref).max())
     if spec.act_dtype == "f16":
         assert np.array_equal(out["y"], out["y64"].astype(np.float16).view(np.uint16))
+    if spec.act_dtype == "f32":                                   # one RNE to f32, x read as f32
+        assert out["y"].dtype == np.float32 and np.array_equal(out["y"], out["y64"].astype(np.float32))
+        assert inp["x"].dtype == np.float32
 
 
-@pytest.mark.parametrize("cfg", [TINY[1], TINY[2], TINY[4]], ids=["int4-k2", "int2-int4-k4", "affine-f16"])
+@pytest.mark.parametrize("cfg", [TINY[1], TINY[2], TINY[4], TINY[5]],
+                         ids=["int4-k2", "int2-int4-k4", "affine-f16", "int4-f32"])
 @pytest.mark.parametrize("T", [1, 3])
 def test_moe_expert_bias_vs_dense_bruteforce(oracle_lib, cfg, T):
     spec = custom_moe_spec(**cfg)
