@@ -474,6 +474,25 @@ def main():
                 log(f"[bench] variants {json.dumps(variants)}")
             del bb
         variants[f"runtime_scales_{d3.name}"] = runtime_scales_time(lay3[0], i3)
+        # f32 activations over the same prepacked weights (the packed buffer
+        # does not depend on the activation dtype; only the descriptor does)
+        import copy
+        import dataclasses
+        from skinny_gemm_amd import layer_desc
+        d3f = dataclasses.replace(d3, act_dtype="f32", name=d3.name + "_f32")
+        lay3f = []
+        for lay in lay3:
+            c = copy.copy(lay)
+            c.act_dtype = "f32"
+            c.desc = layer_desc(d3.E, d3.H, d3.I, "f32", (d3.fc1.fmt, d3.fc1.block, d3.fc1.scale_dtype),
+                                (d3.fc2.fmt, d3.fc2.block, d3.fc2.scale_dtype))
+            lay3f.append(c)
+        for t in (1, 8):
+            r, bb = bench_moe(d3f, t, 100, 10, 3, lay3f, i3, stages=False)
+            base = next(x["us_per_layer"] for x in extras["dsv2lite_int4"] if x["T"] == t)
+            variants[f"{d3.name}_T{t}_f32_activations"] = {"us": r["us_per_layer"], "bf16_us": base}
+            del bb
+        del lay3f
         log(f"[bench] variants {json.dumps(variants)}")
         del lay3
         torch.cuda.empty_cache()

@@ -70,7 +70,7 @@
 extern "C" {
 #endif
 
-#define QMOE_ABI_VERSION 5
+#define QMOE_ABI_VERSION 6
 
 typedef enum qmoe_status {
   QMOE_OK = 0,
@@ -83,7 +83,7 @@ typedef enum qmoe_status {
 typedef enum qmoe_dtype {
   QMOE_DTYPE_BF16 = 0,
   QMOE_DTYPE_F16 = 1,
-  QMOE_DTYPE_F32 = 2 /* reserved: not accepted as activation or scale dtype */
+  QMOE_DTYPE_F32 = 2 /* activations only, on the GEMV path (see qmoe_layer_desc) */
 } qmoe_dtype;
 
 typedef enum qmoe_qtype {
@@ -115,7 +115,11 @@ typedef struct qmoe_layer_desc {
   int32_t num_experts; /* E in [1, 256] */
   int32_t hidden;      /* H */
   int32_t inter;       /* I */
-  int32_t act_dtype;   /* QMOE_DTYPE_BF16 or QMOE_DTYPE_F16: x and y */
+  int32_t act_dtype;   /* QMOE_DTYPE_BF16, F16 or F32: x and y.  F32 (onnx-genai pull request
+                          1167, Parity: f16/bf16/f32 decode) runs the GEMV path only (T <= 16;
+                          larger T or a forced grouped path: QMOE_ERR_UNSUPPORTED), with x
+                          split into bf16 hi + lo parts for the matrix cores, y rounded once to
+                          f32, and no expert biases (QMOE_ERR_UNSUPPORTED) */
   qmoe_qmatrix_desc fc1;
   qmoe_qmatrix_desc fc2;
 } qmoe_layer_desc;

@@ -75,8 +75,8 @@ qmoe_status check_layer(const qmoe_layer_desc *d) {
     return fail(QMOE_ERR_UNSUPPORTED, "num_experts %d > %d", d->num_experts, kMaxExperts);
   if (d->hidden <= 0 || d->inter <= 0)
     return fail(QMOE_ERR_INVALID_ARGUMENT, "hidden and inter must be positive");
-  if (d->act_dtype != QMOE_DTYPE_BF16 && d->act_dtype != QMOE_DTYPE_F16)
-    return fail(QMOE_ERR_UNSUPPORTED, "activation dtype %d not supported (bf16 or f16)", d->act_dtype);
+  if (d->act_dtype != QMOE_DTYPE_BF16 && d->act_dtype != QMOE_DTYPE_F16 && d->act_dtype != QMOE_DTYPE_F32)
+    return fail(QMOE_ERR_UNSUPPORTED, "activation dtype %d not supported (bf16, f16 or f32)", d->act_dtype);
   qmoe_status st = check_matrix(d->fc1, "fc1", 2 * (int64_t)d->inter, d->hidden);
   if (st != QMOE_OK) return st;
   return check_matrix(d->fc2, "fc2", d->hidden, d->inter);
@@ -146,9 +146,10 @@ struct RouteWs {
 // and the per-token activation scales.  Both paths write o [S][H] fp32.
 struct MoeWs {
   RouteWs route;
-  int64_t h_hi, h_lo, h32, hmax, xsc, xs16, o, total;
+  int64_t h_hi, h_lo, h32, hmax, xsc, xs16, x_hi, x_lo, o, total;
   static MoeWs make(const qmoe_layer_desc &d, int32_t T, int32_t k, bool grouped) {
     MoeWs w;
+    w.x_hi = w.x_lo = 0;
     Carve c;
     const int64_t S = (int64_t)T * k;
     w.route = RouteWs::make(c, S, d.num_experts);
@@ -162,6 +163,9 @@ struct MoeWs {
       w.h_hi = c.take(S * d.inter * 2);
       w.h_lo = c.take(S * d.inter * 2);
       w.h32 = w.hmax = w.xsc = w.xs16 = 0;
+      // f32 activations: x as bf16 hi + lo rows (the FC1 A operand)
+      w.x_hi = d.act_dtype == QMOE_DTYPE_F32 ? c.take((int64_t)T * d.hidden * 2) : 0;
+      w.x_lo = d.act_dtype == QMOE_DTYPE_F32 ? c.take((int64_t)T * d.hidden * 2) : 0;
     }
     w.o = c.take(S * d.hidden * 4);
     w.total = c.off;
@@ -256,6 +260,11 @@ struct Plan {
   std::string kernels;
 };
 
+// FC1 input mode of the GEMV for an activation dtype.
+int gemv_in_mode(int act_dtype) {
+  return act_dtype == QMOE_DTYPE_F32 ? kGemvInSplitF32 : act_dtype == QMOE_DTYPE_F16 ? 1 : 0;
+}
+
 qmoe_status make_plan(const qmoe_layer_desc &d, int32_t T, int32_t k, int path_req, bool softmax_all, Plan &p) {
   const MoeLayout L = MoeLayout::make(d);
   p = Plan{};
@@ -267,6 +276,9 @@ qmoe_status make_plan(const qmoe_layer_desc &d, int32_t T, int32_t k, int path_r
     return fail(QMOE_ERR_UNSUPPORTED, "GEMV path needs T <= %d (got %d)", kGemvMaxRows, T);
   p.path = path;
   p.max_active = (int)std::min<int64_t>(d.num_experts, (int64_t)T * k);
+  const bool f32 = d.act_dtype == QMOE_DTYPE_F32;
+  if (f32 && path == QMOE_PATH_GROUPED)
+    return fail(QMOE_ERR_UNSUPPORTED, "f32 activations run on the GEMV path only (T <= %d, got %d)", kGemvMaxRows, T);
   if (path == QMOE_PATH_GROUPED) {
     if ((L.fc1.affine && L.fc1.nblk > kGroupedMaxAffineBlocks) ||
         (L.fc2.affine && L.fc2.nblk > kGroupedMaxAffineBlocks))
@@ -288,7 +300,7 @@ qmoe_status make_plan(const qmoe_layer_desc &d, int32_t T, int32_t k, int path_r
   p.max_active = (int)std::min<int64_t>(d.num_experts, (int64_t)T * k);
   p.mmax = p.mmax1 = p.mmax2 = T;  // no expert gets more rows than there are tokens
   const GemvShape g1 = pick_gemv((int64_t)p.max_active * L.fc1.RG, L.fc1, T,
-                                 p.fc1_routes ? kEpiSwiGLURouted : kEpiSwiGLU, d.act_dtype == QMOE_DTYPE_F16);
+                                 p.fc1_routes ? kEpiSwiGLURouted : kEpiSwiGLU, gemv_in_mode(d.act_dtype));
   const GemvShape g2 = pick_gemv((int64_t)p.max_active * L.fc2.RG, L.fc2, T, kEpiDown, 0);
   p.ks1 = g1.waves;
   p.tn1 = g1.tn;
@@ -298,9 +310,11 @@ qmoe_status make_plan(const qmoe_layer_desc &d, int32_t T, int32_t k, int path_r
   // the weights of SOFTMAX_ALL replace the routing's weights once the ids
   // exist, before the first reader of the weights (FC2 or the combine)
   p.softmax_all = softmax_all;
-  p.kernels = std::string(p.fc1_routes ? "route_fc1_swiglu" : "route,gemv_fc1_swiglu") +
-              (softmax_all ? ",route_weights" : "") + ",gemv_fc2" + (k == 1 ? "" : ",combine");
-  p.launches = (p.fc1_routes ? 2 : 3) + (k == 1 ? 0 : 1) + (softmax_all ? 1 : 0);
+  // f32 activations: a split pass first, and y always from the combine
+  const bool combine = k > 1 || f32;
+  p.kernels = std::string(f32 ? "split_x," : "") + (p.fc1_routes ? "route_fc1_swiglu" : "route,gemv_fc1_swiglu") +
+              (softmax_all ? ",route_weights" : "") + ",gemv_fc2" + (combine ? ",combine" : "");
+  p.launches = (p.fc1_routes ? 2 : 3) + (combine ? 1 : 0) + (softmax_all ? 1 : 0) + (f32 ? 1 : 0);
   return ok();
 }
 
@@ -555,6 +569,8 @@ qmoe_status qmoe_forward_ex(const qmoe_layer_desc *desc, const void *packed, con
     return fail(QMOE_ERR_INVALID_ARGUMENT, "opts.topk_weights %d is not a qmoe_topk_weights value",
                 opts->topk_weights);
   if (opts && opts->workspace_limit < 0) return fail(QMOE_ERR_INVALID_ARGUMENT, "negative workspace_limit");
+  if (opts && (opts->fc1_bias || opts->fc2_bias) && desc->act_dtype == QMOE_DTYPE_F32)
+    return fail(QMOE_ERR_UNSUPPORTED, "expert biases need 16-bit activations");
   if (T == 0) return ok();
   const bool softmax_all = opts && opts->topk_weights == QMOE_TOPK_SOFTMAX_ALL;
   if (opts && opts->workspace_limit > 0) {
@@ -578,14 +594,16 @@ qmoe_status qmoe_forward_ex(const qmoe_layer_desc *desc, const void *packed, con
       qmoe_forward_opts o = *opts;
       o.workspace_limit = 0;
       const int64_t H = desc->hidden, E = desc->num_experts, I = desc->inter;
+      const int64_t act_bytes = desc->act_dtype == QMOE_DTYPE_F32 ? 4 : 2;
       for (int32_t t0 = 0; t0 < T; t0 += tl.rows) {
         const int32_t n = std::min(tl.rows, T - t0);
         const int64_t s0 = (int64_t)t0 * top_k;
         o.h_out = opts->h_out ? opts->h_out + s0 * I : nullptr;
         o.ids_out = opts->ids_out ? opts->ids_out + s0 : nullptr;
         o.w_out = opts->w_out ? opts->w_out + s0 : nullptr;
-        st = qmoe_forward_ex(desc, packed, (const uint16_t *)x + (int64_t)t0 * H, logits + (int64_t)t0 * E, n,
-                             top_k, (uint16_t *)y + (int64_t)t0 * H, ws, ws_bytes, stream, &o);
+        const int64_t xoff = (int64_t)t0 * H * act_bytes;  // bytes: rows of x and y
+        st = qmoe_forward_ex(desc, packed, (const uint8_t *)x + xoff, logits + (int64_t)t0 * E, n, top_k,
+                             (uint8_t *)y + xoff, ws, ws_bytes, stream, &o);
         if (st != QMOE_OK) return st;
       }
       return ok();
@@ -643,6 +661,14 @@ qmoe_status qmoe_forward_ex(const qmoe_layer_desc *desc, const void *packed, con
     return hipSuccess;
   };
   hipError_t e = hipSuccess;
+  const bool f32 = desc->act_dtype == QMOE_DTYPE_F32;
+  uint16_t *x_hi = (uint16_t *)(wsb + W.x_hi), *x_lo = (uint16_t *)(wsb + W.x_lo);
+  if (f32) {  // x as bf16 hi + lo rows for FC1
+    e = begin();
+    if (e == hipSuccess) e = launch_split_f32((const float *)x, (int64_t)T * desc->hidden, x_hi, x_lo, s);
+    if (e == hipSuccess) e = end();
+    if (e != hipSuccess) return hip_status(e, "split x");
+  }
   const bool fc1_routes = p.path == QMOE_PATH_GEMV && p.fc1_routes;
   if (!fc1_routes) {
     e = begin();
@@ -725,8 +751,9 @@ qmoe_status qmoe_forward_ex(const qmoe_layer_desc *desc, const void *packed, con
   g1.token_of = ra.r.token_of;
   g1.row_list = ra.r.row_list;
   g1.top_k = top_k;
-  g1.in = (const uint32_t *)x;
+  g1.in = (const uint32_t *)(f32 ? x_hi : x);
   g1.in_row_pairs = desc->hidden / 2;
+  g1.in_part_stride = f32 ? (int64_t)(x_lo - x_hi) / 2 : 0;
   g1.in_gather_token = 1;
   g1.h_hi = h_hi;
   g1.h_lo = h_lo;
@@ -735,7 +762,7 @@ qmoe_status qmoe_forward_ex(const qmoe_layer_desc *desc, const void *packed, con
   g1.act_dtype = desc->act_dtype;
   e = begin();
   if (e == hipSuccess)
-    e = launch_gemv(g1, fc1_routes ? kEpiSwiGLURouted : kEpiSwiGLU, desc->act_dtype == QMOE_DTYPE_F16, p.mmax1,
+    e = launch_gemv(g1, fc1_routes ? kEpiSwiGLURouted : kEpiSwiGLU, gemv_in_mode(desc->act_dtype), p.mmax1,
                     p.ks1, p.tn1, L.fc1.block, p.max_active, s);
   if (e == hipSuccess) e = end();
   if (e != hipSuccess) return hip_status(e, "gemv fc1");
@@ -745,7 +772,7 @@ qmoe_status qmoe_forward_ex(const qmoe_layer_desc *desc, const void *packed, con
   g2.slot_info = ra.r.slot_info;
   g2.token_of = ra.r.token_of;
   g2.row_list = ra.r.row_list;
-  g2.top_k = top_k;
+  g2.top_k = f32 ? 0 : top_k;  // 1: FC2 writes y itself (16-bit y only); otherwise o and the combine
   g2.in = (const uint32_t *)h_hi;
   g2.in_row_pairs = desc->inter / 2;
   g2.in_part_stride = (int64_t)(h_lo - h_hi) / 2;
@@ -759,10 +786,9 @@ qmoe_status qmoe_forward_ex(const qmoe_layer_desc *desc, const void *packed, con
   if (e == hipSuccess) e = launch_gemv(g2, kEpiDown, 0, p.mmax2, p.ks2, p.tn2, L.fc2.block, p.max_active, s);
   if (e == hipSuccess) e = end();
   if (e != hipSuccess) return hip_status(e, "gemv fc2");
-  if (top_k > 1) {
+  if (top_k > 1 || f32) {
     e = begin();
-    if (e == hipSuccess)
-      e = launch_combine(o, ra.r.slot_pos, ra.r.w, T, top_k, desc->hidden, desc->act_dtype, (uint16_t *)y, s);
+    if (e == hipSuccess) e = launch_combine(o, ra.r.slot_pos, ra.r.w, T, top_k, desc->hidden, desc->act_dtype, y, s);
     if (e == hipSuccess) e = end();
     if (e != hipSuccess) return hip_status(e, "combine");
   }

@@ -3,7 +3,8 @@
 // dispatch over quantization formats.
 //
 // y[t][n] = sum_{j=0..k-1} w[t][j] * o[pos(t, j)][n], summed in fp32 in
-// ascending j from 0, rounded once to nearest-even in the activation dtype.
+// ascending j from 0, rounded once to nearest-even in the activation dtype
+// (stored as is for f32 activations).
 // o holds the per-slot FC2 outputs in expert-sorted order; pos is the
 // inverse of the row list.
 #include <map>
@@ -18,7 +19,7 @@ namespace qmoe {
 __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ o,
                                                       const int32_t *__restrict__ slot_pos,
                                                       const float *__restrict__ w, int T, int k,
-                                                      int H, int is_f16, uint16_t *__restrict__ y) {
+                                                      int H, int act_dtype, void *__restrict__ y) {
   const int H4 = H / 4;
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= (int64_t)T * H4) return;
@@ -33,18 +34,40 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
     acc.z = fmaf(wt, v.z, acc.z);
     acc.w = fmaf(wt, v.w, acc.w);
   }
+  if (act_dtype == QMOE_DTYPE_F32) {
+    reinterpret_cast<float4 *>(reinterpret_cast<float *>(y) + (int64_t)t * H)[n4] = acc;
+    return;
+  }
+  const int is_f16 = act_dtype == QMOE_DTYPE_F16;
   uint2 out;
   out.x = (uint32_t)f32_to_act(acc.x, is_f16) | ((uint32_t)f32_to_act(acc.y, is_f16) << 16);
   out.y = (uint32_t)f32_to_act(acc.z, is_f16) | ((uint32_t)f32_to_act(acc.w, is_f16) << 16);
-  reinterpret_cast<uint2 *>(y + (int64_t)t * H)[n4] = out;
+  reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(y) + (int64_t)t * H)[n4] = out;
+}
+
+// f32 rows -> bf16 hi + lo rows (hi = x rounded to nearest-even, lo = the
+// rest rounded the same way), the two-part A operand of the GEMV.
+__global__ __launch_bounds__(256) void split_f32_kernel(const float *__restrict__ x, int64_t n,
+                                                        uint16_t *__restrict__ hi, uint16_t *__restrict__ lo) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const float v = x[i];
+  const uint16_t h = f32_to_bf16_rne(v);
+  hi[i] = h;
+  lo[i] = f32_to_bf16_rne(v - bf16_to_f32(h));
+}
+
+hipError_t launch_split_f32(const float *x, int64_t n, uint16_t *hi, uint16_t *lo, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  return qlaunch(split_f32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, x, n, hi, lo);
 }
 
 hipError_t launch_combine(const float *o, const int32_t *slot_pos, const float *w, int T, int k,
-                          int H, int act_dtype, uint16_t *y, hipStream_t s) {
+                          int H, int act_dtype, void *y, hipStream_t s) {
   const int64_t total = (int64_t)T * (H / 4);
   if (total == 0) return hipSuccess;
   return qlaunch(combine_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, o, slot_pos, w, T, k, H,
-                 act_dtype == QMOE_DTYPE_F16 ? 1 : 0, y);
+                 act_dtype, y);
 }
 
 const void *gemv_ptr_sym_int4(int, int, int, int, int);

@@ -481,12 +481,15 @@ const void *gemv_ptr_rows(int rows, int block, int tn) {
 template <int QT>
 const void *gemv_ptr_qt(int epilogue, int in_f16, int rows, int block, int tn) {
   if (epilogue == kEpiDown) return gemv_ptr_rows<QT, false, 2, kEpiDown>(rows, block, tn);
+  // FC1 input: bf16 or f16 rows, or (kGemvInSplitF32) f32 rows given as bf16 hi + lo parts
   if (epilogue == kEpiSwiGLU)
-    return in_f16 ? gemv_ptr_rows<QT, true, 1, kEpiSwiGLU>(rows, block, tn)
-                  : gemv_ptr_rows<QT, false, 1, kEpiSwiGLU>(rows, block, tn);
+    return in_f16 == kGemvInSplitF32 ? gemv_ptr_rows<QT, false, 2, kEpiSwiGLU>(rows, block, tn)
+           : in_f16                  ? gemv_ptr_rows<QT, true, 1, kEpiSwiGLU>(rows, block, tn)
+                                     : gemv_ptr_rows<QT, false, 1, kEpiSwiGLU>(rows, block, tn);
   if (epilogue == kEpiSwiGLURouted)
-    return in_f16 ? gemv_ptr_rows<QT, true, 1, kEpiSwiGLURouted>(rows, block, tn)
-                  : gemv_ptr_rows<QT, false, 1, kEpiSwiGLURouted>(rows, block, tn);
+    return in_f16 == kGemvInSplitF32 ? gemv_ptr_rows<QT, false, 2, kEpiSwiGLURouted>(rows, block, tn)
+           : in_f16                  ? gemv_ptr_rows<QT, true, 1, kEpiSwiGLURouted>(rows, block, tn)
+                                     : gemv_ptr_rows<QT, false, 1, kEpiSwiGLURouted>(rows, block, tn);
   return in_f16 ? gemv_ptr_rows<QT, true, 1, kEpiStoreAct>(rows, block, tn)
                 : gemv_ptr_rows<QT, false, 1, kEpiStoreAct>(rows, block, tn);
 }

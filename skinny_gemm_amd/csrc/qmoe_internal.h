@@ -191,6 +191,9 @@ struct RouteArgs {
 // routing kernel); workgroup 0 also writes the routing lists for FC2, the
 // combine and the diagnostics.
 enum GemvEpilogue { kEpiSwiGLU = 0, kEpiDown = 1, kEpiStoreAct = 2, kEpiSwiGLURouted = 3 };
+// Input of the FC1 epilogues (the in_f16 argument of launch_gemv): 0 bf16
+// rows, 1 f16 rows, kGemvInSplitF32 f32 rows given as bf16 hi + lo parts.
+constexpr int kGemvInSplitF32 = 2;
 constexpr int kFc1RouteMaxSlots = 16;  // <= 64 (one slot per lane of the expand)
 
 struct GemvArgs {
@@ -203,7 +206,7 @@ struct GemvArgs {
   // rows: routed (slot_info / token_of) or dense (M rows)
   const int4 *slot_info;
   const int32_t *token_of, *row_list;
-  int top_k;
+  int top_k;               // kEpiDown: 1 = write y itself (one expert per token), else o
   int dense_M;             // >0: dense rows 0..M-1, expert 0, no routing
   // input activations as 16-bit pairs; parts = 1 (x) or 2 (hi, lo)
   const uint32_t *in;
@@ -263,7 +266,9 @@ hipError_t launch_gemv(const GemvArgs &a, int epilogue, int in_f16, int rows, in
 // cannot tell).
 int gemv_blocks_per_cu(int qtype, int epilogue, int in_f16, int rows, int waves, int tn, int block);
 hipError_t launch_combine(const float *o, const int32_t *slot_pos, const float *w, int T, int k,
-                          int H, int act_dtype, uint16_t *y, hipStream_t s);
+                          int H, int act_dtype, void *y, hipStream_t s);
+// f32 rows -> bf16 hi (RNE of x) and lo (RNE of the remainder) rows.
+hipError_t launch_split_f32(const float *x, int64_t n, uint16_t *hi, uint16_t *lo, hipStream_t s);
 
 // ----------------------------------------------------------- grouped MFMA
 constexpr int kTileM = 64;   // rows (tokens) per grouped tile

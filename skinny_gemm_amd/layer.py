@@ -13,13 +13,15 @@ from . import (layer_desc, qmatrix_desc, prepacked_size, prepack, prepack_scales
                linear_prepacked_size, linear_prepack, linear, linear_workspace_size, unpack_codes,
                linear_unpack_codes)
 
-TORCH_ACT = {"bf16": torch.bfloat16, "f16": torch.float16}
+TORCH_ACT = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}
 
 
 def to_device_bits(a: np.ndarray, dtype: str = None, device="cuda") -> torch.Tensor:
     """uint16 bit patterns -> a device tensor of that dtype (bf16/f16), or uint8 bytes."""
     if a is None:
         return None
+    if a.dtype == np.float32:  # f32 activations are carried as values
+        return torch.from_numpy(np.ascontiguousarray(a)).to(device)
     if a.dtype == np.uint8:
         return torch.from_numpy(np.ascontiguousarray(a)).to(device)
     t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device)
@@ -27,6 +29,9 @@ def to_device_bits(a: np.ndarray, dtype: str = None, device="cuda") -> torch.Ten
 
 
 def bits_of(t: torch.Tensor) -> np.ndarray:
+    """uint16 bit patterns of a bf16/f16 tensor; float32 values of an f32 one."""
+    if t.dtype == torch.float32:
+        return t.detach().contiguous().cpu().numpy()
     return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
 
 

@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_abi_version():
-    assert q.abi_version() == 5
+    assert q.abi_version() == 6
 
 
 def _desc(**kw):
@@ -54,7 +54,7 @@ def test_prepacked_size_matches_layout():
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(E=0), 1), (dict(E=257), 2), (dict(act="f32"), 2),
+    (dict(E=0), 1), (dict(E=257), 2),
     (dict(fc1=("sym_int4", 32, "bf16")), 2), (dict(fc1=("sym_int4", 96, "bf16")), 2),
     (dict(H=2000), 2), (dict(I=1400), 2),
     (dict(fc1=("sym_int4", 64, "f32")), 2),
@@ -265,3 +265,23 @@ def test_prepack_scales_validation():
     assert L.qmoe_prepack_scales(C.byref(d), fake, None, fake, None, fake, need - 1, None) == 3
     da = _desc(fc1=("affine_int2", 128, "f16"))
     assert L.qmoe_prepack_scales(C.byref(da), fake, None, fake, None, fake, q.prepacked_size(da), None) == 1
+
+
+def test_plan_f32_activations():
+    """f32 activations: a split pass first, y from the combine (also for
+    top-1), GEMV path only."""
+    d = _desc(act="f32")
+    assert q.forward_plan(d, 1, 6)["kernels"] == ["split_x", "route_fc1_swiglu", "gemv_fc2", "combine"]
+    assert q.forward_plan(d, 8, 6)["kernels"] == ["split_x", "route", "gemv_fc1_swiglu", "gemv_fc2", "combine"]
+    p1 = q.forward_plan(d, 1, 1)
+    assert p1["kernels"] == ["split_x", "route_fc1_swiglu", "gemv_fc2", "combine"] and p1["num_launches"] == 4
+    b = q.forward_plan(_desc(), 4, 6)["workspace_bytes"]
+    assert q.forward_plan(d, 4, 6)["workspace_bytes"] == b + 2 * (4 * 2048 * 2)   # x hi + lo rows
+    for T, path in ((17, "auto"), (4, "grouped")):
+        with pytest.raises(q.QmoeError) as ei:
+            q.forward_plan(d, T, 6, path)
+        assert ei.value.status == 2
+    L = q.lib()
+    fake = C.c_void_p(0x100000)
+    o = q.ForwardOpts(0, 0, None, None, None, None, None, 0, 0, fake, None, 0, 0, 0)   # expert bias
+    assert L.qmoe_forward_ex(C.byref(d), fake, fake, fake, 4, 6, fake, fake, 1 << 30, None, C.byref(o)) == 2

@@ -496,3 +496,46 @@ def test_graph_replays_match_eager(name, T, path):
         torch.cuda.synchronize()
         assert np.array_equal(got, ref), f"replay {rep} differs from eager"
     log("       3 replays equal to eager")
+
+
+# ------------------------------------------------------- f32 activations
+def _f32(spec):
+    import dataclasses
+    return dataclasses.replace(spec, act_dtype="f32", name=spec.name + "_f32")
+
+
+@pytest.mark.parametrize("T", [1, 4, 6, 8])
+def test_f32_activations_dsv2lite(T):
+    """f32 x and y on the decode path (x split into bf16 hi + lo for the
+    matrix cores), the token counts of the pages' f16/bf16/f32 decode matrix."""
+    run_case(_f32(synth.MOE_WORKLOADS["dsv2lite_int4"]), T, 2)
+
+
+def test_f32_activations_switch_top1():
+    """Top-1 with f32 y: FC2 writes o and the combine rounds to f32."""
+    run_case(_f32(synth.MOE_WORKLOADS["switch_base_ternary"]), 1, 2)
+
+
+@pytest.mark.parametrize("cfg", [SWEEP[1], SWEEP[3], SWEEP[4]], ids=["int2-int4", "affine", "affine-int4-b128"])
+@pytest.mark.parametrize("T", [2, 16])
+def test_f32_activations_sweep(cfg, T):
+    run_case(custom_moe_spec(**{**cfg, "act_dtype": "f32"}), T, 60 + T)
+
+
+def test_f32_activations_unnormalised_weights_and_tiling():
+    """f32 with unnormalised top-k weights, then in row tiles of 4 tokens."""
+    spec = custom_moe_spec(E=8, H=256, I=128, top_k=3, fc1="sym_int4", act_dtype="f32")
+    run_case(spec, 5, 71, topk_weights="softmax_all")
+    import skinny_gemm_amd as q
+    inp = synth.moe_inputs(spec, 14, 72)
+    from skinny_gemm_amd.layer import MoeLayer
+    d = MoeLayer.from_spec(spec, inp).desc
+    limit = q.forward_plan(d, 14, 3)["workspace_bytes"] // 3
+    plan = q.forward_plan(d, 14, 3, workspace_limit=limit)
+    log(f"[f32 tiling] row_tile={plan['row_tile']} tiles={plan['num_tiles']}")
+    assert plan["num_tiles"] > 1
+    _, _, _, y, _ = _tiled_run(spec, inp, 14, limit)
+    ref = oracle.moe(inp)
+    res = compare(y, ref["y"], ref["y64"], "f32")
+    log(f"       y: max_row_rel={res['max_row_rel']:.3e}")
+    assert res["ok"], res
