@@ -5,13 +5,15 @@
  *
  *   route    ids[t][0..k-1] = the k experts with the largest router logits
  *            (ties to the lower expert index, ordered by descending logit);
- *            w[t][j] = softmax of those k logits, so sum_j w[t][j] = 1.
+ *            w[t][j] = softmax of those k logits, so sum_j w[t][j] = 1 (or,
+ *            as an option, the selected entries of the softmax over all E
+ *            logits: qmoe_topk_weights).
  *   expand   tokens grouped by expert: per-expert row counts, exclusive
  *            offsets and a stable row list of flat slots r = t*k + j.
- *   FC1      a = W1[e] x[t], W1[e] is [2I][H] with gate/up rows interleaved:
- *            row 2i is gate_i, row 2i+1 is up_i.
+ *   FC1      a = W1[e] x[t] (+ an optional per-expert bias), W1[e] is [2I][H]
+ *            with gate/up rows interleaved: row 2i is gate_i, row 2i+1 is up_i.
  *   SwiGLU   h_i = silu(a[2i]) * a[2i+1],  silu(g) = g / (1 + exp(-g)).
- *   FC2      o = W2[e] h, W2[e] is [H][I].
+ *   FC2      o = W2[e] h (+ an optional per-expert bias), W2[e] is [H][I].
  *   combine  y[t] = sum_j w[t][j] * o_(t,j), summed in fp32, rounded once
  *            (nearest-even) to the activation dtype.
  *
@@ -34,7 +36,8 @@
  *     bits) with W as [N][K], affine groups of 128, ternary as affine.
  *   - onnx-genai pull request 1167 ("QMoE gate/up SwiGLU expert-GEMV
  *     occupancy lever"): the fused gate/up SwiGLU expert GEMV and the
- *     separate down-projection GEMV.
+ *     separate down-projection GEMV; Parity: f16, bf16 and f32 activations
+ *     on the decode GEMV.
  *
  * Canonical input format (what qmoe_prepack / qmoe_linear_prepack read):
  *   codes   [E][N][K*bits/8] bytes; within a byte, fields run LSB-first along
@@ -200,7 +203,7 @@ const char *qmoe_last_error(void);
 
 /* Bytes of the opaque prepacked buffer for `desc` (host call, no device work).
  * Errors: INVALID_ARGUMENT (null, inconsistent shapes), UNSUPPORTED (qtype,
- * block not in {64,128}, E > 256, dims not multiples of 64, f32 dtypes). */
+ * block not in {64,128}, E > 256, dims not multiples of 64, f32 scales). */
 qmoe_status qmoe_prepacked_size(const qmoe_layer_desc *desc, size_t *bytes);
 
 /* Rearranges canonical codes and scales (device pointers, layout above) into
@@ -228,7 +231,9 @@ qmoe_status qmoe_prepack_scales(const qmoe_layer_desc *desc, const void *fc1_sca
                                 size_t packed_bytes, void *stream);
 
 /* Worst-case workspace bytes of one forward call with T tokens and top_k
- * (host call).  top_k in [1, min(E, 16)], T >= 0, T*top_k <= INT32_MAX. */
+ * (host call).  top_k in [1, min(E, 16)], T >= 0, T*top_k <= INT32_MAX.
+ * With row tiling (qmoe_forward_opts.workspace_limit) a call needs only the
+ * tile workspace that qmoe_forward_plan reports. */
 qmoe_status qmoe_workspace_size(const qmoe_layer_desc *desc, int32_t T, int32_t top_k,
                                 size_t *bytes);
 
@@ -240,8 +245,11 @@ qmoe_status qmoe_forward(const qmoe_layer_desc *desc, const void *packed, const 
                          const float *logits, int32_t T, int32_t top_k, void *y,
                          void *ws, size_t ws_bytes, void *stream);
 
-/* qmoe_forward with explicit path choice and optional diagnostic outputs
- * (opts may be NULL).  UNSUPPORTED if path = GEMV and T > 16. */
+/* qmoe_forward with the options of qmoe_forward_opts: path choice,
+ * diagnostic outputs, stage events, expert biases, routing-weight mode and
+ * row tiling (opts may be NULL: the defaults of qmoe_forward).  UNSUPPORTED
+ * if path = GEMV and T > 16, and for f32 activations where the grouped path
+ * would run. */
 qmoe_status qmoe_forward_ex(const qmoe_layer_desc *desc, const void *packed, const void *x,
                             const float *logits, int32_t T, int32_t top_k, void *y,
                             void *ws, size_t ws_bytes, void *stream,
@@ -251,7 +259,8 @@ qmoe_status qmoe_forward_ex(const qmoe_layer_desc *desc, const void *packed, con
 qmoe_status qmoe_forward_plan(const qmoe_layer_desc *desc, int32_t T, int32_t top_k,
                               const qmoe_forward_opts *opts, qmoe_plan *plan);
 
-/* Routing alone, with the same kernels as the forward (bit-exact checks).
+/* Routing alone, with the same kernels as the forward (bit-exact checks),
+ * renormalised weights.
  * logits [T][E] fp32 -> ids [T][k] int32, w [T][k] fp32, counts [E],
  * offsets [E+1] (exclusive scan), row_list [T*k] (slots t*k+j grouped by
  * expert, ascending within an expert).  ws >= qmoe_route_workspace_size. */
@@ -275,7 +284,8 @@ qmoe_status qmoe_linear_prepack(const qmoe_qmatrix_desc *desc, const void *codes
                                 const void *scales, const void *biases, void *dst,
                                 size_t dst_bytes, void *stream);
 qmoe_status qmoe_linear_workspace_size(const qmoe_qmatrix_desc *desc, int32_t M, size_t *bytes);
-/* path: QMOE_PATH_AUTO, GEMV (M <= 16) or GROUPED (MFMA tiles, any M >= 1). */
+/* path: QMOE_PATH_AUTO, GEMV (M <= 32) or GROUPED (MFMA tiles, any M >= 1);
+ * x_dtype BF16 or F16. */
 qmoe_status qmoe_linear(const qmoe_qmatrix_desc *desc, const void *packed, const void *x,
                         int32_t x_dtype, int32_t M, void *y, void *ws, size_t ws_bytes,
                         int32_t path, void *stream);
