@@ -58,7 +58,7 @@ def lib():
         L.orc_silu.argtypes = [C.c_double]
         L.orc_moe.restype = C.c_int
         L.orc_moe.argtypes = ([C.c_int] * 5 + [C.c_int] * 3 + [P] * 3 + [C.c_int] * 3 + [P] * 3
-                              + [P, P, C.c_int] + [P, P, C.c_int] + [P] * 5)
+                              + [P, P, C.c_int, C.c_int] + [P, P, C.c_int] + [P] * 5)
         L.orc_linear.argtypes = [C.c_int, C.c_int, C.c_int, P, P, P, i64, i64, P, C.c_int, C.c_int,
                                  i64, i64, P, P]
         _lib = L
@@ -155,7 +155,7 @@ def moe(inp: dict, debug: bool = False, tokens=None, renorm: bool = True):
     y16 = np.empty((T, H), dtype=adt)
     a = h = o = None
     if debug:
-        a = np.empty((T * k, 2 * I), dtype=np.float64)
+        a = np.empty((T * k, I if sp.activation == "relu" else 2 * I), dtype=np.float64)
         h = np.empty((T * k, I), dtype=np.float64)
         o = np.empty((T * k, H), dtype=np.float64)
     arr = {n: _c(inp[n], np.uint8 if n.endswith("codes") else np.uint16)
@@ -167,7 +167,7 @@ def moe(inp: dict, debug: bool = False, tokens=None, renorm: bool = True):
         _p(arr["fc1_codes"]), _p(arr["fc1_scales"]), _p(arr["fc1_biases"]),
         FMT[sp.fc2.fmt], sp.fc2.block, DT[sp.fc2.scale_dtype],
         _p(arr["fc2_codes"]), _p(arr["fc2_scales"]), _p(arr["fc2_biases"]),
-        _p(eb["fc1_expert_bias"]), _p(eb["fc2_expert_bias"]), int(bool(renorm)),
+        _p(eb["fc1_expert_bias"]), _p(eb["fc2_expert_bias"]), int(bool(renorm)), int(sp.activation == "relu"),
         _p(x), _p(lg), T, _p(y64), _p(y16), _p(a), _p(h), _p(o))
     out = {"y64": y64, "y": y16, "status": rc}
     if debug:

@@ -259,15 +259,17 @@ static void orc_matvec(const orc_mat *m, int64_t e, int64_t N, int64_t K, const 
  * added to FC1's output before the SwiGLU, and fc2_ebias [E][H] to FC2's
  * output before the top-k weighting (onnxruntime pull request 33005,
  * Description: expert bias before the SwiGLU, FC2 bias in the finalize).
- * Returns 0, or -1 if a ternary row it used holds the invalid field value 3
- * (read as 0).  renorm selects the routing weights as in orc_route.
+ * With relu, FC1 is a single [I][H] matrix and h = max(a, 0) (the Switch
+ * Transformer FFN); a_dbg and fc1_ebias then have I entries per slot /
+ * expert.  Returns 0, or -1 if a ternary row it used holds the invalid field
+ * value 3 (read as 0).  renorm selects the routing weights as in orc_route.
  */
 int orc_moe(int E, int H, int I, int k, int act_dtype,
             int fc1_fmt, int fc1_block, int fc1_sdtype,
             const uint8_t *fc1_codes, const uint16_t *fc1_scales, const uint16_t *fc1_biases,
             int fc2_fmt, int fc2_block, int fc2_sdtype,
             const uint8_t *fc2_codes, const uint16_t *fc2_scales, const uint16_t *fc2_biases,
-            const void *fc1_ebias, const void *fc2_ebias, int renorm,
+            const void *fc1_ebias, const void *fc2_ebias, int renorm, int relu,
             const void *x, const float *logits, int T,
             double *y64, void *y_out, double *a_dbg, double *h_dbg, double *o_dbg) {
   orc_mat w1 = {fc1_fmt, fc1_block, fc1_sdtype, fc1_codes, fc1_scales, fc1_biases};
@@ -279,7 +281,8 @@ int orc_moe(int E, int H, int I, int k, int act_dtype,
   int32_t *offsets = (int32_t *)malloc(sizeof(int32_t) * (size_t)(E + 1));
   int32_t *rows = (int32_t *)malloc(sizeof(int32_t) * (size_t)(S > 0 ? S : 1));
   double *xv = (double *)malloc(sizeof(double) * (size_t)H);
-  double *a = (double *)malloc(sizeof(double) * (size_t)(2 * I));
+  const int64_t R1 = relu ? (int64_t)I : 2 * (int64_t)I;  /* FC1 rows */
+  double *a = (double *)malloc(sizeof(double) * (size_t)R1);
   double *h = (double *)malloc(sizeof(double) * (size_t)I);
   double *o = (double *)malloc(sizeof(double) * (size_t)H);
   double *wrow = (double *)malloc(sizeof(double) * (size_t)(H > I ? H : I));
@@ -292,16 +295,18 @@ int orc_moe(int E, int H, int I, int k, int act_dtype,
     for (int j = 0; j < k; ++j) {
       const int64_t r = (int64_t)t * k + j;
       const int e = ids[r];
-      orc_matvec(&w1, e, 2 * (int64_t)I, H, xv, a, wrow, &bad);
+      orc_matvec(&w1, e, R1, H, xv, a, wrow, &bad);
       if (fc1_ebias)
-        for (int64_t n = 0; n < 2 * I; ++n)
-          a[n] += orc_act(fc1_ebias, (int64_t)e * 2 * I + n, act_dtype);
-      for (int64_t i = 0; i < I; ++i) h[i] = orc_silu(a[2 * i]) * a[2 * i + 1];
+        for (int64_t n = 0; n < R1; ++n) a[n] += orc_act(fc1_ebias, (int64_t)e * R1 + n, act_dtype);
+      if (relu)
+        for (int64_t i = 0; i < I; ++i) h[i] = a[i] > 0.0 ? a[i] : 0.0;
+      else
+        for (int64_t i = 0; i < I; ++i) h[i] = orc_silu(a[2 * i]) * a[2 * i + 1];
       orc_matvec(&w2, e, H, I, h, o, wrow, &bad);
       if (fc2_ebias)
         for (int64_t n = 0; n < H; ++n) o[n] += orc_act(fc2_ebias, (int64_t)e * H + n, act_dtype);
       for (int64_t n = 0; n < H; ++n) yt[n] += wts[r] * o[n];
-      if (a_dbg) memcpy(a_dbg + r * 2 * I, a, sizeof(double) * (size_t)(2 * I));
+      if (a_dbg) memcpy(a_dbg + r * R1, a, sizeof(double) * (size_t)R1);
       if (h_dbg) memcpy(h_dbg + r * I, h, sizeof(double) * (size_t)I);
       if (o_dbg) memcpy(o_dbg + r * H, o, sizeof(double) * (size_t)H);
     }

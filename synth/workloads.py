@@ -77,6 +77,11 @@ class MoeSpec:
     logit_bias: bool = False
     scale_sigma: float = 0.02
     bias_sigma: float = 0.01
+    activation: str = "swiglu"  # or "relu": FC1 is one [I][H] matrix, h = max(a, 0)
+
+    @property
+    def fc1_rows(self) -> int:
+        return self.I if self.activation == "relu" else 2 * self.I
 
 
 @dataclass(frozen=True)
@@ -163,7 +168,7 @@ def moe_inputs(spec: MoeSpec, T: int, seed: int = 0, logits_mode: str = "iid",
     are equal and the selection depends on the tie rule.
     weight_copy selects an independent set of expert weights (distinct copies
     for cache-cold timing); activations and logits do not depend on it.
-    expert_bias > 0 adds per-expert output biases of FC1 ([E][2I]) and FC2
+    expert_bias > 0 adds per-expert output biases of FC1 ([E][fc1 rows]) and FC2
     ([E][H]), N(0, expert_bias^2) in the activation dtype; otherwise both are
     None.
     """
@@ -172,15 +177,15 @@ def moe_inputs(spec: MoeSpec, T: int, seed: int = 0, logits_mode: str = "iid",
     if weights:
         wtag = "" if weight_copy == 0 else f"@copy{weight_copy}"
         out["fc1_codes"], out["fc1_scales"], out["fc1_biases"] = _matrix(
-            wl, "fc1" + wtag, seed, spec.fc1, spec.E, 2 * spec.I, spec.H, spec.scale_sigma, spec.bias_sigma)
+            wl, "fc1" + wtag, seed, spec.fc1, spec.E, spec.fc1_rows, spec.H, spec.scale_sigma, spec.bias_sigma)
         out["fc2_codes"], out["fc2_scales"], out["fc2_biases"] = _matrix(
             wl, "fc2" + wtag, seed, spec.fc2, spec.E, spec.H, spec.I, spec.scale_sigma, spec.bias_sigma)
     out["fc1_expert_bias"] = out["fc2_expert_bias"] = None
     if expert_bias > 0:
         wtag = "" if weight_copy == 0 else f"@copy{weight_copy}"
-        b1 = expert_bias * normals(Key(seed, wl, "fc1_expert_bias" + wtag), spec.E * 2 * spec.I)
+        b1 = expert_bias * normals(Key(seed, wl, "fc1_expert_bias" + wtag), spec.E * spec.fc1_rows)
         b2 = expert_bias * normals(Key(seed, wl, "fc2_expert_bias" + wtag), spec.E * spec.H)
-        out["fc1_expert_bias"] = _to_bits(b1, spec.act_dtype).reshape(spec.E, 2 * spec.I)
+        out["fc1_expert_bias"] = _to_bits(b1, spec.act_dtype).reshape(spec.E, spec.fc1_rows)
         out["fc2_expert_bias"] = _to_bits(b2, spec.act_dtype).reshape(spec.E, spec.H)
     x = normals(Key(seed, wl, f"x[T={T}]"), T * spec.H)
     out["x"] = _to_bits(x, spec.act_dtype).reshape(T, spec.H)
@@ -215,13 +220,16 @@ def linear_inputs(spec: LinearSpec, N: int, M: int, seed: int = 0, weight_copy: 
 
 def custom_moe_spec(E: int, H: int, I: int, top_k: int, fc1: str = "sym_int4", fc2: Optional[str] = None,
                     block1: int = 64, block2: Optional[int] = None, scale_dtype: str = "bf16",
-                    act_dtype: str = "bf16", logit_bias: bool = False, name: Optional[str] = None) -> MoeSpec:
+                    act_dtype: str = "bf16", logit_bias: bool = False, name: Optional[str] = None,
+                    activation: str = "swiglu") -> MoeSpec:
     """A small MoE layer of the same recipe, for parity sweeps over shapes."""
     fc2 = fc2 or fc1
     block2 = block2 or block1
-    nm = name or f"custom_E{E}_H{H}_I{I}_k{top_k}_{fc1}{block1}_{fc2}{block2}_{scale_dtype}_{act_dtype}"
+    nm = name or (f"custom_E{E}_H{H}_I{I}_k{top_k}_{fc1}{block1}_{fc2}{block2}_{scale_dtype}_{act_dtype}"
+                  + ("" if activation == "swiglu" else f"_{activation}"))
     return MoeSpec(nm, E=E, H=H, I=I, top_k=top_k, fc1=MatFmt(fc1, block1, scale_dtype),
-                   fc2=MatFmt(fc2, block2, scale_dtype), act_dtype=act_dtype, logit_bias=logit_bias)
+                   fc2=MatFmt(fc2, block2, scale_dtype), act_dtype=act_dtype, logit_bias=logit_bias,
+                   activation=activation)
 
 
 def custom_linear_spec(K: int, fmt: str = "affine_int2", block: int = 128, scale_dtype: str = "f16",

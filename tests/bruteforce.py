@@ -74,8 +74,11 @@ def moe_dense(inp: dict, renorm: bool = True) -> np.ndarray:
         a = x @ W1.T
         if inp.get("fc1_expert_bias") is not None:
             a = a + half_bits_to_f64(inp["fc1_expert_bias"][e], sp.act_dtype)[None, :]
-        gate, up = a[:, 0::2], a[:, 1::2]
-        h = gate / (1.0 + np.exp(-gate)) * up
+        if getattr(sp, "activation", "swiglu") == "relu":
+            h = np.maximum(a, 0.0)
+        else:
+            gate, up = a[:, 0::2], a[:, 1::2]
+            h = gate / (1.0 + np.exp(-gate)) * up
         o = h @ W2.T
         if inp.get("fc2_expert_bias") is not None:
             o = o + half_bits_to_f64(inp["fc2_expert_bias"][e], sp.act_dtype)[None, :]

@@ -293,6 +293,36 @@ def test_moe_unnormalised_weights_vs_dense_bruteforce(oracle_lib, cfg):
     assert not np.allclose(out["y64"], oracle_lib.moe(inp)["y64"])
 
 
+RELU = [dict(E=4, H=128, I=128, top_k=2, fc1="sym_int4", activation="relu"),
+        dict(E=3, H=128, I=256, top_k=1, fc1="ternary", block1=128, scale_dtype="f16", activation="relu")]
+
+
+@pytest.mark.parametrize("cfg", RELU, ids=["int4-k2", "ternary-k1"])
+@pytest.mark.parametrize("bias", [0.0, 0.1])
+def test_moe_relu_ffn_vs_dense_bruteforce(oracle_lib, cfg, bias):
+    spec = custom_moe_spec(**cfg)
+    inp = synth.moe_inputs(spec, T=3, seed=41, expert_bias=bias)
+    assert inp["fc1_codes"].shape[1] == spec.I                    # one [I][H] matrix
+    out = oracle_lib.moe(inp, debug=True)
+    ref = bf.moe_dense(inp)
+    assert np.allclose(out["y64"], ref, rtol=1e-10, atol=1e-12 * np.abs(ref).max())
+    assert np.array_equal(out["h"], np.maximum(out["a"], 0.0)) and np.any(out["h"] == 0.0)
+
+
+def test_moe_relu_zero_weights_closed_form(oracle_lib):
+    # all codes 0: a = b1, so h = max(b1, 0) and y = sum_j w_j * b2[e_j]
+    spec = custom_moe_spec(E=5, H=64, I=64, top_k=2, activation="relu")
+    inp = synth.moe_inputs(spec, T=3, seed=8, expert_bias=0.1)
+    inp["fc1_codes"] = np.full_like(inp["fc1_codes"], 0x88)
+    inp["fc2_codes"] = np.full_like(inp["fc2_codes"], 0x88)
+    out = oracle_lib.moe(inp, debug=True)
+    r = oracle_lib.route(inp["logits"], 2)
+    b1 = bf.half_bits_to_f64(inp["fc1_expert_bias"], "bf16")
+    b2 = bf.half_bits_to_f64(inp["fc2_expert_bias"], "bf16")
+    assert np.array_equal(out["h"], np.maximum(b1[r["ids"].ravel()], 0.0))
+    assert np.allclose(out["y64"], (r["w"][:, :, None] * b2[r["ids"]]).sum(axis=1), rtol=1e-14, atol=1e-16)
+
+
 def test_moe_expert_bias_zero_weights_closed_form(oracle_lib):
     # all codes 0: FC1's output is its bias, so h = silu(b_gate) * b_up with the
     # gate in even rows, and y = sum_j w_j * b2[e_j]
