@@ -65,13 +65,13 @@ def parse():
 # ------------------------------------------------------------------ helpers
 def expert_bytes(spec) -> int:
     import synth
-    return (synth.canonical_matrix_bytes(spec.fc1, 2 * spec.I, spec.H)
+    return (synth.canonical_matrix_bytes(spec.fc1, spec.fc1_rows, spec.H)
             + synth.canonical_matrix_bytes(spec.fc2, spec.H, spec.I))
 
 
 def fc1_bytes(spec) -> int:
     import synth
-    return synth.canonical_matrix_bytes(spec.fc1, 2 * spec.I, spec.H)
+    return synth.canonical_matrix_bytes(spec.fc1, spec.fc1_rows, spec.H)
 
 
 def targeted_logits(logits: np.ndarray, targets: np.ndarray) -> np.ndarray:
@@ -459,6 +459,15 @@ def main():
     del b, layers
     torch.cuda.empty_cache()
     if not args.no_extras:
+        # the same layer with the Switch Transformer's own ReLU FFN (FC1 one [I][H] matrix)
+        import dataclasses
+        rspec = dataclasses.replace(spec, activation="relu", name=spec.name + "_relu")
+        layr, ir = make_layers(rspec, args.rotate_bytes)
+        r, bb = bench_moe(rspec, T, args.steps, args.warmup, 3, layr, ir)
+        variants[f"{rspec.name}_T{T}"] = {k: r[k] for k in ("us_per_layer", "effective_GBps", "stage_us")}
+        log(f"[bench] variants {json.dumps(variants)}")
+        del bb, layr
+        torch.cuda.empty_cache()
         extras = {}
         d3 = synth.MOE_WORKLOADS["dsv2lite_int4"]
         extras["dsv2lite_int4"] = []

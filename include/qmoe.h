@@ -12,7 +12,8 @@
  *            offsets and a stable row list of flat slots r = t*k + j.
  *   FC1      a = W1[e] x[t] (+ an optional per-expert bias), W1[e] is [2I][H]
  *            with gate/up rows interleaved: row 2i is gate_i, row 2i+1 is up_i.
- *   SwiGLU   h_i = silu(a[2i]) * a[2i+1],  silu(g) = g / (1 + exp(-g)).
+ *   SwiGLU   h_i = silu(a[2i]) * a[2i+1],  silu(g) = g / (1 + exp(-g))
+ *            (or ReLU, h_i = max(a_i, 0) over a single [I][H] FC1: qmoe_activation).
  *   FC2      o = W2[e] h (+ an optional per-expert bias), W2[e] is [H][I].
  *   combine  y[t] = sum_j w[t][j] * o_(t,j), summed in fp32, rounded once
  *            (nearest-even) to the activation dtype.
@@ -73,7 +74,7 @@
 extern "C" {
 #endif
 
-#define QMOE_ABI_VERSION 6
+#define QMOE_ABI_VERSION 7
 
 typedef enum qmoe_status {
   QMOE_OK = 0,
@@ -113,7 +114,17 @@ typedef struct qmoe_qmatrix_desc {
   int64_t cols;        /* K, a positive multiple of 64 and of block */
 } qmoe_qmatrix_desc;
 
-/* One MoE layer.  fc1 must be [2*inter][hidden], fc2 [hidden][inter]. */
+/* Expert FFN activation.  SWIGLU: FC1 is [2I][H] with interleaved gate/up
+   rows and h_i = silu(a[2i]) * a[2i+1].  RELU: the single-matrix FFN of the
+   Switch Transformer family (QMoE gotcha page, on the SwitchTransformer
+   expert shapes): FC1 is [I][H] and h_i = max(a_i, 0). */
+typedef enum qmoe_activation {
+  QMOE_ACT_SWIGLU = 0,
+  QMOE_ACT_RELU = 1
+} qmoe_activation;
+
+/* One MoE layer.  fc1 must be [2*inter][hidden] (SWIGLU) or [inter][hidden]
+   (RELU), fc2 [hidden][inter]. */
 typedef struct qmoe_layer_desc {
   int32_t num_experts; /* E in [1, 256] */
   int32_t hidden;      /* H */
@@ -125,6 +136,8 @@ typedef struct qmoe_layer_desc {
                           f32, and no expert biases (QMOE_ERR_UNSUPPORTED) */
   qmoe_qmatrix_desc fc1;
   qmoe_qmatrix_desc fc2;
+  int32_t activation;  /* qmoe_activation */
+  int32_t reserved;    /* must be 0 */
 } qmoe_layer_desc;
 
 /* Routing weights of the k selected experts of a token (top-k by logit, ties
@@ -270,7 +283,7 @@ qmoe_status qmoe_route(int32_t T, int32_t E, int32_t top_k, const float *logits,
                        int32_t *row_list, void *ws, size_t ws_bytes, void *stream);
 
 /* Diagnostic: read the prepacked layout back to integer codes.  which = 1
- * for FC1 ([E][2I][H]), 2 for FC2 ([E][H][I]); codes_out int8, device. */
+ * for FC1 ([E][fc1.rows][H]), 2 for FC2 ([E][H][I]); codes_out int8, device. */
 qmoe_status qmoe_unpack_codes(const qmoe_layer_desc *desc, const void *packed, int32_t which,
                               int8_t *codes_out, void *stream);
 

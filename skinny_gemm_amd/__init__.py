@@ -36,7 +36,8 @@ class QMatrixDesc(C.Structure):
 
 class LayerDesc(C.Structure):
     _fields_ = [("num_experts", C.c_int32), ("hidden", C.c_int32), ("inter", C.c_int32),
-                ("act_dtype", C.c_int32), ("fc1", QMatrixDesc), ("fc2", QMatrixDesc)]
+                ("act_dtype", C.c_int32), ("fc1", QMatrixDesc), ("fc2", QMatrixDesc),
+                ("activation", C.c_int32), ("reserved", C.c_int32)]
 
 
 class ForwardOpts(C.Structure):
@@ -130,10 +131,14 @@ def qmatrix_desc(fmt: str, block: int, scale_dtype: str, rows: int, cols: int) -
     return QMatrixDesc(QTYPE[fmt], block, DTYPE[scale_dtype], 0, rows, cols)
 
 
-def layer_desc(E: int, H: int, I: int, act_dtype: str, fc1, fc2) -> LayerDesc:
-    """fc1/fc2 = (fmt, block, scale_dtype)."""
-    return LayerDesc(E, H, I, DTYPE[act_dtype], qmatrix_desc(fc1[0], fc1[1], fc1[2], 2 * I, H),
-                     qmatrix_desc(fc2[0], fc2[1], fc2[2], H, I))
+ACTIVATION = {"swiglu": 0, "relu": 1}
+
+
+def layer_desc(E: int, H: int, I: int, act_dtype: str, fc1, fc2, activation: str = "swiglu") -> LayerDesc:
+    """fc1/fc2 = (fmt, block, scale_dtype); FC1 has 2I rows (SwiGLU) or I (ReLU)."""
+    rows1 = I if activation == "relu" else 2 * I
+    return LayerDesc(E, H, I, DTYPE[act_dtype], qmatrix_desc(fc1[0], fc1[1], fc1[2], rows1, H),
+                     qmatrix_desc(fc2[0], fc2[1], fc2[2], H, I), ACTIVATION[activation], 0)
 
 
 # ------------------------------------------------------------------- MoE

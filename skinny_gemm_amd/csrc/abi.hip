@@ -77,7 +77,11 @@ qmoe_status check_layer(const qmoe_layer_desc *d) {
     return fail(QMOE_ERR_INVALID_ARGUMENT, "hidden and inter must be positive");
   if (d->act_dtype != QMOE_DTYPE_BF16 && d->act_dtype != QMOE_DTYPE_F16 && d->act_dtype != QMOE_DTYPE_F32)
     return fail(QMOE_ERR_UNSUPPORTED, "activation dtype %d not supported (bf16, f16 or f32)", d->act_dtype);
-  qmoe_status st = check_matrix(d->fc1, "fc1", 2 * (int64_t)d->inter, d->hidden);
+  if (d->activation != QMOE_ACT_SWIGLU && d->activation != QMOE_ACT_RELU)
+    return fail(QMOE_ERR_INVALID_ARGUMENT, "activation %d is not a qmoe_activation value", d->activation);
+  if (d->reserved != 0) return fail(QMOE_ERR_INVALID_ARGUMENT, "layer reserved field must be 0");
+  const int64_t fc1_rows = d->activation == QMOE_ACT_RELU ? (int64_t)d->inter : 2 * (int64_t)d->inter;
+  qmoe_status st = check_matrix(d->fc1, "fc1", fc1_rows, d->hidden);
   if (st != QMOE_OK) return st;
   return check_matrix(d->fc2, "fc2", d->hidden, d->inter);
 }
@@ -287,8 +291,8 @@ qmoe_status make_plan(const qmoe_layer_desc &d, int32_t T, int32_t k, int path_r
     p.route_fused = (T <= 16) ? 1 : 0;
     p.max_tiles = (int)grouped_max_tiles((int64_t)T * k, d.num_experts);
     p.softmax_all = softmax_all;
-    p.kernels = std::string("route,") + (softmax_all ? "route_weights," : "") +
-                "rowscale,grouped_fc1_swiglu,grouped_fc2,combine";
+    p.kernels = std::string("route,") + (softmax_all ? "route_weights," : "") + "rowscale,grouped_fc1_" +
+                (d.activation == QMOE_ACT_RELU ? "relu" : "swiglu") + ",grouped_fc2,combine";
     p.launches = (p.route_fused ? 1 : 2) + 4 + (softmax_all ? 1 : 0);
     return ok();
   }
@@ -312,7 +316,8 @@ qmoe_status make_plan(const qmoe_layer_desc &d, int32_t T, int32_t k, int path_r
   p.softmax_all = softmax_all;
   // f32 activations: a split pass first, and y always from the combine
   const bool combine = k > 1 || f32;
-  p.kernels = std::string(f32 ? "split_x," : "") + (p.fc1_routes ? "route_fc1_swiglu" : "route,gemv_fc1_swiglu") +
+  const std::string act = d.activation == QMOE_ACT_RELU ? "relu" : "swiglu";
+  p.kernels = std::string(f32 ? "split_x," : "") + (p.fc1_routes ? "route_fc1_" + act : "route,gemv_fc1_" + act) +
               (softmax_all ? ",route_weights" : "") + ",gemv_fc2" + (combine ? ",combine" : "");
   p.launches = (p.fc1_routes ? 2 : 3) + (combine ? 1 : 0) + (softmax_all ? 1 : 0) + (f32 ? 1 : 0);
   return ok();
@@ -711,6 +716,7 @@ qmoe_status qmoe_forward_ex(const qmoe_layer_desc *desc, const void *packed, con
     q1.h_dbg = opts ? opts->h_out : nullptr;
     q1.row_list = ra.r.row_list;
     q1.bias = opts ? (const uint16_t *)opts->fc1_bias : nullptr;
+    q1.relu = desc->activation == QMOE_ACT_RELU;
     q1.act_dtype = desc->act_dtype;
     e = begin();
     if (e == hipSuccess) e = launch_grouped(q1, kGEpiSwiGLU, p.max_tiles, s);
@@ -759,6 +765,7 @@ qmoe_status qmoe_forward_ex(const qmoe_layer_desc *desc, const void *packed, con
   g1.h_lo = h_lo;
   g1.h_dbg = opts ? opts->h_out : nullptr;
   g1.bias = opts ? (const uint16_t *)opts->fc1_bias : nullptr;
+  g1.relu = desc->activation == QMOE_ACT_RELU;
   g1.act_dtype = desc->act_dtype;
   e = begin();
   if (e == hipSuccess)

@@ -424,13 +424,14 @@ __global__ __launch_bounds__(512) void gemv_kernel(const GemvArgs a) {
     if constexpr (EPI == kEpiStoreAct) {
       if (valid) a.out_act[(int64_t)m * N + n] = f32_to_act(v, a.act_dtype == QMOE_DTYPE_F16);
     } else if constexpr (SWIGLU) {
-      // rows 2i (gate) and 2i+1 (up) sit in neighbouring lanes
+      // SwiGLU: rows 2i (gate) and 2i+1 (up) sit in neighbouring lanes;
+      // ReLU (a.relu): every row is one channel, h = max(a, 0)
       const float up = __shfl_xor(v, 1);
-      if (valid && (lo & 1) == 0) {
+      if (valid && (a.relu || (lo & 1) == 0)) {
         const float gt = v;
-        const float h = gt / (1.f + expf(-gt)) * up;
-        const int64_t Ih = N / 2;
-        const int64_t i = n / 2;
+        const float h = a.relu ? fmaxf(v, 0.f) : gt / (1.f + expf(-gt)) * up;
+        const int64_t Ih = a.relu ? N : N / 2;
+        const int64_t i = a.relu ? n : n / 2;
         const int64_t p = pbase + m;
         const uint16_t hi = f32_to_bf16_rne(h);
         a.h_hi[p * Ih + i] = hi;

@@ -483,12 +483,14 @@ __global__ __launch_bounds__(256) void grouped_kernel(const GroupedArgs a) {
         const float v = fmaf(acc[i][j][el], inv, bv[j]);
         const int64_t n = nw + 16 * j + (lane & 15);
         if constexpr (EPI == kGEpiSwiGLU) {
+          // SwiGLU over neighbouring gate/up lanes, or (a.relu) h = max(a, 0) per row
           const float up = __shfl_xor(v, 1);
-          if (valid && (lane & 1) == 0) {
-            const float h = v / (1.f + expf(-v)) * up;
+          if (valid && (a.relu || (lane & 1) == 0)) {
+            const float h = a.relu ? fmaxf(v, 0.f) : v / (1.f + expf(-v)) * up;
             const int64_t p = p0 + m;
-            a.out_f32[p * (a.N / 2) + n / 2] = h;
-            if (a.h_dbg) a.h_dbg[(int64_t)a.row_list[p] * (a.N / 2) + n / 2] = h;
+            const int64_t Ih = a.relu ? a.N : a.N / 2, i = a.relu ? n : n / 2;
+            a.out_f32[p * Ih + i] = h;
+            if (a.h_dbg) a.h_dbg[(int64_t)a.row_list[p] * Ih + i] = h;
             hmax = fmaxf(hmax, fabsf(h));
           }
         } else if constexpr (EPI == kGEpiStoreF32) {

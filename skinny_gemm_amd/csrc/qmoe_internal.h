@@ -217,7 +217,8 @@ struct GemvArgs {
   float *out_f32;          // kEpiDown: o [p][N]
   uint16_t *out_act;       // kEpiStoreAct: [m][N]; kEpiDown with top-1: y [t][N]
   uint16_t *h_hi, *h_lo;   // kEpiSwiGLU: [p][N/2] bf16 parts of h
-  float *h_dbg;            // kEpiSwiGLU: optional [slot][N/2] fp32
+  float *h_dbg;            // kEpiSwiGLU: optional [slot][N/2] fp32 ([slot][N] with relu)
+  int relu;                // kEpiSwiGLU: the FC1 rows are single ReLU channels, h = max(a, 0)
   const uint16_t *bias;    // kEpiSwiGLU, kEpiDown: optional per-expert output bias [E][N] in act_dtype
   int act_dtype;           // activation dtype of out_act and bias
   const float *route_w;    // kEpiDown: routing weights [T*k]
@@ -302,6 +303,7 @@ struct GroupedArgs {
   const uint16_t *bias;    // routed: optional per-expert output bias [E][N] in act_dtype
   int act_dtype;           // activation dtype of out_act and bias
   float *h_dbg;            // optional fp32 copy of h in slot order
+  int relu;                // kGEpiSwiGLU: h = max(a, 0) per row instead of SwiGLU pairs
   const int32_t *row_list;
 };
 

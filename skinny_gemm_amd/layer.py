@@ -38,9 +38,9 @@ def bits_of(t: torch.Tensor) -> np.ndarray:
 class MoeLayer:
     """One prepacked MoE layer on the current device."""
 
-    def __init__(self, E, H, I, act_dtype, fc1, fc2, arrays: dict, device="cuda"):
+    def __init__(self, E, H, I, act_dtype, fc1, fc2, arrays: dict, device="cuda", activation="swiglu"):
         self.E, self.H, self.I, self.act_dtype = E, H, I, act_dtype
-        self.desc = layer_desc(E, H, I, act_dtype, fc1, fc2)
+        self.desc = layer_desc(E, H, I, act_dtype, fc1, fc2, activation)
         self.device = device
         dev = {k: to_device_bits(arrays[k], None, device) for k in
                ("fc1_codes", "fc1_scales", "fc1_biases", "fc2_codes", "fc2_scales", "fc2_biases")}
@@ -48,7 +48,7 @@ class MoeLayer:
         prepack(self.desc, dev["fc1_codes"], dev["fc1_scales"], dev["fc1_biases"], dev["fc2_codes"],
                 dev["fc2_scales"], dev["fc2_biases"], self.packed)
         del dev
-        # optional per-expert output biases of FC1 [E][2I] and FC2 [E][H]
+        # optional per-expert output biases of FC1 [E][FC1 rows] and FC2 [E][H]
         self.fc1_bias = to_device_bits(arrays.get("fc1_expert_bias"), None, device)
         self.fc2_bias = to_device_bits(arrays.get("fc2_expert_bias"), None, device)
 
@@ -56,7 +56,8 @@ class MoeLayer:
     def from_spec(cls, spec, arrays, device="cuda"):
         return cls(spec.E, spec.H, spec.I, spec.act_dtype,
                    (spec.fc1.fmt, spec.fc1.block, spec.fc1.scale_dtype),
-                   (spec.fc2.fmt, spec.fc2.block, spec.fc2.scale_dtype), arrays, device)
+                   (spec.fc2.fmt, spec.fc2.block, spec.fc2.scale_dtype), arrays, device,
+                   getattr(spec, "activation", "swiglu"))
 
     def update_scales(self, arrays: dict, stream=None):
         """Runtime scales: new fc1/fc2 scales (and affine biases), codes kept."""
@@ -95,7 +96,7 @@ class MoeLayer:
         return (y, dbg) if debug else y
 
     def unpack(self, which: int) -> torch.Tensor:
-        rows, cols = (2 * self.I, self.H) if which == 1 else (self.H, self.I)
+        rows, cols = (self.desc.fc1.rows, self.H) if which == 1 else (self.H, self.I)
         out = torch.empty((self.E, rows, cols), dtype=torch.int8, device=self.device)
         unpack_codes(self.desc, self.packed, which, out)
         return out

@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_abi_version():
-    assert q.abi_version() == 6
+    assert q.abi_version() == 7
 
 
 def _desc(**kw):
@@ -285,3 +285,23 @@ def test_plan_f32_activations():
     fake = C.c_void_p(0x100000)
     o = q.ForwardOpts(0, 0, None, None, None, None, None, 0, 0, fake, None, 0, 0, 0)   # expert bias
     assert L.qmoe_forward_ex(C.byref(d), fake, fake, fake, 4, 6, fake, fake, 1 << 30, None, C.byref(o)) == 2
+
+
+def test_relu_layer_descriptor_and_plan():
+    d = q.layer_desc(64, 768, 3072, "bf16", ("ternary", 128, "f16"), ("ternary", 128, "f16"), "relu")
+    assert d.fc1.rows == 3072
+    sw = q.layer_desc(64, 768, 3072, "bf16", ("ternary", 128, "f16"), ("ternary", 128, "f16"))
+    assert q.prepacked_size(d) < q.prepacked_size(sw)              # FC1 half the rows
+    assert q.forward_plan(d, 1, 1)["kernels"] == ["route_fc1_relu", "gemv_fc2"]
+    assert q.forward_plan(d, 9, 2)["kernels"] == ["route", "gemv_fc1_relu", "gemv_fc2", "combine"]
+    assert q.forward_plan(d, 64, 2)["kernels"] == ["route", "rowscale", "grouped_fc1_relu", "grouped_fc2", "combine"]
+    bad = q.layer_desc(64, 768, 3072, "bf16", ("ternary", 128, "f16"), ("ternary", 128, "f16"), "relu")
+    bad.fc1.rows = 2 * 3072                                         # SwiGLU-shaped FC1 with ReLU
+    bad2 = q.layer_desc(64, 768, 3072, "bf16", ("ternary", 128, "f16"), ("ternary", 128, "f16"))
+    bad2.activation = 7
+    bad3 = q.layer_desc(64, 768, 3072, "bf16", ("ternary", 128, "f16"), ("ternary", 128, "f16"))
+    bad3.reserved = 1
+    for b in (bad, bad2, bad3):
+        with pytest.raises(q.QmoeError) as ei:
+            q.prepacked_size(b)
+        assert ei.value.status == 1, q.last_error()

@@ -539,3 +539,30 @@ def test_f32_activations_unnormalised_weights_and_tiling():
     res = compare(y, ref["y"], ref["y64"], "f32")
     log(f"       y: max_row_rel={res['max_row_rel']:.3e}")
     assert res["ok"], res
+
+
+# ------------------------------------------- ReLU single-matrix expert FFN
+def _relu(spec):
+    import dataclasses
+    return dataclasses.replace(spec, activation="relu", name=spec.name + "_relu")
+
+
+@pytest.mark.parametrize("T,path", [(1, "auto"), (4, "auto"), (33, "grouped")])
+def test_relu_switch_base(T, path):
+    """The Switch Transformer's own FFN on the switch-base expert shapes:
+    FC1 one ternary [3072][768] matrix, h = max(a, 0), FC2, top-1."""
+    run_case(_relu(synth.MOE_WORKLOADS["switch_base_ternary"]), T, 4, path=path)
+
+
+@pytest.mark.parametrize("cfg", [
+    dict(E=4, H=128, I=128, top_k=2, fc1="sym_int4"),
+    dict(E=6, H=256, I=192, top_k=3, fc1="affine_int2", fc2="affine_int4", scale_dtype="f16", act_dtype="f16"),
+    dict(E=5, H=256, I=256, top_k=2, fc1="sym_int2", block1=128, fc2="ternary", block2=128, scale_dtype="f16"),
+], ids=["int4", "affine-f16", "int2-ternary"])
+@pytest.mark.parametrize("T,path", [(2, "auto"), (16, "auto"), (33, "grouped")])
+def test_relu_sweep_with_biases(cfg, T, path):
+    run_case(custom_moe_spec(**cfg, activation="relu"), T, 80 + T, path=path, expert_bias=0.1)
+
+
+def test_relu_f32_activations():
+    run_case(custom_moe_spec(E=4, H=128, I=128, top_k=2, activation="relu", act_dtype="f32"), 5, 90)
