@@ -566,3 +566,15 @@ def test_relu_sweep_with_biases(cfg, T, path):
 
 def test_relu_f32_activations():
     run_case(custom_moe_spec(E=4, H=128, I=128, top_k=2, activation="relu", act_dtype="f32"), 5, 90)
+
+
+# ------------------------------------------------------------ top-k = 16
+@pytest.mark.parametrize("T,path", [(1, "auto"), (2, "auto"), (5, "auto"), (9, "grouped")])
+def test_top16(T, path):
+    """The largest top-k: one token fills the 16 slots that FC1 routes by
+    itself, two take the small routing kernel."""
+    run_case(custom_moe_spec(E=32, H=128, I=128, top_k=16, fc1="sym_int2", fc2="sym_int4"), T, 95 + T, path=path)
+
+
+def test_top16_of_256_experts():
+    run_case(custom_moe_spec(E=256, H=64, I=64, top_k=16, fc1="sym_int4"), 3, 99)
