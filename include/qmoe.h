@@ -183,7 +183,9 @@ typedef struct qmoe_forward_opts {
      Otherwise the tokens run in consecutive tiles of R rows and a final tile
      of the rest, R = T halved (rounding up) until the workspace of a full
      tile and of the final tile each fit in workspace_limit bytes; each tile
-     takes its own path (auto: by its row count).  ws_bytes must hold the
+     takes its own path (auto: by its row count), and a tile size whose path
+     is not built (f32 activations or a forced GEMV path above 16 rows) is
+     halved further too, so such calls can run in tiles.  ws_bytes must hold the
      tile workspace that qmoe_forward_plan reports.  counts_out and events
      need a single tile (QMOE_ERR_UNSUPPORTED otherwise); ids_out, w_out and
      h_out are written as without tiling.  If one row does not fit:

@@ -506,6 +506,12 @@ qmoe_status pick_tiling(const qmoe_layer_desc &d, int32_t T, int32_t k, int path
   int32_t R = T;
   for (;;) {
     qmoe_status st = tile_need(d, T, k, path_req, softmax_all, R, t);
+    // a tile size whose path is not built (f32 activations or a forced GEMV
+    // path above its row bound) counts as not fitting: halve further
+    if (st == QMOE_ERR_UNSUPPORTED && limit > 0 && R > 1) {
+      R = (R + 1) / 2;
+      continue;
+    }
     if (st != QMOE_OK) return st;
     if (limit <= 0 || t.ws <= limit) return QMOE_OK;
     if (R == 1)
@@ -523,38 +529,30 @@ qmoe_status qmoe_forward_plan(const qmoe_layer_desc *desc, int32_t T, int32_t to
   if (st != QMOE_OK) return st;
   if (!plan) return fail(QMOE_ERR_INVALID_ARGUMENT, "null plan output");
   const bool softmax_all = opts && opts->topk_weights == QMOE_TOPK_SOFTMAX_ALL;
+  if (opts && opts->workspace_limit < 0) return fail(QMOE_ERR_INVALID_ARGUMENT, "negative workspace_limit");
+  // with a workspace limit, the plan of a full tile (and the totals over all tiles)
+  const bool tiled = T > 0 && opts && opts->workspace_limit > 0;
+  Tiling tl;
+  tl.rows = T;
+  tl.tiles = T == 0 ? 0 : 1;
+  if (tiled) {
+    st = pick_tiling(*desc, T, top_k, opts->path, softmax_all, opts->workspace_limit, tl);
+    if (st != QMOE_OK) return st;
+  }
   Plan p;
-  st = make_plan(*desc, T, top_k, opts ? opts->path : QMOE_PATH_AUTO, softmax_all, p);
+  st = make_plan(*desc, tl.rows, top_k, opts ? opts->path : QMOE_PATH_AUTO, softmax_all, p);
   if (st != QMOE_OK) return st;
   memset(plan, 0, sizeof *plan);
   plan->path = p.path;
-  plan->num_launches = T == 0 ? 0 : p.launches;
+  plan->num_launches = T == 0 ? 0 : tiled ? tl.launches : p.launches;
   plan->gemv_mmax = p.mmax;
   plan->gemv_fc1_waves = p.ks1;
   plan->gemv_fc2_waves = p.ks2;
   plan->max_active = p.max_active;
-  plan->workspace_bytes = MoeWs::make(*desc, T, top_k, p.path == QMOE_PATH_GROUPED).total;
+  plan->workspace_bytes = tiled ? tl.ws : MoeWs::make(*desc, T, top_k, p.path == QMOE_PATH_GROUPED).total;
   snprintf(plan->kernels, sizeof plan->kernels, "%s", T == 0 ? "" : p.kernels.c_str());
-  plan->row_tile = T;
-  plan->num_tiles = T == 0 ? 0 : 1;
-  if (T > 0 && opts && opts->workspace_limit != 0) {
-    if (opts->workspace_limit < 0) return fail(QMOE_ERR_INVALID_ARGUMENT, "negative workspace_limit");
-    Tiling tl;
-    st = pick_tiling(*desc, T, top_k, opts->path, softmax_all, opts->workspace_limit, tl);
-    if (st != QMOE_OK) return st;
-    st = make_plan(*desc, tl.rows, top_k, opts->path, softmax_all, p);
-    if (st != QMOE_OK) return st;
-    plan->path = p.path;
-    plan->num_launches = tl.launches;
-    plan->gemv_mmax = p.mmax;
-    plan->gemv_fc1_waves = p.ks1;
-    plan->gemv_fc2_waves = p.ks2;
-    plan->max_active = p.max_active;
-    plan->workspace_bytes = tl.ws;
-    snprintf(plan->kernels, sizeof plan->kernels, "%s", p.kernels.c_str());
-    plan->row_tile = tl.rows;
-    plan->num_tiles = tl.tiles;
-  }
+  plan->row_tile = tl.rows;
+  plan->num_tiles = tl.tiles;
   return ok();
 }
 

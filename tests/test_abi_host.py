@@ -305,3 +305,15 @@ def test_relu_layer_descriptor_and_plan():
         with pytest.raises(q.QmoeError) as ei:
             q.prepacked_size(b)
         assert ei.value.status == 1, q.last_error()
+
+
+def test_row_tiling_reaches_the_gemv_path():
+    """f32 activations above 16 rows, or a forced GEMV path, run in tiles of
+    at most 16 rows when a workspace limit is given."""
+    d = _desc(act="f32")
+    with pytest.raises(q.QmoeError):
+        q.forward_plan(d, 40, 6)
+    p = q.forward_plan(d, 40, 6, workspace_limit=1 << 40)
+    assert (p["row_tile"], p["num_tiles"], p["path"]) == (10, 4, 1)
+    g = q.forward_plan(_desc(), 100, 6, path="gemv", workspace_limit=1 << 40)
+    assert g["row_tile"] <= 16 and g["path"] == 1

@@ -578,3 +578,16 @@ def test_top16(T, path):
 
 def test_top16_of_256_experts():
     run_case(custom_moe_spec(E=256, H=64, I=64, top_k=16, fc1="sym_int4"), 3, 99)
+
+
+def test_f32_activations_40_tokens_in_gemv_tiles():
+    """40 tokens with f32 activations: the grouped path has no f32 input, so a
+    workspace limit runs them as four GEMV-path tiles of 10 rows."""
+    spec = custom_moe_spec(E=8, H=256, I=128, top_k=2, fc1="sym_int4", act_dtype="f32")
+    inp = synth.moe_inputs(spec, 40, 73)
+    _, _, _, y, dbg = _tiled_run(spec, inp, 40, 1 << 40)
+    ref = oracle.moe(inp)
+    assert np.array_equal(dbg["ids"].cpu().numpy(), oracle.route(inp["logits"], 2)["ids"])
+    res = compare(y, ref["y"], ref["y64"], "f32")
+    log(f"[f32 tiles] y: max_row_rel={res['max_row_rel']:.3e}")
+    assert res["ok"], res
