@@ -70,25 +70,26 @@ hipError_t launch_combine(const float *o, const int32_t *slot_pos, const float *
                  act_dtype, y);
 }
 
-const void *gemv_ptr_sym_int4(int, int, int, int, int);
-const void *gemv_ptr_sym_int2(int, int, int, int, int);
-const void *gemv_ptr_ternary(int, int, int, int, int);
-const void *gemv_ptr_affine_int2(int, int, int, int, int);
-const void *gemv_ptr_affine_int4(int, int, int, int, int);
+const void *gemv_ptr_sym_int4(int, int, int, int, int, int);
+const void *gemv_ptr_sym_int2(int, int, int, int, int, int);
+const void *gemv_ptr_ternary(int, int, int, int, int, int);
+const void *gemv_ptr_affine_int2(int, int, int, int, int, int);
+const void *gemv_ptr_affine_int4(int, int, int, int, int, int);
 
-const void *gemv_kernel_ptr(int qtype, int epilogue, int in_f16, int rows, int block, int tn) {
+const void *gemv_kernel_ptr(int qtype, int epilogue, int in_f16, int rows, int block, int tn, int ext) {
   switch (qtype) {
-    case QMOE_QTYPE_SYM_INT4: return gemv_ptr_sym_int4(epilogue, in_f16, rows, block, tn);
-    case QMOE_QTYPE_SYM_INT2: return gemv_ptr_sym_int2(epilogue, in_f16, rows, block, tn);
-    case QMOE_QTYPE_TERNARY: return gemv_ptr_ternary(epilogue, in_f16, rows, block, tn);
-    case QMOE_QTYPE_AFFINE_INT2: return gemv_ptr_affine_int2(epilogue, in_f16, rows, block, tn);
-    default: return gemv_ptr_affine_int4(epilogue, in_f16, rows, block, tn);
+    case QMOE_QTYPE_SYM_INT4: return gemv_ptr_sym_int4(epilogue, in_f16, rows, block, tn, ext);
+    case QMOE_QTYPE_SYM_INT2: return gemv_ptr_sym_int2(epilogue, in_f16, rows, block, tn, ext);
+    case QMOE_QTYPE_TERNARY: return gemv_ptr_ternary(epilogue, in_f16, rows, block, tn, ext);
+    case QMOE_QTYPE_AFFINE_INT2: return gemv_ptr_affine_int2(epilogue, in_f16, rows, block, tn, ext);
+    default: return gemv_ptr_affine_int4(epilogue, in_f16, rows, block, tn, ext);
   }
 }
 
 hipError_t launch_gemv(const GemvArgs &a, int epilogue, int in_f16, int rows, int waves, int tn, int block,
                        int grid_slots, hipStream_t s) {
-  const void *fn = gemv_kernel_ptr(a.qtype, epilogue, in_f16, rows, block, tn);
+  // the instances with bias / ReLU epilogue work only when the call uses them
+  const void *fn = gemv_kernel_ptr(a.qtype, epilogue, in_f16, rows, block, tn, a.bias != nullptr || a.relu != 0);
   if (fn == nullptr) return hipErrorInvalidConfiguration;  // no kernel for this (rows, tn) pairing
   GemvArgs args = a;
   void *kargs[] = {&args};
@@ -97,7 +98,7 @@ hipError_t launch_gemv(const GemvArgs &a, int epilogue, int in_f16, int rows, in
 }
 
 int gemv_blocks_per_cu(int qtype, int epilogue, int in_f16, int rows, int waves, int tn, int block) {
-  const void *fn = gemv_kernel_ptr(qtype, epilogue, in_f16, rows, block, tn);
+  const void *fn = gemv_kernel_ptr(qtype, epilogue, in_f16, rows, block, tn, 0);
   if (fn == nullptr) return 0;
   const size_t lds = gemv_lds_bytes(rows, epilogue, waves, tn);
   int dev = 0;

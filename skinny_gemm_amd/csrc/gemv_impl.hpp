@@ -118,7 +118,7 @@ __device__ inline void load_scales(__amdgpu_buffer_rsrc_t r, int voff, int soff,
 // PARTS: 2 = the input is an fp32 value split into bf16 hi + lo rows;
 // MR: accumulator rows kept per lane (1: a single row, 4: up to 16 rows per
 // tile); MT: 16-row tiles; BLOCK: scale block along K.
-template <int QT, bool XF16, int PARTS, int EPI, int MR, int MT, int BLOCK, int TN>
+template <int QT, bool XF16, int PARTS, int EPI, int MR, int MT, int BLOCK, int TN, bool EXT>
 __global__ __launch_bounds__(512) void gemv_kernel(const GemvArgs a) {
   using TR = QtTraits<QT>;
   using CD = Codec<TR::kBits, XF16>;
@@ -416,22 +416,24 @@ __global__ __launch_bounds__(512) void gemv_kernel(const GemvArgs a) {
     float v = 0.f;
     for (int w = 0; w < KS; ++w) v += s_red[w * NV * kLanes + idx];
     const int64_t n = (int64_t)rg * kRowsPerGroup + 16 * (t0 + t) + (lo & 15);
-    // optional per-expert output bias: FC1 before the SwiGLU, FC2 before the
-    // routing weight
-    if constexpr (EPI != kEpiStoreAct) {
+    // EXT instances only: the optional per-expert output bias (FC1 before
+    // the activation, FC2 before the routing weight) and the ReLU FFN
+    bool relu = false;
+    if constexpr (EXT && EPI != kEpiStoreAct) {
       if (a.bias) v += half_to_f32_rt(a.bias[(int64_t)e * N + n], a.act_dtype == QMOE_DTYPE_F16);
+      relu = a.relu != 0;
     }
     if constexpr (EPI == kEpiStoreAct) {
       if (valid) a.out_act[(int64_t)m * N + n] = f32_to_act(v, a.act_dtype == QMOE_DTYPE_F16);
     } else if constexpr (SWIGLU) {
       // SwiGLU: rows 2i (gate) and 2i+1 (up) sit in neighbouring lanes;
-      // ReLU (a.relu): every row is one channel, h = max(a, 0)
+      // ReLU (EXT, a.relu): every row is one channel, h = max(a, 0)
       const float up = __shfl_xor(v, 1);
-      if (valid && (a.relu || (lo & 1) == 0)) {
+      if (valid && (relu || (lo & 1) == 0)) {
         const float gt = v;
-        const float h = a.relu ? fmaxf(v, 0.f) : gt / (1.f + expf(-gt)) * up;
-        const int64_t Ih = a.relu ? N : N / 2;
-        const int64_t i = a.relu ? n : n / 2;
+        const float h = relu ? fmaxf(v, 0.f) : gt / (1.f + expf(-gt)) * up;
+        const int64_t Ih = relu ? N : N / 2;
+        const int64_t i = relu ? n : n / 2;
         const int64_t p = pbase + m;
         const uint16_t hi = f32_to_bf16_rne(h);
         a.h_hi[p * Ih + i] = hi;
@@ -459,40 +461,49 @@ __global__ __launch_bounds__(512) void gemv_kernel(const GemvArgs a) {
 }
 
 // Kernel of a configuration: rows = the row bound of the launch, tn = 16-row
-// tiles per wave (1: four workgroups share a row group's 64 rows).
-template <int QT, bool XF16, int PARTS, int EPI, int MR, int MT>
+// tiles per wave (1: four workgroups share a row group's 64 rows), ext = the
+// instance with the optional epilogue work (expert bias, ReLU FFN); the
+// default instances carry none of it.
+template <int QT, bool XF16, int PARTS, int EPI, int MR, int MT, bool EXT>
 const void *gemv_ptr_block(int block, int tn) {
   if (tn == 1)
-    return block == 64 ? reinterpret_cast<const void *>(&gemv_kernel<QT, XF16, PARTS, EPI, MR, MT, 64, 1>)
-                       : reinterpret_cast<const void *>(&gemv_kernel<QT, XF16, PARTS, EPI, MR, MT, 128, 1>);
+    return block == 64 ? reinterpret_cast<const void *>(&gemv_kernel<QT, XF16, PARTS, EPI, MR, MT, 64, 1, EXT>)
+                       : reinterpret_cast<const void *>(&gemv_kernel<QT, XF16, PARTS, EPI, MR, MT, 128, 1, EXT>);
   if (tn != 4) return nullptr;
-  return block == 64 ? reinterpret_cast<const void *>(&gemv_kernel<QT, XF16, PARTS, EPI, MR, MT, 64, 4>)
-                     : reinterpret_cast<const void *>(&gemv_kernel<QT, XF16, PARTS, EPI, MR, MT, 128, 4>);
+  return block == 64 ? reinterpret_cast<const void *>(&gemv_kernel<QT, XF16, PARTS, EPI, MR, MT, 64, 4, EXT>)
+                     : reinterpret_cast<const void *>(&gemv_kernel<QT, XF16, PARTS, EPI, MR, MT, 128, 4, EXT>);
 }
 
-template <int QT, bool XF16, int PARTS, int EPI>
+template <int QT, bool XF16, int PARTS, int EPI, bool EXT>
 const void *gemv_ptr_rows(int rows, int block, int tn) {
-  if (rows <= 1) return gemv_ptr_block<QT, XF16, PARTS, EPI, 1, 1>(block, tn);
+  if (rows <= 1) return gemv_ptr_block<QT, XF16, PARTS, EPI, 1, 1, EXT>(block, tn);
   if constexpr (EPI == kEpiStoreAct) {
-    if (rows > 16) return gemv_ptr_block<QT, XF16, PARTS, EPI, 4, 2>(block, tn);
+    if (rows > 16) return gemv_ptr_block<QT, XF16, PARTS, EPI, 4, 2, EXT>(block, tn);
   }
-  return gemv_ptr_block<QT, XF16, PARTS, EPI, 4, 1>(block, tn);
+  return gemv_ptr_block<QT, XF16, PARTS, EPI, 4, 1, EXT>(block, tn);
+}
+
+template <int QT, int EPI, bool EXT>
+const void *gemv_ptr_fc1(int in_f16, int rows, int block, int tn) {
+  // FC1 input: bf16 or f16 rows, or (kGemvInSplitF32) f32 rows given as bf16 hi + lo parts
+  return in_f16 == kGemvInSplitF32 ? gemv_ptr_rows<QT, false, 2, EPI, EXT>(rows, block, tn)
+         : in_f16                  ? gemv_ptr_rows<QT, true, 1, EPI, EXT>(rows, block, tn)
+                                   : gemv_ptr_rows<QT, false, 1, EPI, EXT>(rows, block, tn);
 }
 
 template <int QT>
-const void *gemv_ptr_qt(int epilogue, int in_f16, int rows, int block, int tn) {
-  if (epilogue == kEpiDown) return gemv_ptr_rows<QT, false, 2, kEpiDown>(rows, block, tn);
-  // FC1 input: bf16 or f16 rows, or (kGemvInSplitF32) f32 rows given as bf16 hi + lo parts
+const void *gemv_ptr_qt(int epilogue, int in_f16, int rows, int block, int tn, int ext) {
+  if (epilogue == kEpiDown)
+    return ext ? gemv_ptr_rows<QT, false, 2, kEpiDown, true>(rows, block, tn)
+               : gemv_ptr_rows<QT, false, 2, kEpiDown, false>(rows, block, tn);
   if (epilogue == kEpiSwiGLU)
-    return in_f16 == kGemvInSplitF32 ? gemv_ptr_rows<QT, false, 2, kEpiSwiGLU>(rows, block, tn)
-           : in_f16                  ? gemv_ptr_rows<QT, true, 1, kEpiSwiGLU>(rows, block, tn)
-                                     : gemv_ptr_rows<QT, false, 1, kEpiSwiGLU>(rows, block, tn);
+    return ext ? gemv_ptr_fc1<QT, kEpiSwiGLU, true>(in_f16, rows, block, tn)
+               : gemv_ptr_fc1<QT, kEpiSwiGLU, false>(in_f16, rows, block, tn);
   if (epilogue == kEpiSwiGLURouted)
-    return in_f16 == kGemvInSplitF32 ? gemv_ptr_rows<QT, false, 2, kEpiSwiGLURouted>(rows, block, tn)
-           : in_f16                  ? gemv_ptr_rows<QT, true, 1, kEpiSwiGLURouted>(rows, block, tn)
-                                     : gemv_ptr_rows<QT, false, 1, kEpiSwiGLURouted>(rows, block, tn);
-  return in_f16 ? gemv_ptr_rows<QT, true, 1, kEpiStoreAct>(rows, block, tn)
-                : gemv_ptr_rows<QT, false, 1, kEpiStoreAct>(rows, block, tn);
+    return ext ? gemv_ptr_fc1<QT, kEpiSwiGLURouted, true>(in_f16, rows, block, tn)
+               : gemv_ptr_fc1<QT, kEpiSwiGLURouted, false>(in_f16, rows, block, tn);
+  return in_f16 ? gemv_ptr_rows<QT, true, 1, kEpiStoreAct, false>(rows, block, tn)
+                : gemv_ptr_rows<QT, false, 1, kEpiStoreAct, false>(rows, block, tn);
 }
 
 }  // namespace qmoe
