@@ -259,7 +259,7 @@ struct Plan {
   int mmax, mmax1, mmax2, ks1, ks2, tn1, tn2, max_active, max_tiles;
   int route_fused;
   int fc1_routes;  // GEMV path: FC1 routes the tokens itself (no routing kernel)
-  bool softmax_all;  // a route_weights stage replaces the routing weights
+  bool softmax_all;  // unnormalised top-k weights, computed by the routing top-k
   int launches;
   std::string kernels;
 };
@@ -291,9 +291,9 @@ qmoe_status make_plan(const qmoe_layer_desc &d, int32_t T, int32_t k, int path_r
     p.route_fused = (T <= 16) ? 1 : 0;
     p.max_tiles = (int)grouped_max_tiles((int64_t)T * k, d.num_experts);
     p.softmax_all = softmax_all;
-    p.kernels = std::string("route,") + (softmax_all ? "route_weights," : "") + "rowscale,grouped_fc1_" +
+    p.kernels = std::string("route,") + "rowscale,grouped_fc1_" +
                 (d.activation == QMOE_ACT_RELU ? "relu" : "swiglu") + ",grouped_fc2,combine";
-    p.launches = (p.route_fused ? 1 : 2) + 4 + (softmax_all ? 1 : 0);
+    p.launches = (p.route_fused ? 1 : 2) + 4;
     return ok();
   }
   p.route_fused = (T <= 16) ? 1 : 0;
@@ -318,8 +318,8 @@ qmoe_status make_plan(const qmoe_layer_desc &d, int32_t T, int32_t k, int path_r
   const bool combine = k > 1 || f32;
   const std::string act = d.activation == QMOE_ACT_RELU ? "relu" : "swiglu";
   p.kernels = std::string(f32 ? "split_x," : "") + (p.fc1_routes ? "route_fc1_" + act : "route,gemv_fc1_" + act) +
-              (softmax_all ? ",route_weights" : "") + ",gemv_fc2" + (combine ? ",combine" : "");
-  p.launches = (p.fc1_routes ? 2 : 3) + (combine ? 1 : 0) + (softmax_all ? 1 : 0) + (f32 ? 1 : 0);
+              ",gemv_fc2" + (combine ? ",combine" : "");
+  p.launches = (p.fc1_routes ? 2 : 3) + (combine ? 1 : 0) + (f32 ? 1 : 0);
   return ok();
 }
 
@@ -642,6 +642,7 @@ qmoe_status qmoe_forward_ex(const qmoe_layer_desc *desc, const void *packed, con
   ra.zero_len = p.path == QMOE_PATH_GROUPED ? (int)((int64_t)T * top_k) : 0;
   ra.tile_rows = p.path == QMOE_PATH_GROUPED ? kTileM : 0;
   ra.max_tiles = p.max_tiles;
+  ra.softmax_all = p.softmax_all ? 1 : 0;
   // optional per-stage events (diagnostic timing): stage i of the plan's
   // stage list stamps events 2i / 2i+1 with the begin of its first kernel
   // and the end of its last (see StageEvents)
@@ -680,19 +681,8 @@ qmoe_status qmoe_forward_ex(const qmoe_layer_desc *desc, const void *packed, con
     if (e != hipSuccess) return hip_status(e, "route");
   }
 
-  // SOFTMAX_ALL weights, once the ids exist and before FC2 or the combine reads them
-  auto route_weights = [&]() -> qmoe_status {
-    if (!p.softmax_all) return QMOE_OK;
-    hipError_t e2 = begin();
-    if (e2 == hipSuccess)
-      e2 = launch_route_weights_all(logits, T, desc->num_experts, top_k, ra.r.ids, ra.r.w, s);
-    if (e2 == hipSuccess) e2 = end();
-    return e2 == hipSuccess ? QMOE_OK : hip_status(e2, "route weights");
-  };
-
   float *o = (float *)(wsb + W.o);
   if (p.path == QMOE_PATH_GROUPED) {
-    if ((st = route_weights()) != QMOE_OK) return st;
     float *xsc = (float *)(wsb + W.xsc), *h32 = (float *)(wsb + W.h32);
     uint32_t *hmax = (uint32_t *)(wsb + W.hmax);
     uint16_t *xs16 = (uint16_t *)(wsb + W.xs16);
@@ -749,6 +739,7 @@ qmoe_status qmoe_forward_ex(const qmoe_layer_desc *desc, const void *packed, con
     g1.route_E = desc->num_experts;
     g1.route_k = top_k;
     g1.route_max_slots = p.max_active;
+    g1.route_softmax_all = p.softmax_all ? 1 : 0;
     g1.route = ra.r;
   }
   g1.slot_info = ra.r.slot_info;
@@ -771,7 +762,6 @@ qmoe_status qmoe_forward_ex(const qmoe_layer_desc *desc, const void *packed, con
                     p.ks1, p.tn1, L.fc1.block, p.max_active, s);
   if (e == hipSuccess) e = end();
   if (e != hipSuccess) return hip_status(e, "gemv fc1");
-  if ((st = route_weights()) != QMOE_OK) return st;
 
   GemvArgs g2 = gemv_base(L.fc2, pk + L.fc2_off);
   g2.slot_info = ra.r.slot_info;
@@ -844,6 +834,7 @@ qmoe_status qmoe_route(int32_t T, int32_t E, int32_t top_k, const float *logits,
   ra.zero_len = 0;
   ra.tile_rows = 0;
   ra.max_tiles = 0;
+  ra.softmax_all = 0;
   hipError_t e = launch_route(ra, s);
   if (e != hipSuccess) return hip_status(e, "route");
   const int64_t S = (int64_t)T * top_k;

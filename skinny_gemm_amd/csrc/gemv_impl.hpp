@@ -164,10 +164,19 @@ __global__ __launch_bounds__(512) void gemv_kernel(const GemvArgs a) {
     __shared__ int4 s_slot;
     __shared__ TopkScratch s_tk[kGemvMaxWaves];
     const bool lead = blockIdx.x == 0;
-    for (int t = wave; t < a.route_T; t += KS)
-      wave_topk(a.logits + (int64_t)t * a.route_E, a.route_E, a.route_k,
-                lead ? a.route.ids + (int64_t)t * a.route_k : nullptr,
-                lead ? a.route.w + (int64_t)t * a.route_k : nullptr, s_ids + t * a.route_k, &s_tk[wave]);
+    for (int t = wave; t < a.route_T; t += KS) {
+      const float *lt = a.logits + (int64_t)t * a.route_E;
+      int32_t *ids_t = lead ? a.route.ids + (int64_t)t * a.route_k : nullptr;
+      float *w_t = lead ? a.route.w + (int64_t)t * a.route_k : nullptr;
+      // EXT instances also serve the unnormalised top-k weights
+      if constexpr (EXT) {
+        if (a.route_softmax_all) {
+          wave_topk<true>(lt, a.route_E, a.route_k, ids_t, w_t, s_ids + t * a.route_k, &s_tk[wave]);
+          continue;
+        }
+      }
+      wave_topk(lt, a.route_E, a.route_k, ids_t, w_t, s_ids + t * a.route_k, &s_tk[wave]);
+    }
     __syncthreads();
     if (wave == 0) wave_expand_want(s_ids, a.route_T * a.route_k, slot, &s_slot, s_rslot);
     // workgroup 0: the expert map of all slots for the later kernels (on a

@@ -179,6 +179,7 @@ struct RouteArgs {
   int zero_len;
   int tile_rows;       // rows per grouped-path tile (0: no tile list)
   int max_tiles;       // entries of tile_info to fill
+  int softmax_all;     // 1: weights are the selected entries of the softmax over all E logits
 };
 
 // -------------------------------------------------------------------- GEMV
@@ -225,6 +226,7 @@ struct GemvArgs {
   // kEpiSwiGLURouted: router logits [T][E] and the routing outputs
   const float *logits;
   int route_T, route_E, route_k, route_max_slots;
+  int route_softmax_all;   // kEpiSwiGLURouted (EXT instances): as RouteArgs::softmax_all
   RouteBufs route;
 };
 
@@ -253,12 +255,6 @@ hipError_t launch_prepack_scales(const MatLayout &L, int E, const uint16_t *scal
 hipError_t launch_unpack_matrix(const MatLayout &L, int E, const uint8_t *src, int8_t *codes_out,
                                 hipStream_t s);
 hipError_t launch_route(const RouteArgs &a, hipStream_t s);
-// Replace the routing weights w [T][k] of the selected ids by the selected
-// entries of the softmax over all E logits of each token (the weights of
-// qmoe_topk_weights SOFTMAX_ALL); ids [T][k] are in selection order, so
-// ids[t][0] holds the maximum logit.
-hipError_t launch_route_weights_all(const float *logits, int T, int E, int k, const int32_t *ids, float *w,
-                                    hipStream_t s);
 // rows: bound on the rows of any expert (or dense M), <= kGemvMaxRowsDense;
 // waves: waves per workgroup (K split); tn: 16-row n-tiles per wave (1 or 4).
 hipError_t launch_gemv(const GemvArgs &a, int epilogue, int in_f16, int rows, int waves, int tn, int block,

@@ -19,16 +19,18 @@ constexpr int kExpandThreads = 1024;
 constexpr int kExpandWaves = kExpandThreads / kLanes;
 constexpr int kCachedTiles = 16;  // slot ids per thread held in registers by the expand kernel
 
+template <bool ALL>
 __global__ __launch_bounds__(256) void route_topk_kernel(RouteArgs a) {
   __shared__ TopkScratch s_tk[256 / kLanes];
   const int t = blockIdx.x * (blockDim.x / kLanes) + (threadIdx.x / kLanes);
   if (t >= a.T) return;
-  wave_topk(a.logits + (int64_t)t * a.E, a.E, a.k, a.r.ids + (int64_t)t * a.k,
+  wave_topk<ALL>(a.logits + (int64_t)t * a.E, a.E, a.k, a.r.ids + (int64_t)t * a.k,
             a.r.w + (int64_t)t * a.k, nullptr, &s_tk[threadIdx.x / kLanes]);
 }
 
 // Single workgroup.  With topk_in_expand (T <= kExpandWaves) the workgroup
 // first routes the tokens itself, one wave per token.
+template <bool ALL>
 __global__ __launch_bounds__(kExpandThreads) void route_expand_kernel(RouteArgs a) {
   __shared__ int s_cnt[kMaxExperts];
   __shared__ int s_off[kMaxExperts + 1];
@@ -42,7 +44,7 @@ __global__ __launch_bounds__(kExpandThreads) void route_expand_kernel(RouteArgs 
   const bool fused = a.topk_in_expand != 0;
 
   if (fused && wave < a.T) {
-    wave_topk(a.logits + (int64_t)wave * E, E, a.k, a.r.ids + (int64_t)wave * a.k,
+    wave_topk<ALL>(a.logits + (int64_t)wave * E, E, a.k, a.r.ids + (int64_t)wave * a.k,
               a.r.w + (int64_t)wave * a.k, s_ids + wave * a.k, &s_tk[wave]);
   }
   for (int e = tid; e < kMaxExperts; e += kExpandThreads) {
@@ -198,54 +200,33 @@ __global__ __launch_bounds__(kExpandThreads) void route_expand_kernel(RouteArgs 
 
 // Small decode batches (T * k <= 64 slots, no grouped-path lists): one wave
 // per token routes it, then wave 0 alone builds the expert map.
+template <bool ALL>
 __global__ __launch_bounds__(1024) void route_small_kernel(RouteArgs a) {
   __shared__ int32_t s_ids[kExpandWaves * kMaxTopK];
   __shared__ TopkScratch s_tk[kExpandWaves];
   const int wave = threadIdx.x / kLanes;
   if (wave < a.T)
-    wave_topk(a.logits + (int64_t)wave * a.E, a.E, a.k, a.r.ids + (int64_t)wave * a.k,
+    wave_topk<ALL>(a.logits + (int64_t)wave * a.E, a.E, a.k, a.r.ids + (int64_t)wave * a.k,
               a.r.w + (int64_t)wave * a.k, s_ids + wave * a.k, &s_tk[wave]);
   __syncthreads();
   if (wave == 0) wave_expand_lists(s_ids, a.T * a.k, a.k, a.E, a.max_slots, a.r);
 }
 
-// One wave per token: m = the token's maximum logit (that of its first
-// selected expert), the wave sum of exp(l - m) over all E logits, then lane j
-// writes exp(l[id_j] - m) / sum for j < k.
-__global__ __launch_bounds__(256) void route_weights_all_kernel(const float *__restrict__ logits, int T, int E,
-                                                                int k, const int32_t *__restrict__ ids,
-                                                                float *__restrict__ w) {
-  const int lane = threadIdx.x & (kLanes - 1);
-  const int t = blockIdx.x * (blockDim.x / kLanes) + (threadIdx.x / kLanes);
-  if (t >= T) return;  // whole waves leave together
-  const float *l = logits + (int64_t)t * E;
-  const float m = l[ids[(int64_t)t * k]];
-  float part = 0.f;
-  for (int e = lane; e < E; e += kLanes) part += expf(l[e] - m);
-#pragma unroll
-  for (int off = 1; off < kLanes; off <<= 1) part += __shfl_xor(part, off);
-  if (lane < k) w[(int64_t)t * k + lane] = expf(l[ids[(int64_t)t * k + lane]] - m) / part;
-}
-
-hipError_t launch_route_weights_all(const float *logits, int T, int E, int k, const int32_t *ids, float *w,
-                                    hipStream_t s) {
-  if (T <= 0) return hipSuccess;
-  if (k < 1 || k > kLanes || E < 1) return hipErrorInvalidValue;
-  constexpr int kWaves = 256 / kLanes;
-  const int grid = (T + kWaves - 1) / kWaves;
-  return qlaunch(route_weights_all_kernel, dim3(grid), dim3(256), 0, s, logits, T, E, k, ids, w);
+// The ALL instances (unnormalised top-k weights) only when the call asks for them.
+template <bool ALL>
+hipError_t launch_route_as(const RouteArgs &a, hipStream_t s) {
+  if (a.topk_in_expand && a.T > 0 && (int64_t)a.T * a.k <= kLanes && a.tile_rows == 0 && a.zero_len == 0)
+    return qlaunch(route_small_kernel<ALL>, dim3(1), dim3(a.T * kLanes), 0, s, a);
+  if (!a.topk_in_expand && a.T > 0) {
+    const int per = 256 / kLanes;
+    const hipError_t e = qlaunch(route_topk_kernel<ALL>, dim3((a.T + per - 1) / per), dim3(256), 0, s, a);
+    if (e != hipSuccess) return e;
+  }
+  return qlaunch(route_expand_kernel<ALL>, dim3(1), dim3(kExpandThreads), 0, s, a);
 }
 
 hipError_t launch_route(const RouteArgs &a, hipStream_t s) {
-  if (a.topk_in_expand && a.T > 0 && (int64_t)a.T * a.k <= kLanes && a.tile_rows == 0 && a.zero_len == 0) {
-    return qlaunch(route_small_kernel, dim3(1), dim3(a.T * kLanes), 0, s, a);
-  }
-  if (!a.topk_in_expand && a.T > 0) {
-    const int per = 256 / kLanes;
-    const hipError_t e = qlaunch(route_topk_kernel, dim3((a.T + per - 1) / per), dim3(256), 0, s, a);
-    if (e != hipSuccess) return e;
-  }
-  return qlaunch(route_expand_kernel, dim3(1), dim3(kExpandThreads), 0, s, a);
+  return a.softmax_all ? launch_route_as<true>(a, s) : launch_route_as<false>(a, s);
 }
 
 }  // namespace qmoe

@@ -46,6 +46,13 @@ __device__ inline float wave_max(float v) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), kLanes - 1));
 }
 
+// Sum of v over the wavefront, in every lane (xor butterfly).
+__device__ inline float wave_sum(float v) {
+#pragma unroll
+  for (int off = 1; off < kLanes; off <<= 1) v += __shfl_xor(v, off);
+  return v;
+}
+
 // Wave-wide top-k of one token.  Lane 0 writes the ids and weights to
 // ids_out / w_out (when not null) and the ids to ids_lds (when not null),
 // in selection order.  Requires 1 <= k <= E.
@@ -56,11 +63,15 @@ __device__ inline float wave_max(float v) {
 // logits).  Each of the k rounds takes a DPP wave maximum over the experts
 // not yet taken and the lowest expert holding it (one logit per lane for
 // E <= 64, E / 64 per lane beyond).  The selection is recorded in sc; the
-// weights are the softmax of the selected logits, computed by lane 0 in
-// fp32 in selection order.
+// weights are computed by lane 0 in fp32 in selection order: the softmax of
+// the selected logits, or (ALL) exp(l - max) over the wave sum of
+// exp(l - max) of all E logits, the selected entries of the softmax over
+// every expert.
+template <bool ALL = false>
 __device__ inline void wave_topk(const float *__restrict__ l, int E, int k, int32_t *ids_out, float *w_out,
                                  int32_t *ids_lds, TopkScratch *sc) {
   const int lane = threadIdx.x & (kLanes - 1);
+  float all_sum = 0.f;  // ALL: sum of exp(l - max) over all E logits
   // the selection goes to sc->id / sc->v in selection order (LDS: no
   // private arrays indexed by the runtime k)
   if (E <= kLanes) {
@@ -77,6 +88,9 @@ __device__ inline void wave_topk(const float *__restrict__ l, int E, int k, int3
       if (lane == 0) {
         sc->id[j] = sel;
         sc->v[j] = m;
+      }
+      if constexpr (ALL) {
+        if (j == 0) all_sum = wave_sum(have ? expf(v - m) : 0.f);
       }
     }
   } else {
@@ -108,13 +122,22 @@ __device__ inline void wave_topk(const float *__restrict__ l, int E, int k, int3
         sc->id[j] = sel;
         sc->v[j] = m;
       }
+      if constexpr (ALL) {
+        if (j == 0) {
+          float part = 0.f;
+#pragma unroll
+          for (int i = 0; i < PER; ++i) part += (lane + kLanes * i < E) ? expf(v[i] - m) : 0.f;
+          all_sum = wave_sum(part);
+        }
+      }
     }
   }
   // lane 0 recorded the selection above and computes the weights
   if (lane == 0) {
     const float m = sc->v[0];
-    float sum = 0.f;
-    for (int j = 0; j < k; ++j) sum += expf(sc->v[j] - m);
+    float sum = all_sum;
+    if constexpr (!ALL)
+      for (int j = 0; j < k; ++j) sum += expf(sc->v[j] - m);
     for (int j = 0; j < k; ++j) {
       const int id = sc->id[j];
       if (ids_out) ids_out[j] = id;
