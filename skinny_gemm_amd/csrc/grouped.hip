@@ -122,6 +122,55 @@ __global__ __launch_bounds__(1024) void wscale_kernel(MatLayout L, const uint8_t
   }
 }
 
+// Few experts (the dense matrix is one) would leave most compute units idle
+// with one workgroup each; there the same power of two comes from three
+// stream-ordered passes over the same scale section: clear the per-expert
+// maxima, take the maximum of |s| over slices of kWscaleSlice vectors of
+// 16 B with one atomic per workgroup (|s| bits order like the values; NaN
+// entries are skipped), then turn each maximum into the power of two in
+// place.
+constexpr int kWscaleSlice = 4096;       // 16-B vectors per workgroup (64 KiB)
+constexpr int kWscalePerExpertMin = 32;  // from this many experts on: one workgroup per expert
+
+__global__ __launch_bounds__(256) void wscale_clear_kernel(uint32_t *__restrict__ m, int E) {
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e < E) m[e] = 0u;
+}
+
+__global__ __launch_bounds__(256) void wscale_max_kernel(MatLayout L, const uint8_t *__restrict__ mat,
+                                                         uint32_t *__restrict__ mbits) {
+  __shared__ float red[256 / 64];
+  const int e = blockIdx.y;
+  const uint4 *sb = reinterpret_cast<const uint4 *>(mat + (int64_t)e * L.stride + L.scales_off);
+  const int64_t nv = L.RG * L.NKT * kLanes * L.bpk * (L.affine ? 4 : 2) / 16;
+  const int64_t v0 = (int64_t)blockIdx.x * kWscaleSlice;
+  const int64_t v1 = v0 + kWscaleSlice < nv ? v0 + kWscaleSlice : nv;
+  const int f16 = L.sdtype == QMOE_DTYPE_F16;
+  float m = 0.f;
+  for (int64_t i = v0 + threadIdx.x; i < v1; i += blockDim.x) {
+    const uint4 v = sb[i];
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      m = fmaxf(m, fabsf(half_to_f32_rt(w[q] & 0xFFFFu, f16)));
+      if (!L.affine) m = fmaxf(m, fabsf(half_to_f32_rt(w[q] >> 16, f16)));
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const float mm = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    atomicMax(&mbits[e], __float_as_uint(mm));
+  }
+}
+
+__global__ __launch_bounds__(256) void wscale_final_kernel(MatLayout L, float *__restrict__ wsc, int E) {
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e < E) wsc[e] = pow2_below(wsc[e] * (float)qtype_qmax(L.qtype), 15);  // wsc[e] holds max |s|
+}
+
 // ---------------------------------------------------------------- GEMM
 constexpr int kMaxAffineBlocks = kGroupedMaxAffineBlocks;
 
@@ -546,7 +595,16 @@ hipError_t launch_rowscale(const void *x, int rows, int64_t K, int in_f16, float
 }
 
 hipError_t launch_wscale(const MatLayout &L, int E, const uint8_t *mat, float *wsc, hipStream_t s) {
-  return qlaunch(wscale_kernel, dim3(E), dim3(1024), 0, s, L, mat, wsc);
+  if (E >= kWscalePerExpertMin) return qlaunch(wscale_kernel, dim3(E), dim3(1024), 0, s, L, mat, wsc);
+  // wsc holds the maxima' bits between the passes
+  uint32_t *mbits = reinterpret_cast<uint32_t *>(wsc);
+  const int64_t nv = L.RG * L.NKT * kLanes * L.bpk * (L.affine ? 4 : 2) / 16;
+  const unsigned slices = (unsigned)((nv + kWscaleSlice - 1) / kWscaleSlice);
+  hipError_t e = qlaunch(wscale_clear_kernel, dim3((unsigned)((E + 255) / 256)), dim3(256), 0, s, mbits, E);
+  if (e == hipSuccess && slices > 0)
+    e = qlaunch(wscale_max_kernel, dim3(slices, (unsigned)E), dim3(256), 0, s, L, mat, mbits);
+  if (e == hipSuccess) e = qlaunch(wscale_final_kernel, dim3((unsigned)((E + 255) / 256)), dim3(256), 0, s, L, wsc, E);
+  return e;
 }
 
 }  // namespace qmoe

@@ -49,29 +49,34 @@ __global__ __launch_bounds__(256) void prepack_codes_kernel(MatLayout L, int64_t
 }
 
 // One workgroup per (row group, expert).  The source of a row group is one
-// contiguous [64 rows][nblk] block of the canonical scales; threads walk the
-// destination [k-tile][row][block of the k-tile] in order (coalesced
-// stores), and the reads stay inside that small block (cache-resident).
+// contiguous [64 rows][nblk] block of the canonical scales.  A thread takes
+// one (k-tile, row) pair, in destination order [k-tile][row], and writes its
+// bpk block entries side by side (coalesced stores, index math once per
+// pair); the reads stay inside the small source block (cache-resident).
 // Entries past the last block are zero.
 __global__ __launch_bounds__(256) void prepack_scales_kernel(MatLayout L, const uint16_t *__restrict__ scales,
                                                              const uint16_t *__restrict__ biases,
                                                              uint8_t *__restrict__ dst) {
   const int rg = blockIdx.x, e = blockIdx.y;
-  const int nblk = (int)L.nblk, bpk = L.bpk;
-  const int per_rg = (int)L.NKT * kLanes * bpk;  // destination entries of one row group
+  const int nblk = (int)L.nblk, bpk = L.bpk;  // bpk in {1, 2, 4}
+  const int pairs = (int)L.NKT * kLanes;      // (k-tile, row) pairs of one row group
   const int64_t src0 = ((int64_t)e * L.N + (int64_t)rg * kRowsPerGroup) * nblk;
-  const int64_t dst0 = (int64_t)rg * per_rg;
+  const int64_t dst0 = (int64_t)rg * pairs * bpk;
   uint8_t *base = dst + (int64_t)e * L.stride + L.scales_off;
-  for (int i = threadIdx.x; i < per_rg; i += blockDim.x) {
-    const int bi = i % bpk, row = (i / bpk) & (kLanes - 1), kt = i / (bpk * kLanes);
-    const int b = kt * bpk + bi;
-    const bool real = b < nblk;
-    const int64_t src = src0 + (int64_t)row * nblk + b;
-    if (L.affine) {
-      reinterpret_cast<uint32_t *>(base)[dst0 + i] =
-          real ? ((uint32_t)scales[src] | ((uint32_t)biases[src] << 16)) : 0u;
-    } else {
-      reinterpret_cast<uint16_t *>(base)[dst0 + i] = real ? scales[src] : (uint16_t)0;
+  for (int q = threadIdx.x; q < pairs; q += blockDim.x) {
+    const int row = q & (kLanes - 1), kt = q / kLanes;
+    const int b0 = kt * bpk;
+    const int64_t src = src0 + (int64_t)row * nblk + b0;
+    const int64_t d = dst0 + (int64_t)q * bpk;
+#pragma unroll
+    for (int bi = 0; bi < 4; ++bi) {
+      if (bi >= bpk) break;
+      const bool real = b0 + bi < nblk;
+      if (L.affine)
+        reinterpret_cast<uint32_t *>(base)[d + bi] =
+            real ? ((uint32_t)scales[src + bi] | ((uint32_t)biases[src + bi] << 16)) : 0u;
+      else
+        reinterpret_cast<uint16_t *>(base)[d + bi] = real ? scales[src + bi] : (uint16_t)0;
     }
   }
 }
