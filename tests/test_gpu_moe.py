@@ -591,3 +591,26 @@ def test_f32_activations_40_tokens_in_gemv_tiles():
     res = compare(y, ref["y"], ref["y64"], "f32")
     log(f"[f32 tiles] y: max_row_rel={res['max_row_rel']:.3e}")
     assert res["ok"], res
+
+
+# ------------------------------------------------------ options combined
+@pytest.mark.parametrize("T,path", [(3, "auto"), (20, "gemv"), (33, "grouped")])
+def test_relu_bias_unnormalised_weights_together(T, path):
+    """ReLU FFN, expert biases and unnormalised top-k weights in one call:
+    routing inside FC1 (T = 3), the routing kernels (T = 20 on the GEMV
+    path, in row tiles) and the grouped path."""
+    spec = custom_moe_spec(E=12, H=128, I=192, top_k=3, fc1="sym_int4", fc2="sym_int2", activation="relu")
+    if path == "gemv":
+        from skinny_gemm_amd.layer import MoeLayer, to_device_bits, bits_of
+        inp = synth.moe_inputs(spec, T, 120, expert_bias=0.1)
+        layer = MoeLayer.from_spec(spec, inp)
+        x = to_device_bits(inp["x"], spec.act_dtype)
+        lg = torch.from_numpy(inp["logits"]).cuda()
+        y = bits_of(layer.forward(x, lg, 3, path="gemv", topk_weights="softmax_all", workspace_limit=1 << 40))
+        torch.cuda.synchronize()
+        ref = oracle.moe(inp, renorm=False)
+        res = compare(y, ref["y"], ref["y64"], spec.act_dtype)
+        log(f"[combo] T={T} gemv tiles: max_row_rel={res['max_row_rel']:.3e}")
+        assert res["ok"], res
+    else:
+        run_case(spec, T, 121 + T, path=path, expert_bias=0.1, topk_weights="softmax_all")
