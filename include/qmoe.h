@@ -264,7 +264,8 @@ qmoe_status qmoe_forward(const qmoe_layer_desc *desc, const void *packed, const 
  * diagnostic outputs, stage events, expert biases, routing-weight mode and
  * row tiling (opts may be NULL: the defaults of qmoe_forward).  UNSUPPORTED
  * if path = GEMV and T > 16, and for f32 activations where the grouped path
- * would run. */
+ * would run, unless a workspace limit runs the call in row tiles of at most
+ * 16 rows. */
 qmoe_status qmoe_forward_ex(const qmoe_layer_desc *desc, const void *packed, const void *x,
                             const float *logits, int32_t T, int32_t top_k, void *y,
                             void *ws, size_t ws_bytes, void *stream,
