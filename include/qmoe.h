@@ -99,8 +99,9 @@ typedef enum qmoe_qtype {
 } qmoe_qtype;
 
 typedef enum qmoe_path {
-  QMOE_PATH_AUTO = 0,    /* GEMV kernels when every expert row count can be <= 16, else grouped */
-  QMOE_PATH_GEMV = 1,    /* register-accumulator GEMV kernels (needs T <= 16) */
+  QMOE_PATH_AUTO = 0,    /* GEMV kernels when every expert row count can be <= 16 (T <= 16), or in
+                            row tiles of <= 16 rows for a layer with no grouped path; else grouped */
+  QMOE_PATH_GEMV = 1,    /* register-accumulator GEMV kernels (needs T <= 16, or row tiles) */
   QMOE_PATH_GROUPED = 2  /* grouped MFMA kernels over expert row tiles */
 } qmoe_path;
 
@@ -130,10 +131,13 @@ typedef struct qmoe_layer_desc {
   int32_t hidden;      /* H */
   int32_t inter;       /* I */
   int32_t act_dtype;   /* QMOE_DTYPE_BF16, F16 or F32: x and y.  F32 (onnx-genai pull request
-                          1167, Parity: f16/bf16/f32 decode) runs the GEMV path only (T <= 16;
-                          larger T or a forced grouped path: QMOE_ERR_UNSUPPORTED), with x
-                          split into bf16 hi + lo parts for the matrix cores, y rounded once to
-                          f32, and no expert biases (QMOE_ERR_UNSUPPORTED) */
+                          1167, Parity: f16/bf16/f32 decode) runs the GEMV path only: above 16
+                          tokens the call runs by itself in GEMV-path row tiles of at most 16
+                          rows (see qmoe_forward_opts.workspace_limit), and a forced grouped
+                          path returns QMOE_ERR_UNSUPPORTED.  x enters the matrix cores as two
+                          bf16 parts, hi = RNE(x) and lo = RNE(x - hi), which carry about 16 of
+                          x's 24 significand bits (relative error below 2^-16 per element);
+                          y is rounded once to f32; no expert biases (QMOE_ERR_UNSUPPORTED) */
   qmoe_qmatrix_desc fc1;
   qmoe_qmatrix_desc fc2;
   int32_t activation;  /* qmoe_activation */
@@ -179,17 +183,19 @@ typedef struct qmoe_forward_opts {
   /* Row tiling under a workspace budget (onnxruntime pull request 33005,
      Current Scope: the prefill is row-tiled to keep its temporary scratch
      within a budget, the tile size halved until it fits, full and final
-     partial tiles sized explicitly).  0: no limit, all T tokens in one pass.
-     Otherwise the tokens run in consecutive tiles of R rows and a final tile
-     of the rest, R = T halved (rounding up) until the workspace of a full
-     tile and of the final tile each fit in workspace_limit bytes; each tile
-     takes its own path (auto: by its row count), and a tile size whose path
-     is not built (f32 activations or a forced GEMV path above 16 rows) is
-     halved further too, so such calls can run in tiles.  ws_bytes must hold the
-     tile workspace that qmoe_forward_plan reports.  counts_out and events
-     need a single tile (QMOE_ERR_UNSUPPORTED otherwise); ids_out, w_out and
-     h_out are written as without tiling.  If one row does not fit:
-     QMOE_ERR_WORKSPACE_TOO_SMALL.  Must not be negative. */
+     partial tiles sized explicitly).  0: no limit.
+     The tokens run in consecutive tiles of R rows and a final tile of the
+     rest.  R starts at T and is halved (rounding up) while it exceeds the
+     row bound of the path -- 16 rows when the layer has no grouped path (f32
+     activations, or an affine format with more than 80 blocks per row), with
+     or without a limit, or when a call with a limit is pinned to the GEMV
+     path -- then while the workspace of a full tile or of the final tile
+     exceeds workspace_limit bytes.  Each tile takes its own path (auto: by
+     its row count).  ws_bytes must hold the tile workspace that
+     qmoe_forward_plan reports.  counts_out and events need a single tile
+     (QMOE_ERR_UNSUPPORTED otherwise); ids_out, w_out and h_out are written
+     as without tiling.  If one row does not fit: QMOE_ERR_WORKSPACE_TOO_SMALL.
+     Must not be negative. */
   int64_t workspace_limit;
 } qmoe_forward_opts;
 
@@ -263,9 +269,9 @@ qmoe_status qmoe_forward(const qmoe_layer_desc *desc, const void *packed, const 
 /* qmoe_forward with the options of qmoe_forward_opts: path choice,
  * diagnostic outputs, stage events, expert biases, routing-weight mode and
  * row tiling (opts may be NULL: the defaults of qmoe_forward).  UNSUPPORTED
- * if path = GEMV and T > 16, and for f32 activations where the grouped path
- * would run, unless a workspace limit runs the call in row tiles of at most
- * 16 rows. */
+ * if path = GEMV and T > 16 without a workspace limit, and if path = GROUPED
+ * for a layer the grouped kernels do not take (f32 activations, or an affine
+ * format with more than 80 blocks per row). */
 qmoe_status qmoe_forward_ex(const qmoe_layer_desc *desc, const void *packed, const void *x,
                             const float *logits, int32_t T, int32_t top_k, void *y,
                             void *ws, size_t ws_bytes, void *stream,

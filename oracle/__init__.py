@@ -59,6 +59,9 @@ def lib():
         L.orc_moe.restype = C.c_int
         L.orc_moe.argtypes = ([C.c_int] * 5 + [C.c_int] * 3 + [P] * 3 + [C.c_int] * 3 + [P] * 3
                               + [P, P, C.c_int, C.c_int] + [P, P, C.c_int] + [P] * 5)
+        L.orc_moe_f32acc.restype = C.c_int
+        L.orc_moe_f32acc.argtypes = ([C.c_int] * 5 + [C.c_int] * 3 + [P] * 3 + [C.c_int] * 3 + [P] * 3
+                                     + [P, P, C.c_int, P, P])
         L.orc_linear.argtypes = [C.c_int, C.c_int, C.c_int, P, P, P, i64, i64, P, C.c_int, C.c_int,
                                  i64, i64, P, P]
         _lib = L
@@ -130,19 +133,33 @@ def route(logits, top_k: int, renorm: bool = True):
 
 
 # -------------------------------------------------------------------- MoE
-def moe(inp: dict, debug: bool = False, tokens=None, renorm: bool = True):
+def moe(inp: dict, debug: bool = False, tokens=None, renorm: bool = True, threads: int = 1):
     """One MoE layer on the canonical inputs of ``synth.moe_inputs``.
 
     ``tokens`` selects a subset of token rows (each token's output depends
     only on its own activation and logits).  Optional ``fc1_expert_bias``
     [E][2I] and ``fc2_expert_bias`` [E][H] (16-bit patterns of the activation
     dtype) are per-expert output biases of FC1 and FC2.  ``renorm`` selects
-    the routing weights as in ``route``.  Returns a dict with ``y64``
+    the routing weights as in ``route``.  ``threads`` > 1 evaluates disjoint token
+    subsets on that many host threads (the C library runs without the
+    interpreter lock); a token's result does not depend on the others, so
+    the outputs are identical to one thread.  Returns a dict with ``y64``
     (float64, unrounded), ``y`` (16-bit patterns of the activation dtype, or
     float32 values for f32 activations) and,
     with ``debug``, per-slot ``a``/``h``/``o`` in slot order t*k+j.
     """
     sp = inp["spec"]
+    if threads > 1:
+        idx = list(range(np.asarray(inp["x"]).shape[0])) if tokens is None else list(tokens)
+        if len(idx) > 1:
+            from concurrent.futures import ThreadPoolExecutor
+            parts = [p for p in np.array_split(np.asarray(idx, dtype=np.int64), min(threads, len(idx))) if p.size]
+            with ThreadPoolExecutor(len(parts)) as ex:
+                outs = list(ex.map(lambda p: moe(inp, debug, p.tolist(), renorm, 1), parts))
+            res = {"status": min(o["status"] for o in outs)}
+            for key in ("y64", "y") + (("a", "h", "o") if debug else ()):
+                res[key] = np.concatenate([o[key] for o in outs])
+            return res
     adt = np.float32 if sp.act_dtype == "f32" else np.uint16   # f32 activations as values
     x = _c(inp["x"], adt)
     lg = _c(inp["logits"], np.float32)
@@ -173,6 +190,35 @@ def moe(inp: dict, debug: bool = False, tokens=None, renorm: bool = True):
     if debug:
         out.update(a=a, h=h, o=o)
     return out
+
+
+def moe_f32acc(inp: dict, tokens=None):
+    """The layer with every sum in single precision (``orc_moe_f32acc``):
+    float dequantized weights, float dot products with k ascending, float
+    silu, top-k weights and combine, one rounding to the activation dtype.
+    SwiGLU, renormalised top-k weights, no expert biases.  Returns ``y32``
+    (float32 sums) and ``y`` (rounded, as in ``moe``)."""
+    sp = inp["spec"]
+    assert sp.activation == "swiglu" and inp.get("fc1_expert_bias") is None
+    adt = np.float32 if sp.act_dtype == "f32" else np.uint16
+    x = _c(inp["x"], adt)
+    lg = _c(inp["logits"], np.float32)
+    if tokens is not None:
+        x = np.ascontiguousarray(x[tokens])
+        lg = np.ascontiguousarray(lg[tokens])
+    T = x.shape[0]
+    y32 = np.empty((T, sp.H), dtype=np.float32)
+    y = np.empty((T, sp.H), dtype=adt)
+    arr = {n: _c(inp[n], np.uint8 if n.endswith("codes") else np.uint16)
+           for n in ("fc1_codes", "fc1_scales", "fc1_biases", "fc2_codes", "fc2_scales", "fc2_biases")}
+    rc = lib().orc_moe_f32acc(
+        sp.E, sp.H, sp.I, sp.top_k, DT[sp.act_dtype],
+        FMT[sp.fc1.fmt], sp.fc1.block, DT[sp.fc1.scale_dtype],
+        _p(arr["fc1_codes"]), _p(arr["fc1_scales"]), _p(arr["fc1_biases"]),
+        FMT[sp.fc2.fmt], sp.fc2.block, DT[sp.fc2.scale_dtype],
+        _p(arr["fc2_codes"]), _p(arr["fc2_scales"]), _p(arr["fc2_biases"]),
+        _p(x), _p(lg), T, _p(y32), _p(y))
+    return {"y32": y32, "y": y, "status": rc}
 
 
 def linear(inp: dict, n0: int = 0, n1=None):

@@ -321,6 +321,96 @@ int orc_moe(int E, int H, int I, int k, int act_dtype,
 }
 
 /*
+ * The same layer with every sum in single precision: weights dequantized to
+ * float (w = s*q is exact in float; affine s*q + b rounds once), each dot
+ * product accumulated in float with k ascending, silu from the float expf,
+ * the top-k weights in float, the combine in float with j ascending from 0,
+ * and one round to nearest even from the float sum to the activation dtype.
+ * This is the fp32-accumulation reading of the layer; it serves as a second
+ * evaluation of the same definitions in another precision, which must agree
+ * with orc_moe's double-precision sums to within fp32 rounding.  Writes the
+ * float sums to y32 [T][H] and the rounded outputs to y_out.  No expert
+ * biases, ReLU or diagnostics.  Returns 0, or -1 for an invalid ternary field.
+ */
+static void orc_dequant_row_f32(int fmt, int block, int sdtype, const uint8_t *codes_row,
+                                const uint16_t *scales_row, const uint16_t *biases_row,
+                                int64_t K, float *w, int *bad) {
+  const int bits = orc_bits(fmt);
+  for (int64_t k = 0; k < K; ++k) {
+    int q = orc_code(fmt, orc_field(codes_row, bits, k), bad);
+    float s = (float)orc_half_to_double(scales_row[k / block], sdtype);
+    float v = s * (float)q;
+    if (orc_is_affine(fmt)) v = v + (float)orc_half_to_double(biases_row[k / block], sdtype);
+    w[k] = v;
+  }
+}
+
+static void orc_matvec_f32(const orc_mat *m, int64_t e, int64_t N, int64_t K, const float *v,
+                           float *out, float *wrow, int *bad) {
+  const int64_t row_bytes = K * orc_bits(m->fmt) / 8, nb = K / m->block;
+  for (int64_t n = 0; n < N; ++n) {
+    const int64_t r = e * N + n;
+    orc_dequant_row_f32(m->fmt, m->block, m->sdtype, m->codes + r * row_bytes, m->scales + r * nb,
+                        m->biases ? m->biases + r * nb : NULL, K, wrow, bad);
+    float acc = 0.0f;
+    for (int64_t k = 0; k < K; ++k) acc = acc + wrow[k] * v[k];
+    out[n] = acc;
+  }
+}
+
+int orc_moe_f32acc(int E, int H, int I, int k, int act_dtype,
+                   int fc1_fmt, int fc1_block, int fc1_sdtype,
+                   const uint8_t *fc1_codes, const uint16_t *fc1_scales, const uint16_t *fc1_biases,
+                   int fc2_fmt, int fc2_block, int fc2_sdtype,
+                   const uint8_t *fc2_codes, const uint16_t *fc2_scales, const uint16_t *fc2_biases,
+                   const void *x, const float *logits, int T, float *y32, void *y_out) {
+  orc_mat w1 = {fc1_fmt, fc1_block, fc1_sdtype, fc1_codes, fc1_scales, fc1_biases};
+  orc_mat w2 = {fc2_fmt, fc2_block, fc2_sdtype, fc2_codes, fc2_scales, fc2_biases};
+  const int64_t S = (int64_t)T * k;
+  int32_t *ids = (int32_t *)malloc(sizeof(int32_t) * (size_t)(S > 0 ? S : 1));
+  double *wd = (double *)malloc(sizeof(double) * (size_t)(S > 0 ? S : 1));
+  int32_t *counts = (int32_t *)malloc(sizeof(int32_t) * (size_t)E);
+  int32_t *offsets = (int32_t *)malloc(sizeof(int32_t) * (size_t)(E + 1));
+  int32_t *rows = (int32_t *)malloc(sizeof(int32_t) * (size_t)(S > 0 ? S : 1));
+  float *xv = (float *)malloc(sizeof(float) * (size_t)H);
+  float *a = (float *)malloc(sizeof(float) * (size_t)(2 * (int64_t)I));
+  float *h = (float *)malloc(sizeof(float) * (size_t)I);
+  float *o = (float *)malloc(sizeof(float) * (size_t)H);
+  float *wrow = (float *)malloc(sizeof(float) * (size_t)(H > I ? H : I));
+  int bad = 0;
+  /* the selection is the same; the weights are recomputed in float */
+  orc_route(T, E, k, 1, logits, ids, wd, counts, offsets, rows);
+  for (int t = 0; t < T; ++t) {
+    const float *l = logits + (int64_t)t * E;
+    const float m = l[ids[(int64_t)t * k]];
+    float sum = 0.0f;
+    for (int j = 0; j < k; ++j) sum = sum + expf(l[ids[(int64_t)t * k + j]] - m);
+    for (int64_t n = 0; n < H; ++n) xv[n] = (float)orc_act(x, (int64_t)t * H + n, act_dtype);
+    float *yt = y32 + (int64_t)t * H;
+    for (int64_t n = 0; n < H; ++n) yt[n] = 0.0f;
+    for (int j = 0; j < k; ++j) {
+      const int64_t r = (int64_t)t * k + j;
+      const int e = ids[r];
+      const float wt = expf(l[ids[r]] - m) / sum;
+      orc_matvec_f32(&w1, e, 2 * (int64_t)I, H, xv, a, wrow, &bad);
+      for (int64_t i = 0; i < I; ++i) {
+        const float g = a[2 * i];
+        h[i] = g / (1.0f + expf(-g)) * a[2 * i + 1];
+      }
+      orc_matvec_f32(&w2, e, H, I, h, o, wrow, &bad);
+      for (int64_t n = 0; n < H; ++n) yt[n] = yt[n] + wt * o[n];
+    }
+    for (int64_t n = 0; n < H; ++n) {
+      if (act_dtype == ORC_F32) ((float *)y_out)[(int64_t)t * H + n] = yt[n];
+      else ((uint16_t *)y_out)[(int64_t)t * H + n] = orc_double_to_half((double)yt[n], act_dtype);
+    }
+  }
+  free(ids); free(wd); free(counts); free(offsets); free(rows);
+  free(xv); free(a); free(h); free(o); free(wrow);
+  return bad ? -1 : 0;
+}
+
+/*
  * Dense quantized matmul y = x W^T for output rows n in [n0, n1):
  * y64 [M][n1-n0] unrounded, y16 the same rounded to x's dtype.
  */

@@ -12,8 +12,7 @@ import ctypes as C
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-# QMOE_LIBRARY selects another build of the same library (e.g. a tuning variant).
-LIB_PATH = os.environ.get("QMOE_LIBRARY") or os.path.join(HERE, "libqmoe.so")
+LIB_PATH = os.path.join(HERE, "libqmoe.so")
 
 QTYPE = {"sym_int4": 0, "sym_int2": 1, "ternary": 2, "affine_int2": 3, "affine_int4": 4}
 DTYPE = {"bf16": 0, "f16": 1, "f32": 2}

@@ -184,12 +184,8 @@ struct MoeWs {
 constexpr size_t kLdsLimit = kGemvLdsLimit;
 
 // Waves on the chip that a GEMV launch aims for when the kernel's occupancy
-// is unknown; the environment variable QMOE_GEMV_TARGET_WAVES overrides it.
-int64_t gemv_target_waves() {
-  const char *e = getenv("QMOE_GEMV_TARGET_WAVES");
-  const long long x = e ? atoll(e) : 0;
-  return x > 0 ? (int64_t)x : (int64_t)4096;
-}
+// is unknown.
+constexpr int64_t kGemvTargetWaves = 4096;
 
 // Compute units of the current device (256 on MI355X when there is none).
 int device_cus() {
@@ -219,16 +215,8 @@ GemvShape pick_gemv(int64_t nwg, const MatLayout &L, int rows, int epilogue, int
   const int64_t kmax = std::min<int64_t>(kGemvMaxWaves, L.NKT);
   const int64_t cus = device_cus();
   // four n-tiles per wave unless that leaves compute units idle
-  int tn = nwg < cus ? 1 : 4;
-  if (const char *e = getenv("QMOE_GEMV_TN")) {  // tuning override
-    const int v = atoi(e);
-    if (v == 1 || v == 4) tn = v;
-  }
+  const int tn = nwg < cus ? 1 : 4;
   nwg *= 4 / tn;
-  if (const char *e = getenv("QMOE_GEMV_WAVES")) {  // tuning override
-    const long long w = atoll(e);
-    if (w > 0) return {(int)std::min<int64_t>(w, kmax), tn};
-  }
   int best = 0;
   int64_t best_cost = 0;
   for (int ks = 1; ks <= kmax; ++ks) {
@@ -248,7 +236,7 @@ GemvShape pick_gemv(int64_t nwg, const MatLayout &L, int rows, int epilogue, int
     }
   }
   if (best > 0) return {best, tn};
-  int64_t ks = (gemv_target_waves() + nwg - 1) / std::max<int64_t>(nwg, 1);
+  int64_t ks = (kGemvTargetWaves + nwg - 1) / std::max<int64_t>(nwg, 1);
   ks = std::max<int64_t>(1, std::min<int64_t>(ks, kmax));
   while (ks > 1 && gemv_lds_bytes(rows, epilogue, (int)ks, tn) > kLdsLimit) --ks;
   return {(int)ks, tn};
@@ -269,23 +257,40 @@ int gemv_in_mode(int act_dtype) {
   return act_dtype == QMOE_DTYPE_F32 ? kGemvInSplitF32 : act_dtype == QMOE_DTYPE_F16 ? 1 : 0;
 }
 
+// Whether the grouped kernels take this layer: 16-bit activations, and affine
+// formats with at most kGroupedMaxAffineBlocks blocks per row (their per-row
+// block sums live in LDS).
+bool grouped_supported(const qmoe_layer_desc &d) {
+  if (d.act_dtype == QMOE_DTYPE_F32) return false;
+  const MoeLayout L = MoeLayout::make(d);
+  return !((L.fc1.affine && L.fc1.nblk > kGroupedMaxAffineBlocks) ||
+           (L.fc2.affine && L.fc2.nblk > kGroupedMaxAffineBlocks));
+}
+
+// Largest tile a call may run as one pass: the GEMV path's row bound when
+// the call is pinned to it or the layer has no grouped path.
+int32_t path_row_bound(const qmoe_layer_desc &d, int path_req) {
+  if (path_req == QMOE_PATH_GEMV || (path_req == QMOE_PATH_AUTO && !grouped_supported(d))) return kGemvMaxRows;
+  return INT32_MAX;
+}
+
 qmoe_status make_plan(const qmoe_layer_desc &d, int32_t T, int32_t k, int path_req, bool softmax_all, Plan &p) {
   const MoeLayout L = MoeLayout::make(d);
   p = Plan{};
   int path = path_req;
-  if (path == QMOE_PATH_AUTO) path = (T <= kGemvMaxRows) ? QMOE_PATH_GEMV : QMOE_PATH_GROUPED;
-  if (path != QMOE_PATH_GEMV && path != QMOE_PATH_GROUPED)
+  if (path != QMOE_PATH_AUTO && path != QMOE_PATH_GEMV && path != QMOE_PATH_GROUPED)
     return fail(QMOE_ERR_INVALID_ARGUMENT, "unknown path %d", path_req);
+  if (path == QMOE_PATH_AUTO)
+    path = (T <= kGemvMaxRows || !grouped_supported(d)) ? QMOE_PATH_GEMV : QMOE_PATH_GROUPED;
   if (path == QMOE_PATH_GEMV && T > kGemvMaxRows)
-    return fail(QMOE_ERR_UNSUPPORTED, "GEMV path needs T <= %d (got %d)", kGemvMaxRows, T);
+    return fail(QMOE_ERR_UNSUPPORTED, "GEMV path needs T <= %d (got %d)%s", kGemvMaxRows, T,
+                path_req == QMOE_PATH_AUTO ? ": this layer has no grouped path, run it in row tiles" : "");
   p.path = path;
   p.max_active = (int)std::min<int64_t>(d.num_experts, (int64_t)T * k);
   const bool f32 = d.act_dtype == QMOE_DTYPE_F32;
-  if (f32 && path == QMOE_PATH_GROUPED)
-    return fail(QMOE_ERR_UNSUPPORTED, "f32 activations run on the GEMV path only (T <= %d, got %d)", kGemvMaxRows, T);
   if (path == QMOE_PATH_GROUPED) {
-    if ((L.fc1.affine && L.fc1.nblk > kGroupedMaxAffineBlocks) ||
-        (L.fc2.affine && L.fc2.nblk > kGroupedMaxAffineBlocks))
+    if (f32) return fail(QMOE_ERR_UNSUPPORTED, "f32 activations run on the GEMV path only");
+    if (!grouped_supported(d))
       return fail(QMOE_ERR_UNSUPPORTED, "affine formats on the grouped path need K/block <= %d",
                   kGroupedMaxAffineBlocks);
     p.route_fused = (T <= 16) ? 1 : 0;
@@ -501,17 +506,19 @@ qmoe_status tile_need(const qmoe_layer_desc &d, int32_t T, int32_t k, int path_r
   return QMOE_OK;
 }
 
+// Row tiles of one call: R starts at T and is halved (rounding up) while it
+// exceeds the row bound of the path (the GEMV path's 16 rows when the layer
+// has no grouped path, or when a call with a workspace limit is pinned to the
+// GEMV path), then while a full tile's or the final tile's workspace exceeds
+// `limit` (0: no limit).
 qmoe_status pick_tiling(const qmoe_layer_desc &d, int32_t T, int32_t k, int path_req, bool softmax_all,
                         int64_t limit, Tiling &t) {
   int32_t R = T;
+  const int32_t bound = path_row_bound(d, path_req);
+  if (path_req == QMOE_PATH_AUTO || limit > 0)
+    while (R > bound) R = (R + 1) / 2;
   for (;;) {
     qmoe_status st = tile_need(d, T, k, path_req, softmax_all, R, t);
-    // a tile size whose path is not built (f32 activations or a forced GEMV
-    // path above its row bound) counts as not fitting: halve further
-    if (st == QMOE_ERR_UNSUPPORTED && limit > 0 && R > 1) {
-      R = (R + 1) / 2;
-      continue;
-    }
     if (st != QMOE_OK) return st;
     if (limit <= 0 || t.ws <= limit) return QMOE_OK;
     if (R == 1)
@@ -519,6 +526,15 @@ qmoe_status pick_tiling(const qmoe_layer_desc &d, int32_t T, int32_t k, int path
                   (long long)t.ws, (long long)limit);
     R = (R + 1) / 2;
   }
+}
+
+// A call runs in row tiles when it has a workspace limit, or when the layer
+// has no grouped path and the tokens exceed the GEMV path's row bound.
+bool call_tiled(const qmoe_layer_desc &d, int32_t T, const qmoe_forward_opts *opts) {
+  if (T <= 0) return false;
+  if (opts && opts->workspace_limit > 0) return true;
+  const int path_req = opts ? opts->path : QMOE_PATH_AUTO;
+  return path_req == QMOE_PATH_AUTO && T > path_row_bound(d, path_req);
 }
 
 qmoe_status qmoe_forward_plan(const qmoe_layer_desc *desc, int32_t T, int32_t top_k,
@@ -531,12 +547,13 @@ qmoe_status qmoe_forward_plan(const qmoe_layer_desc *desc, int32_t T, int32_t to
   const bool softmax_all = opts && opts->topk_weights == QMOE_TOPK_SOFTMAX_ALL;
   if (opts && opts->workspace_limit < 0) return fail(QMOE_ERR_INVALID_ARGUMENT, "negative workspace_limit");
   // with a workspace limit, the plan of a full tile (and the totals over all tiles)
-  const bool tiled = T > 0 && opts && opts->workspace_limit > 0;
+  const bool tiled = call_tiled(*desc, T, opts);
   Tiling tl;
   tl.rows = T;
   tl.tiles = T == 0 ? 0 : 1;
   if (tiled) {
-    st = pick_tiling(*desc, T, top_k, opts->path, softmax_all, opts->workspace_limit, tl);
+    st = pick_tiling(*desc, T, top_k, opts ? opts->path : QMOE_PATH_AUTO, softmax_all,
+                     opts ? opts->workspace_limit : 0, tl);
     if (st != QMOE_OK) return st;
   }
   Plan p;
@@ -576,13 +593,14 @@ qmoe_status qmoe_forward_ex(const qmoe_layer_desc *desc, const void *packed, con
     return fail(QMOE_ERR_UNSUPPORTED, "expert biases need 16-bit activations");
   if (T == 0) return ok();
   const bool softmax_all = opts && opts->topk_weights == QMOE_TOPK_SOFTMAX_ALL;
-  if (opts && opts->workspace_limit > 0) {
+  if (call_tiled(*desc, T, opts)) {
     Tiling tl;
-    st = pick_tiling(*desc, T, top_k, opts->path, softmax_all, opts->workspace_limit, tl);
+    st = pick_tiling(*desc, T, top_k, opts ? opts->path : QMOE_PATH_AUTO, softmax_all,
+                     opts ? opts->workspace_limit : 0, tl);
     if (st != QMOE_OK) return st;
     if (tl.tiles > 1) {
       // everything a tile could reject is checked here, before the first launch
-      if (opts->counts_out || opts->num_events > 0)
+      if (opts && (opts->counts_out || opts->num_events > 0))
         return fail(QMOE_ERR_UNSUPPORTED, "counts_out and events need a single tile (%d tiles)", tl.tiles);
       if (!packed || !x || !logits || !y || !ws) return fail(QMOE_ERR_INVALID_ARGUMENT, "null device pointer");
       if (!aligned(packed, kAlign) || !aligned(ws, kAlign))
@@ -594,16 +612,17 @@ qmoe_status qmoe_forward_ex(const qmoe_layer_desc *desc, const void *packed, con
                     (long long)tl.ws);
       // tiles in order on the stream, sharing the workspace; a tile's rows
       // start at row t0 of x, logits, y and the per-slot diagnostics
-      qmoe_forward_opts o = *opts;
+      qmoe_forward_opts o{};
+      if (opts) o = *opts;
       o.workspace_limit = 0;
       const int64_t H = desc->hidden, E = desc->num_experts, I = desc->inter;
       const int64_t act_bytes = desc->act_dtype == QMOE_DTYPE_F32 ? 4 : 2;
       for (int32_t t0 = 0; t0 < T; t0 += tl.rows) {
         const int32_t n = std::min(tl.rows, T - t0);
         const int64_t s0 = (int64_t)t0 * top_k;
-        o.h_out = opts->h_out ? opts->h_out + s0 * I : nullptr;
-        o.ids_out = opts->ids_out ? opts->ids_out + s0 : nullptr;
-        o.w_out = opts->w_out ? opts->w_out + s0 : nullptr;
+        o.h_out = opts && opts->h_out ? opts->h_out + s0 * I : nullptr;
+        o.ids_out = opts && opts->ids_out ? opts->ids_out + s0 : nullptr;
+        o.w_out = opts && opts->w_out ? opts->w_out + s0 : nullptr;
         const int64_t xoff = (int64_t)t0 * H * act_bytes;  // bytes: rows of x and y
         st = qmoe_forward_ex(desc, packed, (const uint8_t *)x + xoff, logits + (int64_t)t0 * E, n, top_k,
                              (uint8_t *)y + xoff, ws, ws_bytes, stream, &o);

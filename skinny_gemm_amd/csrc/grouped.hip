@@ -516,9 +516,9 @@ __global__ __launch_bounds__(256) void grouped_kernel(const GroupedArgs a) {
   float bv[NJ];
 #pragma unroll
   for (int j = 0; j < NJ; ++j)
-    bv[j] = a.bias ? half_to_f32_rt(a.bias[(int64_t)e * a.N + nw + 16 * j + (lane & 15)],
-                                    a.act_dtype == QMOE_DTYPE_F16)
-                   : 0.f;
+    bv[j] = (a.bias && wave_on) ? half_to_f32_rt(a.bias[(int64_t)e * a.N + nw + 16 * j + (lane & 15)],
+                                                 a.act_dtype == QMOE_DTYPE_F16)
+                                : 0.f;  // idle waves of a partial last tile read nothing
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
 #pragma unroll

@@ -270,10 +270,11 @@ def test_plan_f32_activations():
     assert p1["kernels"] == ["split_x", "route_fc1_swiglu", "gemv_fc2", "combine"] and p1["num_launches"] == 4
     b = q.forward_plan(_desc(), 4, 6)["workspace_bytes"]
     assert q.forward_plan(d, 4, 6)["workspace_bytes"] == b + 2 * (4 * 2048 * 2)   # x hi + lo rows
-    for T, path in ((17, "auto"), (4, "grouped")):
-        with pytest.raises(q.QmoeError) as ei:
-            q.forward_plan(d, T, 6, path)
-        assert ei.value.status == 2
+    with pytest.raises(q.QmoeError) as ei:
+        q.forward_plan(d, 4, 6, "grouped")
+    assert ei.value.status == 2
+    p17 = q.forward_plan(d, 17, 6)          # no grouped path: GEMV row tiles by itself
+    assert (p17["row_tile"], p17["num_tiles"], p17["path"]) == (9, 2, 1)
     L = q.lib()
     fake = C.c_void_p(0x100000)
     o = q.ForwardOpts(0, 0, None, None, None, None, None, 0, 0, fake, None, 0, 0, 0)   # expert bias
@@ -301,12 +302,28 @@ def test_relu_layer_descriptor_and_plan():
 
 
 def test_row_tiling_reaches_the_gemv_path():
-    """f32 activations above 16 rows, or a forced GEMV path, run in tiles of
-    at most 16 rows when a workspace limit is given."""
+    """A layer the grouped kernels cannot take (f32 activations, or an affine
+    format with more than 80 blocks per row) runs above 16 rows in GEMV-path
+    tiles of at most 16 rows, with or without a workspace limit; a call pinned
+    to the GEMV path does so only under a workspace limit."""
     d = _desc(act="f32")
-    with pytest.raises(q.QmoeError):
-        q.forward_plan(d, 40, 6)
-    p = q.forward_plan(d, 40, 6, workspace_limit=1 << 40)
-    assert (p["row_tile"], p["num_tiles"], p["path"]) == (10, 4, 1)
+    for lim in (0, 1 << 40):
+        p = q.forward_plan(d, 40, 6, workspace_limit=lim)
+        assert (p["row_tile"], p["num_tiles"], p["path"]) == (10, 4, 1)
+    aff = q.layer_desc(8, 6144, 256, "bf16", ("affine_int2", 64, "f16"), ("affine_int2", 64, "f16"))
+    pa = q.forward_plan(aff, 100, 2)
+    assert pa["path"] == 1 and pa["row_tile"] <= 16 and pa["num_tiles"] * pa["row_tile"] >= 100
+    with pytest.raises(q.QmoeError) as ei:
+        q.forward_plan(aff, 100, 2, "grouped")
+    assert ei.value.status == 2
+    # a grouped-capable layer keeps one pass on the grouped path
+    assert q.forward_plan(_desc(), 100, 6)["num_tiles"] == 1
+    with pytest.raises(q.QmoeError) as ei:
+        q.forward_plan(_desc(), 100, 6, path="gemv")
+    assert ei.value.status == 2
     g = q.forward_plan(_desc(), 100, 6, path="gemv", workspace_limit=1 << 40)
     assert g["row_tile"] <= 16 and g["path"] == 1
+    # a workspace limit alone never turns a supported grouped call into GEMV tiles
+    big = q.forward_plan(_desc(), 100, 6)["workspace_bytes"]
+    t = q.forward_plan(_desc(), 100, 6, workspace_limit=big // 2)
+    assert t["num_tiles"] >= 2 and t["path"] == 2

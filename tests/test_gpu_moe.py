@@ -5,6 +5,7 @@ Within the stated tolerance (see tests/metrics.py): the layer output.
 """
 
 import functools
+import os
 import sys
 
 import numpy as np
@@ -50,19 +51,25 @@ def _inputs(spec, T, seed, logits_mode="iid", expert_bias=0.0):
     return synth.moe_inputs(spec, T, seed, logits_mode, expert_bias=expert_bias)
 
 
+# host threads for the oracle (the GPU machine's CPU share is 16 cores)
+ORACLE_THREADS = max(1, min(16, len(os.sched_getaffinity(0))))
+
+
 def run_case(spec, T, seed, logits_mode="iid", path="auto", tokens=None, expert_bias=0.0,
-             topk_weights="renormalized"):
+             topk_weights="renormalized", x_edit=None):
     from skinny_gemm_amd.layer import MoeLayer, to_device_bits, bits_of
     renorm = topk_weights == "renormalized"
     log(f"[moe] {spec.name} T={T} seed={seed} logits={logits_mode} path={path} expert_bias={expert_bias} "
-        f"topk_weights={topk_weights}")
+        f"topk_weights={topk_weights} edit={x_edit is not None} tokens={None if tokens is None else len(tokens)}")
     inp = _inputs(spec, T, seed, logits_mode, expert_bias)
+    if x_edit is not None:
+        inp["x"] = x_edit(inp["x"].copy(), spec)
     layer = MoeLayer.from_spec(spec, inp)
     x = to_device_bits(inp["x"], spec.act_dtype)
     lg = torch.from_numpy(inp["logits"]).cuda()
     y, dbg = layer.forward(x, lg, spec.top_k, path=path, debug=True, topk_weights=topk_weights)
     torch.cuda.synchronize()
-    ref = oracle.moe(inp, debug=True, tokens=tokens, renorm=renorm)
+    ref = oracle.moe(inp, debug=True, tokens=tokens, renorm=renorm, threads=ORACLE_THREADS)
     r = oracle.route(inp["logits"] if tokens is None else inp["logits"][tokens], spec.top_k, renorm)
     ybits = bits_of(y)
     if tokens is not None:
@@ -83,9 +90,10 @@ def run_case(spec, T, seed, logits_mode="iid", path="auto", tokens=None, expert_
     res = compare(ybits, ref["y"], ref["y64"], spec.act_dtype)
     log(f"       y: max_row_rel={res['max_row_rel']:.3e} identical={res['frac_identical']:.4f} "
         f"vs_exact={res['max_row_rel_vs_exact']:.3e} h_rel={hn.max():.3e}")
-    # h is a diagnostic (the gate is y): the MFMA path rounds weights of
-    # 4-bit affine codes or f16 scales once to f16, about 2^-11 relative
-    assert hn.max() < 4e-3, f"h row error {hn.max()}"
+    # h is a diagnostic (the gate is y), held to the same 2e-3 row bound:
+    # the kernels' weights are exact and h is an fp32 sum (the GEMV path
+    # hands it to FC2 as a bf16 hi + lo pair, about 16 significant bits)
+    assert hn.max() < 2e-3, f"h row error {hn.max()}"
     assert res["ok"], res
     res["ybits"], res["inp"] = ybits, inp
     return res
@@ -262,17 +270,101 @@ def test_mixed_int2_int4_decode(T):
     run_case(synth.MOE_WORKLOADS["mixed_int2_int4_prefill"], T, 3)
 
 
+def _tile_edge_tokens(logits, k, hottest=4, tile=64):
+    """Tokens whose rows are the first and last row of every 64-row tile of
+    the `hottest` experts with the most rows (from the oracle's own routing
+    lists), so the tile boundaries and the partial last tile of each are
+    compared."""
+    r = oracle.route(logits, k)
+    toks = set()
+    for e in np.argsort(-r["counts"], kind="stable")[:hottest]:
+        lo, hi = int(r["offsets"][e]), int(r["offsets"][e + 1])
+        for p0 in range(lo, hi, tile):
+            for p in (p0, min(p0 + tile, hi) - 1):
+                toks.add(int(r["row_list"][p]) // k)
+    return sorted(toks), r
+
+
 @pytest.mark.parametrize("seed", [0, 1])
 def test_mixed_int2_int4_prefill(seed):
     """2048 tokens, 128 experts, top-8, skewed load: routing checked on every
-    token, outputs on a sample of tokens (the oracle computes them one by one)."""
+    token; outputs on the first and last row of every tile of the 4 hottest
+    experts plus random tokens (the oracle computes them one by one)."""
     spec = synth.MOE_WORKLOADS["mixed_int2_int4_prefill"]
-    rng = np.random.default_rng(seed)
-    sample = np.sort(rng.choice(2048, size=12, replace=False)).tolist()
-    res = run_case(spec, 2048, seed, tokens=sample)
     inp = _inputs(spec, 2048, seed)
-    r = oracle.route(inp["logits"], spec.top_k)
-    log(f"       expert rows: max {r['counts'].max()} min {r['counts'].min()} (mean {r['counts'].mean():.0f})")
+    edges, r = _tile_edge_tokens(inp["logits"], spec.top_k)
+    rng = np.random.default_rng(seed)
+    sample = sorted(set(edges) | set(rng.choice(2048, size=8, replace=False).tolist()))
+    log(f"       expert rows: max {r['counts'].max()} min {r['counts'].min()} (mean {r['counts'].mean():.0f}); "
+        f"{len(sample)} sampled tokens")
+    run_case(spec, 2048, seed, tokens=sample)
+
+
+@pytest.mark.parametrize("cfg,T,logits_mode", [
+    (dict(E=4, H=512, I=256, top_k=2, fc1="sym_int2", fc2="sym_int4"), 300, "shared"),
+    (dict(E=4, H=512, I=256, top_k=2, fc1="sym_int2", fc2="sym_int4"), 300, "iid"),
+    (dict(E=3, H=256, I=384, top_k=2, fc1="affine_int2", fc2="affine_int4", scale_dtype="f16", act_dtype="f16"),
+     200, "shared"),
+    (dict(E=5, H=256, I=256, top_k=3, fc1="ternary", block1=128, fc2="sym_int4", scale_dtype="f16"), 150, "iid"),
+], ids=["int2-int4-shared", "int2-int4-iid", "affine-f16-shared", "ternary-f16-iid"])
+def test_grouped_multi_tile_every_row(cfg, T, logits_mode):
+    """Experts with several 64-row tiles and a partial last one (shared
+    logits: every selected expert gets all T rows), every output row
+    compared with the oracle."""
+    spec = custom_moe_spec(**cfg)
+    inp = _inputs(spec, T, 21, logits_mode)
+    counts = oracle.route(inp["logits"], spec.top_k)["counts"]
+    assert counts.max() > 2 * 64 and np.any((counts > 64) & (counts % 64 != 0)), counts
+    run_case(spec, T, 21, logits_mode=logits_mode, path="grouped")
+
+
+# ------------------------------------------ activation rows at the edges
+def _edge_rows(big, base):
+    """Rows 0-4 replaced: one element of magnitude `big` and the rest about
+    1e-3; all zeros; all tiny (1e-6 * base, bf16 only); three elements of
+    magnitude `big` with both signs and the rest N(0, base^2); one negative
+    element of magnitude `big` and the rest N(0, base^2).  The other rows
+    are N(0, base^2)."""
+    from synth.rng import f32_to_bf16_bits, f32_to_f16_bits
+
+    def edit(xbits, spec):
+        T, H = xbits.shape
+        rng = np.random.default_rng(1234)
+        v = rng.standard_normal((T, H)) * base
+        v[0] = rng.standard_normal(H) * 1e-3
+        v[0, 7] = big
+        if T > 1:
+            v[1] = 0.0
+        if T > 2:
+            v[2] = rng.standard_normal(H) * (1e-6 * base if spec.act_dtype == "bf16" else base)
+        if T > 3:
+            v[3, [1, H // 2, H - 1]] = [big, -big, 0.99 * big]
+        if T > 4:
+            v[4, 3] = -big
+        enc = f32_to_f16_bits if spec.act_dtype == "f16" else f32_to_bf16_bits
+        return enc(v.astype(np.float32)).reshape(T, H)
+    return edit
+
+
+@pytest.mark.parametrize("T,path", [(8, "auto"), (40, "grouped")])
+@pytest.mark.parametrize("kind", ["bf16-3e4", "f16-6e4"])
+def test_activation_edge_rows(kind, T, path):
+    """Rows with a wide dynamic range (one 3e4 element among values of 1e-3;
+    f16 values near 6e4, the top of its range), an all-zero row and an
+    all-tiny row, through the GEMV path and through the grouped path's
+    per-row power-of-two scaling to f16.  The f16 layer has scales and
+    affine biases of magnitude 1e-4 and rows of N(0, 300^2), so its outputs
+    stay inside the normal f16 range."""
+    import dataclasses
+    if kind == "bf16-3e4":
+        spec = custom_moe_spec(E=4, H=256, I=128, top_k=2, fc1="sym_int2", fc2="sym_int4")
+        edit = _edge_rows(3e4, 1.0)
+    else:
+        spec = dataclasses.replace(
+            custom_moe_spec(E=4, H=256, I=128, top_k=2, fc1="affine_int4", fc2="sym_int4", scale_dtype="f16",
+                            act_dtype="f16"), scale_sigma=1e-4, bias_sigma=1e-4, name="edge_f16_small_scales")
+        edit = _edge_rows(6.0e4, 300.0)
+    run_case(spec, T, 31, path=path, x_edit=edit)
 
 
 # ------------------------------------------------- per-expert output biases
@@ -414,7 +506,7 @@ def test_row_tiling_small_tiles(div):
     assert np.array_equal(dbg["ids"].cpu().numpy(), r["ids"])
     h = dbg["h"].cpu().numpy()
     hn = np.linalg.norm(h - ref["h"], axis=1) / np.linalg.norm(ref["h"], axis=1)
-    assert hn.max() < 4e-3
+    assert hn.max() < 2e-3
     res = compare(y, ref["y"], ref["y64"], spec.act_dtype)
     log(f"       y: max_row_rel={res['max_row_rel']:.3e}")
     assert res["ok"], res

@@ -399,3 +399,39 @@ def test_page_byte_and_mac_counts():
     assert synth.canonical_matrix_bytes(sp.fmt, 17408, 5120) == 25067520
     mac = g["FMA per row of the 5120 -> 17408 matmul"]
     assert 5120 * 17408 == mac["exact"] and abs(mac["exact"] - mac["value_approx"]) / mac["value_approx"] < 0.01
+
+
+# ------------------------------------------- fp32 vs fp64 accumulation
+@pytest.mark.parametrize("name,T", [("single_expert_int4", 1), ("switch_base_ternary", 1), ("dsv2lite_int4", 2),
+                                    ("mixed_int2_int4_prefill", 2)])
+def test_fp32_accumulation_agrees_with_fp64(oracle_lib, name, T):
+    """The layer evaluated with every sum in float (the fp32-accumulation
+    reading) and in double: the same definitions in two precisions agree to
+    within fp32 summation error, about sqrt(K) * 2^-24 relative for K-term
+    sums of mixed signs (K <= 4096 here: below 4e-6; gate 2e-5), and their
+    outputs rounded to the activation dtype differ only by rare one-ulp
+    straddles, far inside the 2e-3 row tolerance."""
+    from tests.metrics import compare
+    spec = synth.MOE_WORKLOADS[name]
+    inp = synth.moe_inputs(spec, T, 3)
+    r64 = oracle_lib.moe(inp)
+    r32 = oracle_lib.moe_f32acc(inp)
+    assert r64["status"] == 0 and r32["status"] == 0
+    y32 = r32["y32"].astype(np.float64)
+    rel = np.linalg.norm(y32 - r64["y64"], axis=1) / np.linalg.norm(r64["y64"], axis=1)
+    assert rel.max() < 2e-5, rel.max()
+    res = compare(r32["y"], r64["y"], r64["y64"], spec.act_dtype)
+    assert res["ok"] and res["frac_identical"] > 0.97, res
+
+
+def test_threaded_evaluation_is_identical(oracle_lib):
+    """Token subsets on several host threads give the one-thread result bit
+    for bit (a token's output depends only on its own row)."""
+    spec = custom_moe_spec(E=4, H=256, I=128, top_k=2, fc1="sym_int2", fc2="sym_int4")
+    inp = synth.moe_inputs(spec, 37, 0)
+    a = oracle_lib.moe(inp, debug=True)
+    b = oracle_lib.moe(inp, debug=True, threads=5)
+    for key in ("y64", "y", "a", "h", "o"):
+        assert np.array_equal(a[key], b[key]), key
+    sub = [3, 9, 30, 31]
+    assert np.array_equal(oracle_lib.moe(inp, tokens=sub, threads=3)["y"], a["y"][sub])
