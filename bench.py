@@ -3,20 +3,26 @@
 
 A step is one MoE layer forward (route -> expand -> fused gate/up SwiGLU ->
 down projection -> top-k combine) over one batch of synthetic tokens, through
-the C ABI.  The default workload is the Switch-base-shaped ternary layer (64
-experts, hidden 768, intermediate 3072, top-1, batch-1 decode).
+the C ABI.  The headline workload is the largest single-GPU one: the mixed
+INT2/INT4 prefill layer (128 experts, top-8, hidden 4096, intermediate 1536,
+2048 tokens, skewed routing), 880.8 MB of expert weights and 618.5 GFLOP per
+layer.
 
 Method (the MLX issue's repro times medians of 5 trials after warm calls):
-  * the expert weights rotate over enough distinct prepacked copies (>= 1 GiB)
-    that every step reads its experts from HBM, not from the 256 MB MALL;
-    with top-1 routing the selected expert cycles through every expert of
-    every copy before it repeats;
-  * the K timed steps are captured once in a HIP graph (no host launch gaps)
-    and replayed 5 times; ms_per_step is the median replay / K;
-  * per-stage durations come from HIP events the library records around each
-    stage on the launch stream, over K eager steps;
+  * the expert weights rotate over distinct prepacked copies, and every graph
+    replay touches at least --rotate-bytes (1 GiB) of distinct weights,
+    whatever --steps says: the timed steps are max(--steps, the count that
+    reaches that footprint), so the weights come from HBM, not from the
+    256 MB MALL; with top-1 routing the selected expert cycles through every
+    expert of every copy before it repeats;
+  * the timed steps are captured once in a HIP graph (no host launch gaps)
+    and replayed --trials times; ms_per_step is the median replay / steps;
+  * per-stage durations come from the kernels' own dispatch timestamps (HIP
+    events stamped by hipExtLaunchKernel), over the same steps run eagerly;
   * value = effective weight-read bandwidth: bytes of the experts each step
-    touches (codes + scales) / time per step.
+    touches (codes + scales) / time per step.  The roofline object reports
+    the dominant kernel against its own bound (MFMA for the grouped prefill
+    kernels, HBM for the decode GEMVs).
 """
 
 from __future__ import annotations
@@ -36,6 +42,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_F16_PEAK_TFLOPS = 2500.0
 MALL_BYTES = 256 << 20
 METRIC = "µs per MoE layer and effective weight-read HBM GB/s vs peak, tokens/expert M=1..32"
 
@@ -47,16 +54,17 @@ def log(*a):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=600,
-                    help="timed steps; 600 x 1.9 MB of experts per step > 1 GiB per replay")
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="switch_base_ternary")
+    ap.add_argument("--steps", type=int, default=20,
+                    help="timed steps (raised until one replay touches --rotate-bytes of distinct weights)")
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="mixed_int2_int4_prefill")
     ap.add_argument("--tokens", type=int, default=0, help="tokens per step (default: the workload's first)")
     ap.add_argument("--trials", type=int, default=5)
     ap.add_argument("--rotate-bytes", type=float, default=float(1 << 30))
-    ap.add_argument("--no-extras", action="store_true", help="skip the M-sweep / other workloads")
+    ap.add_argument("--no-extras", action="store_true", help="skip the decode, M-sweep and dense workloads")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="wall seconds of the all-cores oracle sample (plus about 6 s on one core)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 256 MiB device copy (counter calibration under rocprofv3)")
     return ap.parse_args()
@@ -74,6 +82,21 @@ def fc1_bytes(spec) -> int:
     return synth.canonical_matrix_bytes(spec.fc1, spec.fc1_rows, spec.H)
 
 
+def layer_flops(spec, T) -> dict:
+    """Algorithmic flops of one layer call: 2 per multiply-add of FC1 and FC2
+    over every routed slot."""
+    S = T * spec.top_k
+    return {"fc1": 2.0 * S * spec.fc1_rows * spec.H, "fc2": 2.0 * S * spec.H * spec.I}
+
+
+def expected_touched(spec, T) -> float:
+    """Expected distinct experts per step with i.i.d. logits (top-1 steps are
+    targeted at distinct experts)."""
+    if spec.top_k == 1:
+        return float(min(T, spec.E))
+    return spec.E * (1.0 - (1.0 - spec.top_k / spec.E) ** T)
+
+
 def targeted_logits(logits: np.ndarray, targets: np.ndarray) -> np.ndarray:
     """Swap each row's largest logit into column `targets[row]` (keeps the
     row's values, so each row is still a permutation of N(0,1) draws)."""
@@ -82,6 +105,18 @@ def targeted_logits(logits: np.ndarray, targets: np.ndarray) -> np.ndarray:
     r = np.arange(lg.shape[0])
     a, b = lg[r, am].copy(), lg[r, targets].copy()
     lg[r, targets], lg[r, am] = a, b
+    return lg
+
+
+def covering_logits(T: int, E: int, k: int, seed: int = 0) -> np.ndarray:
+    """Logits whose top-k of token t are experts (t*k + j) mod E, j = 0..k-1,
+    in that order (values 8 - j/2 above N(0,1) draws): T*k >= E slots cover
+    every expert with one or two rows."""
+    rng = np.random.default_rng(seed)
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    for t in range(T):
+        for j in range(k):
+            lg[t, (t * k + j) % E] = 8.0 - 0.5 * j
     return lg
 
 
@@ -113,29 +148,39 @@ def graph_time(run_steps, K, trials, check=None):
     return statistics.median(times), times
 
 
-# Sources that define the GEMV kernels and their launch shape: the counter
-# figures in profiles/traffic.json stay valid while these are unchanged.
-GEMV_SOURCES = ("abi.hip", "codec.hpp", "combine.hip", "gemv_impl.hpp", "qmoe_internal.h", "route_impl.hpp",
-                "gemv_sym_int4.hip", "gemv_sym_int2.hip", "gemv_ternary.hip", "gemv_affine_int2.hip",
-                "gemv_affine_int4.hip")
-
-
 def src_hash() -> str:
+    """Hash of every kernel and host source of the library: stored counter
+    figures (profiles/*.json) are used only while it matches."""
     h = hashlib.sha256()
     d = os.path.join(ROOT, "skinny_gemm_amd", "csrc")
-    for f in GEMV_SOURCES:
-        with open(os.path.join(d, f), "rb") as fh:
-            h.update(f.encode() + fh.read())
+    for f in sorted(os.listdir(d)):
+        if f.endswith((".hip", ".hpp", ".h")):
+            with open(os.path.join(d, f), "rb") as fh:
+                h.update(f.encode() + fh.read())
+    with open(os.path.join(ROOT, "include", "qmoe.h"), "rb") as fh:
+        h.update(fh.read())
     return h.hexdigest()[:16]
 
 
+def stored_profile(key: str):
+    """Entry `key` of profiles/counters.json if it was taken with the current
+    sources (else None)."""
+    p = os.path.join(ROOT, "profiles", "counters.json")
+    if not os.path.exists(p):
+        return None
+    ent = json.load(open(p)).get(key)
+    if ent and ent.get("src_hash") == src_hash():
+        return ent
+    return None
+
+
 # ------------------------------------------------------------ MoE stepping
-def make_layers(spec, rotate_bytes, seed=0):
+def make_layers(spec, rotate_bytes, seed=0, min_copies=1):
     """Distinct prepacked weight copies totalling >= rotate_bytes."""
     import synth
     from skinny_gemm_amd.layer import MoeLayer
     layer_bytes = spec.E * expert_bytes(spec)
-    L = max(1, math.ceil(rotate_bytes / layer_bytes))
+    L = max(min_copies, math.ceil(rotate_bytes / layer_bytes))
     log(f"[bench] {spec.name}: {L} weight copies x {layer_bytes / 1e6:.1f} MB")
     t0 = time.time()
     layers, inp0 = [], None
@@ -150,7 +195,11 @@ def make_layers(spec, rotate_bytes, seed=0):
 
 
 class MoeBench:
-    def __init__(self, spec, T, K, W, layers, inp0, seed=0, targeted=True):
+    """K timed steps (after W warm steps) of one workload over rotating
+    weight copies; inputs come from a pool of distinct batches."""
+
+    def __init__(self, spec, T, K, W, layers, inp0, seed=0, targeted=True, logits_mode="iid",
+                 fixed_logits=None, pool_bytes=64 << 20):
         import torch
         import synth
         from skinny_gemm_amd.layer import to_device_bits
@@ -158,24 +207,28 @@ class MoeBench:
         self.layers, self.inp0 = layers, inp0
         self.L = len(layers)
         n = K + W
-        steps = synth.moe_inputs(spec, T * n, seed + 1, weights=False)
+        act_bytes = 4 if spec.act_dtype == "f32" else 2
+        self.P = max(1, min(n, pool_bytes // max(1, T * spec.H * act_bytes)))  # distinct input batches
+        steps = synth.moe_inputs(spec, T * self.P, seed + 1, logits_mode, weights=False)
         lg = steps["logits"]
-        if targeted and spec.top_k == 1:
-            s = np.repeat(np.arange(n), T)
-            t = np.tile(np.arange(T), n)
+        if fixed_logits is not None:
+            lg = np.tile(fixed_logits, (self.P, 1))
+        elif targeted and spec.top_k == 1 and logits_mode == "iid":
+            s = np.repeat(np.arange(self.P), T)
+            t = np.tile(np.arange(T), self.P)
             tgt = ((s // self.L) * T + t) % spec.E
             lg = targeted_logits(lg, tgt)
-        self.x_np = steps["x"].reshape(n, T, spec.H)
-        self.lg_np = lg.reshape(n, T, spec.E)
-        self.x = to_device_bits(steps["x"], spec.act_dtype).view(n, T, spec.H)
-        self.lg = torch.from_numpy(np.ascontiguousarray(lg)).cuda().view(n, T, spec.E)
+        self.x_np = steps["x"].reshape(self.P, T, spec.H)
+        self.lg_np = lg.reshape(self.P, T, spec.E)
+        self.x = to_device_bits(steps["x"], spec.act_dtype).view(self.P, T, spec.H)
+        self.lg = torch.from_numpy(np.ascontiguousarray(lg)).cuda().view(self.P, T, spec.E)
         self.y = torch.empty((T, spec.H), dtype=self.x.dtype, device="cuda")
         self.ws = self.layers[0].workspace(T, spec.top_k)
         self.kw = {}  # forward options of every step (the variants)
 
     def step(self, s, **kw):
-        self.layers[s % self.L].forward(self.x[s], self.lg[s], self.spec.top_k, y=self.y, ws=self.ws,
-                                        **self.kw, **kw)
+        self.layers[s % self.L].forward(self.x[s % self.P], self.lg[s % self.P], self.spec.top_k, y=self.y,
+                                        ws=self.ws, **self.kw, **kw)
 
     def run(self):
         for s in range(self.W, self.W + self.K):
@@ -200,16 +253,23 @@ class MoeBench:
         return ms, all_ms
 
     def touched(self):
-        """Distinct experts routed per timed step (from the GPU's own counts)."""
+        """Distinct experts routed per timed step and distinct (copy, expert)
+        pairs per replay (from the GPU's own counts)."""
         import torch
         from skinny_gemm_amd import forward_ex
         cnt = torch.empty((self.K, self.spec.E), dtype=torch.int32, device="cuda")
         for i, s in enumerate(range(self.W, self.W + self.K)):
             lay = self.layers[s % self.L]
-            forward_ex(lay.desc, lay.packed, self.x[s], self.lg[s], self.T, self.spec.top_k, self.y, self.ws,
-                       counts_out=cnt[i])
+            forward_ex(lay.desc, lay.packed, self.x[s % self.P], self.lg[s % self.P], self.T, self.spec.top_k,
+                       self.y, self.ws, counts_out=cnt[i])
         torch.cuda.synchronize()
-        return (cnt > 0).sum(1).cpu().numpy()
+        c = (cnt > 0).cpu().numpy()
+        per_step = c.sum(1)
+        distinct = set()
+        for i, s in enumerate(range(self.W, self.W + self.K)):
+            for e in np.nonzero(c[i])[0]:
+                distinct.add((s % self.L, int(e)))
+        return per_step, len(distinct)
 
     def stage_names(self):
         """Stage list of the plan the forward call follows (one kernel each)."""
@@ -218,9 +278,9 @@ class MoeBench:
         return forward_plan(lay.desc, self.T, self.spec.top_k)["kernels"]
 
     def stage_times(self, chunk=64):
-        """Average duration (ms) of each plan stage over the K steps, from events
-        recorded on the launch stream around every stage.  Each chunk of steps is
-        queued behind a GPU sleep so the stages run back to back, as in the graph,
+        """Average duration (ms) of each plan stage over the K steps, from the
+        dispatch timestamps of its kernels.  Each chunk of steps is queued
+        behind a GPU sleep so the stages run back to back, as in the graph,
         instead of waiting on the host between launches."""
         import torch
         nst = len(self.stage_names())
@@ -249,18 +309,38 @@ class MoeBench:
         return out / self.K
 
 
-def bench_moe(spec, T, K, W, trials, layers, inp0, stages=True):
-    b = MoeBench(spec, T, K, W, layers, inp0)
+def timed_steps(spec, T, K, rotate_bytes, experts_per_step):
+    """Steps per replay: at least K, and enough to touch rotate_bytes of
+    distinct expert weights (experts per step x expert bytes)."""
+    per_step = experts_per_step * expert_bytes(spec)
+    return max(K, math.ceil(rotate_bytes / per_step))
+
+
+def bench_moe(spec, T, K, W, trials, layers, inp0, stages=True, rotate_bytes=float(1 << 30),
+              logits_mode="iid", fixed_logits=None, stage_steps=64):
+    """Graph-replay timing of one workload; per-stage times over the first
+    `stage_steps` steps run eagerly."""
+    if fixed_logits is not None:
+        eps = float(len(np.unique(np.argsort(-fixed_logits, 1, kind="stable")[:, :spec.top_k])))
+    elif logits_mode == "shared":
+        eps = float(spec.top_k)
+    else:
+        eps = expected_touched(spec, T)
+    Ke = timed_steps(spec, T, K, rotate_bytes, eps)
+    b = MoeBench(spec, T, Ke, W, layers, inp0, logits_mode=logits_mode, fixed_logits=fixed_logits)
     ms, all_ms = b.time_graph(trials)
-    touched = b.touched()
+    touched, distinct = b.touched()
     wbytes = float(touched.mean()) * expert_bytes(spec)
     res = {"workload": spec.name, "T": T, "top_k": spec.top_k, "us_per_layer": ms * 1e3,
-           "trials_us": [t * 1e3 for t in all_ms], "weight_copies": b.L,
+           "trials_us": [t * 1e3 for t in all_ms], "steps": Ke, "weight_copies": b.L,
            "experts_touched_per_step": float(touched.mean()),
+           "distinct_weight_bytes_per_replay": distinct * expert_bytes(spec),
            "weight_bytes_per_step": wbytes, "effective_GBps": wbytes / (ms * 1e-3) / 1e9}
     res["frac_of_hbm_peak"] = res["effective_GBps"] / HBM_PEAK_GBS
     if stages:
+        K0, b.K = b.K, min(b.K, stage_steps)
         st = b.stage_times()
+        b.K = K0
         res["stage_us"] = dict(zip(b.stage_names(), (st * 1e3).tolist()))
         res["fc1_bytes_per_launch"] = float(touched.mean()) * fc1_bytes(spec)
     return res, b
@@ -273,6 +353,7 @@ def bench_linear(spec, N, Ms, K_steps, trials, rotate_bytes, seed=0):
     from skinny_gemm_amd.layer import QLinear, to_device_bits
     wbytes = synth.canonical_matrix_bytes(spec.fmt, N, spec.K)
     L = max(1, math.ceil(rotate_bytes / wbytes))
+    K_steps = max(K_steps, L)  # every replay reads every copy
     log(f"[bench] {spec.name} N={N}: {L} weight copies x {wbytes / 1e6:.1f} MB")
     lins = []
     for c in range(L):
@@ -295,10 +376,33 @@ def bench_linear(spec, N, Ms, K_steps, trials, rotate_bytes, seed=0):
     t1 = out[0]["us"]
     for r in out:
         r["x_M1"] = r["us"] / t1
-    return {"workload": f"{spec.name}[N={N}]", "weight_bytes": wbytes, "copies": L, "sweep": out}
+    return {"workload": f"{spec.name}[N={N}]", "weight_bytes": wbytes, "copies": L, "steps": K_steps,
+            "sweep": out}
 
 
-# ----------------------------------------------------------- CPU baseline
+def read_ceiling(nbytes=1 << 30, reps=20) -> dict:
+    """The library's streaming-read probe over a buffer 4x the MALL."""
+    import torch
+    from skinny_gemm_amd import read_probe
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    for _ in range(3):
+        read_probe(src, sink)
+    a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(reps):
+        read_probe(src, sink)
+    e.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(e) * 1e3 / reps
+    del src
+    return {"bytes": nbytes, "us": us, "GBps": nbytes / (us * 1e-6) / 1e9,
+            "frac_of_hbm_peak": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS}
+
+
+# ------------------------------------------------------------- variants
 def variant_times(b: "MoeBench", trials: int, inp_seed: int = 0) -> dict:
     """The same timed steps with per-expert FC1/FC2 output biases, then with
     unnormalised top-k weights (us per layer, graph replays)."""
@@ -368,28 +472,132 @@ def tiled_prefill_time(layer, spec, T: int, div: int, reps: int = 3) -> dict:
     return res
 
 
+# ----------------------------------------------------------- CPU baseline
 def cpu_baseline(b: "MoeBench", seconds: float):
+    """The oracle (double precision, plain loops) on a bounded sample of the
+    headline workload's tokens: first on one host core, then on all cores of
+    this process's CPU share (at most 16) over disjoint token subsets.  The
+    value is the all-cores rate scaled to a whole layer."""
     import oracle
-    spec = b.spec
+    spec, T = b.spec, b.T
+    cores = max(1, min(16, len(os.sched_getaffinity(0))))
     inp = dict(b.inp0)
-    n = 0
+    inp["x"], inp["logits"] = b.x_np[0], b.lg_np[0]
+    r = oracle.route(inp["logits"], spec.top_k)
+    wbytes = float((r["counts"] > 0).sum()) * expert_bytes(spec)
+    # one core: single tokens until ~1/3 of the budget
     t0 = time.perf_counter()
-    elapsed = 0.0
-    touched = 0
-    while n < b.K + b.W and elapsed < seconds:
-        inp["x"] = b.x_np[n]
-        inp["logits"] = b.lg_np[n]
-        r = oracle.route(inp["logits"], spec.top_k)
-        touched += int((r["counts"] > 0).sum())
-        oracle.moe(inp)
-        n += 1
-        elapsed = time.perf_counter() - t0
-    per = elapsed / n
-    gbs = touched / n * expert_bytes(spec) / per / 1e9
-    return {"value": gbs, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "us_per_layer": per * 1e6,
-            "sample": f"{n} layer calls of {spec.name} (T={b.T}) on one host core, "
-                      f"double-precision oracle, {elapsed:.1f}s"}
+    n1 = 0
+    while n1 < T and time.perf_counter() - t0 < seconds / 3:
+        oracle.moe(inp, tokens=[n1])
+        n1 += 1
+    per1 = (time.perf_counter() - t0) / n1
+    # all cores: enough tokens for about `seconds` of wall time
+    n = int(min(T, max(cores, round(cores * seconds / per1))))
+    toks = list(range(n))
+    t0 = time.perf_counter()
+    oracle.moe(inp, tokens=toks, threads=cores)
+    el = time.perf_counter() - t0
+    layer_s = el * T / n
+    return {"value": wbytes / layer_s / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "us_per_layer": layer_s * 1e6, "us_per_layer_one_core": per1 * T * 1e6,
+            "sample": f"{n} of the {T} tokens of one {spec.name} layer call on {cores} host threads "
+                      f"({el:.1f}s), and {n1} tokens on one thread; double-precision oracle, "
+                      f"scaled to the whole layer ({wbytes / 1e6:.1f} MB of experts touched)"}
+
+
+# ------------------------------------------------------------- extras
+def decode_extras(args, variants) -> dict:
+    import torch
+    import synth
+    import dataclasses
+    import copy
+    from skinny_gemm_amd.layer import MoeLayer  # noqa: F401
+    from skinny_gemm_amd import layer_desc
+    extras = {}
+    rb = args.rotate_bytes
+    # switch-base ternary decode, top-1
+    sw = synth.MOE_WORKLOADS["switch_base_ternary"]
+    lays, isw = make_layers(sw, rb)
+    r, bb = bench_moe(sw, 1, 20, 20, 3, lays, isw, rotate_bytes=rb)
+    extras["switch_base_ternary"] = {k: r[k] for k in ("us_per_layer", "trials_us", "steps", "effective_GBps",
+                                                        "frac_of_hbm_peak", "distinct_weight_bytes_per_replay",
+                                                        "stage_us")}
+    log(f"[bench] {json.dumps(extras['switch_base_ternary'])}")
+    variants[f"{sw.name}_T1"] = {"base_us": r["us_per_layer"], **variant_times(bb, 3)}
+    del bb, lays
+    torch.cuda.empty_cache()
+    # the Switch Transformer's own ReLU FFN on the same shapes
+    rsw = dataclasses.replace(sw, activation="relu", name=sw.name + "_relu")
+    layr, ir = make_layers(rsw, rb)
+    r, bb = bench_moe(rsw, 1, 20, 20, 3, layr, ir, rotate_bytes=rb)
+    variants[f"{rsw.name}_T1"] = {k: r[k] for k in ("us_per_layer", "effective_GBps", "stage_us")}
+    del bb, layr
+    torch.cuda.empty_cache()
+    # DeepSeek-V2-Lite-shaped decode, i.i.d. logits, T = 1, 2, 4, 8
+    d3 = synth.MOE_WORKLOADS["dsv2lite_int4"]
+    lay3, i3 = make_layers(d3, rb)
+    extras["dsv2lite_int4"] = []
+    for t in d3.tokens:
+        r, bb = bench_moe(d3, t, 20, 10, 3, lay3, i3, rotate_bytes=rb)
+        extras["dsv2lite_int4"].append({k: r[k] for k in ("T", "us_per_layer", "steps", "effective_GBps",
+                                                          "frac_of_hbm_peak", "experts_touched_per_step",
+                                                          "distinct_weight_bytes_per_replay", "stage_us")})
+        log(f"[bench] {json.dumps(extras['dsv2lite_int4'][-1])}")
+        if t == 1:
+            variants[f"{d3.name}_T1"] = {"base_us": r["us_per_layer"], **variant_times(bb, 3)}
+        del bb
+    # shared logits: every selected expert receives M = T rows (the M-sweep)
+    extras["dsv2lite_int4_shared_M_sweep"] = []
+    for t in (1, 2, 3, 4, 5, 8, 10, 16, 32):
+        r, bb = bench_moe(d3, t, 20, 5, 3, lay3, i3, stages=False, rotate_bytes=rb, logits_mode="shared")
+        extras["dsv2lite_int4_shared_M_sweep"].append({"M": t, "us_per_layer": r["us_per_layer"],
+                                                       "steps": r["steps"],
+                                                       "experts_touched_per_step": r["experts_touched_per_step"]})
+        del bb
+    t1 = extras["dsv2lite_int4_shared_M_sweep"][0]["us_per_layer"]
+    for e in extras["dsv2lite_int4_shared_M_sweep"]:
+        e["x_M1"] = e["us_per_layer"] / t1
+    log(f"[bench] shared M-sweep {json.dumps(extras['dsv2lite_int4_shared_M_sweep'])}")
+    # the fused gate/up GEMV with all 64 experts active, one or two rows each
+    Tc = math.ceil(d3.E / d3.top_k)
+    cov = covering_logits(Tc, d3.E, d3.top_k)
+    r, bb = bench_moe(d3, Tc, 20, 5, 3, lay3, i3, rotate_bytes=rb, fixed_logits=cov)
+    fc1_stage = next(n for n in r["stage_us"] if "fc1" in n)
+    fc1_all = d3.E * fc1_bytes(d3)
+    extras["dsv2lite_fc1_all_experts"] = {
+        "T": Tc, "experts_touched_per_step": r["experts_touched_per_step"], "us_per_layer": r["us_per_layer"],
+        "stage_us": r["stage_us"], "fc1_kernel": fc1_stage, "fc1_bytes_per_launch": fc1_all,
+        "fc1_GBps": fc1_all / (r["stage_us"][fc1_stage] * 1e-6) / 1e9,
+        "fc1_frac_of_hbm_peak": fc1_all / (r["stage_us"][fc1_stage] * 1e-6) / 1e9 / HBM_PEAK_GBS}
+    log(f"[bench] {json.dumps(extras['dsv2lite_fc1_all_experts'])}")
+    del bb
+    variants[f"runtime_scales_{d3.name}"] = runtime_scales_time(lay3[0], i3)
+    # f32 activations over the same prepacked weights (the packed buffer does
+    # not depend on the activation dtype; only the descriptor does)
+    d3f = dataclasses.replace(d3, act_dtype="f32", name=d3.name + "_f32")
+    lay3f = []
+    for lay in lay3:
+        c = copy.copy(lay)
+        c.act_dtype = "f32"
+        c.desc = layer_desc(d3.E, d3.H, d3.I, "f32", (d3.fc1.fmt, d3.fc1.block, d3.fc1.scale_dtype),
+                            (d3.fc2.fmt, d3.fc2.block, d3.fc2.scale_dtype))
+        lay3f.append(c)
+    for t in (1, 8):
+        r, bb = bench_moe(d3f, t, 20, 10, 3, lay3f, i3, stages=False, rotate_bytes=rb)
+        base = next(x["us_per_layer"] for x in extras["dsv2lite_int4"] if x["T"] == t)
+        variants[f"{d3.name}_T{t}_f32_activations"] = {"us": r["us_per_layer"], "bf16_us": base}
+        del bb
+    del lay3f, lay3
+    torch.cuda.empty_cache()
+    s1 = synth.MOE_WORKLOADS["single_expert_int4"]
+    lay1, i1 = make_layers(s1, rb)
+    r, bb = bench_moe(s1, 1, len(lay1), 20, 3, lay1, i1, rotate_bytes=rb)
+    extras["single_expert_int4"] = {k: r[k] for k in ("us_per_layer", "steps", "effective_GBps", "stage_us")}
+    log(f"[bench] {json.dumps(extras['single_expert_int4'])}")
+    del bb, lay1
+    torch.cuda.empty_cache()
+    return extras
 
 
 def main():
@@ -407,41 +615,63 @@ def main():
     spec = synth.MOE_WORKLOADS[args.workload]
     T = args.tokens or spec.tokens[0]
 
-    layers, inp0 = make_layers(spec, args.rotate_bytes)
-    head, b = bench_moe(spec, T, args.steps, args.warmup, args.trials, layers, inp0)
+    layers, inp0 = make_layers(spec, args.rotate_bytes, min_copies=2)
+    head, b = bench_moe(spec, T, args.steps, args.warmup, args.trials, layers, inp0, rotate_bytes=args.rotate_bytes)
     log(f"[bench] {json.dumps(head)}")
-    fc1_stage = next(n for n in head["stage_us"] if "fc1" in n)
-    fc1_us = head["stage_us"][fc1_stage]
-    achieved = head["fc1_bytes_per_launch"] / (fc1_us * 1e-6) / 1e9
-    traffic = None
-    tpath = os.path.join(ROOT, "profiles", "traffic.json")
-    if os.path.exists(tpath):
-        tr = json.load(open(tpath))
-        ent = tr.get(f"{spec.name}:T{T}")
-        if ent and ent.get("src_hash") == src_hash():
-            traffic = ent.get("bytes_per_launch")
+    st = head["stage_us"]
+    grouped = any(n.startswith("grouped") for n in st)
+    if grouped:
+        # MFMA-bound kernels: algorithmic flops per launch over their duration
+        fl = layer_flops(spec, T)
+        kern = {}
+        for n, f in (("fc1", fl["fc1"]), ("fc2", fl["fc2"])):
+            name = next(s for s in st if s.startswith("grouped_" + n))
+            tf = f / (st[name] * 1e-6) / 1e12
+            kern[name] = {"avg_launch_us": st[name], "flops_per_launch": f, "achieved_TFLOPs": tf,
+                          "frac": tf / MFMA_F16_PEAK_TFLOPS}
+        dom = max(kern, key=lambda k: kern[k]["avg_launch_us"])
+        prof = stored_profile(f"{spec.name}:T{T}:{dom}")
+        roof = {"bound": "mfma", "kernel": dom, "achieved": kern[dom]["achieved_TFLOPs"],
+                "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": kern[dom]["frac"],
+                "traffic": prof.get("hbm_bytes_per_launch") if prof else None,
+                "traffic_source": "rocprofv3 FETCH_SIZE/WRITE_SIZE, stored in profiles/counters.json "
+                                  "for the current sources" if prof else None,
+                "avg_launch_us": kern[dom]["avg_launch_us"],
+                "trace_avg_us": prof.get("trace_avg_us") if prof else None,
+                "algorithmic_flops_per_launch": kern[dom]["flops_per_launch"],
+                "dtype_peak": "f16 dense MFMA 2.5 PFLOP/s", "kernels": kern,
+                "layer_TFLOPs": (fl["fc1"] + fl["fc2"]) / (head["us_per_layer"] * 1e-6) / 1e12}
+        if prof and prof.get("trace_avg_us"):
+            roof["trace_agreement"] = kern[dom]["avg_launch_us"] / prof["trace_avg_us"]
+    else:
+        fc1_stage = next(n for n in st if "fc1" in n)
+        achieved = head["fc1_bytes_per_launch"] / (st[fc1_stage] * 1e-6) / 1e9
+        prof = stored_profile(f"{spec.name}:T{T}:{fc1_stage}")
+        roof = {"bound": "hbm", "kernel": fc1_stage, "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS, "traffic": prof.get("hbm_bytes_per_launch") if prof else None,
+                "avg_launch_us": st[fc1_stage], "algorithmic_bytes_per_launch": head["fc1_bytes_per_launch"]}
     line = {
         "metric": METRIC,
         "value": head["effective_GBps"],
         "unit": "GB/s",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": head["steps"],
         "warmup": args.warmup,
         "ms_per_step": head["us_per_layer"] / 1e3,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": spec.act_dtype,
         "data": "synthetic (seeded SplitMix64 codes, scales, activations and logits)",
         "config": {"workload": spec.name, "tokens": T, "experts": spec.E, "top_k": spec.top_k,
-                   "hidden": spec.H, "intermediate": spec.I, "weights": spec.fc1.fmt,
-                   "block": spec.fc1.block, "us_per_layer": round(head["us_per_layer"], 3),
-                   "frac_of_hbm_peak": head["frac_of_hbm_peak"], "weight_copies": head["weight_copies"]},
-        "roofline": {"bound": "hbm", "kernel": fc1_stage, "achieved": achieved,
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": traffic, "avg_launch_us": fc1_us,
-                     "algorithmic_bytes_per_launch": head["fc1_bytes_per_launch"]},
-        "stage_us": head["stage_us"],
+                   "hidden": spec.H, "intermediate": spec.I,
+                   "weights": f"fc1 {spec.fc1.fmt} block {spec.fc1.block}, fc2 {spec.fc2.fmt} block {spec.fc2.block}",
+                   "us_per_layer": round(head["us_per_layer"], 3), "trials_us": head["trials_us"],
+                   "frac_of_hbm_peak": head["frac_of_hbm_peak"], "weight_copies": head["weight_copies"],
+                   "steps_asked": args.steps,
+                   "distinct_weight_bytes_per_replay": head["distinct_weight_bytes_per_replay"]},
+        "roofline": roof,
+        "stage_us": st,
     }
     if args.copy_probe:
         src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
@@ -452,95 +682,22 @@ def main():
         del src, dst
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(b, args.cpu_seconds)
+        log(f"[bench] cpu {json.dumps(line['cpu_baseline'])}")
+    del b
     variants = {}
     if not args.no_extras:
-        variants[f"{spec.name}_T{T}"] = {"base_us": head["us_per_layer"], **variant_times(b, 3)}
-        log(f"[bench] variants {json.dumps(variants)}")
-    del b, layers
+        if spec.name == "mixed_int2_int4_prefill":
+            variants[f"{spec.name}_row_tiling"] = tiled_prefill_time(layers[0], spec, 8193, 3)
+            log(f"[bench] variants {json.dumps(variants)}")
+    del layers
     torch.cuda.empty_cache()
     if not args.no_extras:
-        # the same layer with the Switch Transformer's own ReLU FFN (FC1 one [I][H] matrix)
-        import dataclasses
-        rspec = dataclasses.replace(spec, activation="relu", name=spec.name + "_relu")
-        layr, ir = make_layers(rspec, args.rotate_bytes)
-        r, bb = bench_moe(rspec, T, args.steps, args.warmup, 3, layr, ir)
-        variants[f"{rspec.name}_T{T}"] = {k: r[k] for k in ("us_per_layer", "effective_GBps", "stage_us")}
-        log(f"[bench] variants {json.dumps(variants)}")
-        del bb, layr
-        torch.cuda.empty_cache()
-        extras = {}
-        d3 = synth.MOE_WORKLOADS["dsv2lite_int4"]
-        extras["dsv2lite_int4"] = []
-        lay3, i3 = make_layers(d3, args.rotate_bytes)
-        for t in d3.tokens:
-            r, bb = bench_moe(d3, t, 100, 10, 3, lay3, i3, stages=True)
-            extras["dsv2lite_int4"].append({k: r[k] for k in ("T", "us_per_layer", "effective_GBps",
-                                                              "frac_of_hbm_peak", "experts_touched_per_step",
-                                                              "stage_us")})
-            log(f"[bench] {json.dumps(extras['dsv2lite_int4'][-1])}")
-            if t == 1:
-                variants[f"{d3.name}_T1"] = {"base_us": r["us_per_layer"], **variant_times(bb, 3)}
-                log(f"[bench] variants {json.dumps(variants)}")
-            del bb
-        variants[f"runtime_scales_{d3.name}"] = runtime_scales_time(lay3[0], i3)
-        # f32 activations over the same prepacked weights (the packed buffer
-        # does not depend on the activation dtype; only the descriptor does)
-        import copy
-        import dataclasses
-        from skinny_gemm_amd import layer_desc
-        d3f = dataclasses.replace(d3, act_dtype="f32", name=d3.name + "_f32")
-        lay3f = []
-        for lay in lay3:
-            c = copy.copy(lay)
-            c.act_dtype = "f32"
-            c.desc = layer_desc(d3.E, d3.H, d3.I, "f32", (d3.fc1.fmt, d3.fc1.block, d3.fc1.scale_dtype),
-                                (d3.fc2.fmt, d3.fc2.block, d3.fc2.scale_dtype))
-            lay3f.append(c)
-        for t in (1, 8):
-            r, bb = bench_moe(d3f, t, 100, 10, 3, lay3f, i3, stages=False)
-            base = next(x["us_per_layer"] for x in extras["dsv2lite_int4"] if x["T"] == t)
-            variants[f"{d3.name}_T{t}_f32_activations"] = {"us": r["us_per_layer"], "bf16_us": base}
-            del bb
-        del lay3f
-        log(f"[bench] variants {json.dumps(variants)}")
-        del lay3
-        torch.cuda.empty_cache()
-        s1 = synth.MOE_WORKLOADS["single_expert_int4"]
-        lay1, i1 = make_layers(s1, args.rotate_bytes)
-        r, bb = bench_moe(s1, 1, len(lay1), 20, 3, lay1, i1)
-        extras["single_expert_int4"] = {k: r[k] for k in ("us_per_layer", "effective_GBps", "stage_us")}
-        log(f"[bench] {json.dumps(extras['single_expert_int4'])}")
-        del bb, lay1
-        torch.cuda.empty_cache()
-        pf = synth.MOE_WORKLOADS["mixed_int2_int4_prefill"]
-        layp, ip = make_layers(pf, 1.0)  # 880 MB per copy: already 3.4x the MALL
-        r, bb = bench_moe(pf, 2048, 10, 2, 3, layp, ip)
-        flops = 2.0 * 2048 * pf.top_k * (2 * pf.I * pf.H + pf.H * pf.I)
-        r["tflops"] = flops / (r["us_per_layer"] * 1e-6) / 1e12
-        extras["mixed_int2_int4_prefill"] = {k: r[k] for k in ("us_per_layer", "effective_GBps", "tflops",
-                                                               "stage_us", "experts_touched_per_step")}
-        log(f"[bench] {json.dumps(extras['mixed_int2_int4_prefill'])}")
-        del bb
-        torch.cuda.empty_cache()
-        variants[f"{pf.name}_row_tiling"] = tiled_prefill_time(layp[0], pf, 8193, 3)
-        log(f"[bench] variants {json.dumps(variants)}")
-        del layp
-        torch.cuda.empty_cache()
+        extras = decode_extras(args, variants)
         dense = synth.LINEAR_WORKLOADS["dense_affine2"]
-        extras["dense_affine2"] = [bench_linear(dense, N, [1, 2, 3, 4, 5, 8, 10, 16, 32], 50, 3, args.rotate_bytes)
+        extras["dense_affine2"] = [bench_linear(dense, N, list(dense.Ms), 20, 3, args.rotate_bytes)
                                    for N in dense.Ns]
-        # The expert GEMV at M=1 with all 64 DeepSeek-V2-Lite-shaped experts
-        # active (one row each): the gate/up matrices of the 64 experts read
-        # as one [64 * 2816][2048] INT4 matrix by the same MFMA GEMV kernel
-        # family (196 MB of weights per launch).
-        from synth.workloads import custom_linear_spec
-        d3 = synth.MOE_WORKLOADS["dsv2lite_int4"]
-        allx = custom_linear_spec(d3.H, fmt=d3.fc1.fmt, block=d3.fc1.block, scale_dtype=d3.fc1.scale_dtype,
-                                  act_dtype=d3.act_dtype)
-        r = bench_linear(allx, d3.E * 2 * d3.I, [1, 2, 4, 8, 16], 20, 3, args.rotate_bytes)
-        r["workload"] = f"dsv2lite_fc1_all{d3.E}_experts_as_dense[N={d3.E * 2 * d3.I},K={d3.H}]"
-        extras["expert_gemv_all_experts_m1"] = r
-        log(f"[bench] {json.dumps(r)}")
+        extras["read_ceiling"] = read_ceiling()
+        log(f"[bench] read ceiling {json.dumps(extras['read_ceiling'])}")
         extras["variants"] = variants
         line["extras"] = extras
     print(json.dumps(line), flush=True)

@@ -314,6 +314,18 @@ qmoe_status qmoe_linear(const qmoe_qmatrix_desc *desc, const void *packed, const
 qmoe_status qmoe_linear_unpack_codes(const qmoe_qmatrix_desc *desc, const void *packed,
                                      int8_t *codes_out, void *stream);
 
+/* --------------------------------------------------------- diagnostics --- */
+
+/* Read-bandwidth probe: streams `bytes` of device memory at `src` (16-B
+ * aligned, bytes a multiple of 16) with one 16-B load per lane per step in a
+ * grid-stride sweep of 8 workgroups of 256 threads per compute unit, and
+ * writes nothing unless the XOR of all words read equals a fixed value
+ * (then one word to sink[0]; sink: device, 4 B).  Its duration over a buffer
+ * much larger than the last-level cache is the achievable HBM read rate that
+ * the GEMV kernels' effective bandwidth is compared with.  Asynchronous on
+ * `stream`. */
+qmoe_status qmoe_read_probe(const void *src, size_t bytes, uint32_t *sink, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -78,6 +78,7 @@ _SIGS = {
     "qmoe_linear_workspace_size": (C.c_int, [C.POINTER(QMatrixDesc), _I32, C.POINTER(_SZ)]),
     "qmoe_linear": (C.c_int, [C.POINTER(QMatrixDesc), _P, _P, _I32, _I32, _P, _P, _SZ, _I32, _P]),
     "qmoe_linear_unpack_codes": (C.c_int, [C.POINTER(QMatrixDesc), _P, _P, _P]),
+    "qmoe_read_probe": (C.c_int, [_P, _SZ, _P, _P]),
 }
 
 
@@ -250,3 +251,9 @@ def linear(desc, packed, x, x_dtype: str, M: int, y, ws=None, path: str = "auto"
 
 def linear_unpack_codes(desc, packed, codes_out, stream=None):
     _check(lib().qmoe_linear_unpack_codes(C.byref(desc), _ptr(packed), _ptr(codes_out), _stream(stream)))
+
+
+# ----------------------------------------------------------- diagnostics
+def read_probe(src, sink, stream=None):
+    """Stream every byte of the device tensor ``src`` (the HBM read-rate probe)."""
+    _check(lib().qmoe_read_probe(_ptr(src), src.numel() * src.element_size(), _ptr(sink), _stream(stream)))

@@ -996,4 +996,13 @@ qmoe_status qmoe_linear_unpack_codes(const qmoe_qmatrix_desc *desc, const void *
                     "linear unpack");
 }
 
+// ---------------------------------------------------------- diagnostics
+qmoe_status qmoe_read_probe(const void *src, size_t bytes, uint32_t *sink, void *stream) {
+  if (bytes == 0) return ok();
+  if (!src || !sink) return fail(QMOE_ERR_INVALID_ARGUMENT, "null device pointer");
+  if (!aligned(src, 16) || bytes % 16 != 0)
+    return fail(QMOE_ERR_INVALID_ARGUMENT, "src must be 16-byte aligned and bytes a multiple of 16");
+  return hip_status(launch_read_probe(src, (int64_t)bytes, sink, device_cus(), (hipStream_t)stream), "read probe");
+}
+
 }  // extern "C"

@@ -7,6 +7,7 @@
 // (stored as is for f32 activations).
 // o holds the per-slot FC2 outputs in expert-sorted order; pos is the
 // inverse of the row list.
+#include <algorithm>
 #include <map>
 #include <mutex>
 #include <tuple>
@@ -68,6 +69,35 @@ hipError_t launch_combine(const float *o, const int32_t *slot_pos, const float *
   if (total == 0) return hipSuccess;
   return qlaunch(combine_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, o, slot_pos, w, T, k, H,
                  act_dtype, y);
+}
+
+// Streaming read of n16 16-byte vectors: each lane issues four independent
+// 16-B loads per round (each wave instruction covers 1 KiB contiguous) over a
+// grid-stride sweep.  The XOR of every word read is stored only if it equals
+// `never`, which the caller picks so that it does not occur, so the loads
+// stay and the kernel writes nothing: its time is the read time.
+__global__ __launch_bounds__(256) void read_probe_kernel(const uint4 *__restrict__ src, int64_t n16,
+                                                         uint32_t never, uint32_t *__restrict__ sink) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  uint32_t acc = 0;
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    const uint4 a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
+    acc ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^ d.z ^ d.w;
+  }
+  for (; i < n16; i += stride) {
+    const uint4 a = src[i];
+    acc ^= a.x ^ a.y ^ a.z ^ a.w;
+  }
+  if (acc == never) sink[0] = acc;
+}
+
+hipError_t launch_read_probe(const void *src, int64_t bytes, uint32_t *sink, int cus, hipStream_t s) {
+  const int64_t n16 = bytes / 16;
+  if (n16 == 0) return hipSuccess;
+  const int64_t blocks = std::min<int64_t>((int64_t)cus * 8, (n16 + 255) / 256);
+  return qlaunch(read_probe_kernel, dim3((unsigned)blocks), dim3(256), 0, s, (const uint4 *)src, n16,
+                 0x9E3779B9u, sink);
 }
 
 const void *gemv_ptr_sym_int4(int, int, int, int, int, int);

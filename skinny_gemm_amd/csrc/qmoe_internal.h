@@ -264,6 +264,8 @@ hipError_t launch_gemv(const GemvArgs &a, int epilogue, int in_f16, int rows, in
 int gemv_blocks_per_cu(int qtype, int epilogue, int in_f16, int rows, int waves, int tn, int block);
 hipError_t launch_combine(const float *o, const int32_t *slot_pos, const float *w, int T, int k,
                           int H, int act_dtype, void *y, hipStream_t s);
+// Streaming read of `bytes` (a multiple of 16) over `cus` x 8 workgroups.
+hipError_t launch_read_probe(const void *src, int64_t bytes, uint32_t *sink, int cus, hipStream_t s);
 // f32 rows -> bf16 hi (RNE of x) and lo (RNE of the remainder) rows.
 hipError_t launch_split_f32(const float *x, int64_t n, uint16_t *hi, uint16_t *lo, hipStream_t s);
 

@@ -327,3 +327,4 @@ def test_row_tiling_reaches_the_gemv_path():
     big = q.forward_plan(_desc(), 100, 6)["workspace_bytes"]
     t = q.forward_plan(_desc(), 100, 6, workspace_limit=big // 2)
     assert t["num_tiles"] >= 2 and t["path"] == 2
+

@@ -305,7 +305,7 @@ def test_mixed_int2_int4_prefill(seed):
     (dict(E=4, H=512, I=256, top_k=2, fc1="sym_int2", fc2="sym_int4"), 300, "iid"),
     (dict(E=3, H=256, I=384, top_k=2, fc1="affine_int2", fc2="affine_int4", scale_dtype="f16", act_dtype="f16"),
      200, "shared"),
-    (dict(E=5, H=256, I=256, top_k=3, fc1="ternary", block1=128, fc2="sym_int4", scale_dtype="f16"), 150, "iid"),
+    (dict(E=5, H=256, I=256, top_k=3, fc1="ternary", block1=128, fc2="sym_int4", scale_dtype="f16"), 250, "iid"),
 ], ids=["int2-int4-shared", "int2-int4-iid", "affine-f16-shared", "ternary-f16-iid"])
 def test_grouped_multi_tile_every_row(cfg, T, logits_mode):
     """Experts with several 64-row tiles and a partial last one (shared
