@@ -277,6 +277,25 @@ qmoe_status qmoe_forward_ex(const qmoe_layer_desc *desc, const void *packed, con
                             void *ws, size_t ws_bytes, void *stream,
                             const qmoe_forward_opts *opts);
 
+/* For callers that cannot allocate (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): qmoe_forward with the
+ * workspace taken from a fixed device array inside the library instead of a
+ * caller buffer.  The array holds QMOE_NOALLOC_SCRATCH_BYTES on every GPU the
+ * library runs on and stays allocated until the process ends; its device
+ * address is looked up once per device on the first call made with that
+ * device current.  The call allocates and frees nothing.  A call whose
+ * workspace (qmoe_forward_plan's workspace_bytes) exceeds the array returns
+ * QMOE_ERR_WORKSPACE_TOO_SMALL before any launch; the layer's own row tiling
+ * (f32 and wide-affine layers above 16 tokens) applies as in qmoe_forward.
+ * All calls on one GPU share the array and it keeps the last call's
+ * contents: calls that overlap on one GPU (other streams, other threads)
+ * race and must be ordered by the caller.  Everything the kernels read from
+ * the workspace is written earlier in the same call, so no clearing is
+ * needed between calls.  Arguments and errors otherwise as qmoe_forward. */
+#define QMOE_NOALLOC_SCRATCH_BYTES (32u << 20)
+qmoe_status qmoe_forward_noalloc(const qmoe_layer_desc *desc, const void *packed, const void *x,
+                                 const float *logits, int32_t T, int32_t top_k, void *y, void *stream);
+
 /* Host-only: the launch plan a qmoe_forward_ex call with these arguments would follow. */
 qmoe_status qmoe_forward_plan(const qmoe_layer_desc *desc, int32_t T, int32_t top_k,
                               const qmoe_forward_opts *opts, qmoe_plan *plan);

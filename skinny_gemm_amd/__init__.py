@@ -79,6 +79,7 @@ _SIGS = {
     "qmoe_linear": (C.c_int, [C.POINTER(QMatrixDesc), _P, _P, _I32, _I32, _P, _P, _SZ, _I32, _P]),
     "qmoe_linear_unpack_codes": (C.c_int, [C.POINTER(QMatrixDesc), _P, _P, _P]),
     "qmoe_read_probe": (C.c_int, [_P, _SZ, _P, _P]),
+    "qmoe_forward_noalloc": (C.c_int, [C.POINTER(LayerDesc), _P, _P, _P, _I32, _I32, _P, _P]),
 }
 
 
@@ -195,6 +196,15 @@ def forward_ex(desc, packed, x, logits, T, top_k, y, ws, stream=None, path="auto
     _check(lib().qmoe_forward_ex(C.byref(desc), _ptr(packed), _ptr(x), _ptr(logits), T, top_k,
                                  _ptr(y), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream),
                                  C.byref(opts)))
+
+
+def forward_noalloc(desc, packed, x, logits, T, top_k, y, stream=None):
+    """qmoe_forward with the library's fixed device scratch as the workspace."""
+    _check(lib().qmoe_forward_noalloc(C.byref(desc), _ptr(packed), _ptr(x), _ptr(logits), T, top_k, _ptr(y),
+                                      _stream(stream)))
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
 def forward_plan(desc, T: int, top_k: int, path: str = "auto", topk_weights: str = "renormalized",

@@ -13,6 +13,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <string>
 
 #include "qmoe_internal.h"
@@ -814,6 +815,56 @@ qmoe_status qmoe_forward(const qmoe_layer_desc *desc, const void *packed, const 
                          const float *logits, int32_t T, int32_t top_k, void *y, void *ws,
                          size_t ws_bytes, void *stream) {
   return qmoe_forward_ex(desc, packed, x, logits, T, top_k, y, ws, ws_bytes, stream, nullptr);
+}
+
+// ------------------------------------------------- no-allocation forward
+// The workspace of qmoe_forward_noalloc: one fixed device array per GPU the
+// library runs on, held until the process ends.  In host code `scratch` only
+// names the symbol; its device address on each GPU comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+static __device__ __align__(256) uint8_t scratch[QMOE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+qmoe_status scratch_for_current_device(void **out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(QMOE_ERR_UNSUPPORTED, "device %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> g(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void *ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr) {
+      (void)hipGetLastError();
+      return fail(QMOE_ERR_DEVICE, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                  e != hipSuccess ? hipGetErrorString(e) : "null address");
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return ok();
+}
+}  // namespace
+
+qmoe_status qmoe_forward_noalloc(const qmoe_layer_desc *desc, const void *packed, const void *x,
+                                 const float *logits, int32_t T, int32_t top_k, void *y, void *stream) {
+  qmoe_plan plan;
+  qmoe_status st = qmoe_forward_plan(desc, T, top_k, nullptr, &plan);
+  if (st != QMOE_OK) return st;
+  if (T == 0) return ok();
+  if (plan.workspace_bytes > (int64_t)QMOE_NOALLOC_SCRATCH_BYTES)
+    return fail(QMOE_ERR_WORKSPACE_TOO_SMALL,
+                "qmoe_forward_noalloc: %d tokens need %lld workspace bytes, the fixed scratch holds %lld",
+                T, (long long)plan.workspace_bytes, (long long)QMOE_NOALLOC_SCRATCH_BYTES);
+  void *ws = nullptr;
+  st = scratch_for_current_device(&ws);
+  if (st != QMOE_OK) return st;
+  return qmoe_forward_ex(desc, packed, x, logits, T, top_k, y, ws, (size_t)QMOE_NOALLOC_SCRATCH_BYTES, stream,
+                         nullptr);
 }
 
 qmoe_status qmoe_route_workspace_size(int32_t T, int32_t E, int32_t top_k, size_t *bytes) {

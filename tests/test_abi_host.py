@@ -328,3 +328,15 @@ def test_row_tiling_reaches_the_gemv_path():
     t = q.forward_plan(_desc(), 100, 6, workspace_limit=big // 2)
     assert t["num_tiles"] >= 2 and t["path"] == 2
 
+def test_noalloc_rejects_beyond_scratch_before_any_launch():
+    """qmoe_forward_noalloc checks the workspace against its fixed scratch on
+    the host: the 2048-token mixed prefill needs more and is refused without
+    touching the device (fake pointers)."""
+    d = q.layer_desc(128, 4096, 1536, "bf16", ("sym_int2", 64, "bf16"), ("sym_int4", 64, "bf16"))
+    L = q.lib()
+    fake = C.c_void_p(0x100000)
+    assert q.forward_plan(d, 2048, 8)["workspace_bytes"] > q.NOALLOC_SCRATCH_BYTES
+    assert L.qmoe_forward_noalloc(C.byref(d), fake, fake, fake, 2048, 8, fake, None) == 3
+    assert "scratch" in q.last_error()
+    assert L.qmoe_forward_noalloc(C.byref(d), fake, fake, fake, -1, 8, fake, None) == 1
+    assert L.qmoe_forward_noalloc(C.byref(d), fake, fake, fake, 0, 8, fake, None) == 0
