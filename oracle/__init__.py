@@ -56,9 +56,11 @@ def lib():
         L.orc_route.argtypes = [C.c_int, C.c_int, C.c_int, C.c_int, P, P, P, P, P, P]
         L.orc_silu.restype = C.c_double
         L.orc_silu.argtypes = [C.c_double]
+        L.orc_swiglu.restype = C.c_double
+        L.orc_swiglu.argtypes = [C.c_double] * 5
         L.orc_moe.restype = C.c_int
         L.orc_moe.argtypes = ([C.c_int] * 5 + [C.c_int] * 3 + [P] * 3 + [C.c_int] * 3 + [P] * 3
-                              + [P, P, C.c_int, C.c_int] + [P, P, C.c_int] + [P] * 5)
+                              + [P, P, C.c_int, C.c_int] + [C.c_double] * 3 + [P, P, C.c_int] + [P] * 5)
         L.orc_moe_f32acc.restype = C.c_int
         L.orc_moe_f32acc.argtypes = ([C.c_int] * 5 + [C.c_int] * 3 + [P] * 3 + [C.c_int] * 3 + [P] * 3
                                      + [P, P, C.c_int, P, P])
@@ -93,6 +95,14 @@ def double_to_half(v, dtype: str) -> np.ndarray:
 
 def silu(g: float) -> float:
     return lib().orc_silu(float(g))
+
+
+PLAIN_SWIGLU = (1.0, 0.0, 0.0)
+
+
+def swiglu(g: float, u: float, alpha: float = 1.0, beta: float = 0.0, limit: float = 0.0) -> float:
+    """Configurable SwiGLU: clip (limit > 0), then g * sigmoid(alpha g) * (u + beta)."""
+    return lib().orc_swiglu(float(g), float(u), float(alpha), float(beta), float(limit))
 
 
 # ------------------------------------------------------------------ codec
@@ -139,7 +149,9 @@ def moe(inp: dict, debug: bool = False, tokens=None, renorm: bool = True, thread
     ``tokens`` selects a subset of token rows (each token's output depends
     only on its own activation and logits).  Optional ``fc1_expert_bias``
     [E][2I] and ``fc2_expert_bias`` [E][H] (16-bit patterns of the activation
-    dtype) are per-expert output biases of FC1 and FC2.  ``renorm`` selects
+    dtype) are per-expert output biases of FC1 and FC2.  Optional
+    ``swiglu`` = (alpha, beta, limit) configures the SwiGLU (``swiglu``;
+    default the plain silu(g) * u).  ``renorm`` selects
     the routing weights as in ``route``.  ``threads`` > 1 evaluates disjoint token
     subsets on that many host threads (the C library runs without the
     interpreter lock); a token's result does not depend on the others, so
@@ -185,6 +197,7 @@ def moe(inp: dict, debug: bool = False, tokens=None, renorm: bool = True, thread
         FMT[sp.fc2.fmt], sp.fc2.block, DT[sp.fc2.scale_dtype],
         _p(arr["fc2_codes"]), _p(arr["fc2_scales"]), _p(arr["fc2_biases"]),
         _p(eb["fc1_expert_bias"]), _p(eb["fc2_expert_bias"]), int(bool(renorm)), int(sp.activation == "relu"),
+        *[float(v) for v in (inp.get("swiglu") or PLAIN_SWIGLU)],
         _p(x), _p(lg), T, _p(y64), _p(y16), _p(a), _p(h), _p(o))
     out = {"y64": y64, "y": y16, "status": rc}
     if debug:

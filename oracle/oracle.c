@@ -223,6 +223,20 @@ void orc_route(int T, int E, int k, int renorm, const float *logits, int32_t *id
 
 double orc_silu(double g) { return g / (1.0 + exp(-g)); }
 
+/* Configurable SwiGLU (onnxruntime pull request 33005, Description: the
+ * expert bias is followed by a configurable SwiGLU; the page gives no
+ * parameters).  With limit > 0 the gate is clipped from above and the up
+ * value to [-limit, limit]; then h = g * sigmoid(alpha * g) * (u + beta).
+ * alpha = 1, beta = 0, limit = 0 (no clipping) is the plain silu(g) * u. */
+double orc_swiglu(double g, double u, double alpha, double beta, double limit) {
+  if (limit > 0.0) {
+    if (g > limit) g = limit;
+    if (u > limit) u = limit;
+    if (u < -limit) u = -limit;
+  }
+  return g / (1.0 + exp(-alpha * g)) * (u + beta);
+}
+
 /* Activation-dtype element i of p: 16-bit patterns of bf16 / f16, or f32. */
 static double orc_act(const void *p, int64_t i, int dtype) {
   if (dtype == ORC_F32) return (double)((const float *)p)[i];
@@ -263,6 +277,8 @@ static void orc_matvec(const orc_mat *m, int64_t e, int64_t N, int64_t K, const 
  * Transformer FFN); a_dbg and fc1_ebias then have I entries per slot /
  * expert.  Returns 0, or -1 if a ternary row it used holds the invalid field
  * value 3 (read as 0).  renorm selects the routing weights as in orc_route.
+ * sw_alpha, sw_beta, sw_limit configure the SwiGLU as in orc_swiglu (1, 0, 0:
+ * the plain silu(g) * u).
  */
 int orc_moe(int E, int H, int I, int k, int act_dtype,
             int fc1_fmt, int fc1_block, int fc1_sdtype,
@@ -270,6 +286,7 @@ int orc_moe(int E, int H, int I, int k, int act_dtype,
             int fc2_fmt, int fc2_block, int fc2_sdtype,
             const uint8_t *fc2_codes, const uint16_t *fc2_scales, const uint16_t *fc2_biases,
             const void *fc1_ebias, const void *fc2_ebias, int renorm, int relu,
+            double sw_alpha, double sw_beta, double sw_limit,
             const void *x, const float *logits, int T,
             double *y64, void *y_out, double *a_dbg, double *h_dbg, double *o_dbg) {
   orc_mat w1 = {fc1_fmt, fc1_block, fc1_sdtype, fc1_codes, fc1_scales, fc1_biases};
@@ -301,7 +318,7 @@ int orc_moe(int E, int H, int I, int k, int act_dtype,
       if (relu)
         for (int64_t i = 0; i < I; ++i) h[i] = a[i] > 0.0 ? a[i] : 0.0;
       else
-        for (int64_t i = 0; i < I; ++i) h[i] = orc_silu(a[2 * i]) * a[2 * i + 1];
+        for (int64_t i = 0; i < I; ++i) h[i] = orc_swiglu(a[2 * i], a[2 * i + 1], sw_alpha, sw_beta, sw_limit);
       orc_matvec(&w2, e, H, I, h, o, wrow, &bad);
       if (fc2_ebias)
         for (int64_t n = 0; n < H; ++n) o[n] += orc_act(fc2_ebias, (int64_t)e * H + n, act_dtype);

@@ -78,7 +78,10 @@ def moe_dense(inp: dict, renorm: bool = True) -> np.ndarray:
             h = np.maximum(a, 0.0)
         else:
             gate, up = a[:, 0::2], a[:, 1::2]
-            h = gate / (1.0 + np.exp(-gate)) * up
+            alpha, beta, limit = inp.get("swiglu") or (1.0, 0.0, 0.0)
+            if limit > 0:
+                gate, up = np.minimum(gate, limit), np.clip(up, -limit, limit)
+            h = gate * (1.0 / (1.0 + np.exp(-alpha * gate))) * (up + beta)
         o = h @ W2.T
         if inp.get("fc2_expert_bias") is not None:
             o = o + half_bits_to_f64(inp["fc2_expert_bias"][e], sp.act_dtype)[None, :]

@@ -435,3 +435,43 @@ def test_threaded_evaluation_is_identical(oracle_lib):
         assert np.array_equal(a[key], b[key]), key
     sub = [3, 9, 30, 31]
     assert np.array_equal(oracle_lib.moe(inp, tokens=sub, threads=3)["y"], a["y"][sub])
+
+
+# ------------------------------------------------------ configurable SwiGLU
+SWIGLU_PARAMS = [(1.702, 1.0, 0.7), (0.5, -0.25, 0.0), (2.0, 0.5, 0.3)]
+
+
+@pytest.mark.parametrize("params", SWIGLU_PARAMS, ids=["a1.702-b1-l0.7", "a0.5-bm0.25", "a2-b0.5-l0.3"])
+def test_moe_configurable_swiglu_vs_dense_bruteforce(oracle_lib, params):
+    """alpha, beta and limit against the independent float64 brute force; the
+    inputs are scaled so that the limit clips a share of the gate and up values."""
+    spec = custom_moe_spec(E=4, H=128, I=64, top_k=2, fc1="sym_int4")
+    inp = synth.moe_inputs(spec, T=4, seed=41)
+    inp["swiglu"] = params
+    out = oracle_lib.moe(inp, debug=True)
+    ref = bf.moe_dense(inp)
+    assert np.allclose(out["y64"], ref, rtol=1e-10, atol=1e-12 * np.abs(ref).max())
+    assert not np.allclose(out["y64"], oracle_lib.moe(dict(inp, swiglu=None))["y64"])
+    if params[2] > 0:
+        a = out["a"]
+        assert np.mean(np.abs(a) > params[2]) > 0.02, "the limit clips nothing"
+
+
+def test_swiglu_closed_forms(oracle_lib):
+    """The plain parameters reproduce silu(g) * u; u = -beta gives 0; a gate
+    above the limit gives limit * sigmoid(alpha * limit) * (u + beta); a
+    large alpha turns sigmoid into the step, h -> max(g, 0) * (u + beta)."""
+    rng = np.random.default_rng(3)
+    for g, u in rng.standard_normal((50, 2)) * 4:
+        assert oracle_lib.swiglu(g, u) == oracle_lib.silu(g) * u
+        assert oracle_lib.swiglu(g, -0.75, 1.3, 0.75, 0.0) == 0.0
+        lim = 1.0
+        if g > lim and abs(u) < lim:
+            want = lim / (1.0 + np.exp(-1.702 * lim)) * (u + 1.0)
+            assert abs(oracle_lib.swiglu(g, u, 1.702, 1.0, lim) - want) <= 1e-15 * abs(want) + 1e-300
+        step = max(g, 0.0) * (u + 0.5)
+        if abs(g) > 0.5:
+            assert abs(oracle_lib.swiglu(g, u, 1e4, 0.5, 0.0) - step) <= 1e-12 * max(1.0, abs(step))
+    # clipping of the up value on both sides
+    assert oracle_lib.swiglu(2.0, 50.0, 1.0, 0.0, 3.0) == oracle_lib.swiglu(2.0, 3.0, 1.0, 0.0, 0.0)
+    assert oracle_lib.swiglu(2.0, -50.0, 1.0, 0.0, 3.0) == oracle_lib.swiglu(2.0, -3.0, 1.0, 0.0, 0.0)
