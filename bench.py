@@ -133,6 +133,9 @@ def graph_time(run_steps, K, trials, check=None):
     with torch.cuda.graph(g):
         run_steps()
     torch.cuda.synchronize()
+    for _ in range(2):  # untimed replays: clocks and caches settle before the trials
+        g.replay()
+    torch.cuda.synchronize()
     times = []
     for _ in range(trials):
         a = torch.cuda.Event(enable_timing=True)

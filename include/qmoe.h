@@ -74,7 +74,7 @@
 extern "C" {
 #endif
 
-#define QMOE_ABI_VERSION 7
+#define QMOE_ABI_VERSION 8
 
 typedef enum qmoe_status {
   QMOE_OK = 0,
@@ -197,6 +197,17 @@ typedef struct qmoe_forward_opts {
      as without tiling.  If one row does not fit: QMOE_ERR_WORKSPACE_TOO_SMALL.
      Must not be negative. */
   int64_t workspace_limit;
+  /* Configurable SwiGLU (onnxruntime pull request 33005, Description: a
+     configurable SwiGLU follows the expert bias; the page names no
+     parameters).  swiglu_params = 0: the plain h = silu(g) * u.  1: with
+     swiglu_limit > 0 the gate is clipped from above, g = min(g, limit), and
+     the up value to [-limit, limit]; then h = g * sigmoid(swiglu_alpha * g) *
+     (u + swiglu_beta).  alpha and beta finite, limit finite and >= 0 (0: no
+     clipping); SWIGLU layers only (INVALID_ARGUMENT otherwise). */
+  int32_t swiglu_params;
+  float swiglu_alpha;
+  float swiglu_beta;
+  float swiglu_limit;
 } qmoe_forward_opts;
 
 /* Host-side description of what a forward call would launch (diagnostic). */

@@ -44,7 +44,8 @@ class ForwardOpts(C.Structure):
                 ("ids_out", C.c_void_p), ("w_out", C.c_void_p), ("counts_out", C.c_void_p),
                 ("events", C.POINTER(C.c_void_p)), ("num_events", C.c_int32), ("reserved2", C.c_int32),
                 ("fc1_bias", C.c_void_p), ("fc2_bias", C.c_void_p), ("topk_weights", C.c_int32),
-                ("reserved3", C.c_int32), ("workspace_limit", C.c_int64)]
+                ("reserved3", C.c_int32), ("workspace_limit", C.c_int64), ("swiglu_params", C.c_int32),
+                ("swiglu_alpha", C.c_float), ("swiglu_beta", C.c_float), ("swiglu_limit", C.c_float)]
 
 
 class Plan(C.Structure):
@@ -180,19 +181,22 @@ def forward(desc, packed, x, logits, T, top_k, y, ws, stream=None):
 
 def forward_ex(desc, packed, x, logits, T, top_k, y, ws, stream=None, path="auto", h_out=None,
                ids_out=None, w_out=None, counts_out=None, events=None, fc1_bias=None, fc2_bias=None,
-               topk_weights="renormalized", workspace_limit=0):
+               topk_weights="renormalized", workspace_limit=0, swiglu=None):
     """``events``: optional list of raw hipEvent_t handles (ints), two per plan stage.
     ``fc1_bias`` [E][2I] / ``fc2_bias`` [E][H]: optional per-expert output biases
     in the activation dtype.  ``topk_weights``: "renormalized" (softmax over
     the selected logits) or "softmax_all" (selected entries of the softmax
     over all experts).  ``workspace_limit`` > 0 runs the tokens in row tiles
-    whose workspace fits the limit (``forward_plan`` gives the tile sizes)."""
+    whose workspace fits the limit (``forward_plan`` gives the tile sizes).
+    ``swiglu`` = (alpha, beta, limit) selects the configurable SwiGLU
+    (None: the plain silu(g) * u)."""
     ev = None
     if events:
         ev = (C.c_void_p * len(events))(*[C.c_void_p(int(e)) for e in events])
     opts = ForwardOpts(PATH[path], 0, _ptr(h_out), _ptr(ids_out), _ptr(w_out), _ptr(counts_out),
                        ev, len(events) if events else 0, 0, _ptr(fc1_bias), _ptr(fc2_bias),
-                       TOPK_WEIGHTS[topk_weights], 0, int(workspace_limit))
+                       TOPK_WEIGHTS[topk_weights], 0, int(workspace_limit), 1 if swiglu else 0,
+                       *([float(v) for v in swiglu] if swiglu else [0.0, 0.0, 0.0]))
     _check(lib().qmoe_forward_ex(C.byref(desc), _ptr(packed), _ptr(x), _ptr(logits), T, top_k,
                                  _ptr(y), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream),
                                  C.byref(opts)))

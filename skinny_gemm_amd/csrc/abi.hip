@@ -13,6 +13,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <cmath>
 #include <mutex>
 #include <string>
 
@@ -107,8 +108,11 @@ struct Carve {
   }
 };
 
-inline int64_t grouped_max_tiles(int64_t S, int E) {
-  const int64_t t = (S + kTileM - 1) / kTileM + std::min<int64_t>(E, S);
+// Upper bound of the grouped tiles of S routed rows over E experts in tiles
+// of tm rows (one partial tile per active expert at most).  The workspace
+// holds the bound of the smallest tile, so it does not depend on the choice.
+inline int64_t grouped_max_tiles(int64_t S, int E, int tm = kTileM) {
+  const int64_t t = (S + tm - 1) / tm + std::min<int64_t>(E, S);
   return (t + 7) / 8 * 8;  // a multiple of 8 lets the kernel spread tiles over the XCDs
 }
 
@@ -245,7 +249,7 @@ GemvShape pick_gemv(int64_t nwg, const MatLayout &L, int rows, int epilogue, int
 
 struct Plan {
   int path;
-  int mmax, mmax1, mmax2, ks1, ks2, tn1, tn2, max_active, max_tiles;
+  int mmax, mmax1, mmax2, ks1, ks2, tn1, tn2, max_active, max_tiles, tile_rows;
   int route_fused;
   int fc1_routes;  // GEMV path: FC1 routes the tokens itself (no routing kernel)
   bool softmax_all;  // unnormalised top-k weights, computed by the routing top-k
@@ -295,7 +299,8 @@ qmoe_status make_plan(const qmoe_layer_desc &d, int32_t T, int32_t k, int path_r
       return fail(QMOE_ERR_UNSUPPORTED, "affine formats on the grouped path need K/block <= %d",
                   kGroupedMaxAffineBlocks);
     p.route_fused = (T <= 16) ? 1 : 0;
-    p.max_tiles = (int)grouped_max_tiles((int64_t)T * k, d.num_experts);
+    p.tile_rows = grouped_tile_rows(L.fc1.affine || L.fc2.affine);
+    p.max_tiles = (int)grouped_max_tiles((int64_t)T * k, d.num_experts, p.tile_rows);
     p.softmax_all = softmax_all;
     p.kernels = std::string("route,") + "rowscale,grouped_fc1_" +
                 (d.activation == QMOE_ACT_RELU ? "relu" : "swiglu") + ",grouped_fc2,combine";
@@ -363,6 +368,15 @@ qmoe_status copy_diagnostics(const qmoe_layer_desc *desc, const qmoe_forward_opt
   if (e == hipSuccess && opts && opts->counts_out)
     e = hipMemcpyAsync(opts->counts_out, r.counts, (size_t)desc->num_experts * 4, hipMemcpyDeviceToDevice, s);
   return hip_status(e, "diagnostic copies");
+}
+
+// The configurable SwiGLU parameters of the call, if any.
+template <typename Args>
+void set_swiglu(Args &g, const qmoe_forward_opts *opts) {
+  g.sw_custom = (opts && opts->swiglu_params == 1) ? 1 : 0;
+  g.sw_alpha = g.sw_custom ? opts->swiglu_alpha : 1.f;
+  g.sw_beta = g.sw_custom ? opts->swiglu_beta : 0.f;
+  g.sw_limit = g.sw_custom ? opts->swiglu_limit : 0.f;
 }
 
 GemvArgs gemv_base(const MatLayout &L, const uint8_t *w) {
@@ -592,6 +606,15 @@ qmoe_status qmoe_forward_ex(const qmoe_layer_desc *desc, const void *packed, con
   if (opts && opts->workspace_limit < 0) return fail(QMOE_ERR_INVALID_ARGUMENT, "negative workspace_limit");
   if (opts && (opts->fc1_bias || opts->fc2_bias) && desc->act_dtype == QMOE_DTYPE_F32)
     return fail(QMOE_ERR_UNSUPPORTED, "expert biases need 16-bit activations");
+  if (opts && opts->swiglu_params != 0) {
+    if (opts->swiglu_params != 1)
+      return fail(QMOE_ERR_INVALID_ARGUMENT, "opts.swiglu_params must be 0 or 1");
+    if (desc->activation != QMOE_ACT_SWIGLU)
+      return fail(QMOE_ERR_INVALID_ARGUMENT, "SwiGLU parameters need a SWIGLU layer");
+    if (!std::isfinite(opts->swiglu_alpha) || !std::isfinite(opts->swiglu_beta) ||
+        !std::isfinite(opts->swiglu_limit) || opts->swiglu_limit < 0.f)
+      return fail(QMOE_ERR_INVALID_ARGUMENT, "SwiGLU alpha and beta must be finite, limit finite and >= 0");
+  }
   if (T == 0) return ok();
   const bool softmax_all = opts && opts->topk_weights == QMOE_TOPK_SOFTMAX_ALL;
   if (call_tiled(*desc, T, opts)) {
@@ -660,7 +683,7 @@ qmoe_status qmoe_forward_ex(const qmoe_layer_desc *desc, const void *packed, con
   ra.max_slots = p.max_active;
   ra.zero_buf = p.path == QMOE_PATH_GROUPED ? (int32_t *)(wsb + W.hmax) : nullptr;
   ra.zero_len = p.path == QMOE_PATH_GROUPED ? (int)((int64_t)T * top_k) : 0;
-  ra.tile_rows = p.path == QMOE_PATH_GROUPED ? kTileM : 0;
+  ra.tile_rows = p.path == QMOE_PATH_GROUPED ? p.tile_rows : 0;
   ra.max_tiles = p.max_tiles;
   ra.softmax_all = p.softmax_all ? 1 : 0;
   // optional per-stage events (diagnostic timing): stage i of the plan's
@@ -712,6 +735,7 @@ qmoe_status qmoe_forward_ex(const qmoe_layer_desc *desc, const void *packed, con
     if (e == hipSuccess) e = end();
     if (e != hipSuccess) return hip_status(e, "rowscale");
     GroupedArgs q1 = grouped_base(L.fc1, pk + L.fc1_off, wsc);
+    q1.tile_rows = p.tile_rows;
     q1.tile_info = ra.r.tile_info;
     q1.token_of = ra.r.token_of;
     q1.in_gather_token = 1;
@@ -725,12 +749,14 @@ qmoe_status qmoe_forward_ex(const qmoe_layer_desc *desc, const void *packed, con
     q1.row_list = ra.r.row_list;
     q1.bias = opts ? (const uint16_t *)opts->fc1_bias : nullptr;
     q1.relu = desc->activation == QMOE_ACT_RELU;
+    set_swiglu(q1, opts);
     q1.act_dtype = desc->act_dtype;
     e = begin();
     if (e == hipSuccess) e = launch_grouped(q1, kGEpiSwiGLU, p.max_tiles, s);
     if (e == hipSuccess) e = end();
     if (e != hipSuccess) return hip_status(e, "grouped fc1");
     GroupedArgs q2 = grouped_base(L.fc2, pk + L.fc2_off, wsc + desc->num_experts);
+    q2.tile_rows = p.tile_rows;
     q2.tile_info = ra.r.tile_info;
     q2.in = h32;
     q2.in_f32 = 1;
@@ -775,6 +801,7 @@ qmoe_status qmoe_forward_ex(const qmoe_layer_desc *desc, const void *packed, con
   g1.h_dbg = opts ? opts->h_out : nullptr;
   g1.bias = opts ? (const uint16_t *)opts->fc1_bias : nullptr;
   g1.relu = desc->activation == QMOE_ACT_RELU;
+  set_swiglu(g1, opts);
   g1.act_dtype = desc->act_dtype;
   e = begin();
   if (e == hipSuccess)
@@ -1017,13 +1044,14 @@ qmoe_status qmoe_linear(const qmoe_qmatrix_desc *desc, const void *packed, const
     GroupedArgs g = grouped_base(L, (const uint8_t *)packed,
                                  (const float *)((const uint8_t *)packed + L.stride + kLinearWscOff));
     g.dense_M = M;
+    g.tile_rows = grouped_tile_rows(L.affine);
     g.in = x;
     g.in_f16 = x_dtype == QMOE_DTYPE_F16;
     g.in_row_elems = L.K;
     g.in_rowsc = xsc;
     g.out_act = (uint16_t *)y;
     g.act_dtype = x_dtype;
-    return hip_status(launch_grouped(g, kGEpiStoreAct, (M + kTileM - 1) / kTileM, s), "linear mfma");
+    return hip_status(launch_grouped(g, kGEpiStoreAct, (M + g.tile_rows - 1) / g.tile_rows, s), "linear mfma");
   }
   const GemvShape gs = pick_gemv(L.RG, L, M, kEpiStoreAct, x_dtype == QMOE_DTYPE_F16);
   GemvArgs g = gemv_base(L, (const uint8_t *)packed);

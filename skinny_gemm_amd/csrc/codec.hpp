@@ -211,4 +211,14 @@ __device__ inline uint16_t f32_to_act(float v, int is_f16) {
   return is_f16 ? f32_to_f16_rne(v) : f32_to_bf16_rne(v);
 }
 
+// Configurable SwiGLU: with limit > 0 the gate is clipped from above and the
+// up value to [-limit, limit]; then g * sigmoid(alpha g) * (u + beta).
+__device__ inline float swiglu_cfg(float g, float u, float alpha, float beta, float limit) {
+  if (limit > 0.f) {
+    g = fminf(g, limit);
+    u = fminf(fmaxf(u, -limit), limit);
+  }
+  return g / (1.f + expf(-alpha * g)) * (u + beta);
+}
+
 }  // namespace qmoe

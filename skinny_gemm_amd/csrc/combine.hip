@@ -120,7 +120,8 @@ hipError_t launch_gemv(const GemvArgs &a, int epilogue, int in_f16, int rows, in
                        int grid_slots, hipStream_t s) {
   // the EXT instances (bias, ReLU, unnormalised routed weights) only when the call uses them
   const void *fn = gemv_kernel_ptr(a.qtype, epilogue, in_f16, rows, block, tn,
-                                   a.bias != nullptr || a.relu != 0 || a.route_softmax_all != 0);
+                                   a.bias != nullptr || a.relu != 0 || a.route_softmax_all != 0 ||
+                                       a.sw_custom != 0);
   if (fn == nullptr) return hipErrorInvalidConfiguration;  // no kernel for this (rows, tn) pairing
   GemvArgs args = a;
   void *kargs[] = {&args};

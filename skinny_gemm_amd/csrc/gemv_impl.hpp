@@ -427,10 +427,11 @@ __global__ __launch_bounds__(512) void gemv_kernel(const GemvArgs a) {
     const int64_t n = (int64_t)rg * kRowsPerGroup + 16 * (t0 + t) + (lo & 15);
     // EXT instances only: the optional per-expert output bias (FC1 before
     // the activation, FC2 before the routing weight) and the ReLU FFN
-    bool relu = false;
+    bool relu = false, custom = false;
     if constexpr (EXT && EPI != kEpiStoreAct) {
       if (a.bias) v += half_to_f32_rt(a.bias[(int64_t)e * N + n], a.act_dtype == QMOE_DTYPE_F16);
       relu = a.relu != 0;
+      custom = a.sw_custom != 0;
     }
     if constexpr (EPI == kEpiStoreAct) {
       if (valid) a.out_act[(int64_t)m * N + n] = f32_to_act(v, a.act_dtype == QMOE_DTYPE_F16);
@@ -440,7 +441,9 @@ __global__ __launch_bounds__(512) void gemv_kernel(const GemvArgs a) {
       const float up = __shfl_xor(v, 1);
       if (valid && (relu || (lo & 1) == 0)) {
         const float gt = v;
-        const float h = relu ? fmaxf(v, 0.f) : gt / (1.f + expf(-gt)) * up;
+        const float h = relu     ? fmaxf(v, 0.f)
+                        : custom ? swiglu_cfg(gt, up, a.sw_alpha, a.sw_beta, a.sw_limit)
+                                 : gt / (1.f + expf(-gt)) * up;
         const int64_t Ih = relu ? N : N / 2;
         const int64_t i = relu ? n : n / 2;
         const int64_t p = pbase + m;

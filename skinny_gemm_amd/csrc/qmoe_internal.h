@@ -220,6 +220,8 @@ struct GemvArgs {
   uint16_t *h_hi, *h_lo;   // kEpiSwiGLU: [p][N/2] bf16 parts of h
   float *h_dbg;            // kEpiSwiGLU: optional [slot][N/2] fp32 ([slot][N] with relu)
   int relu;                // kEpiSwiGLU: the FC1 rows are single ReLU channels, h = max(a, 0)
+  int sw_custom;           // kEpiSwiGLU (EXT instances): configurable SwiGLU with the next three
+  float sw_alpha, sw_beta, sw_limit;
   const uint16_t *bias;    // kEpiSwiGLU, kEpiDown: optional per-expert output bias [E][N] in act_dtype
   int act_dtype;           // activation dtype of out_act and bias
   const float *route_w;    // kEpiDown: routing weights [T*k]
@@ -270,9 +272,51 @@ hipError_t launch_read_probe(const void *src, int64_t bytes, uint32_t *sink, int
 hipError_t launch_split_f32(const float *x, int64_t n, uint16_t *hi, uint16_t *lo, hipStream_t s);
 
 // ----------------------------------------------------------- grouped MFMA
-constexpr int kTileM = 64;   // rows (tokens) per grouped tile
-constexpr int kTileN = 128;      // outputs per grouped tile, 16-bit input (4 waves x 32)
-constexpr int kTileNWide = 256;  // outputs per grouped tile, fp32 input (4 waves x 64)
+// Shape of a grouped workgroup tile (4 waves): MI 16-row MFMA row tiles
+// (TM = 16 MI rows), NJ 16-column slices per wave (64 NJ outputs per tile)
+// and KT k per staged activation tile.  Affine formats keep per-row block
+// sums of the activations in LDS, laid out for 64-row tiles; the other
+// formats take the shapes below (compile-time tuning constants).
+#ifndef QMOE_GROUPED_MI
+#define QMOE_GROUPED_MI 8
+#endif
+#ifndef QMOE_GROUPED_NJ16
+#define QMOE_GROUPED_NJ16 2
+#endif
+#ifndef QMOE_GROUPED_KT16
+#define QMOE_GROUPED_KT16 64
+#endif
+#ifndef QMOE_GROUPED_NJ32
+#define QMOE_GROUPED_NJ32 4
+#endif
+#ifndef QMOE_GROUPED_KT32
+#define QMOE_GROUPED_KT32 64
+#endif
+// workgroups per compute unit the 128-row kernels are built for (registers)
+#ifndef QMOE_GROUPED_WG_PER_CU
+#define QMOE_GROUPED_WG_PER_CU 2
+#endif
+constexpr int kTileM = 64;  // rows per grouped tile with an affine matrix
+
+struct GroupedShape {
+  int mi, nj, kt;
+};
+// in_f32: the fp32 FC2 input, staged as f16 hi + lo parts.  The 64-row shape
+// (affine formats, and a non-affine matrix whose layer has an affine one):
+__host__ __device__ constexpr GroupedShape grouped_shape_64(bool in_f32) {
+  return GroupedShape{4, in_f32 ? 4 : 2, in_f32 ? 64 : 128};
+}
+// The shape of the other layers:
+__host__ __device__ constexpr GroupedShape grouped_shape_main(bool in_f32) {
+  return GroupedShape{QMOE_GROUPED_MI, in_f32 ? QMOE_GROUPED_NJ32 : QMOE_GROUPED_NJ16,
+                      in_f32 ? QMOE_GROUPED_KT32 : QMOE_GROUPED_KT16};
+}
+// Rows per grouped tile of a call (FC1 and FC2 share the tile list).
+inline int grouped_tile_rows(bool any_affine) { return any_affine ? kTileM : 16 * QMOE_GROUPED_MI; }
+// The shape one matrix runs with for those tile rows.
+inline GroupedShape grouped_shape(bool affine, int tile_rows, bool in_f32) {
+  return (!affine && tile_rows == 16 * QMOE_GROUPED_MI) ? grouped_shape_main(in_f32) : grouped_shape_64(in_f32);
+}
 
 enum GroupedEpilogue { kGEpiSwiGLU = 0, kGEpiStoreF32 = 1, kGEpiStoreAct = 2 };
 
@@ -284,7 +328,8 @@ struct GroupedArgs {
   const float *wsc;        // [E] power-of-two weight pre-scale
   // rows
   const int4 *tile_info;   // routed: {expert, first position, rows, 0}
-  int dense_M;             // > 0: dense rows, tiles of kTileM over M
+  int tile_rows;           // rows per tile: kTileM or kTileMWide (routed: as the tile list)
+  int dense_M;             // > 0: dense rows, tiles of tile_rows over M
   const int32_t *token_of; // routed FC1: input row of position p
   int in_gather_token;
   // input: 16-bit rows (in_f32 = 0, dtype in_f16), fp32 rows (in_f32 = 1),
@@ -302,6 +347,8 @@ struct GroupedArgs {
   int act_dtype;           // activation dtype of out_act and bias
   float *h_dbg;            // optional fp32 copy of h in slot order
   int relu;                // kGEpiSwiGLU: h = max(a, 0) per row instead of SwiGLU pairs
+  int sw_custom;           // kGEpiSwiGLU: configurable SwiGLU with the next three
+  float sw_alpha, sw_beta, sw_limit;
   const int32_t *row_list;
 };
 

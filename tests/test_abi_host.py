@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_abi_version():
-    assert q.abi_version() == 7
+    assert q.abi_version() == 8
 
 
 def _desc(**kw):
@@ -340,3 +340,21 @@ def test_noalloc_rejects_beyond_scratch_before_any_launch():
     assert "scratch" in q.last_error()
     assert L.qmoe_forward_noalloc(C.byref(d), fake, fake, fake, -1, 8, fake, None) == 1
     assert L.qmoe_forward_noalloc(C.byref(d), fake, fake, fake, 0, 8, fake, None) == 0
+
+
+def test_swiglu_parameters_validated_before_launch():
+    d = _desc()
+    L = q.lib()
+    fake = C.c_void_p(0x100000)
+
+    def opts(flag, a, b, lim):
+        o = q.ForwardOpts()
+        o.swiglu_params, o.swiglu_alpha, o.swiglu_beta, o.swiglu_limit = flag, a, b, lim
+        return o
+    for o in (opts(2, 1.0, 0.0, 0.0), opts(1, float("nan"), 0.0, 0.0), opts(1, 1.0, float("inf"), 0.0),
+              opts(1, 1.0, 0.0, -1.0)):
+        assert L.qmoe_forward_ex(C.byref(d), fake, fake, fake, 4, 6, fake, fake, 1 << 30, None, C.byref(o)) == 1
+    relu = q.layer_desc(64, 768, 3072, "bf16", ("ternary", 128, "f16"), ("ternary", 128, "f16"), "relu")
+    o = opts(1, 1.702, 1.0, 7.0)
+    assert L.qmoe_forward_ex(C.byref(relu), fake, fake, fake, 4, 1, fake, fake, 1 << 30, None, C.byref(o)) == 1
+    assert "SWIGLU" in q.last_error()

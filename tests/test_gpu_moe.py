@@ -56,7 +56,7 @@ ORACLE_THREADS = max(1, min(16, len(os.sched_getaffinity(0))))
 
 
 def run_case(spec, T, seed, logits_mode="iid", path="auto", tokens=None, expert_bias=0.0,
-             topk_weights="renormalized", x_edit=None):
+             topk_weights="renormalized", x_edit=None, swiglu=None):
     from skinny_gemm_amd.layer import MoeLayer, to_device_bits, bits_of
     renorm = topk_weights == "renormalized"
     log(f"[moe] {spec.name} T={T} seed={seed} logits={logits_mode} path={path} expert_bias={expert_bias} "
@@ -64,10 +64,12 @@ def run_case(spec, T, seed, logits_mode="iid", path="auto", tokens=None, expert_
     inp = _inputs(spec, T, seed, logits_mode, expert_bias)
     if x_edit is not None:
         inp["x"] = x_edit(inp["x"].copy(), spec)
+    if swiglu is not None:
+        inp["swiglu"] = swiglu
     layer = MoeLayer.from_spec(spec, inp)
     x = to_device_bits(inp["x"], spec.act_dtype)
     lg = torch.from_numpy(inp["logits"]).cuda()
-    y, dbg = layer.forward(x, lg, spec.top_k, path=path, debug=True, topk_weights=topk_weights)
+    y, dbg = layer.forward(x, lg, spec.top_k, path=path, debug=True, topk_weights=topk_weights, swiglu=swiglu)
     torch.cuda.synchronize()
     ref = oracle.moe(inp, debug=True, tokens=tokens, renorm=renorm, threads=ORACLE_THREADS)
     r = oracle.route(inp["logits"] if tokens is None else inp["logits"][tokens], spec.top_k, renorm)
@@ -706,3 +708,30 @@ def test_relu_bias_unnormalised_weights_together(T, path):
         assert res["ok"], res
     else:
         run_case(spec, T, 121 + T, path=path, expert_bias=0.1, topk_weights="softmax_all")
+
+
+# ------------------------------------------------- configurable SwiGLU
+@pytest.mark.parametrize("name,T,path,params", [
+    ("dsv2lite_int4", 1, "auto", (1.702, 1.0, 7.0)),     # routing inside FC1 (EXT instance)
+    ("dsv2lite_int4", 8, "auto", (1.702, 1.0, 7.0)),     # routing kernels
+    ("dsv2lite_int4", 40, "grouped", (1.702, 1.0, 7.0)),
+    ("switch_base_ternary", 1, "auto", (0.5, -0.25, 0.0)),
+])
+def test_configurable_swiglu_workloads(name, T, path, params):
+    """alpha, beta and limit in the FC1 epilogue of both paths; the inputs
+    are such that the plain SwiGLU misses the tolerance (checked on the
+    oracle), and the limit clips a share of the FC1 outputs."""
+    spec = synth.MOE_WORKLOADS[name]
+    res = run_case(spec, T, 51, path=path, swiglu=params)
+    inp = res["inp"]
+    plain = oracle.moe(dict(inp, swiglu=None), threads=ORACLE_THREADS)
+    assert not compare(res["ybits"], plain["y"], plain["y64"], spec.act_dtype)["ok"]
+    if params[2] > 0:
+        a = oracle.moe(inp, debug=True, tokens=[0])["a"]
+        assert np.mean(np.abs(a) > params[2]) > 0.01, "the limit clips nothing"
+
+
+@pytest.mark.parametrize("T,path", [(3, "auto"), (33, "grouped")])
+def test_configurable_swiglu_with_biases(T, path):
+    spec = custom_moe_spec(E=4, H=128, I=192, top_k=2, fc1="sym_int2", fc2="sym_int4")
+    run_case(spec, T, 52, path=path, expert_bias=0.1, swiglu=(2.0, 0.5, 0.6))
