@@ -64,6 +64,9 @@ def lib():
         L.orc_moe_f32acc.restype = C.c_int
         L.orc_moe_f32acc.argtypes = ([C.c_int] * 5 + [C.c_int] * 3 + [P] * 3 + [C.c_int] * 3 + [P] * 3
                                      + [P, P, C.c_int, P, P])
+        L.orc_moe_channels.restype = C.c_int
+        L.orc_moe_channels.argtypes = ([C.c_int] * 5 + [C.c_int] * 3 + [P] * 2 + [C.c_int] * 3 + [P] * 2
+                                       + [P, P, C.c_int, P, C.c_int] + [P] * 3)
         L.orc_linear.argtypes = [C.c_int, C.c_int, C.c_int, P, P, P, i64, i64, P, C.c_int, C.c_int,
                                  i64, i64, P, P]
         _lib = L
@@ -232,6 +235,37 @@ def moe_f32acc(inp: dict, tokens=None):
         _p(arr["fc2_codes"]), _p(arr["fc2_scales"]), _p(arr["fc2_biases"]),
         _p(x), _p(lg), T, _p(y32), _p(y))
     return {"y32": y32, "y": y, "status": rc}
+
+
+def moe_channels(inp: dict, channels, debug: bool = False):
+    """Gathered channels (``orc_moe_channels``): ``channels`` [T][k][C] int32,
+    entries < 0 unused; the down projection comes channel-major from
+    ``inp["down_codes"]`` [E][I][H*bits/8] and ``inp["down_scales"]``
+    [E][I][H/block] in the format ``inp["down_fmt"]`` = (fmt, block,
+    scale_dtype).  SwiGLU layers with renormalised weights, no biases."""
+    sp = inp["spec"]
+    assert sp.activation == "swiglu" and sp.act_dtype in ("bf16", "f16", "f32")
+    adt = np.float32 if sp.act_dtype == "f32" else np.uint16
+    x = _c(inp["x"], adt)
+    lg = _c(inp["logits"], np.float32)
+    T = x.shape[0]
+    ch = _c(channels, np.int32)
+    assert ch.shape[:2] == (T, sp.top_k)
+    Cn = ch.shape[2]
+    dfmt, dblock, dsd = inp["down_fmt"]
+    y64 = np.empty((T, sp.H), dtype=np.float64)
+    y = np.empty((T, sp.H), dtype=adt)
+    h = np.empty((T, sp.top_k, Cn), dtype=np.float64) if debug else None
+    c1, s1 = _c(inp["fc1_codes"], np.uint8), _c(inp["fc1_scales"], np.uint16)
+    cd, sd = _c(inp["down_codes"], np.uint8), _c(inp["down_scales"], np.uint16)
+    rc = lib().orc_moe_channels(sp.E, sp.H, sp.I, sp.top_k, DT[sp.act_dtype],
+                                FMT[sp.fc1.fmt], sp.fc1.block, DT[sp.fc1.scale_dtype], _p(c1), _p(s1),
+                                FMT[dfmt], dblock, DT[dsd], _p(cd), _p(sd),
+                                _p(x), _p(lg), T, _p(ch), Cn, _p(y64), _p(y), _p(h))
+    out = {"y64": y64, "y": y, "status": rc}
+    if debug:
+        out["h"] = h
+    return out
 
 
 def linear(inp: dict, n0: int = 0, n1=None):

@@ -428,6 +428,81 @@ int orc_moe_f32acc(int E, int H, int I, int k, int act_dtype,
 }
 
 /*
+ * Gathered channels (MoE channel selection explainer: top-k channel
+ * selection reads the selected channels in full and computes them exactly).
+ * For each routed slot (t, j) with expert e, channels ch[t][j][0..C-1]
+ * (entries < 0 are unused) are the only ones computed:
+ *   g = W1[e][2c] . x_t,  u = W1[e][2c+1] . x_t,  h_c = silu(g) * u,
+ *   y_t = sum_j w[t][j] * sum_{listed c} h_c * D[e][c][:],
+ * where D[e] = the down projection stored channel-major, [I][H], row c being
+ * channel c's column of the down matrix (its own canonical codes and block
+ * scales along H).  Summed in double in list order, y rounded once.  Routing
+ * as orc_route with renormalised weights.  Returns 0, or -1 for an invalid
+ * ternary field.
+ */
+int orc_moe_channels(int E, int H, int I, int k, int act_dtype,
+                     int fc1_fmt, int fc1_block, int fc1_sdtype,
+                     const uint8_t *fc1_codes, const uint16_t *fc1_scales,
+                     int dn_fmt, int dn_block, int dn_sdtype,
+                     const uint8_t *dn_codes, const uint16_t *dn_scales,
+                     const void *x, const float *logits, int T, const int32_t *ch, int C,
+                     double *y64, void *y_out, double *h_dbg) {
+  orc_mat w1 = {fc1_fmt, fc1_block, fc1_sdtype, fc1_codes, fc1_scales, NULL};
+  const int64_t S = (int64_t)T * k;
+  int32_t *ids = (int32_t *)malloc(sizeof(int32_t) * (size_t)(S > 0 ? S : 1));
+  double *wts = (double *)malloc(sizeof(double) * (size_t)(S > 0 ? S : 1));
+  int32_t *counts = (int32_t *)malloc(sizeof(int32_t) * (size_t)E);
+  int32_t *offsets = (int32_t *)malloc(sizeof(int32_t) * (size_t)(E + 1));
+  int32_t *rows = (int32_t *)malloc(sizeof(int32_t) * (size_t)(S > 0 ? S : 1));
+  double *xv = (double *)malloc(sizeof(double) * (size_t)H);
+  double *wrow = (double *)malloc(sizeof(double) * (size_t)H);
+  double *o = (double *)malloc(sizeof(double) * (size_t)H);
+  const int64_t row1 = (int64_t)H * orc_bits(fc1_fmt) / 8, nb1 = H / fc1_block;
+  const int64_t rowd = (int64_t)H * orc_bits(dn_fmt) / 8, nbd = H / dn_block;
+  int bad = 0;
+  orc_route(T, E, k, 1, logits, ids, wts, counts, offsets, rows);
+  for (int t = 0; t < T; ++t) {
+    for (int64_t n = 0; n < H; ++n) xv[n] = orc_act(x, (int64_t)t * H + n, act_dtype);
+    double *yt = y64 + (int64_t)t * H;
+    for (int64_t n = 0; n < H; ++n) yt[n] = 0.0;
+    for (int j = 0; j < k; ++j) {
+      const int64_t r = (int64_t)t * k + j;
+      const int64_t e = ids[r];
+      for (int64_t n = 0; n < H; ++n) o[n] = 0.0;
+      for (int c = 0; c < C; ++c) {
+        const int32_t cc = ch[r * C + c];
+        double h = 0.0;
+        if (cc >= 0) {
+          double a[2];
+          for (int q = 0; q < 2; ++q) {
+            const int64_t rr = e * 2 * (int64_t)I + 2 * (int64_t)cc + q;
+            orc_dequant_row(w1.fmt, w1.block, w1.sdtype, w1.codes + rr * row1, w1.scales + rr * nb1, NULL, H, wrow,
+                            &bad);
+            double acc = 0.0;
+            for (int64_t kk = 0; kk < H; ++kk) acc += wrow[kk] * xv[kk];
+            a[q] = acc;
+          }
+          h = orc_silu(a[0]) * a[1];
+          const int64_t dr = e * (int64_t)I + cc;
+          orc_dequant_row(dn_fmt, dn_block, dn_sdtype, dn_codes + dr * rowd, dn_scales + dr * nbd, NULL, H, wrow,
+                          &bad);
+          for (int64_t n = 0; n < H; ++n) o[n] += h * wrow[n];
+        }
+        if (h_dbg) h_dbg[r * C + c] = h;
+      }
+      for (int64_t n = 0; n < H; ++n) yt[n] += wts[r] * o[n];
+    }
+    for (int64_t n = 0; n < H; ++n) {
+      if (act_dtype == ORC_F32) ((float *)y_out)[(int64_t)t * H + n] = (float)yt[n];
+      else ((uint16_t *)y_out)[(int64_t)t * H + n] = orc_double_to_half(yt[n], act_dtype);
+    }
+  }
+  free(ids); free(wts); free(counts); free(offsets); free(rows);
+  free(xv); free(wrow); free(o);
+  return bad ? -1 : 0;
+}
+
+/*
  * Dense quantized matmul y = x W^T for output rows n in [n0, n1):
  * y64 [M][n1-n0] unrounded, y16 the same rounded to x's dtype.
  */

@@ -40,4 +40,5 @@ from .workloads import (  # noqa: F401
     moe_inputs,
     linear_inputs,
     canonical_matrix_bytes,
+    channel_inputs,
 )

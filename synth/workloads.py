@@ -34,7 +34,7 @@ from typing import Optional
 
 import numpy as np
 
-from .rng import Key, normals, f32_to_bf16_bits, f32_to_f16_bits, codes_uniform, codes_ternary
+from .rng import Key, normals, f32_to_bf16_bits, f32_to_f16_bits, codes_uniform, codes_ternary, raw_u64
 
 # name -> (bits per stored field, has a per-block bias)
 FORMATS = {
@@ -236,3 +236,38 @@ def custom_linear_spec(K: int, fmt: str = "affine_int2", block: int = 128, scale
                        act_dtype: str = "f16", name: Optional[str] = None) -> LinearSpec:
     nm = name or f"custom_linear_K{K}_{fmt}{block}_{scale_dtype}_{act_dtype}"
     return LinearSpec(nm, K=K, Ns=(), fmt=MatFmt(fmt, block, scale_dtype), act_dtype=act_dtype)
+
+
+def channel_inputs(spec: MoeSpec, inp: dict, budget: float, seed: int = 0, down: Optional[MatFmt] = None) -> dict:
+    """Inputs of a gathered-channel call on top of ``moe_inputs``' arrays.
+
+    The down projection stored channel-major: ``down_codes`` [E][I][H*bits/8]
+    and ``down_scales`` [E][I][H/block] (row c is channel c's column of the
+    down matrix, quantized along H), drawn with the same recipe in the format
+    ``down`` (default: the layer's FC2 format).  ``channels`` [T][k][C] int32:
+    per token, round(budget * k * I) distinct channel picks split at random
+    over its k routed slots (so one slot may get many and another none), each
+    slot's channels a random subset of [0, I) in random order, padded with -1
+    to the longest list.
+    """
+    down = down or spec.fc2
+    wl = spec.name
+    c, sc, _ = _matrix(wl, "down_cm", seed, down, spec.E, spec.I, spec.H, spec.scale_sigma, spec.bias_sigma)
+    out = {"down_codes": c, "down_scales": sc, "down_fmt": (down.fmt, down.block, down.scale_dtype)}
+    T, k, I = inp["x"].shape[0], spec.top_k, spec.I
+    n = int(round(budget * k * I))
+    r = Key(seed, wl, f"channels[T={T},n={n}]")
+    u = raw_u64(r, T * (k * I + 1)).reshape(T, k * I + 1)
+    lists = []
+    for t in range(T):
+        # a random permutation of the (slot, channel) pairs, first n kept
+        order = np.argsort(u[t, :k * I], kind="stable")[:n]
+        slot, chan = order // I, order % I
+        lists.append([chan[slot == j] for j in range(k)])
+    C = max(1, max(len(l) for per in lists for l in per))
+    ch = np.full((T, k, C), -1, dtype=np.int32)
+    for t in range(T):
+        for j in range(k):
+            ch[t, j, :len(lists[t][j])] = lists[t][j]
+    out["channels"] = ch
+    return out

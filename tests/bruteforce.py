@@ -95,3 +95,32 @@ def linear_dense(inp: dict) -> np.ndarray:
                 inp["biases"], sp.K)
     x = half_bits_to_f64(inp["x"], sp.act_dtype)
     return x @ W.T
+
+
+def moe_channels_dense(inp: dict, channels) -> np.ndarray:
+    """Gathered channels by dense masking: for each token, h over all channels
+    of each selected expert, kept (with multiplicity) only where listed, then
+    y_t = sum_j g_j * sum_c h_c D_e[c]."""
+    sp = inp["spec"]
+    E, H, I, k = sp.E, sp.H, sp.I, sp.top_k
+    x = half_bits_to_f64(inp["x"], sp.act_dtype)
+    logits = np.asarray(inp["logits"])
+    dfmt, dblock, dsd = inp["down_fmt"]
+    y = np.zeros((x.shape[0], H), dtype=np.float64)
+    for t in range(x.shape[0]):
+        order = np.lexsort((np.arange(E), -logits[t].astype(np.float64)))[:k]
+        z = logits[t].astype(np.float64)
+        p = np.exp(z[order] - z[order].max())
+        g = p / p.sum()
+        for j, e in enumerate(order):
+            W1 = dequant(sp.fc1.fmt, sp.fc1.block, sp.fc1.scale_dtype, inp["fc1_codes"][e], inp["fc1_scales"][e],
+                         None, H)
+            D = dequant(dfmt, dblock, dsd, inp["down_codes"][e], inp["down_scales"][e], None, H)
+            a = W1 @ x[t]
+            h = a[0::2] / (1.0 + np.exp(-a[0::2])) * a[1::2]
+            mult = np.zeros(I)
+            for c in np.asarray(channels)[t, j]:
+                if c >= 0:
+                    mult[c] += 1.0
+            y[t] += g[j] * ((h * mult) @ D)
+    return y

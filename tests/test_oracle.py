@@ -475,3 +475,60 @@ def test_swiglu_closed_forms(oracle_lib):
     # clipping of the up value on both sides
     assert oracle_lib.swiglu(2.0, 50.0, 1.0, 0.0, 3.0) == oracle_lib.swiglu(2.0, 3.0, 1.0, 0.0, 0.0)
     assert oracle_lib.swiglu(2.0, -50.0, 1.0, 0.0, 3.0) == oracle_lib.swiglu(2.0, -3.0, 1.0, 0.0, 0.0)
+
+
+# --------------------------------------------------- gathered channels
+def _transpose_fc2_to_down(inp):
+    """Channel-major down projection equal to the FC2 matrix exactly: every
+    FC2 scale of an expert set to that expert's first scale, the codes
+    transposed and repacked along H (blocks of the FC2 block size)."""
+    sp = inp["spec"]
+    bits = bf.BITS[sp.fc2.fmt]
+    q = bf.fields(np.asarray(inp["fc2_codes"], dtype=np.uint8), bits, sp.I)          # [E][H][I] fields
+    s = np.repeat(np.asarray(inp["fc2_scales"])[:, :1, :1], sp.H, 1)
+    s = np.repeat(s, sp.I // sp.fc2.block, 2)
+    inp = dict(inp, fc2_scales=np.ascontiguousarray(s))
+    qt = np.ascontiguousarray(np.transpose(q, (0, 2, 1)))                             # [E][I][H]
+    per = 8 // bits
+    packed = np.zeros(qt.shape[:2] + (sp.H // per,), dtype=np.uint8)
+    for f in range(per):
+        packed |= (qt[:, :, f::per] << (bits * f)).astype(np.uint8)
+    ds = np.repeat(np.asarray(inp["fc2_scales"])[:, :1, :1], sp.I, 1)
+    ds = np.repeat(ds, sp.H // sp.fc2.block, 2)
+    inp["down_codes"], inp["down_scales"] = packed, np.ascontiguousarray(ds)
+    inp["down_fmt"] = (sp.fc2.fmt, sp.fc2.block, sp.fc2.scale_dtype)
+    return inp
+
+
+@pytest.mark.parametrize("cfg", [dict(E=4, H=128, I=64, top_k=2, fc1="sym_int4"),
+                                 dict(E=3, H=128, I=128, top_k=3, fc1="sym_int2", fc2="ternary", block2=128,
+                                      scale_dtype="f16")], ids=["int4", "int2-ternary"])
+def test_channels_all_selected_equal_the_full_layer(oracle_lib, cfg):
+    """Every channel listed once, in order, with a down projection equal to
+    FC2: the gathered layer is the full layer (same products, same order)."""
+    spec = custom_moe_spec(**cfg)
+    inp = _transpose_fc2_to_down(synth.moe_inputs(spec, T=3, seed=8))
+    ch = np.broadcast_to(np.arange(spec.I, dtype=np.int32), (3, spec.top_k, spec.I)).copy()
+    got = oracle_lib.moe_channels(inp, ch)
+    ref = oracle_lib.moe(inp)
+    assert np.array_equal(got["y64"], ref["y64"]) and np.array_equal(got["y"], ref["y"])
+
+
+@pytest.mark.parametrize("budget", [0.05, 0.18, 0.6])
+def test_channels_vs_dense_bruteforce(oracle_lib, budget):
+    spec = custom_moe_spec(E=6, H=128, I=128, top_k=3, fc1="sym_int4")
+    inp = synth.moe_inputs(spec, T=4, seed=9)
+    inp.update(synth.channel_inputs(spec, inp, budget, seed=9))
+    ch = inp["channels"]
+    assert ch.shape[:2] == (4, 3) and (ch >= 0).sum() == 4 * round(budget * 3 * 128)
+    got = oracle_lib.moe_channels(inp, ch)
+    ref = bf.moe_channels_dense(inp, ch)
+    assert np.allclose(got["y64"], ref, rtol=1e-10, atol=1e-12 * np.abs(ref).max())
+    # a repeated channel counts twice, an empty list gives zero
+    ch2 = ch.copy()
+    ch2[0, 0, :] = -1
+    ch2[0, 0, 0] = ch2[0, 0, 1] = 5
+    assert np.allclose(oracle_lib.moe_channels(inp, ch2)["y64"], bf.moe_channels_dense(inp, ch2),
+                       rtol=1e-10, atol=1e-12 * np.abs(ref).max())
+    zero = oracle_lib.moe_channels(inp, np.full_like(ch, -1))
+    assert np.all(zero["y64"] == 0.0)
