@@ -476,6 +476,67 @@ def tiled_prefill_time(layer, spec, T: int, div: int, reps: int = 3) -> dict:
 
 
 # ----------------------------------------------------------- CPU baseline
+def channel_decode_time(spec, T: int, budget: float, K: int = 32, trials: int = 5,
+                        rotate_bytes: float = float(1 << 30), seed: int = 0) -> dict:
+    """Gathered-channel calls (qmoe_forward_channels) at a per-token channel
+    budget: graph-replay time per call over rotating channel-packed weight
+    copies and distinct input batches, and the bytes of the listed FC1 rows
+    and down rows (with their scales) each call reads."""
+    import torch
+    import synth
+    import skinny_gemm_amd as q
+    from skinny_gemm_amd.layer import to_device_bits
+    desc = q.layer_desc(spec.E, spec.H, spec.I, spec.act_dtype, (spec.fc1.fmt, spec.fc1.block, spec.fc1.scale_dtype),
+                        (spec.fc2.fmt, spec.fc2.block, spec.fc2.scale_dtype))
+    size = q.channel_prepacked_size(desc)
+    L = max(2, math.ceil(rotate_bytes / size))
+    packs = []
+    for c in range(L):
+        inp = synth.moe_inputs(spec, 1, seed, weight_copy=c)
+        inp.update(synth.channel_inputs(spec, inp, budget, seed))
+        pk = torch.empty(size, dtype=torch.uint8, device="cuda")
+        src = [to_device_bits(inp[k], None) for k in ("fc1_codes", "fc1_scales", "down_codes", "down_scales")]
+        q.channel_prepack(desc, *src, pk)
+        torch.cuda.synchronize()
+        packs.append(pk)
+        del src, inp
+    P = K
+    steps = synth.moe_inputs(spec, T * P, seed + 1, weights=False)
+    ch = synth.channel_inputs(spec, steps, budget, seed + 1)["channels"]
+    Cn = ch.shape[2]
+    x = to_device_bits(steps["x"], spec.act_dtype).view(P, T, spec.H)
+    lg = torch.from_numpy(np.ascontiguousarray(steps["logits"])).cuda().view(P, T, spec.E)
+    chd = torch.from_numpy(ch).cuda().view(P, T, spec.top_k, Cn)
+    y = torch.empty((T, spec.H), dtype=x.dtype, device="cuda")
+    ws = torch.empty(q.channel_workspace_size(desc, T, spec.top_k, Cn), dtype=torch.uint8, device="cuda")
+
+    def step(s):
+        q.forward_channels(desc, packs[s % L], x[s % P], lg[s % P], T, spec.top_k, chd[s % P], Cn, y, ws)
+
+    step(K - 1)
+    torch.cuda.synchronize()
+    ref = y.clone()
+    bad = []
+
+    def check():
+        if not torch.equal(y.view(torch.int16), ref.view(torch.int16)):
+            bad.append(1)
+    ms, all_ms = graph_time(lambda: [step(s) for s in range(K)], K, trials, check)
+    if bad:
+        raise RuntimeError("graph replay output differs from the eager output")
+    listed = float((ch >= 0).sum()) / P  # listed (slot, channel) entries per call
+    # per listed entry: the gate and up rows of FC1 and one down row, [H] each
+    nbytes = listed * (synth.canonical_matrix_bytes(spec.fc1, 2, spec.H)
+                       + synth.canonical_matrix_bytes(spec.fc2, 1, spec.H))
+    us = ms * 1e3
+    out = {"T": T, "budget": budget, "channels_per_call": listed, "list_len": Cn, "us_per_call": us,
+           "trials_us": [t * 1e3 for t in all_ms], "steps": K, "weight_copies": L,
+           "listed_bytes_per_call": nbytes, "effective_GBps": nbytes / (us * 1e-6) / 1e9}
+    del packs
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(b: "MoeBench", seconds: float):
     """The oracle (double precision, plain loops) on a bounded sample of the
     headline workload's tokens: first on one host core, then on all cores of
@@ -550,6 +611,13 @@ def decode_extras(args, variants) -> dict:
         if t == 1:
             variants[f"{d3.name}_T1"] = {"base_us": r["us_per_layer"], **variant_times(bb, 3)}
         del bb
+    # gathered channels at an 18% budget against the full layer
+    extras["dsv2lite_int4_channels"] = []
+    for t in (1, 8):
+        r = channel_decode_time(d3, t, 0.18, rotate_bytes=rb)
+        r["full_layer_us"] = next(x["us_per_layer"] for x in extras["dsv2lite_int4"] if x["T"] == t)
+        extras["dsv2lite_int4_channels"].append(r)
+        log(f"[bench] channels {json.dumps(r)}")
     # shared logits: every selected expert receives M = T rows (the M-sweep)
     extras["dsv2lite_int4_shared_M_sweep"] = []
     for t in (1, 2, 3, 4, 5, 8, 10, 16, 32):

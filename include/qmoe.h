@@ -74,7 +74,7 @@
 extern "C" {
 #endif
 
-#define QMOE_ABI_VERSION 8
+#define QMOE_ABI_VERSION 9
 
 typedef enum qmoe_status {
   QMOE_OK = 0,
@@ -325,6 +325,56 @@ qmoe_status qmoe_route(int32_t T, int32_t E, int32_t top_k, const float *logits,
  * for FC1 ([E][fc1.rows][H]), 2 for FC2 ([E][H][I]); codes_out int8, device. */
 qmoe_status qmoe_unpack_codes(const qmoe_layer_desc *desc, const void *packed, int32_t which,
                               int8_t *codes_out, void *stream);
+
+/* ---------------------------------------------------- gathered channels --- */
+
+/* Top-k channel selection inside the routed experts (learnaivisually
+ * explainer "MoE channel selection, top-k vs calibrated threshold", the
+ * channel-selection section): for each token and each of its k routed
+ * experts only the listed channels c are computed, channel c being the gate
+ * row 2c and the up row 2c+1 of FC1 and column c of the down projection:
+ *
+ *   y_t = sum_j w_j sum_{c in list(t, j)} silu(g_c(x_t)) u_c(x_t) D_e[:, c]
+ *
+ * with e = the j-th routed expert and w_j its renormalised routing weight
+ * (routing exactly as qmoe_forward).  Choosing the channels (scores,
+ * thresholds, calibration) is the caller's; a channel listed twice counts
+ * twice.
+ *
+ * Supported layers: activation SWIGLU, act_dtype BF16 or F16, fc1 and fc2
+ * qtypes SYM_INT4, SYM_INT2 or TERNARY (no affine formats), no biases,
+ * hidden <= 4096.
+ *
+ * Channel-packed buffer: fc1 codes and scales exactly as for qmoe_prepack
+ * (canonical [E][2I][H*bits/8] rows, [E][2I][H/block] scales), and the down
+ * projection CHANNEL-MAJOR: down_codes [E][I][H*bits/8] (row c holds column c
+ * of the [H][I] down matrix, quantized along H in fc2's qtype, fc2.block
+ * weights per block) and down_scales [E][I][H/fc2.block] in fc2.scale_dtype.
+ * All sources are device pointers; the call copies them into `dst` (256-byte
+ * aligned, >= qmoe_channel_prepacked_size bytes), waits for the stream, and
+ * returns QMOE_ERR_INVALID_ARGUMENT if a TERNARY field holds the value 3. */
+qmoe_status qmoe_channel_prepacked_size(const qmoe_layer_desc *desc, size_t *bytes);
+qmoe_status qmoe_channel_prepack(const qmoe_layer_desc *desc, const void *fc1_codes,
+                                 const void *fc1_scales, const void *down_codes,
+                                 const void *down_scales, void *dst, size_t dst_bytes,
+                                 void *stream);
+
+/* Workspace bytes of qmoe_forward_channels for T tokens, top_k and list
+ * length C (host call). */
+qmoe_status qmoe_channel_workspace_size(const qmoe_layer_desc *desc, int32_t T, int32_t top_k,
+                                        int32_t C, size_t *bytes);
+
+/* x [T][H] (16-byte aligned) and y [T][H] in act_dtype, logits [T][E] fp32,
+ * channels [T][top_k][C] int32 (device): the list of token t's j-th routed
+ * expert, entries outside [0, I) unused (padding).  1 <= C <= 65536.  Each
+ * output is an fp32 sum rounded once (nearest even) to act_dtype; the sum
+ * order is fixed, so repeated calls give identical bits.  ws: device,
+ * 256-byte aligned, >= qmoe_channel_workspace_size.  Asynchronous on
+ * `stream`. */
+qmoe_status qmoe_forward_channels(const qmoe_layer_desc *desc, const void *packed, const void *x,
+                                  const float *logits, int32_t T, int32_t top_k,
+                                  const int32_t *channels, int32_t C, void *y, void *ws,
+                                  size_t ws_bytes, void *stream);
 
 /* --------------------------------------------------------------- dense --- */
 

@@ -81,6 +81,11 @@ _SIGS = {
     "qmoe_linear_unpack_codes": (C.c_int, [C.POINTER(QMatrixDesc), _P, _P, _P]),
     "qmoe_read_probe": (C.c_int, [_P, _SZ, _P, _P]),
     "qmoe_forward_noalloc": (C.c_int, [C.POINTER(LayerDesc), _P, _P, _P, _I32, _I32, _P, _P]),
+    "qmoe_channel_prepacked_size": (C.c_int, [C.POINTER(LayerDesc), C.POINTER(_SZ)]),
+    "qmoe_channel_prepack": (C.c_int, [C.POINTER(LayerDesc)] + [_P] * 5 + [_SZ, _P]),
+    "qmoe_channel_workspace_size": (C.c_int, [C.POINTER(LayerDesc), _I32, _I32, _I32, C.POINTER(_SZ)]),
+    "qmoe_forward_channels": (C.c_int, [C.POINTER(LayerDesc), _P, _P, _P, _I32, _I32, _P, _I32, _P, _P, _SZ,
+                                        _P]),
 }
 
 
@@ -209,6 +214,33 @@ def forward_noalloc(desc, packed, x, logits, T, top_k, y, stream=None):
 
 
 NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def channel_prepacked_size(desc) -> int:
+    n = C.c_size_t()
+    _check(lib().qmoe_channel_prepacked_size(C.byref(desc), C.byref(n)))
+    return n.value
+
+
+def channel_prepack(desc, fc1_codes, fc1_scales, down_codes, down_scales, dst, stream=None):
+    """Channel-packed buffer: FC1 rows as given, the down projection
+    channel-major ([E][I][H*bits/8] codes, [E][I][H/block] scales)."""
+    _check(lib().qmoe_channel_prepack(C.byref(desc), _ptr(fc1_codes), _ptr(fc1_scales), _ptr(down_codes),
+                                      _ptr(down_scales), _ptr(dst), dst.numel() * dst.element_size(),
+                                      _stream(stream)))
+
+
+def channel_workspace_size(desc, T: int, top_k: int, Cn: int) -> int:
+    n = C.c_size_t()
+    _check(lib().qmoe_channel_workspace_size(C.byref(desc), T, top_k, Cn, C.byref(n)))
+    return n.value
+
+
+def forward_channels(desc, packed, x, logits, T, top_k, channels, Cn, y, ws, stream=None):
+    """Gathered-channel forward: ``channels`` [T][top_k][Cn] int32 lists."""
+    _check(lib().qmoe_forward_channels(C.byref(desc), _ptr(packed), _ptr(x), _ptr(logits), T, top_k,
+                                       _ptr(channels), Cn, _ptr(y), _ptr(ws), ws.numel() * ws.element_size(),
+                                       _stream(stream)))
 
 
 def forward_plan(desc, T: int, top_k: int, path: str = "auto", topk_weights: str = "renormalized",

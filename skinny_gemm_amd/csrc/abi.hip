@@ -894,6 +894,157 @@ qmoe_status qmoe_forward_noalloc(const qmoe_layer_desc *desc, const void *packed
                          nullptr);
 }
 
+// ------------------------------------------------------ gathered channels
+namespace {
+constexpr uint64_t kChanMagic = 0x31304843454f4d51ull;  // "QMOECH01"
+constexpr int32_t kChanMaxList = 65536;
+
+qmoe_status check_channel_layer(const qmoe_layer_desc *d) {
+  qmoe_status st = check_layer(d);
+  if (st != QMOE_OK) return st;
+  if (d->activation != QMOE_ACT_SWIGLU)
+    return fail(QMOE_ERR_UNSUPPORTED, "gathered channels: SWIGLU layers only");
+  if (d->act_dtype != QMOE_DTYPE_BF16 && d->act_dtype != QMOE_DTYPE_F16)
+    return fail(QMOE_ERR_UNSUPPORTED, "gathered channels: bf16 or f16 activations only");
+  if (qtype_affine(d->fc1.qtype) || qtype_affine(d->fc2.qtype))
+    return fail(QMOE_ERR_UNSUPPORTED, "gathered channels: symmetric formats only (sym_int4, sym_int2, ternary)");
+  if (d->hidden % d->fc2.block != 0)
+    return fail(QMOE_ERR_INVALID_ARGUMENT, "gathered channels: hidden %d not a multiple of fc2 block %d",
+                d->hidden, d->fc2.block);
+  if (d->hidden > kChanMaxHidden)
+    return fail(QMOE_ERR_UNSUPPORTED, "gathered channels: hidden %d > %d", d->hidden, kChanMaxHidden);
+  const ChanLayout L = ChanLayout::make(*d);
+  if ((int64_t)d->num_experts * d->inter * (L.dn_row_bytes / 4) > (int64_t)UINT32_MAX)
+    return fail(QMOE_ERR_UNSUPPORTED, "gathered channels: down projection beyond 16 GiB");
+  return ok();
+}
+
+struct ChanWs {
+  int64_t partial, end;
+  int groups;
+  static ChanWs make(const qmoe_layer_desc &d, int64_t T, int k, int C) {
+    ChanWs w;
+    Carve c;
+    w.groups = (int)(((int64_t)k * C + kChanGroupEntries - 1) / kChanGroupEntries);
+    w.partial = c.take(T * w.groups * (int64_t)d.hidden * 4);
+    w.end = c.off;
+    return w;
+  }
+};
+}  // namespace
+
+qmoe_status qmoe_channel_prepacked_size(const qmoe_layer_desc *desc, size_t *bytes) {
+  qmoe_status st = check_channel_layer(desc);
+  if (st != QMOE_OK) return st;
+  if (!bytes) return fail(QMOE_ERR_INVALID_ARGUMENT, "null size output");
+  *bytes = (size_t)ChanLayout::make(*desc).total;
+  return ok();
+}
+
+qmoe_status qmoe_channel_prepack(const qmoe_layer_desc *desc, const void *fc1_codes, const void *fc1_scales,
+                                 const void *down_codes, const void *down_scales, void *dst, size_t dst_bytes,
+                                 void *stream) {
+  qmoe_status st = check_channel_layer(desc);
+  if (st != QMOE_OK) return st;
+  if (!fc1_codes || !fc1_scales || !down_codes || !down_scales || !dst)
+    return fail(QMOE_ERR_INVALID_ARGUMENT, "null source or destination pointer");
+  if (!aligned(dst, kAlign)) return fail(QMOE_ERR_INVALID_ARGUMENT, "dst must be 256-byte aligned");
+  if (!aligned(fc1_scales, 2) || !aligned(down_scales, 2))
+    return fail(QMOE_ERR_INVALID_ARGUMENT, "scale arrays must be 2-byte aligned");
+  const ChanLayout L = ChanLayout::make(*desc);
+  if (dst_bytes < (size_t)L.total)
+    return fail(QMOE_ERR_WORKSPACE_TOO_SMALL, "dst holds %zu bytes, %lld needed", dst_bytes, (long long)L.total);
+  const int64_t E = desc->num_experts, H = desc->hidden, I = desc->inter;
+  const int64_t fc1_bytes = E * 2 * I * L.fc1_row_bytes, fc1_sc = E * 2 * I * (H / desc->fc1.block) * 2;
+  const int64_t dn_bytes = E * I * L.dn_row_bytes, dn_sc = E * I * (H / desc->fc2.block) * 2;
+  hipStream_t s = (hipStream_t)stream;
+  uint8_t *d = (uint8_t *)dst;
+  uint8_t header[kHeaderBytes];
+  memset(header, 0, sizeof header);
+  const uint64_t magic = kChanMagic;
+  memcpy(header, &magic, 8);
+  memcpy(header + 8, desc, sizeof(qmoe_layer_desc) < 112 ? sizeof(qmoe_layer_desc) : 112);
+  hipError_t e = hipMemcpyAsync(d, header, kHeaderBytes, hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipMemcpyAsync(d + L.fc1_off, fc1_codes, fc1_bytes, hipMemcpyDeviceToDevice, s);
+  if (e == hipSuccess) e = hipMemcpyAsync(d + L.fc1_sc_off, fc1_scales, fc1_sc, hipMemcpyDeviceToDevice, s);
+  if (e == hipSuccess) e = hipMemcpyAsync(d + L.dn_off, down_codes, dn_bytes, hipMemcpyDeviceToDevice, s);
+  if (e == hipSuccess) e = hipMemcpyAsync(d + L.dn_sc_off, down_scales, dn_sc, hipMemcpyDeviceToDevice, s);
+  if (e != hipSuccess) return hip_status(e, "channel prepack copies");
+  uint32_t *err = (uint32_t *)(d + kErrWordOff);
+  if (desc->fc1.qtype == QMOE_QTYPE_TERNARY) e = launch_count_invalid_ternary(d + L.fc1_off, fc1_bytes, err, s);
+  if (e == hipSuccess && desc->fc2.qtype == QMOE_QTYPE_TERNARY)
+    e = launch_count_invalid_ternary(d + L.dn_off, dn_bytes, err, s);
+  if (e != hipSuccess) return hip_status(e, "channel prepack ternary check");
+  uint32_t nbad = 0;
+  e = hipMemcpyAsync(&nbad, err, 4, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_status(e, "channel prepack error word");
+  if (nbad) return fail(QMOE_ERR_INVALID_ARGUMENT, "%u ternary fields hold the invalid value 3", nbad);
+  return ok();
+}
+
+qmoe_status qmoe_channel_workspace_size(const qmoe_layer_desc *desc, int32_t T, int32_t top_k, int32_t C,
+                                        size_t *bytes) {
+  qmoe_status st = check_channel_layer(desc);
+  if (st == QMOE_OK) st = check_tokens(desc, T, top_k);
+  if (st != QMOE_OK) return st;
+  if (C < 1 || C > kChanMaxList) return fail(QMOE_ERR_INVALID_ARGUMENT, "list length C %d outside [1, %d]", C,
+                                             kChanMaxList);
+  if ((int64_t)T * top_k * C > INT32_MAX) return fail(QMOE_ERR_INVALID_ARGUMENT, "T * top_k * C overflows int32");
+  if (!bytes) return fail(QMOE_ERR_INVALID_ARGUMENT, "null size output");
+  *bytes = (size_t)ChanWs::make(*desc, T, top_k, C).end;
+  return ok();
+}
+
+qmoe_status qmoe_forward_channels(const qmoe_layer_desc *desc, const void *packed, const void *x,
+                                  const float *logits, int32_t T, int32_t top_k, const int32_t *channels,
+                                  int32_t C, void *y, void *ws, size_t ws_bytes, void *stream) {
+  size_t need = 0;
+  qmoe_status st = qmoe_channel_workspace_size(desc, T, top_k, C, &need);
+  if (st != QMOE_OK) return st;
+  if (T == 0) return ok();
+  if (!packed || !x || !logits || !channels || !y || !ws) return fail(QMOE_ERR_INVALID_ARGUMENT, "null pointer");
+  if (!aligned(packed, kAlign) || !aligned(ws, kAlign))
+    return fail(QMOE_ERR_INVALID_ARGUMENT, "packed and ws must be 256-byte aligned");
+  if (!aligned(x, 16) || !aligned(y, 2) || !aligned(logits, 4) || !aligned(channels, 4))
+    return fail(QMOE_ERR_INVALID_ARGUMENT, "x must be 16-byte aligned (y 2, logits and channels 4)");
+  if (ws_bytes < need)
+    return fail(QMOE_ERR_WORKSPACE_TOO_SMALL, "workspace holds %zu bytes, %zu needed", ws_bytes, need);
+  const ChanWs W = ChanWs::make(*desc, T, top_k, C);
+  const ChanLayout L = ChanLayout::make(*desc);
+  const uint8_t *pk = (const uint8_t *)packed;
+  ChanArgs a{};
+  a.fc1 = pk + L.fc1_off;
+  a.fc1_scales = pk + L.fc1_sc_off;
+  a.fc1_row_bytes = L.fc1_row_bytes;
+  a.fc1_bits = qtype_bits(desc->fc1.qtype);
+  a.fc1_block = desc->fc1.block;
+  a.fc1_sf16 = desc->fc1.scale_dtype == QMOE_DTYPE_F16;
+  a.fc1_zp = qtype_zero_point(desc->fc1.qtype);
+  a.dn = pk + L.dn_off;
+  a.dn_scales = pk + L.dn_sc_off;
+  a.dn_row_bytes = L.dn_row_bytes;
+  a.dn_bits = qtype_bits(desc->fc2.qtype);
+  a.dn_block = desc->fc2.block;
+  a.dn_sf16 = desc->fc2.scale_dtype == QMOE_DTYPE_F16;
+  a.dn_zp = qtype_zero_point(desc->fc2.qtype);
+  a.T = T;
+  a.E = desc->num_experts;
+  a.k = top_k;
+  a.C = C;
+  a.I = desc->inter;
+  a.H = desc->hidden;
+  a.groups = W.groups;
+  a.x = (const uint16_t *)x;
+  a.x_f16 = desc->act_dtype == QMOE_DTYPE_F16;
+  a.logits = logits;
+  a.channels = channels;
+  a.partial = (float *)ws;
+  a.y = (uint16_t *)y;
+  hipStream_t s = (hipStream_t)stream;
+  return hip_status(launch_channels(a, s), "gathered channels");
+}
+
 qmoe_status qmoe_route_workspace_size(int32_t T, int32_t E, int32_t top_k, size_t *bytes) {
   if (E < 1 || E > kMaxExperts) return fail(QMOE_ERR_UNSUPPORTED, "E %d outside [1, 256]", E);
   if (T < 0 || top_k < 1 || top_k > E || top_k > kMaxTopK || (int64_t)T * top_k > INT32_MAX)

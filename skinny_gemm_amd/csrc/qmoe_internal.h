@@ -271,6 +271,51 @@ hipError_t launch_read_probe(const void *src, int64_t bytes, uint32_t *sink, int
 // f32 rows -> bf16 hi (RNE of x) and lo (RNE of the remainder) rows.
 hipError_t launch_split_f32(const float *x, int64_t n, uint16_t *hi, uint16_t *lo, hipStream_t s);
 
+// ------------------------------------------------------ gathered channels
+// Channel-packed buffer (per matrix, experts one after another, 256-B
+// aligned sections): FC1 rows [E][2I][H*b/8] in the canonical byte order and
+// their scales [E][2I][H/B]; the channel-major down projection [E][I][H*b/8]
+// and its scales [E][I][H/B].
+struct ChanLayout {
+  int64_t fc1_row_bytes, dn_row_bytes;
+  int64_t fc1_off, fc1_sc_off, dn_off, dn_sc_off, total;
+  static ChanLayout make(const qmoe_layer_desc &d) {
+    ChanLayout L{};
+    const int64_t E = d.num_experts, H = d.hidden, I = d.inter;
+    L.fc1_row_bytes = H * qtype_bits(d.fc1.qtype) / 8;
+    L.dn_row_bytes = H * qtype_bits(d.fc2.qtype) / 8;
+    L.fc1_off = kHeaderBytes;
+    L.fc1_sc_off = L.fc1_off + align_up(E * 2 * I * L.fc1_row_bytes, kAlign);
+    L.dn_off = L.fc1_sc_off + align_up(E * 2 * I * (H / d.fc1.block) * 2, kAlign);
+    L.dn_sc_off = L.dn_off + align_up(E * I * L.dn_row_bytes, kAlign);
+    L.total = L.dn_sc_off + align_up(E * I * (H / d.fc2.block) * 2, kAlign);
+    return L;
+  }
+};
+
+constexpr int kChanGroupEntries = 16;  // list entries per workgroup (partial sums per token: k C / 16)
+constexpr int kChanMaxHidden = 4096;
+
+struct ChanArgs {
+  const uint8_t *fc1, *fc1_scales;
+  int64_t fc1_row_bytes;
+  int fc1_bits, fc1_block, fc1_sf16, fc1_zp;
+  const uint8_t *dn, *dn_scales;
+  int64_t dn_row_bytes;
+  int dn_bits, dn_block, dn_sf16, dn_zp;
+  int T, E, k, C, I, H;
+  int groups;               // ceil(k * C / kChanGroupEntries) list groups per token
+  const uint16_t *x;        // [T][H], 16-byte aligned
+  int x_f16;
+  const float *logits;      // [T][E]
+  const int32_t *channels;  // [T][k][C]
+  float *partial;           // [T][groups][H]
+  uint16_t *y;
+};
+hipError_t launch_channels(const ChanArgs &a, hipStream_t s);
+// Counts ternary fields holding the invalid value 3 in `bytes` bytes.
+hipError_t launch_count_invalid_ternary(const uint8_t *p, int64_t bytes, uint32_t *count, hipStream_t s);
+
 // ----------------------------------------------------------- grouped MFMA
 // Shape of a grouped workgroup tile (4 waves): MI 16-row MFMA row tiles
 // (TM = 16 MI rows), NJ 16-column slices per wave (64 NJ outputs per tile)

@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_abi_version():
-    assert q.abi_version() == 8
+    assert q.abi_version() == 9
 
 
 def _desc(**kw):
@@ -358,3 +358,26 @@ def test_swiglu_parameters_validated_before_launch():
     o = opts(1, 1.702, 1.0, 7.0)
     assert L.qmoe_forward_ex(C.byref(relu), fake, fake, fake, 4, 1, fake, fake, 1 << 30, None, C.byref(o)) == 1
     assert "SWIGLU" in q.last_error()
+
+
+def test_channel_calls_validate_before_launch():
+    """Gathered channels: unsupported layers and bad list lengths fail on the
+    host; sizes follow the layout (FC1 rows and the channel-major down rows)."""
+    ok = q.layer_desc(64, 2048, 1408, "bf16", ("sym_int4", 64, "bf16"), ("sym_int4", 64, "bf16"))
+    n = q.channel_prepacked_size(ok)
+    assert n >= 256 + 64 * 2816 * 1024 + 64 * 2816 * 32 * 2 + 64 * 1408 * 1024 + 64 * 1408 * 32 * 2
+    ws = q.channel_workspace_size(ok, 4, 6, 300)
+    groups = (6 * 300 + 15) // 16
+    assert ws >= 4 * groups * 2048 * 4  # fp32 partial sums per token and group of 16 entries
+    for bad in [q.layer_desc(8, 512, 256, "bf16", ("affine_int2", 64, "f16"), ("sym_int4", 64, "bf16")),
+                q.layer_desc(8, 512, 256, "f32", ("sym_int4", 64, "bf16"), ("sym_int4", 64, "bf16")),
+                q.layer_desc(8, 512, 256, "bf16", ("sym_int4", 64, "bf16"), ("sym_int4", 64, "bf16"), "relu"),
+                q.layer_desc(8, 4160, 256, "bf16", ("sym_int4", 64, "bf16"), ("sym_int4", 64, "bf16"))]:
+        with pytest.raises(q.QmoeError) as ei:
+            q.channel_prepacked_size(bad)
+        assert ei.value.status == 2  # unsupported
+    for Cn in (0, 65537):
+        with pytest.raises(q.QmoeError, match="list length"):
+            q.channel_workspace_size(ok, 1, 6, Cn)
+    st = q.lib().qmoe_forward_channels(C.byref(ok), None, None, None, 1, 6, None, 8, None, None, 0, None)
+    assert st != 0 and "null" in q.last_error()
