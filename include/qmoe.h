@@ -87,7 +87,7 @@ typedef enum qmoe_status {
 typedef enum qmoe_dtype {
   QMOE_DTYPE_BF16 = 0,
   QMOE_DTYPE_F16 = 1,
-  QMOE_DTYPE_F32 = 2 /* activations only, on the GEMV path (see qmoe_layer_desc) */
+  QMOE_DTYPE_F32 = 2 /* activations only (see qmoe_layer_desc) */
 } qmoe_dtype;
 
 typedef enum qmoe_qtype {
@@ -131,13 +131,13 @@ typedef struct qmoe_layer_desc {
   int32_t hidden;      /* H */
   int32_t inter;       /* I */
   int32_t act_dtype;   /* QMOE_DTYPE_BF16, F16 or F32: x and y.  F32 (onnx-genai pull request
-                          1167, Parity: f16/bf16/f32 decode) runs the GEMV path only: above 16
-                          tokens the call runs by itself in GEMV-path row tiles of at most 16
-                          rows (see qmoe_forward_opts.workspace_limit), and a forced grouped
-                          path returns QMOE_ERR_UNSUPPORTED.  x enters the matrix cores as two
-                          bf16 parts, hi = RNE(x) and lo = RNE(x - hi), which carry about 16 of
-                          x's 24 significand bits (relative error below 2^-16 per element);
-                          y is rounded once to f32; no expert biases (QMOE_ERR_UNSUPPORTED) */
+                          1167, Parity: f16/bf16/f32 decode) is NOT fp32 arithmetic on x: on the
+                          GEMV path x enters the matrix cores as two bf16 parts, hi = RNE(x) and
+                          lo = RNE(x - hi), about 16 of x's 24 significand bits (relative error
+                          below 2^-16 per element); on the grouped path as two f16 parts of
+                          x 2^r (r a per-row power of two), about 22 bits.  The products and
+                          sums are fp32; y is rounded once to f32.  No expert biases
+                          (QMOE_ERR_UNSUPPORTED). */
   qmoe_qmatrix_desc fc1;
   qmoe_qmatrix_desc fc2;
   int32_t activation;  /* qmoe_activation */
@@ -186,8 +186,8 @@ typedef struct qmoe_forward_opts {
      partial tiles sized explicitly).  0: no limit.
      The tokens run in consecutive tiles of R rows and a final tile of the
      rest.  R starts at T and is halved (rounding up) while it exceeds the
-     row bound of the path -- 16 rows when the layer has no grouped path (f32
-     activations, or an affine format with more than 80 blocks per row), with
+     row bound of the path -- 16 rows when the layer has no grouped path (an
+     affine format with more than 80 blocks per row), with
      or without a limit, or when a call with a limit is pinned to the GEMV
      path -- then while the workspace of a full tile or of the final tile
      exceeds workspace_limit bytes.  Each tile takes its own path (auto: by
@@ -281,8 +281,8 @@ qmoe_status qmoe_forward(const qmoe_layer_desc *desc, const void *packed, const 
  * diagnostic outputs, stage events, expert biases, routing-weight mode and
  * row tiling (opts may be NULL: the defaults of qmoe_forward).  UNSUPPORTED
  * if path = GEMV and T > 16 without a workspace limit, and if path = GROUPED
- * for a layer the grouped kernels do not take (f32 activations, or an affine
- * format with more than 80 blocks per row). */
+ * for a layer the grouped kernels do not take (an affine format with more
+ * than 80 blocks per row). */
 qmoe_status qmoe_forward_ex(const qmoe_layer_desc *desc, const void *packed, const void *x,
                             const float *logits, int32_t T, int32_t top_k, void *y,
                             void *ws, size_t ws_bytes, void *stream,
@@ -297,7 +297,7 @@ qmoe_status qmoe_forward_ex(const qmoe_layer_desc *desc, const void *packed, con
  * device current.  The call allocates and frees nothing.  A call whose
  * workspace (qmoe_forward_plan's workspace_bytes) exceeds the array returns
  * QMOE_ERR_WORKSPACE_TOO_SMALL before any launch; the layer's own row tiling
- * (f32 and wide-affine layers above 16 tokens) applies as in qmoe_forward.
+ * (wide-affine layers above 16 tokens) applies as in qmoe_forward.
  * All calls on one GPU share the array and it keeps the last call's
  * contents: calls that overlap on one GPU (other streams, other threads)
  * race and must be ordered by the caller.  Everything the kernels read from

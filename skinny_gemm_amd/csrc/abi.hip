@@ -262,11 +262,10 @@ int gemv_in_mode(int act_dtype) {
   return act_dtype == QMOE_DTYPE_F32 ? kGemvInSplitF32 : act_dtype == QMOE_DTYPE_F16 ? 1 : 0;
 }
 
-// Whether the grouped kernels take this layer: 16-bit activations, and affine
-// formats with at most kGroupedMaxAffineBlocks blocks per row (their per-row
-// block sums live in LDS).
+// Whether the grouped kernels take this layer: affine formats need at most
+// kGroupedMaxAffineBlocks blocks per row (their per-row block sums live in
+// LDS).
 bool grouped_supported(const qmoe_layer_desc &d) {
-  if (d.act_dtype == QMOE_DTYPE_F32) return false;
   const MoeLayout L = MoeLayout::make(d);
   return !((L.fc1.affine && L.fc1.nblk > kGroupedMaxAffineBlocks) ||
            (L.fc2.affine && L.fc2.nblk > kGroupedMaxAffineBlocks));
@@ -294,7 +293,6 @@ qmoe_status make_plan(const qmoe_layer_desc &d, int32_t T, int32_t k, int path_r
   p.max_active = (int)std::min<int64_t>(d.num_experts, (int64_t)T * k);
   const bool f32 = d.act_dtype == QMOE_DTYPE_F32;
   if (path == QMOE_PATH_GROUPED) {
-    if (f32) return fail(QMOE_ERR_UNSUPPORTED, "f32 activations run on the GEMV path only");
     if (!grouped_supported(d))
       return fail(QMOE_ERR_UNSUPPORTED, "affine formats on the grouped path need K/block <= %d",
                   kGroupedMaxAffineBlocks);
@@ -710,7 +708,7 @@ qmoe_status qmoe_forward_ex(const qmoe_layer_desc *desc, const void *packed, con
   hipError_t e = hipSuccess;
   const bool f32 = desc->act_dtype == QMOE_DTYPE_F32;
   uint16_t *x_hi = (uint16_t *)(wsb + W.x_hi), *x_lo = (uint16_t *)(wsb + W.x_lo);
-  if (f32) {  // x as bf16 hi + lo rows for FC1
+  if (f32 && p.path == QMOE_PATH_GEMV) {  // x as bf16 hi + lo rows for the FC1 GEMV
     e = begin();
     if (e == hipSuccess) e = launch_split_f32((const float *)x, (int64_t)T * desc->hidden, x_hi, x_lo, s);
     if (e == hipSuccess) e = end();
@@ -730,8 +728,12 @@ qmoe_status qmoe_forward_ex(const qmoe_layer_desc *desc, const void *packed, con
     uint32_t *hmax = (uint32_t *)(wsb + W.hmax);
     uint16_t *xs16 = (uint16_t *)(wsb + W.xs16);
     const float *wsc = (const float *)(pk + L.wsc_off);
+    // fp32 x: the kernel stages each row as f16 hi + lo parts under a power
+    // of two from the row's max |x|; 16-bit x: the rows scaled once to f16
     e = begin();
-    if (e == hipSuccess) e = launch_rowscale(x, T, desc->hidden, desc->act_dtype == QMOE_DTYPE_F16, xsc, xs16, s);
+    if (e == hipSuccess)
+      e = f32 ? launch_rowmax_f32((const float *)x, T, desc->hidden, (uint32_t *)xsc, s)
+              : launch_rowscale(x, T, desc->hidden, desc->act_dtype == QMOE_DTYPE_F16, xsc, xs16, s);
     if (e == hipSuccess) e = end();
     if (e != hipSuccess) return hip_status(e, "rowscale");
     GroupedArgs q1 = grouped_base(L.fc1, pk + L.fc1_off, wsc);
@@ -739,10 +741,16 @@ qmoe_status qmoe_forward_ex(const qmoe_layer_desc *desc, const void *packed, con
     q1.tile_info = ra.r.tile_info;
     q1.token_of = ra.r.token_of;
     q1.in_gather_token = 1;
-    q1.in = xs16;  // the token rows scaled once, staged by copy in every tile
-    q1.in_scaled = 1;
     q1.in_row_elems = desc->hidden;
-    q1.in_rowsc = xsc;
+    if (f32) {
+      q1.in = x;
+      q1.in_f32 = 1;
+      q1.in_rowmax = (const uint32_t *)xsc;
+    } else {
+      q1.in = xs16;  // the token rows scaled once, staged by copy in every tile
+      q1.in_scaled = 1;
+      q1.in_rowsc = xsc;
+    }
     q1.out_f32 = h32;
     q1.out_rowmax = hmax;
     q1.h_dbg = opts ? opts->h_out : nullptr;

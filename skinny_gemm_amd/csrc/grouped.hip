@@ -43,6 +43,25 @@ __global__ __launch_bounds__(256) void rowscale_kernel(const uint16_t *__restric
   }
 }
 
+// One wave per fp32 row: the bits of max |x| (non-negative floats order like
+// their bits), which the grouped kernel turns into the row's power of two
+// when it stages the row as f16 hi + lo parts.
+__global__ __launch_bounds__(256) void rowmax_f32_kernel(const float *__restrict__ x, int rows, int64_t K,
+                                                         uint32_t *__restrict__ rowmax) {
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (r >= rows) return;
+  const float4 *xr = reinterpret_cast<const float4 *>(x + (int64_t)r * K);
+  float m = 0.f;
+  for (int64_t i = lane; i < K / 4; i += 64) {
+    const float4 v = xr[i];
+    m = fmaxf(fmaxf(m, fmaxf(fabsf(v.x), fabsf(v.y))), fmaxf(fabsf(v.z), fabsf(v.w)));
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  if (lane == 0) rowmax[r] = __float_as_uint(m);
+}
+
 // One 1024-thread workgroup per expert: power of two that keeps
 // max |s| * qmax below 2^15.  The prepacked scale section is read in 16-byte
 // vectors (it is 256-B aligned and a multiple of 128 B long; padding
@@ -125,7 +144,8 @@ __global__ __launch_bounds__(256) void wscale_final_kernel(MatLayout L, float *_
 }
 
 hipError_t launch_grouped(const GroupedArgs &a, int epilogue, int grid_tiles, hipStream_t s) {
-  const int tw = 64 * grouped_shape(qtype_affine(a.qtype), a.tile_rows, a.in_f32 != 0).nj;  // the kernel's tile width
+  // the kernel's tile width (FC2 with its fp32 per-slot output has a shape of its own)
+  const int tw = 64 * grouped_shape(qtype_affine(a.qtype), a.tile_rows, epilogue == kGEpiStoreF32).nj;
   const int ntn = (int)((a.N + tw - 1) / tw);
   const int grid = grid_tiles * ntn;
   if (grid == 0) return hipSuccess;
@@ -139,6 +159,11 @@ hipError_t launch_rowscale(const void *x, int rows, int64_t K, int in_f16, float
   if (rows <= 0) return hipSuccess;
   return qlaunch(rowscale_kernel, dim3((rows + 3) / 4), dim3(256), 0, s, (const uint16_t *)x, rows, K, in_f16,
                  rowsc, xs);
+}
+
+hipError_t launch_rowmax_f32(const float *x, int rows, int64_t K, uint32_t *rowmax, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  return qlaunch(rowmax_f32_kernel, dim3((rows + 3) / 4), dim3(256), 0, s, x, rows, K, rowmax);
 }
 
 hipError_t launch_wscale(const MatLayout &L, int E, const uint8_t *mat, float *wsc, hipStream_t s) {

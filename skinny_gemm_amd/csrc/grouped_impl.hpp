@@ -492,9 +492,13 @@ template <int QT, int EPI, bool MAIN, bool SPLIT>
 hipError_t launch_grouped_split(const GroupedArgs &a, int grid, hipStream_t s) {
   constexpr GroupedShape S16 = MAIN ? grouped_shape_main(false) : grouped_shape_64(false);
   constexpr GroupedShape S32 = MAIN ? grouped_shape_main(true) : grouped_shape_64(true);
-  // the inputs each epilogue is used with: FC1 pre-scaled token rows, FC2
-  // the fp32 SwiGLU output, the dense matrix 16-bit rows
+  // the inputs each epilogue is used with: FC1 pre-scaled token rows (or
+  // fp32 token rows, staged as hi + lo parts), FC2 the fp32 SwiGLU output,
+  // the dense matrix 16-bit rows
   if constexpr (EPI == kGEpiSwiGLU) {
+    if (a.in_f32)
+      return qlaunch(grouped_kernel<QT, EPI, kInF32, S16.mi, S16.nj, S16.kt, SPLIT>, dim3(grid), dim3(256), 0, s,
+                     a);
     if (!a.in_scaled) return hipErrorInvalidConfiguration;
     return qlaunch(grouped_kernel<QT, EPI, kInScaled, S16.mi, S16.nj, S16.kt, SPLIT>, dim3(grid), dim3(256), 0, s,
                    a);

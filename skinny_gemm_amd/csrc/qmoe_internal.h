@@ -346,8 +346,10 @@ constexpr int kTileM = 64;  // rows per grouped tile with an affine matrix
 struct GroupedShape {
   int mi, nj, kt;
 };
-// in_f32: the fp32 FC2 input, staged as f16 hi + lo parts.  The 64-row shape
-// (affine formats, and a non-affine matrix whose layer has an affine one):
+// in_f32: the shape of FC2 (fp32 input staged as f16 hi + lo parts, fp32
+// per-slot output); FC1 and the dense matrix take the other shape whatever
+// their input.  The 64-row shape (affine formats, and a non-affine matrix
+// whose layer has an affine one):
 __host__ __device__ constexpr GroupedShape grouped_shape_64(bool in_f32) {
   return GroupedShape{4, in_f32 ? 4 : 2, in_f32 ? 64 : 128};
 }
@@ -402,6 +404,8 @@ hipError_t launch_grouped(const GroupedArgs &a, int epilogue, int grid_tiles, hi
 // scaled rows as f16 (exact: x * 2^r of a bf16/f16 x below 2^14).
 hipError_t launch_rowscale(const void *x, int rows, int64_t K, int in_f16, float *rowsc, uint16_t *xs,
                            hipStream_t s);
+// Bits of max |x| per fp32 row (K a multiple of 4, rows 16-B aligned).
+hipError_t launch_rowmax_f32(const float *x, int rows, int64_t K, uint32_t *rowmax, hipStream_t s);
 hipError_t launch_wscale(const MatLayout &L, int E, const uint8_t *mat, float *wsc, hipStream_t s);
 
 // ---------------------------------------------------------------- launches

@@ -261,8 +261,9 @@ def test_prepack_scales_validation():
 
 
 def test_plan_f32_activations():
-    """f32 activations: a split pass first, y from the combine (also for
-    top-1), GEMV path only."""
+    """f32 activations: on the GEMV path a split pass first and y from the
+    combine (also for top-1); above 16 tokens the grouped path, whose FC1
+    stages the fp32 rows itself after a row-maximum pass."""
     d = _desc(act="f32")
     assert q.forward_plan(d, 1, 6)["kernels"] == ["split_x", "route_fc1_swiglu", "gemv_fc2", "combine"]
     assert q.forward_plan(d, 8, 6)["kernels"] == ["split_x", "route", "gemv_fc1_swiglu", "gemv_fc2", "combine"]
@@ -270,11 +271,10 @@ def test_plan_f32_activations():
     assert p1["kernels"] == ["split_x", "route_fc1_swiglu", "gemv_fc2", "combine"] and p1["num_launches"] == 4
     b = q.forward_plan(_desc(), 4, 6)["workspace_bytes"]
     assert q.forward_plan(d, 4, 6)["workspace_bytes"] == b + 2 * (4 * 2048 * 2)   # x hi + lo rows
-    with pytest.raises(q.QmoeError) as ei:
-        q.forward_plan(d, 4, 6, "grouped")
-    assert ei.value.status == 2
-    p17 = q.forward_plan(d, 17, 6)          # no grouped path: GEMV row tiles by itself
-    assert (p17["row_tile"], p17["num_tiles"], p17["path"]) == (9, 2, 1)
+    g4 = q.forward_plan(d, 4, 6, "grouped")
+    assert g4["kernels"] == ["route", "rowscale", "grouped_fc1_swiglu", "grouped_fc2", "combine"]
+    p17 = q.forward_plan(d, 17, 6)          # the grouped path in one pass
+    assert (p17["num_tiles"], p17["path"]) == (1, 2)
     L = q.lib()
     fake = C.c_void_p(0x100000)
     o = q.ForwardOpts(0, 0, None, None, None, None, None, 0, 0, fake, None, 0, 0, 0)   # expert bias
@@ -302,15 +302,14 @@ def test_relu_layer_descriptor_and_plan():
 
 
 def test_row_tiling_reaches_the_gemv_path():
-    """A layer the grouped kernels cannot take (f32 activations, or an affine
-    format with more than 80 blocks per row) runs above 16 rows in GEMV-path
-    tiles of at most 16 rows, with or without a workspace limit; a call pinned
-    to the GEMV path does so only under a workspace limit."""
-    d = _desc(act="f32")
-    for lim in (0, 1 << 40):
-        p = q.forward_plan(d, 40, 6, workspace_limit=lim)
-        assert (p["row_tile"], p["num_tiles"], p["path"]) == (10, 4, 1)
+    """A layer the grouped kernels cannot take (an affine format with more
+    than 80 blocks per row) runs above 16 rows in GEMV-path tiles of at most
+    16 rows, with or without a workspace limit; a call pinned to the GEMV path
+    does so only under a workspace limit."""
     aff = q.layer_desc(8, 6144, 256, "bf16", ("affine_int2", 64, "f16"), ("affine_int2", 64, "f16"))
+    for lim in (0, 1 << 40):
+        p = q.forward_plan(aff, 40, 2, workspace_limit=lim)
+        assert (p["row_tile"], p["num_tiles"], p["path"]) == (10, 4, 1)
     pa = q.forward_plan(aff, 100, 2)
     assert pa["path"] == 1 and pa["row_tile"] <= 16 and pa["num_tiles"] * pa["row_tile"] >= 100
     with pytest.raises(q.QmoeError) as ei:

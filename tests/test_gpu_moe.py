@@ -616,6 +616,36 @@ def test_f32_activations_sweep(cfg, T):
     run_case(custom_moe_spec(**{**cfg, "act_dtype": "f32"}), T, 60 + T)
 
 
+@pytest.mark.parametrize("cfg", [SWEEP[1], SWEEP[3], SWEEP[4], SWEEP[6]],
+                         ids=["int2-int4", "affine", "affine-int4-b128", "int2-ternary-f16scales"])
+@pytest.mark.parametrize("T", [33, 300])
+def test_f32_activations_grouped(cfg, T):
+    """f32 x on the grouped path: FC1 stages each fp32 row as f16 hi + lo
+    parts under the row's power of two; T = 300 gives every expert several
+    row tiles and a partial last one."""
+    run_case(custom_moe_spec(**{**cfg, "act_dtype": "f32"}), T, 160 + T, path="grouped")
+
+
+def test_f32_activations_grouped_dsv2lite_and_edges():
+    """The decode workload's layer at 64 tokens with f32 x, and rows with one
+    large element among tiny ones, an all-zero row and values near 1e-6."""
+    run_case(_f32(synth.MOE_WORKLOADS["dsv2lite_int4"]), 64, 5, path="grouped")
+
+    def edit(x, spec):
+        x[0, :] = 1e-3 * x[0, :]
+        x[0, 7] = 3.0e4
+        x[1, :] = 0.0
+        x[2, :] = 1e-6 * x[2, :]
+        return x
+    run_case(custom_moe_spec(E=4, H=256, I=128, top_k=2, fc1="sym_int4", act_dtype="f32"), 40, 6, path="grouped",
+             x_edit=edit)
+
+
+def test_relu_f32_activations_grouped():
+    run_case(custom_moe_spec(E=4, H=128, I=128, top_k=2, activation="relu", act_dtype="f32"), 33, 91,
+             path="grouped")
+
+
 def test_f32_activations_unnormalised_weights_and_tiling():
     """f32 with unnormalised top-k weights, then in row tiles of 4 tokens."""
     spec = custom_moe_spec(E=8, H=256, I=128, top_k=3, fc1="sym_int4", act_dtype="f32")
@@ -675,11 +705,11 @@ def test_top16_of_256_experts():
 
 
 def test_f32_activations_40_tokens_in_gemv_tiles():
-    """40 tokens with f32 activations: the grouped path has no f32 input, so a
-    workspace limit runs them as four GEMV-path tiles of 10 rows."""
+    """40 tokens with f32 activations pinned to the GEMV path: a workspace
+    limit runs them as four GEMV-path tiles of 10 rows."""
     spec = custom_moe_spec(E=8, H=256, I=128, top_k=2, fc1="sym_int4", act_dtype="f32")
     inp = synth.moe_inputs(spec, 40, 73)
-    _, _, _, y, dbg = _tiled_run(spec, inp, 40, 1 << 40)
+    _, _, _, y, dbg = _tiled_run(spec, inp, 40, 1 << 40, path="gemv")
     ref = oracle.moe(inp)
     assert np.array_equal(dbg["ids"].cpu().numpy(), oracle.route(inp["logits"], 2)["ids"])
     res = compare(y, ref["y"], ref["y64"], "f32")
