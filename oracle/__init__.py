@@ -28,9 +28,9 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "liboracle.so")
 
-FMT = {"sym_int4": 0, "sym_int2": 1, "ternary": 2, "affine_int2": 3, "affine_int4": 4}
+FMT = {"sym_int4": 0, "sym_int2": 1, "ternary": 2, "affine_int2": 3, "affine_int4": 4, "ternary_b3": 5}
 DT = {"bf16": 0, "f16": 1, "f32": 2}
-BITS = {"sym_int4": 4, "sym_int2": 2, "ternary": 2, "affine_int2": 2, "affine_int4": 4}
+BITS = {"sym_int4": 4, "sym_int2": 2, "ternary": 2, "affine_int2": 2, "affine_int4": 4}  # fixed-width formats
 
 _lib = None
 
@@ -52,6 +52,10 @@ def lib():
         L.orc_doubles_to_half.argtypes = [P, i64, C.c_int, P]
         L.orc_unpack_codes.restype = i64
         L.orc_unpack_codes.argtypes = [C.c_int, P, i64, i64, P]
+        L.orc_unpack_codes_b.restype = i64
+        L.orc_unpack_codes_b.argtypes = [C.c_int, C.c_int, P, i64, i64, P]
+        L.orc_row_bytes.restype = i64
+        L.orc_row_bytes.argtypes = [C.c_int, C.c_int, i64]
         L.orc_dequant.argtypes = [C.c_int, C.c_int, C.c_int, P, P, P, i64, i64, P]
         L.orc_route.argtypes = [C.c_int, C.c_int, C.c_int, C.c_int, P, P, P, P, P, P]
         L.orc_silu.restype = C.c_double
@@ -109,12 +113,18 @@ def swiglu(g: float, u: float, alpha: float = 1.0, beta: float = 0.0, limit: flo
 
 
 # ------------------------------------------------------------------ codec
-def unpack_codes(fmt: str, packed, rows: int, K: int):
-    """Integer codes [rows][K] (int8) and the number of invalid fields."""
+def row_bytes(fmt: str, block: int, K: int) -> int:
+    """Bytes of one packed row (base-3: ceil(block/5) bytes per block)."""
+    return int(lib().orc_row_bytes(FMT[fmt], block, K))
+
+
+def unpack_codes(fmt: str, packed, rows: int, K: int, block: int = 128):
+    """Integer codes [rows][K] (int8) and the number of invalid fields (for
+    base-3 rows, of weights in invalid bytes; the block matters only there)."""
     pk = _c(packed, np.uint8)
-    assert pk.size == rows * K * BITS[fmt] // 8
+    assert pk.size == rows * row_bytes(fmt, block, K)
     out = np.empty((rows, K), dtype=np.int8)
-    nbad = lib().orc_unpack_codes(FMT[fmt], _p(pk), rows, K, _p(out))
+    nbad = lib().orc_unpack_codes_b(FMT[fmt], block, _p(pk), rows, K, _p(out))
     return out, int(nbad)
 
 

@@ -36,13 +36,22 @@
  *   silu(g) = g / (1 + exp(-g)); top-k ties go to the lower expert index and
  *   the ids are ordered by descending logit; the routing weights are the
  *   softmax of the k selected logits; every routed slot is computed.
+ *
+ * Base-3 ternary (the denser ternary storage of about 1.6 bits per weight in
+ * MLX issue 3852's closing remarks; the ternary sketch blocks of about 30
+ * bytes per 128 weights in the channel-selection explainer): each block of
+ * B weights takes ceil(B/5) bytes; weight i of the block is base-3 digit
+ * i mod 5 (least significant first) of byte i / 5, q = digit - 1, and a byte
+ * whose value needs more digits than it holds (>= 243, or >= 3^(B mod 5)
+ * for a block's last partial byte) is invalid.
  */
 #include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
 
-enum { ORC_SYM_INT4 = 0, ORC_SYM_INT2 = 1, ORC_TERNARY = 2, ORC_AFFINE_INT2 = 3, ORC_AFFINE_INT4 = 4 };
+enum { ORC_SYM_INT4 = 0, ORC_SYM_INT2 = 1, ORC_TERNARY = 2, ORC_AFFINE_INT2 = 3, ORC_AFFINE_INT4 = 4,
+       ORC_TERNARY_B3 = 5 };
 enum { ORC_BF16 = 0, ORC_F16 = 1, ORC_F32 = 2 };
 
 /* ---------- 16-bit floating point, from the IEEE 754 definitions ---------- */
@@ -117,6 +126,12 @@ int orc_bits(int fmt) {
   return (fmt == ORC_SYM_INT4 || fmt == ORC_AFFINE_INT4) ? 4 : 2;
 }
 
+/* Bytes of one packed row of K weights in blocks of `block`. */
+int64_t orc_row_bytes(int fmt, int block, int64_t K) {
+  if (fmt == ORC_TERNARY_B3) return (K / block) * ((block + 4) / 5);
+  return K * orc_bits(fmt) / 8;
+}
+
 /* Stored field u of weight k in a packed row: fields run LSB-first along K. */
 static int orc_field(const uint8_t *row, int bits, int64_t k) {
   int64_t bit = k * bits;
@@ -137,28 +152,56 @@ static int orc_code(int fmt, int u, int *bad) {
 
 static int orc_is_affine(int fmt) { return fmt == ORC_AFFINE_INT2 || fmt == ORC_AFFINE_INT4; }
 
-/* Integer codes of a [rows][K] matrix; returns the number of invalid fields. */
-int64_t orc_unpack_codes(int fmt, const uint8_t *packed, int64_t rows, int64_t K, int8_t *out) {
-  const int bits = orc_bits(fmt);
-  const int64_t row_bytes = K * bits / 8;
+/* Base-3 digit d (0 = least significant) of byte v, by repeated division. */
+static int orc_b3_digit(int v, int d) {
+  for (int i = 0; i < d; ++i) v /= 3;
+  return v % 3;
+}
+
+/* Integer code of weight k of a packed row (any format).  *bad is set for an
+ * invalid field or byte. */
+static int orc_code_at(int fmt, int block, const uint8_t *row, int64_t k, int *bad) {
+  if (fmt == ORC_TERNARY_B3) {
+    const int64_t per = (block + 4) / 5;          /* bytes per block */
+    const int64_t b = k / block, i = k % block;   /* block, position in block */
+    const int j = (int)(i / 5);                   /* byte within the block */
+    const int held = (j == per - 1 && block % 5) ? block % 5 : 5;
+    int limit = 1;
+    for (int h = 0; h < held; ++h) limit *= 3;
+    const int v = row[b * per + j];
+    if (v >= limit) { *bad = 1; return 0; }
+    return orc_b3_digit(v, (int)(i % 5)) - 1;
+  }
+  return orc_code(fmt, orc_field(row, orc_bits(fmt), k), bad);
+}
+
+/* Integer codes of a [rows][K] matrix with blocks of `block` (the block only
+ * matters for base-3 rows); returns the number of invalid fields (or, for
+ * base-3, of weights in invalid bytes). */
+int64_t orc_unpack_codes_b(int fmt, int block, const uint8_t *packed, int64_t rows, int64_t K, int8_t *out) {
+  const int64_t row_bytes = orc_row_bytes(fmt, block, K);
   int64_t nbad = 0;
   for (int64_t n = 0; n < rows; ++n) {
     for (int64_t k = 0; k < K; ++k) {
       int bad = 0;
-      out[n * K + k] = (int8_t)orc_code(fmt, orc_field(packed + n * row_bytes, bits, k), &bad);
+      out[n * K + k] = (int8_t)orc_code_at(fmt, block, packed + n * row_bytes, k, &bad);
       nbad += bad;
     }
   }
   return nbad;
 }
 
+/* Integer codes of a [rows][K] matrix; returns the number of invalid fields. */
+int64_t orc_unpack_codes(int fmt, const uint8_t *packed, int64_t rows, int64_t K, int8_t *out) {
+  return orc_unpack_codes_b(fmt, 128, packed, rows, K, out);
+}
+
 /* One dequantized row: w[k] = s*q (+ b for affine), s and b of block k/B. */
 static void orc_dequant_row(int fmt, int block, int sdtype, const uint8_t *codes_row,
                             const uint16_t *scales_row, const uint16_t *biases_row,
                             int64_t K, double *w, int *bad) {
-  const int bits = orc_bits(fmt);
   for (int64_t k = 0; k < K; ++k) {
-    int q = orc_code(fmt, orc_field(codes_row, bits, k), bad);
+    int q = orc_code_at(fmt, block, codes_row, k, bad);
     double s = orc_half_to_double(scales_row[k / block], sdtype);
     double v = s * (double)q;
     if (orc_is_affine(fmt)) v += orc_half_to_double(biases_row[k / block], sdtype);
@@ -168,7 +211,7 @@ static void orc_dequant_row(int fmt, int block, int sdtype, const uint8_t *codes
 
 void orc_dequant(int fmt, int block, int sdtype, const uint8_t *codes, const uint16_t *scales,
                  const uint16_t *biases, int64_t rows, int64_t K, double *W) {
-  const int64_t row_bytes = K * orc_bits(fmt) / 8, nb = K / block;
+  const int64_t row_bytes = orc_row_bytes(fmt, block, K), nb = K / block;
   int bad = 0;
   for (int64_t n = 0; n < rows; ++n)
     orc_dequant_row(fmt, block, sdtype, codes + n * row_bytes, scales + n * nb,
@@ -252,7 +295,7 @@ typedef struct {
 /* out[n] = sum_k W[e][n][k] * v[k] for n in [0, N). */
 static void orc_matvec(const orc_mat *m, int64_t e, int64_t N, int64_t K, const double *v,
                        double *out, double *wrow, int *bad) {
-  const int64_t row_bytes = K * orc_bits(m->fmt) / 8, nb = K / m->block;
+  const int64_t row_bytes = orc_row_bytes(m->fmt, m->block, K), nb = K / m->block;
   for (int64_t n = 0; n < N; ++n) {
     const int64_t r = e * N + n;
     orc_dequant_row(m->fmt, m->block, m->sdtype, m->codes + r * row_bytes, m->scales + r * nb,
@@ -352,9 +395,8 @@ int orc_moe(int E, int H, int I, int k, int act_dtype,
 static void orc_dequant_row_f32(int fmt, int block, int sdtype, const uint8_t *codes_row,
                                 const uint16_t *scales_row, const uint16_t *biases_row,
                                 int64_t K, float *w, int *bad) {
-  const int bits = orc_bits(fmt);
   for (int64_t k = 0; k < K; ++k) {
-    int q = orc_code(fmt, orc_field(codes_row, bits, k), bad);
+    int q = orc_code_at(fmt, block, codes_row, k, bad);
     float s = (float)orc_half_to_double(scales_row[k / block], sdtype);
     float v = s * (float)q;
     if (orc_is_affine(fmt)) v = v + (float)orc_half_to_double(biases_row[k / block], sdtype);
@@ -364,7 +406,7 @@ static void orc_dequant_row_f32(int fmt, int block, int sdtype, const uint8_t *c
 
 static void orc_matvec_f32(const orc_mat *m, int64_t e, int64_t N, int64_t K, const float *v,
                            float *out, float *wrow, int *bad) {
-  const int64_t row_bytes = K * orc_bits(m->fmt) / 8, nb = K / m->block;
+  const int64_t row_bytes = orc_row_bytes(m->fmt, m->block, K), nb = K / m->block;
   for (int64_t n = 0; n < N; ++n) {
     const int64_t r = e * N + n;
     orc_dequant_row_f32(m->fmt, m->block, m->sdtype, m->codes + r * row_bytes, m->scales + r * nb,
@@ -457,8 +499,8 @@ int orc_moe_channels(int E, int H, int I, int k, int act_dtype,
   double *xv = (double *)malloc(sizeof(double) * (size_t)H);
   double *wrow = (double *)malloc(sizeof(double) * (size_t)H);
   double *o = (double *)malloc(sizeof(double) * (size_t)H);
-  const int64_t row1 = (int64_t)H * orc_bits(fc1_fmt) / 8, nb1 = H / fc1_block;
-  const int64_t rowd = (int64_t)H * orc_bits(dn_fmt) / 8, nbd = H / dn_block;
+  const int64_t row1 = orc_row_bytes(fc1_fmt, fc1_block, H), nb1 = H / fc1_block;
+  const int64_t rowd = orc_row_bytes(dn_fmt, dn_block, H), nbd = H / dn_block;
   int bad = 0;
   orc_route(T, E, k, 1, logits, ids, wts, counts, offsets, rows);
   for (int t = 0; t < T; ++t) {
@@ -510,7 +552,7 @@ void orc_linear(int fmt, int block, int sdtype, const uint8_t *codes, const uint
                 const uint16_t *biases, int64_t N, int64_t K, const uint16_t *x, int x_dtype, int M,
                 int64_t n0, int64_t n1, double *y64, uint16_t *y16) {
   (void)N;
-  const int64_t row_bytes = K * orc_bits(fmt) / 8, nb = K / block, W = n1 - n0;
+  const int64_t row_bytes = orc_row_bytes(fmt, block, K), nb = K / block, W = n1 - n0;
   double *wrow = (double *)malloc(sizeof(double) * (size_t)K);
   double *xv = (double *)malloc(sizeof(double) * (size_t)K * (size_t)(M > 0 ? M : 1));
   for (int m = 0; m < M; ++m)

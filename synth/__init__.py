@@ -27,6 +27,8 @@ from .rng import (  # noqa: F401
     random_bytes,
     codes_uniform,
     codes_ternary,
+    ternary_digits,
+    pack_base3,
 )
 from .workloads import (  # noqa: F401
     MatFmt,

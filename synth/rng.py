@@ -103,6 +103,37 @@ def codes_uniform(key: Key, nbytes: int) -> np.ndarray:
     return random_bytes(key, nbytes)
 
 
+def ternary_digits(key: Key, nfields: int) -> np.ndarray:
+    """Ternary stored digits u in {0, 1, 2} (q = u - 1) with the distribution
+    of codes_ternary, one per weight, from the same random bits: the 2-bit
+    and base-3 forms drawn with one key hold the same weights."""
+    assert nfields % 4 == 0
+    r = random_bytes(key, nfields // 4)
+    lut = np.array([1, 1, 0, 2], dtype=np.uint8)
+    out = np.empty(nfields, dtype=np.uint8)
+    for f in range(4):
+        out[f::4] = lut[(r >> (2 * f)) & 3]
+    return out
+
+
+def pack_base3(digits: np.ndarray, block: int) -> np.ndarray:
+    """Rows of digits [..., K] in {0, 1, 2} -> base-3 storage [..., K/block *
+    ceil(block/5)]: byte j of a block holds the block's digits 5j..5j+4 as
+    sum d_i 3^i (least significant first); a block's last byte holds the
+    block % 5 remaining digits."""
+    d = np.asarray(digits, dtype=np.int64)
+    K = d.shape[-1]
+    assert K % block == 0
+    per = (block + 4) // 5
+    pad = per * 5 - block
+    blocks = d.reshape(*d.shape[:-1], K // block, block)
+    if pad:
+        blocks = np.concatenate([blocks, np.zeros((*blocks.shape[:-1], pad), dtype=np.int64)], axis=-1)
+    g = blocks.reshape(*blocks.shape[:-1], per, 5)
+    v = (g * np.array([1, 3, 9, 27, 81], dtype=np.int64)).sum(-1)
+    return v.astype(np.uint8).reshape(*d.shape[:-1], (K // block) * per)
+
+
 def codes_ternary(key: Key, nfields: int) -> np.ndarray:
     """Packed 2-bit ternary fields with P(q=0)=1/2 and P(q=-1)=P(q=+1)=1/4.
 

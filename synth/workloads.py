@@ -34,7 +34,8 @@ from typing import Optional
 
 import numpy as np
 
-from .rng import Key, normals, f32_to_bf16_bits, f32_to_f16_bits, codes_uniform, codes_ternary, raw_u64
+from .rng import (Key, normals, f32_to_bf16_bits, f32_to_f16_bits, codes_uniform, codes_ternary, raw_u64,
+                  ternary_digits, pack_base3)
 
 # name -> (bits per stored field, has a per-block bias)
 FORMATS = {
@@ -43,6 +44,7 @@ FORMATS = {
     "ternary": (2, False),
     "affine_int2": (2, True),
     "affine_int4": (4, True),
+    "ternary_b3": (0, False),  # base-3: five weights per byte, ceil(block/5) bytes per block
 }
 
 DTYPES = ("bf16", "f16")
@@ -61,6 +63,12 @@ class MatFmt:
     @property
     def affine(self) -> bool:
         return FORMATS[self.fmt][1]
+
+    def row_bytes(self, K: int) -> int:
+        """Bytes of one packed row of K weights."""
+        if self.fmt == "ternary_b3":
+            return (K // self.block) * ((self.block + 4) // 5)
+        return K * self.bits // 8
 
 
 @dataclass(frozen=True)
@@ -133,20 +141,22 @@ def _to_bits(v64: np.ndarray, dtype: str) -> np.ndarray:
 def canonical_matrix_bytes(fmt: MatFmt, N: int, K: int) -> int:
     """Bytes of one matrix in the canonical format: codes + scales (+ biases)."""
     nb = K // fmt.block
-    per_row = K * fmt.bits // 8 + nb * 2 * (2 if fmt.affine else 1)
+    per_row = fmt.row_bytes(K) + nb * 2 * (2 if fmt.affine else 1)
     return N * per_row
 
 
 def _matrix(workload: str, tag: str, seed: int, fmt: MatFmt, E: int, N: int, K: int,
             scale_sigma: float, bias_sigma: float):
-    assert K % fmt.block == 0 and (K * fmt.bits) % 8 == 0
+    assert K % fmt.block == 0 and (fmt.fmt == "ternary_b3" or (K * fmt.bits) % 8 == 0)
     kc = Key(seed, workload, tag + ".codes")
     nfields = E * N * K
     if fmt.fmt == "ternary":
         codes = codes_ternary(kc, nfields)
+    elif fmt.fmt == "ternary_b3":
+        codes = pack_base3(ternary_digits(kc, nfields).reshape(E * N, K), fmt.block)
     else:
         codes = codes_uniform(kc, nfields * fmt.bits // 8)
-    codes = codes.reshape(E, N, K * fmt.bits // 8)
+    codes = codes.reshape(E, N, fmt.row_bytes(K))
     nb = K // fmt.block
     s = np.abs(scale_sigma * normals(Key(seed, workload, tag + ".scales"), E * N * nb))
     scales = _to_bits(s, fmt.scale_dtype).reshape(E, N, nb)

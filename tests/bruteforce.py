@@ -35,8 +35,25 @@ def half_bits_to_f64(bits: np.ndarray, dtype: str) -> np.ndarray:
     return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
 
 
+# base-3 digits of every byte value, least significant first, from numpy's
+# base-3 string of the value (values of more than five digits stay invalid)
+_B3 = np.array([[int(c) for c in np.base_repr(v, 3).zfill(5)[::-1][:5]] for v in range(243)], dtype=np.int64)
+
+
+def b3_fields(packed: np.ndarray, block: int, K: int) -> np.ndarray:
+    """Stored digits u of base-3 rows [..., K/block * ceil(block/5)] -> [..., K]."""
+    per = (block + 4) // 5
+    b = np.asarray(packed, dtype=np.int64).reshape(*packed.shape[:-1], K // block, per)
+    assert (b < 243).all()
+    d = _B3[b].reshape(*packed.shape[:-1], K // block, per * 5)[..., :block]
+    return d.reshape(*packed.shape[:-1], K)
+
+
 def dequant(fmt: str, block: int, sdtype: str, codes, scales, biases, K: int) -> np.ndarray:
-    q = fields(np.asarray(codes, dtype=np.uint8), BITS[fmt], K) - OFFSET[fmt]
+    if fmt == "ternary_b3":
+        q = b3_fields(np.asarray(codes, dtype=np.uint8), block, K) - 1
+    else:
+        q = fields(np.asarray(codes, dtype=np.uint8), BITS[fmt], K) - OFFSET[fmt]
     s = np.repeat(half_bits_to_f64(scales, sdtype), block, axis=-1)
     w = s * q
     if biases is not None:

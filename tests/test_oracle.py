@@ -532,3 +532,81 @@ def test_channels_vs_dense_bruteforce(oracle_lib, budget):
                        rtol=1e-10, atol=1e-12 * np.abs(ref).max())
     zero = oracle_lib.moe_channels(inp, np.full_like(ch, -1))
     assert np.all(zero["y64"] == 0.0)
+
+
+# ------------------------------------------------------------ base-3 ternary
+def test_base3_every_byte_value_decodes(oracle_lib):
+    """All 243 valid bytes: with blocks of 5 weights (one byte per block), the
+    codes are the byte's base-3 digits, least significant first, minus 1,
+    against numpy's base-3 string of the value."""
+    v = np.arange(243, dtype=np.uint8)
+    codes, nbad = oracle_lib.unpack_codes("ternary_b3", v[None, :], 1, 5 * 243, block=5)
+    assert nbad == 0
+    want = np.array([[int(c) for c in np.base_repr(int(b), 3).zfill(5)[::-1]] for b in v]).reshape(-1) - 1
+    assert np.array_equal(codes[0].astype(np.int64), want)
+
+
+@pytest.mark.parametrize("block,limit_last", [(64, 81), (128, 27)])
+def test_base3_invalid_bytes_are_flagged(oracle_lib, block, limit_last):
+    """A full byte >= 243 and a block's last partial byte >= 3^(block mod 5)
+    are invalid: each flags the weights it holds; the largest valid values
+    are accepted."""
+    per = (block + 4) // 5
+    row = np.zeros((1, 2 * per), dtype=np.uint8)
+    row[0, 0] = 242
+    row[0, per - 1] = limit_last - 1
+    assert oracle_lib.unpack_codes("ternary_b3", row, 1, 2 * block, block=block)[1] == 0
+    bad = row.copy()
+    bad[0, 3] = 243
+    assert oracle_lib.unpack_codes("ternary_b3", bad, 1, 2 * block, block=block)[1] == 5
+    bad = row.copy()
+    bad[0, 2 * per - 1] = limit_last
+    assert oracle_lib.unpack_codes("ternary_b3", bad, 1, 2 * block, block=block)[1] == block % 5
+    spec = custom_moe_spec(E=1, H=block, I=block, top_k=1, fc1="ternary_b3", block1=block, fc2="ternary")
+    inp = synth.moe_inputs(spec, T=1, seed=1)
+    inp["fc1_codes"] = inp["fc1_codes"].copy()
+    inp["fc1_codes"][0, 5, 0] = 255
+    assert oracle_lib.moe(inp)["status"] == -1
+
+
+@pytest.mark.parametrize("block", [64, 128])
+def test_base3_equals_two_bit_ternary(oracle_lib, block):
+    """The same digits stored in base 3 and as 2-bit ternary fields give the
+    same matrix, the same layer output and the same gathered-channel output,
+    bit for bit; the base-3 rows are 1.625 bits per weight."""
+    spec2 = custom_moe_spec(E=4, H=640, I=128, top_k=2, fc1="ternary", fc2="ternary", block1=block)
+    inp2 = synth.moe_inputs(spec2, T=3, seed=12)
+    spec3 = custom_moe_spec(E=4, H=640, I=128, top_k=2, fc1="ternary_b3", fc2="ternary_b3", block1=block,
+                            name="b3_of_" + spec2.name)
+    inp3 = dict(inp2, spec=spec3)
+    for m in ("fc1", "fc2"):
+        rows, K = inp2[m + "_codes"].shape[1], (spec2.H if m == "fc1" else spec2.I)
+        d = bf.fields(inp2[m + "_codes"], 2, K)
+        inp3[m + "_codes"] = synth.pack_base3(d, block)
+        assert inp3[m + "_codes"].shape[-1] * 8 / K == 1.625
+        W2 = oracle_lib.dequant("ternary", block, "bf16", inp2[m + "_codes"][0], inp2[m + "_scales"][0], None,
+                                rows, K)
+        W3 = oracle_lib.dequant("ternary_b3", block, "bf16", inp3[m + "_codes"][0], inp3[m + "_scales"][0], None,
+                                rows, K)
+        assert np.array_equal(W2, W3)
+    r2, r3 = oracle_lib.moe(inp2), oracle_lib.moe(inp3)
+    assert r3["status"] == 0 and np.array_equal(r2["y64"], r3["y64"]) and np.array_equal(r2["y"], r3["y"])
+    ch = synth.channel_inputs(spec2, inp2, 0.3, seed=12)
+    d = bf.fields(ch["down_codes"], 2, spec2.H)
+    c2 = dict(inp2, **ch)
+    c3 = dict(inp3, **ch)
+    c3.update(down_codes=synth.pack_base3(d, block), down_fmt=("ternary_b3", block, "bf16"))
+    a, b = oracle_lib.moe_channels(c2, ch["channels"]), oracle_lib.moe_channels(c3, ch["channels"])
+    assert b["status"] == 0 and np.array_equal(a["y64"], b["y64"])
+
+
+def test_base3_moe_vs_dense_bruteforce(oracle_lib):
+    """A base-3 layer against the independent float64 dense mixture (digits
+    from numpy's base-3 strings)."""
+    spec = custom_moe_spec(E=5, H=320, I=64, top_k=2, fc1="ternary_b3", fc2="ternary_b3", block1=64,
+                           scale_dtype="f16")
+    inp = synth.moe_inputs(spec, T=4, seed=13)
+    out = oracle_lib.moe(inp)
+    ref = bf.moe_dense(inp)
+    assert out["status"] == 0
+    assert np.max(np.abs(out["y64"] - ref)) <= 1e-12 * np.max(np.abs(ref))
