@@ -95,7 +95,15 @@ typedef enum qmoe_qtype {
   QMOE_QTYPE_SYM_INT2 = 1,
   QMOE_QTYPE_TERNARY = 2,
   QMOE_QTYPE_AFFINE_INT2 = 3,
-  QMOE_QTYPE_AFFINE_INT4 = 4
+  QMOE_QTYPE_AFFINE_INT4 = 4,
+  QMOE_QTYPE_TERNARY_B3 = 5 /* ternary in base 3, five weights per byte (MLX issue 3852, closing
+                               remarks: a denser ternary storage of about 1.6 bits per weight):
+                               each block of B weights takes ceil(B/5) bytes, weight i of the block
+                               is base-3 digit i mod 5 (least significant first) of byte i/5,
+                               q = digit - 1; a byte holding more than its digits allow (>= 243,
+                               or >= 3^(B mod 5) for a block's last byte) is invalid.  Gathered
+                               channels only (fc1 and fc2 both); the MoE and dense calls return
+                               QMOE_ERR_UNSUPPORTED. */
 } qmoe_qtype;
 
 typedef enum qmoe_path {
@@ -342,17 +350,21 @@ qmoe_status qmoe_unpack_codes(const qmoe_layer_desc *desc, const void *packed, i
  * twice.
  *
  * Supported layers: activation SWIGLU, act_dtype BF16 or F16, fc1 and fc2
- * qtypes SYM_INT4, SYM_INT2 or TERNARY (no affine formats), no biases,
- * hidden <= 4096.
+ * qtypes SYM_INT4, SYM_INT2 or TERNARY (no affine formats), or both
+ * TERNARY_B3, no biases, hidden <= 4096 (base-3: hidden <= 2048).
  *
  * Channel-packed buffer: fc1 codes and scales exactly as for qmoe_prepack
  * (canonical [E][2I][H*bits/8] rows, [E][2I][H/block] scales), and the down
  * projection CHANNEL-MAJOR: down_codes [E][I][H*bits/8] (row c holds column c
  * of the [H][I] down matrix, quantized along H in fc2's qtype, fc2.block
  * weights per block) and down_scales [E][I][H/fc2.block] in fc2.scale_dtype.
+ * TERNARY_B3 rows hold (H/B) * ceil(B/5) bytes; the packed buffer keeps each
+ * of their blocks as one 4-byte aligned record of its digit bytes followed by
+ * its scale (16 bytes for B = 64, 28 for B = 128).
  * All sources are device pointers; the call copies them into `dst` (256-byte
  * aligned, >= qmoe_channel_prepacked_size bytes), waits for the stream, and
- * returns QMOE_ERR_INVALID_ARGUMENT if a TERNARY field holds the value 3. */
+ * returns QMOE_ERR_INVALID_ARGUMENT if a TERNARY field holds the value 3 or a
+ * TERNARY_B3 byte is invalid. */
 qmoe_status qmoe_channel_prepacked_size(const qmoe_layer_desc *desc, size_t *bytes);
 qmoe_status qmoe_channel_prepack(const qmoe_layer_desc *desc, const void *fc1_codes,
                                  const void *fc1_scales, const void *down_codes,

@@ -14,7 +14,7 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libqmoe.so")
 
-QTYPE = {"sym_int4": 0, "sym_int2": 1, "ternary": 2, "affine_int2": 3, "affine_int4": 4}
+QTYPE = {"sym_int4": 0, "sym_int2": 1, "ternary": 2, "affine_int2": 3, "affine_int4": 4, "ternary_b3": 5}
 DTYPE = {"bf16": 0, "f16": 1, "f32": 2}
 PATH = {"auto": 0, "gemv": 1, "grouped": 2}
 TOPK_WEIGHTS = {"renormalized": 0, "softmax_all": 1}

@@ -48,7 +48,7 @@ bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
 qmoe_status check_matrix(const qmoe_qmatrix_desc &m, const char *name, int64_t rows, int64_t cols) {
   if (m.reserved != 0) return fail(QMOE_ERR_INVALID_ARGUMENT, "%s: reserved field must be 0", name);
-  if (m.qtype < QMOE_QTYPE_SYM_INT4 || m.qtype > QMOE_QTYPE_AFFINE_INT4)
+  if (m.qtype < QMOE_QTYPE_SYM_INT4 || m.qtype > QMOE_QTYPE_TERNARY_B3)
     return fail(QMOE_ERR_UNSUPPORTED, "%s: unknown qtype %d", name, m.qtype);
   if (m.scale_dtype != QMOE_DTYPE_BF16 && m.scale_dtype != QMOE_DTYPE_F16)
     return fail(QMOE_ERR_UNSUPPORTED, "%s: scale dtype %d not supported (bf16 or f16)", name,
@@ -70,7 +70,8 @@ qmoe_status check_matrix(const qmoe_qmatrix_desc &m, const char *name, int64_t r
   return ok();
 }
 
-qmoe_status check_layer(const qmoe_layer_desc *d) {
+// channels: the gathered-channel calls, the only ones that take base-3 rows.
+qmoe_status check_layer(const qmoe_layer_desc *d, bool channels = false) {
   if (!d) return fail(QMOE_ERR_INVALID_ARGUMENT, "null layer descriptor");
   if (d->num_experts < 1) return fail(QMOE_ERR_INVALID_ARGUMENT, "num_experts must be >= 1");
   if (d->num_experts > kMaxExperts)
@@ -84,8 +85,11 @@ qmoe_status check_layer(const qmoe_layer_desc *d) {
   if (d->reserved != 0) return fail(QMOE_ERR_INVALID_ARGUMENT, "layer reserved field must be 0");
   const int64_t fc1_rows = d->activation == QMOE_ACT_RELU ? (int64_t)d->inter : 2 * (int64_t)d->inter;
   qmoe_status st = check_matrix(d->fc1, "fc1", fc1_rows, d->hidden);
+  if (st == QMOE_OK) st = check_matrix(d->fc2, "fc2", d->hidden, d->inter);
   if (st != QMOE_OK) return st;
-  return check_matrix(d->fc2, "fc2", d->hidden, d->inter);
+  if (!channels && (d->fc1.qtype == QMOE_QTYPE_TERNARY_B3 || d->fc2.qtype == QMOE_QTYPE_TERNARY_B3))
+    return fail(QMOE_ERR_UNSUPPORTED, "base-3 ternary rows are read by the gathered-channel calls only");
+  return ok();
 }
 
 qmoe_status check_tokens(const qmoe_layer_desc *d, int32_t T, int32_t top_k) {
@@ -908,7 +912,7 @@ constexpr uint64_t kChanMagic = 0x31304843454f4d51ull;  // "QMOECH01"
 constexpr int32_t kChanMaxList = 65536;
 
 qmoe_status check_channel_layer(const qmoe_layer_desc *d) {
-  qmoe_status st = check_layer(d);
+  qmoe_status st = check_layer(d, true);
   if (st != QMOE_OK) return st;
   if (d->activation != QMOE_ACT_SWIGLU)
     return fail(QMOE_ERR_UNSUPPORTED, "gathered channels: SWIGLU layers only");
@@ -916,6 +920,10 @@ qmoe_status check_channel_layer(const qmoe_layer_desc *d) {
     return fail(QMOE_ERR_UNSUPPORTED, "gathered channels: bf16 or f16 activations only");
   if (qtype_affine(d->fc1.qtype) || qtype_affine(d->fc2.qtype))
     return fail(QMOE_ERR_UNSUPPORTED, "gathered channels: symmetric formats only (sym_int4, sym_int2, ternary)");
+  if ((d->fc1.qtype == QMOE_QTYPE_TERNARY_B3) != (d->fc2.qtype == QMOE_QTYPE_TERNARY_B3))
+    return fail(QMOE_ERR_UNSUPPORTED, "gathered channels: base-3 rows need both matrices in TERNARY_B3");
+  if (d->fc1.qtype == QMOE_QTYPE_TERNARY_B3 && d->hidden > kChanMaxHiddenB3)
+    return fail(QMOE_ERR_UNSUPPORTED, "gathered channels: base-3 rows need hidden <= %d", kChanMaxHiddenB3);
   if (d->hidden % d->fc2.block != 0)
     return fail(QMOE_ERR_INVALID_ARGUMENT, "gathered channels: hidden %d not a multiple of fc2 block %d",
                 d->hidden, d->fc2.block);
@@ -973,12 +981,23 @@ qmoe_status qmoe_channel_prepack(const qmoe_layer_desc *desc, const void *fc1_co
   memcpy(header, &magic, 8);
   memcpy(header + 8, desc, sizeof(qmoe_layer_desc) < 112 ? sizeof(qmoe_layer_desc) : 112);
   hipError_t e = hipMemcpyAsync(d, header, kHeaderBytes, hipMemcpyHostToDevice, s);
-  if (e == hipSuccess) e = hipMemcpyAsync(d + L.fc1_off, fc1_codes, fc1_bytes, hipMemcpyDeviceToDevice, s);
-  if (e == hipSuccess) e = hipMemcpyAsync(d + L.fc1_sc_off, fc1_scales, fc1_sc, hipMemcpyDeviceToDevice, s);
-  if (e == hipSuccess) e = hipMemcpyAsync(d + L.dn_off, down_codes, dn_bytes, hipMemcpyDeviceToDevice, s);
-  if (e == hipSuccess) e = hipMemcpyAsync(d + L.dn_sc_off, down_scales, dn_sc, hipMemcpyDeviceToDevice, s);
-  if (e != hipSuccess) return hip_status(e, "channel prepack copies");
   uint32_t *err = (uint32_t *)(d + kErrWordOff);
+  if (L.b3) {  // block records with the scales inside, and the invalid-byte count
+    if (e == hipSuccess)
+      e = launch_pack_b3_records((const uint8_t *)fc1_codes, (const uint16_t *)fc1_scales, E * 2 * I, H,
+                                 desc->fc1.block, d + L.fc1_off, err, s);
+    if (e == hipSuccess)
+      e = launch_pack_b3_records((const uint8_t *)down_codes, (const uint16_t *)down_scales, E * I, H,
+                                 desc->fc2.block, d + L.dn_off, err, s);
+    if (e != hipSuccess) return hip_status(e, "channel prepack base-3 records");
+  }
+  if (!L.b3) {
+    if (e == hipSuccess) e = hipMemcpyAsync(d + L.fc1_off, fc1_codes, fc1_bytes, hipMemcpyDeviceToDevice, s);
+    if (e == hipSuccess) e = hipMemcpyAsync(d + L.fc1_sc_off, fc1_scales, fc1_sc, hipMemcpyDeviceToDevice, s);
+    if (e == hipSuccess) e = hipMemcpyAsync(d + L.dn_off, down_codes, dn_bytes, hipMemcpyDeviceToDevice, s);
+    if (e == hipSuccess) e = hipMemcpyAsync(d + L.dn_sc_off, down_scales, dn_sc, hipMemcpyDeviceToDevice, s);
+  }
+  if (e != hipSuccess) return hip_status(e, "channel prepack copies");
   if (desc->fc1.qtype == QMOE_QTYPE_TERNARY) e = launch_count_invalid_ternary(d + L.fc1_off, fc1_bytes, err, s);
   if (e == hipSuccess && desc->fc2.qtype == QMOE_QTYPE_TERNARY)
     e = launch_count_invalid_ternary(d + L.dn_off, dn_bytes, err, s);
@@ -987,7 +1006,10 @@ qmoe_status qmoe_channel_prepack(const qmoe_layer_desc *desc, const void *fc1_co
   e = hipMemcpyAsync(&nbad, err, 4, hipMemcpyDeviceToHost, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess) return hip_status(e, "channel prepack error word");
-  if (nbad) return fail(QMOE_ERR_INVALID_ARGUMENT, "%u ternary fields hold the invalid value 3", nbad);
+  if (nbad)
+    return fail(QMOE_ERR_INVALID_ARGUMENT, L.b3 ? "%u base-3 bytes hold more digits than allowed"
+                                              : "%u ternary fields hold the invalid value 3",
+                nbad);
   return ok();
 }
 
@@ -1036,6 +1058,7 @@ qmoe_status qmoe_forward_channels(const qmoe_layer_desc *desc, const void *packe
   a.dn_block = desc->fc2.block;
   a.dn_sf16 = desc->fc2.scale_dtype == QMOE_DTYPE_F16;
   a.dn_zp = qtype_zero_point(desc->fc2.qtype);
+  a.b3 = L.b3 ? 1 : 0;
   a.T = T;
   a.E = desc->num_experts;
   a.k = top_k;
@@ -1122,6 +1145,8 @@ qmoe_status qmoe_unpack_codes(const qmoe_layer_desc *desc, const void *packed, i
 qmoe_status qmoe_linear_prepacked_size(const qmoe_qmatrix_desc *desc, size_t *bytes) {
   if (!desc) return fail(QMOE_ERR_INVALID_ARGUMENT, "null descriptor");
   qmoe_status st = check_matrix(*desc, "linear", -1, -1);
+  if (st == QMOE_OK && desc->qtype == QMOE_QTYPE_TERNARY_B3)
+    st = fail(QMOE_ERR_UNSUPPORTED, "base-3 ternary rows are read by the gathered-channel calls only");
   if (st != QMOE_OK) return st;
   if (!bytes) return fail(QMOE_ERR_INVALID_ARGUMENT, "null size output");
   *bytes = (size_t)(MatLayout::make(*desc).stride + kLinearTail);  // + the tail (error word, pre-scale)
@@ -1173,6 +1198,8 @@ qmoe_status qmoe_linear(const qmoe_qmatrix_desc *desc, const void *packed, const
                         void *stream) {
   if (!desc) return fail(QMOE_ERR_INVALID_ARGUMENT, "null descriptor");
   qmoe_status st = check_matrix(*desc, "linear", -1, -1);
+  if (st == QMOE_OK && desc->qtype == QMOE_QTYPE_TERNARY_B3)
+    st = fail(QMOE_ERR_UNSUPPORTED, "base-3 ternary rows are read by the gathered-channel calls only");
   if (st != QMOE_OK) return st;
   if (x_dtype != QMOE_DTYPE_BF16 && x_dtype != QMOE_DTYPE_F16)
     return fail(QMOE_ERR_UNSUPPORTED, "x dtype %d not supported", x_dtype);
@@ -1227,6 +1254,8 @@ qmoe_status qmoe_linear_unpack_codes(const qmoe_qmatrix_desc *desc, const void *
                                      int8_t *codes_out, void *stream) {
   if (!desc) return fail(QMOE_ERR_INVALID_ARGUMENT, "null descriptor");
   qmoe_status st = check_matrix(*desc, "linear", -1, -1);
+  if (st == QMOE_OK && desc->qtype == QMOE_QTYPE_TERNARY_B3)
+    st = fail(QMOE_ERR_UNSUPPORTED, "base-3 ternary rows are read by the gathered-channel calls only");
   if (st != QMOE_OK) return st;
   if (!packed || !codes_out) return fail(QMOE_ERR_INVALID_ARGUMENT, "null device pointer");
   const MatLayout L = MatLayout::make(*desc);

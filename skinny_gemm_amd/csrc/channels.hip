@@ -360,6 +360,262 @@ __global__ __launch_bounds__(kChanWaves * 64) void chan_fused_kernel(ChanArgs a)
   }
 }
 
+// ------------------------------------------------------------ base-3 rows
+// Both matrices TERNARY_B3: every row is a run of block records (the digit
+// bytes of B weights, five per byte, then the block's 16-bit scale in the
+// record's last two bytes; RW = record bytes / 4 dwords).  A "unit" is one
+// record dword: its (up to) four digit bytes hold 20 consecutive weights,
+// b B + 20 j + i for record b, dword j, i < min(20, B - 20 j); the last
+// dword's other bytes are padding and the scale, whose digits are masked.
+// A 256-entry table in LDS turns a byte into its five base-3 digits (least
+// significant first) as bytes, read with v_cvt_f32_ubyte.
+__device__ inline void b3_table(uint2 *lut) {
+  for (int v = threadIdx.x; v < 256; v += blockDim.x) {
+    uint32_t d[5] = {0u, 0u, 0u, 0u, 0u};
+    if (v < 243) {
+      int r = v;
+      for (int i = 0; i < 5; ++i) {
+        d[i] = (uint32_t)(r % 3);
+        r /= 3;
+      }
+    }
+    lut[v] = make_uint2(d[0] | (d[1] << 8) | (d[2] << 16) | (d[3] << 24), d[4]);
+  }
+}
+
+// The 20 digits of a unit dword as floats.
+__device__ inline void b3_digits(const uint2 *lut, uint32_t w, float (&dg)[20]) {
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const uint2 e = lut[(w >> (8 * m)) & 0xFFu];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dg[5 * m + i] = ubyte_f(e.x, i);
+    dg[5 * m + 4] = ubyte_f(e.y, 0);
+  }
+}
+
+// The same workgroup shape and steps as chan_fused_kernel; HC: H <= 1024 << HC.
+template <int HC>
+__global__ __launch_bounds__(kChanWaves * 64) void chan_b3_kernel(ChanArgs a) {
+  constexpr int NU1 = 2 << HC;   // units per lane of a half wave (FC1 rows: <= 64 << HC units)
+  constexpr int NU2 = 1 << HC;   // units per lane (down rows)
+  constexpr int NPL = 20 * NU2;  // down outputs per lane
+  constexpr int RS = NPL / 4 + 1;
+  __shared__ TopkScratch s_sc;
+  __shared__ int32_t s_ids[kMaxTopK];
+  __shared__ float s_w[kMaxTopK];
+  __shared__ float s_ex[kMaxTopK];
+  __shared__ uint2 s_lut[256];
+  __shared__ __align__(16) float s_x[(1024 << HC) + 32];
+  __shared__ float4 s_red[kChanWaves / 2][64 * RS];
+
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int half = lane >> 5, l = lane & 31;
+  const int G = a.groups;
+  const int t = blockIdx.x / G, grp = blockIdx.x % G;
+  const int per_tok = a.k * a.C;
+  const int q0 = grp * kChanPerWg + wv * kChanEpw;
+  const int RW1 = b3_record_bytes(a.fc1_block) / 4, RW2 = b3_record_bytes(a.dn_block) / 4;
+  const int U1 = (a.H / a.fc1_block) * RW1, U2 = (a.H / a.dn_block) * RW2;
+
+  // ---- round 1: list entries, activations (to LDS), logits; digit table
+  int chv = -1;
+  if (lane < kChanEpw && q0 + lane < per_tok) chv = a.channels[(int64_t)t * per_tok + q0 + lane];
+  for (int n = threadIdx.x; n < a.H + 32; n += blockDim.x)
+    s_x[n] = n < a.H ? half_to_f32_rt(a.x[(int64_t)t * a.H + n], a.x_f16) : 0.f;
+  b3_table(s_lut);
+  if (wv == 0) {
+    if (a.E <= 64) wave_topk_rank(a.logits + (int64_t)t * a.E, a.E, a.k, s_ids, s_w, s_ex);
+    else wave_topk<false>(a.logits + (int64_t)t * a.E, a.E, a.k, nullptr, s_w, s_ids, &s_sc);
+  }
+  __syncthreads();
+
+  // ---- round 2: every unit dword and its record's scale dword, all entries
+  uint32_t c1[kChanEpw][NU1], k1[kChanEpw][NU1];
+  uint32_t c2[kChanEpw][NU2], k2[kChanEpw][NU2];
+  float wj[kChanEpw];
+  bool on[kChanEpw];
+#pragma unroll
+  for (int i = 0; i < kChanEpw; ++i) {
+    const int c = __builtin_amdgcn_readlane(chv, i);
+    on[i] = c >= 0 && c < a.I;
+    const int j = on[i] ? (q0 + i) / a.C : 0;
+    const int e = on[i] ? __builtin_amdgcn_readfirstlane(s_ids[j]) : 0;
+    wj[i] = on[i] ? s_w[j] : 0.f;
+    const int cc = on[i] ? c : 0;
+    const uint32_t *row1 = reinterpret_cast<const uint32_t *>(
+        a.fc1 + ((int64_t)e * 2 * a.I + 2 * (int64_t)cc + half) * a.fc1_row_bytes);
+#pragma unroll
+    for (int iu = 0; iu < NU1; ++iu) {
+      const int u = l + 32 * iu;
+      const int uc = u < U1 ? u : U1 - 1;
+      c1[i][iu] = row1[uc];
+      k1[i][iu] = row1[(uc / RW1) * RW1 + RW1 - 1];
+    }
+    const uint32_t *row2 =
+        reinterpret_cast<const uint32_t *>(a.dn + ((int64_t)e * a.I + cc) * a.dn_row_bytes);
+#pragma unroll
+    for (int iu = 0; iu < NU2; ++iu) {
+      const int u = lane + 64 * iu;
+      const int uc = u < U2 ? u : U2 - 1;
+      c2[i][iu] = row2[uc];
+      k2[i][iu] = row2[(uc / RW2) * RW2 + RW2 - 1];
+    }
+  }
+
+  // ---- FC1: per unit, su = sum d x and sx = sum x over its weights
+  float dot[kChanEpw];
+#pragma unroll
+  for (int i = 0; i < kChanEpw; ++i) dot[i] = 0.f;
+#pragma unroll
+  for (int iu = 0; iu < NU1; ++iu) {
+    const int u = l + 32 * iu;
+    const int b = u / RW1, jd = u - b * RW1;
+    const int cnt = u < U1 ? min(20, a.fc1_block - 20 * jd) : 0;
+    const int base = b * a.fc1_block + 20 * jd;
+    float xv[20];
+    float sx = 0.f;
+#pragma unroll
+    for (int q = 0; q < 5; ++q) {
+      const float4 v = u < U1 ? *reinterpret_cast<const float4 *>(&s_x[base + 4 * q]) : make_float4(0.f, 0.f, 0.f, 0.f);
+      xv[4 * q] = v.x;
+      xv[4 * q + 1] = v.y;
+      xv[4 * q + 2] = v.z;
+      xv[4 * q + 3] = v.w;
+    }
+#pragma unroll
+    for (int m = 0; m < 20; ++m) {
+      xv[m] = m < cnt ? xv[m] : 0.f;
+      sx += xv[m];
+    }
+#pragma unroll
+    for (int i = 0; i < kChanEpw; ++i) {
+      float dg[20];
+      b3_digits(s_lut, c1[i][iu], dg);
+      float su = 0.f;
+#pragma unroll
+      for (int m = 0; m < 20; ++m) su = fmaf(dg[m], xv[m], su);
+      const float sc = half_to_f32_rt(k1[i][iu] >> 16, a.fc1_sf16);
+      dot[i] = fmaf(sc, su - sx, dot[i]);  // q = digit - 1
+    }
+  }
+
+  // ---- down rows: acc += w_j h_c s d per unit; the zero point per unit at the end
+  float acc[NPL];
+#pragma unroll
+  for (int o = 0; o < NPL; ++o) acc[o] = 0.f;
+  float csum[NU2];
+#pragma unroll
+  for (int iu = 0; iu < NU2; ++iu) csum[iu] = 0.f;
+#pragma unroll
+  for (int i = 0; i < kChanEpw; ++i) {
+    float d1 = dot[i];
+#pragma unroll
+    for (int off = 16; off >= 1; off >>= 1) d1 += __shfl_xor(d1, off);
+    const float g = __shfl(d1, 0), uu = __shfl(d1, 32);
+    const float coef = on[i] ? wj[i] * (g / (1.f + expf(-g)) * uu) : 0.f;
+#pragma unroll
+    for (int iu = 0; iu < NU2; ++iu) {
+      const float cs = on[i] ? coef * half_to_f32_rt(k2[i][iu] >> 16, a.dn_sf16) : 0.f;
+      csum[iu] += cs;
+      float dg[20];
+      b3_digits(s_lut, c2[i][iu], dg);
+#pragma unroll
+      for (int m = 0; m < 20; ++m) acc[20 * iu + m] = fmaf(cs, dg[m], acc[20 * iu + m]);
+    }
+  }
+#pragma unroll
+  for (int iu = 0; iu < NU2; ++iu)
+#pragma unroll
+    for (int m = 0; m < 20; ++m) acc[20 * iu + m] -= csum[iu];  // zero point 1
+
+  // ---- the waves' sums (fixed order, as in chan_fused_kernel), then the
+  // valid outputs of each unit
+  if (wv >= 4) {
+#pragma unroll
+    for (int o = 0; o < NPL / 4; ++o)
+      s_red[wv - 4][lane * RS + o] = make_float4(acc[4 * o], acc[4 * o + 1], acc[4 * o + 2], acc[4 * o + 3]);
+  }
+  __syncthreads();
+  if (wv < 4) {
+#pragma unroll
+    for (int o = 0; o < NPL / 4; ++o) {
+      float4 r = s_red[wv][lane * RS + o];
+      r.x += acc[4 * o];
+      r.y += acc[4 * o + 1];
+      r.z += acc[4 * o + 2];
+      r.w += acc[4 * o + 3];
+      s_red[wv][lane * RS + o] = r;
+    }
+  }
+  __syncthreads();
+  float *dst = a.partial + ((int64_t)t * G + grp) * a.H;
+  for (int idx = threadIdx.x; idx < 64 * (NPL / 4); idx += kChanWaves * 64) {
+    const int L = idx / (NPL / 4), o = idx % (NPL / 4);
+    const int u = L + 64 * (o / 5);
+    if (u >= U2) continue;
+    const int b = u / RW2, jd = u - b * RW2;
+    const int cnt = min(20, a.dn_block - 20 * jd);
+    float4 r = s_red[0][L * RS + o];
+#pragma unroll
+    for (int w = 1; w < kChanWaves / 2; ++w) {
+      const float4 q = s_red[w][L * RS + o];
+      r.x += q.x;
+      r.y += q.y;
+      r.z += q.z;
+      r.w += q.w;
+    }
+    const int m0 = 4 * (o % 5);
+    const int64_t n0 = (int64_t)b * a.dn_block + 20 * jd + m0;
+    const float rv[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+      if (m0 + m < cnt) dst[n0 + m] = rv[m];
+  }
+}
+
+// One thread per (row, block): a canonical base-3 block (ceil(B/5) bytes) and
+// its scale into one record; bytes holding more digits than they may are
+// counted.
+__global__ __launch_bounds__(256) void pack_b3_kernel(const uint8_t *__restrict__ codes,
+                                                      const uint16_t *__restrict__ scales, int64_t rows, int nblk,
+                                                      int block, uint8_t *__restrict__ dst, uint32_t *count) {
+  const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (id >= rows * nblk) return;
+  const int per = b3_block_bytes(block), R = b3_record_bytes(block);
+  const int last = block % 5 ? block % 5 : 5;  // digits of the block's last byte
+  const uint8_t *src = codes + id * per;       // rows are nblk blocks of per bytes, back to back
+  uint32_t *out = reinterpret_cast<uint32_t *>(dst + id * R);
+  uint32_t bad = 0;
+  for (int wd = 0; wd < R / 4; ++wd) {
+    uint32_t w = 0;
+    for (int m = 0; m < 4; ++m) {
+      const int j = 4 * wd + m;
+      uint32_t v = 0;
+      if (j < per) {
+        v = src[j];
+        const uint32_t limit = j == per - 1 ? (last == 5 ? 243u : (last == 4 ? 81u : last == 3 ? 27u : last == 2 ? 9u : 3u))
+                                            : 243u;
+        bad += v >= limit ? 1u : 0u;
+      } else if (j >= R - 2) {
+        v = (scales[id] >> (8 * (j - (R - 2)))) & 0xFFu;
+      }
+      w |= v << (8 * m);
+    }
+    out[wd] = w;
+  }
+  if (bad) atomicAdd(count, bad);
+}
+
+hipError_t launch_pack_b3_records(const uint8_t *codes, const uint16_t *scales, int64_t rows, int64_t K, int block,
+                                  uint8_t *dst, uint32_t *count, hipStream_t s) {
+  const int nblk = (int)(K / block);
+  const int64_t n = rows * nblk;
+  if (n == 0) return hipSuccess;
+  return qlaunch(pack_b3_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, codes, scales, rows, nblk, block,
+                 dst, count);
+}
+
 // Workgroup (t, 64 outputs): wave v sums groups v, v + kChanReduceWaves, ...
 // in order, then wave 0 adds the waves' sums in wave order.
 __global__ __launch_bounds__(kChanReduceWaves * 64) void chan_reduce_kernel(ChanArgs a) {
@@ -419,7 +675,14 @@ hipError_t launch_fused(const ChanArgs &a, hipStream_t s) {
 hipError_t launch_channels(const ChanArgs &a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
   if (a.H > kChanMaxHidden) return hipErrorInvalidValue;
-  hipError_t e = a.x_f16 ? launch_fused<true>(a, s) : launch_fused<false>(a, s);
+  hipError_t e;
+  if (a.b3) {
+    const dim3 grid((unsigned)((int64_t)a.T * a.groups)), block(kChanWaves * 64);
+    if (a.H > kChanMaxHiddenB3) return hipErrorInvalidValue;
+    e = a.H <= 1024 ? qlaunch(chan_b3_kernel<0>, grid, block, 0, s, a) : qlaunch(chan_b3_kernel<1>, grid, block, 0, s, a);
+  } else {
+    e = a.x_f16 ? launch_fused<true>(a, s) : launch_fused<false>(a, s);
+  }
   if (e != hipSuccess) return e;
   const int64_t blocks = (int64_t)a.T * ((a.H + 63) / 64);
   return qlaunch(chan_reduce_kernel, dim3((unsigned)blocks), dim3(kChanReduceWaves * 64), 0, s, a);

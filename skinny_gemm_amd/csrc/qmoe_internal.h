@@ -26,6 +26,11 @@ __host__ __device__ inline int64_t align_up(int64_t v, int64_t a) { return (v + 
 __host__ __device__ inline int qtype_bits(int qt) {
   return (qt == QMOE_QTYPE_SYM_INT4 || qt == QMOE_QTYPE_AFFINE_INT4) ? 4 : 2;
 }
+// Base-3 ternary rows: ceil(B/5) digit bytes per block of B weights in the
+// canonical form; in the channel-packed buffer one 4-byte aligned record of
+// the digit bytes and the block's 16-bit scale in its last two bytes.
+__host__ __device__ inline int b3_block_bytes(int block) { return (block + 4) / 5; }
+__host__ __device__ inline int b3_record_bytes(int block) { return (b3_block_bytes(block) + 2 + 3) / 4 * 4; }
 __host__ __device__ inline bool qtype_affine(int qt) {
   return qt == QMOE_QTYPE_AFFINE_INT2 || qt == QMOE_QTYPE_AFFINE_INT4;
 }
@@ -35,6 +40,7 @@ __host__ __device__ inline int qtype_zero_point(int qt) {
     case QMOE_QTYPE_SYM_INT4: return 8;
     case QMOE_QTYPE_SYM_INT2: return 2;
     case QMOE_QTYPE_TERNARY: return 1;
+    case QMOE_QTYPE_TERNARY_B3: return 1;
     default: return 0;
   }
 }
@@ -276,25 +282,32 @@ hipError_t launch_split_f32(const float *x, int64_t n, uint16_t *hi, uint16_t *l
 // aligned sections): FC1 rows [E][2I][H*b/8] in the canonical byte order and
 // their scales [E][2I][H/B]; the channel-major down projection [E][I][H*b/8]
 // and its scales [E][I][H/B].
+// Base-3 rows (both matrices TERNARY_B3): the rows are block records with the
+// scales inside them, and the scale sections are empty.
 struct ChanLayout {
+  bool b3;
   int64_t fc1_row_bytes, dn_row_bytes;
   int64_t fc1_off, fc1_sc_off, dn_off, dn_sc_off, total;
   static ChanLayout make(const qmoe_layer_desc &d) {
     ChanLayout L{};
     const int64_t E = d.num_experts, H = d.hidden, I = d.inter;
-    L.fc1_row_bytes = H * qtype_bits(d.fc1.qtype) / 8;
-    L.dn_row_bytes = H * qtype_bits(d.fc2.qtype) / 8;
+    L.b3 = d.fc1.qtype == QMOE_QTYPE_TERNARY_B3;
+    L.fc1_row_bytes = L.b3 ? (H / d.fc1.block) * b3_record_bytes(d.fc1.block) : H * qtype_bits(d.fc1.qtype) / 8;
+    L.dn_row_bytes = L.b3 ? (H / d.fc2.block) * b3_record_bytes(d.fc2.block) : H * qtype_bits(d.fc2.qtype) / 8;
+    const int64_t sc1 = L.b3 ? 0 : E * 2 * I * (H / d.fc1.block) * 2;
+    const int64_t sc2 = L.b3 ? 0 : E * I * (H / d.fc2.block) * 2;
     L.fc1_off = kHeaderBytes;
     L.fc1_sc_off = L.fc1_off + align_up(E * 2 * I * L.fc1_row_bytes, kAlign);
-    L.dn_off = L.fc1_sc_off + align_up(E * 2 * I * (H / d.fc1.block) * 2, kAlign);
+    L.dn_off = L.fc1_sc_off + align_up(sc1, kAlign);
     L.dn_sc_off = L.dn_off + align_up(E * I * L.dn_row_bytes, kAlign);
-    L.total = L.dn_sc_off + align_up(E * I * (H / d.fc2.block) * 2, kAlign);
+    L.total = L.dn_sc_off + align_up(sc2, kAlign);
     return L;
   }
 };
 
 constexpr int kChanGroupEntries = 16;  // list entries per workgroup (partial sums per token: k C / 16)
 constexpr int kChanMaxHidden = 4096;
+constexpr int kChanMaxHiddenB3 = 2048;  // base-3 rows
 
 struct ChanArgs {
   const uint8_t *fc1, *fc1_scales;
@@ -303,6 +316,7 @@ struct ChanArgs {
   const uint8_t *dn, *dn_scales;
   int64_t dn_row_bytes;
   int dn_bits, dn_block, dn_sf16, dn_zp;
+  int b3;                   // both matrices base-3 block records (row bytes: records)
   int T, E, k, C, I, H;
   int groups;               // ceil(k * C / kChanGroupEntries) list groups per token
   const uint16_t *x;        // [T][H], 16-byte aligned
@@ -313,6 +327,10 @@ struct ChanArgs {
   uint16_t *y;
 };
 hipError_t launch_channels(const ChanArgs &a, hipStream_t s);
+// Canonical base-3 rows [rows][(K/B) ceil(B/5)] and scales [rows][K/B] ->
+// block records; counts the invalid bytes into *count.
+hipError_t launch_pack_b3_records(const uint8_t *codes, const uint16_t *scales, int64_t rows, int64_t K, int block,
+                                  uint8_t *dst, uint32_t *count, hipStream_t s);
 // Counts ternary fields holding the invalid value 3 in `bytes` bytes.
 hipError_t launch_count_invalid_ternary(const uint8_t *p, int64_t bytes, uint32_t *count, hipStream_t s);
 

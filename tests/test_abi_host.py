@@ -380,3 +380,25 @@ def test_channel_calls_validate_before_launch():
             q.channel_workspace_size(ok, 1, 6, Cn)
     st = q.lib().qmoe_forward_channels(C.byref(ok), None, None, None, 1, 6, None, 8, None, None, 0, None)
     assert st != 0 and "null" in q.last_error()
+
+
+def test_base3_rows_only_on_the_channel_calls():
+    """TERNARY_B3 layers: the MoE and dense calls refuse them, the channel
+    calls take them when both matrices are base 3 and H <= 2048; the packed
+    rows are block records (16 bytes per 64 weights, 28 per 128)."""
+    b3 = q.layer_desc(8, 2048, 256, "bf16", ("ternary_b3", 128, "bf16"), ("ternary_b3", 64, "bf16"))
+    for fn in (lambda: q.prepacked_size(b3), lambda: q.workspace_size(b3, 1, 2),
+               lambda: q.linear_prepacked_size(q.qmatrix_desc("ternary_b3", 128, "f16", 64, 640))):
+        with pytest.raises(q.QmoeError) as ei:
+            fn()
+        assert ei.value.status == 2
+    n = q.channel_prepacked_size(b3)
+    fc1 = 8 * 512 * 16 * 28          # 16 records of 28 B per FC1 row
+    dn = 8 * 256 * 32 * 16           # 32 records of 16 B per down row
+    assert fc1 + dn + 256 <= n <= fc1 + dn + 256 + 3 * 256
+    mixed = q.layer_desc(8, 2048, 256, "bf16", ("ternary_b3", 128, "bf16"), ("ternary", 128, "bf16"))
+    wide = q.layer_desc(8, 4096, 256, "bf16", ("ternary_b3", 128, "bf16"), ("ternary_b3", 128, "bf16"))
+    for d in (mixed, wide):
+        with pytest.raises(q.QmoeError) as ei:
+            q.channel_prepacked_size(d)
+        assert ei.value.status == 2

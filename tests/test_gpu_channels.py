@@ -154,3 +154,51 @@ def test_channels_invalid_ternary_rejected():
     src = [to_device_bits(inp[k], None) for k in ("fc1_codes", "fc1_scales", "down_codes", "down_scales")]
     with pytest.raises(q.QmoeError, match="4 ternary fields"):
         q.channel_prepack(desc, *src, packed)
+
+
+# ------------------------------------------------------------ base-3 rows
+@pytest.mark.parametrize("H,block,sd,act,budget", [
+    (640, 64, "bf16", "bf16", 0.2),
+    (640, 128, "f16", "f16", 0.35),
+    (768, 128, "f16", "bf16", 0.5),
+    (2048, 64, "bf16", "bf16", 0.18),
+    (2048, 128, "bf16", "f16", 0.1),
+])
+def test_channels_base3(H, block, sd, act, budget):
+    """Both matrices in base-3 ternary (five weights per byte, block records
+    with the scale inside) against the oracle."""
+    spec = custom_moe_spec(16, H, 256, 4, fc1="ternary_b3", fc2="ternary_b3", block1=block, scale_dtype=sd,
+                           act_dtype=act)
+    run_case(spec, 5, 21, budget, repeat=True)
+
+
+def test_channels_base3_dsv2lite_shape():
+    """The decode layer's shape (E 64, k 6, H 2048, I 1408) in base 3 at the
+    18% budget."""
+    spec = custom_moe_spec(64, 2048, 1408, 6, fc1="ternary_b3", fc2="ternary_b3", block1=64)
+    run_case(spec, 2, 22, 0.18)
+
+
+def test_channels_base3_full_layer():
+    """Every channel of every routed expert listed once (budget 1): the whole
+    switch-shaped ternary layer from base-3 rows."""
+    spec = custom_moe_spec(8, 768, 768, 1, fc1="ternary_b3", fc2="ternary_b3", block1=128, scale_dtype="f16")
+    run_case(spec, 3, 23, 1.0)
+
+
+def test_channels_base3_invalid_bytes_rejected():
+    import skinny_gemm_amd as q
+    from skinny_gemm_amd.layer import to_device_bits
+    spec = custom_moe_spec(4, 640, 128, 1, fc1="ternary_b3", fc2="ternary_b3", block1=128)
+    inp = synth.moe_inputs(spec, 1, 0)
+    inp.update(synth.channel_inputs(spec, inp, 0.2, 0))
+    inp["fc1_codes"] = inp["fc1_codes"].copy()
+    inp["fc1_codes"][2, 9, 4] = 250          # a full byte >= 243
+    inp["down_codes"] = inp["down_codes"].copy()
+    inp["down_codes"][1, 3, 25] = 27         # a block's last byte (3 digits) >= 27
+    desc = q.layer_desc(spec.E, spec.H, spec.I, spec.act_dtype, ("ternary_b3", 128, "bf16"),
+                        ("ternary_b3", 128, "bf16"))
+    packed = torch.empty(q.channel_prepacked_size(desc), dtype=torch.uint8, device="cuda")
+    src = [to_device_bits(inp[k], None) for k in ("fc1_codes", "fc1_scales", "down_codes", "down_scales")]
+    with pytest.raises(q.QmoeError, match="2 base-3 bytes"):
+        q.channel_prepack(desc, *src, packed)
