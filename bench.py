@@ -537,6 +537,29 @@ def channel_decode_time(spec, T: int, budget: float, K: int = 32, trials: int = 
     return out
 
 
+def base3_channel_times(rotate_bytes: float) -> list:
+    import dataclasses
+    import synth
+    out = []
+    sw = synth.MOE_WORKLOADS["switch_base_ternary"]
+    d3 = synth.MOE_WORKLOADS["dsv2lite_int4"]
+    d3t = dataclasses.replace(d3, name="dsv2lite_ternary", fc1=synth.MatFmt("ternary", 64, "bf16"),
+                              fc2=synth.MatFmt("ternary", 64, "bf16"))
+    for base, budget in ((sw, 1.0), (d3t, 0.18)):
+        row = {"layer": base.name, "T": 1, "budget": budget}
+        for fmt in ("ternary", "ternary_b3"):
+            spec = dataclasses.replace(base, name=f"{base.name}_{fmt}",
+                                       fc1=dataclasses.replace(base.fc1, fmt=fmt),
+                                       fc2=dataclasses.replace(base.fc2, fmt=fmt))
+            r = channel_decode_time(spec, 1, budget, rotate_bytes=rotate_bytes)
+            row[fmt] = {k: r[k] for k in ("us_per_call", "listed_bytes_per_call", "effective_GBps", "list_len")}
+        row["bytes_ratio"] = row["ternary_b3"]["listed_bytes_per_call"] / row["ternary"]["listed_bytes_per_call"]
+        row["time_ratio"] = row["ternary_b3"]["us_per_call"] / row["ternary"]["us_per_call"]
+        log(f"[bench] base-3 {json.dumps(row)}")
+        out.append(row)
+    return out
+
+
 def cpu_baseline(b: "MoeBench", seconds: float):
     """The oracle (double precision, plain loops) on a bounded sample of the
     headline workload's tokens: first on one host core, then on all cores of
@@ -618,6 +641,10 @@ def decode_extras(args, variants) -> dict:
         r["full_layer_us"] = next(x["us_per_layer"] for x in extras["dsv2lite_int4"] if x["T"] == t)
         extras["dsv2lite_int4_channels"].append(r)
         log(f"[bench] channels {json.dumps(r)}")
+    # base-3 ternary rows against 2-bit ternary rows on the gathered-channel
+    # path: the switch-base layer whole (every channel of the routed expert)
+    # and the DeepSeek-V2-Lite shape in ternary at the 18% budget
+    extras["ternary_base3_channels"] = base3_channel_times(rb)
     # shared logits: every selected expert receives M = T rows (the M-sweep)
     extras["dsv2lite_int4_shared_M_sweep"] = []
     for t in (1, 2, 3, 4, 5, 8, 10, 16, 32):
