@@ -256,6 +256,7 @@ struct Plan {
   int mmax, mmax1, mmax2, ks1, ks2, tn1, tn2, max_active, max_tiles, tile_rows;
   int route_fused;
   int fc1_routes;  // GEMV path: FC1 routes the tokens itself (no routing kernel)
+  int fc2_cat;     // GEMV path, one token, k > 1: FC2 over the k experts' concatenated K writes y (no combine)
   bool softmax_all;  // unnormalised top-k weights, computed by the routing top-k
   int launches;
   std::string kernels;
@@ -282,7 +283,8 @@ int32_t path_row_bound(const qmoe_layer_desc &d, int path_req) {
   return INT32_MAX;
 }
 
-qmoe_status make_plan(const qmoe_layer_desc &d, int32_t T, int32_t k, int path_req, bool softmax_all, Plan &p) {
+qmoe_status make_plan(const qmoe_layer_desc &d, int32_t T, int32_t k, int path_req, bool softmax_all, bool fc2_bias,
+                      Plan &p) {
   const MoeLayout L = MoeLayout::make(d);
   p = Plan{};
   int path = path_req;
@@ -318,20 +320,33 @@ qmoe_status make_plan(const qmoe_layer_desc &d, int32_t T, int32_t k, int path_r
   p.mmax = p.mmax1 = p.mmax2 = T;  // no expert gets more rows than there are tokens
   const GemvShape g1 = pick_gemv((int64_t)p.max_active * L.fc1.RG, L.fc1, T,
                                  p.fc1_routes ? kEpiSwiGLURouted : kEpiSwiGLU, gemv_in_mode(d.act_dtype));
-  const GemvShape g2 = pick_gemv((int64_t)p.max_active * L.fc2.RG, L.fc2, T, kEpiDown, 0);
+  // one token with k > 1 (16-bit y, no FC2 bias): FC2 runs over the k
+  // matrices end to end, routing weights in the block scales, and writes y
+  p.fc2_cat = (T == 1 && k > 1 && d.act_dtype != QMOE_DTYPE_F32 && !fc2_bias) ? 1 : 0;
+  MatLayout L2 = L.fc2;
+  if (p.fc2_cat) L2.NKT *= k;  // the K split of the concatenated matrices
+  const GemvShape g2 = p.fc2_cat ? pick_gemv(L.fc2.RG, L2, T, kEpiDownCat, 0)
+                                 : pick_gemv((int64_t)p.max_active * L.fc2.RG, L.fc2, T, kEpiDown, 0);
   p.ks1 = g1.waves;
   p.tn1 = g1.tn;
   p.ks2 = g2.waves;
   p.tn2 = g2.tn;
+  // concatenated FC2: the same number of waves on each expert matrix (the
+  // most that fit a workgroup of kGemvCatMaxWaves), so that no wave's range
+  // crosses from one expert to the next
+  if (p.fc2_cat && k <= kGemvCatMaxWaves) {
+    const int m = kGemvCatMaxWaves / k;
+    if (gemv_lds_bytes(T, kEpiDownCat, k * m, p.tn2) <= kLdsLimit) p.ks2 = k * m;
+  }
   // top-1: the down GEMV writes y; otherwise a combine kernel follows
   // the weights of SOFTMAX_ALL replace the routing's weights once the ids
   // exist, before the first reader of the weights (FC2 or the combine)
   p.softmax_all = softmax_all;
   // f32 activations: a split pass first, and y always from the combine
-  const bool combine = k > 1 || f32;
+  const bool combine = (k > 1 || f32) && !p.fc2_cat;
   const std::string act = d.activation == QMOE_ACT_RELU ? "relu" : "swiglu";
   p.kernels = std::string(f32 ? "split_x," : "") + (p.fc1_routes ? "route_fc1_" + act : "route,gemv_fc1_" + act) +
-              ",gemv_fc2" + (combine ? ",combine" : "");
+              (p.fc2_cat ? ",gemv_fc2_combine" : ",gemv_fc2") + (combine ? ",combine" : "");
   p.launches = (p.fc1_routes ? 2 : 3) + (combine ? 1 : 0) + (f32 ? 1 : 0);
   return ok();
 }
@@ -508,14 +523,14 @@ struct Tiling {
 };
 
 qmoe_status tile_need(const qmoe_layer_desc &d, int32_t T, int32_t k, int path_req, bool softmax_all,
-                      int32_t R, Tiling &t) {
+                      bool fc2_bias, int32_t R, Tiling &t) {
   t = Tiling{};
   t.rows = R;
   t.tiles = (int32_t)(((int64_t)T + R - 1) / R);
   const int32_t last = T - (t.tiles - 1) * R;  // in [1, R]
   Plan pf, pl;
-  qmoe_status st = make_plan(d, R, k, path_req, softmax_all, pf);
-  if (st == QMOE_OK) st = make_plan(d, last, k, path_req, softmax_all, pl);
+  qmoe_status st = make_plan(d, R, k, path_req, softmax_all, fc2_bias, pf);
+  if (st == QMOE_OK) st = make_plan(d, last, k, path_req, softmax_all, fc2_bias, pl);
   if (st != QMOE_OK) return st;
   t.ws = std::max(MoeWs::make(d, R, k, pf.path == QMOE_PATH_GROUPED).total,
                   MoeWs::make(d, last, k, pl.path == QMOE_PATH_GROUPED).total);
@@ -529,13 +544,13 @@ qmoe_status tile_need(const qmoe_layer_desc &d, int32_t T, int32_t k, int path_r
 // GEMV path), then while a full tile's or the final tile's workspace exceeds
 // `limit` (0: no limit).
 qmoe_status pick_tiling(const qmoe_layer_desc &d, int32_t T, int32_t k, int path_req, bool softmax_all,
-                        int64_t limit, Tiling &t) {
+                        bool fc2_bias, int64_t limit, Tiling &t) {
   int32_t R = T;
   const int32_t bound = path_row_bound(d, path_req);
   if (path_req == QMOE_PATH_AUTO || limit > 0)
     while (R > bound) R = (R + 1) / 2;
   for (;;) {
-    qmoe_status st = tile_need(d, T, k, path_req, softmax_all, R, t);
+    qmoe_status st = tile_need(d, T, k, path_req, softmax_all, fc2_bias, R, t);
     if (st != QMOE_OK) return st;
     if (limit <= 0 || t.ws <= limit) return QMOE_OK;
     if (R == 1)
@@ -569,12 +584,13 @@ qmoe_status qmoe_forward_plan(const qmoe_layer_desc *desc, int32_t T, int32_t to
   tl.rows = T;
   tl.tiles = T == 0 ? 0 : 1;
   if (tiled) {
-    st = pick_tiling(*desc, T, top_k, opts ? opts->path : QMOE_PATH_AUTO, softmax_all,
+    st = pick_tiling(*desc, T, top_k, opts ? opts->path : QMOE_PATH_AUTO, softmax_all, opts && opts->fc2_bias,
                      opts ? opts->workspace_limit : 0, tl);
     if (st != QMOE_OK) return st;
   }
   Plan p;
-  st = make_plan(*desc, tl.rows, top_k, opts ? opts->path : QMOE_PATH_AUTO, softmax_all, p);
+  st = make_plan(*desc, tl.rows, top_k, opts ? opts->path : QMOE_PATH_AUTO, softmax_all,
+                 opts && opts->fc2_bias, p);
   if (st != QMOE_OK) return st;
   memset(plan, 0, sizeof *plan);
   plan->path = p.path;
@@ -621,7 +637,7 @@ qmoe_status qmoe_forward_ex(const qmoe_layer_desc *desc, const void *packed, con
   const bool softmax_all = opts && opts->topk_weights == QMOE_TOPK_SOFTMAX_ALL;
   if (call_tiled(*desc, T, opts)) {
     Tiling tl;
-    st = pick_tiling(*desc, T, top_k, opts ? opts->path : QMOE_PATH_AUTO, softmax_all,
+    st = pick_tiling(*desc, T, top_k, opts ? opts->path : QMOE_PATH_AUTO, softmax_all, opts && opts->fc2_bias,
                      opts ? opts->workspace_limit : 0, tl);
     if (st != QMOE_OK) return st;
     if (tl.tiles > 1) {
@@ -658,7 +674,7 @@ qmoe_status qmoe_forward_ex(const qmoe_layer_desc *desc, const void *packed, con
     }
   }
   Plan p;
-  st = make_plan(*desc, T, top_k, opts ? opts->path : QMOE_PATH_AUTO, softmax_all, p);
+  st = make_plan(*desc, T, top_k, opts ? opts->path : QMOE_PATH_AUTO, softmax_all, opts && opts->fc2_bias, p);
   if (st != QMOE_OK) return st;
   if (!packed || !x || !logits || !y || !ws)
     return fail(QMOE_ERR_INVALID_ARGUMENT, "null device pointer");
@@ -836,11 +852,15 @@ qmoe_status qmoe_forward_ex(const qmoe_layer_desc *desc, const void *packed, con
   g2.act_dtype = desc->act_dtype;
   g2.bias = opts ? (const uint16_t *)opts->fc2_bias : nullptr;
   g2.route_w = ra.r.w;
+  g2.route = ra.r;
+  g2.route_k = top_k;
   e = begin();
-  if (e == hipSuccess) e = launch_gemv(g2, kEpiDown, 0, p.mmax2, p.ks2, p.tn2, L.fc2.block, p.max_active, s);
+  if (e == hipSuccess)
+    e = p.fc2_cat ? launch_gemv(g2, kEpiDownCat, 0, 1, p.ks2, p.tn2, L.fc2.block, 1, s)
+                  : launch_gemv(g2, kEpiDown, 0, p.mmax2, p.ks2, p.tn2, L.fc2.block, p.max_active, s);
   if (e == hipSuccess) e = end();
   if (e != hipSuccess) return hip_status(e, "gemv fc2");
-  if (top_k > 1 || f32) {
+  if ((top_k > 1 || f32) && !p.fc2_cat) {
     e = begin();
     if (e == hipSuccess) e = launch_combine(o, ra.r.slot_pos, ra.r.w, T, top_k, desc->hidden, desc->act_dtype, y, s);
     if (e == hipSuccess) e = end();

@@ -119,7 +119,7 @@ __device__ inline void load_scales(__amdgpu_buffer_rsrc_t r, int voff, int soff,
 // MR: accumulator rows kept per lane (1: a single row, 4: up to 16 rows per
 // tile); MT: 16-row tiles; BLOCK: scale block along K.
 template <int QT, bool XF16, int PARTS, int EPI, int MR, int MT, int BLOCK, int TN, bool EXT>
-__global__ __launch_bounds__(512) void gemv_kernel(const GemvArgs a) {
+__global__ __launch_bounds__(EPI == kEpiDownCat ? 64 * kGemvCatMaxWaves : 512) void gemv_kernel(const GemvArgs a) {
   using TR = QtTraits<QT>;
   using CD = Codec<TR::kBits, XF16>;
   constexpr int BITS = TR::kBits;
@@ -149,11 +149,16 @@ __global__ __launch_bounds__(512) void gemv_kernel(const GemvArgs a) {
 
   constexpr bool ROUTED = EPI == kEpiSwiGLURouted;
   constexpr bool SWIGLU = EPI == kEpiSwiGLU || ROUTED;
+  constexpr bool CAT = EPI == kEpiDownCat;  // one token's k experts as one concatenated K
   // routed: this workgroup's expert and the flat slots of its rows
   __shared__ int32_t s_rslot[ROUTED ? kGemvMaxRows : 1];
   __shared__ int32_t s_ids[ROUTED ? kLanes : 1];  // routed: expert of each flat slot
   int e, M, pbase;
-  if (a.dense_M > 0) {
+  if (CAT) {
+    e = 0;  // per k segment below
+    M = 1;
+    pbase = 0;
+  } else if (a.dense_M > 0) {
     e = 0;
     M = a.dense_M;
     pbase = 0;
@@ -199,7 +204,20 @@ __global__ __launch_bounds__(512) void gemv_kernel(const GemvArgs a) {
   if (M > 16 * MT) M = 16 * MT;  // the host sizes MT for every row count; the clamp keeps accesses in bounds
   const int r = lane & 15, g = lane >> 4;
   const int NKT = (int)a.NKT, NC = (int)a.NC;
-  const int kt0 = (int)((int64_t)wave * NKT / KS), kt1 = (int)((int64_t)(wave + 1) * NKT / KS);
+  // this wave's k-tiles: of the matrix, or (CAT) of the k matrices end to end
+  const int NKW = CAT ? NKT * a.route_k : NKT;
+  const int kw0 = (int)((int64_t)wave * NKW / KS), kw1 = (int)((int64_t)(wave + 1) * NKW / KS);
+  // CAT: the routing entries of the wave's first matrix, loaded before the
+  // set-up below so that their latency overlaps it
+  int cat_e0 = 0;
+  float cat_w0 = 0.f;
+  int cat_p0 = 0;
+  if constexpr (CAT) {
+    const int j0 = min(kw0 / NKT, a.route_k - 1);
+    cat_e0 = a.route.ids[j0];
+    cat_w0 = a.route.w[j0];
+    cat_p0 = a.route.slot_pos[j0];
+  }
 
   // A operand rows: lane (r, g) supplies row 16 mt + r.  Rows past M read
   // row 0 instead: an A row only feeds the output row of the same index,
@@ -211,18 +229,27 @@ __global__ __launch_bounds__(512) void gemv_kernel(const GemvArgs a) {
     const int m = m0 < M ? m0 : 0;
     int64_t row = 0;
     {
-      if (a.dense_M > 0) row = m;
+      if (CAT) row = 0;  // per k segment below
+      else if (a.dense_M > 0) row = m;
       else if constexpr (ROUTED) row = s_rslot[m] / a.route_k;
       else row = a.in_gather_token ? (int64_t)a.token_of[pbase + m] : (int64_t)(pbase + m);
     }
     arow[mt] = a.in + row * a.in_row_pairs;
   }
 
-  // this row group's codes (NKT x 4 KiB) and scales (NKT x 64 rows x BPK entries)
-  const uint8_t *wexp = a.w + (int64_t)e * a.expert_stride;
-  const __amdgpu_buffer_rsrc_t wrs = make_rsrc(wexp + (int64_t)rg * NKT * (4 * kLanes * 16), (uint32_t)NKT * (4 * kLanes * 16));
-  const __amdgpu_buffer_rsrc_t srs = make_rsrc(wexp + a.scales_off + (int64_t)rg * NKT * kLanes * (BPK * ESZ),
-                                               (uint32_t)NKT * kLanes * (BPK * ESZ));
+  // this row group's codes (NKT x 4 KiB) and scales (NKT x 64 rows x BPK
+  // entries) of expert e (CAT: reset for each segment's expert)
+  auto code_rsrc = [&](int ex) {
+    return make_rsrc(a.w + (int64_t)ex * a.expert_stride + (int64_t)rg * NKT * (4 * kLanes * 16),
+                     (uint32_t)NKT * (4 * kLanes * 16));
+  };
+  auto scale_rsrc = [&](int ex) {
+    return make_rsrc(a.w + (int64_t)ex * a.expert_stride + a.scales_off + (int64_t)rg * NKT * kLanes * (BPK * ESZ),
+                     (uint32_t)NKT * kLanes * (BPK * ESZ));
+  };
+  __amdgpu_buffer_rsrc_t wrs = code_rsrc(e);
+  __amdgpu_buffer_rsrc_t srs = scale_rsrc(e);
+  float wseg = 1.f;  // CAT: the routing weight of the segment's expert
   const int wvoff = lane * 16, svoff = r * (BPK * ESZ);
   const uint32_t smask = opaque_v(a.sdtype == QMOE_DTYPE_F16 ? 0xFFFFFFFFu : 0u);
 
@@ -334,9 +361,13 @@ __global__ __launch_bounds__(512) void gemv_kernel(const GemvArgs a) {
 #pragma unroll
           for (int t = 0; t < TN; ++t) {
             const uint32_t ent = ESZ == 4 ? T.sv[t][bi] : ((T.sv[t][bi / 2] >> (16 * (bi % 2))) & 0xFFFFu);
-            const float s = half_to_f32_sel(ent & 0xFFFFu, smask);
+            float s = half_to_f32_sel(ent & 0xFFFFu, smask);
             float b = 0.f;
             if constexpr (AFF) b = half_to_f32_sel(ent >> 16, smask);
+            if constexpr (CAT) {  // the segment's routing weight scales the block's whole term
+              s *= wseg;
+              b *= wseg;
+            }
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -364,46 +395,67 @@ __global__ __launch_bounds__(512) void gemv_kernel(const GemvArgs a) {
   // one k-tile at a time.
   static_assert(QMOE_GEMV_PREFETCH == 0 || QMOE_GEMV_PREFETCH == 1, "QMOE_GEMV_PREFETCH is 0 or 1");
   constexpr int PF = MT > 1 ? 0 : QMOE_GEMV_PREFETCH;
-  const int ktf = min(kt1, NC / 4);  // end of this wave's whole k-tiles
   Tile TA, TB;
-  if constexpr (PF == 0) {
-    for (int kt = kt0; kt < ktf; ++kt) {
-      load_a(kt, TA);
-      load_w(kt, TA);
-      compute(kt, TA);
-    }
-  } else if (kt0 < ktf) {
-    int kt = kt0;
-    if ((ktf - kt0) & 1) {  // odd count: one k-tile without prefetch first
-      load_a(kt, TA);
-      load_w(kt, TA);
-      compute(kt, TA);
-      ++kt;
-    }
-    if (kt < ktf) {
-      const int last = ktf - 1;
-      load_w(kt, TA);
-      // the fences keep the scheduler from starting a k-tile's decode before
-      // the loads issued ahead of it, which would wait for the prefetch
-      for (; kt < ktf; kt += 2) {
+  auto kloop = [&](const int kt0, const int kt1) __attribute__((always_inline)) {
+    const int ktf = min(kt1, NC / 4);  // end of this wave's whole k-tiles
+    if constexpr (PF == 0) {
+      for (int kt = kt0; kt < ktf; ++kt) {
         load_a(kt, TA);
-        load_w(kt + 1, TB);
-        __builtin_amdgcn_sched_barrier(0);
+        load_w(kt, TA);
         compute(kt, TA);
-        __builtin_amdgcn_sched_barrier(0);
-        load_a(kt + 1, TB);
-        load_w(min(kt + 2, last), TA);
-        __builtin_amdgcn_sched_barrier(0);
-        compute(kt + 1, TB);
-        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else if (kt0 < ktf) {
+      int kt = kt0;
+      if ((ktf - kt0) & 1) {  // odd count: one k-tile without prefetch first
+        load_a(kt, TA);
+        load_w(kt, TA);
+        compute(kt, TA);
+        ++kt;
+      }
+      if (kt < ktf) {
+        const int last = ktf - 1;
+        load_w(kt, TA);
+        // the fences keep the scheduler from starting a k-tile's decode before
+        // the loads issued ahead of it, which would wait for the prefetch
+        for (; kt < ktf; kt += 2) {
+          load_a(kt, TA);
+          load_w(kt + 1, TB);
+          __builtin_amdgcn_sched_barrier(0);
+          compute(kt, TA);
+          __builtin_amdgcn_sched_barrier(0);
+          load_a(kt + 1, TB);
+          load_w(min(kt + 2, last), TA);
+          __builtin_amdgcn_sched_barrier(0);
+          compute(kt + 1, TB);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
     }
-  }
-  // the partial last k-tile of the matrix, when it is this wave's
-  for (int kt = max(kt0, ktf); kt < kt1; ++kt) {
-    load_a_partial(kt, TA);
-    load_w(kt, TA);
-    compute(kt, TA);
+    // the partial last k-tile of the matrix, when it is this wave's
+    for (int kt = max(kt0, ktf); kt < kt1; ++kt) {
+      load_a_partial(kt, TA);
+      load_w(kt, TA);
+      compute(kt, TA);
+    }
+  };
+  if constexpr (CAT) {
+    // the wave's range over the k matrices: each overlapped matrix j with its
+    // expert's weights, the token's h row of slot j and w_j (the first
+    // matrix's routing entries were loaded at the start of the kernel)
+    for (int j = kw0 / NKT; j < a.route_k && j * NKT < kw1; ++j) {
+      const int lo = max(kw0, j * NKT) - j * NKT, hi = min(kw1, (j + 1) * NKT) - j * NKT;
+      const bool first = j == kw0 / NKT;
+      const int ej = __builtin_amdgcn_readfirstlane(first ? cat_e0 : a.route.ids[j]);
+      wrs = code_rsrc(ej);
+      srs = scale_rsrc(ej);
+      wseg = first ? cat_w0 : a.route.w[j];
+      const int64_t prow = first ? cat_p0 : a.route.slot_pos[j];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) arow[mt] = a.in + prow * a.in_row_pairs;
+      kloop(lo, hi);
+    }
+  } else {
+    kloop(kw0, kw1);
   }
 
   // cross-wave reduction in a fixed order, then the epilogue
@@ -457,6 +509,8 @@ __global__ __launch_bounds__(512) void gemv_kernel(const GemvArgs a) {
           a.h_dbg[slot_of_row * Ih + i] = h;
         }
       }
+    } else if constexpr (CAT) {
+      if (valid) a.out_act[n] = f32_to_act(v, a.act_dtype == QMOE_DTYPE_F16);  // y of the one token
     } else {
       if (valid) {
         if (a.top_k == 1) {
@@ -508,6 +562,8 @@ const void *gemv_ptr_qt(int epilogue, int in_f16, int rows, int block, int tn, i
   if (epilogue == kEpiDown)
     return ext ? gemv_ptr_rows<QT, false, 2, kEpiDown, true>(rows, block, tn)
                : gemv_ptr_rows<QT, false, 2, kEpiDown, false>(rows, block, tn);
+  if (epilogue == kEpiDownCat)  // one token, no expert bias
+    return (ext || rows > 1) ? nullptr : gemv_ptr_block<QT, false, 2, kEpiDownCat, 1, 1, false>(block, tn);
   if (epilogue == kEpiSwiGLU)
     return ext ? gemv_ptr_fc1<QT, kEpiSwiGLU, true>(in_f16, rows, block, tn)
                : gemv_ptr_fc1<QT, kEpiSwiGLU, false>(in_f16, rows, block, tn);

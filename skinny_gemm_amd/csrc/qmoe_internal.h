@@ -197,7 +197,10 @@ struct RouteArgs {
 // kFc1RouteMaxSlots) whose workgroups route the tokens themselves (no
 // routing kernel); workgroup 0 also writes the routing lists for FC2, the
 // combine and the diagnostics.
-enum GemvEpilogue { kEpiSwiGLU = 0, kEpiDown = 1, kEpiStoreAct = 2, kEpiSwiGLURouted = 3 };
+// kEpiDownCat: FC2 of one token with k > 1 as one GEMV over the concatenated
+// k expert matrices (the routing weight folded into each block's scale), so
+// y is written directly and no combine follows.
+enum GemvEpilogue { kEpiSwiGLU = 0, kEpiDown = 1, kEpiStoreAct = 2, kEpiSwiGLURouted = 3, kEpiDownCat = 4 };
 // Input of the FC1 epilogues (the in_f16 argument of launch_gemv): 0 bf16
 // rows, 1 f16 rows, kGemvInSplitF32 f32 rows given as bf16 hi + lo parts.
 constexpr int kGemvInSplitF32 = 2;
@@ -242,6 +245,7 @@ struct GemvArgs {
 // dense inputs.
 constexpr int kGemvMaxRowsDense = 32;
 constexpr int kGemvMaxWaves = 8;
+constexpr int kGemvCatMaxWaves = 16;  // concatenated FC2: k x (waves per expert) <= 16
 
 // Dynamic LDS of one GEMV workgroup: the cross-wave partial sums of the
 // tn n-tiles x row tiles x accumulator elements x 64 lanes.

@@ -131,8 +131,9 @@ def test_plan_gemv_decode():
     # up to 64 routed slots: FC1 routes the tokens itself
     p = q.forward_plan(_desc(), 1, 6)
     assert p["path"] == 1 and p["gemv_mmax"] == 1 and p["max_active"] == 6
-    assert p["kernels"] == ["route_fc1_swiglu", "gemv_fc2", "combine"]
-    assert p["num_launches"] == 3
+    # one token, k > 1: FC2 over the six experts' concatenated K writes y
+    assert p["kernels"] == ["route_fc1_swiglu", "gemv_fc2_combine"]
+    assert p["num_launches"] == 2
     p1 = q.forward_plan(_desc(), 1, 1)
     assert p1["kernels"] == ["route_fc1_swiglu", "gemv_fc2"] and p1["num_launches"] == 2
     p2 = q.forward_plan(_desc(), 2, 6)
