@@ -1,6 +1,7 @@
 """GPU parity of the dense skinny-M quantized matmul (HIP kernels through the
 C ABI) against the oracle."""
 
+import os
 import sys
 
 import numpy as np
@@ -42,6 +43,21 @@ def _layer(spec, N, seed):
         f = spec.fmt
         _cache[key] = (w, QLinear(f.fmt, f.block, f.scale_dtype, N, spec.K, w["codes"], w["scales"], w["biases"]))
     return _cache[key]
+
+
+# host threads for the oracle (the GPU machine's CPU share is 16 cores)
+ORACLE_THREADS = max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def oracle_rows_parallel(inp, N, chunk=8192):
+    """oracle.linear over all N rows in chunks on ORACLE_THREADS host threads
+    (the C call releases the GIL; each chunk is its own row range)."""
+    from concurrent.futures import ThreadPoolExecutor
+    spans = [(n0, min(N, n0 + chunk)) for n0 in range(0, N, chunk)]
+    with ThreadPoolExecutor(ORACLE_THREADS) as ex:
+        parts = list(ex.map(lambda sp: oracle.linear(inp, sp[0], sp[1]), spans))
+    return {"y": np.concatenate([p["y"] for p in parts], axis=1),
+            "y64": np.concatenate([p["y64"] for p in parts], axis=1)}
 
 
 def run_linear(spec, N, M, seed=0, rows=None, path="auto"):
@@ -122,6 +138,24 @@ def test_dense_unpack_bit_exact(N):
 @pytest.mark.parametrize("M", [17, 32, 64])
 def test_dense_affine2_17408_mfma(M):
     run_linear(DENSE, 17408, M)
+
+
+@pytest.mark.parametrize("M", [1, 4])
+def test_dense_affine2_248320_all_rows(M):
+    """The 248320-row matrix compared on every output row (the oracle in
+    parallel row chunks)."""
+    from skinny_gemm_amd.layer import to_device_bits, bits_of
+    N = 248320
+    log(f"[linear] all rows N={N} M={M} threads={ORACLE_THREADS}")
+    w, lin = _layer(DENSE, N, 0)
+    inp = synth.linear_inputs(DENSE, N, M, 0, weights=False)
+    inp.update(codes=w["codes"], scales=w["scales"], biases=w["biases"])
+    y = lin(to_device_bits(inp["x"], DENSE.act_dtype), DENSE.act_dtype)
+    torch.cuda.synchronize()
+    ref = oracle_rows_parallel(inp, N)
+    res = compare(bits_of(y), ref["y"], ref["y64"], DENSE.act_dtype)
+    log(f"       max_row_rel={res['max_row_rel']:.3e} identical={res['frac_identical']:.4f}")
+    assert res["ok"], res
 
 
 def test_dense_affine2_248320_m32_sampled_rows():
