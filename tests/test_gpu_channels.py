@@ -202,3 +202,12 @@ def test_channels_base3_invalid_bytes_rejected():
     src = [to_device_bits(inp[k], None) for k in ("fc1_codes", "fc1_scales", "down_codes", "down_scales")]
     with pytest.raises(q.QmoeError, match="2 base-3 bytes"):
         q.channel_prepack(desc, *src, packed)
+
+
+@pytest.mark.parametrize("fmt", ["sym_int4", "ternary_b3"])
+def test_channels_many_experts_and_top16(fmt):
+    """E = 128 (the routing wave then takes two logits per lane and the k
+    rounds of arg-max instead of the per-lane rank count) and top-16 routing,
+    for 16-bit and base-3 rows."""
+    run_case(custom_moe_spec(128, 640, 128, 16, fc1=fmt, fc2=fmt, block1=128), 3, 31, 0.15)
+    run_case(custom_moe_spec(256, 512, 128, 4, fc1=fmt, fc2=fmt, block1=128), 2, 32, 0.3)
