@@ -145,7 +145,8 @@ __global__ __launch_bounds__(256) void wscale_final_kernel(MatLayout L, float *_
 
 hipError_t launch_grouped(const GroupedArgs &a, int epilogue, int grid_tiles, hipStream_t s) {
   // the kernel's tile width (FC2 with its fp32 per-slot output has a shape of its own)
-  const int tw = 64 * grouped_shape(qtype_affine(a.qtype), a.tile_rows, epilogue == kGEpiStoreF32).nj;
+  const GroupedShape sh = grouped_shape(qtype_affine(a.qtype), a.tile_rows, epilogue == kGEpiStoreF32);
+  const int tw = sh.nw * 16 * sh.nj;
   const int ntn = (int)((a.N + tw - 1) / tw);
   const int grid = grid_tiles * ntn;
   if (grid == 0) return hipSuccess;

@@ -60,6 +60,8 @@ __device__ inline float pow2_below(float amax, int lim) {
 }
 
 // ---------------------------------------------------------------- GEMM
+// s_waitcnt immediate of gfx9: vmcnt 0, expcnt and lgkmcnt at their maxima
+constexpr int kWaitVmcnt0 = 0x0F70;
 constexpr int kMaxAffineBlocks = kGroupedMaxAffineBlocks;
 
 // Input modes: 16-bit rows (bf16 or f16) scaled while staged, fp32 rows
@@ -73,8 +75,9 @@ enum { kInBf16 = 0, kInF16 = 1, kInF32 = 2, kInScaled = 3 };
 // SPLIT: f16 scales of a multi-bit format, split into a head and a tail
 // (two MFMAs per weight fragment); an instance of its own, so the common
 // case keeps no registers for the tail.
-template <int QT, int EPI, int INM, int MI, int NJ, int KT, bool SPLIT>
-__global__ __launch_bounds__(256, MI == 8 ? QMOE_GROUPED_WG_PER_CU : 1) void grouped_kernel(const GroupedArgs a) {
+template <int QT, int EPI, int INM, int MI, int NJ, int KT, int NW, bool SPLIT>
+__global__ __launch_bounds__(64 * NW, MI == 8 && QMOE_GROUPED_WG_PER_CU * 4 >= NW ? QMOE_GROUPED_WG_PER_CU * 4 / NW : 1) void grouped_kernel(
+    const GroupedArgs a) {
   constexpr bool IN_F32 = INM == kInF32, IN_F16 = INM == kInF16, PRE = INM == kInScaled;
   using TR = QtTraits<QT>;
   using CD = Codec<TR::kBits, true>;
@@ -88,7 +91,9 @@ __global__ __launch_bounds__(256, MI == 8 ? QMOE_GROUPED_WG_PER_CU : 1) void gro
   static_assert(MI == 4 || MI == 8, "row tiles per wave");
   static_assert(NJ == 2 || NJ == 4, "column slices per wave");
   static_assert(KT == 64 || KT == 128, "k per staged tile");
-  static_assert(!AFF || MI == 4, "affine block sums are laid out for 64-row tiles");
+  static_assert(!AFF || (MI == 4 && NW == 4), "affine block sums are laid out for 64-row tiles, 4 threads a row");
+  static_assert(NW == 4 || NW == 8 || NW == 16, "waves per workgroup");
+  constexpr int NT = 64 * NW;          // threads per workgroup
   // codes enter the MFMA as q = u - zc: the symmetric codes, and affine codes
   // recentred to [-2^(b-1), 2^(b-1)-1] (bias b + zc*s added in the epilogue)
   constexpr int ZC = AFF ? (1 << (TR::kBits - 1)) : TR::kZeroPoint;
@@ -103,15 +108,28 @@ __global__ __launch_bounds__(256, MI == 8 ? QMOE_GROUPED_WG_PER_CU : 1) void gro
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  constexpr int TW = 4 * 16 * NJ;  // outputs per tile
+  constexpr int TW = NW * 16 * NJ;  // outputs per tile
   const int ntn = (int)((a.N + TW - 1) / TW);
 
-  // XCD-aware remap: blocks are dealt round-robin to 8 XCDs; give each XCD a
-  // contiguous range of tiles (n-tile major, row tiles of an expert adjacent)
+  // XCD-aware order: blocks are dealt round-robin to the 8 XCDs.  The work
+  // items (row tile, column tile) run row-tile major, and each XCD takes a
+  // contiguous eighth of them: the column tiles of one row tile run together
+  // on one XCD, so its L2 serves the staged activation rows to all of them
+  // (and the weights to the next row tile of the same expert).  The grid
+  // holds the upper bound of routed tiles; blocks past the actual number exit.
   const int G = gridDim.x;
-  const int bid = (G % 8 == 0) ? ((int)(blockIdx.x % 8) * (G / 8) + (int)(blockIdx.x / 8)) : (int)blockIdx.x;
-  const int tiles_m = G / ntn;
-  const int nt = bid / tiles_m, tile = bid - nt * tiles_m;
+  const int ntiles = a.dense_M > 0 ? G / ntn : a.tile_info[0].w;
+  const int total = ntiles * ntn;
+  int bid;
+  if (G % 8 == 0) {
+    const int chunk = (total + 7) / 8;
+    const int r = (int)(blockIdx.x / 8);
+    bid = r < chunk ? (int)(blockIdx.x % 8) * chunk + r : total;
+  } else {
+    bid = (int)blockIdx.x;
+  }
+  if (bid >= total) return;
+  const int tile = bid / ntn, nt = bid - tile * ntn;
 
   int e, p0, rows;
   if (a.dense_M > 0) {
@@ -181,7 +199,7 @@ __global__ __launch_bounds__(256, MI == 8 ? QMOE_GROUPED_WG_PER_CU : 1) void gro
       for (int j = 0; j < NJ; ++j) acc[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
     // staging assignment: TPR threads per row, KT/TPR consecutive k each
-    constexpr int TPR = 256 / TM;
+    constexpr int TPR = NT / TM;
     constexpr int SEG = KT / TPR;
     const int st_r = threadIdx.x / TPR, st_k = (threadIdx.x % TPR) * SEG;
     const int st_in = s_row[st_r];
@@ -203,6 +221,10 @@ __global__ __launch_bounds__(256, MI == 8 ? QMOE_GROUPED_WG_PER_CU : 1) void gro
     // scaled f16 into LDS buffer `buf` (zeros past the rows or past K), and
     // the affine block sums of the scaled values
     auto stage_store = [&](int64_t kt, const uint4 (&S)[SV], int buf) __attribute__((always_inline)) {
+      // every load of the tile has arrived (the weights were issued first), on
+      // every path: the compiler's wait counting then knows that nothing is
+      // in flight when the next k-tile's compute() reads the weight registers
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
       // 16-B LDS stores of 8 converted values each
       half8_t *dst = reinterpret_cast<half8_t *>(&sA[buf][0][st_r][st_k]);
       half8_t *dlo = reinterpret_cast<half8_t *>(&sA[buf][NPART - 1][st_r][st_k]);
@@ -282,7 +304,10 @@ __global__ __launch_bounds__(256, MI == 8 ? QMOE_GROUPED_WG_PER_CU : 1) void gro
     // its block within the k-tile is (c >> log2(chunks per block)) & (bpk - 1)
     const int cpb_log = __builtin_ctz((unsigned)(a.block / KC));
     const int bpk = a.bpk;
-    auto load_b = [&](int64_t kt, uint32_t (&bw)[CPT][NJ], uint32_t (&sv)[CPT][NJ]) __attribute__((always_inline)) {
+    // scale entries stay 16-bit until compute() widens them: a widening at the
+    // load would make the loop wait for the prefetched scales at once
+    using ST = std::conditional_t<AFF, uint32_t, uint16_t>;
+    auto load_b = [&](int64_t kt, uint32_t (&bw)[CPT][NJ], ST (&sv)[CPT][NJ]) __attribute__((always_inline)) {
       static_for<CPT>([&](auto cc) {
         constexpr int c = decltype(cc)::value;
         const int chunk = min((int)(kt / KC) + c, (int)a.NC - 1);
@@ -293,13 +318,13 @@ __global__ __launch_bounds__(256, MI == 8 ? QMOE_GROUPED_WG_PER_CU : 1) void gro
         for (int j = 0; j < NJ; ++j) {
           const int wj = wso + j * (kLanes * 16), sj = sso + j * 16 * bpk * SES;
           bw[c][j] = __builtin_amdgcn_raw_buffer_load_b32(wrs, wvo, wj, 0);
-          sv[c][j] = AFF ? __builtin_amdgcn_raw_buffer_load_b32(srs, svo, sj, 0)
-                         : (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(srs, svo, sj, 0);
+          if constexpr (AFF) sv[c][j] = __builtin_amdgcn_raw_buffer_load_b32(srs, svo, sj, 0);
+          else sv[c][j] = __builtin_amdgcn_raw_buffer_load_b16(srs, svo, sj, 0);
         }
       });
     };
     const RegConsts<CD::kNC> dk = CodecOps<CD>::in_registers();  // decoder constants in registers
-    auto compute = [&](int buf, const uint32_t (&bw)[CPT][NJ], const uint32_t (&sv)[CPT][NJ])
+    auto compute = [&](int buf, const uint32_t (&bw)[CPT][NJ], const ST (&sv)[CPT][NJ])
                        __attribute__((always_inline)) {
       // per chunk and slice: the pre-scaled f16 scale (head) and its tail,
       // once per tile
@@ -349,7 +374,7 @@ __global__ __launch_bounds__(256, MI == 8 ? QMOE_GROUPED_WG_PER_CU : 1) void gro
         // the A fragments of row tile i + 2 are read while row tile i's
         // MFMAs run (three fragments in flight), and scheduling fences keep
         // that order, so at most three fragments are held in registers
-        constexpr int AD = 2;
+        constexpr int AD = QMOE_GROUPED_AD;
         half8_t af[AD][NPART];
         auto read_a = [&](int i, half8_t(&d)[NPART]) __attribute__((always_inline)) {
 #pragma unroll
@@ -374,7 +399,8 @@ __global__ __launch_bounds__(256, MI == 8 ? QMOE_GROUPED_WG_PER_CU : 1) void gro
     // Two-stage pipeline over the k-tiles: the next tile's weights, scales and
     // activations are loaded while the current one is multiplied; one barrier
     // per tile (the staged buffers alternate).
-    uint32_t bwA[CPT][NJ], svA[CPT][NJ], bwB[CPT][NJ], svB[CPT][NJ];
+    uint32_t bwA[CPT][NJ], bwB[CPT][NJ];
+    ST svA[CPT][NJ], svB[CPT][NJ];
     uint4 S[SV];
     load_b(0, bwA, svA);
     stage_load(0, S);
@@ -490,6 +516,7 @@ __global__ __launch_bounds__(256, MI == 8 ? QMOE_GROUPED_WG_PER_CU : 1) void gro
 
 template <int QT, int EPI, bool MAIN, bool SPLIT>
 hipError_t launch_grouped_split(const GroupedArgs &a, int grid, hipStream_t s) {
+#define QMOE_GK(INM, S) grouped_kernel<QT, EPI, INM, S.mi, S.nj, S.kt, S.nw, SPLIT>, dim3(grid), dim3(64 * S.nw), 0, s, a
   constexpr GroupedShape S16 = MAIN ? grouped_shape_main(false) : grouped_shape_64(false);
   constexpr GroupedShape S32 = MAIN ? grouped_shape_main(true) : grouped_shape_64(true);
   // the inputs each epilogue is used with: FC1 pre-scaled token rows (or
@@ -497,20 +524,19 @@ hipError_t launch_grouped_split(const GroupedArgs &a, int grid, hipStream_t s) {
   // the dense matrix 16-bit rows
   if constexpr (EPI == kGEpiSwiGLU) {
     if (a.in_f32)
-      return qlaunch(grouped_kernel<QT, EPI, kInF32, S16.mi, S16.nj, S16.kt, SPLIT>, dim3(grid), dim3(256), 0, s,
-                     a);
+      return qlaunch(QMOE_GK(kInF32, S16));
     if (!a.in_scaled) return hipErrorInvalidConfiguration;
-    return qlaunch(grouped_kernel<QT, EPI, kInScaled, S16.mi, S16.nj, S16.kt, SPLIT>, dim3(grid), dim3(256), 0, s,
-                   a);
+    return qlaunch(QMOE_GK(kInScaled, S16));
   } else if constexpr (EPI == kGEpiStoreF32) {
     if (!a.in_f32) return hipErrorInvalidConfiguration;
-    return qlaunch(grouped_kernel<QT, EPI, kInF32, S32.mi, S32.nj, S32.kt, SPLIT>, dim3(grid), dim3(256), 0, s, a);
+    return qlaunch(QMOE_GK(kInF32, S32));
   } else {
     if (a.in_f32 || a.in_scaled) return hipErrorInvalidConfiguration;
     if (a.in_f16)
-      return qlaunch(grouped_kernel<QT, EPI, kInF16, S16.mi, S16.nj, S16.kt, SPLIT>, dim3(grid), dim3(256), 0, s, a);
-    return qlaunch(grouped_kernel<QT, EPI, kInBf16, S16.mi, S16.nj, S16.kt, SPLIT>, dim3(grid), dim3(256), 0, s, a);
+      return qlaunch(QMOE_GK(kInF16, S16));
+    return qlaunch(QMOE_GK(kInBf16, S16));
   }
+#undef QMOE_GK
 }
 
 template <int QT, int EPI, bool MAIN>

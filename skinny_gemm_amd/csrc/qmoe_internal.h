@@ -172,7 +172,7 @@ struct RouteBufs {
   int32_t *active;     // [E]     experts with count > 0, ascending
   int32_t *num_active; // [1]
   int4 *slot_info;     // [max_slots] {expert, rows, first position, 0}; rows = 0 past num_active
-  int4 *tile_info;     // [max_tiles] {expert, first position, rows (<= tile), 0}; rows = 0 past the end
+  int4 *tile_info;     // [max_tiles] {expert, first position, rows (<= tile), tiles}; rows = 0 past the end
 };
 
 struct RouteArgs {
@@ -359,6 +359,16 @@ hipError_t launch_count_invalid_ternary(const uint8_t *p, int64_t bytes, uint32_
 #ifndef QMOE_GROUPED_KT32
 #define QMOE_GROUPED_KT32 64
 #endif
+// A fragments read ahead of the MFMAs that use them, plus one
+#ifndef QMOE_GROUPED_AD
+#define QMOE_GROUPED_AD 2
+#endif
+#ifndef QMOE_GROUPED_NW16
+#define QMOE_GROUPED_NW16 4
+#endif
+#ifndef QMOE_GROUPED_NW32
+#define QMOE_GROUPED_NW32 4
+#endif
 // workgroups per compute unit the 128-row kernels are built for (registers)
 #ifndef QMOE_GROUPED_WG_PER_CU
 #define QMOE_GROUPED_WG_PER_CU 2
@@ -366,19 +376,19 @@ hipError_t launch_count_invalid_ternary(const uint8_t *p, int64_t bytes, uint32_
 constexpr int kTileM = 64;  // rows per grouped tile with an affine matrix
 
 struct GroupedShape {
-  int mi, nj, kt;
+  int mi, nj, kt, nw;  // nw: waves per workgroup, which share the staged activation tile
 };
 // in_f32: the shape of FC2 (fp32 input staged as f16 hi + lo parts, fp32
 // per-slot output); FC1 and the dense matrix take the other shape whatever
 // their input.  The 64-row shape (affine formats, and a non-affine matrix
 // whose layer has an affine one):
 __host__ __device__ constexpr GroupedShape grouped_shape_64(bool in_f32) {
-  return GroupedShape{4, in_f32 ? 4 : 2, in_f32 ? 64 : 128};
+  return GroupedShape{4, in_f32 ? 4 : 2, in_f32 ? 64 : 128, 4};
 }
 // The shape of the other layers:
 __host__ __device__ constexpr GroupedShape grouped_shape_main(bool in_f32) {
   return GroupedShape{QMOE_GROUPED_MI, in_f32 ? QMOE_GROUPED_NJ32 : QMOE_GROUPED_NJ16,
-                      in_f32 ? QMOE_GROUPED_KT32 : QMOE_GROUPED_KT16};
+                      in_f32 ? QMOE_GROUPED_KT32 : QMOE_GROUPED_KT16, in_f32 ? QMOE_GROUPED_NW32 : QMOE_GROUPED_NW16};
 }
 // Rows per grouped tile of a call (FC1 and FC2 share the tile list).
 inline int grouped_tile_rows(bool any_affine) { return any_affine ? kTileM : 16 * QMOE_GROUPED_MI; }
@@ -396,7 +406,7 @@ struct GroupedArgs {
   int qtype, sdtype, block, bpk;
   const float *wsc;        // [E] power-of-two weight pre-scale
   // rows
-  const int4 *tile_info;   // routed: {expert, first position, rows, 0}
+  const int4 *tile_info;   // routed: {expert, first position, rows, number of tiles}
   int tile_rows;           // rows per tile: kTileM or kTileMWide (routed: as the tile list)
   int dense_M;             // > 0: dense rows, tiles of tile_rows over M
   const int32_t *token_of; // routed FC1: input row of position p

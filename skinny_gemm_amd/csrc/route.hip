@@ -119,7 +119,9 @@ __global__ __launch_bounds__(kExpandThreads) void route_expand_kernel(RouteArgs 
     const int na = __shfl(fi, kLanes - 1);
     for (int sl = na + lane; sl < a.max_slots; sl += kLanes) a.r.slot_info[sl] = make_int4(0, 0, 0, 0);
 
-    // grouped path: tiles of tile_rows rows per expert, in expert order
+    // grouped path: tiles of tile_rows rows per expert, in expert order; every
+    // entry's last field holds the number of tiles (the grouped kernels map
+    // their workgroups over that many)
     if (a.tile_rows > 0) {
       int nt[PER];
       int ts = 0;
@@ -136,17 +138,18 @@ __global__ __launch_bounds__(kExpandThreads) void route_expand_kernel(RouteArgs 
       }
       int tpos = ti - ts;
       int roff = ci - cs;
+      const int ntot = __shfl(ti, kLanes - 1);
 #pragma unroll
       for (int i = 0; i < PER; ++i) {
         const int e = lane * PER + i;
         for (int t = 0; t < nt[i]; ++t)
           if (tpos + t < a.max_tiles)
-            a.r.tile_info[tpos + t] = make_int4(e, roff + t * a.tile_rows, min(a.tile_rows, c[i] - t * a.tile_rows), 0);
+            a.r.tile_info[tpos + t] =
+                make_int4(e, roff + t * a.tile_rows, min(a.tile_rows, c[i] - t * a.tile_rows), ntot);
         tpos += nt[i];
         roff += c[i];
       }
-      const int ntot = __shfl(ti, kLanes - 1);
-      for (int t = ntot + lane; t < a.max_tiles; t += kLanes) a.r.tile_info[t] = make_int4(0, 0, 0, 0);
+      for (int t = ntot + lane; t < a.max_tiles; t += kLanes) a.r.tile_info[t] = make_int4(0, 0, 0, ntot);
     }
   }
   __syncthreads();
