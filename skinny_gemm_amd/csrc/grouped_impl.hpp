@@ -60,6 +60,83 @@ __device__ inline float pow2_below(float amax, int lim) {
 }
 
 // ---------------------------------------------------------------- GEMM
+// Waves per SIMD the 128-row kernels are compiled for (it bounds their
+// registers): 16-bit input rows 4 (128 registers); fp32 rows (two parts) or
+// split scales (two weight fragments) 2.
+__host__ __device__ constexpr int grouped_waves_per_simd(bool in_f32, bool split) {
+  return in_f32 || split ? 2 : 4;
+}
+// Cross-lane moves within 16-lane rows (DPP): quad_perm [1,0,3,2] (lane ^ 1),
+// quad_perm [2,3,0,1] (lane ^ 2), and rotations by 4 and 8 lanes.
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppRor4 = 0x124, kDppRor8 = 0x128;
+template <int CTRL>
+__device__ inline float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+// SwiGLU epilogue of FC1 (gate and up in neighbouring columns, so in
+// neighbouring lanes).  A lane holds rows 4g + {0..3} of its column; the
+// even lane of a pair keeps the gates of rows 4g + {0, 1} and takes the ups
+// from its partner, the odd lane takes the gates of rows 4g + {2, 3}: every
+// lane evaluates two SwiGLUs.  The per-row maximum of |h| (for FC2's row
+// scale) is reduced over the 8 lanes of one parity in the 16-lane row, and
+// one atomic per row and wave goes out.
+template <int NI, int NJ>
+__device__ inline void swiglu_epilogue(const GroupedArgs &a, const floatx4_t (&acc)[NI][NJ], const float *s_rinv,
+                                       float winv, const float (&bv)[NJ], int rows, bool wave_on, int p0, int nw,
+                                       int lane) {
+  const bool odd = lane & 1;
+  const int g = lane >> 4;
+  const int64_t Ih = a.N / 2;
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    float inv[4];
+#pragma unroll
+    for (int el = 0; el < 4; ++el) {
+      const int m = 16 * i + 4 * g + el;
+      inv[el] = (m < rows && wave_on) ? winv * s_rinv[m] : 0.f;
+    }
+    const int mr = 16 * i + 4 * g + 2 * (lane & 1);  // this lane's two rows: mr, mr + 1
+    const bool v0 = mr < rows && wave_on, v1 = mr + 1 < rows && wave_on;
+    float hm0 = 0.f, hm1 = 0.f;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      float v[4];
+#pragma unroll
+      for (int el = 0; el < 4; ++el) v[el] = fmaf(acc[i][j][el], inv[el], bv[j]);
+      const float r0 = dpp_f<kDppXor1>(odd ? v[0] : v[2]);
+      const float r1 = dpp_f<kDppXor1>(odd ? v[1] : v[3]);
+      const float g0 = odd ? r0 : v[0], g1 = odd ? r1 : v[1];
+      const float u0 = odd ? v[2] : r0, u1 = odd ? v[3] : r1;
+      const float h0 = a.sw_custom ? swiglu_cfg(g0, u0, a.sw_alpha, a.sw_beta, a.sw_limit)
+                                   : g0 / (1.f + expf(-g0)) * u0;
+      const float h1 = a.sw_custom ? swiglu_cfg(g1, u1, a.sw_alpha, a.sw_beta, a.sw_limit)
+                                   : g1 / (1.f + expf(-g1)) * u1;
+      const int64_t col = (nw + 16 * j + (lane & 15)) >> 1;
+      if (v0) {
+        a.out_f32[(int64_t)(p0 + mr) * Ih + col] = h0;
+        if (a.h_dbg) a.h_dbg[(int64_t)a.row_list[p0 + mr] * Ih + col] = h0;
+        hm0 = fmaxf(hm0, fabsf(h0));
+      }
+      if (v1) {
+        a.out_f32[(int64_t)(p0 + mr + 1) * Ih + col] = h1;
+        if (a.h_dbg) a.h_dbg[(int64_t)a.row_list[p0 + mr + 1] * Ih + col] = h1;
+        hm1 = fmaxf(hm1, fabsf(h1));
+      }
+    }
+    hm0 = fmaxf(hm0, dpp_f<kDppXor2>(hm0));
+    hm1 = fmaxf(hm1, dpp_f<kDppXor2>(hm1));
+    hm0 = fmaxf(hm0, dpp_f<kDppRor4>(hm0));
+    hm1 = fmaxf(hm1, dpp_f<kDppRor4>(hm1));
+    hm0 = fmaxf(hm0, dpp_f<kDppRor8>(hm0));
+    hm1 = fmaxf(hm1, dpp_f<kDppRor8>(hm1));
+    if ((lane & 14) == 0) {
+      if (v0) atomicMax(&a.out_rowmax[p0 + mr], __float_as_uint(hm0));
+      if (v1) atomicMax(&a.out_rowmax[p0 + mr + 1], __float_as_uint(hm1));
+    }
+  }
+}
+
 // s_waitcnt immediate of gfx9: vmcnt 0, expcnt and lgkmcnt at their maxima
 constexpr int kWaitVmcnt0 = 0x0F70;
 constexpr int kMaxAffineBlocks = kGroupedMaxAffineBlocks;
@@ -76,7 +153,7 @@ enum { kInBf16 = 0, kInF16 = 1, kInF32 = 2, kInScaled = 3 };
 // (two MFMAs per weight fragment); an instance of its own, so the common
 // case keeps no registers for the tail.
 template <int QT, int EPI, int INM, int MI, int NJ, int KT, int NW, bool SPLIT>
-__global__ __launch_bounds__(64 * NW, MI == 8 && QMOE_GROUPED_WG_PER_CU * 4 >= NW ? QMOE_GROUPED_WG_PER_CU * 4 / NW : 1) void grouped_kernel(
+__global__ __launch_bounds__(64 * NW, MI == 8 ? grouped_waves_per_simd(INM == 2, SPLIT) * 4 / NW : 1) void grouped_kernel(
     const GroupedArgs a) {
   constexpr bool IN_F32 = INM == kInF32, IN_F16 = INM == kInF16, PRE = INM == kInScaled;
   using TR = QtTraits<QT>;
@@ -104,6 +181,7 @@ __global__ __launch_bounds__(64 * NW, MI == 8 && QMOE_GROUPED_WG_PER_CU * 4 >= N
   __shared__ _Float16 sA[2][NPART][TM][KT + APAD];
   __shared__ int s_row[TM];
   __shared__ float s_rsc[TM];
+  __shared__ float s_rinv[TM];  // 1 / s_rsc (exact: powers of two), 0 past the rows
   __shared__ float s_X[AFF ? TM : 1][AFF ? kMaxAffineBlocks : 1];  // per-row block sums of x
 
   const int lane = threadIdx.x & 63;
@@ -155,6 +233,7 @@ __global__ __launch_bounds__(64 * NW, MI == 8 && QMOE_GROUPED_WG_PER_CU * 4 >= N
     }
     s_row[r] = inrow;
     s_rsc[r] = sc;
+    s_rinv[r] = sc > 0.f ? 1.f / sc : 0.f;
   }
   __syncthreads();
 
@@ -462,13 +541,19 @@ __global__ __launch_bounds__(64 * NW, MI == 8 && QMOE_GROUPED_WG_PER_CU * 4 >= N
       bv[j] = (a.bias && wave_on) ? half_to_f32_rt(a.bias[(int64_t)e * a.N + nw + 16 * j + (lane & 15)],
                                                    a.act_dtype == QMOE_DTYPE_F16)
                                   : 0.f;  // idle waves of a partial last tile read nothing
+    if constexpr (EPI == kGEpiSwiGLU) {
+      if (!a.relu) {
+        swiglu_epilogue<NI, NJ>(a, acc, s_rinv, winv, bv, rows, wave_on, p0, nw, lane);
+        return;
+      }
+    }
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
 #pragma unroll
       for (int el = 0; el < 4; ++el) {
         const int m = 16 * i + 4 * g + el;
         const bool valid = m < rows && wave_on;
-        const float inv = valid ? winv / s_rsc[m] : 0.f;
+        const float inv = valid ? winv * s_rinv[m] : 0.f;
         float hmax = 0.f;
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {

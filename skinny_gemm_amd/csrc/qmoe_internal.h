@@ -369,10 +369,6 @@ hipError_t launch_count_invalid_ternary(const uint8_t *p, int64_t bytes, uint32_
 #ifndef QMOE_GROUPED_NW32
 #define QMOE_GROUPED_NW32 4
 #endif
-// workgroups per compute unit the 128-row kernels are built for (registers)
-#ifndef QMOE_GROUPED_WG_PER_CU
-#define QMOE_GROUPED_WG_PER_CU 2
-#endif
 constexpr int kTileM = 64;  // rows per grouped tile with an affine matrix
 
 struct GroupedShape {
