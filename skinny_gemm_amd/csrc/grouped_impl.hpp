@@ -60,8 +60,8 @@ __device__ inline float pow2_below(float amax, int lim) {
 }
 
 // ---------------------------------------------------------------- GEMM
-// Waves per SIMD the 128-row kernels are compiled for (it bounds their
-// registers): 16-bit input rows 4 (128 registers); fp32 rows (two parts) or
+// Waves per SIMD (the second launch bound) the 128-row kernels are compiled
+// for, which bounds their registers: 16-bit input rows 4 (128 registers); fp32 rows (two parts) or
 // split scales (two weight fragments) 2.
 __host__ __device__ constexpr int grouped_waves_per_simd(bool in_f32, bool split) {
   return in_f32 || split ? 2 : 4;
@@ -153,7 +153,7 @@ enum { kInBf16 = 0, kInF16 = 1, kInF32 = 2, kInScaled = 3 };
 // (two MFMAs per weight fragment); an instance of its own, so the common
 // case keeps no registers for the tail.
 template <int QT, int EPI, int INM, int MI, int NJ, int KT, int NW, bool SPLIT>
-__global__ __launch_bounds__(64 * NW, MI == 8 ? grouped_waves_per_simd(INM == 2, SPLIT) * 4 / NW : 1) void grouped_kernel(
+__global__ __launch_bounds__(64 * NW, MI == 8 ? grouped_waves_per_simd(INM == 2, SPLIT) : 1) void grouped_kernel(
     const GroupedArgs a) {
   constexpr bool IN_F32 = INM == kInF32, IN_F16 = INM == kInF16, PRE = INM == kInScaled;
   using TR = QtTraits<QT>;

@@ -364,7 +364,7 @@ hipError_t launch_count_invalid_ternary(const uint8_t *p, int64_t bytes, uint32_
 #define QMOE_GROUPED_AD 2
 #endif
 #ifndef QMOE_GROUPED_NW16
-#define QMOE_GROUPED_NW16 4
+#define QMOE_GROUPED_NW16 8
 #endif
 #ifndef QMOE_GROUPED_NW32
 #define QMOE_GROUPED_NW32 4
