@@ -80,11 +80,13 @@ __device__ inline float dpp_f(float v) {
 // from its partner, the odd lane takes the gates of rows 4g + {2, 3}: every
 // lane evaluates two SwiGLUs.  The per-row maximum of |h| (for FC2's row
 // scale) is reduced over the 8 lanes of one parity in the 16-lane row, and
-// one atomic per row and wave goes out.
+// its lanes' maximum goes into the workgroup's per-row maximum in LDS.  The
+// SwiGLU itself uses the hardware exponential and reciprocal (about 1 ulp
+// each, far below the f16 hi + lo precision FC2 reads h with).
 template <int NI, int NJ>
 __device__ inline void swiglu_epilogue(const GroupedArgs &a, const floatx4_t (&acc)[NI][NJ], const float *s_rinv,
-                                       float winv, const float (&bv)[NJ], int rows, bool wave_on, int p0, int nw,
-                                       int lane) {
+                                       uint32_t *s_hmax, float winv, const float (&bv)[NJ], int rows, bool wave_on,
+                                       int p0, int nw, int lane) {
   const bool odd = lane & 1;
   const int g = lane >> 4;
   const int64_t Ih = a.N / 2;
@@ -109,9 +111,9 @@ __device__ inline void swiglu_epilogue(const GroupedArgs &a, const floatx4_t (&a
       const float g0 = odd ? r0 : v[0], g1 = odd ? r1 : v[1];
       const float u0 = odd ? v[2] : r0, u1 = odd ? v[3] : r1;
       const float h0 = a.sw_custom ? swiglu_cfg(g0, u0, a.sw_alpha, a.sw_beta, a.sw_limit)
-                                   : g0 / (1.f + expf(-g0)) * u0;
+                                   : g0 * __builtin_amdgcn_rcpf(1.f + __expf(-g0)) * u0;
       const float h1 = a.sw_custom ? swiglu_cfg(g1, u1, a.sw_alpha, a.sw_beta, a.sw_limit)
-                                   : g1 / (1.f + expf(-g1)) * u1;
+                                   : g1 * __builtin_amdgcn_rcpf(1.f + __expf(-g1)) * u1;
       const int64_t col = (nw + 16 * j + (lane & 15)) >> 1;
       if (v0) {
         a.out_f32[(int64_t)(p0 + mr) * Ih + col] = h0;
@@ -131,8 +133,8 @@ __device__ inline void swiglu_epilogue(const GroupedArgs &a, const floatx4_t (&a
     hm0 = fmaxf(hm0, dpp_f<kDppRor8>(hm0));
     hm1 = fmaxf(hm1, dpp_f<kDppRor8>(hm1));
     if ((lane & 14) == 0) {
-      if (v0) atomicMax(&a.out_rowmax[p0 + mr], __float_as_uint(hm0));
-      if (v1) atomicMax(&a.out_rowmax[p0 + mr + 1], __float_as_uint(hm1));
+      if (v0) atomicMax(&s_hmax[mr], __float_as_uint(hm0));
+      if (v1) atomicMax(&s_hmax[mr + 1], __float_as_uint(hm1));
     }
   }
 }
@@ -182,6 +184,7 @@ __global__ __launch_bounds__(64 * NW, MI == 8 ? grouped_waves_per_simd(INM == 2,
   __shared__ int s_row[TM];
   __shared__ float s_rsc[TM];
   __shared__ float s_rinv[TM];  // 1 / s_rsc (exact: powers of two), 0 past the rows
+  __shared__ uint32_t s_hmax[EPI == kGEpiSwiGLU ? TM : 1];  // SwiGLU: the workgroup's max |h| bits per row
   __shared__ float s_X[AFF ? TM : 1][AFF ? kMaxAffineBlocks : 1];  // per-row block sums of x
 
   const int lane = threadIdx.x & 63;
@@ -234,6 +237,7 @@ __global__ __launch_bounds__(64 * NW, MI == 8 ? grouped_waves_per_simd(INM == 2,
     s_row[r] = inrow;
     s_rsc[r] = sc;
     s_rinv[r] = sc > 0.f ? 1.f / sc : 0.f;
+    if constexpr (EPI == kGEpiSwiGLU) s_hmax[r] = 0u;
   }
   __syncthreads();
 
@@ -387,6 +391,33 @@ __global__ __launch_bounds__(64 * NW, MI == 8 ? grouped_waves_per_simd(INM == 2,
     // load would make the loop wait for the prefetched scales at once
     using ST = std::conditional_t<AFF, uint32_t, uint16_t>;
     auto load_b = [&](int64_t kt, uint32_t (&bw)[CPT][NJ], ST (&sv)[CPT][NJ]) __attribute__((always_inline)) {
+      if constexpr (CPT == 2 && !AFF) {
+        // a tile of two chunks: its first chunk is even, so both sit in one
+        // 8-B half of the lane's 16 B (a partial last tile reads the padding
+        // chunk beside it; its A columns are zero), and one scale serves both
+        // chunks when a block spans two or more
+        const int chunk = (int)(kt / KC);
+        const int ktile = chunk >> 2, bi0 = (chunk >> cpb_log) & (bpk - 1);
+        const int wso = ktile * (4 * kLanes * 16) + (chunk & 3) * 4;
+        const int sso = (ktile * kLanes * bpk + bi0) * SES;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          const int wj = wso + j * (kLanes * 16), sj = sso + j * 16 * bpk * SES;
+          const auto w2 = __builtin_amdgcn_raw_buffer_load_b64(wrs, wvo, wj, 0);
+          bw[0][j] = w2[0];
+          bw[1][j] = w2[1];
+          sv[0][j] = __builtin_amdgcn_raw_buffer_load_b16(srs, svo, sj, 0);
+        }
+        if (cpb_log == 0) {
+#pragma unroll
+          for (int j = 0; j < NJ; ++j)
+            sv[1][j] = __builtin_amdgcn_raw_buffer_load_b16(srs, svo, sso + SES + j * 16 * bpk * SES, 0);
+        } else {
+#pragma unroll
+          for (int j = 0; j < NJ; ++j) sv[1][j] = sv[0][j];
+        }
+        return;
+      }
       static_for<CPT>([&](auto cc) {
         constexpr int c = decltype(cc)::value;
         const int chunk = min((int)(kt / KC) + c, (int)a.NC - 1);
@@ -543,7 +574,10 @@ __global__ __launch_bounds__(64 * NW, MI == 8 ? grouped_waves_per_simd(INM == 2,
                                   : 0.f;  // idle waves of a partial last tile read nothing
     if constexpr (EPI == kGEpiSwiGLU) {
       if (!a.relu) {
-        swiglu_epilogue<NI, NJ>(a, acc, s_rinv, winv, bv, rows, wave_on, p0, nw, lane);
+        swiglu_epilogue<NI, NJ>(a, acc, s_rinv, s_hmax, winv, bv, rows, wave_on, p0, nw, lane);
+        // one global atomic per row and workgroup
+        __syncthreads();
+        if ((int)threadIdx.x < rows) atomicMax(&a.out_rowmax[p0 + threadIdx.x], s_hmax[threadIdx.x]);
         return;
       }
     }
