@@ -63,8 +63,11 @@ __device__ inline float pow2_below(float amax, int lim) {
 // Waves per SIMD (the second launch bound) the 128-row kernels are compiled
 // for, which bounds their registers: 16-bit input rows 4 (128 registers); fp32 rows (two parts) or
 // split scales (two weight fragments) 2.
+#ifndef QMOE_GROUPED_F32_WAVES
+#define QMOE_GROUPED_F32_WAVES 2
+#endif
 __host__ __device__ constexpr int grouped_waves_per_simd(bool in_f32, bool split) {
-  return in_f32 || split ? 2 : 4;
+  return split ? 2 : in_f32 ? QMOE_GROUPED_F32_WAVES : 4;
 }
 // Cross-lane moves within 16-lane rows (DPP): quad_perm [1,0,3,2] (lane ^ 1),
 // quad_perm [2,3,0,1] (lane ^ 2), and rotations by 4 and 8 lanes.
@@ -180,7 +183,13 @@ __global__ __launch_bounds__(64 * NW, MI == 8 ? grouped_waves_per_simd(INM == 2,
   // fit f16: the scale is split into an 8-bit head and its tail (two MFMAs)
   constexpr bool MULTIBIT = (QT == QMOE_QTYPE_SYM_INT4 || QT == QMOE_QTYPE_AFFINE_INT4);
 
-  __shared__ _Float16 sA[2][NPART][TM][KT + APAD];
+  // DIRECT: pre-scaled 16-bit rows (a plain copy) are loaded straight into
+  // LDS (global_load_lds, 16 B a lane) into two separate arrays; the other
+  // modes convert in registers and store into sA
+  constexpr bool DIRECT = PRE && !AFF;
+  __shared__ _Float16 sA[DIRECT ? 1 : 2][NPART][DIRECT ? 1 : TM][DIRECT ? 1 : KT + APAD];
+  __shared__ __attribute__((aligned(16))) _Float16 sD0[DIRECT ? TM * KT : 8];
+  __shared__ __attribute__((aligned(16))) _Float16 sD1[DIRECT ? TM * KT : 8];
   __shared__ int s_row[TM];
   __shared__ float s_rsc[TM];
   __shared__ float s_rinv[TM];  // 1 / s_rsc (exact: powers of two), 0 past the rows
@@ -434,8 +443,12 @@ __global__ __launch_bounds__(64 * NW, MI == 8 ? grouped_waves_per_simd(INM == 2,
       });
     };
     const RegConsts<CD::kNC> dk = CodecOps<CD>::in_registers();  // decoder constants in registers
-    auto compute = [&](int buf, const uint32_t (&bw)[CPT][NJ], const ST (&sv)[CPT][NJ])
-                       __attribute__((always_inline)) {
+    // A: part 0 of the staged tile; RS halves between rows, PS between parts;
+    // SWZ: 16-B pieces stored at slot piece ^ (row & 7) (the direct layout)
+    auto compute = [&](const _Float16 *A, auto rs_c, auto ps_c, auto swz_c, const uint32_t (&bw)[CPT][NJ],
+                       const ST (&sv)[CPT][NJ]) __attribute__((always_inline)) {
+      constexpr int RS = decltype(rs_c)::value, PS = decltype(ps_c)::value;
+      constexpr bool SWZ = decltype(swz_c)::value;
       // per chunk and slice: the pre-scaled f16 scale (head) and its tail,
       // once per tile
       f16x2_t s2c[CPT][NJ], l2c[CPT][NJ];
@@ -479,8 +492,9 @@ __global__ __launch_bounds__(64 * NW, MI == 8 ? grouped_waves_per_simd(INM == 2,
         }
         // A fragments: row (lane % 16) of each 16-row slice, 8 k in the order of B
         const int koff = (TR::kBits == 4) ? (ks * 32 + 8 * g) : (c * 64 + 16 * g + 8 * half);
-        const _Float16 *abase = &sA[buf][0][lane & 15][koff];
-        constexpr int PST = TM * (KT + APAD), RST = 16 * (KT + APAD);  // halves between parts, row tiles
+        const int kslot = SWZ ? (((koff >> 3) ^ (lane & 7)) << 3) : koff;  // rows 16 i + r share r & 7
+        const _Float16 *abase = A + (lane & 15) * RS + kslot;
+        constexpr int PST = PS, RST = 16 * RS;  // halves between parts, row tiles
         // the A fragments of row tile i + 2 are read while row tile i's
         // MFMAs run (three fragments in flight), and scheduling fences keep
         // that order, so at most three fragments are held in registers
@@ -511,31 +525,103 @@ __global__ __launch_bounds__(64 * NW, MI == 8 ? grouped_waves_per_simd(INM == 2,
     // per tile (the staged buffers alternate).
     uint32_t bwA[CPT][NJ], bwB[CPT][NJ];
     ST svA[CPT][NJ], svB[CPT][NJ];
-    uint4 S[SV];
-    load_b(0, bwA, svA);
-    stage_load(0, S);
-    stage_store(0, S, 0);
-    __syncthreads();
-    int buf = 0;
-    for (int64_t kt = 0; kt < a.K; kt += KT) {
-      const bool more = kt + KT < a.K;
-      if (more) {
-        load_b(kt + KT, bwB, svB);
-        stage_load(kt + KT, S);
-        __builtin_amdgcn_sched_barrier(0);
+    if constexpr (DIRECT) {
+      // Each wave copies IPW blocks of 1 KiB (RPI rows) per tile: lane l
+      // takes piece slot l % PPR of row l / PPR, and reads the row's global
+      // piece slot ^ (row & 7).  Rows past the tile read token row 0 (their
+      // outputs are never stored); pieces past K are cleared after the copy.
+      constexpr int PPR = KT / 8, RPI = kLanes / PPR, IPW = TM / RPI / NW;
+      static_assert(TM % (RPI * NW) == 0, "direct copy blocks");
+      const uint16_t *gsrc[IPW];
+      int dslot[IPW];
+#pragma unroll
+      for (int q = 0; q < IPW; ++q) {
+        const int row = (q * NW + wave) * RPI + lane / PPR, slot = lane % PPR;
+        const int in = s_row[row];
+        gsrc[q] = reinterpret_cast<const uint16_t *>(a.in) + (int64_t)(in >= 0 ? in : 0) * a.in_row_elems;
+        dslot[q] = (slot ^ (row & 7)) * 8;  // k of this lane's piece within the tile
       }
-      if (wave_on) compute(buf, bwA, svA);  // uniform: idle waves of a partial last column tile only stage
-      __builtin_amdgcn_sched_barrier(0);
-      if (more) stage_store(kt + KT, S, buf ^ 1);
-      __syncthreads();
+      // a piece past K reads the row's last 8 values instead (K >= 32)
+      auto dma = [&](int64_t kt, _Float16 *D) __attribute__((always_inline)) {
 #pragma unroll
-      for (int c = 0; c < CPT; ++c)
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-          bwA[c][j] = bwB[c][j];
-          svA[c][j] = svB[c][j];
+        for (int q = 0; q < IPW; ++q) {
+          const int64_t k = kt + dslot[q] < a.K - 8 ? kt + dslot[q] : a.K - 8;
+          // (untyped pointers: a typed source pointer keeps the host pass from emitting the kernel's stub)
+          __builtin_amdgcn_global_load_lds((const void *)(gsrc[q] + k), (void *)(D + (q * NW + wave) * RPI * KT), 16,
+                                           0, 0);
         }
-      buf ^= 1;
+      };
+      // after the copy of the tile at kt has landed: clear its pieces past K
+      auto clear_tail = [&](int64_t kt, _Float16 *D) __attribute__((always_inline)) {
+        if (kt + KT > a.K) {
+#pragma unroll
+          for (int q = 0; q < IPW; ++q)
+            if (kt + dslot[q] >= a.K)
+              *reinterpret_cast<uint4 *>(D + (q * NW + wave) * RPI * KT + lane * 8) = make_uint4(0u, 0u, 0u, 0u);
+        }
+      };
+      using RSc = std::integral_constant<int, KT>;
+      using PSc = std::integral_constant<int, 0>;
+      using SWc = std::integral_constant<bool, true>;
+      load_b(0, bwA, svA);
+      dma(0, sD0);
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+      clear_tail(0, sD0);
+      __syncthreads();
+      for (int64_t kt = 0; kt < a.K; kt += 2 * KT) {
+        const bool more0 = kt + KT < a.K;
+        if (more0) {
+          load_b(kt + KT, bwB, svB);
+          dma(kt + KT, sD1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (wave_on) compute(sD0, RSc{}, PSc{}, SWc{}, bwA, svA);
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        if (!more0) break;
+        clear_tail(kt + KT, sD1);
+        __syncthreads();
+        const bool more1 = kt + 2 * KT < a.K;
+        if (more1) {
+          load_b(kt + 2 * KT, bwA, svA);
+          dma(kt + 2 * KT, sD0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (wave_on) compute(sD1, RSc{}, PSc{}, SWc{}, bwB, svB);
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        if (more1) clear_tail(kt + 2 * KT, sD0);
+        __syncthreads();
+      }
+    } else {
+      uint4 S[SV];
+      load_b(0, bwA, svA);
+      stage_load(0, S);
+      stage_store(0, S, 0);
+      __syncthreads();
+      int buf = 0;
+      for (int64_t kt = 0; kt < a.K; kt += KT) {
+        const bool more = kt + KT < a.K;
+        if (more) {
+          load_b(kt + KT, bwB, svB);
+          stage_load(kt + KT, S);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if (wave_on)  // uniform: idle waves of a partial last column tile only stage
+          compute(&sA[buf][0][0][0], std::integral_constant<int, KT + APAD>{},
+                  std::integral_constant<int, TM * (KT + APAD)>{}, std::integral_constant<bool, false>{}, bwA, svA);
+        __builtin_amdgcn_sched_barrier(0);
+        if (more) stage_store(kt + KT, S, buf ^ 1);
+        __syncthreads();
+#pragma unroll
+        for (int c = 0; c < CPT; ++c)
+#pragma unroll
+          for (int j = 0; j < NJ; ++j) {
+            bwA[c][j] = bwB[c][j];
+            svA[c][j] = svB[c][j];
+          }
+        buf ^= 1;
+      }
     }
 
     // affine: + sum over blocks of (b + zc*s) * X[row][block], scaled like acc
