@@ -257,6 +257,7 @@ struct Plan {
   int route_fused;
   int fc1_routes;  // GEMV path: FC1 routes the tokens itself (no routing kernel)
   int fc2_cat;     // GEMV path, one token, k > 1: FC2 over the k experts' concatenated K writes y (no combine)
+  int cat_stage;   // fc2_cat: the token's h rows fit LDS beside the reduction (the one-request weight path)
   bool softmax_all;  // unnormalised top-k weights, computed by the routing top-k
   int launches;
   std::string kernels;
@@ -338,6 +339,10 @@ qmoe_status make_plan(const qmoe_layer_desc &d, int32_t T, int32_t k, int path_r
     const int m = kGemvCatMaxWaves / k;
     if (gemv_lds_bytes(T, kEpiDownCat, k * m, p.tn2) <= kLdsLimit) p.ks2 = k * m;
   }
+  p.cat_stage = (p.fc2_cat && p.ks2 % k == 0 &&
+                 gemv_lds_bytes(T, kEpiDownCat, p.ks2, p.tn2) + gemv_cat_stage_bytes(k, d.inter) <= kLdsLimit)
+                    ? 1
+                    : 0;
   // top-1: the down GEMV writes y; otherwise a combine kernel follows
   // the weights of SOFTMAX_ALL replace the routing's weights once the ids
   // exist, before the first reader of the weights (FC2 or the combine)
@@ -831,6 +836,7 @@ qmoe_status qmoe_forward_ex(const qmoe_layer_desc *desc, const void *packed, con
   g1.relu = desc->activation == QMOE_ACT_RELU;
   set_swiglu(g1, opts);
   g1.act_dtype = desc->act_dtype;
+  g1.h_by_slot = p.fc2_cat;  // the concatenated FC2 reads the token's h rows in slot order
   e = begin();
   if (e == hipSuccess)
     e = launch_gemv(g1, fc1_routes ? kEpiSwiGLURouted : kEpiSwiGLU, gemv_in_mode(desc->act_dtype), p.mmax1,
@@ -854,6 +860,7 @@ qmoe_status qmoe_forward_ex(const qmoe_layer_desc *desc, const void *packed, con
   g2.route_w = ra.r.w;
   g2.route = ra.r;
   g2.route_k = top_k;
+  g2.cat_stage = p.cat_stage;
   e = begin();
   if (e == hipSuccess)
     e = p.fc2_cat ? launch_gemv(g2, kEpiDownCat, 0, 1, p.ks2, p.tn2, L.fc2.block, 1, s)

@@ -125,8 +125,10 @@ hipError_t launch_gemv(const GemvArgs &a, int epilogue, int in_f16, int rows, in
   if (fn == nullptr) return hipErrorInvalidConfiguration;  // no kernel for this (rows, tn) pairing
   GemvArgs args = a;
   void *kargs[] = {&args};
+  const size_t lds = gemv_lds_bytes(rows, epilogue, waves, tn) +
+                     (epilogue == kEpiDownCat && a.cat_stage ? gemv_cat_stage_bytes(a.route_k, a.K) : 0);
   return launch_raw(fn, dim3((unsigned)(grid_slots * a.RG * (4 / tn))), dim3((unsigned)(waves * kLanes)), kargs,
-                    gemv_lds_bytes(rows, epilogue, waves, tn), s);
+                    lds, s);
 }
 
 int gemv_blocks_per_cu(int qtype, int epilogue, int in_f16, int rows, int waves, int tn, int block) {

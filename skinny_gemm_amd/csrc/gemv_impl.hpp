@@ -60,6 +60,7 @@ struct QtTraits {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float floatx4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
 // v_mfma_f32_16x16x32_{bf16,f16}: c + A (16 x 32) * B (32 x 16).  Lane l
 // supplies row l % 16 of A and column l % 16 of B for k = 8 (l / 16) .. +7;
@@ -211,12 +212,10 @@ __global__ __launch_bounds__(EPI == kEpiDownCat ? 64 * kGemvCatMaxWaves : 512) v
   // set-up below so that their latency overlaps it
   int cat_e0 = 0;
   float cat_w0 = 0.f;
-  int cat_p0 = 0;
   if constexpr (CAT) {
     const int j0 = min(kw0 / NKT, a.route_k - 1);
     cat_e0 = a.route.ids[j0];
     cat_w0 = a.route.w[j0];
-    cat_p0 = a.route.slot_pos[j0];
   }
 
   // A operand rows: lane (r, g) supplies row 16 mt + r.  Rows past M read
@@ -438,7 +437,62 @@ __global__ __launch_bounds__(EPI == kEpiDownCat ? 64 * kGemvCatMaxWaves : 512) v
       compute(kt, TA);
     }
   };
-  if constexpr (CAT) {
+  // CAT, when every wave's range lies inside one of the k matrices (KS a
+  // multiple of k) and holds at most kCatDeep whole k-tiles: all of the
+  // wave's weights are requested at once, and the token's h rows (both
+  // parts, all k slots) are copied into LDS behind them, so the loop waits for
+  // memory once instead of once per k-tile.
+  bool deep = false;
+  if constexpr (CAT && TN == 1)  // (with 4 n-tiles a wave the requested weights would not fit the registers)
+    deep = a.cat_stage && NC % 4 == 0 && KS % a.route_k == 0 && (NKT * a.route_k + KS - 1) / KS <= kCatDeep &&
+           a.route_k * 2 * (int)(a.K / 8) <= kCatStagePer * (int)blockDim.x;
+  if (CAT && TN == 1 && deep) {
+    // the h rows (slot order, no dependence on the routing) are requested
+    // first, then the weights once the segment's expert id has arrived
+    const int64_t P = a.K / 2;
+    const int pieces = (int)(P / 4), total = a.route_k * 2 * pieces;
+    u32x4_t hv[kCatStagePer];  // a native vector (a struct array here would stay in scratch memory)
+#pragma unroll
+    for (int r = 0; r < kCatStagePer; ++r) {
+      const int idx = (int)threadIdx.x + r * (int)blockDim.x;
+      if (idx < total) {
+        const int rp = idx / pieces, pc = idx - rp * pieces;
+        hv[r] = *reinterpret_cast<const u32x4_t *>(a.in + (int64_t)(rp >> 1) * a.in_row_pairs +
+                                                   (rp & 1) * a.in_part_stride + pc * 4);
+      }
+    }
+    const int jseg = kw0 / NKT, lo = kw0 - jseg * NKT, n = kw1 - kw0;
+    const int eseg = __builtin_amdgcn_readfirstlane(cat_e0);
+    wrs = code_rsrc(eseg);
+    srs = scale_rsrc(eseg);
+    wseg = cat_w0;
+    Tile W[kCatDeep];
+#pragma unroll
+    for (int i = 0; i < kCatDeep; ++i) load_w(lo + min(i, n - 1), W[i]);  // past n: the last tile again
+    // h of the k slots: [slot][part][K/2 pairs] after the reduction buffer
+    uint32_t *sH = reinterpret_cast<uint32_t *>(s_red) + KS * (TN * MT * MR) * kLanes;
+#pragma unroll
+    for (int r = 0; r < kCatStagePer; ++r) {
+      const int idx = (int)threadIdx.x + r * (int)blockDim.x;
+      if (idx < total) reinterpret_cast<u32x4_t *>(sH)[idx] = hv[r];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kCatDeep; ++i) {
+      if (i < n) {
+        const int kt = lo + i;
+        static_for<KSTEPS>([&](auto kc_) {
+          constexpr int ks = decltype(kc_)::value;
+          constexpr int jj = ks / HALVES, h = ks % HALVES;
+          const int64_t kp = (int64_t)kt * (KT / 2) + (BITS == 2 ? (32 * jj + 8 * g + 4 * h) : (16 * jj + 4 * g));
+#pragma unroll
+          for (int p = 0; p < PARTS; ++p)
+            W[i].af[ks][0][p] = *reinterpret_cast<const uint4 *>(sH + (jseg * 2 + p) * P + kp);
+        });
+        compute(kt, W[i]);
+      }
+    }
+  } else if constexpr (CAT) {
     // the wave's range over the k matrices: each overlapped matrix j with its
     // expert's weights, the token's h row of slot j and w_j (the first
     // matrix's routing entries were loaded at the start of the kernel)
@@ -449,7 +503,7 @@ __global__ __launch_bounds__(EPI == kEpiDownCat ? 64 * kGemvCatMaxWaves : 512) v
       wrs = code_rsrc(ej);
       srs = scale_rsrc(ej);
       wseg = first ? cat_w0 : a.route.w[j];
-      const int64_t prow = first ? cat_p0 : a.route.slot_pos[j];
+      const int64_t prow = j;  // FC1 wrote the one token's h rows in slot order
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) arow[mt] = a.in + prow * a.in_row_pairs;
       kloop(lo, hi);
@@ -498,16 +552,14 @@ __global__ __launch_bounds__(EPI == kEpiDownCat ? 64 * kGemvCatMaxWaves : 512) v
                                  : gt / (1.f + expf(-gt)) * up;
         const int64_t Ih = relu ? N : N / 2;
         const int64_t i = relu ? n : n / 2;
-        const int64_t p = pbase + m;
+        int64_t slot_of_row;
+        if constexpr (ROUTED) slot_of_row = s_rslot[m];
+        else slot_of_row = a.row_list[pbase + m];
+        const int64_t p = a.h_by_slot ? slot_of_row : pbase + m;
         const uint16_t hi = f32_to_bf16_rne(h);
         a.h_hi[p * Ih + i] = hi;
         a.h_lo[p * Ih + i] = f32_to_bf16_rne(h - bf16_to_f32(hi));
-        if (a.h_dbg) {
-          int64_t slot_of_row;
-          if constexpr (ROUTED) slot_of_row = s_rslot[m];
-          else slot_of_row = a.row_list[p];
-          a.h_dbg[slot_of_row * Ih + i] = h;
-        }
+        if (a.h_dbg) a.h_dbg[slot_of_row * Ih + i] = h;
       }
     } else if constexpr (CAT) {
       if (valid) a.out_act[n] = f32_to_act(v, a.act_dtype == QMOE_DTYPE_F16);  // y of the one token

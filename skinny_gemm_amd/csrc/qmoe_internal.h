@@ -239,6 +239,9 @@ struct GemvArgs {
   int route_T, route_E, route_k, route_max_slots;
   int route_softmax_all;   // kEpiSwiGLURouted (EXT instances): as RouteArgs::softmax_all
   RouteBufs route;
+  int cat_stage;           // kEpiDownCat: LDS holds the token's h rows after the reduction buffer
+  int h_by_slot;           // kEpiSwiGLU(Routed): h rows at the flat slot index, not the sorted position (the
+                           // concatenated FC2 of one token reads them)
 };
 
 // Rows per GEMV launch: one 16-row MFMA tile for routed experts, two for
@@ -246,6 +249,11 @@ struct GemvArgs {
 constexpr int kGemvMaxRowsDense = 32;
 constexpr int kGemvMaxWaves = 8;
 constexpr int kGemvCatMaxWaves = 16;  // concatenated FC2: k x (waves per expert) <= 16
+constexpr int kCatDeep = 8;           // concatenated FC2: k-tiles per wave requested at once
+constexpr int kCatStagePer = 4;       // concatenated FC2: 16-B pieces of h per thread staged in LDS
+// Concatenated FC2: the token's h rows (k slots, hi + lo parts of K bf16)
+// staged in LDS after the reduction buffer.
+inline size_t gemv_cat_stage_bytes(int k, int64_t K) { return (size_t)k * 2 * (size_t)K * 2; }
 
 // Dynamic LDS of one GEMV workgroup: the cross-wave partial sums of the
 // tn n-tiles x row tiles x accumulator elements x 64 lanes.
