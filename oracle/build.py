@@ -14,12 +14,13 @@ LIB = os.path.join(HERE, "liboracle.so")
 
 
 def build(verbose: bool = False) -> str:
+    tmp = f"{LIB}.tmp{os.getpid()}"  # per process: concurrent test workers may build at once
     cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off", "-fno-fast-math",
-           "-Wall", "-Wextra", "-o", LIB + ".tmp", SRC, "-lm"]
+           "-Wall", "-Wextra", "-o", tmp, SRC, "-lm"]
     if verbose:
         print(" ".join(cmd))
     subprocess.run(cmd, check=True)
-    os.replace(LIB + ".tmp", LIB)
+    os.replace(tmp, LIB)
     return LIB
 
 
