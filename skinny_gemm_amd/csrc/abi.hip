@@ -244,7 +244,16 @@ GemvShape pick_gemv(int64_t nwg, const MatLayout &L, int rows, int epilogue, int
       best_cost = cost;
     }
   }
-  if (best > 0) return {best, tn};
+  if (best > 0) {
+    // FC1 launches that fill the chip (four n-tiles a wave) keep at least 4
+    // k-tiles a wave: the per-wave fixed work (routing prologue, 64-row
+    // SwiGLU epilogue, the LDS reduction) outweighs the shorter chain there
+    // (DeepSeek-V2-Lite-shaped decode, 16 k-tiles: FC1 at 4 waves measured
+    // 4-13% faster than at 8)
+    if (tn == 4 && (epilogue == kEpiSwiGLU || epilogue == kEpiSwiGLURouted))
+      while (best > 1 && L.NKT / best < 4) best /= 2;
+    return {best, tn};
+  }
   int64_t ks = (kGemvTargetWaves + nwg - 1) / std::max<int64_t>(nwg, 1);
   ks = std::max<int64_t>(1, std::min<int64_t>(ks, kmax));
   while (ks > 1 && gemv_lds_bytes(rows, epilogue, (int)ks, tn) > kLdsLimit) --ks;

@@ -1,6 +1,6 @@
-// grouped_impl.hpp -- grouped larger-M path: tiles of 64 routed rows x 128 or 256 outputs
-// per workgroup, MFMA (v_mfma_f32_16x16x32_f16) on weights dequantized once
-// per tile in registers.
+// grouped_impl.hpp -- grouped larger-M path: tiles of 128 routed rows (64 for
+// affine formats) x 128 or 256 outputs per workgroup, MFMA
+// (v_mfma_f32_16x16x32_f16) on weights dequantized once per tile in registers.
 //
 // The pages' prefill path runs a grouped GEMM over the rows of each expert
 // that dequantizes each weight tile once instead of materialising dense
@@ -61,13 +61,15 @@ __device__ inline float pow2_below(float amax, int lim) {
 
 // ---------------------------------------------------------------- GEMM
 // Waves per SIMD (the second launch bound) the 128-row kernels are compiled
-// for, which bounds their registers: 16-bit input rows 4 (128 registers); fp32 rows (two parts) or
-// split scales (two weight fragments) 2.
+// for, which bounds their registers: 16-bit input rows 4 (128 registers);
+// split scales (two weight fragments) 2; fp32 rows (two parts) 4 for FC2,
+// whose 8-wave workgroups of 2 column slices a wave fit 4 a SIMD by LDS (a
+// few registers spill, measured faster than 2 waves a SIMD), and 2 for FC1.
 #ifndef QMOE_GROUPED_F32_WAVES
 #define QMOE_GROUPED_F32_WAVES 2
 #endif
-__host__ __device__ constexpr int grouped_waves_per_simd(bool in_f32, bool split) {
-  return split ? 2 : in_f32 ? QMOE_GROUPED_F32_WAVES : 4;
+__host__ __device__ constexpr int grouped_waves_per_simd(bool in_f32, bool split, bool fc2) {
+  return split ? 2 : !in_f32 ? 4 : fc2 ? 4 : QMOE_GROUPED_F32_WAVES;
 }
 // Cross-lane moves within 16-lane rows (DPP): quad_perm [1,0,3,2] (lane ^ 1),
 // quad_perm [2,3,0,1] (lane ^ 2), and rotations by 4 and 8 lanes.
@@ -158,7 +160,7 @@ enum { kInBf16 = 0, kInF16 = 1, kInF32 = 2, kInScaled = 3 };
 // (two MFMAs per weight fragment); an instance of its own, so the common
 // case keeps no registers for the tail.
 template <int QT, int EPI, int INM, int MI, int NJ, int KT, int NW, bool SPLIT>
-__global__ __launch_bounds__(64 * NW, MI == 8 ? grouped_waves_per_simd(INM == 2, SPLIT) : 1) void grouped_kernel(
+__global__ __launch_bounds__(64 * NW, MI == 8 ? grouped_waves_per_simd(INM == 2, SPLIT, EPI == kGEpiStoreF32) : 1) void grouped_kernel(
     const GroupedArgs a) {
   constexpr bool IN_F32 = INM == kInF32, IN_F16 = INM == kInF16, PRE = INM == kInScaled;
   using TR = QtTraits<QT>;

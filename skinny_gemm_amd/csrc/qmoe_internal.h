@@ -347,9 +347,10 @@ hipError_t launch_pack_b3_records(const uint8_t *codes, const uint16_t *scales, 
 hipError_t launch_count_invalid_ternary(const uint8_t *p, int64_t bytes, uint32_t *count, hipStream_t s);
 
 // ----------------------------------------------------------- grouped MFMA
-// Shape of a grouped workgroup tile (4 waves): MI 16-row MFMA row tiles
-// (TM = 16 MI rows), NJ 16-column slices per wave (64 NJ outputs per tile)
-// and KT k per staged activation tile.  Affine formats keep per-row block
+// Shape of a grouped workgroup tile: MI 16-row MFMA row tiles (TM = 16 MI
+// rows), NJ 16-column slices per wave, NW waves (16 NJ NW outputs per tile,
+// all waves sharing the staged activation tile) and KT k per staged
+// activation tile.  Affine formats keep per-row block
 // sums of the activations in LDS, laid out for 64-row tiles; the other
 // formats take the shapes below (compile-time tuning constants).
 #ifndef QMOE_GROUPED_MI
@@ -362,7 +363,7 @@ hipError_t launch_count_invalid_ternary(const uint8_t *p, int64_t bytes, uint32_
 #define QMOE_GROUPED_KT16 64
 #endif
 #ifndef QMOE_GROUPED_NJ32
-#define QMOE_GROUPED_NJ32 4
+#define QMOE_GROUPED_NJ32 2
 #endif
 #ifndef QMOE_GROUPED_KT32
 #define QMOE_GROUPED_KT32 64
@@ -375,7 +376,7 @@ hipError_t launch_count_invalid_ternary(const uint8_t *p, int64_t bytes, uint32_
 #define QMOE_GROUPED_NW16 8
 #endif
 #ifndef QMOE_GROUPED_NW32
-#define QMOE_GROUPED_NW32 4
+#define QMOE_GROUPED_NW32 8
 #endif
 constexpr int kTileM = 64;  // rows per grouped tile with an affine matrix
 
