@@ -497,10 +497,10 @@ __global__ __launch_bounds__(64 * NW, MI == 8 ? grouped_waves_per_simd(INM == 2,
         const int kslot = SWZ ? (((koff >> 3) ^ (lane & 7)) << 3) : koff;  // rows 16 i + r share r & 7
         const _Float16 *abase = A + (lane & 15) * RS + kslot;
         constexpr int PST = PS, RST = 16 * RS;  // halves between parts, row tiles
-        // the A fragments of row tile i + 2 are read while row tile i's
-        // MFMAs run (three fragments in flight), and scheduling fences keep
-        // that order, so at most three fragments are held in registers
-        constexpr int AD = QMOE_GROUPED_AD;
+        // the A fragments of row tile i + AD - 1 are read while row tile i's
+        // MFMAs run, and scheduling fences keep that order, so at most AD
+        // fragments (per part) are held in registers
+        constexpr int AD = (NPART == 1 && MI == 8) ? QMOE_GROUPED_AD16 : QMOE_GROUPED_AD;
         half8_t af[AD][NPART];
         auto read_a = [&](int i, half8_t(&d)[NPART]) __attribute__((always_inline)) {
 #pragma unroll

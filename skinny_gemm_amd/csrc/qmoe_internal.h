@@ -368,9 +368,14 @@ hipError_t launch_count_invalid_ternary(const uint8_t *p, int64_t bytes, uint32_
 #ifndef QMOE_GROUPED_KT32
 #define QMOE_GROUPED_KT32 64
 #endif
-// A fragments read ahead of the MFMAs that use them, plus one
+// A fragments read ahead of the MFMAs that use them, plus one: 3 for the
+// 128-row tiles of 16-bit rows (FC1: 489 against 506 us on the mixed
+// INT2/INT4 prefill), 2 for the others (FC2's two h parts spill with 3)
 #ifndef QMOE_GROUPED_AD
 #define QMOE_GROUPED_AD 2
+#endif
+#ifndef QMOE_GROUPED_AD16
+#define QMOE_GROUPED_AD16 3
 #endif
 #ifndef QMOE_GROUPED_NW16
 #define QMOE_GROUPED_NW16 8
