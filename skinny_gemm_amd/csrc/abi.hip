@@ -121,7 +121,8 @@ inline int64_t grouped_max_tiles(int64_t S, int E, int tm = kTileM) {
 }
 
 struct RouteWs {
-  int64_t ids, w, counts, offsets, row_list, slot_pos, token_of, active, num_active, slot_info, tile_info, end;
+  int64_t ids, w, counts, offsets, row_list, slot_pos, token_of, active, num_active, slot_info, tile_info,
+      range_base, end;
   static RouteWs make(Carve &c, int64_t S, int E) {
     RouteWs r;
     r.ids = c.take(S * 4);
@@ -135,6 +136,7 @@ struct RouteWs {
     r.num_active = c.take(4);
     r.slot_info = c.take((int64_t)E * 16);
     r.tile_info = c.take(grouped_max_tiles(S, E) * 16);
+    r.range_base = c.take((int64_t)kPlaceRanges * E * 4);
     r.end = c.off;
     return r;
   }
@@ -151,6 +153,7 @@ struct RouteWs {
     b.num_active = (int32_t *)(ws + num_active);
     b.slot_info = (int4 *)(ws + slot_info);
     b.tile_info = (int4 *)(ws + tile_info);
+    b.range_base = (int32_t *)(ws + range_base);
     return b;
   }
 };
@@ -318,7 +321,7 @@ qmoe_status make_plan(const qmoe_layer_desc &d, int32_t T, int32_t k, int path_r
     p.softmax_all = softmax_all;
     p.kernels = std::string("route,") + "rowscale,grouped_fc1_" +
                 (d.activation == QMOE_ACT_RELU ? "relu" : "swiglu") + ",grouped_fc2,combine";
-    p.launches = (p.route_fused ? 1 : 2) + 4;
+    p.launches = (p.route_fused ? 2 : 4) + 4;  // routing: [top-k, count,] expand, place
     return ok();
   }
   p.route_fused = (T <= 16) ? 1 : 0;
@@ -361,7 +364,8 @@ qmoe_status make_plan(const qmoe_layer_desc &d, int32_t T, int32_t k, int path_r
   const std::string act = d.activation == QMOE_ACT_RELU ? "relu" : "swiglu";
   p.kernels = std::string(f32 ? "split_x," : "") + (p.fc1_routes ? "route_fc1_" + act : "route,gemv_fc1_" + act) +
               (p.fc2_cat ? ",gemv_fc2_combine" : ",gemv_fc2") + (combine ? ",combine" : "");
-  p.launches = (p.fc1_routes ? 2 : 3) + (combine ? 1 : 0) + (f32 ? 1 : 0);
+  // routing kernel: the small one up to 64 slots, else expand and place
+  p.launches = (p.fc1_routes ? 2 : (int64_t)T * k <= kLanes ? 3 : 4) + (combine ? 1 : 0) + (f32 ? 1 : 0);
   return ok();
 }
 

@@ -173,7 +173,11 @@ struct RouteBufs {
   int32_t *num_active; // [1]
   int4 *slot_info;     // [max_slots] {expert, rows, first position, 0}; rows = 0 past num_active
   int4 *tile_info;     // [max_tiles] {expert, first position, rows (<= tile), tiles}; rows = 0 past the end
+  int32_t *range_base; // [kPlaceRanges][E] first row_list position of each slot range's rows of each expert
 };
+// Contiguous slot ranges whose rows the expand kernel counts and a placing
+// kernel (one workgroup per range) writes into the row list.
+constexpr int kPlaceRanges = 64;
 
 struct RouteArgs {
   const float *logits;
