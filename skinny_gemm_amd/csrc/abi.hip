@@ -321,7 +321,9 @@ qmoe_status make_plan(const qmoe_layer_desc &d, int32_t T, int32_t k, int path_r
     p.softmax_all = softmax_all;
     p.kernels = std::string("route,") + "rowscale,grouped_fc1_" +
                 (d.activation == QMOE_ACT_RELU ? "relu" : "swiglu") + ",grouped_fc2,combine";
-    p.launches = (p.route_fused ? 2 : 4) + 4;  // routing: [top-k, count,] expand, place
+    // routing: the one-workgroup expand (with the top-k up to 16 tokens, else
+    // after it), or from kPlaceMinSlots slots top-k, count, expand, place
+    p.launches = (p.route_fused ? 1 : (int64_t)T * k >= kPlaceMinSlots ? 4 : 2) + 4;
     return ok();
   }
   p.route_fused = (T <= 16) ? 1 : 0;
@@ -343,7 +345,9 @@ qmoe_status make_plan(const qmoe_layer_desc &d, int32_t T, int32_t k, int path_r
   p.ks1 = g1.waves;
   p.tn1 = g1.tn;
   p.ks2 = g2.waves;
-  p.tn2 = g2.tn;
+  // the concatenated FC2 keeps one n-tile a wave: with four its weights and
+  // partial sums do not fit the registers (it spills 36-488 B a lane)
+  p.tn2 = p.fc2_cat ? 1 : g2.tn;
   // concatenated FC2: the same number of waves on each expert matrix (the
   // most that fit a workgroup of kGemvCatMaxWaves), so that no wave's range
   // crosses from one expert to the next
@@ -364,8 +368,7 @@ qmoe_status make_plan(const qmoe_layer_desc &d, int32_t T, int32_t k, int path_r
   const std::string act = d.activation == QMOE_ACT_RELU ? "relu" : "swiglu";
   p.kernels = std::string(f32 ? "split_x," : "") + (p.fc1_routes ? "route_fc1_" + act : "route,gemv_fc1_" + act) +
               (p.fc2_cat ? ",gemv_fc2_combine" : ",gemv_fc2") + (combine ? ",combine" : "");
-  // routing kernel: the small one up to 64 slots, else expand and place
-  p.launches = (p.fc1_routes ? 2 : (int64_t)T * k <= kLanes ? 3 : 4) + (combine ? 1 : 0) + (f32 ? 1 : 0);
+  p.launches = (p.fc1_routes ? 2 : 3) + (combine ? 1 : 0) + (f32 ? 1 : 0);
   return ok();
 }
 

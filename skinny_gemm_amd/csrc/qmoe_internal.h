@@ -178,6 +178,7 @@ struct RouteBufs {
 // Contiguous slot ranges whose rows the expand kernel counts and a placing
 // kernel (one workgroup per range) writes into the row list.
 constexpr int kPlaceRanges = 64;
+constexpr int kPlaceMinSlots = 4096;  // routed slots from which that ranged sort runs (fewer: one workgroup)
 
 struct RouteArgs {
   const float *logits;

@@ -3,15 +3,16 @@
 //
 //   top-k   one wavefront per token (wave_topk).
 //   expand  a stable counting sort of the flat slots r = t*k + j by expert,
-//           over kPlaceRanges contiguous slot ranges.  One workgroup counts
-//           each range's rows per expert (64 slots a step, ranks inside a
-//           step from ballots over the expert id bits; one wave per range
-//           after a separate top-k kernel), and from the counts
-//           gives offsets (exclusive scan), the active experts, the slot and
-//           tile lists and each range's first position per expert; then one
-//           wave per range writes its slots into row_list and the inverse
-//           maps (route_place_kernel), so the scattered stores come from
-//           many compute units.
+//           over kPlaceRanges contiguous slot ranges: one wave per range
+//           counts its rows per expert (64 slots a step, ranks inside a step
+//           from ballots over the expert id bits); one workgroup turns the
+//           counts into offsets (exclusive scan), the active experts, the
+//           slot and tile lists and each range's first position per expert;
+//           one wave per range writes its slots into row_list and the
+//           inverse maps, so the per-slot work and the scattered stores are
+//           spread over many compute units.
+//   expand (fewer than kPlaceMinSlots slots) one workgroup sorts the slots
+//           on its own (and for T <= 16 routes the tokens itself first).
 //   small   (T*k <= 64 slots, no tile list) one workgroup: one wavefront
 //           per token for the top-k, then one wavefront builds every list
 //           from ballots (wave_expand_lists).
@@ -29,6 +30,185 @@ __global__ __launch_bounds__(256) void route_topk_kernel(RouteArgs a) {
   if (t >= a.T) return;
   wave_topk<ALL>(a.logits + (int64_t)t * a.E, a.E, a.k, a.r.ids + (int64_t)t * a.k,
             a.r.w + (int64_t)t * a.k, nullptr, &s_tk[threadIdx.x / kLanes]);
+}
+
+constexpr int kSmallCachedTiles = 16;  // slot ids per thread held in registers by the one-workgroup expand
+
+// Small batches: one workgroup (which with topk_in_expand, T <= kExpandWaves,
+// first routes the tokens itself, one wave per token) builds the LDS histogram
+// -> counts, the exclusive scan -> offsets, the active experts and the slot
+// and tile lists, then sorts the slots stably by expert one tile of
+// kExpandThreads slots at a time (rank inside a wave from ballots over the
+// expert id bits, ranks across waves from per-wave counts in LDS).
+template <bool ALL>
+__global__ __launch_bounds__(kExpandThreads) void route_expand_one_kernel(RouteArgs a) {
+  __shared__ int s_cnt[kMaxExperts];
+  __shared__ int s_off[kMaxExperts + 1];
+  __shared__ int s_base[kMaxExperts];
+  __shared__ int s_wc[2][kExpandWaves][kMaxExperts];  // per tile parity: wave counts, then prefixes
+  __shared__ int32_t s_ids[kExpandWaves * kMaxTopK];
+  __shared__ TopkScratch s_tk[kExpandWaves];
+  const int tid = threadIdx.x, lane = tid & (kLanes - 1), wave = tid / kLanes;
+  const int E = a.E;
+  const int S = a.T * a.k;
+  const bool fused = a.topk_in_expand != 0;
+
+  if (fused && wave < a.T) {
+    wave_topk<ALL>(a.logits + (int64_t)wave * E, E, a.k, a.r.ids + (int64_t)wave * a.k,
+              a.r.w + (int64_t)wave * a.k, s_ids + wave * a.k, &s_tk[wave]);
+  }
+  for (int e = tid; e < kMaxExperts; e += kExpandThreads) {
+    s_cnt[e] = 0;
+    s_base[e] = 0;
+  }
+  for (int i = tid; i < a.zero_len; i += kExpandThreads) a.zero_buf[i] = 0;
+  for (int i = tid; i < 2 * kExpandWaves * kMaxExperts; i += kExpandThreads) (&s_wc[0][0][0])[i] = 0;
+  __syncthreads();
+
+  // the first kSmallCachedTiles tiles of slot ids, loaded once into registers
+  // (one memory latency for all of them instead of one per tile)
+  int ecache[kSmallCachedTiles];
+#pragma unroll
+  for (int i = 0; i < kSmallCachedTiles; ++i) {
+    const int r = i * kExpandThreads + tid;
+    ecache[i] = (r < S) ? (fused ? s_ids[r] : a.r.ids[r]) : 0;
+  }
+#pragma unroll
+  for (int i = 0; i < kSmallCachedTiles; ++i)
+    if (i * kExpandThreads + tid < S) atomicAdd(&s_cnt[ecache[i]], 1);
+  for (int r = kSmallCachedTiles * kExpandThreads + tid; r < S; r += kExpandThreads) {
+    const int e = fused ? s_ids[r] : a.r.ids[r];
+    atomicAdd(&s_cnt[e], 1);
+  }
+  __syncthreads();
+
+  // Exclusive scan of counts and compaction of the active experts (wave 0).
+  if (wave == 0) {
+    constexpr int PER = kMaxExperts / kLanes;
+    int c[PER], f[PER];
+    int cs = 0, fs = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int e = lane * PER + i;
+      c[i] = (e < E) ? s_cnt[e] : 0;
+      f[i] = (c[i] > 0) ? 1 : 0;
+      cs += c[i];
+      fs += f[i];
+    }
+    int ci = cs, fi = fs;  // inclusive scans across lanes
+#pragma unroll
+    for (int off = 1; off < kLanes; off <<= 1) {
+      const int oc = __shfl_up(ci, off), of = __shfl_up(fi, off);
+      if (lane >= off) {
+        ci += oc;
+        fi += of;
+      }
+    }
+    int run = ci - cs, frun = fi - fs;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int e = lane * PER + i;
+      if (e < E) {
+        s_off[e] = run;
+        a.r.offsets[e] = run;
+        a.r.counts[e] = c[i];
+        if (f[i]) {
+          a.r.active[frun] = e;
+          if (frun < a.max_slots) a.r.slot_info[frun] = make_int4(e, c[i], run, 0);
+        }
+      }
+      run += c[i];
+      frun += f[i];
+    }
+    if (lane == kLanes - 1) {
+      s_off[E] = ci;
+      a.r.offsets[E] = ci;
+      a.r.num_active[0] = fi;
+    }
+    // slots past the active experts do no work
+    const int na = __shfl(fi, kLanes - 1);
+    for (int sl = na + lane; sl < a.max_slots; sl += kLanes) a.r.slot_info[sl] = make_int4(0, 0, 0, 0);
+
+    // grouped path: tiles of tile_rows rows per expert, in expert order; every
+    // entry's last field holds the number of tiles (the grouped kernels map
+    // their workgroups over that many)
+    if (a.tile_rows > 0) {
+      int nt[PER];
+      int ts = 0;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        nt[i] = (c[i] + a.tile_rows - 1) / a.tile_rows;
+        ts += nt[i];
+      }
+      int ti = ts;
+#pragma unroll
+      for (int off = 1; off < kLanes; off <<= 1) {
+        const int o = __shfl_up(ti, off);
+        if (lane >= off) ti += o;
+      }
+      int tpos = ti - ts;
+      int roff = ci - cs;
+      const int ntot = __shfl(ti, kLanes - 1);
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        const int e = lane * PER + i;
+        for (int t = 0; t < nt[i]; ++t)
+          if (tpos + t < a.max_tiles)
+            a.r.tile_info[tpos + t] =
+                make_int4(e, roff + t * a.tile_rows, min(a.tile_rows, c[i] - t * a.tile_rows), ntot);
+        tpos += nt[i];
+        roff += c[i];
+      }
+      for (int t = ntot + lane; t < a.max_tiles; t += kLanes) a.r.tile_info[t] = make_int4(0, 0, 0, ntot);
+    }
+  }
+  __syncthreads();
+
+  // Stable scatter, one tile of kExpandThreads slots at a time (ids of the
+  // first tiles from registers, later ones loaded).
+  auto scatter = [&](int t0, int e) __attribute__((always_inline)) {
+    const int r = t0 + tid;
+    const bool valid = r < S;
+    uint64_t same = __ballot(valid);
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      const uint64_t bb = __ballot(valid && ((e >> b) & 1));
+      same &= ((e >> b) & 1) ? bb : ~bb;
+    }
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (kLanes - lane));
+    const int rank = __popcll(same & below);
+    const int pb = (t0 / kExpandThreads) & 1;  // this tile's buffer (all zero on entry)
+    if (valid && rank == 0) s_wc[pb][wave][e] = __popcll(same);
+    __syncthreads();
+    // per expert: the wave counts become exclusive prefixes over the waves
+    // (plus the rows of earlier tiles), the base moves past this tile, and
+    // the other buffer -- read by the previous tile before the barrier
+    // above -- is cleared for the next tile
+    for (int x = tid; x < E; x += kExpandThreads) {
+      int run = s_base[x];
+      for (int w2 = 0; w2 < kExpandWaves; ++w2) {
+        const int c = s_wc[pb][w2][x];
+        s_wc[pb][w2][x] = run;
+        s_wc[pb ^ 1][w2][x] = 0;
+        run += c;
+      }
+      s_base[x] = run;
+    }
+    __syncthreads();
+    if (valid) {
+      const int pos = s_off[e] + s_wc[pb][wave][e] + rank;
+      a.r.row_list[pos] = r;
+      a.r.slot_pos[r] = pos;
+      a.r.token_of[pos] = r / a.k;
+    }
+  };
+#pragma unroll
+  for (int i = 0; i < kSmallCachedTiles; ++i)
+    if (i * kExpandThreads < S) scatter(i * kExpandThreads, ecache[i]);
+  for (int t0 = kSmallCachedTiles * kExpandThreads; t0 < S; t0 += kExpandThreads) {
+    const int r = t0 + tid;
+    scatter(t0, r < S ? (fused ? s_ids[r] : a.r.ids[r]) : 0);
+  }
 }
 
 // Slot ranges: kPlaceRanges contiguous ranges of whole 64-slot steps.
@@ -51,59 +231,22 @@ __device__ inline void step_match(bool valid, int e, uint64_t &same, int &rank) 
   rank = __popcll(same & below);
 }
 
-// Single workgroup.  With topk_in_expand (T <= kExpandWaves) the workgroup
-// first routes the tokens itself, one wave per token.  It counts the rows
-// of each expert in each slot range, and writes counts, offsets, the active
-// experts, the slot and tile lists and each range's first position per
-// expert; route_place_kernel then writes the row list.
+// Single workgroup, after route_topk_kernel and route_count_kernel: from
+// the rows of each expert in each slot range, the counts, offsets, the
+// active experts, the slot and tile lists and each range's first position
+// per expert; route_place_kernel then writes the row list.
 template <bool ALL>
 __global__ __launch_bounds__(kExpandThreads) void route_expand_kernel(RouteArgs a) {
   __shared__ int s_cnt[kMaxExperts];
   __shared__ int s_off[kMaxExperts + 1];
   __shared__ int s_rc[kPlaceRanges][kMaxExperts];  // per range: count, then exclusive prefix over ranges
   __shared__ int s_seg[kExpandThreads / kMaxExperts][kMaxExperts];
-  __shared__ int32_t s_ids[kExpandWaves * kMaxTopK];
-  __shared__ TopkScratch s_tk[kExpandWaves];
   const int tid = threadIdx.x, lane = tid & (kLanes - 1), wave = tid / kLanes;
   const int E = a.E;
-  const int S = a.T * a.k;
-  const bool fused = a.topk_in_expand != 0;
-
-  if (fused && wave < a.T) {
-    wave_topk<ALL>(a.logits + (int64_t)wave * E, E, a.k, a.r.ids + (int64_t)wave * a.k,
-              a.r.w + (int64_t)wave * a.k, s_ids + wave * a.k, &s_tk[wave]);
-  }
   for (int i = tid; i < a.zero_len; i += kExpandThreads) a.zero_buf[i] = 0;
-  for (int i = tid; i < kPlaceRanges * kMaxExperts; i += kExpandThreads) (&s_rc[0][0])[i] = 0;
-  __syncthreads();
-
-  // Counts per range: from route_count_kernel after a top-k kernel, else
-  // here (the slot ids of the fused top-k are in LDS): wave w takes ranges
-  // w, w + 16, ...; a range's steps in chunks of kChunk whose ids are loaded
-  // together (one memory latency per chunk).  One leader lane per expert
-  // and step adds the step's count, so no two lanes touch one entry at once.
-  constexpr int kChunk = 8;
-  const int spr = place_range_steps(S);
-  if (!fused)
-    for (int i = tid; i < kPlaceRanges * E; i += kExpandThreads) s_rc[i / E][i % E] = a.r.range_base[i];
-  for (int q = wave; fused && q < kPlaceRanges; q += kExpandWaves) {
-    for (int c0 = 0; c0 < spr; c0 += kChunk) {
-      int ev[kChunk];
-#pragma unroll
-      for (int i = 0; i < kChunk; ++i) {
-        const int r = (q * spr + c0 + i) * kLanes + lane;
-        ev[i] = (c0 + i < spr && r < S) ? (fused ? s_ids[r] : a.r.ids[r]) : 0;
-      }
-#pragma unroll
-      for (int i = 0; i < kChunk; ++i) {
-        const int r = (q * spr + c0 + i) * kLanes + lane;
-        const bool valid = c0 + i < spr && r < S;
-        uint64_t same;
-        int rank;
-        step_match(valid, ev[i], same, rank);
-        if (valid && rank == 0) s_rc[q][ev[i]] += __popcll(same);
-      }
-    }
+  for (int i = tid; i < kPlaceRanges * kMaxExperts; i += kExpandThreads) {
+    const int q = i / kMaxExperts, e = i % kMaxExperts;
+    s_rc[q][e] = e < E ? a.r.range_base[q * E + e] : 0;
   }
   __syncthreads();
   // Per expert: segment sums of 16 ranges, then each range's count becomes
@@ -309,14 +452,18 @@ template <bool ALL>
 hipError_t launch_route_as(const RouteArgs &a, hipStream_t s) {
   if (a.topk_in_expand && a.T > 0 && (int64_t)a.T * a.k <= kLanes && a.tile_rows == 0 && a.zero_len == 0)
     return qlaunch(route_small_kernel<ALL>, dim3(1), dim3(a.T * kLanes), 0, s, a);
+  // many slots: counted and placed one wave per slot range around the
+  // expand workgroup; fewer: the one-workgroup sort (three fewer launches)
+  const bool ranged = !a.topk_in_expand && (int64_t)a.T * a.k >= kPlaceMinSlots;
   if (!a.topk_in_expand && a.T > 0) {
     const int per = 256 / kLanes;
     hipError_t e = qlaunch(route_topk_kernel<ALL>, dim3((a.T + per - 1) / per), dim3(256), 0, s, a);
-    if (e == hipSuccess) e = qlaunch(route_count_kernel, dim3(kPlaceRanges), dim3(kLanes), 0, s, a);
+    if (e == hipSuccess && ranged) e = qlaunch(route_count_kernel, dim3(kPlaceRanges), dim3(kLanes), 0, s, a);
     if (e != hipSuccess) return e;
   }
+  if (!ranged) return qlaunch(route_expand_one_kernel<ALL>, dim3(1), dim3(kExpandThreads), 0, s, a);
   const hipError_t e = qlaunch(route_expand_kernel<ALL>, dim3(1), dim3(kExpandThreads), 0, s, a);
-  if (e != hipSuccess || (int64_t)a.T * a.k == 0) return e;
+  if (e != hipSuccess) return e;
   return qlaunch(route_place_kernel, dim3(kPlaceRanges), dim3(kLanes), 0, s, a);
 }
 
