@@ -310,13 +310,14 @@ def test_mixed_int2_int4_prefill(seed):
     (dict(E=5, H=256, I=256, top_k=3, fc1="ternary", block1=128, fc2="sym_int4", scale_dtype="f16"), 250, "iid"),
 ], ids=["int2-int4-shared", "int2-int4-iid", "affine-f16-shared", "ternary-f16-iid"])
 def test_grouped_multi_tile_every_row(cfg, T, logits_mode):
-    """Experts with several 64-row tiles and a partial last one (shared
-    logits: every selected expert gets all T rows), every output row
-    compared with the oracle."""
+    """Experts with several grouped tiles (128 rows, 64 in layers with an
+    affine matrix) and a partial last one (shared logits: every selected
+    expert gets all T rows), every output row compared with the oracle."""
     spec = custom_moe_spec(**cfg)
     inp = _inputs(spec, T, 21, logits_mode)
     counts = oracle.route(inp["logits"], spec.top_k)["counts"]
-    assert counts.max() > 2 * 64 and np.any((counts > 64) & (counts % 64 != 0)), counts
+    tile = 64 if "affine" in cfg["fc1"] or "affine" in cfg["fc2"] else 128
+    assert counts.max() > tile and np.any((counts > tile) & (counts % tile != 0)), counts
     run_case(spec, T, 21, logits_mode=logits_mode, path="grouped")
 
 
