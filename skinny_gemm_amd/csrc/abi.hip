@@ -323,7 +323,7 @@ qmoe_status make_plan(const qmoe_layer_desc &d, int32_t T, int32_t k, int path_r
                 (d.activation == QMOE_ACT_RELU ? "relu" : "swiglu") + ",grouped_fc2,combine";
     // routing: the one-workgroup expand (with the top-k up to 16 tokens, else
     // after it), or from kPlaceMinSlots slots top-k, count, expand, place
-    p.launches = (p.route_fused ? 1 : (int64_t)T * k >= kPlaceMinSlots ? 4 : 2) + 4;
+    p.launches = (p.route_fused ? 1 : (int64_t)T * k >= kPlaceMinSlots ? 4 : 2) + 4 + (L.fc2.affine ? 0 : 1);
     return ok();
   }
   p.route_fused = (T <= 16) ? 1 : 0;
@@ -814,7 +814,16 @@ qmoe_status qmoe_forward_ex(const qmoe_layer_desc *desc, const void *packed, con
     q2.out_f32 = o;
     q2.bias = opts ? (const uint16_t *)opts->fc2_bias : nullptr;
     q2.act_dtype = desc->act_dtype;
+    // a non-affine FC2 reads h split once into its scaled f16 parts (in
+    // place), which every column tile then copies into LDS as they are
+    const bool split_h = !L.fc2.affine;
+    if (split_h) {
+      q2.in_f32 = 0;
+      q2.in_split = 1;
+      q2.in_row_elems = 2 * (int64_t)desc->inter;  // halves per row
+    }
     e = begin();
+    if (e == hipSuccess && split_h) e = launch_split_rows(h32, T * top_k, desc->inter, hmax, s);
     if (e == hipSuccess) e = launch_grouped(q2, kGEpiStoreF32, p.max_tiles, s);
     if (e == hipSuccess) e = end();
     if (e != hipSuccess) return hip_status(e, "grouped fc2");

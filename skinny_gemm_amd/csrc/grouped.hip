@@ -162,6 +162,36 @@ hipError_t launch_rowscale(const void *x, int rows, int64_t K, int in_f16, float
                  rowsc, xs);
 }
 
+// FC2's input, once for all column tiles: each fp32 row of h times its power
+// of two (from the row's |max| bits, below 2^14) as f16 hi = RNE(h 2^r) and
+// lo = RNE(h 2^r - hi), the same parts the grouped kernel would form while
+// staging.  Written in place: each group of 8 k becomes [hi 8][lo 8] in the
+// same 32 bytes, so one thread reads its group before writing it.
+__global__ __launch_bounds__(256) void split_rows_kernel(float *__restrict__ h, int64_t groups, int64_t gpr,
+                                                         const uint32_t *__restrict__ rowmax) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= groups) return;
+  const float sc = pow2_below(__uint_as_float(rowmax[i / gpr]), 14);
+  uint4 *g = reinterpret_cast<uint4 *>(h) + 2 * i;
+  const uint4 w0 = g[0], w1 = g[1];
+  const uint32_t w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+  half8_t hi, lo;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float xs = __uint_as_float(w[e]) * sc;
+    hi[e] = (_Float16)xs;
+    lo[e] = (_Float16)(xs - (float)hi[e]);
+  }
+  g[0] = __builtin_bit_cast(uint4, hi);
+  g[1] = __builtin_bit_cast(uint4, lo);
+}
+
+hipError_t launch_split_rows(float *h, int rows, int64_t K, const uint32_t *rowmax, hipStream_t s) {
+  const int64_t groups = (int64_t)rows * (K / 8);
+  if (groups <= 0) return hipSuccess;
+  return qlaunch(split_rows_kernel, dim3((unsigned)((groups + 255) / 256)), dim3(256), 0, s, h, groups, K / 8, rowmax);
+}
+
 hipError_t launch_rowmax_f32(const float *x, int rows, int64_t K, uint32_t *rowmax, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
   return qlaunch(rowmax_f32_kernel, dim3((rows + 3) / 4), dim3(256), 0, s, x, rows, K, rowmax);

@@ -149,8 +149,10 @@ constexpr int kWaitVmcnt0 = 0x0F70;
 constexpr int kMaxAffineBlocks = kGroupedMaxAffineBlocks;
 
 // Input modes: 16-bit rows (bf16 or f16) scaled while staged, fp32 rows
-// split into f16 hi + lo while staged, or f16 rows already scaled (copied).
-enum { kInBf16 = 0, kInF16 = 1, kInF32 = 2, kInScaled = 3 };
+// split into f16 hi + lo while staged, f16 rows already scaled (copied), or
+// fp32 rows already split into scaled f16 hi + lo parts (copied; a row holds
+// the parts of each 8 k together, [hi 8][lo 8], see split_rows_kernel).
+enum { kInBf16 = 0, kInF16 = 1, kInF32 = 2, kInScaled = 3, kInSplit = 4 };
 
 // MI: 16-row MFMA row tiles per wave (tile rows TM = 16 MI).  MI = 8 halves
 // the LDS reads and the weight dequantization per MFMA of MI = 4: every
@@ -162,12 +164,12 @@ enum { kInBf16 = 0, kInF16 = 1, kInF32 = 2, kInScaled = 3 };
 template <int QT, int EPI, int INM, int MI, int NJ, int KT, int NW, bool SPLIT>
 __global__ __launch_bounds__(64 * NW, MI == 8 ? grouped_waves_per_simd(INM == 2, SPLIT, EPI == kGEpiStoreF32) : 1) void grouped_kernel(
     const GroupedArgs a) {
-  constexpr bool IN_F32 = INM == kInF32, IN_F16 = INM == kInF16, PRE = INM == kInScaled;
+  constexpr bool IN_F32 = INM == kInF32, IN_F16 = INM == kInF16, PRE = INM == kInScaled, SPL = INM == kInSplit;
   using TR = QtTraits<QT>;
   using CD = Codec<TR::kBits, true>;
   constexpr int TM = 16 * MI;          // rows per tile
   constexpr int KC = 128 / TR::kBits;  // k per 16-B chunk: 32 (4-bit) or 64 (2-bit)
-  constexpr int NPART = IN_F32 ? 2 : 1;  // fp32 input: f16 hi + lo parts (about 22 bits)
+  constexpr int NPART = (IN_F32 || SPL) ? 2 : 1;  // fp32 input: f16 hi + lo parts (about 22 bits)
   constexpr int CPT = KT / KC;         // chunks per tile
   constexpr int KS = KT / 32;          // MFMA k-steps per tile
   constexpr int APAD = 8;              // row padding of the staged tile (halves)
@@ -185,13 +187,14 @@ __global__ __launch_bounds__(64 * NW, MI == 8 ? grouped_waves_per_simd(INM == 2,
   // fit f16: the scale is split into an 8-bit head and its tail (two MFMAs)
   constexpr bool MULTIBIT = (QT == QMOE_QTYPE_SYM_INT4 || QT == QMOE_QTYPE_AFFINE_INT4);
 
-  // DIRECT: pre-scaled 16-bit rows (a plain copy) are loaded straight into
-  // LDS (global_load_lds, 16 B a lane) into two separate arrays; the other
-  // modes convert in registers and store into sA
-  constexpr bool DIRECT = PRE && !AFF;
+  // DIRECT: pre-scaled 16-bit rows or parts (a plain copy) are loaded
+  // straight into LDS (global_load_lds, 16 B a lane) into two separate
+  // arrays; the other modes convert in registers and store into sA
+  constexpr bool DIRECT = (PRE || SPL) && !AFF;
+  static_assert(!(SPL && AFF), "pre-split rows feed the non-affine formats only");
   __shared__ _Float16 sA[DIRECT ? 1 : 2][NPART][DIRECT ? 1 : TM][DIRECT ? 1 : KT + APAD];
-  __shared__ __attribute__((aligned(16))) _Float16 sD0[DIRECT ? TM * KT : 8];
-  __shared__ __attribute__((aligned(16))) _Float16 sD1[DIRECT ? TM * KT : 8];
+  __shared__ __attribute__((aligned(16))) _Float16 sD0[DIRECT ? NPART * TM * KT : 8];
+  __shared__ __attribute__((aligned(16))) _Float16 sD1[DIRECT ? NPART * TM * KT : 8];
   __shared__ int s_row[TM];
   __shared__ float s_rsc[TM];
   __shared__ float s_rinv[TM];  // 1 / s_rsc (exact: powers of two), 0 past the rows
@@ -243,7 +246,7 @@ __global__ __launch_bounds__(64 * NW, MI == 8 ? grouped_waves_per_simd(INM == 2,
     if (r < rows) {
       const int p = p0 + r;
       inrow = (a.dense_M > 0) ? p : (a.in_gather_token ? a.token_of[p] : p);
-      sc = IN_F32 ? pow2_below(__uint_as_float(a.in_rowmax[inrow]), 14) : a.in_rowsc[inrow];
+      sc = (IN_F32 || SPL) ? pow2_below(__uint_as_float(a.in_rowmax[inrow]), 14) : a.in_rowsc[inrow];
     }
     s_row[r] = inrow;
     s_rsc[r] = sc;
@@ -543,14 +546,19 @@ __global__ __launch_bounds__(64 * NW, MI == 8 ? grouped_waves_per_simd(INM == 2,
         gsrc[q] = reinterpret_cast<const uint16_t *>(a.in) + (int64_t)(in >= 0 ? in : 0) * a.in_row_elems;
         dslot[q] = (slot ^ (row & 7)) * 8;  // k of this lane's piece within the tile
       }
-      // a piece past K reads the row's last 8 values instead (K >= 32)
+      // a piece past K reads the row's last 8 values instead (K >= 32); a
+      // pre-split row holds [hi 8][lo 8] per 8 k, part p of the piece at k
+      // at 2 k + 8 p, and part p lands TM x KT halves after part 0
+      constexpr int KM = SPL ? 2 : 1;
       auto dma = [&](int64_t kt, _Float16 *D) __attribute__((always_inline)) {
 #pragma unroll
         for (int q = 0; q < IPW; ++q) {
           const int64_t k = kt + dslot[q] < a.K - 8 ? kt + dslot[q] : a.K - 8;
-          // (untyped pointers: a typed source pointer keeps the host pass from emitting the kernel's stub)
-          __builtin_amdgcn_global_load_lds((const void *)(gsrc[q] + k), (void *)(D + (q * NW + wave) * RPI * KT), 16,
-                                           0, 0);
+#pragma unroll
+          for (int pp = 0; pp < NPART; ++pp)
+            // (untyped pointers: a typed source pointer keeps the host pass from emitting the kernel's stub)
+            __builtin_amdgcn_global_load_lds((const void *)(gsrc[q] + KM * k + 8 * pp),
+                                             (void *)(D + pp * TM * KT + (q * NW + wave) * RPI * KT), 16, 0, 0);
         }
       };
       // after the copy of the tile at kt has landed: clear its pieces past K
@@ -559,11 +567,14 @@ __global__ __launch_bounds__(64 * NW, MI == 8 ? grouped_waves_per_simd(INM == 2,
 #pragma unroll
           for (int q = 0; q < IPW; ++q)
             if (kt + dslot[q] >= a.K)
-              *reinterpret_cast<uint4 *>(D + (q * NW + wave) * RPI * KT + lane * 8) = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+              for (int pp = 0; pp < NPART; ++pp)
+                *reinterpret_cast<uint4 *>(D + pp * TM * KT + (q * NW + wave) * RPI * KT + lane * 8) =
+                    make_uint4(0u, 0u, 0u, 0u);
         }
       };
       using RSc = std::integral_constant<int, KT>;
-      using PSc = std::integral_constant<int, 0>;
+      using PSc = std::integral_constant<int, TM * KT>;
       using SWc = std::integral_constant<bool, true>;
       load_b(0, bwA, svA);
       dma(0, sD0);
@@ -735,7 +746,10 @@ hipError_t launch_grouped_split(const GroupedArgs &a, int grid, hipStream_t s) {
     if (!a.in_scaled) return hipErrorInvalidConfiguration;
     return qlaunch(QMOE_GK(kInScaled, S16));
   } else if constexpr (EPI == kGEpiStoreF32) {
-    if (!a.in_f32) return hipErrorInvalidConfiguration;
+    if constexpr (!QtTraits<QT>::kAffine) {
+      if (a.in_split) return qlaunch(QMOE_GK(kInSplit, S32));
+    }
+    if (!a.in_f32 || a.in_split) return hipErrorInvalidConfiguration;
     return qlaunch(QMOE_GK(kInF32, S32));
   } else {
     if (a.in_f32 || a.in_scaled) return hipErrorInvalidConfiguration;

@@ -430,6 +430,7 @@ struct GroupedArgs {
   // or f16 rows already multiplied by their power-of-two scale (in_scaled = 1)
   const void *in;
   int in_f32, in_f16, in_scaled;
+  int in_split;              // FC2: fp32 rows already split into scaled f16 parts, [hi 8][lo 8] per 8 k (non-affine)
   int64_t in_row_elems;
   const float *in_rowsc;   // 16-bit input: power-of-two scale per input row
   const uint32_t *in_rowmax; // fp32 input: |max| bits per row (scale derived)
@@ -453,6 +454,9 @@ hipError_t launch_rowscale(const void *x, int rows, int64_t K, int in_f16, float
                            hipStream_t s);
 // Bits of max |x| per fp32 row (K a multiple of 4, rows 16-B aligned).
 hipError_t launch_rowmax_f32(const float *x, int rows, int64_t K, uint32_t *rowmax, hipStream_t s);
+// fp32 rows [rows][K] (K a multiple of 8) -> in place, per 8 k, [hi 8][lo 8]
+// f16 parts of the row times its power of two from rowmax
+hipError_t launch_split_rows(float *h, int rows, int64_t K, const uint32_t *rowmax, hipStream_t s);
 hipError_t launch_wscale(const MatLayout &L, int E, const uint8_t *mat, float *wsc, hipStream_t s);
 
 // ---------------------------------------------------------------- launches

@@ -176,9 +176,9 @@ def test_plan_grouped_prefill():
     p = q.forward_plan(d, 2048, 8)
     assert p["path"] == 2
     assert p["kernels"] == ["route", "rowscale", "grouped_fc1_swiglu", "grouped_fc2", "combine"]
-    assert p["num_launches"] == 8  # top-k, count, expand, place, rowscale, FC1, FC2, combine
+    assert p["num_launches"] == 9  # top-k, count, expand, place, rowscale, FC1, split h, FC2, combine
     pg = q.forward_plan(_desc(), 4, 6, path="grouped")
-    assert pg["path"] == 2 and pg["num_launches"] == 5
+    assert pg["path"] == 2 and pg["num_launches"] == 6
     assert q.workspace_size(d, 2048, 8) >= p["workspace_bytes"]
 
 
