@@ -320,7 +320,8 @@ qmoe_status make_plan(const qmoe_layer_desc &d, int32_t T, int32_t k, int path_r
     p.max_tiles = (int)grouped_max_tiles((int64_t)T * k, d.num_experts, p.tile_rows);
     p.softmax_all = softmax_all;
     p.kernels = std::string("route,") + "rowscale,grouped_fc1_" +
-                (d.activation == QMOE_ACT_RELU ? "relu" : "swiglu") + ",grouped_fc2,combine";
+                (d.activation == QMOE_ACT_RELU ? "relu" : "swiglu") + (L.fc2.affine ? "" : ",split_h") +
+                ",grouped_fc2,combine";
     // routing: the one-workgroup expand (with the top-k up to 16 tokens, else
     // after it), or from kPlaceMinSlots slots top-k, count, expand, place
     p.launches = (p.route_fused ? 1 : (int64_t)T * k >= kPlaceMinSlots ? 4 : 2) + 4 + (L.fc2.affine ? 0 : 1);
@@ -822,8 +823,13 @@ qmoe_status qmoe_forward_ex(const qmoe_layer_desc *desc, const void *packed, con
       q2.in_split = 1;
       q2.in_row_elems = 2 * (int64_t)desc->inter;  // halves per row
     }
+    if (split_h) {
+      e = begin();
+      if (e == hipSuccess) e = launch_split_rows(h32, T * top_k, desc->inter, hmax, s);
+      if (e == hipSuccess) e = end();
+      if (e != hipSuccess) return hip_status(e, "split h");
+    }
     e = begin();
-    if (e == hipSuccess && split_h) e = launch_split_rows(h32, T * top_k, desc->inter, hmax, s);
     if (e == hipSuccess) e = launch_grouped(q2, kGEpiStoreF32, p.max_tiles, s);
     if (e == hipSuccess) e = end();
     if (e != hipSuccess) return hip_status(e, "grouped fc2");

@@ -175,7 +175,7 @@ def test_plan_grouped_prefill():
     d = q.layer_desc(128, 4096, 1536, "bf16", ("sym_int2", 64, "bf16"), ("sym_int4", 64, "bf16"))
     p = q.forward_plan(d, 2048, 8)
     assert p["path"] == 2
-    assert p["kernels"] == ["route", "rowscale", "grouped_fc1_swiglu", "grouped_fc2", "combine"]
+    assert p["kernels"] == ["route", "rowscale", "grouped_fc1_swiglu", "split_h", "grouped_fc2", "combine"]
     assert p["num_launches"] == 9  # top-k, count, expand, place, rowscale, FC1, split h, FC2, combine
     pg = q.forward_plan(_desc(), 4, 6, path="grouped")
     assert pg["path"] == 2 and pg["num_launches"] == 6
@@ -273,7 +273,7 @@ def test_plan_f32_activations():
     b = q.forward_plan(_desc(), 4, 6)["workspace_bytes"]
     assert q.forward_plan(d, 4, 6)["workspace_bytes"] == b + 2 * (4 * 2048 * 2)   # x hi + lo rows
     g4 = q.forward_plan(d, 4, 6, "grouped")
-    assert g4["kernels"] == ["route", "rowscale", "grouped_fc1_swiglu", "grouped_fc2", "combine"]
+    assert g4["kernels"] == ["route", "rowscale", "grouped_fc1_swiglu", "split_h", "grouped_fc2", "combine"]
     p17 = q.forward_plan(d, 17, 6)          # the grouped path in one pass
     assert (p17["num_tiles"], p17["path"]) == (1, 2)
     L = q.lib()
@@ -289,7 +289,8 @@ def test_relu_layer_descriptor_and_plan():
     assert q.prepacked_size(d) < q.prepacked_size(sw)              # FC1 half the rows
     assert q.forward_plan(d, 1, 1)["kernels"] == ["route_fc1_relu", "gemv_fc2"]
     assert q.forward_plan(d, 9, 2)["kernels"] == ["route", "gemv_fc1_relu", "gemv_fc2", "combine"]
-    assert q.forward_plan(d, 64, 2)["kernels"] == ["route", "rowscale", "grouped_fc1_relu", "grouped_fc2", "combine"]
+    assert q.forward_plan(d, 64, 2)["kernels"] == ["route", "rowscale", "grouped_fc1_relu", "split_h", "grouped_fc2",
+                                                   "combine"]
     bad = q.layer_desc(64, 768, 3072, "bf16", ("ternary", 128, "f16"), ("ternary", 128, "f16"), "relu")
     bad.fc1.rows = 2 * 3072                                         # SwiGLU-shaped FC1 with ReLU
     bad2 = q.layer_desc(64, 768, 3072, "bf16", ("ternary", 128, "f16"), ("ternary", 128, "f16"))
